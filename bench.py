@@ -1,0 +1,214 @@
+"""Benchmark of the index-selection sparse attention layer on one MI355X.
+
+A step is one call of li_topk_sfa (indexer scores -> Top-K -> sparse MLA
+attention) over one batch of synthetic decode queries: by default 64
+sequences at context 32768, paged 64-token blocks, 64x128 bf16 indexer,
+K = 2048, 128-head 512+64 bf16 MLA.  Inputs are generated on the GPU before
+timing and stay resident in HBM.
+
+Prints ONE JSON line with the layer throughput (query rows per second), the
+roofline of the dominant kernel (timed live with HIP events on its stream),
+per-stage timings, and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse-attn layer tokens/s (indexer+TopK+SFA) at L=32K; % of HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic(wl, b):
+    """Algorithmic bytes / flops per launch of each stage (what the method must
+    move or compute; the dense attention it avoids is not counted)."""
+    R = b.R
+    vis = sum(int(p) + 1 for p in b.row_pos.tolist())
+    ke = 1 if wl.indexer_dtype == "fp8" else 2
+    ks = 4 if wl.indexer_dtype == "fp8" else 0
+    ve = 1 if wl.kv_dtype == "fp8" else 2
+    sel = sum(min(wl.K, int(p) + 1) for p in b.row_pos.tolist())
+    li_bytes = vis * (wl.D_I * ke + ks) + R * wl.H_I * (wl.D_I * ke + 4)
+    li_flops = 2.0 * wl.H_I * wl.D_I * vis
+    sfa_bytes = sel * (wl.D_qk * ve) + R * wl.H * (wl.D_qk * 2 + wl.D_v * 2 + 4)
+    if wl.kv_dtype == "fp8":
+        sfa_bytes += sel * 4
+    sfa_flops = 2.0 * wl.H * sel * (wl.D_qk + wl.D_v)
+    topk_bytes = vis * 4 + R * wl.K * 4
+    return dict(li=(li_bytes, li_flops), topk=(topk_bytes, 0.0), sfa=(sfa_bytes, sfa_flops))
+
+
+def time_on_stream(fn, stream, warmup, steps):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps * 1e-3  # seconds per call
+
+
+def cpu_baseline(b, budget_s: float):
+    """The oracle, as is, on the first rows of the same batch until about
+    budget_s seconds of CPU work; tokens/s = rows / oracle seconds."""
+    import numpy as np
+    import oracle as O
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    inp = W.to_numpy(b)
+    rows, t_used = 0, 0.0
+    while rows < b.R and t_used < budget_s:
+        t0 = time.perf_counter()
+        O.layer_row(inp, rows)
+        t_used += time.perf_counter() - t0
+        rows += 1
+    return dict(value=rows / t_used, unit="tokens/s", cores=int(cores), kind="oracle",
+                sample=f"first {rows} of {b.R} query rows of the same batch "
+                       f"(float64 NumPy, {t_used:.1f} s of oracle time)")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_paged_64x32768")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stage-steps", type=int, default=None)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer's multi-GPU sharding is a design, not part of this build)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import indexer_selected_sparse_li_amd as lisfa
+    import workloads as W
+
+    lisfa.load()
+    torch.cuda.set_device(0)
+    wl = W.get(args.workload)
+    log(f"[bench] generating {wl.name} on the GPU")
+    b = W.make_batch(wl, device="cuda")
+    torch.cuda.synchronize()
+    R = b.R
+    kc = lisfa.KVCache(data=b.k_data, scale=b.k_scale, scale_group=1, block_table=b.block_table,
+                       block_size=wl.block_size, seq_base=b.seq_base)
+    vc = lisfa.KVCache(data=b.kv_data, scale=b.kv_scale, scale_group=wl.kv_scale_group,
+                       block_table=b.block_table, block_size=wl.block_size, seq_base=b.seq_base)
+    rpg = 8 if (wl.mode == "prefill" and R % 8 == 0) else 1
+    out = torch.empty(R, wl.H, wl.D_v, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(R, wl.H, dtype=torch.float32, device="cuda")
+    idx = torch.empty(R, wl.K, dtype=torch.int32, device="cuda")
+    ws = torch.empty(lisfa.workspace_size(2, R, b.max_visible, wl.K, wl.H, wl.D_v), dtype=torch.uint8,
+                     device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        lisfa.li_topk_sfa(b.q_idx, b.w, kc, b.q, vc, b.row_seq, b.row_pos, wl.K, b.max_visible, out, lse,
+                          idx_out=idx, q_scale=b.q_scale, rows_per_group=rpg,
+                          softmax_scale=wl.softmax_scale, workspace=ws, stream=stream)
+
+    # the whole layer, timed: barrier + synchronize on both sides
+    log(f"[bench] warmup {args.warmup}, timed {args.steps}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    value = R / (ms_step * 1e-3)
+    log(f"[bench] layer {ms_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us)")
+
+    # stages on their own, same stream, same inputs
+    ss = args.stage_steps or args.steps
+    ld = (b.max_visible + 63) // 64 * 64
+    scores = torch.empty(R, ld, dtype=torch.float32, device="cuda")
+    sfa_ws = torch.empty(max(1, lisfa.workspace_size(1, R, 0, wl.K, wl.H, wl.D_v)), dtype=torch.uint8,
+                         device="cuda")
+    t_li = time_on_stream(lambda: lisfa.li_score(b.q_idx, b.w, kc, b.row_seq, b.row_pos, scores,
+                                                 b.max_visible, q_scale=b.q_scale, rows_per_group=rpg,
+                                                 stream=stream), stream, 2, ss)
+    t_tk = time_on_stream(lambda: lisfa.topk_select(scores, b.row_pos, wl.K, idx, stream=stream),
+                          stream, 2, ss)
+    t_sfa = time_on_stream(lambda: lisfa.sparse_mla_attn(b.q, vc, b.row_seq, idx, out, lse,
+                                                         softmax_scale=wl.softmax_scale, workspace=sfa_ws,
+                                                         stream=stream), stream, 2, ss)
+    alg = algorithmic(wl, b)
+
+    def roof(name, t, bound):
+        by, fl = alg[name]
+        if bound == "hbm":
+            ach = by / t / 1e9
+            return dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                        frac=round(ach / HBM_PEAK_GBS, 4))
+        ach = fl / t / 1e12
+        return dict(bound="mfma", achieved=round(ach, 2), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(ach / BF16_PEAK_TFLOPS, 4))
+
+    def bound_of(name):
+        by, fl = alg[name]
+        if name == "topk" or fl == 0:
+            return "hbm"
+        return "mfma" if fl / max(by, 1) > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9) else "hbm"
+
+    stages = {}
+    for name, t in (("li_score", t_li), ("topk_select", t_tk), ("sparse_mla_attn", t_sfa)):
+        key = {"li_score": "li", "topk_select": "topk", "sparse_mla_attn": "sfa"}[name]
+        r = roof(key, t, bound_of(key))
+        stages[name] = dict(us=round(t * 1e6, 2), algorithmic_bytes=int(alg[key][0]),
+                            algorithmic_flops=int(alg[key][1]), roofline=r)
+    dominant = max(stages, key=lambda k: stages[k]["us"])
+    roofline = dict(stages[dominant]["roofline"])
+    roofline["kernel"] = dominant
+    roofline["traffic"] = None
+
+    res = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.kv_dtype,
+        "data": "synthetic (seeded; inputs resident in HBM)",
+        "config": {"workload": wl.name, "rows": R, "context": b.max_visible, "K": wl.K,
+                   "indexer": f"{wl.H_I}x{wl.D_I} {wl.indexer_dtype}",
+                   "mla": f"{wl.H} heads {wl.D_latent}+{wl.D_rope} {wl.kv_dtype}",
+                   "cache": f"paged {wl.block_size}" if wl.paged else "contiguous",
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "stages": stages,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu oracle baseline")
+        res["cpu_baseline"] = cpu_baseline(b, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,205 @@
+/*
+ * lisfa.h - C ABI of the index-selection sparse attention layer for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The layer has three steps (named on "Large Language Model Inference
+ * Acceleration in Practice", section 1.2, and "Kimi New Model Open Source:
+ * Day0 Inference Adaptation and Performance Optimization on Ascend",
+ * section 3):
+ *   1. lightning indexer: relevance scores of the current query against every
+ *      cached position, weighted over the indexer heads;
+ *   2. Top-K: the K most relevant visible positions, emitted as an index list;
+ *   3. sparse flash attention: softmax attention of every MLA head over only
+ *      the selected rows of the latent KV cache.
+ * Concrete definitions used by every entry point below, for one query row r
+ * (sequence b = row_seq[r], position p = row_pos[r]):
+ *   score[s] = sum_j w[r,j] * max(0, q_idx[r,j,:] . k_idx[slot(b,s),:]),  s <= p
+ *   idx      = the min(K, p+1) positions with the largest scores, equal scores
+ *              resolved toward the lower position, sorted ascending, padded
+ *              with -1 to K entries
+ *   z_k      = softmax_scale * q[r,h,:] . kv[slot(b,idx_k),:]   (all D_qk cols)
+ *   out[r,h] = sum_k softmax(z)_k * kv[slot(b,idx_k), :D_latent]
+ *   lse[r,h] = log(sum_k exp(z_k))   (natural log)
+ *
+ * Conventions
+ *   - Every pointer is a DEVICE pointer unless stated otherwise; the argument
+ *     structs themselves live in host memory and are read during the call only.
+ *   - The caller owns every buffer, including the workspace (size it with
+ *     lisfa_workspace_size).  The library never allocates or frees device
+ *     memory, keeps no global state and is safe to call from several threads.
+ *   - All work is enqueued on `stream` (0 = the default stream) and is
+ *     asynchronous; the call returns as soon as the kernels are queued.
+ *     Device faults surface at the caller's next synchronisation.
+ *   - Arguments are validated before anything is launched; a failing call
+ *     returns a negative status and leaves every output untouched.
+ *   - Out-of-range block-table entries or positions beyond a sequence's cached
+ *     extent are never dereferenced: the indexer writes NaN for such a
+ *     position and the attention step treats it as not selected.
+ */
+#ifndef LISFA_H
+#define LISFA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* lisfa_stream_t; /* a hipStream_t */
+
+/* status codes */
+#define LISFA_OK                   0
+#define LISFA_ERR_NULL_ARG        -1
+#define LISFA_ERR_BAD_SHAPE       -2
+#define LISFA_ERR_BAD_DTYPE       -3
+#define LISFA_ERR_WORKSPACE       -4
+#define LISFA_ERR_HIP             -5
+#define LISFA_ERR_UNSUPPORTED     -6
+
+/* element types of stored tensors */
+#define LISFA_BF16      0   /* bfloat16 */
+#define LISFA_FP8_E4M3  1   /* OCP e4m3 (max 448), scaled by fp32 factors */
+
+/*
+ * A cache of fixed-width rows, one per token slot ("Kimi New Model Open
+ * Source ...", section 3: the indexer reads the key cache stored in pages;
+ * the attention step reads the main KV cache by position).  Two layouts:
+ *   paged      (block_table != NULL): slot(b, s) = block_table[b*bt_stride +
+ *              s / block_size] * block_size + s % block_size;
+ *   contiguous (block_table == NULL): slot(b, s) = seq_base_slot[b] + s.
+ * The row of slot t starts at data + t * row_stride_bytes.
+ * fp8 rows are multiplied by scale[t / scale_group_tokens] (scale_group_tokens
+ * consecutive physical slots share one fp32 factor; 1 = per token).
+ */
+typedef struct {
+    const void*    data;               /* [num_slots, row_stride_bytes] */
+    int64_t        num_slots;          /* slots in the pool (bounds checks) */
+    int32_t        dtype;              /* LISFA_BF16 or LISFA_FP8_E4M3 */
+    int32_t        row_stride_bytes;   /* multiple of 16, >= row width in bytes */
+    const float*   scale;              /* fp8: [num_slots / scale_group_tokens]; bf16: NULL */
+    int32_t        scale_group_tokens; /* fp8: >= 1 */
+    int32_t        block_size;         /* paged: tokens per block (> 0) */
+    const int32_t* block_table;        /* paged: [num_seqs, bt_stride], else NULL */
+    int32_t        bt_stride;          /* paged: entries per sequence */
+    int32_t        num_seqs;           /* sequences addressable through the cache */
+    const int64_t* seq_base_slot;      /* contiguous: [num_seqs], else NULL */
+} lisfa_cache;
+
+/* Lightning indexer inputs (one query row per r). */
+typedef struct {
+    const void*    q;            /* [R, H_I, D_I] bf16 or e4m3 (same dtype as k_cache) */
+    const float*   q_scale;      /* fp8: [R] (per query token) or [R, H_I]; bf16: NULL */
+    int32_t        q_scale_per_head; /* fp8: 0 = [R], 1 = [R, H_I] */
+    const float*   w;            /* [R, H_I] fp32 head weights */
+    lisfa_cache    k_cache;      /* rows of D_I elements */
+    const int32_t* row_seq;      /* [R] sequence of each query row */
+    const int32_t* row_pos;      /* [R] position of each query row (sees 0..row_pos) */
+    int32_t        R;            /* query rows (0 = nothing to do) */
+    int32_t        H_I;          /* indexer heads: 1..64 */
+    int32_t        D_I;          /* indexer head dim: 32 or 128 */
+    int32_t        rows_per_group; /* >= 1: aligned groups of this many consecutive rows
+                                      share one sequence (chunked prefill); the kernel
+                                      then reads each key tile once per group.  A row
+                                      whose row_seq differs from its group's first row
+                                      gets NaN scores. */
+    int64_t        max_visible;  /* host-known upper bound of row_pos[r] + 1 */
+} lisfa_indexer_args;
+
+/* Sparse MLA attention inputs. */
+typedef struct {
+    const void*    q;            /* [R, H, D_latent + D_rope] bf16 */
+    lisfa_cache    kv_cache;     /* rows [latent (D_latent) | rope (D_rope)] */
+    const int32_t* row_seq;      /* [R] */
+    int32_t        R;
+    int32_t        H;            /* heads: 1..128 */
+    int32_t        D_latent;     /* 512 (with D_rope 64) or 64 (with D_rope 16) */
+    int32_t        D_rope;
+    float          softmax_scale;
+} lisfa_mla_args;
+
+/*
+ * li_score - lightning indexer scores ("Large Language Model Inference
+ * Acceleration in Practice", section 1.2 and section 3.1, first two steps:
+ * raw relevance scores, then head-weight weighting).
+ *   scores: [R, ld_scores] fp32 (device). Row r receives positions
+ *           0..row_pos[r]; entries after row_pos[r] are left untouched.
+ *   ld_scores >= max_visible.
+ * Scores are accumulated in fp32 (products of bf16 or e4m3 values are exact
+ * in fp32).  fp8: score = k_scale[slot] * sum_j (w_j * q_scale) * ReLU(q8.k8),
+ * which equals the definition because the scales are positive.
+ */
+int li_score(const lisfa_indexer_args* args, float* scores, int64_t ld_scores,
+             lisfa_stream_t stream);
+
+/*
+ * topk_select - per-row Top-K over precomputed scores ("Kimi New Model Open
+ * Source ...", section 3: Top-K position selection that outputs only the
+ * list of selected indices).
+ *   scores: [R, ld_scores] fp32; row r uses entries 0..row_pos[r] (clamped to
+ *           ld_scores - 1; a negative row_pos selects nothing).
+ *   idx:    [R, K] int32 out, ascending positions, -1 padded.
+ * Exact: the order is that of the fp32 values (-0.0 == +0.0; NaN orders above
+ * +inf); equal values at the K-th place go to the lower positions.  The result
+ * is deterministic.  Needs no workspace (ws may be NULL, ws_bytes 0).
+ */
+int topk_select(const float* scores, int64_t ld_scores, const int32_t* row_pos,
+                int32_t R, int32_t K, int32_t* idx, void* ws, size_t ws_bytes,
+                lisfa_stream_t stream);
+
+/*
+ * sparse_mla_attn - sparse flash attention over the selected rows
+ * ("Large Language Model Inference Acceleration in Practice", section 1.2
+ * SFA, and section 3.1, third step: read the paged KV rows named by the
+ * index pointers and run attention over them).
+ *   idx:  [R, K] int32 logical positions; -1 entries are skipped.  Entries
+ *         must be unique.
+ *   out:  [R, H, D_latent] bf16.
+ *   lse:  [R, H] fp32 natural-log normaliser, or NULL.
+ *   ws:   lisfa_workspace_size(LISFA_OP_SPARSE_MLA, R, 0, K, H, D_latent) bytes.
+ * A row with no valid index gets out = 0 and lse = -inf.
+ * Compute: bf16 MFMA with fp32 accumulation; fp8 rows are converted to bf16
+ * exactly and their fp32 factor is applied to the logits and probabilities.
+ */
+int sparse_mla_attn(const lisfa_mla_args* args, const int32_t* idx, int32_t K,
+                    void* out, float* lse, void* ws, size_t ws_bytes,
+                    lisfa_stream_t stream);
+
+/*
+ * li_topk_sfa - the whole layer in one call on one stream: scores, Top-K and
+ * sparse attention ("Day0 Inference Adaptation and Performance Optimization
+ * for Kimi K3.1 Pro", section 3, and "Large Language Model Inference
+ * Acceleration in Practice", section 3.1: scoring, weighting and selection
+ * feed the sparse attention without returning to the host).  Scores and
+ * partial results live in the workspace; rows are processed in chunks so the
+ * score scratch stays bounded.
+ *   idx_out: [R, K] int32 or NULL (then the indices live in the workspace).
+ *   ws: lisfa_workspace_size(LISFA_OP_FUSED, R, max_visible, K, H, D_latent).
+ * The two argument structs must agree on R and row_seq.
+ */
+int li_topk_sfa(const lisfa_indexer_args* iargs, const lisfa_mla_args* margs,
+                int32_t K, int32_t* idx_out, void* out, float* lse,
+                void* ws, size_t ws_bytes, lisfa_stream_t stream);
+
+#define LISFA_OP_TOPK        0
+#define LISFA_OP_SPARSE_MLA  1
+#define LISFA_OP_FUSED       2
+
+/* Workspace bytes an entry point needs for the given sizes (host function). */
+size_t lisfa_workspace_size(int32_t op, int32_t R, int64_t max_visible, int32_t K,
+                            int32_t H, int32_t D_latent);
+
+/* Human-readable text of a status code (static storage, host function). */
+const char* lisfa_status_string(int32_t status);
+
+/* ABI self-description for bindings (host functions):
+ * sizeof of each argument struct: which = 0 cache, 1 indexer args, 2 mla args. */
+size_t lisfa_struct_size(int32_t which);
+/* Version of this header's ABI. */
+int32_t lisfa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LISFA_H */

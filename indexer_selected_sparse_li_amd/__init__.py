@@ -1,0 +1,191 @@
+"""Index-selection sparse attention for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI of liblisfa.so (include/lisfa.h).  It only
+marshals torch device tensors into pointers and sizes; every step of the
+layer runs in the library's HIP kernels.  PyTorch provides device memory and
+streams.  If the library has not been built, every call raises.
+
+Entry points (same names as the C ABI):
+  li_score(...)        lightning-indexer scores  [R, ld] fp32
+  topk_select(...)     per-row Top-K index lists [R, K] int32
+  sparse_mla_attn(...) sparse MLA attention      [R, H, D_latent] bf16 (+ lse)
+  li_topk_sfa(...)     all three in one call on one stream
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+from typing import Optional
+
+import torch
+
+from . import _lib as _c
+
+__all__ = ["KVCache", "LisfaError", "li_score", "topk_select", "sparse_mla_attn", "li_topk_sfa",
+           "workspace_size", "load", "status_string"]
+
+
+class LisfaError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {status_string(code)} (status {code})")
+
+
+def load():
+    return _c.load()
+
+
+def status_string(code: int) -> str:
+    return _c.load().lisfa_status_string(code).decode()
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if t.device.type != "cuda":
+        raise ValueError("tensors passed to the library must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+@dataclasses.dataclass
+class KVCache:
+    """A cache of fixed-width rows (indexer keys or MLA latent rows).
+
+    data:        [num_slots, width] bf16, or uint8 e4m3 codes
+    scale:       fp8 only: fp32 [num_slots // scale_group]
+    block_table: paged layout: int32 [num_seqs, blocks_per_seq]
+    seq_base:    contiguous layout: int64 [num_seqs] first slot of each sequence
+    """
+    data: torch.Tensor
+    scale: Optional[torch.Tensor] = None
+    scale_group: int = 1
+    block_table: Optional[torch.Tensor] = None
+    block_size: int = 64
+    seq_base: Optional[torch.Tensor] = None
+
+    @property
+    def fp8(self) -> bool:
+        return self.data.dtype == torch.uint8
+
+    def c_struct(self) -> _c.Cache:
+        d = self.data
+        if d.dim() != 2:
+            raise ValueError("cache data must be [num_slots, width]")
+        nseq = (self.block_table.shape[0] if self.block_table is not None
+                else self.seq_base.shape[0] if self.seq_base is not None else 0)
+        if self.block_table is not None and self.block_table.dtype != torch.int32:
+            raise ValueError("block_table must be int32")
+        if self.seq_base is not None and self.seq_base.dtype != torch.int64:
+            raise ValueError("seq_base must be int64")
+        if self.fp8 and (self.scale is None or self.scale.dtype != torch.float32):
+            raise ValueError("fp8 caches need fp32 scales")
+        return _c.Cache(
+            data=_ptr(d), num_slots=d.shape[0],
+            dtype=_c.LISFA_FP8_E4M3 if self.fp8 else _c.LISFA_BF16,
+            row_stride_bytes=d.stride(0) * d.element_size(),
+            scale=_ptr(self.scale), scale_group_tokens=self.scale_group,
+            block_size=self.block_size, block_table=_ptr(self.block_table),
+            bt_stride=self.block_table.shape[1] if self.block_table is not None else 0,
+            num_seqs=nseq, seq_base_slot=_ptr(self.seq_base))
+
+
+def _check(code: int, where: str):
+    if code != _c.LISFA_OK:
+        raise LisfaError(code, where)
+
+
+def _indexer_args(q_idx, w, k_cache, row_seq, row_pos, max_visible, q_scale, rows_per_group):
+    R, H_I, D_I = q_idx.shape
+    if q_scale is not None and q_scale.dtype != torch.float32:
+        raise ValueError("q_scale must be fp32")
+    per_head = q_scale is not None and q_scale.dim() == 2
+    for t, dt in ((w, torch.float32), (row_seq, torch.int32), (row_pos, torch.int32)):
+        if t.dtype != dt:
+            raise ValueError(f"expected {dt}, got {t.dtype}")
+    return _c.IndexerArgs(
+        q=_ptr(q_idx), q_scale=_ptr(q_scale), q_scale_per_head=int(per_head), w=_ptr(w),
+        k_cache=k_cache.c_struct(), row_seq=_ptr(row_seq), row_pos=_ptr(row_pos),
+        R=R, H_I=H_I, D_I=D_I, rows_per_group=rows_per_group, max_visible=int(max_visible))
+
+
+def _mla_args(q, kv_cache, row_seq, D_latent, softmax_scale):
+    R, H, D_qk = q.shape
+    if q.dtype != torch.bfloat16:
+        raise ValueError("MLA queries must be bf16")
+    return _c.MlaArgs(q=_ptr(q), kv_cache=kv_cache.c_struct(), row_seq=_ptr(row_seq), R=R, H=H,
+                      D_latent=D_latent, D_rope=D_qk - D_latent, softmax_scale=float(softmax_scale))
+
+
+def workspace_size(op: int, R: int, max_visible: int, K: int, H: int, D_latent: int) -> int:
+    return int(_c.load().lisfa_workspace_size(op, R, max_visible, K, H, D_latent))
+
+
+def _workspace(ws: Optional[torch.Tensor], need: int, device) -> Optional[torch.Tensor]:
+    if need == 0:
+        return ws
+    if ws is None:
+        return torch.empty(need, dtype=torch.uint8, device=device)
+    if ws.numel() * ws.element_size() < need:
+        raise ValueError(f"workspace of {ws.numel() * ws.element_size()} bytes < {need}")
+    return ws
+
+
+def li_score(q_idx, w, k_cache: KVCache, row_seq, row_pos, scores, max_visible: int,
+             q_scale=None, rows_per_group: int = 1, stream=None):
+    """scores[r, s] for s <= row_pos[r]; scores is [R, ld] fp32 with ld >= max_visible."""
+    lib = _c.load()
+    a = _indexer_args(q_idx, w, k_cache, row_seq, row_pos, max_visible, q_scale, rows_per_group)
+    if scores.dtype != torch.float32 or scores.dim() != 2:
+        raise ValueError("scores must be [R, ld] fp32")
+    _check(lib.li_score(ctypes.byref(a), _ptr(scores), scores.shape[1], _stream(stream)), "li_score")
+    return scores
+
+
+def topk_select(scores, row_pos, K: int, idx, stream=None):
+    """idx[r] = ascending positions of the K largest scores[r, :row_pos[r]+1], -1 padded."""
+    lib = _c.load()
+    if idx.dtype != torch.int32 or tuple(idx.shape) != (scores.shape[0], K):
+        raise ValueError("idx must be [R, K] int32")
+    _check(lib.topk_select(_ptr(scores), scores.shape[1], _ptr(row_pos), scores.shape[0], K, _ptr(idx),
+                           None, 0, _stream(stream)), "topk_select")
+    return idx
+
+
+def sparse_mla_attn(q, kv_cache: KVCache, row_seq, idx, out, lse=None, softmax_scale: float = None,
+                    workspace=None, stream=None):
+    """out[r, h] = softmax attention of q[r, h] over the latent rows named by idx[r]."""
+    lib = _c.load()
+    R, H, D_qk = q.shape
+    D_latent = out.shape[2]
+    K = idx.shape[1]
+    a = _mla_args(q, kv_cache, row_seq, D_latent, softmax_scale)
+    need = lib.lisfa_workspace_size(_c.LISFA_OP_SPARSE_MLA, R, 0, K, H, D_latent)
+    ws = _workspace(workspace, need, q.device)
+    _check(lib.sparse_mla_attn(ctypes.byref(a), _ptr(idx), K, _ptr(out), _ptr(lse),
+                               _ptr(ws) if ws is not None else None, need, _stream(stream)),
+           "sparse_mla_attn")
+    return out, lse
+
+
+def li_topk_sfa(q_idx, w, k_cache: KVCache, q, kv_cache: KVCache, row_seq, row_pos, K: int,
+                max_visible: int, out, lse=None, idx_out=None, q_scale=None, rows_per_group: int = 1,
+                softmax_scale: float = None, workspace=None, stream=None):
+    """The whole layer on one stream: scores -> Top-K -> sparse attention."""
+    lib = _c.load()
+    R, H, D_qk = q.shape
+    D_latent = out.shape[2]
+    ia = _indexer_args(q_idx, w, k_cache, row_seq, row_pos, max_visible, q_scale, rows_per_group)
+    ma = _mla_args(q, kv_cache, row_seq, D_latent, softmax_scale)
+    need = lib.lisfa_workspace_size(_c.LISFA_OP_FUSED, R, max_visible, K, H, D_latent)
+    ws = _workspace(workspace, need, q.device)
+    _check(lib.li_topk_sfa(ctypes.byref(ia), ctypes.byref(ma), K, _ptr(idx_out), _ptr(out), _ptr(lse),
+                           _ptr(ws), need, _stream(stream)), "li_topk_sfa")
+    return out, lse

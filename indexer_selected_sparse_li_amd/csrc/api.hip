@@ -1,0 +1,275 @@
+// C ABI entry points: argument validation, workspace layout and kernel
+// sequencing on the caller's stream.  No allocation, no global state.
+#include <string.h>
+
+#include "common.hpp"
+
+namespace lisfa {
+
+hipError_t li_score_dispatch(const IndexerDev& a, int D_I, int fp8, int qg, float* scores, int64_t ld,
+                             int64_t max_visible, hipStream_t stream);
+hipError_t topk_dispatch(const float* scores, int64_t ld, const int32_t* row_pos, int R, int K,
+                         int32_t* idx, hipStream_t stream);
+hipError_t sfa_dispatch(const MlaDev& a, int D_latent, int fp8, __bf16* out, float* lse, void* ws,
+                        hipStream_t stream);
+size_t sfa_workspace_bytes(int R, int K, int H, int D_latent);
+
+namespace {
+
+constexpr int64_t kScoreScratchCap = 256ll << 20;  // bytes of scores per fused chunk
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int check_cache(const lisfa_cache& c, int width) {
+    if (!c.data) return LISFA_ERR_NULL_ARG;
+    if (c.dtype != LISFA_BF16 && c.dtype != LISFA_FP8_E4M3) return LISFA_ERR_BAD_DTYPE;
+    const int elt = c.dtype == LISFA_BF16 ? 2 : 1;
+    if (c.row_stride_bytes < width * elt || c.row_stride_bytes % 16 != 0) return LISFA_ERR_BAD_SHAPE;
+    if (!aligned(c.data, 16)) return LISFA_ERR_BAD_SHAPE;
+    if (c.num_slots <= 0 || c.num_seqs <= 0) return LISFA_ERR_BAD_SHAPE;
+    if (c.dtype == LISFA_FP8_E4M3) {
+        if (!c.scale) return LISFA_ERR_NULL_ARG;
+        if (c.scale_group_tokens < 1) return LISFA_ERR_BAD_SHAPE;
+    }
+    if (c.block_table) {
+        if (c.block_size < 1 || c.block_size > (1 << 20) || (c.block_size & (c.block_size - 1)))
+            return LISFA_ERR_BAD_SHAPE;
+        if (c.bt_stride < 1) return LISFA_ERR_BAD_SHAPE;
+    } else if (!c.seq_base_slot) {
+        return LISFA_ERR_NULL_ARG;
+    }
+    return LISFA_OK;
+}
+
+CacheDev to_dev(const lisfa_cache& c) {
+    CacheDev d;
+    d.data = (const uint8_t*)c.data;
+    d.num_slots = c.num_slots;
+    d.scale = c.scale;
+    d.block_table = c.block_table;
+    d.seq_base = c.seq_base_slot;
+    d.row_stride = c.row_stride_bytes;
+    d.scale_group = c.scale_group_tokens < 1 ? 1 : c.scale_group_tokens;
+    d.bs_shift = 0;
+    if (c.block_table)
+        while ((1 << d.bs_shift) < c.block_size) ++d.bs_shift;
+    d.bt_stride = c.bt_stride;
+    d.num_seqs = c.num_seqs;
+    d.paged = c.block_table != nullptr;
+    return d;
+}
+
+int check_indexer(const lisfa_indexer_args* a) {
+    if (!a) return LISFA_ERR_NULL_ARG;
+    if (a->R < 0 || a->max_visible < 0) return LISFA_ERR_BAD_SHAPE;
+    if (a->H_I < 1 || a->H_I > 64) return LISFA_ERR_UNSUPPORTED;
+    if (a->D_I != 32 && a->D_I != 128) return LISFA_ERR_UNSUPPORTED;
+    if (a->rows_per_group < 1) return LISFA_ERR_BAD_SHAPE;
+    if (a->R == 0) return LISFA_OK;
+    if (!a->q || !a->w || !a->row_seq || !a->row_pos) return LISFA_ERR_NULL_ARG;
+    int e = check_cache(a->k_cache, a->D_I);
+    if (e) return e;
+    if (a->k_cache.dtype == LISFA_FP8_E4M3) {
+        if (!a->q_scale) return LISFA_ERR_NULL_ARG;
+        if (!aligned(a->q, 8)) return LISFA_ERR_BAD_SHAPE;
+    } else if (!aligned(a->q, 16)) {
+        return LISFA_ERR_BAD_SHAPE;
+    }
+    return LISFA_OK;
+}
+
+IndexerDev to_dev(const lisfa_indexer_args* a) {
+    IndexerDev d;
+    d.q = (const uint8_t*)a->q;
+    d.q_scale = a->q_scale;
+    d.w = a->w;
+    d.row_seq = a->row_seq;
+    d.row_pos = a->row_pos;
+    d.k = to_dev(a->k_cache);
+    d.q_scale_per_head = a->q_scale_per_head;
+    d.R = a->R;
+    d.H_I = a->H_I;
+    return d;
+}
+
+int check_mla(const lisfa_mla_args* a) {
+    if (!a) return LISFA_ERR_NULL_ARG;
+    if (a->R < 0) return LISFA_ERR_BAD_SHAPE;
+    if (a->H < 1 || a->H > 128) return LISFA_ERR_UNSUPPORTED;
+    if (!((a->D_latent == 512 && a->D_rope == 64) || (a->D_latent == 64 && a->D_rope == 16)))
+        return LISFA_ERR_UNSUPPORTED;
+    if (!(a->softmax_scale == a->softmax_scale)) return LISFA_ERR_BAD_SHAPE;
+    if (a->R == 0) return LISFA_OK;
+    if (!a->q || !a->row_seq) return LISFA_ERR_NULL_ARG;
+    if (!aligned(a->q, 16)) return LISFA_ERR_BAD_SHAPE;
+    return check_cache(a->kv_cache, a->D_latent + a->D_rope);
+}
+
+MlaDev to_dev(const lisfa_mla_args* a, const int32_t* idx, int K) {
+    MlaDev d;
+    d.q = (const uint8_t*)a->q;
+    d.row_seq = a->row_seq;
+    d.idx = idx;
+    d.kv = to_dev(a->kv_cache);
+    d.R = a->R;
+    d.H = a->H;
+    d.K = K;
+    d.scale_log2 = a->softmax_scale * kLog2e;
+    return d;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? LISFA_OK : LISFA_ERR_HIP; }
+
+int64_t scores_ld(int64_t max_visible) { return (max_visible + 63) / 64 * 64; }
+
+int64_t fused_chunk_rows(int32_t R, int64_t max_visible) {
+    const int64_t ld = scores_ld(max_visible) > 0 ? scores_ld(max_visible) : 64;
+    int64_t rc = kScoreScratchCap / (ld * 4);
+    if (rc >= R) return R;
+    rc = rc / 8 * 8;
+    return rc < 8 ? 8 : rc;
+}
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+struct FusedLayout {
+    size_t scores, idx, sfa, total;
+};
+
+FusedLayout fused_layout(int32_t R, int64_t max_visible, int32_t K, int32_t H, int32_t D_latent) {
+    FusedLayout L;
+    const int64_t rc = fused_chunk_rows(R, max_visible);
+    L.scores = 0;
+    L.idx = align256((size_t)rc * scores_ld(max_visible) * sizeof(float));
+    L.sfa = L.idx + align256((size_t)R * K * sizeof(int32_t));
+    L.total = L.sfa + align256(sfa_workspace_bytes(R, K, H, D_latent));
+    return L;
+}
+
+}  // namespace
+}  // namespace lisfa
+
+using namespace lisfa;
+
+extern "C" {
+
+int32_t lisfa_abi_version(void) { return 1; }
+
+size_t lisfa_struct_size(int32_t which) {
+    switch (which) {
+        case 0: return sizeof(lisfa_cache);
+        case 1: return sizeof(lisfa_indexer_args);
+        case 2: return sizeof(lisfa_mla_args);
+        default: return 0;
+    }
+}
+
+const char* lisfa_status_string(int32_t s) {
+    switch (s) {
+        case LISFA_OK: return "ok";
+        case LISFA_ERR_NULL_ARG: return "a required pointer argument is NULL";
+        case LISFA_ERR_BAD_SHAPE: return "a size, stride, alignment or layout argument is invalid";
+        case LISFA_ERR_BAD_DTYPE: return "unsupported element type";
+        case LISFA_ERR_WORKSPACE: return "workspace too small";
+        case LISFA_ERR_HIP: return "HIP launch error";
+        case LISFA_ERR_UNSUPPORTED: return "unsupported head count or head dimension";
+        default: return "unknown status";
+    }
+}
+
+size_t lisfa_workspace_size(int32_t op, int32_t R, int64_t max_visible, int32_t K, int32_t H,
+                            int32_t D_latent) {
+    if (R < 0 || K < 1) return 0;
+    switch (op) {
+        case LISFA_OP_TOPK: return 0;
+        case LISFA_OP_SPARSE_MLA: return sfa_workspace_bytes(R, K, H, D_latent);
+        case LISFA_OP_FUSED: return fused_layout(R, max_visible, K, H, D_latent).total;
+        default: return 0;
+    }
+}
+
+int li_score(const lisfa_indexer_args* args, float* scores, int64_t ld_scores, lisfa_stream_t stream) {
+    int e = check_indexer(args);
+    if (e) return e;
+    if (args->R == 0 || args->max_visible == 0) return LISFA_OK;
+    if (!scores) return LISFA_ERR_NULL_ARG;
+    if (ld_scores < args->max_visible) return LISFA_ERR_BAD_SHAPE;
+    const IndexerDev d = to_dev(args);
+    const int qg = (args->rows_per_group % 8 == 0) ? 8 : 1;
+    return hip_status(li_score_dispatch(d, args->D_I, args->k_cache.dtype == LISFA_FP8_E4M3, qg, scores,
+                                        ld_scores, args->max_visible, (hipStream_t)stream));
+}
+
+int topk_select(const float* scores, int64_t ld_scores, const int32_t* row_pos, int32_t R, int32_t K,
+                int32_t* idx, void* ws, size_t ws_bytes, lisfa_stream_t stream) {
+    (void)ws;
+    (void)ws_bytes;
+    if (R < 0 || K < 1 || ld_scores < 1) return LISFA_ERR_BAD_SHAPE;
+    if (R == 0) return LISFA_OK;
+    if (!scores || !row_pos || !idx) return LISFA_ERR_NULL_ARG;
+    return hip_status(topk_dispatch(scores, ld_scores, row_pos, R, K, idx, (hipStream_t)stream));
+}
+
+int sparse_mla_attn(const lisfa_mla_args* args, const int32_t* idx, int32_t K, void* out, float* lse,
+                    void* ws, size_t ws_bytes, lisfa_stream_t stream) {
+    int e = check_mla(args);
+    if (e) return e;
+    if (K < 1) return LISFA_ERR_BAD_SHAPE;
+    if (args->R == 0) return LISFA_OK;
+    if (!idx || !out) return LISFA_ERR_NULL_ARG;
+    const size_t need = sfa_workspace_bytes(args->R, K, args->H, args->D_latent);
+    if (need > 0 && (!ws || ws_bytes < need)) return LISFA_ERR_WORKSPACE;
+    if (!aligned(out, 8)) return LISFA_ERR_BAD_SHAPE;
+    const MlaDev d = to_dev(args, idx, K);
+    return hip_status(sfa_dispatch(d, args->D_latent, args->kv_cache.dtype == LISFA_FP8_E4M3, (__bf16*)out,
+                                   lse, ws, (hipStream_t)stream));
+}
+
+int li_topk_sfa(const lisfa_indexer_args* iargs, const lisfa_mla_args* margs, int32_t K, int32_t* idx_out,
+                void* out, float* lse, void* ws, size_t ws_bytes, lisfa_stream_t stream) {
+    int e = check_indexer(iargs);
+    if (e) return e;
+    e = check_mla(margs);
+    if (e) return e;
+    if (K < 1) return LISFA_ERR_BAD_SHAPE;
+    if (iargs->R != margs->R) return LISFA_ERR_BAD_SHAPE;
+    const int32_t R = iargs->R;
+    if (R == 0) return LISFA_OK;
+    if (!out) return LISFA_ERR_NULL_ARG;
+    if (!aligned(out, 8)) return LISFA_ERR_BAD_SHAPE;
+    const FusedLayout L = fused_layout(R, iargs->max_visible, K, margs->H, margs->D_latent);
+    if (!ws || ws_bytes < L.total) return LISFA_ERR_WORKSPACE;
+    if (!aligned(ws, 256)) return LISFA_ERR_BAD_SHAPE;
+    hipStream_t st = (hipStream_t)stream;
+    uint8_t* w = (uint8_t*)ws;
+    float* scores = (float*)(w + L.scores);
+    int32_t* idx = idx_out ? idx_out : (int32_t*)(w + L.idx);
+    void* sfa_ws = w + L.sfa;
+
+    const int64_t ld = scores_ld(iargs->max_visible) > 0 ? scores_ld(iargs->max_visible) : 64;
+    const int64_t rc = fused_chunk_rows(R, iargs->max_visible);
+    const int qg = (iargs->rows_per_group % 8 == 0) ? 8 : 1;
+    const int elt = iargs->k_cache.dtype == LISFA_FP8_E4M3 ? 1 : 2;
+    IndexerDev d = to_dev(iargs);
+    for (int64_t c0 = 0; c0 < R; c0 += rc) {
+        const int64_t c1 = c0 + rc < R ? c0 + rc : R;
+        IndexerDev dc = d;
+        dc.R = (int32_t)(c1 - c0);
+        dc.q = d.q + c0 * (int64_t)iargs->H_I * iargs->D_I * elt;
+        dc.w = d.w + c0 * iargs->H_I;
+        if (d.q_scale) dc.q_scale = d.q_scale + c0 * (iargs->q_scale_per_head ? iargs->H_I : 1);
+        dc.row_seq = d.row_seq + c0;
+        dc.row_pos = d.row_pos + c0;
+        if (iargs->max_visible > 0) {
+            hipError_t he = li_score_dispatch(dc, iargs->D_I, elt == 1, qg, scores, ld, iargs->max_visible, st);
+            if (he != hipSuccess) return LISFA_ERR_HIP;
+        }
+        hipError_t he = topk_dispatch(scores, ld, dc.row_pos, dc.R, K, idx + c0 * K, st);
+        if (he != hipSuccess) return LISFA_ERR_HIP;
+    }
+    const MlaDev md = to_dev(margs, idx, K);
+    return hip_status(sfa_dispatch(md, margs->D_latent, margs->kv_cache.dtype == LISFA_FP8_E4M3, (__bf16*)out,
+                                   lse, sfa_ws, st));
+}
+
+}  // extern "C"

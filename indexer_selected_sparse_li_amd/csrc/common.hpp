@@ -1,0 +1,127 @@
+// Device-side helpers shared by the lisfa kernels (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "lisfa.h"
+
+namespace lisfa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Kernel-side view of a cache (passed by value).
+struct CacheDev {
+    const uint8_t* data;
+    int64_t num_slots;
+    const float* scale;
+    const int32_t* block_table;
+    const int64_t* seq_base;
+    int32_t row_stride;      // bytes
+    int32_t scale_group;     // fp8 scale group (slots)
+    int32_t bs_shift;        // log2(block_size) (paged)
+    int32_t bt_stride;
+    int32_t num_seqs;
+    int32_t paged;
+};
+
+struct IndexerDev {
+    const uint8_t* q;
+    const float* q_scale;
+    const float* w;
+    const int32_t* row_seq;
+    const int32_t* row_pos;
+    CacheDev k;
+    int32_t q_scale_per_head;
+    int32_t R;
+    int32_t H_I;
+};
+
+struct MlaDev {
+    const uint8_t* q;        // bf16 [R, H, DQK]
+    const int32_t* row_seq;
+    const int32_t* idx;      // [R, K]
+    CacheDev kv;
+    int32_t R, H, K;
+    float scale_log2;        // softmax_scale * log2(e)
+};
+
+// Physical slot of (sequence, logical position), or -1 when the position is
+// outside what the block table / pool can address.
+__device__ __forceinline__ int64_t slot_of(const CacheDev& c, int seq, int64_t pos) {
+    if (seq < 0 || seq >= c.num_seqs || pos < 0) return -1;
+    int64_t s;
+    if (c.paged) {
+        int64_t blk = pos >> c.bs_shift;
+        if (blk >= c.bt_stride) return -1;
+        int32_t b = c.block_table[(int64_t)seq * c.bt_stride + blk];
+        if (b < 0) return -1;
+        s = ((int64_t)b << c.bs_shift) + (pos & ((1 << c.bs_shift) - 1));
+    } else {
+        s = c.seq_base[seq] + pos;
+    }
+    return (s >= 0 && s < c.num_slots) ? s : -1;
+}
+
+// Order-preserving map fp32 -> uint32 (-0.0 is folded onto +0.0).
+__device__ __forceinline__ uint32_t float_key(float f) {
+    uint32_t b = __float_as_uint(f);
+    if (b == 0x80000000u) b = 0u;
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// Exact e4m3 (OCP) pair -> fp32 pair via the hardware converter.
+template <bool HI>
+__device__ __forceinline__ f32x2 fp8x2_to_f32(uint32_t word) {
+    return __builtin_amdgcn_cvt_pk_f32_fp8((int)word, HI);
+}
+
+// fp32 whose low 16 bits are zero -> bf16 bits (exact truncation).
+__device__ __forceinline__ uint32_t pack_hi16(float lo, float hi) {
+    return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+}
+
+// 8 e4m3 codes (two dwords) -> 8 bf16 (exact: every e4m3 value is a bf16 value).
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(u32x2 v) {
+    f32x2 a = fp8x2_to_f32<false>(v.x), b = fp8x2_to_f32<true>(v.x);
+    f32x2 c = fp8x2_to_f32<false>(v.y), d = fp8x2_to_f32<true>(v.y);
+    u32x4 r;
+    r.x = pack_hi16(a.x, a.y);
+    r.y = pack_hi16(b.x, b.y);
+    r.z = pack_hi16(c.x, c.y);
+    r.w = pack_hi16(d.x, d.y);
+    return __builtin_bit_cast(bf16x8, r);
+}
+
+__device__ __forceinline__ f32x16 mfma32x32x16_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma32x32x16_fp8(int64_t a, int64_t b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t lanemask_count(uint64_t mask) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+}  // namespace lisfa

@@ -1,0 +1,175 @@
+"""CPU checks of the C ABI: the library loads, exports every function that
+include/lisfa.h declares, agrees with the binding on struct layouts, and
+rejects bad arguments before touching the GPU."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import indexer_selected_sparse_li_amd as lisfa
+from indexer_selected_sparse_li_amd import _lib as C
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lisfa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while")))
+
+
+@pytest.fixture(scope="module")
+def clib():
+    return C.load()
+
+
+def test_header_declares_the_four_layer_entry_points():
+    names = declared_functions()
+    for n in ("li_score", "topk_select", "sparse_mla_attn", "li_topk_sfa"):
+        assert n in names
+    assert set(names) == set(C.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(clib):
+    out = subprocess.run(["nm", "-D", "--defined-only", C.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if " T " in l)
+    for n in declared_functions():
+        assert n in exported, n
+        assert hasattr(clib, n)
+
+
+def test_struct_layouts_match(clib):
+    assert clib.lisfa_struct_size(0) == ctypes.sizeof(C.Cache)
+    assert clib.lisfa_struct_size(1) == ctypes.sizeof(C.IndexerArgs)
+    assert clib.lisfa_struct_size(2) == ctypes.sizeof(C.MlaArgs)
+    assert clib.lisfa_abi_version() == 1
+
+
+def test_status_strings(clib):
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        s = clib.lisfa_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert clib.lisfa_status_string(42).decode() == "unknown status"
+
+
+def test_workspace_sizes(clib):
+    assert clib.lisfa_workspace_size(C.LISFA_OP_TOPK, 64, 32768, 2048, 128, 512) == 0
+    sfa = clib.lisfa_workspace_size(C.LISFA_OP_SPARSE_MLA, 64, 0, 2048, 128, 512)
+    fused = clib.lisfa_workspace_size(C.LISFA_OP_FUSED, 64, 32768, 2048, 128, 512)
+    assert fused >= sfa + 64 * 32768 * 4 + 64 * 2048 * 4
+    # many rows: one row alone needs no split, so no partial buffers
+    assert clib.lisfa_workspace_size(C.LISFA_OP_SPARSE_MLA, 4096, 0, 2048, 128, 512) == 0
+    # bounded score scratch for long prefill
+    big = clib.lisfa_workspace_size(C.LISFA_OP_FUSED, 4096, 65536, 2048, 128, 512)
+    assert big < (300 << 20) + 4096 * 2048 * 4
+    assert clib.lisfa_workspace_size(C.LISFA_OP_FUSED, 4, 100, 0, 8, 64) == 0
+
+
+def _fake_cache(**kw):
+    c = C.Cache(data=16, num_slots=100, dtype=C.LISFA_BF16, row_stride_bytes=256, scale=None,
+                scale_group_tokens=1, block_size=64, block_table=None, bt_stride=0, num_seqs=1,
+                seq_base_slot=16)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def _idx_args(**kw):
+    a = C.IndexerArgs(q=16, q_scale=None, q_scale_per_head=0, w=16, k_cache=_fake_cache(), row_seq=16,
+                      row_pos=16, R=1, H_I=64, D_I=128, rows_per_group=1, max_visible=100)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def _mla_args(**kw):
+    a = C.MlaArgs(q=16, kv_cache=_fake_cache(row_stride_bytes=1152), row_seq=16, R=1, H=128,
+                  D_latent=512, D_rope=64, softmax_scale=0.04)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), C.LISFA_ERR_NULL_ARG),
+    (dict(w=None), C.LISFA_ERR_NULL_ARG),
+    (dict(H_I=65), C.LISFA_ERR_UNSUPPORTED),
+    (dict(D_I=64), C.LISFA_ERR_UNSUPPORTED),
+    (dict(R=-1), C.LISFA_ERR_BAD_SHAPE),
+    (dict(rows_per_group=0), C.LISFA_ERR_BAD_SHAPE),
+    (dict(k_cache=_fake_cache(dtype=7)), C.LISFA_ERR_BAD_DTYPE),
+    (dict(k_cache=_fake_cache(row_stride_bytes=200)), C.LISFA_ERR_BAD_SHAPE),
+    (dict(k_cache=_fake_cache(row_stride_bytes=264)), C.LISFA_ERR_BAD_SHAPE),
+    (dict(k_cache=_fake_cache(dtype=C.LISFA_FP8_E4M3)), C.LISFA_ERR_NULL_ARG),
+    (dict(k_cache=_fake_cache(seq_base_slot=None)), C.LISFA_ERR_NULL_ARG),
+    (dict(k_cache=_fake_cache(block_table=16, block_size=48, bt_stride=4)), C.LISFA_ERR_BAD_SHAPE),
+    (dict(q=18), C.LISFA_ERR_BAD_SHAPE),
+])
+def test_li_score_validation(clib, kw, code):
+    a = _idx_args(**kw)
+    assert clib.li_score(ctypes.byref(a), 16, 128, None) == code
+
+
+def test_li_score_rejects_short_ld(clib):
+    a = _idx_args()
+    assert clib.li_score(ctypes.byref(a), 16, 99, None) == C.LISFA_ERR_BAD_SHAPE
+    assert clib.li_score(ctypes.byref(a), None, 128, None) == C.LISFA_ERR_NULL_ARG
+    assert clib.li_score(None, 16, 128, None) == C.LISFA_ERR_NULL_ARG
+
+
+def test_empty_calls_are_no_ops(clib):
+    a = _idx_args(R=0, q=None, w=None)
+    assert clib.li_score(ctypes.byref(a), None, 0, None) == C.LISFA_OK
+    assert clib.topk_select(None, 10, None, 0, 4, None, None, 0, None) == C.LISFA_OK
+    m = _mla_args(R=0, q=None)
+    assert clib.sparse_mla_attn(ctypes.byref(m), None, 4, None, None, None, 0, None) == C.LISFA_OK
+
+
+def test_topk_validation(clib):
+    assert clib.topk_select(16, 10, 16, 1, 0, 16, None, 0, None) == C.LISFA_ERR_BAD_SHAPE
+    assert clib.topk_select(16, 0, 16, 1, 4, 16, None, 0, None) == C.LISFA_ERR_BAD_SHAPE
+    assert clib.topk_select(None, 10, 16, 1, 4, 16, None, 0, None) == C.LISFA_ERR_NULL_ARG
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H=129), C.LISFA_ERR_UNSUPPORTED),
+    (dict(D_latent=256), C.LISFA_ERR_UNSUPPORTED),
+    (dict(D_rope=32), C.LISFA_ERR_UNSUPPORTED),
+    (dict(q=None), C.LISFA_ERR_NULL_ARG),
+    (dict(kv_cache=_fake_cache(row_stride_bytes=1024)), C.LISFA_ERR_BAD_SHAPE),
+    (dict(softmax_scale=float("nan")), C.LISFA_ERR_BAD_SHAPE),
+])
+def test_sparse_mla_validation(clib, kw, code):
+    m = _mla_args(**kw)
+    assert clib.sparse_mla_attn(ctypes.byref(m), 16, 2048, 16, None, 16, 1 << 30, None) == code
+
+
+def test_sparse_mla_workspace_checked(clib):
+    m = _mla_args(R=4)
+    need = clib.lisfa_workspace_size(C.LISFA_OP_SPARSE_MLA, 4, 0, 2048, 128, 512)
+    assert need > 0
+    assert clib.sparse_mla_attn(ctypes.byref(m), 16, 2048, 16, None, 16, need - 1, None) == C.LISFA_ERR_WORKSPACE
+    assert clib.sparse_mla_attn(ctypes.byref(m), 16, 2048, 16, None, None, need, None) == C.LISFA_ERR_WORKSPACE
+
+
+def test_fused_validation(clib):
+    a, m = _idx_args(R=2), _mla_args(R=3)
+    assert clib.li_topk_sfa(ctypes.byref(a), ctypes.byref(m), 2048, None, 16, None, 256, 1 << 40,
+                            None) == C.LISFA_ERR_BAD_SHAPE
+    m = _mla_args(R=2)
+    need = clib.lisfa_workspace_size(C.LISFA_OP_FUSED, 2, 100, 2048, 128, 512)
+    assert clib.li_topk_sfa(ctypes.byref(a), ctypes.byref(m), 2048, None, 16, None, 256, need - 1,
+                            None) == C.LISFA_ERR_WORKSPACE
+    assert clib.li_topk_sfa(ctypes.byref(a), ctypes.byref(m), 0, None, 16, None, 256, need,
+                            None) == C.LISFA_ERR_BAD_SHAPE
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        lisfa.KVCache(data=torch.zeros(4, 128, dtype=torch.bfloat16),
+                      seq_base=torch.zeros(1, dtype=torch.int64)).c_struct()
