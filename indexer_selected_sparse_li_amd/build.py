@@ -25,13 +25,19 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-munsafe-fp-atomics", "-Wno-unused-result",
-    f"-I{INCLUDE}", f"-I{CSRC}",
+    f"-I{INCLUDE}", f"-I{CSRC}", *os.environ.get("LISFA_EXTRA_FLAGS", "").split(),
 ]
+# Per-source flags.  sparse_mla: keep MFMA accumulators in architectural VGPRs
+# (the online-softmax rescale touches them with VALU instructions; AGPR
+# accumulators would be copied back and forth every tile).
+FILE_FLAGS = {
+    "sparse_mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{res.stderr}")

@@ -41,8 +41,14 @@ __device__ __attribute__((aligned(16))) uint8_t g_zero16[64];
 
 constexpr int kSfaMaxKeys = 2048;  // index entries one workgroup handles
 
+// XOR swizzle of the 16-byte chunks of LDS row r (values < 8, so a chunk stays
+// inside its aligned group of 8).  With it, 16 consecutive rows read at one
+// chunk (QK operand) hit 16 distinct bank groups, and the transpose reads of
+// the PV operand (8 consecutive rows x 4 chunks) are at the 2-way minimum.
+__device__ __forceinline__ int sfa_swz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
+
 template <int DLAT, int DROPE, bool FP8, int NHG>
-__global__ __launch_bounds__(128 * NHG) void sfa_kernel(MlaDev a, int kps, int nsplit,
+__global__ __launch_bounds__(128 * NHG) void sfa_kernel(MlaDev a, int kps, int nsplit, int nhb,
                                                         __bf16* __restrict__ out, float* __restrict__ lse,
                                                         float* __restrict__ part_o,
                                                         float* __restrict__ part_lse) {
@@ -50,37 +56,45 @@ __global__ __launch_bounds__(128 * NHG) void sfa_kernel(MlaDev a, int kps, int n
     constexpr int ELT = FP8 ? 1 : 2;
     constexpr int RB = DQK * ELT;           // bytes per cached row
     constexpr int CPK = RB / 16;            // 16-byte chunks per row
-    constexpr int CPKP = CPK + 1;           // + 1 pad chunk (bank spread)
+    // bf16 rows whose chunk count is a multiple of 8: swizzled, unpadded rows
+    // and transpose reads (ds_read_b64_tr_b16) for the value operand.
+    // Otherwise: one pad chunk per row and gathered value reads.
+    constexpr bool SWZ = !FP8 && (CPK % 8 == 0);
+    constexpr int CPKP = SWZ ? CPK : CPK + 1;
     constexpr int RBP = CPKP * 16;          // LDS row stride
     constexpr int TROWS = 32;               // rows per tile
-    constexpr int TCH = TROWS * CPKP;       // chunks per tile (with pads)
+    constexpr int NBUF = 3;                 // tile ring: PV(t) | QK(t+1) | loading t+2
+    constexpr int TCH = TROWS * CPKP;       // chunk positions per tile
     constexpr int NT = 128 * NHG;           // threads
     constexpr int NLD = (TCH + NT - 1) / NT;
     constexpr int KS = DQK / 16;            // QK K-steps
     constexpr int KS0 = (KS + 1) / 2;       // K-steps of the dh = 0 wave
     constexpr int DVH = DLAT / 2;           // value columns per wave
     constexpr int MTV = DVH / 32;           // PV M-tiles per wave
+    constexpr bool ILV = !SWZ && (MTV % 4 == 0);  // interleaved value columns (gathered path)
     static_assert(DQK % 16 == 0 && DVH % 32 == 0, "shape");
 
-    __shared__ __attribute__((aligned(16))) uint8_t tile[2][TROWS * RBP];
-    __shared__ int64_t slots[kSfaMaxKeys];
-    __shared__ float kvs[FP8 ? kSfaMaxKeys : 1];
-    __shared__ __attribute__((aligned(16))) float xbuf[NHG * 2 * 64 * 16];
+    __shared__ __attribute__((aligned(16))) uint8_t tile[NBUF][TROWS * RBP];
+    __shared__ int64_t roff[kSfaMaxKeys];              // byte offset of each selected row, -1 = skip
+    __shared__ float kvs[FP8 ? kSfaMaxKeys : 1];        // fp8 row factor (0 for skipped rows)
+    __shared__ uint32_t vmask[kSfaMaxKeys / 32];        // valid-row bits of each 32-row tile
+    __shared__ __attribute__((aligned(16))) float xbuf[2][NHG * 2 * 4 * 64 * 4];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int hg = wave >> 1, dh = wave & 1;
-    const int sp = blockIdx.x, hb = blockIdx.y, r = blockIdx.z;
+    // 1-D grid, XCD-aware: workgroups are dealt round-robin to the 8 XCDs, so
+    // the nhb head blocks of one (row, split) get ids 8 apart and share the
+    // XCD's L2 (and run at about the same time).
+    const int bid = blockIdx.x;
+    const int hb = (bid >> 3) % nhb;
+    const int u = ((bid >> 3) / nhb) * 8 + (bid & 7);
+    if (u >= a.R * nsplit) return;
+    const int r = u / nsplit, sp = u % nsplit;
     const int k0 = sp * kps;
     const int k1 = (k0 + kps < a.K) ? k0 + kps : a.K;
     const int nk = k1 - k0;
     const int seq = a.row_seq[r];
-
-    for (int i = tid; i < nk; i += NT) {
-        const int p = a.idx[(int64_t)r * a.K + k0 + i];
-        const int64_t s = p >= 0 ? slot_of(a.kv, seq, p) : -1;
-        slots[i] = s;
-        if constexpr (FP8) kvs[i] = s >= 0 ? a.kv.scale[s / a.kv.scale_group] : 0.f;
-    }
+    const int ntiles = (nk + TROWS - 1) / TROWS;
 
     // query half of this wave in B-operand layout (col = head, 8 consecutive d)
     const int head = hb * 32 * NHG + hg * 32 + (lane & 31);
@@ -94,23 +108,112 @@ __global__ __launch_bounds__(128 * NHG) void sfa_kernel(MlaDev a, int kps, int n
         else
             qb[j] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
     }
-    __syncthreads();  // slots ready
 
-    const int ntiles = (nk + TROWS - 1) / TROWS;
+    // selected rows -> byte offsets, and one validity bit per row via ballots
+    for (int i0 = 0; i0 < ntiles * TROWS; i0 += NT) {
+        const int i = i0 + tid;
+        int64_t s = -1;
+        if (i < nk) {
+            const int p = a.idx[(int64_t)r * a.K + k0 + i];
+            s = p >= 0 ? slot_of(a.kv, seq, p) : -1;
+        }
+        if (i < ntiles * TROWS) {
+            roff[i] = s >= 0 ? s * a.kv.row_stride : -1;
+            if constexpr (FP8) kvs[i] = s >= 0 ? a.kv.scale[s / a.kv.scale_group] : 0.f;
+        }
+        const uint64_t bal = __ballot(s >= 0);
+        if (lane == 0 && i < ntiles * TROWS) {
+            vmask[i / 32] = (uint32_t)bal;
+            if (i + 32 < ntiles * TROWS) vmask[i / 32 + 1] = (uint32_t)(bal >> 32);
+        }
+    }
+    __syncthreads();
+
+    // per-lane constants of the LDS addressing
+    const int krow = lane & 31;                 // QK: cached row = key of this lane
+    const int kswz = SWZ ? sfa_swz(krow) : 0;
+    const int g16 = lane >> 4, i16 = lane & 15; // PV transpose reads: 16-lane group, lane in group
+    const int trow = 4 * (g16 >> 1) + (i16 >> 2);          // + 16 kk + 8 j
+    const int tcol = 16 * (g16 & 1) + 4 * (i16 & 3);       // + value column base
+    // transpose-read byte offsets of rows 8 j + trow at value column
+    // dh * DVH + tcol + 32 (mt % 2); other (kk, mt) add immediates
+    uint32_t pvb[2][2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int par = 0; par < 2; ++par) {
+            const int rr = 8 * j + trow;
+            const int byte = (dh * DVH + tcol + 32 * par) * 2;
+            pvb[j][par] = (uint32_t)(rr * RBP + (((byte >> 4) ^ (SWZ ? sfa_swz(rr) : 0)) << 4) + (byte & 15));
+        }
+
+    // tile loads: chunk position P = j * NT + tid of the tile (row P / CPKP,
+    // position P % CPKP) receives global chunk (position ^ swizzle(row)) of
+    // that row; row offsets come from roff.  The LDS destination of a wave's
+    // instruction is contiguous (lane * 16 bytes from a wave-uniform base).
     auto issue_tile = [&](int t, int buf) {
+        const uint32_t lds0 = (uint32_t)(uintptr_t)(tile[buf]) + (uint32_t)((tid & ~63) * 16);
 #pragma unroll
         for (int j = 0; j < NLD; ++j) {
-            const int P = j * NT + tid;          // chunk position in the tile
-            if (P < TCH) {
-                const int row = P / CPKP, part = P % CPKP;
-                const int kk = t * TROWS + row;
-                const int64_t s = kk < nk ? slots[kk] : -1;
-                const uint8_t* g = (s >= 0 && part < CPK) ? a.kv.data + s * a.kv.row_stride + part * 16
-                                                          : g_zero16;
+            const int P = j * NT + tid;           // chunk position in the tile
+            if (TCH % NT == 0 || P < TCH) {
+                const int row = P / CPKP, pos = P - row * CPKP;
+                const int part = SWZ ? (pos ^ sfa_swz(row)) : pos;
+                const int64_t off = roff[t * TROWS + row];
+                const uint8_t* g = (off >= 0 && part < CPK) ? a.kv.data + off + part * 16 : g_zero16;
+                const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(j * NT * 16));
                 __builtin_amdgcn_global_load_lds(
-                    g, (__attribute__((address_space(3))) void*)(tile[buf] + (j * NT + wave * 64) * 16), 16, 0, 0);
+                    g, (__attribute__((address_space(3))) void*)(uintptr_t)dst, 16, 0, 0);
             }
         }
+    };
+
+    // partial S^T[32 keys x 32 heads] over this wave's K-steps of tile buffer T.
+    // The K-steps of each half are compile-time constants, so every operand
+    // read is one of four per-lane base addresses plus an immediate offset
+    // (the swizzle only permutes chunks inside aligned groups of 8).
+    uint32_t qkb[4];                              // SWZ: byte offset of chunk (8q + 2m + h) ^ swz
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+        qkb[m] = (uint32_t)(krow * RBP + ((((2 * m) + (lane >> 5)) ^ kswz) << 4));
+    auto qk_half = [&](const lds_u8* T, auto ksb_c) {
+        constexpr int KSB = decltype(ksb_c)::value;
+        constexpr int NKS = KSB == 0 ? KS0 : KS - KS0;
+        auto operand = [&](int ks) -> bf16x8 {
+            if constexpr (FP8) {
+                return fp8x8_to_bf16x8(*(const lds_u32x2*)(T + krow * RBP + ks * 16 + (lane >> 5) * 8));
+            } else if constexpr (SWZ) {
+                // chunk 2 ks + h = 8 (ks / 4) + 2 (ks % 4) + h
+                return *(const lds_bf16x8*)(T + qkb[ks & 3] + 128 * (ks >> 2));
+            } else {
+                return *(const lds_bf16x8*)(T + krow * RBP + (2 * ks + (lane >> 5)) * 16);
+            }
+        };
+        constexpr int PF = 3;  // operands in flight ahead of the MFMA that uses them
+        f32x16 s;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[i] = 0.f;
+        bf16x8 buf[PF];
+#pragma unroll
+        for (int j = 0; j < PF && j < NKS; ++j) buf[j] = operand(KSB + j);
+#pragma unroll
+        for (int j = 0; j < NKS; ++j) {
+            const bf16x8 av = buf[j % PF];
+            if (j + PF < NKS) buf[j % PF] = operand(KSB + j + PF);
+            s = mfma32x32x16_bf16(av, qb[j], s);
+        }
+        return s;
+    };
+    auto qk = [&](const lds_u8* T) {
+        if (dh == 0) return qk_half(T, std::integral_constant<int, 0>{});
+        return qk_half(T, std::integral_constant<int, KS0>{});
+    };
+    // the two waves of a pair exchange partial logits through LDS;
+    // layout [pair][i/4][lane][4]: consecutive lanes write consecutive 16 bytes
+    auto put_partial = [&](const f32x16& s, int xb) {
+        float* xs = xbuf[xb] + (hg * 2 + dh) * 1024 + lane * 4;
+#pragma unroll
+        for (int i = 0; i < 16; i += 4) *(f32x4*)(xs + i * 64) = f32x4{s[i], s[i + 1], s[i + 2], s[i + 3]};
     };
 
     f32x16 o[MTV];
@@ -119,136 +222,270 @@ __global__ __launch_bounds__(128 * NHG) void sfa_kernel(MlaDev a, int kps, int n
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[mt][i] = 0.f;
     float m2 = -__builtin_inff(), lsum = 0.f;
+    f32x16 s_cur;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s_cur[i] = 0.f;
 
     if (ntiles > 0) issue_tile(0, 0);
-    for (int t = 0; t < ntiles; ++t) {
-        const int buf = t & 1;
+    if (ntiles > 1) issue_tile(1, 1);
+    if (ntiles > 0) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (t + 1 < ntiles) issue_tile(t + 1, buf ^ 1);
-        const uint8_t* T = tile[buf];
-
-        // QK^T partial over this wave's K-steps: A = cached rows (key = lane%32)
-        f32x16 s;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[i] = 0.f;
-        const uint8_t* arow = T + (lane & 31) * RBP;
-#pragma unroll
-        for (int j = 0; j < KS0; ++j) {
-            if (j < nks) {
-                const int ks = ksb + j;
-                bf16x8 av;
-                if constexpr (FP8) av = fp8x8_to_bf16x8(*(const u32x2*)(arow + ks * 16 + (lane >> 5) * 8));
-                else av = *(const bf16x8*)(arow + (ks * 16 + (lane >> 5) * 8) * 2);
-                s = mfma32x32x16_bf16(av, qb[j], s);
-            }
-        }
-        // sum the two halves' partial logits through LDS
-        float* xs = xbuf + ((hg * 2 + dh) * 64 + lane) * 16;
-#pragma unroll
-        for (int i = 0; i < 16; i += 4) *(f32x4*)(xs + i) = f32x4{s[i], s[i + 1], s[i + 2], s[i + 3]};
-        __syncthreads();
-        const float* xp = xbuf + ((hg * 2 + (dh ^ 1)) * 64 + lane) * 16;
-#pragma unroll
-        for (int i = 0; i < 16; i += 4) {
-            const f32x4 v = *(const f32x4*)(xp + i);
-            s[i] += v.x;
-            s[i + 1] += v.y;
-            s[i + 2] += v.z;
-            s[i + 3] += v.w;
-        }
-
-        // logits (base 2), masking, online softmax -- in place on s
-        float tmax = -__builtin_inff();
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int kk = t * TROWS + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-            const bool valid = kk < nk && slots[kk] >= 0;
-            float f = a.scale_log2;
-            if constexpr (FP8) f *= valid ? kvs[kk] : 0.f;
-            s[i] = valid ? s[i] * f : -__builtin_inff();
-            tmax = fmaxf(tmax, s[i]);
-        }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float mnew = fmaxf(m2, tmax);
-        if (mnew == -__builtin_inff()) continue;  // nothing valid yet (same in both waves)
-        const float alpha = exp2f(m2 - mnew);     // m2 = -inf -> 0
-        float rs = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            s[i] = exp2f(s[i] - mnew);
-            rs += s[i];
-        }
-        rs += __shfl_xor(rs, 32);
-        lsum = lsum * alpha + rs;
-        m2 = mnew;
-#pragma unroll
-        for (int mt = 0; mt < MTV; ++mt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) o[mt][i] *= alpha;
-        bf16x8 pb[2];
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float p = s[8 * kk + e];
-                if constexpr (FP8) {
-                    const int key = t * TROWS + 8 * (2 * kk + (e >> 2)) + 4 * (lane >> 5) + (e & 3);
-                    p = key < nk ? p * kvs[key] : 0.f;
-                }
-                pb[kk][e] = (__bf16)p;
-            }
-
-        // PV: A = V^T (row = value column lane%32, 8 keys of the K-step)
-#pragma unroll
-        for (int mt = 0; mt < MTV; ++mt) {
-            const int col = dh * DVH + mt * 32 + (lane & 31);
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                bf16x8 av;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int key = 16 * kk + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                    if constexpr (FP8) {
-                        const uint32_t code = T[key * RBP + col];
-                        const f32x2 f = fp8x2_to_f32<false>(code);
-                        av[e] = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(f.x) >> 16));
-                    } else {
-                        av[e] = *(const __bf16*)(T + key * RBP + col * 2);
-                    }
-                }
-                o[mt] = mfma32x32x16_bf16(av, pb[kk], o[mt]);
-            }
-        }
+        s_cur = qk((const lds_u8*)tile[0]);
+        put_partial(s_cur, 0);
     }
 
-    // epilogue: normalise and store (O^T layout: lane = head, 4 runs of 4 columns)
+    const lds_u8* tile0 = (const lds_u8*)tile[0];
+    int bcur = 0;                               // ring index of tile t
+    for (int t = 0; t < ntiles; ++t) {
+        const int bnext = bcur == NBUF - 1 ? 0 : bcur + 1;
+        const int bnext2 = bnext == NBUF - 1 ? 0 : bnext + 1;
+        // tile t+1 landed; everyone is done with tile t-1 (its buffer is free)
+        // and has published the partial logits of tile t
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (t + 2 < ntiles) issue_tile(t + 2, bnext2);
+        const lds_u8* T = tile0 + bcur * (TROWS * RBP);
+        const uint32_t vm = vmask[t];
+
+        // full logits of tile t = own partial + partner's partial
+        f32x16 s = s_cur;
+        {
+            const float* xp = xbuf[t & 1] + (hg * 2 + (dh ^ 1)) * 1024 + lane * 4;
+#pragma unroll
+            for (int i = 0; i < 16; i += 4) {
+                const f32x4 v = *(const f32x4*)(xp + i * 64);
+                s[i] += v.x;
+                s[i + 1] += v.y;
+                s[i + 2] += v.z;
+                s[i + 3] += v.w;
+            }
+        }
+        bf16x8 pb[2];
+        {
+            // logits (base 2), masking, online softmax in place on s.  The
+            // reference maximum m2 of a head is raised only when a tile's maximum
+            // exceeds it by more than kLazy (log2 units); otherwise probabilities
+            // are formed against the stale maximum (at most 2^kLazy) and the
+            // accumulator is not rescaled.  Same softmax; only rounding differs.
+            constexpr float kLazy = 8.0f;
+            float tmax = -__builtin_inff();
+            if constexpr (FP8) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int key = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+                    const float f = a.scale_log2 * kvs[t * TROWS + key];
+                    s[i] = ((vm >> key) & 1u) ? s[i] * f : -__builtin_inff();
+                    tmax = fmaxf(tmax, s[i]);
+                }
+            } else if (vm == 0xFFFFFFFFu) {     // every row of the tile selected (common case)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    s[i] *= a.scale_log2;
+                    tmax = fmaxf(tmax, s[i]);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int key = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+                    s[i] = ((vm >> key) & 1u) ? s[i] * a.scale_log2 : -__builtin_inff();
+                    tmax = fmaxf(tmax, s[i]);
+                }
+            }
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            const bool raise = tmax > m2 + kLazy;   // also true on the first valid tile
+            if (__ballot(raise) != 0ull) {
+                const float mnew = raise ? tmax : m2;
+                const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);  // m2 = -inf -> 0
+                lsum *= alpha;
+#pragma unroll
+                for (int mt = 0; mt < MTV; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) o[mt][i] *= alpha;
+                m2 = mnew;
+            }
+            // a head with no valid row so far keeps m2 = -inf; its probabilities
+            // (all of masked rows) must come out 0, not NaN
+            const float mref = m2 == -__builtin_inff() ? 0.f : m2;
+            float rs = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                s[i] = __builtin_amdgcn_exp2f(s[i] - mref);
+                rs += s[i];
+            }
+            rs += __shfl_xor(rs, 32);
+            lsum += rs;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float p = s[8 * kk + e];
+                    if constexpr (FP8) p *= kvs[t * TROWS + 8 * (2 * kk + (e >> 2)) + 4 * (lane >> 5) + (e & 3)];
+                    pb[kk][e] = (__bf16)p;
+                }
+        }
+        // QK^T of the next tile: independent of this tile's PV, so the two MFMA
+        // streams interleave (same basic block, no branch in between)
+        if (t + 1 < ntiles) s_cur = qk(tile0 + bnext * (TROWS * RBP));
+        {
+
+            // PV: O^T[32 value columns x 32 heads] += V^T[32 x 16 keys] * P^T.
+            // Keys of K-step kk for lane half h are 16 kk + 4 h + {0..3} (operand
+            // elements 0..3) and 16 kk + 8 + 4 h + {0..3} (elements 4..7), the
+            // same keys the S^T accumulator registers 8 kk .. 8 kk + 7 hold.
+            if constexpr (SWZ) {
+                // Two transpose reads per operand: the 16 lanes of group g16 read
+                // rows 16 kk + 8 j + 4 (g16 / 2) + i16 / 4 at columns
+                // base + 16 (g16 % 2) + 4 (i16 % 4); lane l then holds column
+                // base + l % 32 of four consecutive keys.
+                typedef short s16x4 __attribute__((ext_vector_type(4)));
+                typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+                // row 16 kk + 8 j + trow; chunk (4 (mt % 2) + c0) ^ swz + 8 (mt / 2)
+                auto trd = [&](int mt, int kk, int j) -> s16x4 {
+                    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_s16x4*)(T + pvb[j][mt & 1] + 16 * kk * RBP + 128 * (mt >> 1)));
+                };
+                s16x4 cur[4], nxt[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) cur[q] = trd(0, q >> 1, q & 1);
+#pragma unroll
+                for (int mt = 0; mt < MTV; ++mt) {
+                    if (mt + 1 < MTV) {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) nxt[q] = trd(mt + 1, q >> 1, q & 1);
+                    }
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk) {
+                        const u32x2 lo = __builtin_bit_cast(u32x2, cur[2 * kk]);
+                        const u32x2 hi = __builtin_bit_cast(u32x2, cur[2 * kk + 1]);
+                        const u32x4 w = {lo.x, lo.y, hi.x, hi.y};
+                        o[mt] = mfma32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pb[kk], o[mt]);
+                    }
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) cur[q] = nxt[q];
+                }
+            } else if constexpr (ILV) {
+                // Interleaved columns over groups of 4 M-tiles: in group g, M-tile
+                // j holds columns base + 128 g + 4 c + j (c = lane % 32); one read
+                // of 4 consecutive columns per key feeds all 4 M-tiles after a
+                // 16-bit transpose with v_perm.
+#pragma unroll
+                for (int g = 0; g < MTV / 4; ++g) {
+                    const int col = dh * DVH + 128 * g + 4 * (lane & 31);
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk) {
+                        u32x2 x[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const int key = 16 * kk + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                            if constexpr (FP8) {
+                                const uint32_t c4 = *(const lds_u32*)(T + key * RBP + col);
+                                const f32x2 f0 = fp8x2_to_f32<false>(c4), f1 = fp8x2_to_f32<true>(c4);
+                                x[e] = u32x2{pack_hi16(f0.x, f0.y), pack_hi16(f1.x, f1.y)};
+                            } else {
+                                x[e] = *(const lds_u32x2*)(T + key * RBP + col * 2);
+                            }
+                        }
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            u32x4 w;
+                            const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+                            for (int m = 0; m < 4; ++m) {
+                                const uint32_t a0 = (j < 2) ? x[2 * m].x : x[2 * m].y;
+                                const uint32_t a1 = (j < 2) ? x[2 * m + 1].x : x[2 * m + 1].y;
+                                w[m] = __builtin_amdgcn_perm(a1, a0, sel);
+                            }
+                            o[4 * g + j] = mfma32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pb[kk], o[4 * g + j]);
+                        }
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int mt = 0; mt < MTV; ++mt) {
+                    const int col = dh * DVH + mt * 32 + (lane & 31);
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk) {
+                        bf16x8 av;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const int key = 16 * kk + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                            if constexpr (FP8) {
+                                const uint32_t code = T[key * RBP + col];
+                                const f32x2 f = fp8x2_to_f32<false>(code);
+                                av[e] = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(f.x) >> 16));
+                            } else {
+                                av[e] = *(const lds_bf16*)(T + key * RBP + col * 2);
+                            }
+                        }
+                        o[mt] = mfma32x32x16_bf16(av, pb[kk], o[mt]);
+                    }
+                }
+            }
+        }
+        if constexpr (SWZ) {
+            // interleave the QK^T(t+1) and PV(t) streams: operand reads run ahead
+            // of the MFMAs that consume them
+#pragma unroll
+            for (int i = 0; i < KS0 + 2 * MTV; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            }
+        }
+        if (t + 1 < ntiles) put_partial(s_cur, (t + 1) & 1);
+        bcur = bnext;
+    }
+
+    // epilogue: normalise and store.  O^T layout: lane = head; accumulator
+    // register i of M-tile m is value row rho = 8 (i / 4) + 4 h + i % 4.
+    auto store_rows = [&](auto* dst, float inv) {
+        typedef typename std::remove_pointer<decltype(dst)>::type E;
+        if constexpr (ILV) {
+            // interleaved M-tiles: column = base + 128 g + 4 rho + j
+#pragma unroll
+            for (int g = 0; g < MTV / 4; ++g)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int rho = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+                    const int col = dh * DVH + 128 * g + 4 * rho;
+                    if constexpr (std::is_same<E, float>::value) {
+                        *(f32x4*)(dst + col) = f32x4{o[4 * g][i] * inv, o[4 * g + 1][i] * inv,
+                                                     o[4 * g + 2][i] * inv, o[4 * g + 3][i] * inv};
+                    } else {
+                        bf16x4 v;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) v[j] = (__bf16)(o[4 * g + j][i] * inv);
+                        *(bf16x4*)(dst + col) = v;
+                    }
+                }
+        } else {
+#pragma unroll
+            for (int mt = 0; mt < MTV; ++mt)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int col = dh * DVH + mt * 32 + 8 * q4 + 4 * (lane >> 5);
+                    if constexpr (std::is_same<E, float>::value) {
+                        *(f32x4*)(dst + col) = f32x4{o[mt][4 * q4] * inv, o[mt][4 * q4 + 1] * inv,
+                                                     o[mt][4 * q4 + 2] * inv, o[mt][4 * q4 + 3] * inv};
+                    } else {
+                        bf16x4 v;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) v[j] = (__bf16)(o[mt][4 * q4 + j] * inv);
+                        *(bf16x4*)(dst + col) = v;
+                    }
+                }
+        }
+    };
     if (head < a.H) {
         const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
         const float l_nat = lsum > 0.f ? (m2 + log2f(lsum)) * kLn2 : -__builtin_inff();
         if (nsplit == 1) {
             __bf16* orow = out + ((int64_t)r * a.H + head) * DLAT;
-#pragma unroll
-            for (int mt = 0; mt < MTV; ++mt)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int col = dh * DVH + mt * 32 + 8 * g + 4 * (lane >> 5);
-                    bf16x4 v;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) v[j] = (__bf16)(o[mt][4 * g + j] * inv);
-                    *(bf16x4*)(orow + col) = v;
-                }
+            store_rows(orow, inv);
             if (lse != nullptr && dh == 0 && lane < 32) lse[(int64_t)r * a.H + head] = l_nat;
         } else {
             float* prow = part_o + (((int64_t)r * nsplit + sp) * a.H + head) * DLAT;
-#pragma unroll
-            for (int mt = 0; mt < MTV; ++mt)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int col = dh * DVH + mt * 32 + 8 * g + 4 * (lane >> 5);
-                    *(f32x4*)(prow + col) = f32x4{o[mt][4 * g] * inv, o[mt][4 * g + 1] * inv,
-                                                  o[mt][4 * g + 2] * inv, o[mt][4 * g + 3] * inv};
-                }
+            store_rows(prow, inv);
             if (dh == 0 && lane < 32) part_lse[((int64_t)r * nsplit + sp) * a.H + head] = l_nat;
         }
     }
@@ -302,7 +539,7 @@ struct SfaPlan {
 
 SfaPlan sfa_plan(int R, int K, int H) {
     SfaPlan p;
-    p.nhg = H <= 32 ? 1 : (H <= 64 ? 2 : 4);
+    p.nhg = H <= 32 ? 1 : 2;  // 4 waves (64 heads) per workgroup, 1 per SIMD
     p.nhb = (H + 32 * p.nhg - 1) / (32 * p.nhg);
     const int64_t wgs = (int64_t)(R > 0 ? R : 1) * p.nhb;
     int64_t ns = (256 + wgs - 1) / wgs;
@@ -322,9 +559,10 @@ SfaPlan sfa_plan(int R, int K, int H) {
 template <int DLAT, int DROPE, bool FP8, int NHG>
 static hipError_t launch_sfa_t(const MlaDev& a, const SfaPlan& p, __bf16* out, float* lse, float* part_o,
                                float* part_lse, hipStream_t stream) {
-    dim3 grid((unsigned)p.nsplit, (unsigned)p.nhb, (unsigned)a.R);
-    hipLaunchKernelGGL((sfa_kernel<DLAT, DROPE, FP8, NHG>), grid, dim3(128 * NHG), 0, stream, a, p.kps,
-                       p.nsplit, out, lse, part_o, part_lse);
+    const int64_t units = (int64_t)a.R * p.nsplit;
+    const int64_t nwg = (units + 7) / 8 * 8 * p.nhb;
+    hipLaunchKernelGGL((sfa_kernel<DLAT, DROPE, FP8, NHG>), dim3((unsigned)nwg), dim3(128 * NHG), 0, stream, a,
+                       p.kps, p.nsplit, p.nhb, out, lse, part_o, part_lse);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.nsplit == 1) return e;
     hipLaunchKernelGGL((sfa_combine_kernel<DLAT>), dim3((unsigned)(a.R * a.H)), dim3(128), 0, stream, part_o,
@@ -340,8 +578,6 @@ hipError_t sfa_dispatch(const MlaDev& a, int D_latent, int fp8, __bf16* out, flo
 #define LISFA_SFA_CASE(DL_, DR_, F8_, G_)                                                     \
     if (D_latent == DL_ && (fp8 != 0) == F8_ && p.nhg == G_)                                   \
         return launch_sfa_t<DL_, DR_, F8_, G_>(a, p, out, lse, part_o, part_lse, stream);
-    LISFA_SFA_CASE(512, 64, false, 4)
-    LISFA_SFA_CASE(512, 64, true, 4)
     LISFA_SFA_CASE(512, 64, false, 2)
     LISFA_SFA_CASE(512, 64, true, 2)
     LISFA_SFA_CASE(512, 64, false, 1)
@@ -350,8 +586,6 @@ hipError_t sfa_dispatch(const MlaDev& a, int D_latent, int fp8, __bf16* out, flo
     LISFA_SFA_CASE(64, 16, true, 1)
     LISFA_SFA_CASE(64, 16, false, 2)
     LISFA_SFA_CASE(64, 16, true, 2)
-    LISFA_SFA_CASE(64, 16, false, 4)
-    LISFA_SFA_CASE(64, 16, true, 4)
 #undef LISFA_SFA_CASE
     return hipErrorInvalidValue;
 }
