@@ -6,46 +6,70 @@
 // head-weight weighting).
 //
 // Work decomposition.  A workgroup of 8 wavefronts owns QG query rows of one
-// sequence and a contiguous chunk of key positions.  Key tiles of TK keys are
-// gathered from the (paged or contiguous) key cache with coalesced 16-byte
-// loads into registers one tile ahead, then written to a padded LDS tile.
-// Wave w handles query row (w % QG) and the 32-key subtile (w / QG):
-//   decode  (QG = 1): the 8 waves split a 256-key tile, one query row;
-//   prefill (QG = 8): the 8 waves share a 32-key tile, eight query rows.
-// Per wave the head x key product S[32 heads, 32 keys] is one
-// v_mfma_f32_32x32x16 per 16-element K-step and 32-head M-tile: A = the
-// query's heads (held in VGPRs for the whole kernel), B = K^T read from LDS.
-// In the 32x32 accumulator layout lane l holds key l%32 and 16 heads, so the
-// weighted ReLU sum over heads is 16*MT fused multiply-adds per lane plus one
-// cross-half exchange (lane l ^ 32).  Scores are fp32 end to end.
+// sequence and a contiguous chunk of key positions, streamed in tiles of TK
+// keys through a 4-deep LDS ring:
+//   * tiles are gathered with direct global->LDS 16-byte loads (no VGPR
+//     staging), three tiles in flight while one is consumed, with exact
+//     vmcnt waits; rows are stored unpadded with their 16-byte chunks
+//     XOR-swizzled by row so operand reads are bank-conflict free;
+//   * one fp32 factor per key rides along in the same ring (fp8: the key's
+//     scale; bf16: 1; NaN for a position the cache cannot address);
+//   * wave w scores query row (w % QG) against 16-key subtiles of the tile:
+//     decode (QG = 1) splits each tile over the 8 waves, prefill (QG = 8)
+//     gives every wave its own query and all subtiles.
+// Per 16-key subtile a wave computes S[heads, keys] with v_mfma_f32_16x16x32
+// (A = the query's heads, held in VGPRs; B = K^T from LDS).  In the 16x16
+// accumulator lane l holds key l%16 and 4 heads per M-tile, so the weighted
+// ReLU sum over heads is 4*MT fused multiply-adds plus two lane exchanges.
+// Scores are fp32 end to end.
 #include "common.hpp"
 
 namespace lisfa {
 
 constexpr int kLiMaxBlocks = 512;  // block-table entries one workgroup may touch
+constexpr int kLiNbuf = 4;         // tiles in the LDS ring
+
+__device__ __attribute__((aligned(16))) uint8_t g_li_zero16[16];
+__device__ float g_li_one = 1.0f;
+__device__ float g_li_nan = __builtin_nanf("");
+
+__device__ __forceinline__ f32x4 mfma16x16x32_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16x16x32_fp8(int64_t a, int64_t b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c, 0, 0, 0);
+}
+
+template <int DI, int MT, int QG, bool FP8>
+struct LiCfg {
+    static constexpr int ELT = FP8 ? 1 : 2;
+    static constexpr int RB = DI * ELT;                    // bytes of one key row
+    static constexpr int CPK = RB / 16;                    // 16-byte chunks per row
+    static constexpr int TK0 = QG == 1 ? 128 : 64;
+    static constexpr int TK = (TK0 * CPK >= 512) ? TK0 : 512 / CPK;  // >= one chunk per thread
+    static constexpr int LPT = TK * CPK / 512;             // chunk loads per thread per tile
+    static constexpr int TILE = TK * RB;                   // bytes per tile
+    static constexpr int NSUB = TK / 16;                   // 16-key subtiles per tile
+    static constexpr int KS = DI / 32;                     // MFMA K-steps
+    static_assert(TK * CPK % 512 == 0 && TK <= 512, "tile shape");
+};
 
 template <int DI, int MT, int QG, bool FP8>
 __global__ __launch_bounds__(512) void li_score_kernel(IndexerDev a, float* __restrict__ scores,
                                                        int64_t ld, int keys_per_wg) {
-    constexpr int ELT = FP8 ? 1 : 2;
-    constexpr int RB = DI * ELT;            // bytes of one key row
-    constexpr int CPK = RB / 16;            // 16-byte chunks per key row
-    constexpr int RBP = RB + 16;            // padded LDS row stride (bank spread)
-    constexpr int NST = 8 / QG;             // 32-key subtiles per tile
-    constexpr int TK = 32 * NST;            // keys per tile
-    constexpr int TCH = TK * CPK;           // chunks per tile
-    constexpr int NPRE = (TCH + 511) / 512; // chunks per thread
-    constexpr int KS = DI / 16;             // MFMA K-steps
+    using C = LiCfg<DI, MT, QG, FP8>;
+    constexpr int ELT = C::ELT, RB = C::RB, CPK = C::CPK, TK = C::TK, LPT = C::LPT;
+    constexpr int TILE = C::TILE, NSUB = C::NSUB, KS = C::KS, NBUF = kLiNbuf;
 
-    __shared__ __attribute__((aligned(16))) uint8_t tile[TK * RBP];
-    __shared__ float kmul[TK];
-    __shared__ int32_t blk_id[kLiMaxBlocks];
+    __shared__ __attribute__((aligned(16))) uint8_t ring[NBUF][TILE];
+    __shared__ float kmul[NBUF][512];
+    __shared__ int64_t blk_slot0[kLiMaxBlocks];
+    __shared__ int32_t blk_lim[kLiMaxBlocks];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int qi = wave % QG;
-    const int st = wave / QG;
     const int r0 = blockIdx.y * QG;
     const int r = r0 + qi;
     const int64_t c0 = (int64_t)blockIdx.x * keys_per_wg;
@@ -73,144 +97,175 @@ __global__ __launch_bounds__(512) void li_score_kernel(IndexerDev a, float* __re
         row_bad = !row_ok;
     }
 
-    // block-table entries for [c0, kend)
-    const int sh = a.k.bs_shift;
-    const int64_t b0 = a.k.paged ? (c0 >> sh) : 0;
-    if (a.k.paged) {
+    // Block map of [c0, kend): first slot and addressable length of each block.
+    // Contiguous caches use virtual 64-token blocks.
+    const bool seq_ok = seq0 >= 0 && seq0 < a.k.num_seqs;
+    const int sh = a.k.paged ? a.k.bs_shift : 6;
+    const int64_t bsz = (int64_t)1 << sh;
+    const int64_t b0 = c0 >> sh;
+    {
         const int nb = (int)(((kend - 1) >> sh) - b0 + 1);
         for (int i = tid; i < nb; i += 512) {
-            int64_t blk = b0 + i;
-            int32_t v = -1;
-            if (seq0 >= 0 && seq0 < a.k.num_seqs && blk < a.k.bt_stride)
-                v = a.k.block_table[(int64_t)seq0 * a.k.bt_stride + blk];
-            blk_id[i] = v;
+            const int64_t blk = b0 + i;
+            int64_t s0 = -1;
+            if (seq_ok) {
+                if (a.k.paged) {
+                    if (blk < a.k.bt_stride) {
+                        const int32_t b = a.k.block_table[(int64_t)seq0 * a.k.bt_stride + blk];
+                        if (b >= 0) s0 = (int64_t)b << sh;
+                    }
+                } else {
+                    s0 = a.k.seq_base[seq0] + blk * bsz;
+                }
+            }
+            int64_t lim = 0;
+            if (s0 >= 0 && s0 < a.k.num_slots) {
+                lim = a.k.num_slots - s0;
+                lim = lim < bsz ? lim : bsz;
+            }
+            blk_slot0[i] = s0;
+            blk_lim[i] = (int32_t)lim;
         }
     }
-    const int64_t cbase = (!a.k.paged && seq0 >= 0 && seq0 < a.k.num_seqs) ? a.k.seq_base[seq0] : -1;
-    __syncthreads();
 
-    auto slot_at = [&](int64_t pos) -> int64_t {
-        int64_t s;
-        if (a.k.paged) {
-            int32_t b = blk_id[(pos >> sh) - b0];
-            if (b < 0) return -1;
-            s = ((int64_t)b << sh) + (pos & ((1 << sh) - 1));
-        } else {
-            if (cbase < 0) return -1;
-            s = cbase + pos;
-        }
-        return (s >= 0 && s < a.k.num_slots) ? s : -1;
-    };
-
-    // query heads of this wave's row in MFMA A-operand layout, and weights in
-    // the accumulator's head layout
+    // query heads of this wave's row in A-operand layout (row = head l%16, 8 d)
+    // and weights in the accumulator's head layout (4 heads per M-tile)
     typedef typename std::conditional<FP8, int64_t, bf16x8>::type OpT;
     OpT qa[MT][KS];
-    float wv[MT][16];
-    {
-        const bool have = row_ok;
+    float wv[MT][4];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int head = mt * 32 + (lane & 31);
+    for (int mt = 0; mt < MT; ++mt) {
+        const int head = mt * 16 + (lane & 15);
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                if (have && head < a.H_I) {
-                    const uint8_t* p = a.q + (((int64_t)r * a.H_I + head) * DI + ks * 16 + (lane >> 5) * 8) * ELT;
-                    if constexpr (FP8) qa[mt][ks] = *(const int64_t*)p;
-                    else qa[mt][ks] = *(const bf16x8*)p;
-                } else {
-                    if constexpr (FP8) qa[mt][ks] = 0;
-                    else qa[mt][ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-                }
+        for (int ks = 0; ks < KS; ++ks) {
+            if (row_ok && head < a.H_I) {
+                const uint8_t* p = a.q + (((int64_t)r * a.H_I + head) * DI + ks * 32 + (lane >> 4) * 8) * ELT;
+                if constexpr (FP8) qa[mt][ks] = *(const int64_t*)p;
+                else qa[mt][ks] = *(const bf16x8*)p;
+            } else {
+                if constexpr (FP8) qa[mt][ks] = 0;
+                else qa[mt][ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
             }
+        }
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int h = mt * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-                float wvv = 0.f;
-                if (have && h < a.H_I) {
-                    wvv = a.w[(int64_t)r * a.H_I + h];
-                    if constexpr (FP8)
-                        wvv *= a.q_scale_per_head ? a.q_scale[(int64_t)r * a.H_I + h] : a.q_scale[r];
-                }
-                wv[mt][i] = wvv;
+        for (int i = 0; i < 4; ++i) {
+            const int h = mt * 16 + 4 * (lane >> 4) + i;
+            float wvv = 0.f;
+            if (row_ok && h < a.H_I) {
+                wvv = a.w[(int64_t)r * a.H_I + h];
+                if constexpr (FP8)
+                    wvv *= a.q_scale_per_head ? a.q_scale[(int64_t)r * a.H_I + h] : a.q_scale[r];
             }
+            wv[mt][i] = wvv;
         }
     }
+    __syncthreads();  // block map ready
 
-    u32x4 pre[NPRE];
-    float pre_mul = 0.f;
-    auto prefetch = [&](int64_t t0) {
+    // Tile loads.  Thread tid, load j: chunk position P = j * 512 + tid of the
+    // tile, i.e. row P / CPK, stored position P % CPK, holding global chunk
+    // (P % CPK) ^ (row % CPK).  Every wave issues exactly LPT + 1 loads per
+    // tile (the extra one: 64 key factors), so vmcnt counts are uniform.
+    const uint32_t ring0 = (uint32_t)(uintptr_t)(&ring[0][0]);
+    const uint32_t kmul0 = (uint32_t)(uintptr_t)(&kmul[0][0]);
+    auto issue_tile = [&](int64_t t0, int buf) {
 #pragma unroll
-        for (int j = 0; j < NPRE; ++j) {
-            const int c = tid + j * 512;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (c < TCH) {
-                const int key = c / CPK, part = c % CPK;
-                const int64_t pos = t0 + key;
-                if (pos < kend) {
-                    const int64_t s = slot_at(pos);
-                    if (s >= 0) v = *(const u32x4*)(a.k.data + s * a.k.row_stride + part * 16);
+        for (int j = 0; j < LPT; ++j) {
+            const int P = j * 512 + tid;
+            const int row = P / CPK, pos = P % CPK;
+            const int part = pos ^ (row % CPK);
+            const int64_t kp = t0 + row;
+            const bool inr = kp < kend;
+            const int bi = inr ? (int)((kp >> sh) - b0) : 0;   // tiles may run past kend
+            const int off = (int)(kp & (bsz - 1));
+            const uint8_t* g = g_li_zero16;
+            if (inr && off < blk_lim[bi])
+                g = a.k.data + (blk_slot0[bi] + off) * a.k.row_stride + part * 16;
+            const uint32_t dst = __builtin_amdgcn_readfirstlane(
+                ring0 + (uint32_t)(buf * TILE + (j * 512 + (tid & ~63)) * 16));
+            __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(uintptr_t)dst, 16, 0, 0);
+        }
+        {
+            const int key = tid;  // waves whose keys lie past the tile load a dummy
+            const float* g = &g_li_nan;
+            if (key < TK) {
+                const int64_t kp = t0 + key;
+                const bool inr = kp < kend;
+                const int bi = inr ? (int)((kp >> sh) - b0) : 0;
+                const int off = (int)(kp & (bsz - 1));
+                if (inr && off < blk_lim[bi]) {
+                    if constexpr (FP8) g = a.k.scale + (blk_slot0[bi] + off) / a.k.scale_group;
+                    else g = &g_li_one;
                 }
             }
-            pre[j] = v;
-        }
-        if (tid < TK) {
-            const int64_t pos = t0 + tid;
-            float m = __builtin_nanf("");
-            if (pos < kend) {
-                const int64_t s = slot_at(pos);
-                if (s >= 0) m = FP8 ? a.k.scale[s / a.k.scale_group] : 1.0f;
-            }
-            pre_mul = m;
+            const uint32_t dst = __builtin_amdgcn_readfirstlane(kmul0 + (uint32_t)((buf * 512 + (tid & ~63)) * 4));
+            __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(uintptr_t)dst, 4, 0, 0);
         }
     };
 
-    prefetch(c0);
-    for (int64_t t0 = c0; t0 < kend; t0 += TK) {
-        __syncthreads();  // previous tile fully consumed
-#pragma unroll
-        for (int j = 0; j < NPRE; ++j) {
-            const int c = tid + j * 512;
-            if (c < TCH) {
-                const int key = c / CPK, part = c % CPK;
-                *(u32x4*)(tile + key * RBP + part * 16) = pre[j];
-            }
-        }
-        if (tid < TK) kmul[tid] = pre_mul;
-        __syncthreads();
-        if (t0 + TK < kend) prefetch(t0 + TK);
+    // per-lane LDS byte offset of the B operand of subtile sub, K-step ks
+    // (row = key l%16, 8 elements starting at ks*32 + (l/16)*8)
+    const int krow = lane & 15;
+    auto b_off = [&](int sub, int ks) -> uint32_t {
+        const int rowi = sub * 16 + krow;
+        const int byte = (ks * 32 + (lane >> 4) * 8) * ELT;
+        const int chunk = (byte >> 4) ^ (rowi % CPK);
+        return (uint32_t)(rowi * RB + chunk * 16 + (byte & 15));
+    };
 
-        const int64_t kb = t0 + st * 32;  // first key of this wave's subtile
-        if (row_ok && kb < vis) {
-            f32x16 acc[MT];
+    const int ntiles = (int)((kend - c0 + TK - 1) / TK);
+    // prologue: tiles 0 .. NBUF-2 in flight
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+    for (int p = 0; p < NBUF - 1; ++p)
+        if (p < ntiles) issue_tile(c0 + (int64_t)p * TK, p);
+
+    for (int t = 0; t < ntiles; ++t) {
+        const int buf = t % NBUF;
+        // wait for this wave's loads of tile t: tiles t+1 .. t+NBUF-2 may still fly
+        const int later = (ntiles - 1 - t) < (NBUF - 2) ? (ntiles - 1 - t) : (NBUF - 2);
+        if (later >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (LPT + 1)) : "memory");
+        else if (later == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPT + 1) : "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();  // everyone's part of tile t landed; tile t-1 fully consumed
+        if (t + NBUF - 1 < ntiles) issue_tile(c0 + (int64_t)(t + NBUF - 1) * TK, (t + NBUF - 1) % NBUF);
+
+        const int64_t t0 = c0 + (int64_t)t * TK;
+        const lds_u8* T = (const lds_u8*)&ring[buf][0];
+        // subtiles of this wave: decode splits the tile over the 8 waves
+        constexpr int SUBW = QG == 1 ? NSUB / 8 : NSUB;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) acc[mt][i] = 0.f;
-            const uint8_t* brow = tile + (st * 32 + (lane & 31)) * RBP + (lane >> 5) * 8 * ELT;
+        for (int u = 0; u < SUBW; ++u) {
+            const int sub = QG == 1 ? (u * 8 + wave) : u;
+            const int64_t kb = t0 + sub * 16;
+            if (row_ok && kb < vis) {
+                f32x4 acc[MT];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                if constexpr (FP8) {
-                    const int64_t b = *(const int64_t*)(brow + ks * 16);
+                for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma32x32x16_fp8(qa[mt][ks], b, acc[mt]);
-                } else {
-                    const bf16x8 b = *(const bf16x8*)(brow + ks * 32);
+                for (int ks = 0; ks < KS; ++ks) {
+                    const uint32_t bo = b_off(sub, ks);
+                    if constexpr (FP8) {
+                        const int64_t b = *(const __attribute__((address_space(3))) int64_t*)(T + bo);
 #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma32x32x16_bf16(qa[mt][ks], b, acc[mt]);
+                        for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma16x16x32_fp8(qa[mt][ks], b, acc[mt]);
+                    } else {
+                        const bf16x8 b = *(const lds_bf16x8*)(T + bo);
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma16x16x32_bf16(qa[mt][ks], b, acc[mt]);
+                    }
                 }
+                float part = 0.f;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) part = fmaf(wv[mt][i], fmaxf(acc[mt][i], 0.f), part);
+                part += __shfl_xor(part, 16);
+                part += __shfl_xor(part, 32);
+                const int64_t key = kb + (lane & 15);
+                if (lane < 16 && key < vis) scores[(int64_t)r * ld + key] = part * kmul[buf][sub * 16 + lane];
+            } else if (row_bad && kb < vis) {
+                const int64_t key = kb + (lane & 15);
+                if (lane < 16 && key < vis) scores[(int64_t)r * ld + key] = __builtin_nanf("");
             }
-            float part = 0.f;
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) part = fmaf(wv[mt][i], fmaxf(acc[mt][i], 0.f), part);
-            const float tot = part + __shfl_xor(part, 32);
-            const int64_t key = kb + (lane & 31);
-            if (lane < 32 && key < vis) scores[(int64_t)r * ld + key] = tot * kmul[st * 32 + lane];
-        } else if (row_bad && kb < vis) {
-            const int64_t key = kb + (lane & 31);
-            if (lane < 32 && key < vis) scores[(int64_t)r * ld + key] = __builtin_nanf("");
         }
     }
 }
@@ -220,35 +275,39 @@ __global__ __launch_bounds__(512) void li_score_kernel(IndexerDev a, float* __re
 template <int DI, int MT, int QG, bool FP8>
 static hipError_t launch_li(const IndexerDev& a, float* scores, int64_t ld, int64_t max_visible,
                             hipStream_t stream) {
-    constexpr int TK = 32 * (8 / QG);
-    const int bsz = a.k.paged ? (1 << a.k.bs_shift) : (1 << 30);
+    constexpr int TK = LiCfg<DI, MT, QG, FP8>::TK;
+    const int sh = a.k.paged ? a.k.bs_shift : 6;
+    const int64_t bsz = (int64_t)1 << sh;
     // keys per workgroup: enough workgroups to fill 256 CUs a few times over
     const int64_t groups = (a.R + QG - 1) / QG;
-    int64_t want_wg = 1024;
+    const int64_t want_wg = 256;   // about one long-running workgroup per CU
     int64_t nchunk = (want_wg + groups - 1) / groups;
     int64_t kpw = (max_visible + nchunk - 1) / nchunk;
-    int64_t min_kpw = QG == 1 ? TK : 2048;
+    const int64_t min_kpw = QG == 1 ? 4 * TK : 2048;
     if (kpw < min_kpw) kpw = min_kpw;
-    kpw = (kpw + TK - 1) / TK * TK;
-    if (a.k.paged) {
-        int64_t cap = (int64_t)(kLiMaxBlocks - 1) * bsz / TK * TK;
-        if (kpw > cap) kpw = cap;
-    }
-    if (kpw > (1 << 30)) kpw = (1 << 30) / TK * TK;
+    // chunks start on tile and block boundaries
+    const int64_t align = bsz > TK ? bsz : TK;
+    kpw = (kpw + align - 1) / align * align;
+    const int64_t cap = (int64_t)(kLiMaxBlocks - 1) * bsz / align * align;
+    if (kpw > cap) kpw = cap;
+    if (kpw > (1 << 30)) kpw = (int64_t)(1 << 30) / align * align;
     nchunk = (max_visible + kpw - 1) / kpw;
     if (nchunk < 1) nchunk = 1;
     dim3 grid((unsigned)nchunk, (unsigned)groups);
-    hipLaunchKernelGGL((li_score_kernel<DI, MT, QG, FP8>), grid, dim3(512), 0, stream, a, scores, ld,
-                       (int)kpw);
+    hipLaunchKernelGGL((li_score_kernel<DI, MT, QG, FP8>), grid, dim3(512), 0, stream, a, scores, ld, (int)kpw);
     return hipGetLastError();
 }
 
 hipError_t li_score_dispatch(const IndexerDev& a, int D_I, int fp8, int qg, float* scores, int64_t ld,
                              int64_t max_visible, hipStream_t stream) {
-    const int mt = a.H_I <= 32 ? 1 : 2;
+    const int mt = a.H_I <= 16 ? 1 : (a.H_I <= 32 ? 2 : 4);
 #define LISFA_LI_CASE(DI_, MT_, QG_, F8_)                                                    \
     if (D_I == DI_ && mt == MT_ && qg == QG_ && (fp8 != 0) == F8_)                            \
         return launch_li<DI_, MT_, QG_, F8_>(a, scores, ld, max_visible, stream);
+    LISFA_LI_CASE(128, 4, 1, false)
+    LISFA_LI_CASE(128, 4, 8, false)
+    LISFA_LI_CASE(128, 4, 1, true)
+    LISFA_LI_CASE(128, 4, 8, true)
     LISFA_LI_CASE(128, 2, 1, false)
     LISFA_LI_CASE(128, 2, 8, false)
     LISFA_LI_CASE(128, 2, 1, true)
@@ -257,14 +316,18 @@ hipError_t li_score_dispatch(const IndexerDev& a, int D_I, int fp8, int qg, floa
     LISFA_LI_CASE(128, 1, 8, false)
     LISFA_LI_CASE(128, 1, 1, true)
     LISFA_LI_CASE(128, 1, 8, true)
-    LISFA_LI_CASE(32, 1, 1, false)
-    LISFA_LI_CASE(32, 1, 8, false)
-    LISFA_LI_CASE(32, 1, 1, true)
-    LISFA_LI_CASE(32, 1, 8, true)
+    LISFA_LI_CASE(32, 4, 1, false)
+    LISFA_LI_CASE(32, 4, 8, false)
+    LISFA_LI_CASE(32, 4, 1, true)
+    LISFA_LI_CASE(32, 4, 8, true)
     LISFA_LI_CASE(32, 2, 1, false)
     LISFA_LI_CASE(32, 2, 8, false)
     LISFA_LI_CASE(32, 2, 1, true)
     LISFA_LI_CASE(32, 2, 8, true)
+    LISFA_LI_CASE(32, 1, 1, false)
+    LISFA_LI_CASE(32, 1, 8, false)
+    LISFA_LI_CASE(32, 1, 1, true)
+    LISFA_LI_CASE(32, 1, 8, true)
 #undef LISFA_LI_CASE
     return hipErrorInvalidValue;
 }
