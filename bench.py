@@ -49,6 +49,89 @@ def algorithmic(wl, b):
     return dict(li=(li_bytes, li_flops), topk=(topk_bytes, 0.0), sfa=(sfa_bytes, sfa_flops))
 
 
+KERNEL_SOURCES = {
+    "li_score": ["li_score.hip", "common.hpp"],
+    "topk_select": ["topk.hip", "common.hpp"],
+    "sparse_mla_attn": ["sparse_mla.hip", "common.hpp"],
+}
+
+
+def source_hash(stage: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[stage]:
+        with open(os.path.join(ROOT, "indexer_selected_sparse_li_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_path(stage: str, workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"{stage}_{workload}_traffic.md")
+
+
+def stored_traffic(stage: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none or the kernel source changed since it was taken."""
+    path = traffic_path(stage, workload)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    try:
+        blob = text.split("```json", 1)[1].split("```", 1)[0]
+        d = json.loads(blob)
+    except Exception:
+        return None
+    if d.get("source_hash") != source_hash(stage):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def pmc_per_dispatch(csv_path: str, counter: str, kernel_substr: str):
+    import csv
+    vals = []
+    with open(csv_path) as fh:
+        for row in csv.DictReader(fh):
+            if row["Counter_Name"] == counter and kernel_substr in row["Kernel_Name"]:
+                vals.append(float(row["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no {counter} rows for {kernel_substr} in {csv_path}")
+    vals.sort()
+    return vals[len(vals) // 2], len(vals)
+
+
+def write_traffic_summary(args):
+    """Turn four rocprofv3 --pmc CSVs (kernel FETCH_SIZE / WRITE_SIZE, copy
+    FETCH_SIZE / WRITE_SIZE) into a profiles/ summary with the scaled bytes."""
+    stage, wl_name = args.stage, args.workload
+    kname = {"li_score": "li_score_kernel", "topk_select": "topk_kernel",
+             "sparse_mla_attn": "sfa_kernel"}[stage]
+    copy_bytes = args.copy_bytes
+    kf, nkf = pmc_per_dispatch(args.fetch_csv, "FETCH_SIZE", kname)
+    kw, nkw = pmc_per_dispatch(args.write_csv, "WRITE_SIZE", kname)
+    cf, _ = pmc_per_dispatch(args.copy_fetch_csv, "FETCH_SIZE", "")
+    cw, _ = pmc_per_dispatch(args.copy_write_csv, "WRITE_SIZE", "")
+    f_scale = copy_bytes / (cf * 1024.0)
+    w_scale = copy_bytes / (cw * 1024.0)
+    fetch = kf * 1024.0 * f_scale
+    write = kw * 1024.0 * w_scale
+    d = dict(stage=stage, workload=wl_name, source_hash=source_hash(stage),
+             fetch_kib_raw=kf, write_kib_raw=kw, copy_fetch_kib_raw=cf, copy_write_kib_raw=cw,
+             copy_bytes=copy_bytes, fetch_scale=round(f_scale, 4), write_scale=round(w_scale, 4),
+             hbm_bytes_per_launch=int(fetch + write), fetch_bytes=int(fetch), write_bytes=int(write))
+    path = traffic_path(stage, wl_name)
+    with open(path, "w") as fh:
+        fh.write(f"# HBM traffic of {stage} ({kname}) on {wl_name}\n\n")
+        fh.write("Median per dispatch over the profiled launches, rocprofv3 --pmc counters in KiB.\n")
+        fh.write("Each counter is scaled by what it reads for a plain device copy of known size\n")
+        fh.write(f"(torch copy of {copy_bytes} bytes: expected = copy_bytes / 1024 KiB).\n\n")
+        fh.write("Commands (run from the repository root on the GPU box):\n\n")
+        for c in args.commands or []:
+            fh.write(f"    {c}\n")
+        fh.write("\n```json\n" + json.dumps(d, indent=1) + "\n```\n")
+    print(f"wrote {path}: {d['hbm_bytes_per_launch'] / 1e6:.1f} MB per launch "
+          f"(fetch scale {f_scale:.3f}, write scale {w_scale:.3f})")
+
+
 def time_on_stream(fn, stream, warmup, steps):
     import torch
     for _ in range(warmup):
@@ -77,14 +160,15 @@ def cpu_baseline(b, budget_s: float):
         cores = os.cpu_count() or 1
     inp = W.to_numpy(b)
     rows, t_used = 0, 0.0
-    while rows < b.R and t_used < budget_s:
+    while t_used < budget_s and rows < 64 * b.R:
         t0 = time.perf_counter()
-        O.layer_row(inp, rows)
+        O.layer_row(inp, rows % b.R)
         t_used += time.perf_counter() - t0
         rows += 1
     return dict(value=rows / t_used, unit="tokens/s", cores=int(cores), kind="oracle",
-                sample=f"first {rows} of {b.R} query rows of the same batch "
-                       f"(float64 NumPy, {t_used:.1f} s of oracle time)")
+                sample=f"{rows} query-row evaluations cycling over the {b.R} rows of the same batch "
+                       f"(scores over the full context, selection, attention; float64 NumPy, "
+                       f"{t_used:.1f} s of oracle time)")
 
 
 def main():
@@ -93,10 +177,25 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_paged_64x32768")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stage-steps", type=int, default=None)
+    ap.add_argument("--only", choices=["li_score", "topk_select", "sparse_mla_attn", "layer"],
+                    help="profiling mode: run just this stage (no JSON line)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="profiling mode: run a plain device copy of --copy-bytes bytes")
+    ap.add_argument("--copy-bytes", type=int, default=1 << 30)
+    ap.add_argument("--write-traffic-summary", action="store_true")
+    ap.add_argument("--stage", default="li_score")
+    ap.add_argument("--fetch-csv")
+    ap.add_argument("--write-csv")
+    ap.add_argument("--copy-fetch-csv")
+    ap.add_argument("--copy-write-csv")
+    ap.add_argument("--commands", nargs="*")
     args = ap.parse_args()
+    if args.write_traffic_summary:
+        write_traffic_summary(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the layer's multi-GPU sharding is a design, not part of this build)", file=sys.stderr)
@@ -108,6 +207,14 @@ def main():
 
     lisfa.load()
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        src = torch.empty(args.copy_bytes, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(max(1, args.steps)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {args.copy_bytes} bytes x {args.steps}")
+        return
     wl = W.get(args.workload)
     log(f"[bench] generating {wl.name} on the GPU")
     b = W.make_batch(wl, device="cuda")
@@ -129,6 +236,29 @@ def main():
         lisfa.li_topk_sfa(b.q_idx, b.w, kc, b.q, vc, b.row_seq, b.row_pos, wl.K, b.max_visible, out, lse,
                           idx_out=idx, q_scale=b.q_scale, rows_per_group=rpg,
                           softmax_scale=wl.softmax_scale, workspace=ws, stream=stream)
+
+    if args.only:
+        ld_o = (b.max_visible + 63) // 64 * 64
+        scores_o = torch.empty(R, ld_o, dtype=torch.float32, device="cuda")
+        sfa_ws_o = torch.empty(max(1, lisfa.workspace_size(1, R, 0, wl.K, wl.H, wl.D_v)), dtype=torch.uint8,
+                               device="cuda")
+        fns = {
+            "layer": step,
+            "li_score": lambda: lisfa.li_score(b.q_idx, b.w, kc, b.row_seq, b.row_pos, scores_o, b.max_visible,
+                                               q_scale=b.q_scale, rows_per_group=rpg, stream=stream),
+            "topk_select": lambda: lisfa.topk_select(scores_o, b.row_pos, wl.K, idx, stream=stream),
+            "sparse_mla_attn": lambda: lisfa.sparse_mla_attn(b.q, vc, b.row_seq, idx, out, lse,
+                                                             softmax_scale=wl.softmax_scale, workspace=sfa_ws_o,
+                                                             stream=stream),
+        }
+        if args.only in ("topk_select", "sparse_mla_attn"):
+            fns["li_score"]()
+            fns["topk_select"]()
+        for _ in range(args.warmup + args.steps):
+            fns[args.only]()
+        torch.cuda.synchronize()
+        log(f"[bench] ran {args.only} x {args.warmup + args.steps}")
+        return
 
     # the whole layer, timed: barrier + synchronize on both sides
     log(f"[bench] warmup {args.warmup}, timed {args.steps}")
@@ -189,7 +319,7 @@ def main():
     dominant = max(stages, key=lambda k: stages[k]["us"])
     roofline = dict(stages[dominant]["roofline"])
     roofline["kernel"] = dominant
-    roofline["traffic"] = None
+    roofline["traffic"] = stored_traffic(dominant, wl.name)
 
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
