@@ -491,41 +491,434 @@ __global__ __launch_bounds__(128 * NHG) void sfa_kernel(MlaDev a, int kps, int n
     }
 }
 
-// Merge split-K partials: out = sum_i e^{lse_i - M} O_i / sum_i e^{lse_i - M}.
-template <int DLAT>
-__global__ __launch_bounds__(128) void sfa_combine_kernel(const float* __restrict__ part_o,
-                                                          const float* __restrict__ part_lse, int nsplit,
-                                                          int H, __bf16* __restrict__ out,
-                                                          float* __restrict__ lse) {
-    const int rh = blockIdx.x;           // r * H + h
-    const int r = rh / H, h = rh % H;
-    float M = -__builtin_inff();
-    for (int i = 0; i < nsplit; ++i) M = fmaxf(M, part_lse[((int64_t)r * nsplit + i) * H + h]);
-    float W = 0.f;
-    constexpr int PER = (DLAT + 127) / 128;
-    float acc[PER];
+// Wide bf16 rows (a whole number of 128-byte groups, e.g. 512 + 64) -----------
+//
+// Same decomposition, softmax and MFMA layouts as sfa_kernel; what differs is
+// how the tile is brought in and how each wave's stream is laid out.
+//
+// Blocked tile layout: the 32 rows of a tile form 4 groups of 8 rows; group g
+// holds NJ = CPK / 8 blocks of 1 KB, block j = chunks [8j, 8j + 8) of the
+// group's rows (128 B per row), chunk slots of row r permuted by XOR
+// sfa_swz(r).  Chunk c of tile row r sits at
+//   (r / 8) * NJ KB + (c / 8) KB + (r % 8) * 128 + ((c % 8) ^ swz(r)) * 16.
+// A wave's load instruction j fills exactly one block: lane l brings chunk
+// 8j + ((l % 8) ^ swz(row)) of row 8 w + l / 8 to block + 16 l.  A thread
+// therefore looks up one cache slot per tile and issues NJ loads that differ
+// only in their immediate offsets.
+//
+// Each wave runs a loop specialised for its half of the QK^T reduction (no
+// divergent branch inside), and the exponentials of tile t are computed
+// between the QK^T MFMAs of tile t + 1, which do not depend on them.
+__device__ __attribute__((aligned(16))) uint8_t g_zero_row[2048];
+
+// fn(std::integral_constant<int, i>) for i = 0 .. N-1 (immediate operands)
+template <int I = 0, int N, typename F>
+__device__ __forceinline__ void static_for_impl(F&& fn) {
+    if constexpr (I < N) {
+        fn(std::integral_constant<int, I>{});
+        static_for_impl<I + 1, N>(fn);
+    }
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& fn) { static_for_impl<0, N>(fn); }
+
+template <int DLAT, int DROPE, int NHG>
+__global__ __launch_bounds__(128 * NHG) void sfa_bf16_kernel(MlaDev a, int kps, int nsplit, int nhb,
+                                                             __bf16* __restrict__ out, float* __restrict__ lse,
+                                                             float* __restrict__ part_o,
+                                                             float* __restrict__ part_lse) {
+    constexpr int DQK = DLAT + DROPE;
+    constexpr int CPK = DQK * 2 / 16;       // 16-byte chunks per row
+    static_assert((DQK * 2) % 128 == 0 && CPK * 16 <= 2048, "rows must be whole 128-byte groups");
+    constexpr int NJ = CPK / 8;             // 1 KB blocks per 8-row group
+    constexpr int GB = NJ * 1024;           // bytes per 8-row group
+    constexpr int TROWS = 32;
+    constexpr int TB = (TROWS / 8) * GB;    // bytes per tile
+    constexpr int NBUF = 3;                 // tile ring: PV(t) | QK(t+1) | loading t+2
+    constexpr int NT = 128 * NHG;
+    constexpr int RPP = NT / 8;             // tile rows loaded per pass
+    constexpr int NPASS = TROWS / RPP;
+    constexpr int KS = DQK / 16;            // QK K-steps
+    static_assert(KS % 2 == 0, "even K-step count");
+    constexpr int NKS = KS / 2;             // K-steps per wave
+    constexpr int DVH = DLAT / 2;           // value columns per wave
+    constexpr int MTV = DVH / 32;           // PV M-tiles per wave
+    static_assert(DVH % 64 == 0, "shape");
+
+    __shared__ __attribute__((aligned(1024))) uint8_t tile[NBUF * TB];
+    __shared__ uint32_t rslot[kSfaMaxKeys];            // cache slot of each selected row, ~0 = skip
+    __shared__ uint32_t vmask[kSfaMaxKeys / 32];       // valid-row bits of each 32-row tile
+    __shared__ __attribute__((aligned(16))) float xbuf[2][NHG * 2 * 1024];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hg = wave >> 1;
+    const int bid = blockIdx.x;
+    const int hb = (bid >> 3) % nhb;
+    const int u = ((bid >> 3) / nhb) * 8 + (bid & 7);
+    if (u >= a.R * nsplit) return;
+    const int r = u / nsplit, sp = u % nsplit;
+    const int k0 = sp * kps;
+    const int k1 = (k0 + kps < a.K) ? k0 + kps : a.K;
+    const int nk = k1 - k0;
+    const int seq = a.row_seq[r];
+    const int ntiles = (nk + TROWS - 1) / TROWS;
+
+    for (int i0 = 0; i0 < ntiles * TROWS; i0 += NT) {
+        const int i = i0 + tid;
+        int64_t s = -1;
+        if (i < nk) {
+            const int p = a.idx[(int64_t)r * a.K + k0 + i];
+            s = p >= 0 ? slot_of(a.kv, seq, p) : -1;
+        }
+        if (i < ntiles * TROWS) rslot[i] = s >= 0 ? (uint32_t)s : 0xFFFFFFFFu;
+        const uint64_t bal = __ballot(s >= 0);
+        if (lane == 0 && i < ntiles * TROWS) {
+            vmask[i / 32] = (uint32_t)bal;
+            if (i + 32 < ntiles * TROWS) vmask[i / 32 + 1] = (uint32_t)(bal >> 32);
+        }
+    }
+    __syncthreads();
+
+    const lds_u8* tile0 = (const lds_u8*)tile;
+    const uint32_t tile_lds = (uint32_t)(uintptr_t)tile;
+    // loads: this thread's row within a pass and its chunk permutation
+    const int lrow = tid >> 3;
+    const uint32_t goff = (uint32_t)(((tid & 7) ^ sfa_swz(lrow)) << 4);  // swz(lrow) == swz(lrow + 16)
+    // slots of this thread's rows of tile t (read one iteration ahead of use)
+    auto read_slots = [&](int t, uint32_t (&sl)[NPASS]) {
 #pragma unroll
-    for (int j = 0; j < PER; ++j) acc[j] = 0.f;
+        for (int p = 0; p < NPASS; ++p) sl[p] = rslot[(t < ntiles ? t : 0) * TROWS + p * RPP + lrow];
+    };
+    auto issue_tile = [&](const uint32_t (&sl)[NPASS], int buf) {
+#pragma unroll
+        for (int p = 0; p < NPASS; ++p) {
+            const uint32_t s = sl[p];
+            const uint8_t* g = (s != 0xFFFFFFFFu ? a.kv.data + (uint64_t)s * (uint32_t)a.kv.row_stride : g_zero_row) + goff;
+            const uint32_t blk = tile_lds + (uint32_t)(buf * TB + (p * (RPP / 8) + wave) * GB);
+            static_for<NJ>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                // the immediate offset moves both the global and the LDS address
+                const uint32_t dst = __builtin_amdgcn_readfirstlane(blk + (uint32_t)(j * (1024 - 128)));
+                __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(uintptr_t)dst, 16,
+                                                 j * 128, 0);
+            });
+        }
+    };
+    auto body = [&](auto dh_c) {
+        constexpr int DH = decltype(dh_c)::value;
+        constexpr int KSB = DH * NKS;
+        const int head = hb * 32 * NHG + hg * 32 + (lane & 31);
+        bf16x8 qb[NKS];
+#pragma unroll
+        for (int j = 0; j < NKS; ++j) {
+            if (head < a.H)
+                qb[j] = *(const bf16x8*)(a.q + (((int64_t)r * a.H + head) * DQK + (KSB + j) * 16 + (lane >> 5) * 8) * 2);
+            else
+                qb[j] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+        }
+        // QK operand: lane = key row krow, 8 values of chunk 2 ks + lane / 32
+        const int krow = lane & 31;
+        uint32_t qkb[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            qkb[m] = (uint32_t)((krow >> 3) * GB + (krow & 7) * 128 + ((((2 * m) + (lane >> 5)) ^ sfa_swz(krow)) << 4));
+        auto qk_op = [&](const lds_u8* T, int ks) -> bf16x8 {   // ks: compile-time after unrolling
+            return *(const lds_bf16x8*)(T + qkb[ks & 3] + (ks >> 2) * 1024);
+        };
+        // PV operand (transpose reads): 16-lane group g16 reads rows 8 j + trow
+        // of each 16-key half, at 4 consecutive value columns per lane
+        const int g16 = lane >> 4, i16 = lane & 15;
+        const int trow = 4 * (g16 >> 1) + (i16 >> 2);
+        uint32_t pvb[2][2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int par = 0; par < 2; ++par) {
+                const int cc = 4 * par + 2 * (g16 & 1) + ((i16 & 3) >> 1);
+                pvb[j][par] = (uint32_t)(j * GB + trow * 128 + ((cc ^ sfa_swz(8 * j + trow)) << 4) + 8 * (i16 & 1));
+            }
+        typedef short s16x4 __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+        auto trd = [&](const lds_u8* T, int mt, int kk, int j) -> s16x4 {
+            return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4*)(T + pvb[j][mt & 1] + kk * 2 * GB + (4 * DH + (mt >> 1)) * 1024));
+        };
+        auto qk = [&](const lds_u8* T) {
+            f32x16 s;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[i] = 0.f;
+            constexpr int PF = 4;
+            bf16x8 buf[PF];
+#pragma unroll
+            for (int j = 0; j < PF; ++j) buf[j] = qk_op(T, KSB + j);
+#pragma unroll
+            for (int j = 0; j < NKS; ++j) {
+                const bf16x8 av = buf[j % PF];
+                if (j + PF < NKS) buf[j % PF] = qk_op(T, KSB + j + PF);
+                s = mfma32x32x16_bf16(av, qb[j], s);
+            }
+            return s;
+        };
+        auto put_partial = [&](const f32x16& s, int xb) {
+            float* xs = xbuf[xb] + (hg * 2 + DH) * 1024 + lane * 4;
+#pragma unroll
+            for (int i = 0; i < 16; i += 4) *(f32x4*)(xs + i * 64) = f32x4{s[i], s[i + 1], s[i + 2], s[i + 3]};
+        };
+
+        f32x16 o[MTV];
+#pragma unroll
+        for (int mt = 0; mt < MTV; ++mt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[mt][i] = 0.f;
+        float m2 = -__builtin_inff(), lsum = 0.f;
+        const float c = a.scale_log2;
+        f32x16 s_cur;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s_cur[i] = 0.f;
+
+        uint32_t sl[NPASS];
+        if (ntiles > 0) {
+            read_slots(0, sl);
+            issue_tile(sl, 0);
+        }
+        if (ntiles > 1) {
+            read_slots(1, sl);
+            issue_tile(sl, 1);
+        }
+        read_slots(2, sl);
+        if (ntiles > 0) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            s_cur = qk(tile0);
+            put_partial(s_cur, 0);
+        }
+
+        int bcur = 0;
+        for (int t = 0; t < ntiles; ++t) {
+            const int bnext = bcur == NBUF - 1 ? 0 : bcur + 1;
+            const int bnext2 = bnext == NBUF - 1 ? 0 : bnext + 1;
+            // tile t+1 landed; tile t-1's buffer is free; partials of tile t published
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            const lds_u8* T = tile0 + bcur * TB;
+            const lds_u8* Tn = tile0 + bnext * TB;
+            constexpr int PF = 4;   // QK^T operand reads in flight
+            constexpr int PD = 2;   // PV: M-tiles of operands in flight
+
+            // every LDS read this step needs first is issued here, ahead of
+            // the loads of tile t+2, so a single wait covers them
+            f32x4 xr[4];
+            {
+                const float* xp = xbuf[t & 1] + (hg * 2 + (DH ^ 1)) * 1024 + lane * 4;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) xr[i] = *(const f32x4*)(xp + i * 256);
+            }
+            const uint32_t vmr = vmask[t];
+            bf16x8 buf[PF];
+#pragma unroll
+            for (int j = 0; j < PF; ++j) buf[j] = qk_op(Tn, KSB + j);
+            if (t + 2 < ntiles) issue_tile(sl, bnext2);
+            read_slots(t + 3, sl);
+            __builtin_amdgcn_sched_barrier(0);
+
+            // raw logits of tile t = own partial + partner's partial
+            f32x16 s = s_cur;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                s[4 * i] += xr[i].x;
+                s[4 * i + 1] += xr[i].y;
+                s[4 * i + 2] += xr[i].z;
+                s[4 * i + 3] += xr[i].w;
+            }
+            const uint32_t vm = __builtin_amdgcn_readfirstlane(vmr);
+            if (vm != 0xFFFFFFFFu) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int key = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+                    if (!((vm >> key) & 1u)) s[i] = -__builtin_inff();
+                }
+            }
+            // tile maximum of each head (both lane halves), in log2 units
+            float tmax = fmaxf(fmaxf(s[0], s[1]), s[2]);
+#pragma unroll
+            for (int i = 3; i < 15; i += 2) tmax = fmaxf(fmaxf(tmax, s[i]), s[i + 1]);
+            tmax = fmaxf(tmax, s[15]);
+            {
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+                tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+            }
+            tmax *= c;   // c > 0
+            // lazy reference maximum (raised only past kLazy log2 units)
+            constexpr float kLazy = 8.0f;
+            const bool raise = tmax > m2 + kLazy;   // also true on the first valid tile
+            if (__ballot(raise) != 0ull) {
+                const float mnew = raise ? tmax : m2;
+                const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);  // m2 = -inf -> 0
+                lsum *= alpha;
+#pragma unroll
+                for (int mt = 0; mt < MTV; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) o[mt][i] *= alpha;
+                m2 = mnew;
+            }
+            // a head with no valid row so far keeps m2 = -inf: its (masked)
+            // probabilities must come out 0, not NaN
+            const float negm = m2 == -__builtin_inff() ? 0.f : -m2;
+
+            // Phase 1: QK^T of tile t+1 (independent of this tile's softmax)
+            // with the exponentials of tile t between its MFMAs; operand reads
+            // run PF K-steps ahead.
+            s16x4 rb[PD + 1][4];
+            f32x16 s_next;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s_next[i] = 0.f;
+            float pe[16];
+            {
+#pragma unroll
+                for (int j = 0; j < NKS; ++j) {
+                    const bf16x8 av = buf[j % PF];
+                    if (j + PF < NKS) buf[j % PF] = qk_op(Tn, KSB + j + PF);
+                    s_next = mfma32x32x16_bf16(av, qb[j], s_next);
+                    if (j < 16) pe[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], c, negm));
+                }
+            }
+            float rs = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) rs += pe[i];
+            {
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(rs), __float_as_uint(rs), false, false);
+                rs = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+            }
+            lsum += rs;
+            bf16x8 pb[2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) pb[kk][e] = (__bf16)pe[8 * kk + e];
+#pragma unroll
+            for (int j = 0; j < NKS; ++j) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (j + PF < NKS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int m = 0; m < PD; ++m)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) rb[m][q] = trd(T, m, q >> 1, q & 1);
+
+            // Phase 2, PV(t): O^T[32 value columns x 32 heads] += V^T[32 x 16
+            // keys] * P^T.  Keys of K-step kk for lane half h: 16 kk + 4 h +
+            // {0..3} (operand elements 0..3) and 16 kk + 8 + 4 h + {0..3}
+            // (elements 4..7): the keys of S^T accumulator registers 8 kk ..
+            // 8 kk + 7.  Transpose reads run PD M-tiles ahead.
+#pragma unroll
+            for (int mt = 0; mt < MTV; ++mt) {
+                if (mt + PD < MTV) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) rb[(mt + PD) % (PD + 1)][q] = trd(T, mt + PD, q >> 1, q & 1);
+                }
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const u32x2 lo = __builtin_bit_cast(u32x2, rb[mt % (PD + 1)][2 * kk]);
+                    const u32x2 hi = __builtin_bit_cast(u32x2, rb[mt % (PD + 1)][2 * kk + 1]);
+                    const u32x4 w = {lo.x, lo.y, hi.x, hi.y};
+                    o[mt] = mfma32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pb[kk], o[mt]);
+                }
+            }
+            put_partial(s_next, (t + 1) & 1);
+            __builtin_amdgcn_sched_group_barrier(0x100, 4 * PD, 0);
+#pragma unroll
+            for (int mt = 0; mt < MTV; ++mt) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                if (mt + PD < MTV) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x200, 4, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            s_cur = s_next;
+            bcur = bnext;
+        }
+
+        // epilogue: normalise and store.  O^T layout: lane = head; accumulator
+        // register i of M-tile m is value column 32 m + 8 (i / 4) + 4 h + i % 4.
+        if (head < a.H) {
+            const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+            const float l_nat = lsum > 0.f ? (m2 + log2f(lsum)) * kLn2 : -__builtin_inff();
+            if (nsplit == 1) {
+                __bf16* orow = out + ((int64_t)r * a.H + head) * DLAT;
+#pragma unroll
+                for (int mt = 0; mt < MTV; ++mt)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const int col = DH * DVH + mt * 32 + 8 * q4 + 4 * (lane >> 5);
+                        bf16x4 v;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) v[j] = (__bf16)(o[mt][4 * q4 + j] * inv);
+                        *(bf16x4*)(orow + col) = v;
+                    }
+                if (lse != nullptr && DH == 0 && lane < 32) lse[(int64_t)r * a.H + head] = l_nat;
+            } else {
+                float* prow = part_o + (((int64_t)r * nsplit + sp) * a.H + head) * DLAT;
+#pragma unroll
+                for (int mt = 0; mt < MTV; ++mt)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const int col = DH * DVH + mt * 32 + 8 * q4 + 4 * (lane >> 5);
+                        *(f32x4*)(prow + col) = f32x4{o[mt][4 * q4] * inv, o[mt][4 * q4 + 1] * inv,
+                                                      o[mt][4 * q4 + 2] * inv, o[mt][4 * q4 + 3] * inv};
+                    }
+                if (DH == 0 && lane < 32) part_lse[((int64_t)r * nsplit + sp) * a.H + head] = l_nat;
+            }
+        }
+    };
+    if (wave & 1) body(std::integral_constant<int, 1>{});
+    else body(std::integral_constant<int, 0>{});
+}
+
+// Merge split-K partials: out = sum_i e^{lse_i - M} O_i / sum_i e^{lse_i - M}.
+// 8 consecutive value columns per thread (two 16-byte loads per split, one
+// 16-byte store), DLAT / 8 threads per (row, head), 256 threads per block.
+template <int DLAT>
+__global__ __launch_bounds__(256) void sfa_combine_kernel(const float* __restrict__ part_o,
+                                                          const float* __restrict__ part_lse, int nsplit,
+                                                          int H, int RH, __bf16* __restrict__ out,
+                                                          float* __restrict__ lse) {
+    constexpr int TPH = DLAT / 8;            // threads per (row, head)
+    static_assert(DLAT % 8 == 0 && 256 % TPH == 0, "shape");
+    constexpr int HPB = 256 / TPH;
+    const int rh = blockIdx.x * HPB + threadIdx.x / TPH;   // r * H + h
+    if (rh >= RH) return;
+    const int r = rh / H, h = rh % H;
+    const int c = (threadIdx.x % TPH) * 8;
+    const float* pl = part_lse + (int64_t)r * nsplit * H + h;
+    float M = -__builtin_inff();
+    for (int i = 0; i < nsplit; ++i) M = fmaxf(M, pl[(int64_t)i * H]);
+    float acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+    float W = 0.f;
     if (M != -__builtin_inff()) {
         for (int i = 0; i < nsplit; ++i) {
-            const float li = part_lse[((int64_t)r * nsplit + i) * H + h];
-            const float wi = __expf(li - M);
+            const float wi = __expf(pl[(int64_t)i * H] - M);
             W += wi;
-            const float* po = part_o + (((int64_t)r * nsplit + i) * H + h) * DLAT;
-#pragma unroll
-            for (int j = 0; j < PER; ++j) {
-                const int c = threadIdx.x + 128 * j;
-                if (c < DLAT) acc[j] = fmaf(wi, po[c], acc[j]);
-            }
+            const f32x4* po = (const f32x4*)(part_o + (((int64_t)r * nsplit + i) * H + h) * DLAT + c);
+            const f32x4 v0 = po[0], v1 = po[1];
+            acc[0] = fmaf(wi, v0.x, acc[0]);
+            acc[1] = fmaf(wi, v0.y, acc[1]);
+            acc[2] = fmaf(wi, v0.z, acc[2]);
+            acc[3] = fmaf(wi, v0.w, acc[3]);
+            acc[4] = fmaf(wi, v1.x, acc[4]);
+            acc[5] = fmaf(wi, v1.y, acc[5]);
+            acc[6] = fmaf(wi, v1.z, acc[6]);
+            acc[7] = fmaf(wi, v1.w, acc[7]);
         }
     }
     const float inv = W > 0.f ? 1.f / W : 0.f;
+    bf16x8 v;
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        const int c = threadIdx.x + 128 * j;
-        if (c < DLAT) out[(int64_t)rh * DLAT + c] = (__bf16)(acc[j] * inv);
-    }
-    if (lse != nullptr && threadIdx.x == 0) lse[rh] = W > 0.f ? M + __logf(W) : -__builtin_inff();
+    for (int j = 0; j < 8; ++j) v[j] = (__bf16)(acc[j] * inv);
+    *(bf16x8*)(out + (int64_t)rh * DLAT + c) = v;
+    if (lse != nullptr && c == 0) lse[rh] = W > 0.f ? M + __logf(W) : -__builtin_inff();
 }
 
 // split heuristic shared with the workspace query ------------------------------
@@ -561,12 +954,18 @@ static hipError_t launch_sfa_t(const MlaDev& a, const SfaPlan& p, __bf16* out, f
                                float* part_lse, hipStream_t stream) {
     const int64_t units = (int64_t)a.R * p.nsplit;
     const int64_t nwg = (units + 7) / 8 * 8 * p.nhb;
-    hipLaunchKernelGGL((sfa_kernel<DLAT, DROPE, FP8, NHG>), dim3((unsigned)nwg), dim3(128 * NHG), 0, stream, a,
-                       p.kps, p.nsplit, p.nhb, out, lse, part_o, part_lse);
+    if constexpr (!FP8 && ((DLAT + DROPE) * 2) % 128 == 0)
+        hipLaunchKernelGGL((sfa_bf16_kernel<DLAT, DROPE, NHG>), dim3((unsigned)nwg), dim3(128 * NHG), 0, stream,
+                           a, p.kps, p.nsplit, p.nhb, out, lse, part_o, part_lse);
+    else
+        hipLaunchKernelGGL((sfa_kernel<DLAT, DROPE, FP8, NHG>), dim3((unsigned)nwg), dim3(128 * NHG), 0, stream, a,
+                           p.kps, p.nsplit, p.nhb, out, lse, part_o, part_lse);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.nsplit == 1) return e;
-    hipLaunchKernelGGL((sfa_combine_kernel<DLAT>), dim3((unsigned)(a.R * a.H)), dim3(128), 0, stream, part_o,
-                       part_lse, p.nsplit, a.H, out, lse);
+    constexpr int HPB = 256 / (DLAT / 8);
+    const int RH = a.R * a.H;
+    hipLaunchKernelGGL((sfa_combine_kernel<DLAT>), dim3((unsigned)((RH + HPB - 1) / HPB)), dim3(256), 0, stream,
+                       part_o, part_lse, p.nsplit, a.H, RH, out, lse);
     return hipGetLastError();
 }
 
