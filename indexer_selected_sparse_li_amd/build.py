@@ -32,6 +32,7 @@ FLAGS = [
 # accumulators would be copied back and forth every tile).
 FILE_FLAGS = {
     "sparse_mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "li_score.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 
 

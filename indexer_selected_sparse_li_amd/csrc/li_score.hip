@@ -30,6 +30,7 @@ constexpr int kLiMaxBlocks = 512;  // block-table entries one workgroup may touc
 constexpr int kLiNbuf = 4;         // tiles in the LDS ring
 
 __device__ __attribute__((aligned(16))) uint8_t g_li_zero16[16];
+__device__ __attribute__((aligned(16))) uint8_t g_li_zero_row[256];   // stands in for unaddressable key rows
 __device__ float g_li_one = 1.0f;
 __device__ float g_li_nan = __builtin_nanf("");
 
@@ -270,6 +271,166 @@ __global__ __launch_bounds__(512) void li_score_kernel(IndexerDev a, float* __re
     }
 }
 
+// Decode (one query row per sequence, bf16 keys) -------------------------------
+//
+// Each key row is scored against a single query, so nothing is gained by
+// staging tiles in LDS: every wavefront streams its own 16-key subtiles from
+// HBM straight into MFMA B-operand registers, kLiPrefetch subtiles ahead, and
+// the workgroup shares only the block map.  Lane l of a subtile loads, for
+// K-step ks, the 16 bytes of key row l % 16 holding elements ks * 32 + 8 (l / 16)
+// .. + 8, the same layout the query operand uses, so S[heads, keys] comes out
+// of v_mfma_f32_16x16x32_bf16 exactly as in li_score_kernel.  Key rows are
+// read once, with non-temporal loads.
+constexpr int kLiDecWaves = 4;      // wavefronts per workgroup
+constexpr int kLiPrefetch = 4;      // subtiles in flight per wavefront
+
+template <int DI, int MT>
+__global__ __launch_bounds__(64 * kLiDecWaves) void li_score_dec_kernel(IndexerDev a, float* __restrict__ scores,
+                                                                     int64_t ld, int keys_per_wg) {
+    constexpr int KS = DI / 32;
+    constexpr int NT = 64 * kLiDecWaves;
+    constexpr int P = kLiPrefetch;
+    __shared__ int64_t blk_slot0[kLiMaxBlocks];
+    __shared__ int32_t blk_lim[kLiMaxBlocks];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = blockIdx.y;
+    const int64_t c0 = (int64_t)blockIdx.x * keys_per_wg;
+    int64_t vis = (int64_t)a.row_pos[r] + 1;
+    if (vis < 0) vis = 0;
+    if (vis > ld) vis = ld;
+    const int64_t kend = (c0 + keys_per_wg < vis) ? c0 + keys_per_wg : vis;
+    if (c0 >= kend) return;  // uniform across the workgroup
+    const int seq = a.row_seq[r];
+
+    // block map of [c0, kend) (contiguous caches: virtual 64-token blocks)
+    const bool seq_ok = seq >= 0 && seq < a.k.num_seqs;
+    const int sh = a.k.paged ? a.k.bs_shift : 6;
+    const int64_t bsz = (int64_t)1 << sh;
+    const int64_t b0 = c0 >> sh;
+    {
+        const int nb = (int)(((kend - 1) >> sh) - b0 + 1);
+        for (int i = tid; i < nb; i += NT) {
+            const int64_t blk = b0 + i;
+            int64_t s0 = -1;
+            if (seq_ok) {
+                if (a.k.paged) {
+                    if (blk < a.k.bt_stride) {
+                        const int32_t b = a.k.block_table[(int64_t)seq * a.k.bt_stride + blk];
+                        if (b >= 0) s0 = (int64_t)b << sh;
+                    }
+                } else {
+                    s0 = a.k.seq_base[seq] + blk * bsz;
+                }
+            }
+            int64_t lim = 0;
+            if (s0 >= 0 && s0 < a.k.num_slots) {
+                lim = a.k.num_slots - s0;
+                lim = lim < bsz ? lim : bsz;
+            }
+            blk_slot0[i] = s0;
+            blk_lim[i] = (int32_t)lim;
+        }
+    }
+
+    // query operand (row = head l % 16 of M-tile mt, 8 elements of K-step ks)
+    // and head weights in the accumulator layout (4 heads per M-tile)
+    const int g = lane >> 4;
+    bf16x8 qa[MT][KS];
+    float wv[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int head = mt * 16 + (lane & 15);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (head < a.H_I)
+                qa[mt][ks] = *(const bf16x8*)(a.q + (((int64_t)r * a.H_I + head) * DI + ks * 32 + g * 8) * 2);
+            else
+                qa[mt][ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int h = mt * 16 + 4 * g + i;
+            wv[mt][i] = h < a.H_I ? a.w[(int64_t)r * a.H_I + h] : 0.f;
+        }
+    }
+    __syncthreads();  // block map ready
+
+    // subtiles of this wave: u = wave, wave + W, ... over [c0, kend)
+    const int nsub = (int)((kend - c0 + 15) / 16);
+    const int mine = nsub > wave ? (nsub - wave + kLiDecWaves - 1) / kLiDecWaves : 0;
+    // address of lane's key row in subtile i of this wave (zero row if the
+    // position is past the row or not addressable) and its score factor
+    auto locate = [&](int i, const uint8_t*& gp, float& fac) {
+        const int64_t key = c0 + (int64_t)(wave + i * kLiDecWaves) * 16 + (lane & 15);
+        gp = g_li_zero_row + g * 16;
+        fac = __builtin_nanf("");
+        if (i < mine && key < kend) {
+            const int bi = (int)((key >> sh) - b0);
+            const int off = (int)(key & (bsz - 1));
+            if (off < blk_lim[bi]) {
+                gp = a.k.data + (blk_slot0[bi] + off) * a.k.row_stride + g * 16;
+                fac = 1.f;
+            }
+        }
+    };
+    static_assert(DI * 2 <= 256, "zero row covers one key row");
+    auto fetch = [&](const uint8_t* gp, bf16x8 (&kb)[KS]) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kb[ks] = __builtin_nontemporal_load((const bf16x8*)(gp + ks * 64));
+    };
+
+    bf16x8 kbuf[P][KS];
+    float fac[P];
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+        const uint8_t* gp;
+        locate(j, gp, fac[j]);
+        fetch(gp, kbuf[j]);
+    }
+    // whole groups of P subtiles: those past this wave's share score the
+    // zero row and their stores are masked
+    for (int i0 = 0; i0 < mine; i0 += P) {
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            const int i = i0 + j;
+            f32x4 acc[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma16x16x32_bf16(qa[mt][ks], kbuf[j][ks], acc[mt]);
+            const float f = fac[j];
+            // refill this slot with subtile i + P
+            {
+                const uint8_t* gp;
+                locate(i + P, gp, fac[j]);
+                fetch(gp, kbuf[j]);
+            }
+            // ReLU as an integer max on the bit pattern (negative floats,
+            // -0.0 included, are negative integers; +0.0 is 0)
+            float part = 0.f;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int bits = __float_as_int(acc[mt][q]);
+                    part = fmaf(wv[mt][q], __int_as_float(bits > 0 ? bits : 0), part);
+                }
+            {
+                const auto w16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+                part = __uint_as_float(w16[0]) + __uint_as_float(w16[1]);
+                const auto w32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+                part = __uint_as_float(w32[0]) + __uint_as_float(w32[1]);
+            }
+            const int64_t key = c0 + (int64_t)(wave + i * kLiDecWaves) * 16 + lane;
+            if (lane < 16 && key < kend) scores[(int64_t)r * ld + key] = part * f;
+        }
+    }
+}
+
 // host-side launcher ---------------------------------------------------------
 
 template <int DI, int MT, int QG, bool FP8>
@@ -298,9 +459,40 @@ static hipError_t launch_li(const IndexerDev& a, float* scores, int64_t ld, int6
     return hipGetLastError();
 }
 
+template <int DI, int MT>
+static hipError_t launch_li_dec(const IndexerDev& a, float* scores, int64_t ld, int64_t max_visible,
+                                hipStream_t stream) {
+    const int sh = a.k.paged ? a.k.bs_shift : 6;
+    const int64_t bsz = (int64_t)1 << sh;
+    // about two four-wave workgroups per CU in total
+    const int64_t want_wg = 512;
+    int64_t nchunk = (want_wg + a.R - 1) / a.R;
+    int64_t kpw = (max_visible + nchunk - 1) / nchunk;
+    if (kpw < 1024) kpw = 1024;
+    const int64_t align = bsz > 64 ? bsz : 64;   // chunks start on block boundaries
+    kpw = (kpw + align - 1) / align * align;
+    const int64_t cap = (int64_t)(kLiMaxBlocks - 1) * bsz / align * align;
+    if (kpw > cap) kpw = cap;
+    if (kpw > (1 << 30)) kpw = (int64_t)(1 << 30) / align * align;
+    nchunk = (max_visible + kpw - 1) / kpw;
+    if (nchunk < 1) nchunk = 1;
+    dim3 grid((unsigned)nchunk, (unsigned)a.R);
+    hipLaunchKernelGGL((li_score_dec_kernel<DI, MT>), grid, dim3(64 * kLiDecWaves), 0, stream, a, scores, ld,
+                       (int)kpw);
+    return hipGetLastError();
+}
+
 hipError_t li_score_dispatch(const IndexerDev& a, int D_I, int fp8, int qg, float* scores, int64_t ld,
                              int64_t max_visible, hipStream_t stream) {
     const int mt = a.H_I <= 16 ? 1 : (a.H_I <= 32 ? 2 : 4);
+    if (qg == 1 && fp8 == 0) {
+        if (D_I == 128 && mt == 4) return launch_li_dec<128, 4>(a, scores, ld, max_visible, stream);
+        if (D_I == 128 && mt == 2) return launch_li_dec<128, 2>(a, scores, ld, max_visible, stream);
+        if (D_I == 128 && mt == 1) return launch_li_dec<128, 1>(a, scores, ld, max_visible, stream);
+        if (D_I == 32 && mt == 4) return launch_li_dec<32, 4>(a, scores, ld, max_visible, stream);
+        if (D_I == 32 && mt == 2) return launch_li_dec<32, 2>(a, scores, ld, max_visible, stream);
+        if (D_I == 32 && mt == 1) return launch_li_dec<32, 1>(a, scores, ld, max_visible, stream);
+    }
 #define LISFA_LI_CASE(DI_, MT_, QG_, F8_)                                                    \
     if (D_I == DI_ && mt == MT_ && qg == QG_ && (fp8 != 0) == F8_)                            \
         return launch_li<DI_, MT_, QG_, F8_>(a, scores, ld, max_visible, stream);
