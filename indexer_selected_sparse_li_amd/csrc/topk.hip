@@ -3,21 +3,19 @@
 // selected indices; "Large Language Model Inference Acceleration in
 // Practice", section 3.1: Top-K on chip generating index pointers).
 //
-// One workgroup of 1024 threads (16 wavefronts) per query row.
-//  1. Scores map to order-preserving uint32 keys (-0.0 folded onto +0.0).
-//  2. A min/max reduction gives the key range; selection then works on
-//     d = key - kmin, whose top bit is that of the range.
-//  3. Radix select on d from its top bit down in digits of at most 13 bits:
-//     an LDS histogram of the values that match the prefix chosen so far,
-//     then a block-wide suffix scan locates the digit holding the K-th
-//     largest value (usually two levels for fp32 scores).
-//     At the end T is the K-th largest key and `need` is how many keys equal
-//     to T are taken (the rest of the K are strictly greater than T).
-//  4. Ordered emission: per 1024-position chunk, each wavefront's ballots of
-//     "key > T" and "key == T" give counts; a block scan over (chunk, wave)
-//     in position order gives every selected position its output slot, so
-//     the list comes out ascending and ties at T go to the lowest positions.
-// Every step is integer counting, so the result is deterministic.
+// One workgroup of 1024 threads (16 wavefronts) per query row.  Scores map to
+// order-preserving uint32 keys (-0.0 folded onto +0.0); selection is a radix
+// select on d = key - kmin (so the first digit starts at the top bit of the
+// row's range) followed by an ordered emission that writes the selected
+// positions in ascending order, ties at the K-th value going to the lowest
+// positions.  Every step is integer counting, so the result is deterministic.
+//  * topk_reg_kernel (rows up to 64K positions): thread t keeps the keys of
+//    positions [t * EPT, t * EPT + EPT) in registers; one histogram level
+//    runs over all keys, later levels only over the threshold bin's keys once
+//    they fit in LDS; the emission is a single block scan of per-thread
+//    (greater, equal) counts.
+//  * topk_kernel<0> (longer rows): keys are re-read from global memory on
+//    every pass; emission per 1024-position chunk from wavefront ballots.
 #include "common.hpp"
 
 namespace lisfa {
@@ -240,6 +238,231 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(const float* __restric
     }
 }
 
+// Exclusive block-wide scan of one 64-bit value per thread; also returns the total.
+__device__ __forceinline__ uint64_t block_excl_scan64(uint64_t v, uint64_t* wsum, uint64_t& total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint64_t x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint64_t y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    if (wave == 0) {
+        uint64_t t = lane < kTkWaves ? wsum[lane] : 0ull;
+#pragma unroll
+        for (int o = 1; o < kTkWaves; o <<= 1) {
+            const uint64_t y = __shfl_up(t, o);
+            if (lane >= o) t += y;
+        }
+        if (lane < kTkWaves) wsum[lane] = t;
+    }
+    __syncthreads();
+    const uint64_t before = wave ? wsum[wave - 1] : 0ull;
+    total = wsum[kTkWaves - 1];
+    __syncthreads();
+    return before + x - v;
+}
+
+constexpr int kTkCandMax = 2048;   // threshold-bin candidates kept in LDS
+
+struct TkShared {
+    uint32_t hist[kTkBins];
+    uint32_t cand[kTkCandMax];
+    uint64_t wsum64[kTkWaves];
+    uint32_t wsum[kTkWaves];
+    uint32_t red[2 * kTkWaves];
+    uint32_t digit, above, ncand;
+};
+
+// Selection core shared by the Top-K kernels.  The block holds keys kr[c],
+// c < nv, of thread t at list index t * EPT + c (the list order is the
+// position order).  Selects the K largest keys, ties to the lower index, and
+// calls emit(c, slot) for every selected key with its output slot (list
+// order), for K < number of valid keys.
+//  * min / max key, then radix select on d = key - kmin from the top bit of
+//    the range in digits of at most 13 bits (LDS histogram + block scan).
+//    The first level runs over all keys; once the bin holding the K-th value
+//    has at most kTkCandMax keys, their d values move to LDS and the remaining
+//    levels histogram only them.  T is the K-th largest key, `need` the number
+//    of keys equal to T that are taken.
+//  * Emission: one block scan of each thread's (greater than T, equal to T)
+//    counts gives its first slot; equal keys are taken while their rank among
+//    equals is below `need`.
+template <int EPT, typename Emit>
+__device__ __forceinline__ void tk_select(TkShared& sh, const uint32_t (&kr)[EPT], int nv, uint32_t K,
+                                          Emit&& emit) {
+    static_assert(EPT <= 64, "keys per thread");
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+    for (int c = 0; c < EPT; ++c) {
+        if (c < nv) {
+            kmin = kr[c] < kmin ? kr[c] : kmin;
+            kmax = kr[c] > kmax ? kr[c] : kmax;
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const uint32_t x = __shfl_xor(kmin, o), y = __shfl_xor(kmax, o);
+        kmin = x < kmin ? x : kmin;
+        kmax = y > kmax ? y : kmax;
+    }
+    if (lane == 0) {
+        sh.red[wave] = kmin;
+        sh.red[kTkWaves + wave] = kmax;
+    }
+    if (tid == 0) sh.ncand = 0u;
+    __syncthreads();
+    kmin = sh.red[0];
+    kmax = sh.red[kTkWaves];
+#pragma unroll
+    for (int w = 1; w < kTkWaves; ++w) {
+        kmin = sh.red[w] < kmin ? sh.red[w] : kmin;
+        kmax = sh.red[kTkWaves + w] > kmax ? sh.red[kTkWaves + w] : kmax;
+    }
+
+    uint32_t need = K;
+    uint32_t T;
+    const uint32_t range = kmax - kmin;
+    if (range == 0u) {
+        T = kmin;
+    } else {
+        int hi = 31 - __clz(range);
+        uint32_t prefix = 0u;       // chosen high digits of d
+        bool compact = false;       // the remaining candidates are in sh.cand
+        uint32_t ncand = 0u;
+        while (true) {
+            const int lo = hi - (kTkDigitBits - 1) > 0 ? hi - (kTkDigitBits - 1) : 0;
+            const uint32_t mask = (1u << (hi - lo + 1)) - 1u;
+#pragma unroll
+            for (int j = 0; j < kTkBins / kTkThreads; ++j) sh.hist[tid + j * kTkThreads] = 0u;
+            __syncthreads();
+            if (!compact) {
+#pragma unroll
+                for (int c = 0; c < EPT; ++c) {
+                    const uint32_t d = kr[c] - kmin;
+                    const bool match = hi == 31 ? true : ((d ^ prefix) >> (hi + 1)) == 0u;
+                    if (c < nv && match) atomicAdd(&sh.hist[(d >> lo) & mask], 1u);
+                }
+            } else {
+                for (uint32_t i = tid; i < ncand; i += kTkThreads) {
+                    const uint32_t d = sh.cand[i];
+                    if (((d ^ prefix) >> (hi + 1)) == 0u) atomicAdd(&sh.hist[(d >> lo) & mask], 1u);
+                }
+            }
+            __syncthreads();
+            // thread t owns the kTkBins / 1024 consecutive bins counted from the top
+            constexpr int PB = kTkBins / kTkThreads;
+            uint32_t cb[PB], loc = 0u;
+#pragma unroll
+            for (int j = 0; j < PB; ++j) {
+                cb[j] = sh.hist[kTkBins - 1 - (tid * PB + j)];
+                loc += cb[j];
+            }
+            uint32_t tot;
+            uint32_t E = block_excl_scan(loc, sh.wsum, tot);
+            if (E < need && need <= E + loc) {
+#pragma unroll
+                for (int j = 0; j < PB; ++j) {
+                    if (E < need && need <= E + cb[j]) {
+                        sh.digit = (uint32_t)(kTkBins - 1 - (tid * PB + j));
+                        sh.above = E;
+                    }
+                    E += cb[j];
+                }
+            }
+            __syncthreads();
+            const uint32_t dg = sh.digit;
+            const uint32_t inbin = sh.hist[dg];
+            need -= sh.above;
+            prefix |= dg << lo;
+            if (lo == 0) break;
+            // keys sharing all digits chosen so far: move them to LDS once few enough
+            if (!compact && inbin <= (uint32_t)kTkCandMax) {
+#pragma unroll
+                for (int c = 0; c < EPT; ++c) {
+                    const uint32_t d = kr[c] - kmin;
+                    if (c < nv && ((d ^ prefix) >> lo) == 0u) sh.cand[atomicAdd(&sh.ncand, 1u)] = d;
+                }
+                compact = true;
+                ncand = inbin;
+            }
+            __syncthreads();
+            hi = lo - 1;
+        }
+        T = kmin + prefix;
+    }
+    const uint32_t need_eq = need;
+
+    uint64_t gtm = 0ull, eqm = 0ull;
+#pragma unroll
+    for (int c = 0; c < EPT; ++c) {
+        if (c < nv) {
+            gtm |= (uint64_t)(kr[c] > T) << c;
+            eqm |= (uint64_t)(kr[c] == T) << c;
+        }
+    }
+    const uint64_t cnt = ((uint64_t)__popcll(eqm) << 32) | (uint64_t)__popcll(gtm);
+    uint64_t total;
+    const uint64_t ex = block_excl_scan64(cnt, sh.wsum64, total);
+    uint32_t rg = (uint32_t)ex, re = (uint32_t)(ex >> 32);
+#pragma unroll
+    for (int c = 0; c < EPT; ++c) {
+        const bool gt = (gtm >> c) & 1ull, eq = (eqm >> c) & 1ull;
+        if (gt) {
+            emit(c, rg + (re < need_eq ? re : need_eq));
+            ++rg;
+        } else if (eq) {
+            if (re < need_eq) emit(c, rg + re);
+            ++re;
+        }
+    }
+}
+
+// keys of positions [base, base + EPT) of row s (n valid positions in total)
+template <int EPT>
+__device__ __forceinline__ int tk_load(const float* s, bool vec, int64_t base, int64_t n, uint32_t (&kr)[EPT]) {
+    const int nv = n - base >= EPT ? EPT : (n > base ? (int)(n - base) : 0);
+    if (vec && nv == EPT) {
+#pragma unroll
+        for (int c = 0; c < EPT; c += 4) {
+            const f32x4 v = *(const f32x4*)(s + base + c);
+            kr[c] = float_key(v.x);
+            kr[c + 1] = float_key(v.y);
+            kr[c + 2] = float_key(v.z);
+            kr[c + 3] = float_key(v.w);
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < EPT; ++c) kr[c] = c < nv ? float_key(s[base + c]) : 0u;
+    }
+    return nv;
+}
+
+// One workgroup per row; thread t owns positions [t * EPT, t * EPT + EPT).
+template <int EPT>
+__global__ __launch_bounds__(kTkThreads) void topk_reg_kernel(const float* __restrict__ scores, int64_t ld,
+                                                              const int32_t* __restrict__ row_pos, int K,
+                                                              int32_t* __restrict__ idx) {
+    __shared__ TkShared sh;
+    const int r = blockIdx.x, tid = threadIdx.x;
+    int32_t* out = idx + (int64_t)r * K;
+    int64_t n = (int64_t)row_pos[r] + 1;
+    if (n < 0) n = 0;
+    if (n > ld) n = ld;
+    if (n <= K) {
+        for (int64_t i = tid; i < K; i += kTkThreads) out[i] = i < n ? (int32_t)i : -1;
+        return;
+    }
+    const bool vec = ((ld & 3) == 0) && ((((uintptr_t)scores) & 15) == 0);
+    const int64_t base = (int64_t)tid * EPT;
+    uint32_t kr[EPT];
+    const int nv = tk_load<EPT>(scores + (int64_t)r * ld, vec, base, n, kr);
+    tk_select<EPT>(sh, kr, nv, (uint32_t)K, [&](int c, uint32_t slot) { out[slot] = (int32_t)(base + c); });
+}
+
 hipError_t topk_dispatch(const float* scores, int64_t ld, const int32_t* row_pos, int R, int K,
                          int32_t* idx, hipStream_t stream) {
     if (R <= 0) return hipSuccess;
@@ -248,12 +471,16 @@ hipError_t topk_dispatch(const float* scores, int64_t ld, const int32_t* row_pos
 #define LISFA_TK(E_)                                                                               \
     hipLaunchKernelGGL((topk_kernel<E_>), dim3((unsigned)R), dim3(kTkThreads), 0, stream, scores, ld, \
                        row_pos, K, idx)
-    if (ept <= 8) LISFA_TK(8);
-    else if (ept <= 16) LISFA_TK(16);
-    else if (ept <= 32) LISFA_TK(32);
-    else if (ept <= 64) LISFA_TK(64);
+#define LISFA_TKR(E_)                                                                              \
+    hipLaunchKernelGGL((topk_reg_kernel<E_>), dim3((unsigned)R), dim3(kTkThreads), 0, stream, scores, ld,  \
+                       row_pos, K, idx)
+    if (ept <= 8) LISFA_TKR(8);
+    else if (ept <= 16) LISFA_TKR(16);
+    else if (ept <= 32) LISFA_TKR(32);
+    else if (ept <= 64) LISFA_TKR(64);
     else LISFA_TK(0);
 #undef LISFA_TK
+#undef LISFA_TKR
     return hipGetLastError();
 }
 
