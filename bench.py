@@ -86,30 +86,46 @@ def stored_traffic(stage: str, workload: str):
     return d.get("hbm_bytes_per_launch")
 
 
-def pmc_per_dispatch(csv_path: str, counter: str, kernel_substr: str):
+# kernels one call of each stage launches (name substrings)
+STAGE_KERNELS = {
+    "li_score": ["li_score"],
+    "topk_select": ["topk"],
+    "sparse_mla_attn": ["sfa_w8_kernel", "sfa_bf16_kernel", "sfa_kernel<", "sfa_combine_kernel"],
+}
+
+
+def pmc_per_dispatch(csv_path: str, counter: str, kernel_substrs):
+    """Sum over the stage's kernels of the median per-dispatch counter value."""
     import csv
-    vals = []
+    per = {}
     with open(csv_path) as fh:
         for row in csv.DictReader(fh):
-            if row["Counter_Name"] == counter and kernel_substr in row["Kernel_Name"]:
-                vals.append(float(row["Counter_Value"]))
-    if not vals:
-        raise SystemExit(f"no {counter} rows for {kernel_substr} in {csv_path}")
-    vals.sort()
-    return vals[len(vals) // 2], len(vals)
+            if row["Counter_Name"] != counter:
+                continue
+            for k in kernel_substrs:
+                if k in row["Kernel_Name"]:
+                    per.setdefault(k, []).append(float(row["Counter_Value"]))
+                    break
+    if not per:
+        raise SystemExit(f"no {counter} rows for {kernel_substrs} in {csv_path}")
+    total, n = 0.0, 0
+    for vals in per.values():
+        vals.sort()
+        total += vals[len(vals) // 2]
+        n = max(n, len(vals))
+    return total, n, sorted(per)
 
 
 def write_traffic_summary(args):
     """Turn four rocprofv3 --pmc CSVs (kernel FETCH_SIZE / WRITE_SIZE, copy
     FETCH_SIZE / WRITE_SIZE) into a profiles/ summary with the scaled bytes."""
     stage, wl_name = args.stage, args.workload
-    kname = {"li_score": "li_score_kernel", "topk_select": "topk_kernel",
-             "sparse_mla_attn": "sfa_kernel"}[stage]
     copy_bytes = args.copy_bytes
-    kf, nkf = pmc_per_dispatch(args.fetch_csv, "FETCH_SIZE", kname)
-    kw, nkw = pmc_per_dispatch(args.write_csv, "WRITE_SIZE", kname)
-    cf, _ = pmc_per_dispatch(args.copy_fetch_csv, "FETCH_SIZE", "")
-    cw, _ = pmc_per_dispatch(args.copy_write_csv, "WRITE_SIZE", "")
+    kf, nkf, knames = pmc_per_dispatch(args.fetch_csv, "FETCH_SIZE", STAGE_KERNELS[stage])
+    kw, nkw, _ = pmc_per_dispatch(args.write_csv, "WRITE_SIZE", STAGE_KERNELS[stage])
+    cf, _, _ = pmc_per_dispatch(args.copy_fetch_csv, "FETCH_SIZE", [""])
+    cw, _, _ = pmc_per_dispatch(args.copy_write_csv, "WRITE_SIZE", [""])
+    kname = " + ".join(k.rstrip("<") for k in knames)
     f_scale = copy_bytes / (cf * 1024.0)
     w_scale = copy_bytes / (cw * 1024.0)
     fetch = kf * 1024.0 * f_scale
@@ -121,7 +137,8 @@ def write_traffic_summary(args):
     path = traffic_path(stage, wl_name)
     with open(path, "w") as fh:
         fh.write(f"# HBM traffic of {stage} ({kname}) on {wl_name}\n\n")
-        fh.write("Median per dispatch over the profiled launches, rocprofv3 --pmc counters in KiB.\n")
+        fh.write("Median per dispatch over the profiled launches (summed over the kernels one call\n"
+                 "of the stage launches), rocprofv3 --pmc counters in KiB.\n")
         fh.write("Each counter is scaled by what it reads for a plain device copy of known size\n")
         fh.write(f"(torch copy of {copy_bytes} bytes: expected = copy_bytes / 1024 KiB).\n\n")
         fh.write("Commands (run from the repository root on the GPU box):\n\n")
