@@ -1025,7 +1025,6 @@ __global__ __launch_bounds__(512) void sfa_w8_kernel(MlaDev a, int kps, int nspl
         const float c = a.scale_log2;
         f32x4v s_cur[2] = {f32x4v{0.f, 0.f, 0.f, 0.f}, f32x4v{0.f, 0.f, 0.f, 0.f}};
         constexpr int PF = 4;   // QK^T operand reads in flight
-        constexpr int PD = 2;   // PV: M-tiles of operands in flight
 
         auto qk = [&](const lds_u8* T, f32x4v (&s)[2]) {
             s[0] = f32x4v{0.f, 0.f, 0.f, 0.f};
@@ -1162,30 +1161,37 @@ __global__ __launch_bounds__(512) void sfa_w8_kernel(MlaDev a, int kps, int nspl
             qk_groups(QB, 2 * NKS);
             __builtin_amdgcn_sched_barrier(0);
 
-            // Phase 2, PV(t), transpose reads PD M-tiles ahead
-            s16x4 rb[PD + 1][2];
+            // Phase 2, PV(t), in two batches of MH M-tiles.  While direct-to-LDS
+            // loads are outstanding the compiler waits for every pending LDS
+            // read before an MFMA whose operands are pending, so the operands
+            // come in batches: the second batch's reads go out right after the
+            // first MFMA and fly under the rest of the first batch.
+            constexpr int MH = MTV / 2;
+            s16x4 ra[MH][2], rc[MH][2];
 #pragma unroll
-            for (int m = 0; m < PD; ++m)
+            for (int m = 0; m < MH; ++m)
 #pragma unroll
-                for (int h = 0; h < 2; ++h) rb[m][h] = trd(T, m, h);
-#pragma unroll
-            for (int mt = 0; mt < MTV; ++mt) {
-                if (mt + PD < MTV) {
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) rb[(mt + PD) % (PD + 1)][h] = trd(T, mt + PD, h);
-                }
-                const u32x2 lo = __builtin_bit_cast(u32x2, rb[mt % (PD + 1)][0]);
-                const u32x2 hi = __builtin_bit_cast(u32x2, rb[mt % (PD + 1)][1]);
+                for (int h = 0; h < 2; ++h) ra[m][h] = trd(T, m, h);
+            auto pv_step = [&](int mt, const s16x4 (&v)[2]) {
+                const u32x2 lo = __builtin_bit_cast(u32x2, v[0]);
+                const u32x2 hi = __builtin_bit_cast(u32x2, v[1]);
                 const u32x4 w = {lo.x, lo.y, hi.x, hi.y};
                 o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w), pb, o[mt], 0, 0, 0);
-            }
-            put_partial(s_next, (t + 1) & 1);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2 * PD, 0);
+            };
+            pv_step(0, ra[0]);
 #pragma unroll
-            for (int mt = 0; mt < MTV; ++mt) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (mt + PD < MTV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-            }
+            for (int m = 0; m < MH; ++m)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) rc[m][h] = trd(T, MH + m, h);
+#pragma unroll
+            for (int m = 1; m < MH; ++m) pv_step(m, ra[m]);
+#pragma unroll
+            for (int m = 0; m < MH; ++m) pv_step(MH + m, rc[m]);
+            put_partial(s_next, (t + 1) & 1);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * MH, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * MH, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, MTV - 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
             __builtin_amdgcn_sched_barrier(0);
             s_cur[0] = s_next[0];
