@@ -9,3 +9,7 @@ from .lisfa_oracle import (  # noqa: F401
     indexer_query, mla_query, indexer_scores, select_topk, sparse_mla,
     layer_row, attend_row, scores_row,
 )
+from .cp_oracle import (  # noqa: F401
+    shard_candidates, merge_candidates, combine_partials, zigzag_segments,
+    zigzag_share, zigzag_order, zigzag_restore,
+)
