@@ -24,6 +24,7 @@ sys.path.insert(0, ROOT)
 METRIC = "sparse-attn layer tokens/s (indexer+TopK+SFA) at L=32K; % of HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0
 
 
 def log(*a):
@@ -32,18 +33,28 @@ def log(*a):
 
 def algorithmic(wl, b):
     """Algorithmic bytes / flops per launch of each stage (what the method must
-    move or compute; the dense attention it avoids is not counted)."""
+    move or compute; the dense attention it avoids is not counted).  Cached
+    keys and latent rows count once per sequence: rows of one sequence share
+    them (prefill), and the union of a sequence's selected rows is bounded by
+    both the selections and the visible context."""
     R = b.R
-    vis = sum(int(p) + 1 for p in b.row_pos.tolist())
+    pos = [int(p) for p in b.row_pos.tolist()]
+    seq = [int(s) for s in b.row_seq.tolist()]
     ke = 1 if wl.indexer_dtype == "fp8" else 2
     ks = 4 if wl.indexer_dtype == "fp8" else 0
     ve = 1 if wl.kv_dtype == "fp8" else 2
-    sel = sum(min(wl.K, int(p) + 1) for p in b.row_pos.tolist())
-    li_bytes = vis * (wl.D_I * ke + ks) + R * wl.H_I * (wl.D_I * ke + 4)
+    vs = 4 if wl.kv_dtype == "fp8" else 0
+    vis = sum(p + 1 for p in pos)
+    sel = sum(min(wl.K, p + 1) for p in pos)
+    seq_vis, seq_sel = {}, {}
+    for s, p in zip(seq, pos):
+        seq_vis[s] = max(seq_vis.get(s, 0), p + 1)
+        seq_sel[s] = seq_sel.get(s, 0) + min(wl.K, p + 1)
+    keys = sum(seq_vis.values())
+    rows = sum(min(seq_sel[s], seq_vis[s]) for s in seq_vis)
+    li_bytes = keys * (wl.D_I * ke + ks) + R * (wl.H_I * (wl.D_I * ke + 4) + ks)
     li_flops = 2.0 * wl.H_I * wl.D_I * vis
-    sfa_bytes = sel * (wl.D_qk * ve) + R * wl.H * (wl.D_qk * 2 + wl.D_v * 2 + 4)
-    if wl.kv_dtype == "fp8":
-        sfa_bytes += sel * 4
+    sfa_bytes = rows * (wl.D_qk * ve + vs) + R * wl.H * (wl.D_qk * 2 + wl.D_v * 2 + 4) + sel * 4
     sfa_flops = 2.0 * wl.H * sel * (wl.D_qk + wl.D_v)
     topk_bytes = vis * 4 + R * wl.K * 4
     return dict(li=(li_bytes, li_flops), topk=(topk_bytes, 0.0), sfa=(sfa_bytes, sfa_flops))
@@ -149,18 +160,90 @@ def write_traffic_summary(args):
           f"(fetch scale {f_scale:.3f}, write scale {w_scale:.3f})")
 
 
-def time_on_stream(fn, stream, warmup, steps):
+def write_mfma_summary(args):
+    """Turn one rocprofv3 --pmc CSV (SQ_INSTS_VALU_MFMA_MOPS_BF16, _F8, and the
+    derived MfmaUtil) into a profiles/ summary of MFMA work and utilisation."""
+    import csv
+    stage, wl_name = args.stage, args.workload
+    per = {}
+    with open(args.mfma_csv) as fh:
+        for row in csv.DictReader(fh):
+            for k in STAGE_KERNELS[stage]:
+                if k in row["Kernel_Name"]:
+                    d = per.setdefault(k, {})
+                    d.setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+                    dur = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) * 1e-3
+                    d.setdefault("_us", []).append(dur)
+                    break
+    if not per:
+        raise SystemExit(f"no rows for {STAGE_KERNELS[stage]} in {args.mfma_csv}")
+
+    def med(v):
+        v = sorted(v)
+        return v[len(v) // 2]
+
+    rows = []
+    for k, d in sorted(per.items()):
+        us = med(d["_us"])
+        bf = med(d.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", [0.0])) * 512
+        f8 = med(d.get("SQ_INSTS_VALU_MFMA_MOPS_F8", [0.0])) * 512
+        util = med(d["MfmaUtil"]) if "MfmaUtil" in d else None
+        tf = (bf + f8) / (us * 1e-6) / 1e12 if us > 0 else 0.0
+        pk = (bf / BF16_PEAK_TFLOPS + f8 / FP8_PEAK_TFLOPS) / max(bf + f8, 1.0)   # 1/TFLOP-weighted peak
+        frac = tf * pk if bf + f8 > 0 else 0.0
+        rows.append(dict(kernel=k.rstrip("<"), dispatch_us=round(us, 2), mfma_bf16_flop=int(bf),
+                         mfma_fp8_flop=int(f8), achieved_tflops=round(tf, 2), frac_of_peak=round(frac, 4),
+                         mfma_busy_pct=None if util is None else round(util, 2)))
+    path = os.path.join(ROOT, "profiles", f"{stage}_{wl_name}_mfma.md")
+    with open(path, "w") as fh:
+        fh.write(f"# MFMA work and utilisation of {stage} on {wl_name}\n\n")
+        fh.write("Median per dispatch, rocprofv3 --pmc. Flops = SQ_INSTS_VALU_MFMA_MOPS_* x 512 (rocprofv3's\n"
+                 "MfmaFlops definition); dispatch time from the same run's timestamps (counter collection\n"
+                 "serialises dispatches, so it runs slightly long); peak 2.5 PFLOP/s bf16, 5.0 fp8 dense.\n"
+                 "mfma_busy_pct is rocprofv3's derived MfmaUtil (MFMA-busy cycles over active cycles x SIMDs).\n\n")
+        fh.write("Command (run from the repository root on the GPU box):\n\n")
+        for c in args.commands or []:
+            fh.write(f"    {c}\n")
+        fh.write("\n| kernel | us | bf16 MFMA GFLOP | fp8 MFMA GFLOP | TFLOP/s | % of MFMA peak | MFMA busy % |\n")
+        fh.write("|---|---|---|---|---|---|---|\n")
+        for r in rows:
+            fh.write(f'| {r["kernel"]} | {r["dispatch_us"]} | {r["mfma_bf16_flop"] / 1e9:.2f} | '
+                     f'{r["mfma_fp8_flop"] / 1e9:.2f} | {r["achieved_tflops"]} | {r["frac_of_peak"] * 100:.1f} | '
+                     f'{r["mfma_busy_pct"]} |\n')
+        fh.write("\n```json\n" + json.dumps(dict(stage=stage, workload=wl_name, source_hash=source_hash(stage),
+                                                  kernels=rows), indent=1) + "\n```\n")
+    print(f"wrote {path}")
+
+
+def time_on_stream(fn, stream, warmup, steps, graph=False):
+    """Seconds per call of fn(stream).  With graph=True the calls are captured
+    into one HIP graph first, so the time excludes the host's per-call cost."""
     import torch
     for _ in range(warmup):
-        fn()
+        fn(stream)
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(steps):
-        fn()
-    end.record(stream)
-    torch.cuda.synchronize()
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            st = torch.cuda.current_stream()
+            for _ in range(steps):
+                fn(st)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            g.replay()
+            start.record(stream)
+            g.replay()
+            end.record(stream)
+        torch.cuda.synchronize()
+        del g
+    else:
+        start.record(stream)
+        for _ in range(steps):
+            fn(stream)
+        end.record(stream)
+        torch.cuda.synchronize()
     return start.elapsed_time(end) / steps * 1e-3  # seconds per call
 
 
@@ -209,9 +292,17 @@ def main():
     ap.add_argument("--copy-fetch-csv")
     ap.add_argument("--copy-write-csv")
     ap.add_argument("--commands", nargs="*")
+    ap.add_argument("--report-all", action="store_true",
+                    help="time every workload (hot and cold), one JSON line each")
+    ap.add_argument("--write-mfma-summary", action="store_true")
+    ap.add_argument("--mfma-csv")
+    ap.add_argument("--report-md", help="with --report-all: write a markdown table here")
     args = ap.parse_args()
     if args.write_traffic_summary:
         write_traffic_summary(args)
+        return
+    if args.write_mfma_summary:
+        write_mfma_summary(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -232,7 +323,26 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] copied {args.copy_bytes} bytes x {args.steps}")
         return
+    if args.report_all:
+        report_all(args)
+        return
     wl = W.get(args.workload)
+    res, b = run_workload(args, wl)
+    if res is None:
+        return
+    if not args.no_cpu_baseline:
+        log("[bench] cpu oracle baseline")
+        res["cpu_baseline"] = cpu_baseline(b, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+def run_workload(args, wl, cold=False, graph=False):
+    """Generate one workload on the GPU and time the layer and its stages.
+    Returns (result dict, batch); (None, batch) in the profiling modes."""
+    import torch
+    import indexer_selected_sparse_li_amd as lisfa
+    import workloads as W
+
     log(f"[bench] generating {wl.name} on the GPU")
     b = W.make_batch(wl, device="cuda")
     torch.cuda.synchronize()
@@ -249,10 +359,13 @@ def main():
                      device="cuda")
     stream = torch.cuda.current_stream()
 
-    def step():
+    def step_on(st):
         lisfa.li_topk_sfa(b.q_idx, b.w, kc, b.q, vc, b.row_seq, b.row_pos, wl.K, b.max_visible, out, lse,
                           idx_out=idx, q_scale=b.q_scale, rows_per_group=rpg,
-                          softmax_scale=wl.softmax_scale, workspace=ws, stream=stream)
+                          softmax_scale=wl.softmax_scale, workspace=ws, stream=st)
+
+    def step():
+        step_on(stream)
 
     if args.only:
         ld_o = (b.max_visible + 63) // 64 * 64
@@ -275,7 +388,7 @@ def main():
             fns[args.only]()
         torch.cuda.synchronize()
         log(f"[bench] ran {args.only} x {args.warmup + args.steps}")
-        return
+        return None, b
 
     # the whole layer, timed: barrier + synchronize on both sides
     log(f"[bench] warmup {args.warmup}, timed {args.steps}")
@@ -295,21 +408,46 @@ def main():
     value = R / (ms_step * 1e-3)
     log(f"[bench] layer {ms_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us)")
 
+    ms_cold = None
+    if cold:
+        # each step after a 512 MiB write, which evicts the L2s and the 256 MB MALL
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for i, (e0, e1) in enumerate(evs):
+            flush.fill_(i & 255)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        ms_cold = sum(e0.elapsed_time(e1) for e0, e1 in evs) / args.steps
+        del flush
+        log(f"[bench] layer cold {ms_cold * 1e3:.1f} us/step")
+
+    ms_graph = None
+    if graph:
+        ms_graph = graph_replay_ms(step_on, (idx, out, lse), stream, args.steps)
+        log(f"[bench] layer graph replay {ms_graph * 1e3:.1f} us/step")
+
     # stages on their own, same stream, same inputs
     ss = args.stage_steps or args.steps
     ld = (b.max_visible + 63) // 64 * 64
     scores = torch.empty(R, ld, dtype=torch.float32, device="cuda")
     sfa_ws = torch.empty(max(1, lisfa.workspace_size(1, R, 0, wl.K, wl.H, wl.D_v)), dtype=torch.uint8,
                          device="cuda")
-    t_li = time_on_stream(lambda: lisfa.li_score(b.q_idx, b.w, kc, b.row_seq, b.row_pos, scores,
-                                                 b.max_visible, q_scale=b.q_scale, rows_per_group=rpg,
-                                                 stream=stream), stream, 2, ss)
-    t_tk = time_on_stream(lambda: lisfa.topk_select(scores, b.row_pos, wl.K, idx, stream=stream),
-                          stream, 2, ss)
-    t_sfa = time_on_stream(lambda: lisfa.sparse_mla_attn(b.q, vc, b.row_seq, idx, out, lse,
-                                                         softmax_scale=wl.softmax_scale, workspace=sfa_ws,
-                                                         stream=stream), stream, 2, ss)
+    t_li = time_on_stream(lambda st: lisfa.li_score(b.q_idx, b.w, kc, b.row_seq, b.row_pos, scores,
+                                                    b.max_visible, q_scale=b.q_scale, rows_per_group=rpg,
+                                                    stream=st), stream, 2, ss, graph)
+    t_tk = time_on_stream(lambda st: lisfa.topk_select(scores, b.row_pos, wl.K, idx, stream=st),
+                          stream, 2, ss, graph)
+    t_sfa = time_on_stream(lambda st: lisfa.sparse_mla_attn(b.q, vc, b.row_seq, idx, out, lse,
+                                                            softmax_scale=wl.softmax_scale, workspace=sfa_ws,
+                                                            stream=st), stream, 2, ss, graph)
     alg = algorithmic(wl, b)
+
+    def peak_tflops(name):
+        # the indexer's contraction runs on fp8 MFMA for fp8 keys; sparse MLA always on bf16 MFMA
+        return FP8_PEAK_TFLOPS if (name == "li" and wl.indexer_dtype == "fp8") else BF16_PEAK_TFLOPS
 
     def roof(name, t, bound):
         by, fl = alg[name]
@@ -318,14 +456,14 @@ def main():
             return dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                         frac=round(ach / HBM_PEAK_GBS, 4))
         ach = fl / t / 1e12
-        return dict(bound="mfma", achieved=round(ach, 2), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=round(ach / BF16_PEAK_TFLOPS, 4))
+        pk = peak_tflops(name)
+        return dict(bound="mfma", achieved=round(ach, 2), peak=pk, unit="TFLOP/s", frac=round(ach / pk, 4))
 
     def bound_of(name):
         by, fl = alg[name]
         if name == "topk" or fl == 0:
             return "hbm"
-        return "mfma" if fl / max(by, 1) > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9) else "hbm"
+        return "mfma" if fl / max(by, 1) > peak_tflops(name) * 1e12 / (HBM_PEAK_GBS * 1e9) else "hbm"
 
     stages = {}
     for name, t in (("li_score", t_li), ("topk_select", t_tk), ("sparse_mla_attn", t_sfa)):
@@ -351,10 +489,104 @@ def main():
         "roofline": roofline,
         "stages": stages,
     }
-    if not args.no_cpu_baseline:
-        log("[bench] cpu oracle baseline")
-        res["cpu_baseline"] = cpu_baseline(b, args.cpu_budget)
-    print(json.dumps(res), flush=True)
+    if ms_cold is not None:
+        res["ms_per_step_cold"] = round(ms_cold, 4)
+        res["value_cold"] = round(R / (ms_cold * 1e-3), 1)
+    if ms_graph is not None:
+        res["ms_per_step_graph"] = round(ms_graph, 4)
+        res["value_graph"] = round(R / (ms_graph * 1e-3), 1)
+    return res, b
+
+
+def graph_replay_ms(step_on, outs, stream, steps):
+    """Capture one layer call into a HIP graph and time its replays.  Every
+    replay is checked bit for bit against the eager result first (the kernels
+    are deterministic), with eager work and synchronizations in between."""
+    import torch
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        step_on(side)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step_on(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    for i in range(3):
+        for t in outs:
+            t.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for t, r in zip(outs, ref):
+            if not torch.equal(t.view(torch.uint8) if t.dtype == torch.bfloat16 else t,
+                               r.view(torch.uint8) if r.dtype == torch.bfloat16 else r):
+                raise SystemExit(f"graph replay {i} differs from the eager call")
+        step_on(stream)
+        torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        g.replay()
+        ev0.record(stream)
+        for _ in range(steps):
+            g.replay()
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    del g
+    return ms
+
+
+def report_all(args):
+    """Every workload of the registry, one JSON line each (hot and cold layer
+    timings, per-stage times and rooflines); optionally a markdown table."""
+    import torch
+    import workloads as W
+    lines = []
+    for name in REPORT_ORDER:
+        wl = W.get(name)
+        res, b = run_workload(args, wl, cold=True, graph=True)
+        del b
+        torch.cuda.empty_cache()
+        lines.append(res)
+        print(json.dumps(res), flush=True)
+    if args.report_md:
+        write_report_md(args.report_md, lines, args)
+
+
+REPORT_ORDER = ["tiny_l256", "decode_l8192", "batched_paged_64x4k_32k", "prefill_4096q_l65536",
+                "fp8_decode_16x131072", "decode_paged_1x32768", "decode_paged_64x32768"]
+
+
+def write_report_md(path, lines, args):
+    def st(r, k):
+        s = r["stages"][k]
+        rf = s["roofline"]
+        return f'{s["us"]:.1f} ({rf["frac"] * 100:.1f} % {rf["bound"].upper()})'
+    with open(path, "w") as fh:
+        fh.write("# Layer throughput on every workload (one MI355X)\n\n")
+        fh.write("HIP-event timings on the launch stream; a step is one li_topk_sfa call over the whole batch.\n"
+                 "Cold = each step after a 512 MiB write that evicts the L2s and the MALL; hot = back-to-back\n"
+                 "calls from Python; graph = the same call captured once in a HIP graph and replayed (no\n"
+                 "host overhead per call; every replay checked against the eager result first).\n"
+                 "Stage times are hot, each stage launched on its own (graph-captured); the fraction is of the stage's binding\n"
+                 "roofline (HBM 8 TB/s; MFMA bf16 2.5 PFLOP/s, fp8 5.0) on algorithmic bytes or flops.\n\n")
+        fh.write("Command (from the repository root):\n\n")
+        fh.write(f"    python3 bench.py --report-all --steps {args.steps} --warmup {args.warmup} "
+                 f"--report-md {os.path.relpath(path, ROOT)}\n\n")
+        fh.write("| workload | rows | layer cold us | tokens/s cold | layer hot us | tokens/s hot | "
+                 "graph replay us | tokens/s graph | li_score us | topk_select us | sparse_mla_attn us |\n")
+        fh.write("|---|---|---|---|---|---|---|---|---|---|---|\n")
+        for r in lines:
+            fh.write(f'| {r["config"]["workload"]} | {r["config"]["rows"]} | '
+                     f'{r["ms_per_step_cold"] * 1e3:.1f} | {r["value_cold"]:.0f} | '
+                     f'{r["ms_per_step"] * 1e3:.1f} | {r["value"]:.0f} | '
+                     f'{r["ms_per_step_graph"] * 1e3:.1f} | {r["value_graph"]:.0f} | '
+                     f'{st(r, "li_score")} | {st(r, "topk_select")} | {st(r, "sparse_mla_attn")} |\n')
+    log(f"[bench] wrote {path}")
 
 
 if __name__ == "__main__":

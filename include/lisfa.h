@@ -139,13 +139,64 @@ int li_score(const lisfa_indexer_args* args, float* scores, int64_t ld_scores,
  *   scores: [R, ld_scores] fp32; row r uses entries 0..row_pos[r] (clamped to
  *           ld_scores - 1; a negative row_pos selects nothing).
  *   idx:    [R, K] int32 out, ascending positions, -1 padded.
+ *   ws:     lisfa_workspace_size(LISFA_OP_TOPK, R, ld_scores, K, 0, 0) bytes
+ *           (16-byte aligned), or NULL.  The size is 0 unless ld_scores >
+ *           65536 and K * ceil(ld_scores / 16384) <= 16384; such rows are then
+ *           selected in two passes (slices of 16384 positions keep their own
+ *           Top-K, an ordered merge picks the K best).  Otherwise, or with ws
+ *           NULL, long rows take a slower single-workgroup pass.
  * Exact: the order is that of the fp32 values (-0.0 == +0.0; NaN orders above
  * +inf); equal values at the K-th place go to the lower positions.  The result
- * is deterministic.  Needs no workspace (ws may be NULL, ws_bytes 0).
+ * is deterministic and the same on every path.
  */
 int topk_select(const float* scores, int64_t ld_scores, const int32_t* row_pos,
                 int32_t R, int32_t K, int32_t* idx, void* ws, size_t ws_bytes,
                 lisfa_stream_t stream);
+
+/*
+ * Context parallelism: the cached positions of a sequence are split over G
+ * GPUs; each GPU scores its own positions, keeps its local Top-K with the
+ * scores, the candidates of all GPUs are gathered and merged into the
+ * global index list, each GPU attends over the selected rows it holds, and
+ * the G partial results are merged by their log-sum-exp (the Kimi K3 decode
+ * article, in Japanese, part 1 item 1: with decode context parallelism each
+ * GPU attends over its own region of the KV cache and a fused kernel merges
+ * the partial results; "Day0 Inference Adaptation and Performance
+ * Optimization for Kimi K3.1 Pro", section 5: context parallelism splits
+ * long inputs along the sequence).  The gathers between GPUs are the
+ * caller's (RCCL); these entry points are one GPU's share.  Every globally
+ * selected position is among its own shard's local Top-K, so the merged
+ * list equals the single-GPU topk_select result on the same scores.
+ *
+ * topk_candidates - local Top-K of one shard with scores.
+ *   scores, ld_scores, row_pos: as topk_select, over the shard's local
+ *           positions (local position t = logical position t + pos_offset[r]).
+ *   pos_offset: [R] int32 or NULL (0).
+ *   cand_pos:   [R, K] int32 out: logical positions, ascending, -1 padded.
+ *   cand_score: [R, K] fp32 out: their scores (-inf for padding).
+ *   ws: lisfa_workspace_size(LISFA_OP_TOPK_CANDIDATES, R, ld_scores, K, 0, 0)
+ *       bytes (needed only when ld_scores > 65536; K * ceil(ld / 16384) must
+ *       then be <= 16384, else LISFA_ERR_UNSUPPORTED).
+ */
+int topk_candidates(const float* scores, int64_t ld_scores, const int32_t* row_pos,
+                    int32_t R, int32_t K, const int32_t* pos_offset, int32_t* cand_pos,
+                    float* cand_score, void* ws, size_t ws_bytes, lisfa_stream_t stream);
+
+/*
+ * topk_merge - the K best of n gathered candidates per row.
+ *   cand_score, cand_pos: [R, ld_cand] (first n entries used); a negative
+ *           position marks no candidate.  Positions of a row must be unique.
+ *   ordered: nonzero if the valid candidates of each row come in ascending
+ *           position order (the local lists of a contiguous split gathered in
+ *           rank order); any order is accepted with ordered = 0 (then K <=
+ *           4096).  n <= 16384.
+ *   idx:    [R, K] int32 out, ascending positions, -1 padded.
+ *   idx_score: [R, K] fp32 out (their scores, -inf padding) or NULL.
+ * Order: larger score first, equal scores toward the lower position.
+ */
+int topk_merge(const float* cand_score, const int32_t* cand_pos, int64_t ld_cand,
+               int32_t R, int32_t n, int32_t K, int32_t ordered, int32_t* idx,
+               float* idx_score, lisfa_stream_t stream);
 
 /*
  * sparse_mla_attn - sparse flash attention over the selected rows
@@ -166,6 +217,53 @@ int sparse_mla_attn(const lisfa_mla_args* args, const int32_t* idx, int32_t K,
                     lisfa_stream_t stream);
 
 /*
+ * sparse_mla_attn_partial - one shard's share of sparse attention, as fp32
+ * partial results for lse_combine.
+ *   args: the shard's latent cache addresses its own rows: local position t
+ *         of row r's sequence is logical position range[2r] + t.
+ *   idx:  [R, K] int32 logical positions (the merged list); entries outside
+ *         [range[2r], range[2r+1]) are skipped.  range = NULL: idx already
+ *         holds local positions.
+ *   out:  [R, H, D_latent] fp32 normalised output (16-byte aligned).
+ *   lse:  [R, H] fp32 natural-log normaliser (required).
+ *   ws:   lisfa_workspace_size(LISFA_OP_SPARSE_MLA_PARTIAL, R, 0, K, H,
+ *         D_latent) bytes, 256-byte aligned.
+ * A row with no selected row in the shard gets out = 0 and lse = -inf.
+ */
+int sparse_mla_attn_partial(const lisfa_mla_args* args, const int32_t* idx, int32_t K,
+                            const int32_t* range, float* out, float* lse,
+                            void* ws, size_t ws_bytes, lisfa_stream_t stream);
+
+/*
+ * lse_combine - merge G partial attention results of the same rows:
+ *   M = max_g lse_g,  a_g = exp(lse_g - M),
+ *   out = sum_g a_g out_g / sum_g a_g,  lse = M + log(sum_g a_g).
+ *   part_out: [G, R, H, D_v] fp32 (16-byte aligned); part_lse: [G, R, H].
+ *   out: [R, H, D_v] bf16 (16-byte aligned); lse: [R, H] fp32 or NULL.
+ *   D_v: 64 or 512.  Parts with lse = -inf hold no row; a head with no row
+ *   in any part gets out = 0 and lse = -inf.
+ */
+int lse_combine(const float* part_out, const float* part_lse, int32_t G, int32_t R,
+                int32_t H, int32_t D_v, void* out, float* lse, lisfa_stream_t stream);
+
+/*
+ * Zigzag partition for context-parallel prefill ("Day0 Inference Adaptation
+ * and Performance Optimization for a New Model", section 5.2, and the Kimi
+ * K3.1 Pro page, section 5): n rows are cut into 2G segments, segment i =
+ * [floor(i n / 2G), floor((i+1) n / 2G)); GPU g takes segment g and segment
+ * 2G-1-g, so each GPU pairs a short causal history with a long one.
+ *
+ * lisfa_zigzag_share (host function): ranges[0..4) = the two [start, end)
+ *   ranges of GPU g, head segment first.
+ * zigzag_restore: src holds the gathered shares (GPU 0's two segments, then
+ *   GPU 1's, ...), n rows of row_bytes bytes; dst receives them in original
+ *   order.  src and dst must not overlap.
+ */
+int lisfa_zigzag_share(int64_t n, int32_t G, int32_t g, int64_t* ranges);
+int zigzag_restore(const void* src, void* dst, int64_t n, int32_t G, int64_t row_bytes,
+                   lisfa_stream_t stream);
+
+/*
  * li_topk_sfa - the whole layer in one call on one stream: scores, Top-K and
  * sparse attention ("Day0 Inference Adaptation and Performance Optimization
  * for Kimi K3.1 Pro", section 3, and "Large Language Model Inference
@@ -181,9 +279,11 @@ int li_topk_sfa(const lisfa_indexer_args* iargs, const lisfa_mla_args* margs,
                 int32_t K, int32_t* idx_out, void* out, float* lse,
                 void* ws, size_t ws_bytes, lisfa_stream_t stream);
 
-#define LISFA_OP_TOPK        0
-#define LISFA_OP_SPARSE_MLA  1
-#define LISFA_OP_FUSED       2
+#define LISFA_OP_TOPK               0   /* max_visible argument = ld_scores */
+#define LISFA_OP_SPARSE_MLA         1
+#define LISFA_OP_FUSED              2
+#define LISFA_OP_TOPK_CANDIDATES    3   /* max_visible argument = ld_scores */
+#define LISFA_OP_SPARSE_MLA_PARTIAL 4
 
 /* Workspace bytes an entry point needs for the given sizes (host function). */
 size_t lisfa_workspace_size(int32_t op, int32_t R, int64_t max_visible, int32_t K,

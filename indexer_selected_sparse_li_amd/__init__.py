@@ -10,6 +10,12 @@ Entry points (same names as the C ABI):
   topk_select(...)     per-row Top-K index lists [R, K] int32
   sparse_mla_attn(...) sparse MLA attention      [R, H, D_latent] bf16 (+ lse)
   li_topk_sfa(...)     all three in one call on one stream
+One GPU's share of a context-parallel split:
+  topk_candidates(...)         local Top-K of a shard as (position, score) pairs
+  topk_merge(...)              the K best of the gathered candidates
+  sparse_mla_attn_partial(...) fp32 partial attention over the shard's rows
+  lse_combine(...)             log-sum-exp merge of the gathered partials
+  zigzag_share(...), zigzag_restore(...)  Zigzag partition of prefill rows
 """
 from __future__ import annotations
 
@@ -22,7 +28,8 @@ import torch
 from . import _lib as _c
 
 __all__ = ["KVCache", "LisfaError", "li_score", "topk_select", "sparse_mla_attn", "li_topk_sfa",
-           "workspace_size", "load", "status_string"]
+           "topk_candidates", "topk_merge", "sparse_mla_attn_partial", "lse_combine", "zigzag_share",
+           "zigzag_restore", "workspace_size", "load", "status_string"]
 
 
 class LisfaError(RuntimeError):
@@ -149,13 +156,48 @@ def li_score(q_idx, w, k_cache: KVCache, row_seq, row_pos, scores, max_visible: 
     return scores
 
 
-def topk_select(scores, row_pos, K: int, idx, stream=None):
+def topk_select(scores, row_pos, K: int, idx, workspace=None, stream=None):
     """idx[r] = ascending positions of the K largest scores[r, :row_pos[r]+1], -1 padded."""
     lib = _c.load()
     if idx.dtype != torch.int32 or tuple(idx.shape) != (scores.shape[0], K):
         raise ValueError("idx must be [R, K] int32")
-    _check(lib.topk_select(_ptr(scores), scores.shape[1], _ptr(row_pos), scores.shape[0], K, _ptr(idx),
-                           None, 0, _stream(stream)), "topk_select")
+    R, ld = scores.shape
+    need = lib.lisfa_workspace_size(_c.LISFA_OP_TOPK, R, ld, K, 0, 0)
+    ws = _workspace(workspace, need, scores.device)
+    _check(lib.topk_select(_ptr(scores), ld, _ptr(row_pos), R, K, _ptr(idx),
+                           _ptr(ws) if (ws is not None and need) else None, need, _stream(stream)),
+           "topk_select")
+    return idx
+
+
+def topk_candidates(scores, row_pos, K: int, cand_pos, cand_score, pos_offset=None, workspace=None,
+                    stream=None):
+    """Local Top-K of one context shard: (logical position, score) pairs,
+    positions ascending, (-1, -inf) padded; local position t of row r is
+    logical position t + pos_offset[r]."""
+    lib = _c.load()
+    R, ld = scores.shape
+    for t, dt in ((cand_pos, torch.int32), (cand_score, torch.float32)):
+        if t.dtype != dt or tuple(t.shape) != (R, K):
+            raise ValueError(f"candidate outputs must be [R, K] {dt}")
+    need = lib.lisfa_workspace_size(_c.LISFA_OP_TOPK_CANDIDATES, R, ld, K, 0, 0)
+    ws = _workspace(workspace, need, scores.device)
+    _check(lib.topk_candidates(_ptr(scores), ld, _ptr(row_pos), R, K, _ptr(pos_offset), _ptr(cand_pos),
+                               _ptr(cand_score), _ptr(ws) if (ws is not None and need) else None, need,
+                               _stream(stream)), "topk_candidates")
+    return cand_pos, cand_score
+
+
+def topk_merge(cand_score, cand_pos, K: int, idx, idx_score=None, ordered: bool = False, stream=None):
+    """The K best of each row's gathered candidates ([R, n]); ascending positions."""
+    lib = _c.load()
+    R, n = cand_pos.shape
+    if cand_score.shape != cand_pos.shape or cand_score.dtype != torch.float32 or cand_pos.dtype != torch.int32:
+        raise ValueError("candidates must be [R, n] fp32 scores and int32 positions")
+    if idx.dtype != torch.int32 or tuple(idx.shape) != (R, K):
+        raise ValueError("idx must be [R, K] int32")
+    _check(lib.topk_merge(_ptr(cand_score), _ptr(cand_pos), n, R, n, K, int(ordered), _ptr(idx),
+                          _ptr(idx_score), _stream(stream)), "topk_merge")
     return idx
 
 
@@ -173,6 +215,57 @@ def sparse_mla_attn(q, kv_cache: KVCache, row_seq, idx, out, lse=None, softmax_s
                                _ptr(ws) if ws is not None else None, need, _stream(stream)),
            "sparse_mla_attn")
     return out, lse
+
+
+def sparse_mla_attn_partial(q, kv_cache: KVCache, row_seq, idx, out, lse, shard_range=None,
+                            softmax_scale: float = None, workspace=None, stream=None):
+    """fp32 partial attention of one context shard over the rows of idx
+    (logical positions) inside shard_range[r] = (lo, hi); kv_cache addresses
+    the shard's rows by local position (logical - lo)."""
+    lib = _c.load()
+    R, H, D_qk = q.shape
+    D_latent = out.shape[2]
+    K = idx.shape[1]
+    if out.dtype != torch.float32 or lse is None or lse.dtype != torch.float32:
+        raise ValueError("partial outputs are fp32 out [R, H, D_latent] and lse [R, H]")
+    a = _mla_args(q, kv_cache, row_seq, D_latent, softmax_scale)
+    need = lib.lisfa_workspace_size(_c.LISFA_OP_SPARSE_MLA_PARTIAL, R, 0, K, H, D_latent)
+    ws = _workspace(workspace, need, q.device)
+    _check(lib.sparse_mla_attn_partial(ctypes.byref(a), _ptr(idx), K, _ptr(shard_range), _ptr(out), _ptr(lse),
+                                       _ptr(ws) if ws is not None else None, need, _stream(stream)),
+           "sparse_mla_attn_partial")
+    return out, lse
+
+
+def lse_combine(part_out, part_lse, out, lse=None, stream=None):
+    """Merge G partial results [G, R, H, D] (fp32, with lse [G, R, H]) into out [R, H, D] bf16."""
+    lib = _c.load()
+    G, R, H, D = part_out.shape
+    if part_out.dtype != torch.float32 or part_lse.dtype != torch.float32 or tuple(part_lse.shape) != (G, R, H):
+        raise ValueError("partials must be fp32 [G, R, H, D] and [G, R, H]")
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != (R, H, D):
+        raise ValueError("out must be [R, H, D] bf16")
+    _check(lib.lse_combine(_ptr(part_out), _ptr(part_lse), G, R, H, D, _ptr(out), _ptr(lse), _stream(stream)),
+           "lse_combine")
+    return out, lse
+
+
+def zigzag_share(n: int, G: int, g: int):
+    """The two [start, end) row ranges GPU g of G takes under the Zigzag partition."""
+    r = (ctypes.c_int64 * 4)()
+    _check(_c.load().lisfa_zigzag_share(n, G, g, r), "lisfa_zigzag_share")
+    return [(r[0], r[1]), (r[2], r[3])]
+
+
+def zigzag_restore(src, dst, G: int, stream=None):
+    """dst[t] = row t in original order, from src holding the gathered shares."""
+    lib = _c.load()
+    if src.shape != dst.shape or src.dtype != dst.dtype:
+        raise ValueError("src and dst must have the same shape and dtype")
+    n = src.shape[0]
+    row_bytes = src[0].numel() * src.element_size() if n else 0
+    _check(lib.zigzag_restore(_ptr(src), _ptr(dst), n, G, row_bytes, _stream(stream)), "zigzag_restore")
+    return dst
 
 
 def li_topk_sfa(q_idx, w, k_cache: KVCache, q, kv_cache: KVCache, row_seq, row_pos, K: int,

@@ -21,9 +21,13 @@ LISFA_FP8_E4M3 = 1
 LISFA_OP_TOPK = 0
 LISFA_OP_SPARSE_MLA = 1
 LISFA_OP_FUSED = 2
+LISFA_OP_TOPK_CANDIDATES = 3
+LISFA_OP_SPARSE_MLA_PARTIAL = 4
 
 EXPORTS = (
     "li_score", "topk_select", "sparse_mla_attn", "li_topk_sfa",
+    "topk_candidates", "topk_merge", "sparse_mla_attn_partial", "lse_combine",
+    "lisfa_zigzag_share", "zigzag_restore",
     "lisfa_workspace_size", "lisfa_status_string", "lisfa_struct_size", "lisfa_abi_version",
 )
 
@@ -97,6 +101,18 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.li_topk_sfa.argtypes = [ctypes.POINTER(IndexerArgs), ctypes.POINTER(MlaArgs), i32, vp, vp, vp,
                                 vp, sz, vp]
     lib.li_topk_sfa.restype = ctypes.c_int
+    lib.topk_candidates.argtypes = [vp, i64, vp, i32, i32, vp, vp, vp, vp, sz, vp]
+    lib.topk_candidates.restype = ctypes.c_int
+    lib.topk_merge.argtypes = [vp, vp, i64, i32, i32, i32, i32, vp, vp, vp]
+    lib.topk_merge.restype = ctypes.c_int
+    lib.sparse_mla_attn_partial.argtypes = [ctypes.POINTER(MlaArgs), vp, i32, vp, vp, vp, vp, sz, vp]
+    lib.sparse_mla_attn_partial.restype = ctypes.c_int
+    lib.lse_combine.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp]
+    lib.lse_combine.restype = ctypes.c_int
+    lib.lisfa_zigzag_share.argtypes = [i64, i32, i32, ctypes.POINTER(ctypes.c_int64)]
+    lib.lisfa_zigzag_share.restype = ctypes.c_int
+    lib.zigzag_restore.argtypes = [vp, vp, i64, i32, i64, vp]
+    lib.zigzag_restore.restype = ctypes.c_int
     lib.lisfa_workspace_size.argtypes = [i32, i32, i64, i32, i32, i32]
     lib.lisfa_workspace_size.restype = sz
     lib.lisfa_status_string.argtypes = [i32]

@@ -9,10 +9,25 @@ namespace lisfa {
 hipError_t li_score_dispatch(const IndexerDev& a, int D_I, int fp8, int qg, float* scores, int64_t ld,
                              int64_t max_visible, hipStream_t stream);
 hipError_t topk_dispatch(const float* scores, int64_t ld, const int32_t* row_pos, int R, int K,
-                         int32_t* idx, hipStream_t stream);
-hipError_t sfa_dispatch(const MlaDev& a, int D_latent, int fp8, __bf16* out, float* lse, void* ws,
+                         int32_t* idx, void* ws, hipStream_t stream);
+hipError_t topk_candidates_dispatch(const float* scores, int64_t ld, const int32_t* row_pos, int R, int K,
+                                    const int32_t* pos_offset, int32_t* cand_pos, float* cand_score, void* ws,
+                                    hipStream_t stream);
+hipError_t topk_merge_dispatch(const float* cand_score, const int32_t* cand_pos, int64_t ldc, int R, int n, int K,
+                               int ordered, int32_t* idx, float* idx_score, hipStream_t stream);
+int topk_slices(int64_t ld, int K);
+size_t topk_workspace_bytes(int R, int64_t ld, int K);
+hipError_t sfa_dispatch(const MlaDev& a, int D_latent, int fp8, __bf16* out, float* out_f32, float* lse, void* ws,
                         hipStream_t stream);
 size_t sfa_workspace_bytes(int R, int K, int H, int D_latent);
+hipError_t sfa_partial_dispatch(const MlaDev& a, const int32_t* range, int D_latent, int fp8, float* out_f32,
+                                float* lse, void* ws, hipStream_t stream);
+size_t sfa_partial_workspace_bytes(int R, int K, int H, int D_latent, int with_range);
+hipError_t lse_combine_dispatch(const float* part_o, const float* part_lse, int G, int R, int H, int D, __bf16* out,
+                                float* lse, hipStream_t stream);
+hipError_t zigzag_restore_dispatch(const void* src, void* dst, int64_t n, int G, int64_t row_bytes,
+                                   hipStream_t stream);
+void zigzag_share_ranges(int64_t n, int G, int g, int64_t* r4);
 
 namespace {
 
@@ -133,7 +148,7 @@ int64_t fused_chunk_rows(int32_t R, int64_t max_visible) {
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 struct FusedLayout {
-    size_t scores, idx, sfa, total;
+    size_t scores, idx, cand, sfa, total;
 };
 
 FusedLayout fused_layout(int32_t R, int64_t max_visible, int32_t K, int32_t H, int32_t D_latent) {
@@ -141,7 +156,8 @@ FusedLayout fused_layout(int32_t R, int64_t max_visible, int32_t K, int32_t H, i
     const int64_t rc = fused_chunk_rows(R, max_visible);
     L.scores = 0;
     L.idx = align256((size_t)rc * scores_ld(max_visible) * sizeof(float));
-    L.sfa = L.idx + align256((size_t)R * K * sizeof(int32_t));
+    L.cand = L.idx + align256((size_t)R * K * sizeof(int32_t));
+    L.sfa = L.cand + align256(topk_workspace_bytes((int)rc, scores_ld(max_visible), K));
     L.total = L.sfa + align256(sfa_workspace_bytes(R, K, H, D_latent));
     return L;
 }
@@ -181,9 +197,11 @@ size_t lisfa_workspace_size(int32_t op, int32_t R, int64_t max_visible, int32_t 
                             int32_t D_latent) {
     if (R < 0 || K < 1) return 0;
     switch (op) {
-        case LISFA_OP_TOPK: return 0;
+        case LISFA_OP_TOPK:
+        case LISFA_OP_TOPK_CANDIDATES: return topk_workspace_bytes(R, max_visible, K);
         case LISFA_OP_SPARSE_MLA: return sfa_workspace_bytes(R, K, H, D_latent);
         case LISFA_OP_FUSED: return fused_layout(R, max_visible, K, H, D_latent).total;
+        case LISFA_OP_SPARSE_MLA_PARTIAL: return sfa_partial_workspace_bytes(R, K, H, D_latent, 1);
         default: return 0;
     }
 }
@@ -202,12 +220,42 @@ int li_score(const lisfa_indexer_args* args, float* scores, int64_t ld_scores, l
 
 int topk_select(const float* scores, int64_t ld_scores, const int32_t* row_pos, int32_t R, int32_t K,
                 int32_t* idx, void* ws, size_t ws_bytes, lisfa_stream_t stream) {
-    (void)ws;
-    (void)ws_bytes;
     if (R < 0 || K < 1 || ld_scores < 1) return LISFA_ERR_BAD_SHAPE;
     if (R == 0) return LISFA_OK;
     if (!scores || !row_pos || !idx) return LISFA_ERR_NULL_ARG;
-    return hip_status(topk_dispatch(scores, ld_scores, row_pos, R, K, idx, (hipStream_t)stream));
+    const size_t need = topk_workspace_bytes(R, ld_scores, K);
+    void* w = nullptr;
+    if (ws && need > 0) {
+        if (ws_bytes < need) return LISFA_ERR_WORKSPACE;
+        if (!aligned(ws, 16)) return LISFA_ERR_BAD_SHAPE;
+        w = ws;
+    }
+    return hip_status(topk_dispatch(scores, ld_scores, row_pos, R, K, idx, w, (hipStream_t)stream));
+}
+
+int topk_candidates(const float* scores, int64_t ld_scores, const int32_t* row_pos, int32_t R, int32_t K,
+                    const int32_t* pos_offset, int32_t* cand_pos, float* cand_score, void* ws, size_t ws_bytes,
+                    lisfa_stream_t stream) {
+    if (R < 0 || K < 1 || ld_scores < 1) return LISFA_ERR_BAD_SHAPE;
+    if (R == 0) return LISFA_OK;
+    if (!scores || !row_pos || !cand_pos || !cand_score) return LISFA_ERR_NULL_ARG;
+    if (ld_scores > 65536) {
+        if (topk_slices(ld_scores, K) == 0) return LISFA_ERR_UNSUPPORTED;
+        if (!ws || ws_bytes < topk_workspace_bytes(R, ld_scores, K)) return LISFA_ERR_WORKSPACE;
+        if (!aligned(ws, 16)) return LISFA_ERR_BAD_SHAPE;
+    }
+    return hip_status(topk_candidates_dispatch(scores, ld_scores, row_pos, R, K, pos_offset, cand_pos, cand_score,
+                                               ws, (hipStream_t)stream));
+}
+
+int topk_merge(const float* cand_score, const int32_t* cand_pos, int64_t ld_cand, int32_t R, int32_t n, int32_t K,
+               int32_t ordered, int32_t* idx, float* idx_score, lisfa_stream_t stream) {
+    if (R < 0 || K < 1 || n < 0 || ld_cand < n) return LISFA_ERR_BAD_SHAPE;
+    if (n > 16384 || (!ordered && K > 4096)) return LISFA_ERR_UNSUPPORTED;
+    if (R == 0) return LISFA_OK;
+    if (!idx || (n > 0 && (!cand_score || !cand_pos))) return LISFA_ERR_NULL_ARG;
+    return hip_status(topk_merge_dispatch(cand_score, cand_pos, ld_cand, R, n, K, ordered != 0, idx, idx_score,
+                                          (hipStream_t)stream));
 }
 
 int sparse_mla_attn(const lisfa_mla_args* args, const int32_t* idx, int32_t K, void* out, float* lse,
@@ -222,7 +270,52 @@ int sparse_mla_attn(const lisfa_mla_args* args, const int32_t* idx, int32_t K, v
     if (!aligned(out, 8)) return LISFA_ERR_BAD_SHAPE;
     const MlaDev d = to_dev(args, idx, K);
     return hip_status(sfa_dispatch(d, args->D_latent, args->kv_cache.dtype == LISFA_FP8_E4M3, (__bf16*)out,
-                                   lse, ws, (hipStream_t)stream));
+                                   nullptr, lse, ws, (hipStream_t)stream));
+}
+
+int sparse_mla_attn_partial(const lisfa_mla_args* args, const int32_t* idx, int32_t K, const int32_t* range,
+                            float* out, float* lse, void* ws, size_t ws_bytes, lisfa_stream_t stream) {
+    int e = check_mla(args);
+    if (e) return e;
+    if (K < 1) return LISFA_ERR_BAD_SHAPE;
+    if (args->R == 0) return LISFA_OK;
+    if (!idx || !out || !lse) return LISFA_ERR_NULL_ARG;
+    const size_t need = sfa_partial_workspace_bytes(args->R, K, args->H, args->D_latent, range != nullptr);
+    if (need > 0 && (!ws || ws_bytes < need)) return LISFA_ERR_WORKSPACE;
+    if (need > 0 && !aligned(ws, 256)) return LISFA_ERR_BAD_SHAPE;
+    if (!aligned(out, 16)) return LISFA_ERR_BAD_SHAPE;
+    const MlaDev d = to_dev(args, idx, K);
+    return hip_status(sfa_partial_dispatch(d, range, args->D_latent, args->kv_cache.dtype == LISFA_FP8_E4M3, out,
+                                           lse, ws, (hipStream_t)stream));
+}
+
+int lse_combine(const float* part_out, const float* part_lse, int32_t G, int32_t R, int32_t H, int32_t D_v,
+                void* out, float* lse, lisfa_stream_t stream) {
+    if (G < 1 || R < 0 || H < 1) return LISFA_ERR_BAD_SHAPE;
+    if (D_v != 64 && D_v != 512) return LISFA_ERR_UNSUPPORTED;
+    if ((int64_t)R * H > 0x7FFFFFFF) return LISFA_ERR_BAD_SHAPE;
+    if (R == 0) return LISFA_OK;
+    if (!part_out || !part_lse || !out) return LISFA_ERR_NULL_ARG;
+    if (!aligned(part_out, 16) || !aligned(out, 16)) return LISFA_ERR_BAD_SHAPE;
+    return hip_status(lse_combine_dispatch(part_out, part_lse, G, R, H, D_v, (__bf16*)out, lse, (hipStream_t)stream));
+}
+
+int lisfa_zigzag_share(int64_t n, int32_t G, int32_t g, int64_t* ranges) {
+    if (!ranges) return LISFA_ERR_NULL_ARG;
+    if (n < 0 || G < 1 || g < 0 || g >= G) return LISFA_ERR_BAD_SHAPE;
+    if (n > ((int64_t)1 << 62) / (2 * (int64_t)G)) return LISFA_ERR_BAD_SHAPE;
+    zigzag_share_ranges(n, G, g, ranges);
+    return LISFA_OK;
+}
+
+int zigzag_restore(const void* src, void* dst, int64_t n, int32_t G, int64_t row_bytes, lisfa_stream_t stream) {
+    if (n < 0 || G < 1 || row_bytes < 1) return LISFA_ERR_BAD_SHAPE;
+    if (n > ((int64_t)1 << 40) / (2 * (int64_t)G)) return LISFA_ERR_BAD_SHAPE;
+    if (n == 0) return LISFA_OK;
+    if (!src || !dst) return LISFA_ERR_NULL_ARG;
+    const uintptr_t a = (uintptr_t)src, b = (uintptr_t)dst, len = (uintptr_t)(n * row_bytes);
+    if (a < b + len && b < a + len) return LISFA_ERR_BAD_SHAPE;   // the buffers must not overlap
+    return hip_status(zigzag_restore_dispatch(src, dst, n, G, row_bytes, (hipStream_t)stream));
 }
 
 int li_topk_sfa(const lisfa_indexer_args* iargs, const lisfa_mla_args* margs, int32_t K, int32_t* idx_out,
@@ -264,12 +357,12 @@ int li_topk_sfa(const lisfa_indexer_args* iargs, const lisfa_mla_args* margs, in
             hipError_t he = li_score_dispatch(dc, iargs->D_I, elt == 1, qg, scores, ld, iargs->max_visible, st);
             if (he != hipSuccess) return LISFA_ERR_HIP;
         }
-        hipError_t he = topk_dispatch(scores, ld, dc.row_pos, dc.R, K, idx + c0 * K, st);
+        hipError_t he = topk_dispatch(scores, ld, dc.row_pos, dc.R, K, idx + c0 * K, w + L.cand, st);
         if (he != hipSuccess) return LISFA_ERR_HIP;
     }
     const MlaDev md = to_dev(margs, idx, K);
     return hip_status(sfa_dispatch(md, margs->D_latent, margs->kv_cache.dtype == LISFA_FP8_E4M3, (__bf16*)out,
-                                   lse, sfa_ws, st));
+                                   nullptr, lse, sfa_ws, st));
 }
 
 }  // extern "C"

@@ -94,7 +94,9 @@ __global__ __launch_bounds__(128 * NHG) void sfa_kernel(MlaDev a, int kps, int n
     const int k1 = (k0 + kps < a.K) ? k0 + kps : a.K;
     const int nk = k1 - k0;
     const int seq = a.row_seq[r];
-    const int ntiles = (nk + TROWS - 1) / TROWS;
+    const int nt_fill = (nk + TROWS - 1) / TROWS;
+    __shared__ int s_ntiles;
+    if (tid == 0) s_ntiles = 1;
 
     // query half of this wave in B-operand layout (col = head, 8 consecutive d)
     const int head = hb * 32 * NHG + hg * 32 + (lane & 31);
@@ -110,24 +112,30 @@ __global__ __launch_bounds__(128 * NHG) void sfa_kernel(MlaDev a, int kps, int n
     }
 
     // selected rows -> byte offsets, and one validity bit per row via ballots
-    for (int i0 = 0; i0 < ntiles * TROWS; i0 += NT) {
+    for (int i0 = 0; i0 < nt_fill * TROWS; i0 += NT) {
         const int i = i0 + tid;
         int64_t s = -1;
         if (i < nk) {
             const int p = a.idx[(int64_t)r * a.K + k0 + i];
             s = p >= 0 ? slot_of(a.kv, seq, p) : -1;
         }
-        if (i < ntiles * TROWS) {
+        if (i < nt_fill * TROWS) {
             roff[i] = s >= 0 ? s * a.kv.row_stride : -1;
             if constexpr (FP8) kvs[i] = s >= 0 ? a.kv.scale[s / a.kv.scale_group] : 0.f;
         }
         const uint64_t bal = __ballot(s >= 0);
-        if (lane == 0 && i < ntiles * TROWS) {
+        if (lane == 0 && i < nt_fill * TROWS) {
             vmask[i / 32] = (uint32_t)bal;
-            if (i + 32 < ntiles * TROWS) vmask[i / 32 + 1] = (uint32_t)(bal >> 32);
+            if (i + 32 < nt_fill * TROWS) vmask[i / 32 + 1] = (uint32_t)(bal >> 32);
         }
     }
     __syncthreads();
+    // trailing tiles without a valid row are skipped; at least one tile is
+    // always processed (an empty tile contributes nothing)
+    for (int t = tid; t < nt_fill; t += NT)
+        if (vmask[t] != 0u) atomicMax(&s_ntiles, t + 1);
+    __syncthreads();
+    const int ntiles = s_ntiles;
 
     // per-lane constants of the LDS addressing
     const int krow = lane & 31;                 // QK: cached row = key of this lane
@@ -479,7 +487,7 @@ __global__ __launch_bounds__(128 * NHG) void sfa_kernel(MlaDev a, int kps, int n
     if (head < a.H) {
         const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
         const float l_nat = lsum > 0.f ? (m2 + log2f(lsum)) * kLn2 : -__builtin_inff();
-        if (nsplit == 1) {
+        if (nsplit == 1 && out != nullptr) {
             __bf16* orow = out + ((int64_t)r * a.H + head) * DLAT;
             store_rows(orow, inv);
             if (lse != nullptr && dh == 0 && lane < 32) lse[(int64_t)r * a.H + head] = l_nat;
@@ -562,23 +570,31 @@ __global__ __launch_bounds__(128 * NHG) void sfa_bf16_kernel(MlaDev a, int kps, 
     const int k1 = (k0 + kps < a.K) ? k0 + kps : a.K;
     const int nk = k1 - k0;
     const int seq = a.row_seq[r];
-    const int ntiles = (nk + TROWS - 1) / TROWS;
+    const int nt_fill = (nk + TROWS - 1) / TROWS;
+    __shared__ int s_ntiles;
+    if (tid == 0) s_ntiles = 1;
 
-    for (int i0 = 0; i0 < ntiles * TROWS; i0 += NT) {
+    for (int i0 = 0; i0 < nt_fill * TROWS; i0 += NT) {
         const int i = i0 + tid;
         int64_t s = -1;
         if (i < nk) {
             const int p = a.idx[(int64_t)r * a.K + k0 + i];
             s = p >= 0 ? slot_of(a.kv, seq, p) : -1;
         }
-        if (i < ntiles * TROWS) rslot[i] = s >= 0 ? (uint32_t)s : 0xFFFFFFFFu;
+        if (i < nt_fill * TROWS) rslot[i] = s >= 0 ? (uint32_t)s : 0xFFFFFFFFu;
         const uint64_t bal = __ballot(s >= 0);
-        if (lane == 0 && i < ntiles * TROWS) {
+        if (lane == 0 && i < nt_fill * TROWS) {
             vmask[i / 32] = (uint32_t)bal;
-            if (i + 32 < ntiles * TROWS) vmask[i / 32 + 1] = (uint32_t)(bal >> 32);
+            if (i + 32 < nt_fill * TROWS) vmask[i / 32 + 1] = (uint32_t)(bal >> 32);
         }
     }
     __syncthreads();
+    // trailing tiles without a valid row are skipped; at least one tile is
+    // always processed (an empty tile contributes nothing)
+    for (int t = tid; t < nt_fill; t += NT)
+        if (vmask[t] != 0u) atomicMax(&s_ntiles, t + 1);
+    __syncthreads();
+    const int ntiles = s_ntiles;
 
     const lds_u8* tile0 = (const lds_u8*)tile;
     const uint32_t tile_lds = (uint32_t)(uintptr_t)tile;
@@ -844,7 +860,7 @@ __global__ __launch_bounds__(128 * NHG) void sfa_bf16_kernel(MlaDev a, int kps, 
         if (head < a.H) {
             const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
             const float l_nat = lsum > 0.f ? (m2 + log2f(lsum)) * kLn2 : -__builtin_inff();
-            if (nsplit == 1) {
+            if (nsplit == 1 && out != nullptr) {
                 __bf16* orow = out + ((int64_t)r * a.H + head) * DLAT;
 #pragma unroll
                 for (int mt = 0; mt < MTV; ++mt)
@@ -937,23 +953,31 @@ __global__ __launch_bounds__(512) void sfa_w8_kernel(MlaDev a, int kps, int nspl
     const int k1 = (k0 + kps < a.K) ? k0 + kps : a.K;
     const int nk = k1 - k0;
     const int seq = a.row_seq[r];
-    const int ntiles = (nk + TROWS - 1) / TROWS;
+    const int nt_fill = (nk + TROWS - 1) / TROWS;
+    __shared__ int s_ntiles;
+    if (tid == 0) s_ntiles = 1;
 
-    for (int i0 = 0; i0 < ntiles * TROWS; i0 += NT) {
+    for (int i0 = 0; i0 < nt_fill * TROWS; i0 += NT) {
         const int i = i0 + tid;
         int64_t s = -1;
         if (i < nk) {
             const int p = a.idx[(int64_t)r * a.K + k0 + i];
             s = p >= 0 ? slot_of(a.kv, seq, p) : -1;
         }
-        if (i < ntiles * TROWS) rslot[i] = s >= 0 ? (uint32_t)s : 0xFFFFFFFFu;
+        if (i < nt_fill * TROWS) rslot[i] = s >= 0 ? (uint32_t)s : 0xFFFFFFFFu;
         const uint64_t bal = __ballot(s >= 0);
-        if (lane == 0 && i < ntiles * TROWS) {
+        if (lane == 0 && i < nt_fill * TROWS) {
             vmask[i / 32] = (uint32_t)bal;
-            if (i + 32 < ntiles * TROWS) vmask[i / 32 + 1] = (uint32_t)(bal >> 32);
+            if (i + 32 < nt_fill * TROWS) vmask[i / 32 + 1] = (uint32_t)(bal >> 32);
         }
     }
     __syncthreads();
+    // trailing tiles without a valid row are skipped; at least one tile is
+    // always processed (an empty tile contributes nothing)
+    for (int t = tid; t < nt_fill; t += NT)
+        if (vmask[t] != 0u) atomicMax(&s_ntiles, t + 1);
+    __syncthreads();
+    const int ntiles = s_ntiles;
 
     const lds_u8* tile0 = (const lds_u8*)tile;
     const uint32_t tile_lds = (uint32_t)(uintptr_t)tile;
@@ -1205,7 +1229,7 @@ __global__ __launch_bounds__(512) void sfa_w8_kernel(MlaDev a, int kps, int nspl
         if (head < a.H) {
             const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
             const float l_nat = lsum > 0.f ? (m2 + log2f(lsum)) * kLn2 : -__builtin_inff();
-            if (nsplit == 1) {
+            if (nsplit == 1 && out != nullptr) {
                 __bf16* orow = out + ((int64_t)r * a.H + head) * DLAT + DH * DVH + 4 * g;
 #pragma unroll
                 for (int mt = 0; mt < MTV; ++mt) {
@@ -1227,14 +1251,18 @@ __global__ __launch_bounds__(512) void sfa_w8_kernel(MlaDev a, int kps, int nspl
     else body(std::integral_constant<int, 0>{});
 }
 
-// Merge split-K partials: out = sum_i e^{lse_i - M} O_i / sum_i e^{lse_i - M}.
-// 8 consecutive value columns per thread (two 16-byte loads per split, one
-// 16-byte store), DLAT / 8 threads per (row, head), 256 threads per block.
-template <int DLAT>
+// Merge partial results: out = sum_i e^{lse_i - M} O_i / sum_i e^{lse_i - M},
+// lse = M + log sum_i e^{lse_i - M} (M = max_i lse_i; a part with lse = -inf
+// holds no row).  Partial i of row r lives at entry (r * row_str + i *
+// split_str) * H + h: split-K partials [R, nsplit, H] use (nsplit, 1), the
+// gathered shards of a context split [G, R, H] use (1, R).  8 consecutive
+// value columns per thread (two 16-byte loads per part), DLAT / 8 threads per
+// (row, head), 256 threads per block; bf16 or fp32 output.
+template <int DLAT, bool F32OUT>
 __global__ __launch_bounds__(256) void sfa_combine_kernel(const float* __restrict__ part_o,
                                                           const float* __restrict__ part_lse, int nsplit,
-                                                          int H, int RH, __bf16* __restrict__ out,
-                                                          float* __restrict__ lse) {
+                                                          int64_t row_str, int64_t split_str, int H, int RH,
+                                                          void* __restrict__ out, float* __restrict__ lse) {
     constexpr int TPH = DLAT / 8;            // threads per (row, head)
     static_assert(DLAT % 8 == 0 && 256 % TPH == 0, "shape");
     constexpr int HPB = 256 / TPH;
@@ -1242,18 +1270,18 @@ __global__ __launch_bounds__(256) void sfa_combine_kernel(const float* __restric
     if (rh >= RH) return;
     const int r = rh / H, h = rh % H;
     const int c = (threadIdx.x % TPH) * 8;
-    const float* pl = part_lse + (int64_t)r * nsplit * H + h;
     float M = -__builtin_inff();
-    for (int i = 0; i < nsplit; ++i) M = fmaxf(M, pl[(int64_t)i * H]);
+    for (int i = 0; i < nsplit; ++i) M = fmaxf(M, part_lse[((int64_t)r * row_str + i * split_str) * H + h]);
     float acc[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] = 0.f;
     float W = 0.f;
     if (M != -__builtin_inff()) {
         for (int i = 0; i < nsplit; ++i) {
-            const float wi = __expf(pl[(int64_t)i * H] - M);
+            const int64_t e = ((int64_t)r * row_str + i * split_str) * H + h;
+            const float wi = __expf(part_lse[e] - M);
             W += wi;
-            const f32x4* po = (const f32x4*)(part_o + (((int64_t)r * nsplit + i) * H + h) * DLAT + c);
+            const f32x4* po = (const f32x4*)(part_o + e * DLAT + c);
             const f32x4 v0 = po[0], v1 = po[1];
             acc[0] = fmaf(wi, v0.x, acc[0]);
             acc[1] = fmaf(wi, v0.y, acc[1]);
@@ -1266,11 +1294,50 @@ __global__ __launch_bounds__(256) void sfa_combine_kernel(const float* __restric
         }
     }
     const float inv = W > 0.f ? 1.f / W : 0.f;
-    bf16x8 v;
+    if constexpr (F32OUT) {
+        f32x4* o = (f32x4*)((float*)out + (int64_t)rh * DLAT + c);
+        o[0] = f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+        o[1] = f32x4{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
+    } else {
+        bf16x8 v;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = (__bf16)(acc[j] * inv);
-    *(bf16x8*)(out + (int64_t)rh * DLAT + c) = v;
+        for (int j = 0; j < 8; ++j) v[j] = (__bf16)(acc[j] * inv);
+        *(bf16x8*)((__bf16*)out + (int64_t)rh * DLAT + c) = v;
+    }
     if (lse != nullptr && c == 0) lse[rh] = W > 0.f ? M + __logf(W) : -__builtin_inff();
+}
+
+// Entries of each row's index list inside the row's range [lo, hi) (range[r]
+// = {lo, hi}), as positions relative to lo, compacted in list order and
+// padded with -1: the part of a gathered index list that one context shard
+// holds.  One workgroup of 256 threads per row.
+__global__ __launch_bounds__(256) void sfa_localize_kernel(const int32_t* __restrict__ idx, int K,
+                                                           const int32_t* __restrict__ range,
+                                                           int32_t* __restrict__ out) {
+    __shared__ uint32_t wsum[4];
+    const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int32_t lo = range[2 * r], hi = range[2 * r + 1];
+    const int32_t* in = idx + (int64_t)r * K;
+    int32_t* o = out + (int64_t)r * K;
+    uint32_t base = 0;
+    for (int k0 = 0; k0 < K; k0 += 256) {
+        const int i = k0 + tid;
+        const int32_t e = i < K ? in[i] : -1;
+        const bool take = e >= 0 && e >= lo && e < hi;
+        const uint64_t bal = __ballot(take);
+        if (lane == 0) wsum[wave] = (uint32_t)__popcll(bal);
+        __syncthreads();
+        uint32_t before = 0, total = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            before += w < wave ? wsum[w] : 0u;
+            total += wsum[w];
+        }
+        if (take) o[base + before + lanemask_count(bal)] = e - lo;
+        base += total;
+        __syncthreads();
+    }
+    for (int i = (int)base + tid; i < K; i += 256) o[i] = -1;
 }
 
 // split heuristic shared with the workspace query ------------------------------
@@ -1301,11 +1368,17 @@ SfaPlan sfa_plan(int R, int K, int H) {
     return p;
 }
 
+// out != nullptr: bf16 output; out == nullptr: fp32 normalised output in
+// out_f32 (partial results of one context shard) and lse required.
 template <int DLAT, int DROPE, bool FP8, int NHG>
-static hipError_t launch_sfa_t(const MlaDev& a, const SfaPlan& p, __bf16* out, float* lse, float* part_o,
-                               float* part_lse, hipStream_t stream) {
+static hipError_t launch_sfa_t(const MlaDev& a, const SfaPlan& p, __bf16* out, float* out_f32, float* lse,
+                               float* part_o, float* part_lse, hipStream_t stream) {
     const int64_t units = (int64_t)a.R * p.nsplit;
     const int64_t nwg = (units + 7) / 8 * 8 * p.nhb;
+    if (out == nullptr && p.nsplit == 1) {   // one split writes the fp32 result directly
+        part_o = out_f32;
+        part_lse = lse;
+    }
     if constexpr (!FP8 && ((DLAT + DROPE) * 2) % 128 == 0 && NHG == 2)
         hipLaunchKernelGGL((sfa_w8_kernel<DLAT, DROPE>), dim3((unsigned)nwg), dim3(512), 0, stream, a, p.kps,
                            p.nsplit, p.nhb, out, lse, part_o, part_lse);
@@ -1319,19 +1392,25 @@ static hipError_t launch_sfa_t(const MlaDev& a, const SfaPlan& p, __bf16* out, f
     if (e != hipSuccess || p.nsplit == 1) return e;
     constexpr int HPB = 256 / (DLAT / 8);
     const int RH = a.R * a.H;
-    hipLaunchKernelGGL((sfa_combine_kernel<DLAT>), dim3((unsigned)((RH + HPB - 1) / HPB)), dim3(256), 0, stream,
-                       part_o, part_lse, p.nsplit, a.H, RH, out, lse);
+    if (out != nullptr)
+        hipLaunchKernelGGL((sfa_combine_kernel<DLAT, false>), dim3((unsigned)((RH + HPB - 1) / HPB)), dim3(256), 0,
+                           stream, part_o, part_lse, p.nsplit, (int64_t)p.nsplit, (int64_t)1, a.H, RH, (void*)out,
+                           lse);
+    else
+        hipLaunchKernelGGL((sfa_combine_kernel<DLAT, true>), dim3((unsigned)((RH + HPB - 1) / HPB)), dim3(256), 0,
+                           stream, part_o, part_lse, p.nsplit, (int64_t)p.nsplit, (int64_t)1, a.H, RH,
+                           (void*)out_f32, lse);
     return hipGetLastError();
 }
 
-hipError_t sfa_dispatch(const MlaDev& a, int D_latent, int fp8, __bf16* out, float* lse, void* ws,
+hipError_t sfa_dispatch(const MlaDev& a, int D_latent, int fp8, __bf16* out, float* out_f32, float* lse, void* ws,
                         hipStream_t stream) {
     const SfaPlan p = sfa_plan(a.R, a.K, a.H);
     float* part_o = (float*)ws;
     float* part_lse = part_o + (size_t)a.R * p.nsplit * a.H * D_latent;
 #define LISFA_SFA_CASE(DL_, DR_, F8_, G_)                                                     \
     if (D_latent == DL_ && (fp8 != 0) == F8_ && p.nhg == G_)                                   \
-        return launch_sfa_t<DL_, DR_, F8_, G_>(a, p, out, lse, part_o, part_lse, stream);
+        return launch_sfa_t<DL_, DR_, F8_, G_>(a, p, out, out_f32, lse, part_o, part_lse, stream);
     LISFA_SFA_CASE(512, 64, false, 2)
     LISFA_SFA_CASE(512, 64, true, 2)
     LISFA_SFA_CASE(512, 64, false, 1)
@@ -1344,10 +1423,53 @@ hipError_t sfa_dispatch(const MlaDev& a, int D_latent, int fp8, __bf16* out, flo
     return hipErrorInvalidValue;
 }
 
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Attention of one context shard over the rows of a gathered index list that
+// it holds: range[r] = {lo, hi} are the logical positions of row r's
+// sequence in this shard (its cache addresses them as 0..hi-lo-1); NULL =
+// the list already holds local positions.  fp32 normalised output + lse.
+hipError_t sfa_partial_dispatch(const MlaDev& a, const int32_t* range, int D_latent, int fp8, float* out_f32,
+                                float* lse, void* ws, hipStream_t stream) {
+    MlaDev d = a;
+    uint8_t* w = (uint8_t*)ws;
+    if (range != nullptr) {
+        int32_t* li = (int32_t*)w;
+        hipLaunchKernelGGL(sfa_localize_kernel, dim3((unsigned)a.R), dim3(256), 0, stream, a.idx, a.K, range, li);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        d.idx = li;
+        w += align256((size_t)a.R * a.K * sizeof(int32_t));
+    }
+    return sfa_dispatch(d, D_latent, fp8, nullptr, out_f32, lse, w, stream);
+}
+
+// LSE combine of G gathered partial results [G, R, H, D] -> [R, H, D] bf16.
+hipError_t lse_combine_dispatch(const float* part_o, const float* part_lse, int G, int R, int H, int D, __bf16* out,
+                                float* lse, hipStream_t stream) {
+    const int RH = R * H;
+    if (RH == 0) return hipSuccess;
+#define LISFA_COMB(D_)                                                                                   \
+    if (D == D_) {                                                                                       \
+        constexpr int HPB = 256 / (D_ / 8);                                                              \
+        hipLaunchKernelGGL((sfa_combine_kernel<D_, false>), dim3((unsigned)((RH + HPB - 1) / HPB)), dim3(256), 0, \
+                           stream, part_o, part_lse, G, (int64_t)1, (int64_t)R, H, RH, (void*)out, lse);  \
+        return hipGetLastError();                                                                        \
+    }
+    LISFA_COMB(512)
+    LISFA_COMB(64)
+#undef LISFA_COMB
+    return hipErrorInvalidValue;
+}
+
 size_t sfa_workspace_bytes(int R, int K, int H, int D_latent) {
     const SfaPlan p = sfa_plan(R, K, H);
     if (p.nsplit <= 1) return 0;
     return (size_t)R * p.nsplit * H * ((size_t)D_latent + 1) * sizeof(float);
+}
+
+size_t sfa_partial_workspace_bytes(int R, int K, int H, int D_latent, int with_range) {
+    return (with_range ? align256((size_t)R * K * sizeof(int32_t)) : 0) + sfa_workspace_bytes(R, K, H, D_latent);
 }
 
 }  // namespace lisfa

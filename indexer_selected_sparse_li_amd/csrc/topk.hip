@@ -14,8 +14,14 @@
 //    runs over all keys, later levels only over the threshold bin's keys once
 //    they fit in LDS; the emission is a single block scan of per-thread
 //    (greater, equal) counts.
-//  * topk_kernel<0> (longer rows): keys are re-read from global memory on
-//    every pass; emission per 1024-position chunk from wavefront ballots.
+//  * topk_cand_kernel + topk_merge_kernel (rows longer than 64K positions,
+//    and the local / merged selection of a context-parallel split): slices of
+//    a row keep their own Top-K as (position, score) pairs, a merge selects
+//    the K best of the gathered pairs.  Every globally selected position is
+//    among its own slice's Top-K, so the result is the same.
+//  * topk_kernel<0> (long rows without workspace): keys are re-read from
+//    global memory on every pass; emission per 1024-position chunk from
+//    wavefront ballots.
 #include "common.hpp"
 
 namespace lisfa {
@@ -276,29 +282,24 @@ struct TkShared {
     uint32_t digit, above, ncand;
 };
 
-// Selection core shared by the Top-K kernels.  The block holds keys kr[c],
-// c < nv, of thread t at list index t * EPT + c (the list order is the
-// position order).  Selects the K largest keys, ties to the lower index, and
-// calls emit(c, slot) for every selected key with its output slot (list
-// order), for K < number of valid keys.
+// Threshold of the selection core shared by the Top-K kernels.  The block
+// holds keys kr[c] of thread t (list index t * EPT + c); valid(c) marks the
+// valid ones (a prefix of the thread's keys, or a bit mask).  Finds T, the K-th largest valid key, and `need`, how many
+// keys equal to T belong to the K largest (K < number of valid keys).
 //  * min / max key, then radix select on d = key - kmin from the top bit of
 //    the range in digits of at most 13 bits (LDS histogram + block scan).
 //    The first level runs over all keys; once the bin holding the K-th value
 //    has at most kTkCandMax keys, their d values move to LDS and the remaining
-//    levels histogram only them.  T is the K-th largest key, `need` the number
-//    of keys equal to T that are taken.
-//  * Emission: one block scan of each thread's (greater than T, equal to T)
-//    counts gives its first slot; equal keys are taken while their rank among
-//    equals is below `need`.
-template <int EPT, typename Emit>
-__device__ __forceinline__ void tk_select(TkShared& sh, const uint32_t (&kr)[EPT], int nv, uint32_t K,
-                                          Emit&& emit) {
+//    levels histogram only them.
+template <int EPT, typename Valid>
+__device__ __forceinline__ void tk_threshold(TkShared& sh, const uint32_t (&kr)[EPT], Valid&& valid, uint32_t K,
+                                             uint32_t& T_out, uint32_t& need_out) {
     static_assert(EPT <= 64, "keys per thread");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
     for (int c = 0; c < EPT; ++c) {
-        if (c < nv) {
+        if (valid(c)) {
             kmin = kr[c] < kmin ? kr[c] : kmin;
             kmax = kr[c] > kmax ? kr[c] : kmax;
         }
@@ -344,7 +345,7 @@ __device__ __forceinline__ void tk_select(TkShared& sh, const uint32_t (&kr)[EPT
                 for (int c = 0; c < EPT; ++c) {
                     const uint32_t d = kr[c] - kmin;
                     const bool match = hi == 31 ? true : ((d ^ prefix) >> (hi + 1)) == 0u;
-                    if (c < nv && match) atomicAdd(&sh.hist[(d >> lo) & mask], 1u);
+                    if (valid(c) && match) atomicAdd(&sh.hist[(d >> lo) & mask], 1u);
                 }
             } else {
                 for (uint32_t i = tid; i < ncand; i += kTkThreads) {
@@ -384,7 +385,7 @@ __device__ __forceinline__ void tk_select(TkShared& sh, const uint32_t (&kr)[EPT
 #pragma unroll
                 for (int c = 0; c < EPT; ++c) {
                     const uint32_t d = kr[c] - kmin;
-                    if (c < nv && ((d ^ prefix) >> lo) == 0u) sh.cand[atomicAdd(&sh.ncand, 1u)] = d;
+                    if (valid(c) && ((d ^ prefix) >> lo) == 0u) sh.cand[atomicAdd(&sh.ncand, 1u)] = d;
                 }
                 compact = true;
                 ncand = inbin;
@@ -394,12 +395,34 @@ __device__ __forceinline__ void tk_select(TkShared& sh, const uint32_t (&kr)[EPT
         }
         T = kmin + prefix;
     }
-    const uint32_t need_eq = need;
+    T_out = T;
+    need_out = need;
+}
 
+// validity functors: the first nv keys of the thread, or the bits of a mask
+struct TkPrefix {
+    int nv;
+    __device__ __forceinline__ bool operator()(int c) const { return c < nv; }
+};
+struct TkMask {
+    uint64_t m;
+    __device__ __forceinline__ bool operator()(int c) const { return (m >> c) & 1ull; }
+};
+
+// Selection core: the K largest valid keys, ties to the lower list index;
+// calls emit(c, slot) for every selected key with its output slot (list
+// order), for K < number of valid keys.  Emission: one block scan of each
+// thread's (greater than T, equal to T) counts gives its first slot; equal
+// keys are taken while their rank among equals is below `need`.
+template <int EPT, typename Valid, typename Emit>
+__device__ __forceinline__ void tk_select(TkShared& sh, const uint32_t (&kr)[EPT], Valid&& valid, uint32_t K,
+                                          Emit&& emit) {
+    uint32_t T, need_eq;
+    tk_threshold<EPT>(sh, kr, valid, K, T, need_eq);
     uint64_t gtm = 0ull, eqm = 0ull;
 #pragma unroll
     for (int c = 0; c < EPT; ++c) {
-        if (c < nv) {
+        if (valid(c)) {
             gtm |= (uint64_t)(kr[c] > T) << c;
             eqm |= (uint64_t)(kr[c] == T) << c;
         }
@@ -460,14 +483,284 @@ __global__ __launch_bounds__(kTkThreads) void topk_reg_kernel(const float* __res
     const int64_t base = (int64_t)tid * EPT;
     uint32_t kr[EPT];
     const int nv = tk_load<EPT>(scores + (int64_t)r * ld, vec, base, n, kr);
-    tk_select<EPT>(sh, kr, nv, (uint32_t)K, [&](int c, uint32_t slot) { out[slot] = (int32_t)(base + c); });
+    tk_select<EPT>(sh, kr, TkPrefix{nv}, (uint32_t)K,
+                   [&](int c, uint32_t slot) { out[slot] = (int32_t)(base + c); });
+}
+
+// Local Top-K of slices: workgroup (s, r) selects among positions
+// [s * SL, s * SL + SL) of row r's visible range (SL = 1024 * EPT) and writes
+// min(K, count) (position + pos_offset[r], score) pairs, positions ascending,
+// padded with (-1, -inf), to candidate block (r, s) of S per row.  With one
+// slice per row this is the local Top-K of a context shard; with several it
+// is the first pass of the selection of rows too long for one workgroup.
+template <int EPT>
+__global__ __launch_bounds__(kTkThreads) void topk_cand_kernel(const float* __restrict__ scores, int64_t ld,
+                                                               const int32_t* __restrict__ row_pos, int K, int S,
+                                                               const int32_t* __restrict__ pos_offset,
+                                                               int32_t* __restrict__ cand_pos,
+                                                               float* __restrict__ cand_score) {
+    __shared__ TkShared sh;
+    const int sl = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
+    int64_t n = (int64_t)row_pos[r] + 1;
+    if (n < 0) n = 0;
+    if (n > ld) n = ld;
+    const int64_t lo = (int64_t)sl * kTkThreads * EPT;
+    int64_t cnt = n - lo;
+    if (cnt < 0) cnt = 0;
+    if (cnt > (int64_t)kTkThreads * EPT) cnt = (int64_t)kTkThreads * EPT;
+    const int32_t off = pos_offset ? pos_offset[r] : 0;
+    int32_t* op = cand_pos + ((int64_t)r * S + sl) * K;
+    float* os = cand_score + ((int64_t)r * S + sl) * K;
+    const float* s = scores + (int64_t)r * ld;
+    if (cnt <= K) {
+        for (int64_t i = tid; i < K; i += kTkThreads) {
+            const bool v = i < cnt;
+            op[i] = v ? (int32_t)(lo + i + off) : -1;
+            os[i] = v ? s[lo + i] : -__builtin_inff();
+        }
+        return;
+    }
+    const bool vec = ((ld & 3) == 0) && ((((uintptr_t)scores) & 15) == 0);
+    const int64_t base = lo + (int64_t)tid * EPT;
+    uint32_t kr[EPT];
+    const int nv = tk_load<EPT>(s, vec, base, lo + cnt, kr);
+    tk_select<EPT>(sh, kr, TkPrefix{nv}, (uint32_t)K, [&](int c, uint32_t slot) {
+        op[slot] = (int32_t)(base + c + off);
+        os[slot] = s[base + c];
+    });
+}
+
+constexpr int kTkMergeMaxK = 4096;   // unordered merge: selected pairs sorted in LDS
+
+struct TkMergeShared {
+    TkShared tk;
+    int32_t pos[kTkMergeMaxK];
+    float sc[kTkMergeMaxK];
+};
+
+// Writes the pairs of this thread marked in selm (list order) to out[0..m)
+// sorted by position (bitonic sort in LDS), then pads with -1 to K.  m =
+// number of marked pairs in the block, at most min(K, kTkMergeMaxK) for valid
+// input (unique positions); anything beyond is dropped, never written.
+template <int EPT>
+__device__ __forceinline__ void tk_emit_sorted(TkMergeShared& sh, const int32_t (&pr)[EPT], const float* cs,
+                                               int base, uint64_t selm, int K, int32_t* out, float* out_score) {
+    const int tid = threadIdx.x;
+    uint32_t m;
+    uint32_t at = block_excl_scan((uint32_t)__popcll(selm), sh.tk.wsum, m);
+    const uint32_t cap = (uint32_t)(K < kTkMergeMaxK ? K : kTkMergeMaxK);
+    if (m > cap) m = cap;
+#pragma unroll
+    for (int c = 0; c < EPT; ++c) {
+        if ((selm >> c) & 1ull) {
+            if (at < cap) {
+                sh.pos[at] = pr[c];
+                sh.sc[at] = cs[base + c];
+            }
+            ++at;
+        }
+    }
+    uint32_t P = 1;
+    while (P < m) P <<= 1;
+    for (uint32_t i = m + tid; i < P; i += kTkThreads) {
+        sh.pos[i] = 0x7FFFFFFF;
+        sh.sc[i] = 0.0f;
+    }
+    __syncthreads();
+    for (uint32_t k = 2; k <= P; k <<= 1) {
+        for (uint32_t j = k >> 1; j > 0; j >>= 1) {
+            for (uint32_t i = tid; i < P; i += kTkThreads) {
+                const uint32_t ij = i ^ j;
+                if (ij > i) {
+                    const int32_t a = sh.pos[i], b = sh.pos[ij];
+                    const bool up = (i & k) == 0;
+                    if ((a > b) == up) {
+                        const float fa = sh.sc[i];
+                        sh.pos[i] = b;
+                        sh.pos[ij] = a;
+                        sh.sc[i] = sh.sc[ij];
+                        sh.sc[ij] = fa;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+    for (int i = tid; i < K; i += kTkThreads) {
+        const bool v = (uint32_t)i < m;
+        out[i] = v ? sh.pos[i] : -1;
+        if (out_score) out_score[i] = v ? sh.sc[i] : -__builtin_inff();
+    }
+}
+
+// The K best of n (position, score) candidates per row (position < 0 = none):
+// larger score first, equal scores toward the lower position; ascending
+// positions, -1 padded.  `ordered`: the valid candidates of a row come in
+// ascending position order (slices of one row, or the shards of a contiguous
+// context split gathered in rank order); then list order settles ties and the
+// output needs no sort.  Otherwise ties at the K-th score are settled by a
+// second selection on the positions and the selected pairs are sorted in LDS
+// (K <= kTkMergeMaxK).
+template <int EPT>
+__global__ __launch_bounds__(kTkThreads) void topk_merge_kernel(const float* __restrict__ cand_score,
+                                                                const int32_t* __restrict__ cand_pos, int64_t ldc,
+                                                                int n, int K, int ordered, int32_t* __restrict__ idx,
+                                                                float* __restrict__ idx_score) {
+    __shared__ TkMergeShared sh;
+    const int r = blockIdx.x, tid = threadIdx.x;
+    const float* cs = cand_score + (int64_t)r * ldc;
+    const int32_t* cp = cand_pos + (int64_t)r * ldc;
+    int32_t* out = idx + (int64_t)r * K;
+    float* outs = idx_score ? idx_score + (int64_t)r * K : nullptr;
+    const int base = tid * EPT;
+    uint32_t kr[EPT];
+    int32_t pr[EPT];
+    uint64_t vm = 0ull;
+#pragma unroll
+    for (int c = 0; c < EPT; ++c) {
+        const int i = base + c;
+        const int32_t p = i < n ? cp[i] : -1;
+        pr[c] = p;
+        kr[c] = float_key(p >= 0 ? cs[i] : 0.0f);
+        vm |= (uint64_t)(p >= 0) << c;
+    }
+    uint32_t nvalid;
+    uint32_t first = block_excl_scan((uint32_t)__popcll(vm), sh.tk.wsum, nvalid);
+    if (nvalid <= (uint32_t)K) {
+        if (ordered) {
+#pragma unroll
+            for (int c = 0; c < EPT; ++c) {
+                if ((vm >> c) & 1ull) {
+                    out[first] = pr[c];
+                    if (outs) outs[first] = cs[base + c];
+                    ++first;
+                }
+            }
+            for (int i = (int)nvalid + tid; i < K; i += kTkThreads) {
+                out[i] = -1;
+                if (outs) outs[i] = -__builtin_inff();
+            }
+        } else {
+            tk_emit_sorted<EPT>(sh, pr, cs, base, vm, K, out, outs);
+        }
+        return;
+    }
+    if (ordered) {
+        tk_select<EPT>(sh.tk, kr, TkMask{vm}, (uint32_t)K, [&](int c, uint32_t slot) {
+            out[slot] = pr[c];
+            if (outs) outs[slot] = cs[base + c];
+        });
+        return;
+    }
+    uint32_t T, need_eq;
+    tk_threshold<EPT>(sh.tk, kr, TkMask{vm}, (uint32_t)K, T, need_eq);
+    uint64_t gtm = 0ull, eqm = 0ull;
+#pragma unroll
+    for (int c = 0; c < EPT; ++c) {
+        if ((vm >> c) & 1ull) {
+            gtm |= (uint64_t)(kr[c] > T) << c;
+            eqm |= (uint64_t)(kr[c] == T) << c;
+        }
+    }
+    uint32_t neq;
+    (void)block_excl_scan((uint32_t)__popcll(eqm), sh.tk.wsum, neq);
+    uint64_t selm = gtm | eqm;
+    if (need_eq < neq) {
+        // the need_eq lowest positions among the tied keys = the largest ~position
+#pragma unroll
+        for (int c = 0; c < EPT; ++c) kr[c] = ~(uint32_t)pr[c];
+        uint32_t T2, need2;
+        tk_threshold<EPT>(sh.tk, kr, TkMask{eqm}, need_eq, T2, need2);
+        uint64_t tie = 0ull;
+#pragma unroll
+        for (int c = 0; c < EPT; ++c) tie |= (uint64_t)(((eqm >> c) & 1ull) && kr[c] >= T2) << c;
+        selm = gtm | tie;
+    }
+    tk_emit_sorted<EPT>(sh, pr, cs, base, selm, K, out, outs);
+}
+
+constexpr int kTkSliceEPT = 16;                            // long rows: slices of 16384 positions
+constexpr int64_t kTkSliceLen = (int64_t)kTkThreads * kTkSliceEPT;
+constexpr int kTkMergeMaxN = kTkThreads * 16;            // candidates one merge workgroup holds
+
+// Slices a long row is cut into, or 0 when the two-pass selection does not apply.
+int topk_slices(int64_t ld, int K) {
+    if (ld <= (int64_t)kTkThreads * 64) return 0;
+    const int64_t S = (ld + kTkSliceLen - 1) / kTkSliceLen;
+    if (S * K > kTkMergeMaxN) return 0;
+    return (int)S;
+}
+
+size_t topk_workspace_bytes(int R, int64_t ld, int K) {
+    const int S = topk_slices(ld, K);
+    if (S == 0 || R <= 0) return 0;
+    return (size_t)R * S * K * (sizeof(int32_t) + sizeof(float));
+}
+
+static hipError_t launch_merge(const float* cs, const int32_t* cp, int64_t ldc, int n, int R, int K, int ordered,
+                               int32_t* idx, float* idx_score, hipStream_t stream) {
+    const int ept = (n + kTkThreads - 1) / kTkThreads;
+#define LISFA_TKM(E_)                                                                                    \
+    hipLaunchKernelGGL((topk_merge_kernel<E_>), dim3((unsigned)R), dim3(kTkThreads), 0, stream, cs, cp, ldc, n, \
+                       K, ordered, idx, idx_score)
+    if (ept <= 8) LISFA_TKM(8);
+    else LISFA_TKM(16);
+#undef LISFA_TKM
+    return hipGetLastError();
+}
+
+hipError_t topk_merge_dispatch(const float* cand_score, const int32_t* cand_pos, int64_t ldc, int R, int n, int K,
+                               int ordered, int32_t* idx, float* idx_score, hipStream_t stream) {
+    if (R <= 0) return hipSuccess;
+    return launch_merge(cand_score, cand_pos, ldc, n, R, K, ordered, idx, idx_score, stream);
+}
+
+static hipError_t launch_cand(const float* scores, int64_t ld, const int32_t* row_pos, int R, int K, int S, int ept,
+                              const int32_t* pos_offset, int32_t* cp, float* cs, hipStream_t stream) {
+#define LISFA_TKC(E_)                                                                                    \
+    hipLaunchKernelGGL((topk_cand_kernel<E_>), dim3((unsigned)S, (unsigned)R), dim3(kTkThreads), 0, stream, \
+                       scores, ld, row_pos, K, S, pos_offset, cp, cs)
+    if (ept <= 8) LISFA_TKC(8);
+    else if (ept <= 16) LISFA_TKC(16);
+    else if (ept <= 32) LISFA_TKC(32);
+    else LISFA_TKC(64);
+#undef LISFA_TKC
+    return hipGetLastError();
+}
+
+// Local Top-K candidates of a context shard.  Rows up to 64K positions: one
+// slice per row straight into the outputs; longer rows: slices into ws, then
+// an ordered merge that also carries the scores.
+hipError_t topk_candidates_dispatch(const float* scores, int64_t ld, const int32_t* row_pos, int R, int K,
+                                    const int32_t* pos_offset, int32_t* cand_pos, float* cand_score, void* ws,
+                                    hipStream_t stream) {
+    if (R <= 0) return hipSuccess;
+    if (ld <= (int64_t)kTkThreads * 64) {
+        const int ept = (int)((ld + kTkThreads - 1) / kTkThreads);
+        return launch_cand(scores, ld, row_pos, R, K, 1, ept, pos_offset, cand_pos, cand_score, stream);
+    }
+    const int S = topk_slices(ld, K);
+    int32_t* cp = (int32_t*)ws;
+    float* cs = (float*)((uint8_t*)ws + (size_t)R * S * K * sizeof(int32_t));
+    hipError_t e = launch_cand(scores, ld, row_pos, R, K, S, kTkSliceEPT, pos_offset, cp, cs, stream);
+    if (e != hipSuccess) return e;
+    return launch_merge(cs, cp, (int64_t)S * K, S * K, R, K, 1, cand_pos, cand_score, stream);
 }
 
 hipError_t topk_dispatch(const float* scores, int64_t ld, const int32_t* row_pos, int R, int K,
-                         int32_t* idx, hipStream_t stream) {
+                         int32_t* idx, void* ws, hipStream_t stream) {
     if (R <= 0) return hipSuccess;
     // registers per thread needed for the longest possible row (ld)
     const int64_t ept = (ld + kTkThreads - 1) / kTkThreads;
+    const int S = topk_slices(ld, K);
+    if (ept > 64 && S > 0 && ws) {
+        // rows longer than one workgroup's registers: slice candidates, then an ordered merge
+        int32_t* cp = (int32_t*)ws;
+        float* cs = (float*)((uint8_t*)ws + (size_t)R * S * K * sizeof(int32_t));
+        hipError_t e = launch_cand(scores, ld, row_pos, R, K, S, kTkSliceEPT, nullptr, cp, cs, stream);
+        if (e != hipSuccess) return e;
+        return launch_merge(cs, cp, (int64_t)S * K, S * K, R, K, 1, idx, nullptr, stream);
+    }
 #define LISFA_TK(E_)                                                                               \
     hipLaunchKernelGGL((topk_kernel<E_>), dim3((unsigned)R), dim3(kTkThreads), 0, stream, scores, ld, \
                        row_pos, K, idx)

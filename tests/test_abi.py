@@ -173,3 +173,62 @@ def test_python_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError):
         lisfa.KVCache(data=torch.zeros(4, 128, dtype=torch.bfloat16),
                       seq_base=torch.zeros(1, dtype=torch.int64)).c_struct()
+
+
+def test_topk_workspace_only_for_two_pass_rows(clib):
+    assert clib.lisfa_workspace_size(C.LISFA_OP_TOPK, 16, 65536, 2048, 0, 0) == 0
+    assert clib.lisfa_workspace_size(C.LISFA_OP_TOPK, 16, 131072, 2048, 0, 0) == 16 * 8 * 2048 * 8
+    # too many slice candidates for one merge: single-pass fallback, no workspace
+    assert clib.lisfa_workspace_size(C.LISFA_OP_TOPK, 16, 131072, 4096, 0, 0) == 0
+    assert clib.lisfa_workspace_size(C.LISFA_OP_TOPK_CANDIDATES, 16, 131072, 2048, 0, 0) == 16 * 8 * 2048 * 8
+    # a too-small workspace is refused, none at all is accepted (slower path)
+    assert clib.topk_select(16, 131072, 16, 16, 2048, 16, 16, 100, None) == C.LISFA_ERR_WORKSPACE
+    fused_short = clib.lisfa_workspace_size(C.LISFA_OP_FUSED, 16, 65536, 2048, 128, 512)
+    fused_long = clib.lisfa_workspace_size(C.LISFA_OP_FUSED, 16, 131072, 2048, 128, 512)
+    assert fused_long >= fused_short + 16 * 8 * 2048 * 8
+
+
+def test_context_parallel_validation(clib):
+    # topk_candidates
+    assert clib.topk_candidates(16, 100, 16, 1, 0, None, 16, 16, None, 0, None) == C.LISFA_ERR_BAD_SHAPE
+    assert clib.topk_candidates(16, 100, 16, 1, 4, None, None, 16, None, 0, None) == C.LISFA_ERR_NULL_ARG
+    assert clib.topk_candidates(16, 131072, 16, 1, 2048, None, 16, 16, None, 0, None) == C.LISFA_ERR_WORKSPACE
+    assert clib.topk_candidates(16, 1 << 20, 16, 1, 2048, None, 16, 16, 16, 1 << 30,
+                                None) == C.LISFA_ERR_UNSUPPORTED
+    assert clib.topk_candidates(None, 100, None, 0, 4, None, None, None, None, 0, None) == C.LISFA_OK
+    # topk_merge
+    assert clib.topk_merge(16, 16, 100, 1, 20000, 2048, 1, 16, None, None) == C.LISFA_ERR_BAD_SHAPE
+    assert clib.topk_merge(16, 16, 20000, 1, 20000, 2048, 1, 16, None, None) == C.LISFA_ERR_UNSUPPORTED
+    assert clib.topk_merge(16, 16, 16384, 1, 16384, 8192, 0, 16, None, None) == C.LISFA_ERR_UNSUPPORTED
+    assert clib.topk_merge(16, 16, 16384, 1, 16384, 0, 1, 16, None, None) == C.LISFA_ERR_BAD_SHAPE
+    assert clib.topk_merge(None, 16, 16384, 1, 16384, 2048, 1, 16, None, None) == C.LISFA_ERR_NULL_ARG
+    assert clib.topk_merge(None, None, 0, 0, 0, 2048, 1, None, None, None) == C.LISFA_OK
+    # sparse_mla_attn_partial
+    m = _mla_args(R=4)
+    need = clib.lisfa_workspace_size(C.LISFA_OP_SPARSE_MLA_PARTIAL, 4, 0, 2048, 128, 512)
+    assert need >= 4 * 2048 * 4
+    assert clib.sparse_mla_attn_partial(ctypes.byref(m), 16, 2048, 16, 256, None, 256, need,
+                                        None) == C.LISFA_ERR_NULL_ARG
+    assert clib.sparse_mla_attn_partial(ctypes.byref(m), 16, 2048, 16, 256, 256, 256, need - 1,
+                                        None) == C.LISFA_ERR_WORKSPACE
+    assert clib.sparse_mla_attn_partial(ctypes.byref(m), 16, 2048, 16, 264, 256, 256, need,
+                                        None) == C.LISFA_ERR_BAD_SHAPE
+    # lse_combine
+    assert clib.lse_combine(256, 256, 0, 4, 128, 512, 256, None, None) == C.LISFA_ERR_BAD_SHAPE
+    assert clib.lse_combine(256, 256, 8, 4, 128, 128, 256, None, None) == C.LISFA_ERR_UNSUPPORTED
+    assert clib.lse_combine(256, None, 8, 4, 128, 512, 256, None, None) == C.LISFA_ERR_NULL_ARG
+    assert clib.lse_combine(260, 256, 8, 4, 128, 512, 256, None, None) == C.LISFA_ERR_BAD_SHAPE
+    assert clib.lse_combine(None, None, 8, 0, 128, 512, None, None, None) == C.LISFA_OK
+
+
+def test_zigzag_host_helper_and_validation(clib):
+    r = (ctypes.c_int64 * 4)()
+    assert clib.lisfa_zigzag_share(8, 2, 0, r) == C.LISFA_OK and list(r) == [0, 2, 6, 8]
+    assert clib.lisfa_zigzag_share(8, 2, 1, r) == C.LISFA_OK and list(r) == [2, 4, 4, 6]
+    assert clib.lisfa_zigzag_share(8, 2, 2, r) == C.LISFA_ERR_BAD_SHAPE
+    assert clib.lisfa_zigzag_share(-1, 2, 0, r) == C.LISFA_ERR_BAD_SHAPE
+    assert clib.lisfa_zigzag_share(8, 2, 0, None) == C.LISFA_ERR_NULL_ARG
+    assert clib.zigzag_restore(4096, 4096 + 100, 10, 2, 16, None) == C.LISFA_ERR_BAD_SHAPE   # overlap
+    assert clib.zigzag_restore(None, None, 0, 2, 16, None) == C.LISFA_OK
+    assert clib.zigzag_restore(None, 16, 10, 2, 16, None) == C.LISFA_ERR_NULL_ARG
+    assert clib.zigzag_restore(16, 4096, 10, 0, 16, None) == C.LISFA_ERR_BAD_SHAPE
