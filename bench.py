@@ -296,7 +296,9 @@ def main():
                     help="time every workload (hot and cold), one JSON line each")
     ap.add_argument("--write-mfma-summary", action="store_true")
     ap.add_argument("--mfma-csv")
-    ap.add_argument("--report-md", help="with --report-all: write a markdown table here")
+    ap.add_argument("--report-cp", action="store_true",
+                    help="time one GPU's context-parallel share and the Zigzag prefill balance")
+    ap.add_argument("--report-md", help="with --report-all / --report-cp: write a markdown table here")
     args = ap.parse_args()
     if args.write_traffic_summary:
         write_traffic_summary(args)
@@ -325,6 +327,9 @@ def main():
         return
     if args.report_all:
         report_all(args)
+        return
+    if args.report_cp:
+        report_cp(args)
         return
     wl = W.get(args.workload)
     res, b = run_workload(args, wl)
@@ -555,6 +560,167 @@ def report_all(args):
         print(json.dumps(res), flush=True)
     if args.report_md:
         write_report_md(args.report_md, lines, args)
+
+
+def _cp_caches(lisfa, b, shard):
+    wl = b.wl
+    kc = lisfa.KVCache(data=b.k_data, scale=b.k_scale, scale_group=1, block_table=shard["block_table"],
+                       block_size=wl.block_size, seq_base=shard["seq_base"])
+    vc = lisfa.KVCache(data=b.kv_data, scale=b.kv_scale, scale_group=wl.kv_scale_group,
+                       block_table=shard["block_table"], block_size=wl.block_size, seq_base=shard["seq_base"])
+    return kc, vc
+
+
+def cp_share_timing(args, wl, G):
+    """One GPU's share of a decode context split over G GPUs (rank 0's
+    contiguous range of every sequence): local scores, local candidates, the
+    merge of the G gathered candidate lists, partial attention over the
+    selected rows it holds, and the LSE combine of the G gathered partials.
+    The other ranks' candidates and partials (what the two gathers would
+    bring) are computed first, untimed; the gathers themselves are not part
+    of one GPU.  Each step is graph-captured and timed on its own."""
+    import torch
+    import indexer_selected_sparse_li_amd as lisfa
+    import workloads as W
+    log(f"[bench] context-parallel share of {wl.name}, G={G}")
+    b = W.make_batch(wl, device="cuda")
+    R, K = b.R, wl.K
+    stream = torch.cuda.current_stream()
+    shards = W.context_shards(b, G)
+    st = []
+    for s in shards:
+        kc, vc = _cp_caches(lisfa, b, s)
+        ld = max(64, -(-s["max_vis"] // 64) * 64)
+        scores = torch.empty((R, ld), dtype=torch.float32, device="cuda")
+        lisfa.li_score(b.q_idx, b.w, kc, b.row_seq, s["row_pos"], scores, s["max_vis"], q_scale=b.q_scale)
+        cp = torch.empty((R, K), dtype=torch.int32, device="cuda")
+        cs = torch.empty((R, K), dtype=torch.float32, device="cuda")
+        lisfa.topk_candidates(scores, s["row_pos"], K, cp, cs, pos_offset=s["pos_offset"])
+        st.append(dict(kc=kc, vc=vc, scores=scores, cp=cp, cs=cs))
+    cand_pos = torch.cat([x["cp"] for x in st], 1).contiguous()
+    cand_score = torch.cat([x["cs"] for x in st], 1).contiguous()
+    idx = torch.empty((R, K), dtype=torch.int32, device="cuda")
+    lisfa.topk_merge(cand_score, cand_pos, K, idx, ordered=True)
+    pout = torch.empty((G, R, wl.H, wl.D_v), dtype=torch.float32, device="cuda")
+    plse = torch.empty((G, R, wl.H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(1, lisfa.workspace_size(4, R, 0, K, wl.H, wl.D_v)), dtype=torch.uint8, device="cuda")
+    for g, (s, x) in enumerate(zip(shards, st)):
+        lisfa.sparse_mla_attn_partial(b.q, x["vc"], b.row_seq, idx, pout[g], plse[g], shard_range=s["range"],
+                                      softmax_scale=wl.softmax_scale, workspace=ws)
+    out = torch.empty((R, wl.H, wl.D_v), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((R, wl.H), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    s0, x0 = shards[0], st[0]
+    tws = torch.empty(max(1, lisfa.workspace_size(3, R, x0["scores"].shape[1], K, 0, 0)), dtype=torch.uint8,
+                      device="cuda")
+    cp0 = torch.empty((R, K), dtype=torch.int32, device="cuda")
+    cs0 = torch.empty((R, K), dtype=torch.float32, device="cuda")
+    po0 = torch.empty((R, wl.H, wl.D_v), dtype=torch.float32, device="cuda")
+    pl0 = torch.empty((R, wl.H), dtype=torch.float32, device="cuda")
+    idx0 = torch.empty((R, K), dtype=torch.int32, device="cuda")
+    steps = [
+        ("li_score (local)", lambda q: lisfa.li_score(b.q_idx, b.w, x0["kc"], b.row_seq, s0["row_pos"], x0["scores"],
+                                                      s0["max_vis"], q_scale=b.q_scale, stream=q)),
+        ("topk_candidates", lambda q: lisfa.topk_candidates(x0["scores"], s0["row_pos"], K, cp0, cs0,
+                                                             pos_offset=s0["pos_offset"], workspace=tws, stream=q)),
+        ("topk_merge", lambda q: lisfa.topk_merge(cand_score, cand_pos, K, idx0, ordered=True, stream=q)),
+        ("sparse_mla_attn_partial", lambda q: lisfa.sparse_mla_attn_partial(
+            b.q, x0["vc"], b.row_seq, idx, po0, pl0, shard_range=s0["range"], softmax_scale=wl.softmax_scale,
+            workspace=ws, stream=q)),
+        ("lse_combine", lambda q: lisfa.lse_combine(pout, plse, out, lse, stream=q)),
+    ]
+    times = {}
+    for name, fn in steps:
+        times[name] = time_on_stream(fn, stream, 2, args.steps, graph=True) * 1e6
+    total = sum(times.values())
+    vis_local = int((s0["row_pos"].to(torch.int64) + 1).clamp(min=0).sum().item())
+    ke = 1 if wl.indexer_dtype == "fp8" else 2
+    ks = 4 if wl.indexer_dtype == "fp8" else 0
+    li_bytes = vis_local * (wl.D_I * ke + ks) + R * (wl.H_I * (wl.D_I * ke + 4) + ks)
+    res = dict(workload=wl.name, G=G, rank=0, rows=R, local_positions=vis_local,
+               us={k: round(v, 2) for k, v in times.items()}, share_us=round(total, 2),
+               rows_per_s=round(R / (total * 1e-6), 1),
+               li_score_local_hbm_frac=round(li_bytes / (times["li_score (local)"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4))
+    log(f"[bench] share {res}")
+    return res
+
+
+def zigzag_balance(args, wl, G):
+    """Causal prefill rows split over G GPUs in order and by the Zigzag
+    partition: the fused layer's time on each GPU's rows."""
+    import torch
+    import indexer_selected_sparse_li_amd as lisfa
+    import workloads as W
+    log(f"[bench] zigzag balance on {wl.name}, G={G}")
+    b = W.make_batch(wl, device="cuda")
+    n = b.R
+    kc = lisfa.KVCache(data=b.k_data, scale=b.k_scale, scale_group=1, block_table=b.block_table,
+                       block_size=wl.block_size, seq_base=b.seq_base)
+    vc = lisfa.KVCache(data=b.kv_data, scale=b.kv_scale, scale_group=wl.kv_scale_group,
+                       block_table=b.block_table, block_size=wl.block_size, seq_base=b.seq_base)
+    stream = torch.cuda.current_stream()
+    res = {}
+    for part in ("in-order", "zigzag"):
+        per = []
+        for g in range(G):
+            if part == "zigzag":
+                rng = lisfa.zigzag_share(n, G, g)
+            else:
+                rng = [(g * n // G, (g + 1) * n // G)]
+            rows = torch.cat([torch.arange(a, c) for a, c in rng]).cuda()
+            m = rows.numel()
+            sub = dict(q_idx=b.q_idx[rows].contiguous(), w=b.w[rows].contiguous(), q=b.q[rows].contiguous(),
+                       row_seq=b.row_seq[rows].contiguous(), row_pos=b.row_pos[rows].contiguous())
+            out = torch.empty((m, wl.H, wl.D_v), dtype=torch.bfloat16, device="cuda")
+            lse = torch.empty((m, wl.H), dtype=torch.float32, device="cuda")
+            ws = torch.empty(lisfa.workspace_size(2, m, b.max_visible, wl.K, wl.H, wl.D_v), dtype=torch.uint8,
+                             device="cuda")
+            fn = (lambda q, sub=sub, out=out, lse=lse, ws=ws: lisfa.li_topk_sfa(
+                sub["q_idx"], sub["w"], kc, sub["q"], vc, sub["row_seq"], sub["row_pos"], wl.K, b.max_visible,
+                out, lse, rows_per_group=8, softmax_scale=wl.softmax_scale, workspace=ws, stream=q))
+            per.append(round(time_on_stream(fn, stream, 1, max(2, args.steps // 4)) * 1e3, 3))
+            del ws, out, lse, sub
+        res[part] = dict(ms=per, max_over_min=round(max(per) / min(per), 3), max_ms=max(per))
+        log(f"[bench] {part}: {res[part]}")
+    return dict(workload=wl.name, G=G, rows=n, **res)
+
+
+def report_cp(args):
+    """Context-parallel measurements: one GPU's decode share, and the Zigzag
+    load balance of causal prefill rows; a markdown table if asked."""
+    import workloads as W
+    shares = [cp_share_timing(args, W.get("fp8_decode_16x131072"), 8),
+              cp_share_timing(args, W.get("decode_paged_64x32768"), 8)]
+    pre = W.get("prefill_4096q_l65536").with_(name="prefill_16384q_from0", seq_len=16384, q_rows=16384)
+    zz = zigzag_balance(args, pre, 4)
+    print(json.dumps(dict(shares=shares, zigzag=zz)), flush=True)
+    if args.report_md:
+        with open(args.report_md, "w") as fh:
+            fh.write("# Context-parallel share on one MI355X\n\n")
+            fh.write("One GPU's share of a context split (rank 0 of G). Every step is captured in a HIP graph and\n"
+                     "timed on its own with HIP events; the candidates and partials of the other ranks (what the\n"
+                     "two gathers between GPUs would bring) are computed beforehand, untimed. The gathers are not\n"
+                     "part of one GPU. rows/s = rows / share time, i.e. the whole job's rate when all G GPUs run\n"
+                     "their shares at once, gathers excluded.\n\n")
+            fh.write("Command (from the repository root):\n\n")
+            fh.write(f"    python3 bench.py --report-cp --steps {args.steps} --report-md "
+                     f"{os.path.relpath(args.report_md, ROOT)}\n\n")
+            names = list(shares[0]["us"])
+            fh.write("| workload | G | rows | local positions | " + " | ".join(f"{k} us" for k in names) +
+                     " | share us | rows/s | local li_score % HBM |\n")
+            fh.write("|---" * (7 + len(names)) + "|\n")
+            for s in shares:
+                fh.write(f'| {s["workload"]} | {s["G"]} | {s["rows"]} | {s["local_positions"]} | ' +
+                         " | ".join(str(s["us"][k]) for k in names) +
+                         f' | {s["share_us"]} | {s["rows_per_s"]:.0f} | {s["li_score_local_hbm_frac"] * 100:.1f} |\n')
+            fh.write(f'\nZigzag balance: {zz["rows"]} causal prefill rows (positions 0..{zz["rows"] - 1}) on '
+                     f'{zz["G"]} GPUs, fused layer time per GPU (ms):\n\n')
+            fh.write("| partition | " + " | ".join(f"GPU {g}" for g in range(zz["G"])) + " | max / min |\n")
+            fh.write("|---" * (zz["G"] + 2) + "|\n")
+            for part in ("in-order", "zigzag"):
+                fh.write(f"| {part} | " + " | ".join(str(x) for x in zz[part]["ms"]) +
+                         f' | {zz[part]["max_over_min"]} |\n')
+        log(f"[bench] wrote {args.report_md}")
 
 
 REPORT_ORDER = ["tiny_l256", "decode_l8192", "batched_paged_64x4k_32k", "prefill_4096q_l65536",

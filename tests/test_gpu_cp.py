@@ -112,41 +112,17 @@ def test_topk_merge_matches_oracle(lib, G, K, kind):
 
 # ------------------------------------------------------ the share pipeline ---
 
-def _shards(b, G, align=64):
-    """Contiguous split of every sequence into G shards of whole 64-token
-    blocks; per shard the local caches (views of the same pools addressed
-    by local position), each row's local visible count and its range."""
+def _shards(b, G):
+    """Shard layouts (workloads.context_shards) with the binding's caches."""
     kc, vc = caches(b)
-    L = list(b.seq_lens)
-    S = [-(-Lb // (G * align)) * align for Lb in L]
-    rs, rp = _np(b.row_seq), _np(b.row_pos)
     out = []
-    for g in range(G):
-        lo = [min(g * Sb, Lb) for Sb, Lb in zip(S, L)]
-        hi = [min((g + 1) * Sb, Lb) for Sb, Lb in zip(S, L)]
-        if b.block_table is not None:
-            bt = b.block_table.cpu()
-            btl = torch.zeros_like(bt)
-            for s_ in range(len(L)):
-                nb = -(-(hi[s_] - lo[s_]) // align)
-                btl[s_, :nb] = bt[s_, lo[s_] // align: lo[s_] // align + nb]
-            btl = btl.cuda()
-            kcg = lisfa.KVCache(data=kc.data, scale=kc.scale, scale_group=kc.scale_group, block_table=btl,
-                                block_size=kc.block_size)
-            vcg = lisfa.KVCache(data=vc.data, scale=vc.scale, scale_group=vc.scale_group, block_table=btl,
-                                block_size=vc.block_size)
-        else:
-            sb = b.seq_base + torch.tensor(lo, dtype=torch.int64, device="cuda")
-            kcg = lisfa.KVCache(data=kc.data, scale=kc.scale, scale_group=kc.scale_group, seq_base=sb)
-            vcg = lisfa.KVCache(data=vc.data, scale=vc.scale, scale_group=vc.scale_group, seq_base=sb)
-        lo_r = np.array([lo[int(s_)] for s_ in rs], dtype=np.int64)
-        hi_r = np.array([hi[int(s_)] for s_ in rs], dtype=np.int64)
-        vis = np.clip(rp.astype(np.int64) + 1 - lo_r, 0, hi_r - lo_r)
-        out.append(dict(kc=kcg, vc=vcg, lo=lo_r, hi=hi_r,
-                        row_pos=torch.tensor(vis - 1, dtype=torch.int32, device="cuda"),
-                        pos_offset=torch.tensor(lo_r, dtype=torch.int32, device="cuda"),
-                        range=torch.tensor(np.stack([lo_r, hi_r], 1), dtype=torch.int32, device="cuda"),
-                        max_vis=int(vis.max()) if vis.size else 0))
+    for s in W.context_shards(b, G):
+        s = dict(s)
+        s["kc"] = lisfa.KVCache(data=kc.data, scale=kc.scale, scale_group=kc.scale_group,
+                                block_table=s["block_table"], block_size=kc.block_size, seq_base=s["seq_base"])
+        s["vc"] = lisfa.KVCache(data=vc.data, scale=vc.scale, scale_group=vc.scale_group,
+                                block_table=s["block_table"], block_size=vc.block_size, seq_base=s["seq_base"])
+        out.append(s)
     return out
 
 
