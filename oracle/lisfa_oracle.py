@@ -32,6 +32,13 @@ Inference Acceleration in Practice", section 4 name FP8 caches; the e4m3
 format itself is the OCP 8-bit floating point definition: 1 sign bit, 4
 exponent bits with bias 7, 3 mantissa bits, no infinities, S.1111.111 = NaN).
 Scaled values are code_value * scale, evaluated in float64.
+
+MXFP8 indexer ("Day0 Inference Adaptation and Performance Optimization for
+Kimi K3.1 Pro", section 4 and "... for a New Model", section 4: indexer
+queries and keys in MXFP8 with one shared scale per group of 32 elements):
+the block format is the OCP Microscaling (MX) definition - e4m3 elements and
+one E8M0 scale per 32 consecutive elements of a row, the scale byte e
+standing for 2^(e - 127) (e = 255 is NaN).  Values are code_value * 2^(e-127).
 """
 from __future__ import annotations
 
@@ -74,12 +81,57 @@ def decode_e4m3(codes: np.ndarray) -> np.ndarray:
     return _E4M3[np.asarray(codes).astype(np.intp)]
 
 
+def decode_e8m0(codes: np.ndarray) -> np.ndarray:
+    """E8M0 scale bytes -> float64: byte e is 2^(e - 127); 255 is NaN."""
+    e = np.asarray(codes).astype(np.int64)
+    out = np.ldexp(1.0, e - 127)
+    return np.where(e == 255, np.nan, out)
+
+
+def decode_mx(codes: np.ndarray, scales: np.ndarray, block: int = 32) -> np.ndarray:
+    """MX block values: codes [..., n] e4m3, scales [..., n / block] E8M0."""
+    v = decode_e4m3(codes)
+    return v * np.repeat(decode_e8m0(scales), block, axis=-1)
+
+
 def _decode(arr: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         return decode_bf16(arr)
-    if dtype == "fp8":
+    if dtype in ("fp8", "mxfp8"):
         return decode_e4m3(arr)
     raise ValueError(dtype)
+
+
+def encode_e4m3(v: np.ndarray) -> np.ndarray:
+    """float64 -> OCP e4m3 codes: saturate to +-448, then round to the nearest
+    representable value, ties to the even code (even mantissa)."""
+    v = np.asarray(v, dtype=np.float64)
+    mag = np.minimum(np.abs(v), 448.0)
+    pos = _E4M3[:0x7F]                        # codes 0x00..0x7E, increasing values
+    hi = np.clip(np.searchsorted(pos, mag, side="left"), 0, 0x7E)
+    lo = np.clip(hi - 1, 0, 0x7E)
+    d_hi = pos[hi] - mag
+    d_lo = mag - pos[lo]
+    pick_lo = (d_lo < d_hi) | ((d_lo == d_hi) & (lo % 2 == 0))
+    code = np.where(pick_lo, lo, hi).astype(np.uint8)
+    return np.where(np.signbit(v), code | np.uint8(0x80), code).astype(np.uint8)
+
+
+def mx_quantize(x: np.ndarray, block: int = 32):
+    """OCP MX conversion of rows x [..., n] (n a multiple of block) to MXFP8:
+    per block, shared exponent = floor(log2(max |x|)) - 8 (8 = exponent of
+    e4m3's largest normal), clamped to [-127, 127]; elements x / 2^shared
+    encoded as e4m3 (saturating, round to nearest even).  A block of zeros
+    gets scale 2^0 (the definition leaves it free).  Returns (codes uint8,
+    scale bytes uint8)."""
+    x = np.asarray(x, dtype=np.float64)
+    g = x.reshape(x.shape[:-1] + (x.shape[-1] // block, block))
+    amax = np.abs(g).max(axis=-1)
+    _, ex = np.frexp(amax)                   # amax = m * 2^ex, m in [0.5, 1)
+    shared = np.where(amax > 0, ex - 1 - 8, 0)
+    shared = np.clip(shared, -127, 127)
+    codes = encode_e4m3(g / np.ldexp(1.0, shared)[..., None])
+    return codes.reshape(x.shape), (shared + 127).astype(np.uint8)
 
 
 # ----------------------------------------------------------------------------
@@ -103,6 +155,8 @@ def slots(inp: Dict, seq: int, positions: np.ndarray) -> np.ndarray:
 def indexer_keys(inp: Dict, seq: int, n: int) -> np.ndarray:
     """Keys of positions 0..n-1 of a sequence, dequantised, [n, D_I] float64."""
     sl = slots(inp, seq, np.arange(n))
+    if inp["indexer_dtype"] == "mxfp8":
+        return decode_mx(inp["k_data"][sl], inp["k_scale"][sl])
     k = _decode(inp["k_data"][sl], inp["indexer_dtype"])
     if inp["indexer_dtype"] == "fp8":
         k = k * inp["k_scale"][sl].astype(np.float64)[:, None]
@@ -120,6 +174,8 @@ def latent_rows(inp: Dict, seq: int, positions: np.ndarray) -> np.ndarray:
 
 
 def indexer_query(inp: Dict, r: int) -> np.ndarray:
+    if inp["indexer_dtype"] == "mxfp8":
+        return decode_mx(inp["q_idx"][r], inp["q_scale"][r])
     q = _decode(inp["q_idx"][r], inp["indexer_dtype"])
     if inp["indexer_dtype"] == "fp8":
         qs = np.asarray(inp["q_scale"][r], dtype=np.float64)

@@ -39,7 +39,7 @@ class Workload:
     D_rope: int = 64
     softmax_scale: float = 1.0 / math.sqrt(576.0)
     # storage
-    indexer_dtype: str = "bf16"     # "bf16" | "fp8"
+    indexer_dtype: str = "bf16"     # "bf16" | "fp8" | "mxfp8" (e4m3 + E8M0 scale per 32 elements)
     kv_dtype: str = "bf16"          # "bf16" | "fp8"
     paged: bool = False
     block_size: int = 64
@@ -94,8 +94,14 @@ M32K_B1 = Workload(
     name="decode_paged_1x32768", seed=6, mode="decode", num_seqs=1, seq_len=32768,
     paged=True)
 
+# The headline point with the pages' MXFP8 indexer (queries and keys e4m3 with
+# one E8M0 scale per 32 elements; "Day0 ... for Kimi K3.1 Pro", section 4).
+M32K_B64_MX = Workload(
+    name="decode_paged_64x32768_mxfp8", seed=7, mode="decode", num_seqs=64, seq_len=32768,
+    paged=True, indexer_dtype="mxfp8")
+
 CONFIGS = [TINY, DECODE_8K, BATCHED_PAGED, PREFILL_64K, FP8_LONG]
-BENCH = {w.name: w for w in CONFIGS + [M32K_B64, M32K_B1]}
+BENCH = {w.name: w for w in CONFIGS + [M32K_B64, M32K_B1, M32K_B64_MX]}
 
 
 def get(name: str) -> Workload:

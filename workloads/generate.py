@@ -88,6 +88,21 @@ def quantize_e4m3(x: torch.Tensor, dim) -> (torch.Tensor, torch.Tensor):
     return codes, scale
 
 
+def quantize_mx(x: torch.Tensor, block: int = 32) -> (torch.Tensor, torch.Tensor):
+    """MXFP8 (OCP MX): per block of 32 consecutive elements of the last dim,
+    shared exponent floor(log2(amax)) - 8 clamped to [-127, 127] (0 for an
+    all-zero block); elements x / 2^shared saturated to +-448 and rounded to
+    e4m3 (nearest even).  Returns (e4m3 codes, E8M0 scale bytes)."""
+    shape = x.shape
+    g = x.to(torch.float32).reshape(*shape[:-1], shape[-1] // block, block)
+    amax = g.abs().amax(dim=-1)
+    _, e = torch.frexp(amax)
+    shared = torch.where(amax > 0, e - 9, torch.zeros_like(e)).clamp(-127, 127)
+    y = (g / torch.ldexp(torch.ones_like(amax), shared)[..., None]).clamp(-E4M3_MAX, E4M3_MAX)
+    codes = y.to(torch.float8_e4m3fn).view(torch.uint8).reshape(shape)
+    return codes, (shared + 127).to(torch.uint8)
+
+
 def _values(wl: Workload, shape, gen, device, std=1.0) -> torch.Tensor:
     if wl.dist == "int8range":
         return torch.randint(-8, 9, shape, generator=gen, device=device).to(torch.float32)
@@ -143,10 +158,14 @@ def make_batch(wl: Workload, device="cpu", chunk_tokens: int = 1 << 16) -> Batch
         return seq_base[b] + pos
 
     fp8_idx = wl.indexer_dtype == "fp8"
+    mx_idx = wl.indexer_dtype == "mxfp8"
     fp8_kv = wl.kv_dtype == "fp8"
 
     # 3. indexer keys
-    if fp8_idx:
+    if mx_idx:
+        k_data = torch.full((num_slots, wl.D_I), E4M3_NAN_BITS, dtype=torch.uint8, device=device)
+        k_scale = torch.full((num_slots, wl.D_I // 32), 255, dtype=torch.uint8, device=device)
+    elif fp8_idx:
         k_data = torch.full((num_slots, wl.D_I), E4M3_NAN_BITS, dtype=torch.uint8, device=device)
         k_scale = torch.full((num_slots,), float("nan"), dtype=torch.float32, device=device)
     else:
@@ -158,7 +177,11 @@ def make_batch(wl: Workload, device="cpu", chunk_tokens: int = 1 << 16) -> Batch
             p1 = min(L, p0 + chunk_tokens)
             sl = slots_of(b, p0, p1).to(device)
             x = _values(wl, (p1 - p0, wl.D_I), dev_gen, device)
-            if fp8_idx:
+            if mx_idx:
+                codes, sc = quantize_mx(x)
+                k_data[sl] = codes
+                k_scale[sl] = sc
+            elif fp8_idx:
                 if wl.dist == "int8range":
                     codes = x.to(torch.float8_e4m3fn).view(torch.uint8)
                     sc = torch.ones(p1 - p0, 1, device=device)
@@ -218,7 +241,9 @@ def make_batch(wl: Workload, device="cpu", chunk_tokens: int = 1 << 16) -> Batch
     R = int(row_pos.shape[0])
 
     xq = _values(wl, (R, wl.H_I, wl.D_I), dev_gen, device)
-    if fp8_idx:
+    if mx_idx:
+        q_idx, q_scale = quantize_mx(xq)
+    elif fp8_idx:
         if wl.dist == "int8range":
             q_idx = xq.to(torch.float8_e4m3fn).view(torch.uint8)
             q_scale = torch.ones(R, dtype=torch.float32, device=device)
