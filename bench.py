@@ -40,8 +40,8 @@ def algorithmic(wl, b):
     R = b.R
     pos = [int(p) for p in b.row_pos.tolist()]
     seq = [int(s) for s in b.row_seq.tolist()]
-    ke = 1 if wl.indexer_dtype == "fp8" else 2
-    ks = 4 if wl.indexer_dtype == "fp8" else 0
+    ke = 1 if wl.indexer_dtype in ("fp8", "mxfp8") else 2
+    ks = {"fp8": 4, "mxfp8": wl.D_I // 32}.get(wl.indexer_dtype, 0)   # scale bytes per key (or query head)
     ve = 1 if wl.kv_dtype == "fp8" else 2
     vs = 4 if wl.kv_dtype == "fp8" else 0
     vis = sum(p + 1 for p in pos)
@@ -52,7 +52,8 @@ def algorithmic(wl, b):
         seq_sel[s] = seq_sel.get(s, 0) + min(wl.K, p + 1)
     keys = sum(seq_vis.values())
     rows = sum(min(seq_sel[s], seq_vis[s]) for s in seq_vis)
-    li_bytes = keys * (wl.D_I * ke + ks) + R * (wl.H_I * (wl.D_I * ke + 4) + ks)
+    qs = wl.H_I * ks if wl.indexer_dtype == "mxfp8" else ks
+    li_bytes = keys * (wl.D_I * ke + ks) + R * (wl.H_I * (wl.D_I * ke + 4) + qs)
     li_flops = 2.0 * wl.H_I * wl.D_I * vis
     sfa_bytes = rows * (wl.D_qk * ve + vs) + R * wl.H * (wl.D_qk * 2 + wl.D_v * 2 + 4) + sel * 4
     sfa_flops = 2.0 * wl.H * sel * (wl.D_qk + wl.D_v)
@@ -452,7 +453,7 @@ def run_workload(args, wl, cold=False, graph=False):
 
     def peak_tflops(name):
         # the indexer's contraction runs on fp8 MFMA for fp8 keys; sparse MLA always on bf16 MFMA
-        return FP8_PEAK_TFLOPS if (name == "li" and wl.indexer_dtype == "fp8") else BF16_PEAK_TFLOPS
+        return FP8_PEAK_TFLOPS if (name == "li" and wl.indexer_dtype in ("fp8", "mxfp8")) else BF16_PEAK_TFLOPS
 
     def roof(name, t, bound):
         by, fl = alg[name]
@@ -634,8 +635,8 @@ def cp_share_timing(args, wl, G):
         times[name] = time_on_stream(fn, stream, 2, args.steps, graph=True) * 1e6
     total = sum(times.values())
     vis_local = int((s0["row_pos"].to(torch.int64) + 1).clamp(min=0).sum().item())
-    ke = 1 if wl.indexer_dtype == "fp8" else 2
-    ks = 4 if wl.indexer_dtype == "fp8" else 0
+    ke = 1 if wl.indexer_dtype in ("fp8", "mxfp8") else 2
+    ks = {"fp8": 4, "mxfp8": wl.D_I // 32}.get(wl.indexer_dtype, 0)
     li_bytes = vis_local * (wl.D_I * ke + ks) + R * (wl.H_I * (wl.D_I * ke + 4) + ks)
     res = dict(workload=wl.name, G=G, rank=0, rows=R, local_positions=vis_local,
                us={k: round(v, 2) for k, v in times.items()}, share_us=round(total, 2),
@@ -724,7 +725,8 @@ def report_cp(args):
 
 
 REPORT_ORDER = ["tiny_l256", "decode_l8192", "batched_paged_64x4k_32k", "prefill_4096q_l65536",
-                "fp8_decode_16x131072", "decode_paged_1x32768", "decode_paged_64x32768"]
+                "fp8_decode_16x131072", "decode_paged_1x32768", "decode_paged_64x32768",
+                "decode_paged_64x32768_mxfp8"]
 
 
 def write_report_md(path, lines, args):

@@ -60,6 +60,10 @@ typedef struct ihipStream_t* lisfa_stream_t; /* a hipStream_t */
 /* element types of stored tensors */
 #define LISFA_BF16      0   /* bfloat16 */
 #define LISFA_FP8_E4M3  1   /* OCP e4m3 (max 448), scaled by fp32 factors */
+#define LISFA_MXFP8     2   /* OCP MX block format: e4m3 elements, one E8M0 scale byte
+                               (2^(e-127)) per 32 consecutive elements of a row; indexer
+                               queries and keys only ("Day0 Inference Adaptation and
+                               Performance Optimization for Kimi K3.1 Pro", section 4) */
 
 /*
  * A cache of fixed-width rows, one per token slot ("Kimi New Model Open
@@ -71,13 +75,16 @@ typedef struct ihipStream_t* lisfa_stream_t; /* a hipStream_t */
  * The row of slot t starts at data + t * row_stride_bytes.
  * fp8 rows are multiplied by scale[t / scale_group_tokens] (scale_group_tokens
  * consecutive physical slots share one fp32 factor; 1 = per token).
+ * mxfp8 rows (width a multiple of 32): scale points to E8M0 bytes
+ * [num_slots, width / 32]; element i of slot t is code * 2^(scale[t][i/32] - 127).
  */
 typedef struct {
     const void*    data;               /* [num_slots, row_stride_bytes] */
     int64_t        num_slots;          /* slots in the pool (bounds checks) */
-    int32_t        dtype;              /* LISFA_BF16 or LISFA_FP8_E4M3 */
+    int32_t        dtype;              /* LISFA_BF16, LISFA_FP8_E4M3 or LISFA_MXFP8 */
     int32_t        row_stride_bytes;   /* multiple of 16, >= row width in bytes */
-    const float*   scale;              /* fp8: [num_slots / scale_group_tokens]; bf16: NULL */
+    const void*    scale;              /* fp8: fp32 [num_slots / scale_group_tokens];
+                                          mxfp8: uint8 E8M0 [num_slots, width / 32]; bf16: NULL */
     int32_t        scale_group_tokens; /* fp8: >= 1 */
     int32_t        block_size;         /* paged: tokens per block (> 0) */
     const int32_t* block_table;        /* paged: [num_seqs, bt_stride], else NULL */
@@ -88,9 +95,10 @@ typedef struct {
 
 /* Lightning indexer inputs (one query row per r). */
 typedef struct {
-    const void*    q;            /* [R, H_I, D_I] bf16 or e4m3 (same dtype as k_cache) */
-    const float*   q_scale;      /* fp8: [R] (per query token) or [R, H_I]; bf16: NULL */
-    int32_t        q_scale_per_head; /* fp8: 0 = [R], 1 = [R, H_I] */
+    const void*    q;            /* [R, H_I, D_I] bf16 or e4m3 codes (same dtype as k_cache) */
+    const void*    q_scale;      /* fp8: fp32 [R] (per query token) or [R, H_I];
+                                    mxfp8: uint8 E8M0 [R, H_I, D_I / 32]; bf16: NULL */
+    int32_t        q_scale_per_head; /* fp8: 0 = [R], 1 = [R, H_I]; otherwise ignored */
     const float*   w;            /* [R, H_I] fp32 head weights */
     lisfa_cache    k_cache;      /* rows of D_I elements */
     const int32_t* row_seq;      /* [R] sequence of each query row */
@@ -128,6 +136,9 @@ typedef struct {
  * Scores are accumulated in fp32 (products of bf16 or e4m3 values are exact
  * in fp32).  fp8: score = k_scale[slot] * sum_j (w_j * q_scale) * ReLU(q8.k8),
  * which equals the definition because the scales are positive.
+ * mxfp8 (D_I = 128): the dot products run on gfx950's block-scaled MFMA, which
+ * applies the query's and the key's E8M0 scale to each 32-element block; rows
+ * are scored one by one (rows_per_group is a hint that mxfp8 does not use).
  */
 int li_score(const lisfa_indexer_args* args, float* scores, int64_t ld_scores,
              lisfa_stream_t stream);

@@ -67,7 +67,8 @@ class KVCache:
     """A cache of fixed-width rows (indexer keys or MLA latent rows).
 
     data:        [num_slots, width] bf16, or uint8 e4m3 codes
-    scale:       fp8 only: fp32 [num_slots // scale_group]
+    scale:       fp8: fp32 [num_slots // scale_group]; mxfp8 (uint8 scale):
+                 E8M0 bytes [num_slots, width // 32]
     block_table: paged layout: int32 [num_seqs, blocks_per_seq]
     seq_base:    contiguous layout: int64 [num_seqs] first slot of each sequence
     """
@@ -82,6 +83,16 @@ class KVCache:
     def fp8(self) -> bool:
         return self.data.dtype == torch.uint8
 
+    @property
+    def mx(self) -> bool:
+        return self.fp8 and self.scale is not None and self.scale.dtype == torch.uint8
+
+    @property
+    def dtype_code(self) -> int:
+        if self.mx:
+            return _c.LISFA_MXFP8
+        return _c.LISFA_FP8_E4M3 if self.fp8 else _c.LISFA_BF16
+
     def c_struct(self) -> _c.Cache:
         d = self.data
         if d.dim() != 2:
@@ -92,11 +103,11 @@ class KVCache:
             raise ValueError("block_table must be int32")
         if self.seq_base is not None and self.seq_base.dtype != torch.int64:
             raise ValueError("seq_base must be int64")
-        if self.fp8 and (self.scale is None or self.scale.dtype != torch.float32):
-            raise ValueError("fp8 caches need fp32 scales")
+        if self.fp8 and (self.scale is None or self.scale.dtype not in (torch.float32, torch.uint8)):
+            raise ValueError("fp8 caches need fp32 scales (e4m3) or uint8 E8M0 scales (mxfp8)")
         return _c.Cache(
             data=_ptr(d), num_slots=d.shape[0],
-            dtype=_c.LISFA_FP8_E4M3 if self.fp8 else _c.LISFA_BF16,
+            dtype=self.dtype_code,
             row_stride_bytes=d.stride(0) * d.element_size(),
             scale=_ptr(self.scale), scale_group_tokens=self.scale_group,
             block_size=self.block_size, block_table=_ptr(self.block_table),
@@ -111,9 +122,9 @@ def _check(code: int, where: str):
 
 def _indexer_args(q_idx, w, k_cache, row_seq, row_pos, max_visible, q_scale, rows_per_group):
     R, H_I, D_I = q_idx.shape
-    if q_scale is not None and q_scale.dtype != torch.float32:
-        raise ValueError("q_scale must be fp32")
-    per_head = q_scale is not None and q_scale.dim() == 2
+    if q_scale is not None and q_scale.dtype not in (torch.float32, torch.uint8):
+        raise ValueError("q_scale must be fp32 (e4m3) or uint8 E8M0 (mxfp8)")
+    per_head = q_scale is not None and q_scale.dtype == torch.float32 and q_scale.dim() == 2
     for t, dt in ((w, torch.float32), (row_seq, torch.int32), (row_pos, torch.int32)):
         if t.dtype != dt:
             raise ValueError(f"expected {dt}, got {t.dtype}")

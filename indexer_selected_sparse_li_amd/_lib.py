@@ -17,6 +17,7 @@ LISFA_ERR_UNSUPPORTED = -6
 
 LISFA_BF16 = 0
 LISFA_FP8_E4M3 = 1
+LISFA_MXFP8 = 2
 
 LISFA_OP_TOPK = 0
 LISFA_OP_SPARSE_MLA = 1

@@ -6,7 +6,7 @@
 
 namespace lisfa {
 
-hipError_t li_score_dispatch(const IndexerDev& a, int D_I, int fp8, int qg, float* scores, int64_t ld,
+hipError_t li_score_dispatch(const IndexerDev& a, int D_I, int dtype, int qg, float* scores, int64_t ld,
                              int64_t max_visible, hipStream_t stream);
 hipError_t topk_dispatch(const float* scores, int64_t ld, const int32_t* row_pos, int R, int K,
                          int32_t* idx, void* ws, hipStream_t stream);
@@ -37,7 +37,7 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 
 int check_cache(const lisfa_cache& c, int width) {
     if (!c.data) return LISFA_ERR_NULL_ARG;
-    if (c.dtype != LISFA_BF16 && c.dtype != LISFA_FP8_E4M3) return LISFA_ERR_BAD_DTYPE;
+    if (c.dtype != LISFA_BF16 && c.dtype != LISFA_FP8_E4M3 && c.dtype != LISFA_MXFP8) return LISFA_ERR_BAD_DTYPE;
     const int elt = c.dtype == LISFA_BF16 ? 2 : 1;
     if (c.row_stride_bytes < width * elt || c.row_stride_bytes % 16 != 0) return LISFA_ERR_BAD_SHAPE;
     if (!aligned(c.data, 16)) return LISFA_ERR_BAD_SHAPE;
@@ -45,6 +45,11 @@ int check_cache(const lisfa_cache& c, int width) {
     if (c.dtype == LISFA_FP8_E4M3) {
         if (!c.scale) return LISFA_ERR_NULL_ARG;
         if (c.scale_group_tokens < 1) return LISFA_ERR_BAD_SHAPE;
+    }
+    if (c.dtype == LISFA_MXFP8) {
+        if (!c.scale) return LISFA_ERR_NULL_ARG;
+        if (width % 32 != 0) return LISFA_ERR_BAD_SHAPE;
+        if (!aligned(c.scale, 4)) return LISFA_ERR_BAD_SHAPE;
     }
     if (c.block_table) {
         if (c.block_size < 1 || c.block_size > (1 << 20) || (c.block_size & (c.block_size - 1)))
@@ -60,7 +65,8 @@ CacheDev to_dev(const lisfa_cache& c) {
     CacheDev d;
     d.data = (const uint8_t*)c.data;
     d.num_slots = c.num_slots;
-    d.scale = c.scale;
+    d.scale = c.dtype == LISFA_FP8_E4M3 ? (const float*)c.scale : nullptr;
+    d.mx_scale = c.dtype == LISFA_MXFP8 ? (const uint8_t*)c.scale : nullptr;
     d.block_table = c.block_table;
     d.seq_base = c.seq_base_slot;
     d.row_stride = c.row_stride_bytes;
@@ -84,7 +90,11 @@ int check_indexer(const lisfa_indexer_args* a) {
     if (!a->q || !a->w || !a->row_seq || !a->row_pos) return LISFA_ERR_NULL_ARG;
     int e = check_cache(a->k_cache, a->D_I);
     if (e) return e;
-    if (a->k_cache.dtype == LISFA_FP8_E4M3) {
+    if (a->k_cache.dtype == LISFA_MXFP8) {
+        if (a->D_I != 128) return LISFA_ERR_UNSUPPORTED;
+        if (!a->q_scale) return LISFA_ERR_NULL_ARG;
+        if (!aligned(a->q, 16)) return LISFA_ERR_BAD_SHAPE;
+    } else if (a->k_cache.dtype == LISFA_FP8_E4M3) {
         if (!a->q_scale) return LISFA_ERR_NULL_ARG;
         if (!aligned(a->q, 8)) return LISFA_ERR_BAD_SHAPE;
     } else if (!aligned(a->q, 16)) {
@@ -96,7 +106,9 @@ int check_indexer(const lisfa_indexer_args* a) {
 IndexerDev to_dev(const lisfa_indexer_args* a) {
     IndexerDev d;
     d.q = (const uint8_t*)a->q;
-    d.q_scale = a->q_scale;
+    const bool mx = a->k_cache.dtype == LISFA_MXFP8;
+    d.q_scale = mx ? nullptr : (const float*)a->q_scale;
+    d.q_mx_scale = mx ? (const uint8_t*)a->q_scale : nullptr;
     d.w = a->w;
     d.row_seq = a->row_seq;
     d.row_pos = a->row_pos;
@@ -117,6 +129,7 @@ int check_mla(const lisfa_mla_args* a) {
     if (a->R == 0) return LISFA_OK;
     if (!a->q || !a->row_seq) return LISFA_ERR_NULL_ARG;
     if (!aligned(a->q, 16)) return LISFA_ERR_BAD_SHAPE;
+    if (a->kv_cache.dtype == LISFA_MXFP8) return LISFA_ERR_BAD_DTYPE;
     return check_cache(a->kv_cache, a->D_latent + a->D_rope);
 }
 
@@ -214,8 +227,8 @@ int li_score(const lisfa_indexer_args* args, float* scores, int64_t ld_scores, l
     if (ld_scores < args->max_visible) return LISFA_ERR_BAD_SHAPE;
     const IndexerDev d = to_dev(args);
     const int qg = (args->rows_per_group % 8 == 0) ? 8 : 1;
-    return hip_status(li_score_dispatch(d, args->D_I, args->k_cache.dtype == LISFA_FP8_E4M3, qg, scores,
-                                        ld_scores, args->max_visible, (hipStream_t)stream));
+    return hip_status(li_score_dispatch(d, args->D_I, args->k_cache.dtype, qg, scores, ld_scores,
+                                        args->max_visible, (hipStream_t)stream));
 }
 
 int topk_select(const float* scores, int64_t ld_scores, const int32_t* row_pos, int32_t R, int32_t K,
@@ -342,7 +355,8 @@ int li_topk_sfa(const lisfa_indexer_args* iargs, const lisfa_mla_args* margs, in
     const int64_t ld = scores_ld(iargs->max_visible) > 0 ? scores_ld(iargs->max_visible) : 64;
     const int64_t rc = fused_chunk_rows(R, iargs->max_visible);
     const int qg = (iargs->rows_per_group % 8 == 0) ? 8 : 1;
-    const int elt = iargs->k_cache.dtype == LISFA_FP8_E4M3 ? 1 : 2;
+    const int elt = iargs->k_cache.dtype == LISFA_BF16 ? 2 : 1;
+    const bool mx = iargs->k_cache.dtype == LISFA_MXFP8;
     IndexerDev d = to_dev(iargs);
     for (int64_t c0 = 0; c0 < R; c0 += rc) {
         const int64_t c1 = c0 + rc < R ? c0 + rc : R;
@@ -351,10 +365,12 @@ int li_topk_sfa(const lisfa_indexer_args* iargs, const lisfa_mla_args* margs, in
         dc.q = d.q + c0 * (int64_t)iargs->H_I * iargs->D_I * elt;
         dc.w = d.w + c0 * iargs->H_I;
         if (d.q_scale) dc.q_scale = d.q_scale + c0 * (iargs->q_scale_per_head ? iargs->H_I : 1);
+        if (mx) dc.q_mx_scale = d.q_mx_scale + c0 * (int64_t)iargs->H_I * (iargs->D_I / 32);
         dc.row_seq = d.row_seq + c0;
         dc.row_pos = d.row_pos + c0;
         if (iargs->max_visible > 0) {
-            hipError_t he = li_score_dispatch(dc, iargs->D_I, elt == 1, qg, scores, ld, iargs->max_visible, st);
+            hipError_t he = li_score_dispatch(dc, iargs->D_I, iargs->k_cache.dtype, qg, scores, ld,
+                                              iargs->max_visible, st);
             if (he != hipSuccess) return LISFA_ERR_HIP;
         }
         hipError_t he = topk_dispatch(scores, ld, dc.row_pos, dc.R, K, idx + c0 * K, w + L.cand, st);

@@ -34,7 +34,8 @@ constexpr float kLn2 = 0.6931471805599453f;
 struct CacheDev {
     const uint8_t* data;
     int64_t num_slots;
-    const float* scale;
+    const float* scale;          // fp8: fp32 factor per scale group
+    const uint8_t* mx_scale;     // mxfp8: E8M0 byte per 32 elements, [num_slots, width / 32]
     const int32_t* block_table;
     const int64_t* seq_base;
     int32_t row_stride;      // bytes
@@ -47,7 +48,8 @@ struct CacheDev {
 
 struct IndexerDev {
     const uint8_t* q;
-    const float* q_scale;
+    const float* q_scale;        // fp8: [R] or [R, H_I]
+    const uint8_t* q_mx_scale;   // mxfp8: E8M0 [R, H_I, D_I / 32]
     const float* w;
     const int32_t* row_seq;
     const int32_t* row_pos;

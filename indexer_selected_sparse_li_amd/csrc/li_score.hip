@@ -21,7 +21,8 @@
 // (A = the query's heads, held in VGPRs; B = K^T from LDS).  In the 16x16
 // accumulator lane l holds key l%16 and 4 heads per M-tile, so the weighted
 // ReLU sum over heads is 4*MT fused multiply-adds plus two lane exchanges.
-// Scores are fp32 end to end.
+// Scores are fp32 end to end.  MXFP8 keys (one E8M0 scale per 32 elements)
+// use the block-scaled MFMA decode kernel further down.
 #include "common.hpp"
 
 namespace lisfa {
@@ -431,6 +432,168 @@ __global__ __launch_bounds__(64 * kLiDecWaves) void li_score_dec_kernel(IndexerD
     }
 }
 
+// Decode with MXFP8 queries and keys -------------------------------------------
+//
+// The pages' indexer format ("Day0 Inference Adaptation and Performance
+// Optimization for Kimi K3.1 Pro", section 4; "... for a New Model", section
+// 4): e4m3 elements with one power-of-two (E8M0) scale per 32 consecutive
+// elements, here D_I = 128 = four blocks per row.  gfx950's block-scaled MFMA
+// v_mfma_scale_f32_16x16x128_f8f6f4 multiplies a 16 x 128 e4m3 block of
+// queries (heads) by a 128 x 16 block of keys and applies both operands' E8M0
+// scales per 32-element block, so one instruction per (16-head tile, 16-key
+// subtile) yields the exact scaled dot products.  Operand layout (checked
+// bit-exactly on the GPU): lane l holds row l % 16, bytes [16 g, 16 g + 16)
+// and [64 + 16 g, 64 + 16 g + 16) of it (g = l / 16), and supplies the scale
+// of row l % 16, block g in byte 0 of its scale operand.  The accumulator
+// layout is that of the other 16x16 MFMAs (lane = key l % 16, 4 heads per
+// tile).  Otherwise the kernel is the bf16 decode kernel: subtiles streamed
+// into registers kLiMxPrefetch deep, ReLU as an integer max, head sum by two
+// permlane swaps.  132 bytes per key instead of 256.
+constexpr int kLiMxPrefetch = 8;
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ i32x8 mx_operand(const uint8_t* row, int g) {
+    const u32x4 lo = __builtin_nontemporal_load((const u32x4*)(row + 16 * g));
+    const u32x4 hi = __builtin_nontemporal_load((const u32x4*)(row + 64 + 16 * g));
+    return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+template <int MT>
+__global__ __launch_bounds__(64 * kLiDecWaves) void li_score_mx_kernel(IndexerDev a, float* __restrict__ scores,
+                                                                    int64_t ld, int keys_per_wg) {
+    constexpr int DI = 128;
+    constexpr int NB = DI / 32;          // scale blocks per row
+    constexpr int NT = 64 * kLiDecWaves;
+    constexpr int P = kLiMxPrefetch;
+    __shared__ int64_t blk_slot0[kLiMaxBlocks];
+    __shared__ int32_t blk_lim[kLiMaxBlocks];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = blockIdx.y;
+    const int64_t c0 = (int64_t)blockIdx.x * keys_per_wg;
+    int64_t vis = (int64_t)a.row_pos[r] + 1;
+    if (vis < 0) vis = 0;
+    if (vis > ld) vis = ld;
+    const int64_t kend = (c0 + keys_per_wg < vis) ? c0 + keys_per_wg : vis;
+    if (c0 >= kend) return;  // uniform across the workgroup
+    const int seq = a.row_seq[r];
+
+    // block map of [c0, kend) (contiguous caches: virtual 64-token blocks)
+    const bool seq_ok = seq >= 0 && seq < a.k.num_seqs;
+    const int sh = a.k.paged ? a.k.bs_shift : 6;
+    const int64_t bsz = (int64_t)1 << sh;
+    const int64_t b0 = c0 >> sh;
+    {
+        const int nb = (int)(((kend - 1) >> sh) - b0 + 1);
+        for (int i = tid; i < nb; i += NT) {
+            const int64_t blk = b0 + i;
+            int64_t s0 = -1;
+            if (seq_ok) {
+                if (a.k.paged) {
+                    if (blk < a.k.bt_stride) {
+                        const int32_t b = a.k.block_table[(int64_t)seq * a.k.bt_stride + blk];
+                        if (b >= 0) s0 = (int64_t)b << sh;
+                    }
+                } else {
+                    s0 = a.k.seq_base[seq] + blk * bsz;
+                }
+            }
+            int64_t lim = 0;
+            if (s0 >= 0 && s0 < a.k.num_slots) {
+                lim = a.k.num_slots - s0;
+                lim = lim < bsz ? lim : bsz;
+            }
+            blk_slot0[i] = s0;
+            blk_lim[i] = (int32_t)lim;
+        }
+    }
+
+    // query operand of head tile mt (row = head mt * 16 + l % 16) with its
+    // E8M0 scale (block g), and head weights in the accumulator layout
+    const int g = lane >> 4;
+    i32x8 qa[MT];
+    int qs[MT];
+    float wv[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int head = mt * 16 + (lane & 15);
+        if (head < a.H_I) {
+            const int64_t hr = (int64_t)r * a.H_I + head;
+            qa[mt] = mx_operand(a.q + hr * DI, g);
+            qs[mt] = a.q_mx_scale[hr * NB + g];
+        } else {
+            qa[mt] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+            qs[mt] = 127;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int h = mt * 16 + 4 * g + i;
+            wv[mt][i] = h < a.H_I ? a.w[(int64_t)r * a.H_I + h] : 0.f;
+        }
+    }
+    __syncthreads();  // block map ready
+
+    const int nsub = (int)((kend - c0 + 15) / 16);
+    const int mine = nsub > wave ? (nsub - wave + kLiDecWaves - 1) / kLiDecWaves : 0;
+    // lane's key row in subtile i of this wave (the zero row, scale 2^0 and
+    // factor NaN when the position is past the row or not addressable)
+    auto fetch = [&](int i, i32x8& kb, int& ksc, float& fac) {
+        const int64_t key = c0 + (int64_t)(wave + i * kLiDecWaves) * 16 + (lane & 15);
+        const uint8_t* row = g_li_zero_row;
+        ksc = 127;
+        fac = __builtin_nanf("");
+        if (i < mine && key < kend) {
+            const int bi = (int)((key >> sh) - b0);
+            const int off = (int)(key & (bsz - 1));
+            if (off < blk_lim[bi]) {
+                const int64_t slot = blk_slot0[bi] + off;
+                row = a.k.data + slot * a.k.row_stride;
+                ksc = a.k.mx_scale[slot * NB + g];
+                fac = 1.f;
+            }
+        }
+        kb = mx_operand(row, g);
+    };
+    static_assert(DI <= 256, "zero row covers one key row");
+
+    i32x8 kbuf[P];
+    int ksc[P];
+    float fac[P];
+#pragma unroll
+    for (int j = 0; j < P; ++j) fetch(j, kbuf[j], ksc[j], fac[j]);
+    for (int i0 = 0; i0 < mine; i0 += P) {
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            const int i = i0 + j;
+            f32x4 acc[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[mt], kbuf[j], f32x4{0.f, 0.f, 0.f, 0.f},
+                                                                         0, 0, 0, qs[mt], 0, ksc[j]);
+            const float f = fac[j];
+            fetch(i + P, kbuf[j], ksc[j], fac[j]);
+            float part = 0.f;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int bits = __float_as_int(acc[mt][q]);
+                    part = fmaf(wv[mt][q], __int_as_float(bits > 0 ? bits : 0), part);
+                }
+            {
+                const auto w16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+                part = __uint_as_float(w16[0]) + __uint_as_float(w16[1]);
+                const auto w32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+                part = __uint_as_float(w32[0]) + __uint_as_float(w32[1]);
+            }
+            const int64_t key = c0 + (int64_t)(wave + i * kLiDecWaves) * 16 + lane;
+            if (lane < 16 && key < kend) scores[(int64_t)r * ld + key] = part * f;
+        }
+    }
+}
+
 // host-side launcher ---------------------------------------------------------
 
 template <int DI, int MT, int QG, bool FP8>
@@ -482,9 +645,37 @@ static hipError_t launch_li_dec(const IndexerDev& a, float* scores, int64_t ld, 
     return hipGetLastError();
 }
 
-hipError_t li_score_dispatch(const IndexerDev& a, int D_I, int fp8, int qg, float* scores, int64_t ld,
+template <int MT>
+static hipError_t launch_li_mx(const IndexerDev& a, float* scores, int64_t ld, int64_t max_visible,
+                               hipStream_t stream) {
+    const int sh = a.k.paged ? a.k.bs_shift : 6;
+    const int64_t bsz = (int64_t)1 << sh;
+    const int64_t want_wg = 512;
+    int64_t nchunk = (want_wg + a.R - 1) / a.R;
+    int64_t kpw = (max_visible + nchunk - 1) / nchunk;
+    if (kpw < 1024) kpw = 1024;
+    const int64_t align = bsz > 64 ? bsz : 64;
+    kpw = (kpw + align - 1) / align * align;
+    const int64_t cap = (int64_t)(kLiMaxBlocks - 1) * bsz / align * align;
+    if (kpw > cap) kpw = cap;
+    if (kpw > (1 << 30)) kpw = (int64_t)(1 << 30) / align * align;
+    nchunk = (max_visible + kpw - 1) / kpw;
+    if (nchunk < 1) nchunk = 1;
+    dim3 grid((unsigned)nchunk, (unsigned)a.R);
+    hipLaunchKernelGGL((li_score_mx_kernel<MT>), grid, dim3(64 * kLiDecWaves), 0, stream, a, scores, ld, (int)kpw);
+    return hipGetLastError();
+}
+
+hipError_t li_score_dispatch(const IndexerDev& a, int D_I, int dtype, int qg, float* scores, int64_t ld,
                              int64_t max_visible, hipStream_t stream) {
     const int mt = a.H_I <= 16 ? 1 : (a.H_I <= 32 ? 2 : 4);
+    if (dtype == LISFA_MXFP8) {   // one row at a time whatever the grouping
+        if (D_I != 128) return hipErrorInvalidValue;
+        if (mt == 4) return launch_li_mx<4>(a, scores, ld, max_visible, stream);
+        if (mt == 2) return launch_li_mx<2>(a, scores, ld, max_visible, stream);
+        return launch_li_mx<1>(a, scores, ld, max_visible, stream);
+    }
+    const int fp8 = dtype == LISFA_FP8_E4M3;
     if (qg == 1 && fp8 == 0) {
         if (D_I == 128 && mt == 4) return launch_li_dec<128, 4>(a, scores, ld, max_visible, stream);
         if (D_I == 128 && mt == 2) return launch_li_dec<128, 2>(a, scores, ld, max_visible, stream);

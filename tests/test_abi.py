@@ -108,6 +108,12 @@ def _mla_args(**kw):
     (dict(k_cache=_fake_cache(seq_base_slot=None)), C.LISFA_ERR_NULL_ARG),
     (dict(k_cache=_fake_cache(block_table=16, block_size=48, bt_stride=4)), C.LISFA_ERR_BAD_SHAPE),
     (dict(q=18), C.LISFA_ERR_BAD_SHAPE),
+    (dict(k_cache=_fake_cache(dtype=C.LISFA_MXFP8, row_stride_bytes=128)), C.LISFA_ERR_NULL_ARG),
+    (dict(k_cache=_fake_cache(dtype=C.LISFA_MXFP8, row_stride_bytes=128, scale=17), q_scale=16),
+     C.LISFA_ERR_BAD_SHAPE),
+    (dict(k_cache=_fake_cache(dtype=C.LISFA_MXFP8, row_stride_bytes=128, scale=16)), C.LISFA_ERR_NULL_ARG),
+    (dict(k_cache=_fake_cache(dtype=C.LISFA_MXFP8, row_stride_bytes=32, scale=16), q_scale=16, D_I=32),
+     C.LISFA_ERR_UNSUPPORTED),
 ])
 def test_li_score_validation(clib, kw, code):
     a = _idx_args(**kw)
@@ -142,6 +148,7 @@ def test_topk_validation(clib):
     (dict(q=None), C.LISFA_ERR_NULL_ARG),
     (dict(kv_cache=_fake_cache(row_stride_bytes=1024)), C.LISFA_ERR_BAD_SHAPE),
     (dict(softmax_scale=float("nan")), C.LISFA_ERR_BAD_SHAPE),
+    (dict(kv_cache=_fake_cache(dtype=C.LISFA_MXFP8, row_stride_bytes=1152, scale=16)), C.LISFA_ERR_BAD_DTYPE),
 ])
 def test_sparse_mla_validation(clib, kw, code):
     m = _mla_args(**kw)

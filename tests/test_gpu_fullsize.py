@@ -60,3 +60,7 @@ def test_fp8_decode_16x131072_full(lib):
 
 def test_bench_workload_64x32768_full(lib):
     _run(W.BENCH["decode_paged_64x32768"], [0, 31, 63])
+
+
+def test_bench_workload_mxfp8_full(lib):
+    _run(W.BENCH["decode_paged_64x32768_mxfp8"], [0, 63])
