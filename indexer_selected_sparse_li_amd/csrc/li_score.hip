@@ -446,10 +446,15 @@ __global__ __launch_bounds__(64 * kLiDecWaves) void li_score_dec_kernel(IndexerD
 // and [64 + 16 g, 64 + 16 g + 16) of it (g = l / 16), and supplies the scale
 // of row l % 16, block g in byte 0 of its scale operand.  The accumulator
 // layout is that of the other 16x16 MFMAs (lane = key l % 16, 4 heads per
-// tile).  Otherwise the kernel is the bf16 decode kernel: subtiles streamed
-// into registers kLiMxPrefetch deep, ReLU as an integer max, head sum by two
-// permlane swaps.  132 bytes per key instead of 256.
-constexpr int kLiMxPrefetch = 8;
+// tile).
+// Work: each wave streams whole groups of 64 keys (4 subtiles), kLiMxGroups
+// groups ahead.  The keys' scale bytes are fetched with one coalesced dword
+// per lane per group (lane l: the 4 scales of key l of the group) and handed
+// to the lanes that need them with ds_bpermute: a per-lane byte gather per
+// subtile, or a dword read by 4 lanes at once, costs much more.  ReLU is an
+// integer max, the head sum two permlane swaps.  132 bytes per key instead
+// of 256.
+constexpr int kLiMxGroups = 2;
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
@@ -465,7 +470,7 @@ __global__ __launch_bounds__(64 * kLiDecWaves) void li_score_mx_kernel(IndexerDe
     constexpr int DI = 128;
     constexpr int NB = DI / 32;          // scale blocks per row
     constexpr int NT = 64 * kLiDecWaves;
-    constexpr int P = kLiMxPrefetch;
+    constexpr int PG = kLiMxGroups;
     __shared__ int64_t blk_slot0[kLiMaxBlocks];
     __shared__ int32_t blk_lim[kLiMaxBlocks];
 
@@ -535,61 +540,74 @@ __global__ __launch_bounds__(64 * kLiDecWaves) void li_score_mx_kernel(IndexerDe
     }
     __syncthreads();  // block map ready
 
-    const int nsub = (int)((kend - c0 + 15) / 16);
-    const int mine = nsub > wave ? (nsub - wave + kLiDecWaves - 1) / kLiDecWaves : 0;
-    // lane's key row in subtile i of this wave (the zero row, scale 2^0 and
-    // factor NaN when the position is past the row or not addressable)
-    auto fetch = [&](int i, i32x8& kb, int& ksc, float& fac) {
-        const int64_t key = c0 + (int64_t)(wave + i * kLiDecWaves) * 16 + (lane & 15);
-        const uint8_t* row = g_li_zero_row;
-        ksc = 127;
-        fac = __builtin_nanf("");
-        if (i < mine && key < kend) {
-            const int bi = (int)((key >> sh) - b0);
-            const int off = (int)(key & (bsz - 1));
-            if (off < blk_lim[bi]) {
-                const int64_t slot = blk_slot0[bi] + off;
-                row = a.k.data + slot * a.k.row_stride;
-                ksc = a.k.mx_scale[slot * NB + g];
-                fac = 1.f;
-            }
-        }
-        kb = mx_operand(row, g);
+    // 64-key groups of this wave: u = wave, wave + W, ... over [c0, kend)
+    const int ngrp = (int)((kend - c0 + 63) / 64);
+    const int mine = ngrp > wave ? (ngrp - wave + kLiDecWaves - 1) / kLiDecWaves : 0;
+    auto slot_of_key = [&](int64_t key) -> int64_t {   // -1: past the row or not addressable
+        if (key >= kend) return -1;
+        const int bi = (int)((key >> sh) - b0);
+        const int off = (int)(key & (bsz - 1));
+        return off < blk_lim[bi] ? blk_slot0[bi] + off : -1;
+    };
+    // subtile s4 of group i: operand of key 16 s4 + l % 16 of the group (the
+    // zero row and factor NaN where there is no key); the group's scale dword:
+    // the 4 scales of key l of the group (2^0 where there is none)
+    auto fetch_sub = [&](int i, int s4, i32x8& kb, float& fac) {
+        const int64_t base = c0 + (int64_t)(wave + i * kLiDecWaves) * 64;
+        const int64_t slot = i < mine ? slot_of_key(base + 16 * s4 + (lane & 15)) : -1;
+        kb = mx_operand(slot >= 0 ? a.k.data + slot * a.k.row_stride : g_li_zero_row, g);
+        fac = slot >= 0 ? 1.f : __builtin_nanf("");
+    };
+    auto fetch_scales = [&](int i) -> uint32_t {
+        const int64_t base = c0 + (int64_t)(wave + i * kLiDecWaves) * 64;
+        const int64_t ks = i < mine ? slot_of_key(base + lane) : -1;
+        return ks >= 0 ? __builtin_nontemporal_load((const uint32_t*)(a.k.mx_scale + ks * NB)) : 0x7F7F7F7Fu;
     };
     static_assert(DI <= 256, "zero row covers one key row");
 
-    i32x8 kbuf[P];
-    int ksc[P];
-    float fac[P];
+    i32x8 kbuf[PG][4];
+    uint32_t sbuf[PG];
+    float fac[PG][4];
 #pragma unroll
-    for (int j = 0; j < P; ++j) fetch(j, kbuf[j], ksc[j], fac[j]);
-    for (int i0 = 0; i0 < mine; i0 += P) {
+    for (int j = 0; j < PG; ++j) {
 #pragma unroll
-        for (int j = 0; j < P; ++j) {
+        for (int s4 = 0; s4 < 4; ++s4) fetch_sub(j, s4, kbuf[j][s4], fac[j][s4]);
+        sbuf[j] = fetch_scales(j);
+    }
+    for (int i0 = 0; i0 < mine; i0 += PG) {
+#pragma unroll
+        for (int j = 0; j < PG; ++j) {
             const int i = i0 + j;
-            f32x4 acc[MT];
+            const int64_t base = c0 + (int64_t)(wave + i * kLiDecWaves) * 64;
+            uint32_t sw = sbuf[j];
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-                acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[mt], kbuf[j], f32x4{0.f, 0.f, 0.f, 0.f},
-                                                                         0, 0, 0, qs[mt], 0, ksc[j]);
-            const float f = fac[j];
-            fetch(i + P, kbuf[j], ksc[j], fac[j]);
-            float part = 0.f;
+            for (int s4 = 0; s4 < 4; ++s4) {
+                // byte g of the scale dword held by the lane of this lane's key
+                const uint32_t w = (uint32_t)__builtin_amdgcn_ds_bpermute((16 * s4 + (lane & 15)) * 4, (int)sw);
+                const int ksc = (int)((w >> (8 * g)) & 255u);
+                f32x4 acc[MT];
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+                for (int mt = 0; mt < MT; ++mt)
+                    acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        qa[mt], kbuf[j][s4], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, qs[mt], 0, ksc);
+                const float f = fac[j][s4];
+                fetch_sub(i + PG, s4, kbuf[j][s4], fac[j][s4]);   // same subtile of the group PG ahead
+                if (s4 == 3) sbuf[j] = fetch_scales(i + PG);
+                float part = 0.f;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int bits = __float_as_int(acc[mt][q]);
-                    part = fmaf(wv[mt][q], __int_as_float(bits > 0 ? bits : 0), part);
-                }
-            {
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int bits = __float_as_int(acc[mt][q]);
+                        part = fmaf(wv[mt][q], __int_as_float(bits > 0 ? bits : 0), part);
+                    }
                 const auto w16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(part), __float_as_uint(part), false, false);
                 part = __uint_as_float(w16[0]) + __uint_as_float(w16[1]);
                 const auto w32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
                 part = __uint_as_float(w32[0]) + __uint_as_float(w32[1]);
+                const int64_t key = base + 16 * s4 + lane;
+                if (lane < 16 && key < kend) scores[(int64_t)r * ld + key] = part * f;
             }
-            const int64_t key = c0 + (int64_t)(wave + i * kLiDecWaves) * 16 + lane;
-            if (lane < 16 && key < kend) scores[(int64_t)r * ld + key] = part * f;
         }
     }
 }
