@@ -13,3 +13,4 @@ from .cp_oracle import (  # noqa: F401
     shard_candidates, merge_candidates, combine_partials, zigzag_segments,
     zigzag_share, zigzag_order, zigzag_restore,
 )
+from .prolog_oracle import layer_norm, fp8_token_quantize, quantize_q, bf16_round  # noqa: F401
