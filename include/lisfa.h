@@ -275,6 +275,52 @@ int zigzag_restore(const void* src, void* dst, int64_t n, int32_t G, int64_t row
                    lisfa_stream_t stream);
 
 /*
+ * Indexer prolog ("Day0 Inference Adaptation and Performance Optimization for
+ * Kimi K3.1 Pro", section 3; "Large Language Model Inference Acceleration in
+ * Practice", section 3.2; "... for a New Model", section 3.2: Q quantisation
+ * and K normalisation with the cache update run on separate streams ahead of
+ * the index computation).  Both start from the bf16 outputs of the indexer's
+ * projections (not part of this library).  Rounding to e4m3 is round to
+ * nearest even with saturation to +-448.
+ *
+ * indexer_q_quant - dynamic quantisation of indexer queries.
+ *   q: [R, H_I, D_I] bf16 (4-byte aligned); D_I 32 or 128.
+ *   dtype LISFA_FP8_E4M3: q_scale_out fp32 [R], one scale per row over all
+ *         heads: s = amax / 448 (1 if amax = 0), code = e4m3(x / s) (fp32
+ *         IEEE division).
+ *   dtype LISFA_MXFP8: q_scale_out uint8 E8M0 [R, H_I, D_I / 32]: per block of
+ *         32, shared exponent floor(log2 amax) - 8 (clamped to [-127, 127], 0
+ *         for a zero block), code = e4m3(x * 2^-shared) (exact scaling).
+ *   q_out: [R, H_I, D_I] uint8 e4m3 codes, 16-byte aligned.
+ */
+int indexer_q_quant(const void* q, int32_t R, int32_t H_I, int32_t D_I, int32_t dtype,
+                    void* q_out, void* q_scale_out, lisfa_stream_t stream);
+
+/*
+ * indexer_k_store - normalise new indexer keys and write them into the key
+ * cache (the cache update that runs with K normalisation).
+ *   k:        [T, D_I] bf16 new keys (4-byte aligned); D_I 32 or 128.
+ *   normalize: nonzero = LayerNorm over the D_I elements in fp32:
+ *             y = (x - mean) / sqrt(var + eps) * gamma + beta (biased
+ *             variance; gamma / beta fp32 [D_I] or NULL = 1 / 0); zero = y = x.
+ *   tok_seq, tok_pos: [T] int32 sequence and position of each key; the key
+ *             goes to slot(tok_seq, tok_pos) of k_cache.  A key whose slot the
+ *             cache cannot address (sequence out of range, block-table entry
+ *             past bt_stride or negative, slot past num_slots) is skipped.
+ *   k_cache:  describes the destination; its data (and scale) arrays are
+ *             written.  bf16: y rounded to nearest even.  fp8
+ *             (scale_group_tokens must be 1): per key s = amax / 448 written
+ *             to scale[slot], codes e4m3(y / s).  mxfp8: E8M0 scales per 32
+ *             elements as in indexer_q_quant.
+ * Keys of one call must go to distinct slots (otherwise the survivor is
+ * unspecified).
+ */
+int indexer_k_store(const void* k, int32_t T, int32_t D_I, const float* gamma,
+                    const float* beta, float eps, int32_t normalize,
+                    const int32_t* tok_seq, const int32_t* tok_pos,
+                    const lisfa_cache* k_cache, lisfa_stream_t stream);
+
+/*
  * li_topk_sfa - the whole layer in one call on one stream: scores, Top-K and
  * sparse attention ("Day0 Inference Adaptation and Performance Optimization
  * for Kimi K3.1 Pro", section 3, and "Large Language Model Inference

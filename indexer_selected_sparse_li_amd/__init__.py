@@ -16,6 +16,9 @@ One GPU's share of a context-parallel split:
   sparse_mla_attn_partial(...) fp32 partial attention over the shard's rows
   lse_combine(...)             log-sum-exp merge of the gathered partials
   zigzag_share(...), zigzag_restore(...)  Zigzag partition of prefill rows
+Indexer prolog:
+  indexer_q_quant(...)  dynamic fp8 / MXFP8 quantisation of indexer queries
+  indexer_k_store(...)  LayerNorm of new keys and their store into the key cache
 """
 from __future__ import annotations
 
@@ -29,7 +32,7 @@ from . import _lib as _c
 
 __all__ = ["KVCache", "LisfaError", "li_score", "topk_select", "sparse_mla_attn", "li_topk_sfa",
            "topk_candidates", "topk_merge", "sparse_mla_attn_partial", "lse_combine", "zigzag_share",
-           "zigzag_restore", "workspace_size", "load", "status_string"]
+           "zigzag_restore", "indexer_q_quant", "indexer_k_store", "workspace_size", "load", "status_string"]
 
 
 class LisfaError(RuntimeError):
@@ -277,6 +280,38 @@ def zigzag_restore(src, dst, G: int, stream=None):
     row_bytes = src[0].numel() * src.element_size() if n else 0
     _check(lib.zigzag_restore(_ptr(src), _ptr(dst), n, G, row_bytes, _stream(stream)), "zigzag_restore")
     return dst
+
+
+def indexer_q_quant(q, fmt: str, q_out, q_scale_out, stream=None):
+    """Quantise bf16 indexer queries [R, H_I, D_I]: fmt "fp8" (fp32 scale per
+    row) or "mxfp8" (E8M0 scale per 32 elements); codes into q_out (uint8)."""
+    lib = _c.load()
+    R, H_I, D_I = q.shape
+    if q.dtype != torch.bfloat16 or q_out.dtype != torch.uint8 or tuple(q_out.shape) != (R, H_I, D_I):
+        raise ValueError("q must be bf16 and q_out uint8 of the same shape")
+    dt = {"fp8": _c.LISFA_FP8_E4M3, "mxfp8": _c.LISFA_MXFP8}[fmt]
+    want = (torch.float32, (R,)) if fmt == "fp8" else (torch.uint8, (R, H_I, D_I // 32))
+    if q_scale_out.dtype != want[0] or tuple(q_scale_out.shape) != want[1]:
+        raise ValueError(f"q_scale_out must be {want[0]} {want[1]}")
+    _check(lib.indexer_q_quant(_ptr(q), R, H_I, D_I, dt, _ptr(q_out), _ptr(q_scale_out), _stream(stream)),
+           "indexer_q_quant")
+    return q_out, q_scale_out
+
+
+def indexer_k_store(k, tok_seq, tok_pos, k_cache: KVCache, gamma=None, beta=None, eps: float = 1e-6,
+                    normalize: bool = True, stream=None):
+    """LayerNorm (optional) of new bf16 keys [T, D_I] and their store into
+    k_cache at (tok_seq, tok_pos) in the cache's format."""
+    lib = _c.load()
+    T, D_I = k.shape
+    if k.dtype != torch.bfloat16:
+        raise ValueError("k must be bf16")
+    for t in (gamma, beta):
+        if t is not None and (t.dtype != torch.float32 or t.numel() != D_I):
+            raise ValueError("gamma / beta must be fp32 [D_I]")
+    c = k_cache.c_struct()
+    _check(lib.indexer_k_store(_ptr(k), T, D_I, _ptr(gamma), _ptr(beta), float(eps), int(normalize), _ptr(tok_seq),
+                               _ptr(tok_pos), ctypes.byref(c), _stream(stream)), "indexer_k_store")
 
 
 def li_topk_sfa(q_idx, w, k_cache: KVCache, q, kv_cache: KVCache, row_seq, row_pos, K: int,

@@ -28,7 +28,7 @@ LISFA_OP_SPARSE_MLA_PARTIAL = 4
 EXPORTS = (
     "li_score", "topk_select", "sparse_mla_attn", "li_topk_sfa",
     "topk_candidates", "topk_merge", "sparse_mla_attn_partial", "lse_combine",
-    "lisfa_zigzag_share", "zigzag_restore",
+    "lisfa_zigzag_share", "zigzag_restore", "indexer_q_quant", "indexer_k_store",
     "lisfa_workspace_size", "lisfa_status_string", "lisfa_struct_size", "lisfa_abi_version",
 )
 
@@ -114,6 +114,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lisfa_zigzag_share.restype = ctypes.c_int
     lib.zigzag_restore.argtypes = [vp, vp, i64, i32, i64, vp]
     lib.zigzag_restore.restype = ctypes.c_int
+    lib.indexer_q_quant.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp]
+    lib.indexer_q_quant.restype = ctypes.c_int
+    lib.indexer_k_store.argtypes = [vp, i32, i32, vp, vp, ctypes.c_float, i32, vp, vp, ctypes.POINTER(Cache), vp]
+    lib.indexer_k_store.restype = ctypes.c_int
     lib.lisfa_workspace_size.argtypes = [i32, i32, i64, i32, i32, i32]
     lib.lisfa_workspace_size.restype = sz
     lib.lisfa_status_string.argtypes = [i32]

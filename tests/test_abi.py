@@ -239,3 +239,23 @@ def test_zigzag_host_helper_and_validation(clib):
     assert clib.zigzag_restore(None, None, 0, 2, 16, None) == C.LISFA_OK
     assert clib.zigzag_restore(None, 16, 10, 2, 16, None) == C.LISFA_ERR_NULL_ARG
     assert clib.zigzag_restore(16, 4096, 10, 0, 16, None) == C.LISFA_ERR_BAD_SHAPE
+
+
+def test_prolog_validation(clib):
+    assert clib.indexer_q_quant(16, 2, 64, 64, C.LISFA_MXFP8, 16, 16, None) == C.LISFA_ERR_UNSUPPORTED
+    assert clib.indexer_q_quant(16, 2, 64, 128, C.LISFA_BF16, 16, 16, None) == C.LISFA_ERR_BAD_DTYPE
+    assert clib.indexer_q_quant(16, 2, 64, 128, C.LISFA_MXFP8, 16, None, None) == C.LISFA_ERR_NULL_ARG
+    assert clib.indexer_q_quant(16, 2, 64, 128, C.LISFA_MXFP8, 24, 16, None) == C.LISFA_ERR_BAD_SHAPE
+    assert clib.indexer_q_quant(None, 0, 64, 128, C.LISFA_FP8_E4M3, None, None, None) == C.LISFA_OK
+    kc = _fake_cache()
+    assert clib.indexer_k_store(16, 4, 64, None, None, 1e-6, 1, 16, 16, ctypes.byref(kc), None) == \
+        C.LISFA_ERR_UNSUPPORTED
+    assert clib.indexer_k_store(16, 4, 128, None, None, 1e-6, 1, 16, 16, None, None) == C.LISFA_ERR_NULL_ARG
+    assert clib.indexer_k_store(16, 4, 128, None, None, -1.0, 1, 16, 16, ctypes.byref(kc), None) == \
+        C.LISFA_ERR_BAD_SHAPE
+    f8 = _fake_cache(dtype=C.LISFA_FP8_E4M3, row_stride_bytes=128, scale=16, scale_group_tokens=64)
+    assert clib.indexer_k_store(16, 4, 128, None, None, 1e-6, 1, 16, 16, ctypes.byref(f8), None) == \
+        C.LISFA_ERR_BAD_SHAPE
+    assert clib.indexer_k_store(16, 4, 128, None, None, 1e-6, 1, None, 16, ctypes.byref(kc), None) == \
+        C.LISFA_ERR_NULL_ARG
+    assert clib.indexer_k_store(None, 0, 128, None, None, 1e-6, 1, None, None, ctypes.byref(kc), None) == C.LISFA_OK

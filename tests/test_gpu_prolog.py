@@ -1,0 +1,176 @@
+"""GPU parity of the indexer prolog through the C ABI: dynamic query
+quantisation (bit-exact: the decision is exact or fixed in fp32 on both
+sides), key store without normalisation (bit-exact in every cache format and
+layout, other slots untouched), with LayerNorm on exactly representable rows
+(bit-exact), and with LayerNorm on Gaussian rows (every stored value a
+correct rounding of a value within 1e-5 relative of the float64 oracle: the
+fp32 LayerNorm may land on the other side of a rounding boundary)."""
+import numpy as np
+import pytest
+import torch
+
+import indexer_selected_sparse_li_amd as lisfa
+import oracle as O
+import workloads as W
+from gpu_util import say
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf16_bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _queries(R, H_I, D_I, seed):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(R, H_I, D_I, generator=g)
+    q[0] *= 1e-3
+    q[1, 3] = 0.0                                        # an all-zero head (zero MX blocks)
+    q[2] *= 500.0
+    q[3, :, 5] = 1e4                                     # one huge element per head
+    return q.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "fp8"])
+@pytest.mark.parametrize("D_I", [128, 32])
+def test_q_quant_bit_exact(lib, fmt, D_I):
+    say(f"[case] q quant {fmt} D_I={D_I}")
+    R, H_I = 6, 64
+    q = _queries(R, H_I, D_I, 71).cuda()
+    out = torch.full((R, H_I, D_I), 0xEE, dtype=torch.uint8, device="cuda")
+    sc = (torch.zeros(R, dtype=torch.float32, device="cuda") if fmt == "fp8"
+          else torch.zeros(R, H_I, D_I // 32, dtype=torch.uint8, device="cuda"))
+    lisfa.indexer_q_quant(q, fmt, out, sc)
+    torch.cuda.synchronize()
+    ref_c, ref_s = O.quantize_q(O.decode_bf16(_bf16_bits(q)), fmt)
+    assert np.array_equal(out.cpu().numpy(), ref_c)
+    assert np.array_equal(sc.cpu().numpy(), ref_s)
+
+
+def _cache(fmt, paged, num_slots, D_I, num_seqs, blocks_per_seq, seed):
+    """A key cache filled with sentinel bytes, in the given format/layout."""
+    if fmt == "bf16":
+        data = torch.full((num_slots, D_I), 0x7FC1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+        scale = None
+    else:
+        data = torch.full((num_slots, D_I), 0x5A, dtype=torch.uint8, device="cuda")
+        scale = (torch.full((num_slots,), -3.0, dtype=torch.float32, device="cuda") if fmt == "fp8"
+                 else torch.full((num_slots, D_I // 32), 0xA5, dtype=torch.uint8, device="cuda"))
+    if paged:
+        perm = torch.randperm(num_slots // 64, generator=torch.Generator().manual_seed(seed)).to(torch.int32)
+        bt = perm[: num_seqs * blocks_per_seq].view(num_seqs, blocks_per_seq).cuda()
+        return lisfa.KVCache(data=data, scale=scale, block_table=bt, block_size=64)
+    base = torch.arange(num_seqs, dtype=torch.int64, device="cuda") * (blocks_per_seq * 64)
+    return lisfa.KVCache(data=data, scale=scale, seq_base=base)
+
+
+def _slot(kc, s, p):
+    if kc.block_table is not None:
+        return int(kc.block_table[s, p // 64]) * 64 + p % 64
+    return int(kc.seq_base[s]) + p
+
+
+def _run_store(fmt, paged, D_I, T, keys, normalize, gamma=None, beta=None, eps=1e-6, seed=0):
+    num_seqs, bps = 4, 8
+    kc = _cache(fmt, paged, num_seqs * bps * 64 + 128, D_I, num_seqs, bps, seed)
+    rng = np.random.default_rng(seed)
+    flat = rng.choice(num_seqs * bps * 64, size=T, replace=False)
+    seq = torch.tensor(flat // (bps * 64), dtype=torch.int32, device="cuda")
+    pos = torch.tensor(flat % (bps * 64), dtype=torch.int32, device="cuda")
+    before_d = kc.data.view(torch.uint8).clone()
+    before_s = kc.scale.view(torch.uint8).clone() if kc.scale is not None else None
+    lisfa.indexer_k_store(keys, seq, pos, kc, gamma=gamma, beta=beta, eps=eps, normalize=normalize)
+    torch.cuda.synchronize()
+    slots = [_slot(kc, int(s), int(p)) for s, p in zip(seq.tolist(), pos.tolist())]
+    # untouched elsewhere
+    mask = torch.ones(kc.data.shape[0], dtype=torch.bool)
+    mask[slots] = False
+    assert torch.equal(kc.data.view(torch.uint8).cpu()[mask], before_d.cpu()[mask])
+    if before_s is not None:
+        sv = kc.scale.view(torch.uint8).cpu().view(kc.scale.shape[0], -1)
+        assert torch.equal(sv[mask], before_s.cpu().view(kc.scale.shape[0], -1)[mask])
+    return kc, slots
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "mxfp8"])
+@pytest.mark.parametrize("paged", [True, False], ids=["paged", "contiguous"])
+def test_k_store_without_norm_bit_exact(lib, fmt, paged):
+    say(f"[case] k store {fmt} paged={paged}")
+    D_I, T = 128, 300
+    keys = (torch.randn(T, D_I, generator=torch.Generator().manual_seed(72)) * 3).to(torch.bfloat16).cuda()
+    kc, slots = _run_store(fmt, paged, D_I, T, keys, normalize=False, seed=73)
+    x = O.decode_bf16(_bf16_bits(keys))
+    d = kc.data[slots].cpu()
+    if fmt == "bf16":
+        assert np.array_equal(_bf16_bits(d), _bf16_bits(keys))
+    elif fmt == "fp8":
+        c, s = O.fp8_token_quantize(x.astype(np.float32))
+        assert np.array_equal(d.numpy(), c) and np.array_equal(kc.scale[slots].cpu().numpy(), s)
+    else:
+        c, s = O.mx_quantize(x)
+        assert np.array_equal(d.numpy(), c) and np.array_equal(kc.scale[slots].cpu().numpy(), s)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "mxfp8"])
+@pytest.mark.parametrize("D_I", [128, 32])
+def test_k_store_layer_norm_exact_rows(lib, fmt, D_I):
+    """Rows of +-a (a a power of two, half each sign): LayerNorm with eps = 0
+    gives exactly +-1, so the stored codes are fixed."""
+    say(f"[case] k store exact layernorm {fmt} D_I={D_I}")
+    T = 64
+    rng = np.random.default_rng(74)
+    rows = np.stack([rng.permutation(np.repeat([1.0, -1.0], D_I // 2)) * 2.0 ** rng.integers(-6, 6)
+                     for _ in range(T)]).astype(np.float32)
+    keys = torch.from_numpy(rows).to(torch.bfloat16).cuda()
+    kc, slots = _run_store(fmt, False, D_I, T, keys, normalize=True, eps=0.0, seed=75)
+    y = rows / np.abs(rows)
+    d = kc.data[slots].cpu()
+    if fmt == "bf16":
+        assert np.array_equal(O.decode_bf16(_bf16_bits(d)), y)
+    elif fmt == "fp8":
+        c, s = O.fp8_token_quantize(y)
+        assert np.array_equal(d.numpy(), c) and np.array_equal(kc.scale[slots].cpu().numpy(), s)
+    else:
+        c, s = O.mx_quantize(y)
+        assert np.array_equal(d.numpy(), c) and np.array_equal(kc.scale[slots].cpu().numpy(), s)
+
+
+def _e4m3_half_step(v):
+    """Half the spacing of the e4m3 grid at magnitude |v| (subnormal grid below 2^-6)."""
+    a = np.maximum(np.abs(v), 2.0 ** -6)
+    return 0.5 * 2.0 ** (np.floor(np.log2(a)) - 3)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "mxfp8"])
+def test_k_store_layer_norm_gaussian(lib, fmt):
+    say(f"[case] k store layernorm gaussian {fmt}")
+    D_I, T = 128, 256
+    g = torch.Generator().manual_seed(76)
+    keys = (torch.randn(T, D_I, generator=g) * 2 + 0.5).to(torch.bfloat16).cuda()
+    gamma = (torch.rand(D_I, generator=g) + 0.5).cuda()
+    beta = (torch.randn(D_I, generator=g) * 0.1).cuda()
+    kc, slots = _run_store(fmt, True, D_I, T, keys, normalize=True, gamma=gamma, beta=beta, eps=1e-6, seed=77)
+    y = O.layer_norm(O.decode_bf16(_bf16_bits(keys)), gamma.cpu().numpy(), beta.cpu().numpy(), 1e-6)
+    tol = 1e-5 * np.abs(y) + 1e-6
+    d = kc.data[slots].cpu()
+    if fmt == "bf16":
+        v = O.decode_bf16(_bf16_bits(d))
+        ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(y), 1e-30))) - 7)
+        assert np.all(np.abs(v - y) <= 0.5 * ulp + tol)
+    elif fmt == "fp8":
+        s = kc.scale[slots].cpu().numpy().astype(np.float64)
+        amax = np.abs(y).max(1)
+        assert np.all(np.abs(s - amax / 448) <= 2e-5 * amax / 448)
+        v = O.decode_e4m3(d.numpy()) * s[:, None]
+        assert np.all(np.abs(v - y) <= _e4m3_half_step(y / s[:, None]) * s[:, None] + tol * 3)
+    else:
+        e = kc.scale[slots].cpu().numpy()
+        ce, se = O.mx_quantize(y)
+        lg = np.log2(np.abs(y).reshape(T, 4, 32).max(-1)) % 1.0
+        near_pow2 = (lg < 1e-4) | (lg > 1 - 1e-4)
+        assert np.all((e == se) | near_pow2)
+        X = np.repeat(O.decode_e8m0(e), 32, axis=1)
+        v = O.decode_e4m3(d.numpy()) * X
+        sat = np.abs(y / X) > 448
+        assert np.all((np.abs(v - y) <= _e4m3_half_step(y / X) * X + tol)[~sat])
+        assert np.all(np.abs(O.decode_e4m3(d.numpy())[sat]) == 448)
