@@ -299,6 +299,7 @@ def main():
     ap.add_argument("--mfma-csv")
     ap.add_argument("--report-cp", action="store_true",
                     help="time one GPU's context-parallel share and the Zigzag prefill balance")
+    ap.add_argument("--report-prolog", action="store_true", help="time the indexer prolog kernels")
     ap.add_argument("--report-md", help="with --report-all / --report-cp: write a markdown table here")
     args = ap.parse_args()
     if args.write_traffic_summary:
@@ -331,6 +332,9 @@ def main():
         return
     if args.report_cp:
         report_cp(args)
+        return
+    if args.report_prolog:
+        report_prolog(args)
         return
     wl = W.get(args.workload)
     res, b = run_workload(args, wl)
@@ -721,6 +725,68 @@ def report_cp(args):
             for part in ("in-order", "zigzag"):
                 fh.write(f"| {part} | " + " | ".join(str(x) for x in zz[part]["ms"]) +
                          f' | {zz[part]["max_over_min"]} |\n')
+        log(f"[bench] wrote {args.report_md}")
+
+
+def report_prolog(args):
+    """The indexer prolog kernels on a decode step (64 query rows, 64 new
+    keys) and a prefill chunk (4096 of each): query quantisation (fp8 per row
+    and MXFP8) and key LayerNorm + store (bf16, fp8, MXFP8 paged caches).
+    Each call graph-captured and timed on its own; bytes = bf16 inputs read +
+    codes and scales written."""
+    import torch
+    import indexer_selected_sparse_li_amd as lisfa
+    stream = torch.cuda.current_stream()
+    rows = []
+    for n in (64, 4096):
+        g = torch.Generator(device="cuda").manual_seed(n)
+        q = torch.randn(n, 64, 128, device="cuda", generator=g).to(torch.bfloat16)
+        for fmt in ("fp8", "mxfp8"):
+            qo = torch.empty(n, 64, 128, dtype=torch.uint8, device="cuda")
+            qs = (torch.empty(n, dtype=torch.float32, device="cuda") if fmt == "fp8"
+                  else torch.empty(n, 64, 4, dtype=torch.uint8, device="cuda"))
+            t = time_on_stream(lambda st: lisfa.indexer_q_quant(q, fmt, qo, qs, stream=st), stream, 2, args.steps,
+                               graph=True)
+            by = q.numel() * 2 + qo.numel() + qs.numel() * qs.element_size()
+            rows.append(("indexer_q_quant", fmt, n, t * 1e6, by))
+        k = torch.randn(n, 128, device="cuda", generator=g).to(torch.bfloat16)
+        gamma = torch.rand(128, device="cuda", generator=g) + 0.5
+        beta = torch.randn(128, device="cuda", generator=g) * 0.1
+        nblk = 2 * (n // 64 + 1)
+        bt = torch.randperm(nblk, device="cuda", generator=g).to(torch.int32).view(1, nblk)
+        seq = torch.zeros(n, dtype=torch.int32, device="cuda")
+        pos = torch.arange(n, dtype=torch.int32, device="cuda")
+        for fmt in ("bf16", "fp8", "mxfp8"):
+            if fmt == "bf16":
+                data, scale = torch.empty(nblk * 64, 128, dtype=torch.bfloat16, device="cuda"), None
+            else:
+                data = torch.empty(nblk * 64, 128, dtype=torch.uint8, device="cuda")
+                scale = (torch.empty(nblk * 64, dtype=torch.float32, device="cuda") if fmt == "fp8"
+                         else torch.empty(nblk * 64, 4, dtype=torch.uint8, device="cuda"))
+            kc = lisfa.KVCache(data=data, scale=scale, block_table=bt, block_size=64)
+            t = time_on_stream(lambda st: lisfa.indexer_k_store(k, seq, pos, kc, gamma=gamma, beta=beta, stream=st),
+                               stream, 2, args.steps, graph=True)
+            elt = 2 if fmt == "bf16" else 1
+            sc = {"bf16": 0, "fp8": 4, "mxfp8": 4}[fmt]
+            by = k.numel() * 2 + n * (128 * elt + sc) + 2 * 128 * 4 + n * 8
+            rows.append(("indexer_k_store (LayerNorm)", fmt, n, t * 1e6, by))
+    for r in rows:
+        log(f"[bench] {r[0]} {r[1]} n={r[2]}: {r[3]:.2f} us, {r[4] / r[3] / 1e3:.2f} GB/s")
+    print(json.dumps([dict(kernel=r[0], format=r[1], rows=r[2], us=round(r[3], 2), bytes=r[4]) for r in rows]),
+          flush=True)
+    if args.report_md:
+        with open(args.report_md, "w") as fh:
+            fh.write("# Indexer prolog kernels on one MI355X\n\n")
+            fh.write("Query quantisation of [n, 64, 128] bf16 queries and LayerNorm + store of n new 128-wide keys\n"
+                     "into a paged key cache (random 64-token blocks). Each call captured in a HIP graph and timed\n"
+                     "on its own with HIP events; bytes = bf16 inputs read + codes and scales written.\n\n")
+            fh.write("Command (from the repository root):\n\n")
+            fh.write(f"    python3 bench.py --report-prolog --steps {args.steps} --report-md "
+                     f"{os.path.relpath(args.report_md, ROOT)}\n\n")
+            fh.write("| kernel | format | rows | us | GB/s | % of HBM peak |\n|---|---|---|---|---|---|\n")
+            for r in rows:
+                gbs = r[4] / r[3] / 1e3
+                fh.write(f"| {r[0]} | {r[1]} | {r[2]} | {r[3]:.2f} | {gbs:.1f} | {gbs / HBM_PEAK_GBS * 100:.1f} |\n")
         log(f"[bench] wrote {args.report_md}")
 
 

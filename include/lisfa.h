@@ -284,7 +284,7 @@ int zigzag_restore(const void* src, void* dst, int64_t n, int32_t G, int64_t row
  * nearest even with saturation to +-448.
  *
  * indexer_q_quant - dynamic quantisation of indexer queries.
- *   q: [R, H_I, D_I] bf16 (4-byte aligned); D_I 32 or 128.
+ *   q: [R, H_I, D_I] bf16 (16-byte aligned); H_I <= 64, D_I 32 or 128.
  *   dtype LISFA_FP8_E4M3: q_scale_out fp32 [R], one scale per row over all
  *         heads: s = amax / 448 (1 if amax = 0), code = e4m3(x / s) (fp32
  *         IEEE division).

@@ -392,7 +392,7 @@ int indexer_q_quant(const void* q, int32_t R, int32_t H_I, int32_t D_I, int32_t 
     if (dtype != LISFA_FP8_E4M3 && dtype != LISFA_MXFP8) return LISFA_ERR_BAD_DTYPE;
     if (R == 0) return LISFA_OK;
     if (!q || !q_out || !q_scale_out) return LISFA_ERR_NULL_ARG;
-    if (!aligned(q, 4) || !aligned(q_out, 16) || !aligned(q_scale_out, 4)) return LISFA_ERR_BAD_SHAPE;
+    if (!aligned(q, 16) || !aligned(q_out, 16) || !aligned(q_scale_out, 4)) return LISFA_ERR_BAD_SHAPE;
     return hip_status(q_quant_dispatch(q, R, H_I * D_I, dtype == LISFA_MXFP8, q_out, q_scale_out,
                                        (hipStream_t)stream));
 }

@@ -8,7 +8,8 @@
 // normalisation with the cache update on one stream, Q quantisation on
 // another.  The projections that produce q and k need trained weights and are
 // not part of this library; these kernels start from their bf16 outputs.
-//  * indexer_q_quant: one workgroup per query row.  fp8: one scale per row
+//  * indexer_q_quant: one workgroup per query row, read once into registers
+//    (16-byte loads; a row holds at most 64 x 128 elements).  fp8: one scale per row
 //    over all heads, scale = amax / 448 (1 if amax = 0), element = x / scale
 //    (IEEE division) rounded to e4m3; MXFP8: per 32-element block the shared
 //    exponent floor(log2 amax) - 8 (clamped to [-127, 127], 0 for a zero
@@ -55,52 +56,67 @@ __device__ __forceinline__ int mx_shared_exp(float amax) {
 
 // queries -------------------------------------------------------------------
 
+// One workgroup per query row of n = H_I * D_I <= 8192 elements: thread t
+// holds the 32-element block t (four 16-byte loads) in registers, so the row
+// is read once whichever the format.
 template <bool MX>
 __global__ __launch_bounds__(256) void q_quant_kernel(const uint16_t* __restrict__ q, int n, uint8_t* __restrict__ out,
                                                       void* __restrict__ scale_out) {
     __shared__ float red[4];
     const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const uint16_t* x = q + (int64_t)r * n;
-    uint8_t* o = out + (int64_t)r * n;
-    if constexpr (MX) {
-        uint8_t* sc = (uint8_t*)scale_out + (int64_t)r * (n / 32);
-        for (int b = tid; b < n / 32; b += 256) {
-            float v[32];
-            float amax = 0.f;
+    const bool on = tid < n / 32;
+    float v[32];
+    float amax = 0.f;
+    {
+        const u32x4* x = (const u32x4*)(q + (int64_t)r * n + tid * 32);
 #pragma unroll
-            for (int i = 0; i < 32; ++i) {
-                v[i] = bf16_bits_to_float(x[b * 32 + i]);
-                amax = fmaxf(amax, fabsf(v[i]));
+        for (int c = 0; c < 4; ++c) {
+            const u32x4 w = on ? x[c] : u32x4{0u, 0u, 0u, 0u};
+            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[8 * c + 2 * i] = bf16_bits_to_float(ws[i] & 0xFFFFu);
+                v[8 * c + 2 * i + 1] = bf16_bits_to_float(ws[i] >> 16);
             }
-            const int se = mx_shared_exp(amax);
-            uint32_t w[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                w[i] = 0u;
-#pragma unroll
-                for (int k = 0; k < 4; ++k) w[i] |= e4m3_encode(__builtin_ldexpf(v[4 * i + k], -se)) << (8 * k);
-            }
-            u32x4* d = (u32x4*)(o + b * 32);
-            d[0] = u32x4{w[0], w[1], w[2], w[3]};
-            d[1] = u32x4{w[4], w[5], w[6], w[7]};
-            sc[b] = (uint8_t)(se + 127);
         }
+#pragma unroll
+        for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    }
+    uint32_t w[8];
+    if constexpr (MX) {
+        const int se = mx_shared_exp(amax);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            w[i] = 0u;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) w[i] |= e4m3_encode(__builtin_ldexpf(v[4 * i + k], -se)) << (8 * k);
+        }
+        if (on) ((uint8_t*)scale_out)[(int64_t)r * (n / 32) + tid] = (uint8_t)(se + 127);
     } else {
-        float amax = 0.f;
-        for (int i = tid; i < n; i += 256) amax = fmaxf(amax, fabsf(bf16_bits_to_float(x[i])));
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
         if (lane == 0) red[wave] = amax;
         __syncthreads();
         amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-        const float s = amax > 0.f ? amax / 448.f : 1.f;
-        for (int i = tid; i < n; i += 256) o[i] = (uint8_t)e4m3_encode(bf16_bits_to_float(x[i]) / s);
-        if (tid == 0) ((float*)scale_out)[r] = s;
+        const float sc = amax > 0.f ? amax / 448.f : 1.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            w[i] = 0u;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) w[i] |= e4m3_encode(v[4 * i + k] / sc) << (8 * k);
+        }
+        if (tid == 0) ((float*)scale_out)[r] = sc;
+    }
+    if (on) {
+        u32x4* d = (u32x4*)(out + (int64_t)r * n + tid * 32);
+        d[0] = u32x4{w[0], w[1], w[2], w[3]};
+        d[1] = u32x4{w[4], w[5], w[6], w[7]};
     }
 }
 
 hipError_t q_quant_dispatch(const void* q, int R, int n, int mx, void* out, void* scale_out, hipStream_t stream) {
     if (R <= 0) return hipSuccess;
+    if (n > 256 * 32 || n % 32 != 0) return hipErrorInvalidValue;
     if (mx)
         hipLaunchKernelGGL(q_quant_kernel<true>, dim3((unsigned)R), dim3(256), 0, stream, (const uint16_t*)q, n,
                            (uint8_t*)out, scale_out);

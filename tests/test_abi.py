@@ -246,6 +246,7 @@ def test_prolog_validation(clib):
     assert clib.indexer_q_quant(16, 2, 64, 128, C.LISFA_BF16, 16, 16, None) == C.LISFA_ERR_BAD_DTYPE
     assert clib.indexer_q_quant(16, 2, 64, 128, C.LISFA_MXFP8, 16, None, None) == C.LISFA_ERR_NULL_ARG
     assert clib.indexer_q_quant(16, 2, 64, 128, C.LISFA_MXFP8, 24, 16, None) == C.LISFA_ERR_BAD_SHAPE
+    assert clib.indexer_q_quant(20, 2, 64, 128, C.LISFA_MXFP8, 16, 16, None) == C.LISFA_ERR_BAD_SHAPE
     assert clib.indexer_q_quant(None, 0, 64, 128, C.LISFA_FP8_E4M3, None, None, None) == C.LISFA_OK
     kc = _fake_cache()
     assert clib.indexer_k_store(16, 4, 64, None, None, 1e-6, 1, 16, 16, ctypes.byref(kc), None) == \
