@@ -182,9 +182,7 @@ __global__ __launch_bounds__(512) void li_score_kernel(IndexerDev a, float* __re
             const uint8_t* g = g_li_zero16;
             if (inr && off < blk_lim[bi])
                 g = a.k.data + (blk_slot0[bi] + off) * a.k.row_stride + part * 16;
-            const uint32_t dst = __builtin_amdgcn_readfirstlane(
-                ring0 + (uint32_t)(buf * TILE + (j * 512 + (tid & ~63)) * 16));
-            __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(uintptr_t)dst, 16, 0, 0);
+            lds_dma<16, 0>(g, ring0 + (uint32_t)(buf * TILE + (j * 512 + (tid & ~63)) * 16));
         }
         {
             const int key = tid;  // waves whose keys lie past the tile load a dummy
@@ -199,8 +197,7 @@ __global__ __launch_bounds__(512) void li_score_kernel(IndexerDev a, float* __re
                     else g = &g_li_one;
                 }
             }
-            const uint32_t dst = __builtin_amdgcn_readfirstlane(kmul0 + (uint32_t)((buf * 512 + (tid & ~63)) * 4));
-            __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(uintptr_t)dst, 4, 0, 0);
+            lds_dma<4, 0>(g, kmul0 + (uint32_t)((buf * 512 + (tid & ~63)) * 4));
         }
     };
 

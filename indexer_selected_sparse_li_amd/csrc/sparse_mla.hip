@@ -40,6 +40,7 @@ namespace lisfa {
 __device__ __attribute__((aligned(16))) uint8_t g_zero16[64];
 
 constexpr int kSfaMaxKeys = 2048;  // index entries one workgroup handles
+constexpr bool kSfaWarpSpecialised = true;   // 512 + 64 bf16 rows, 64-head blocks: sfa_ws_kernel
 
 // XOR swizzle of the 16-byte chunks of LDS row r (values < 8, so a chunk stays
 // inside its aligned group of 8).  With it, 16 consecutive rows read at one
@@ -169,9 +170,7 @@ __global__ __launch_bounds__(128 * NHG) void sfa_kernel(MlaDev a, int kps, int n
                 const int part = SWZ ? (pos ^ sfa_swz(row)) : pos;
                 const int64_t off = roff[t * TROWS + row];
                 const uint8_t* g = (off >= 0 && part < CPK) ? a.kv.data + off + part * 16 : g_zero16;
-                const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(j * NT * 16));
-                __builtin_amdgcn_global_load_lds(
-                    g, (__attribute__((address_space(3))) void*)(uintptr_t)dst, 16, 0, 0);
+                lds_dma<16, 0>(g, lds0 + (uint32_t)(j * NT * 16));
             }
         }
     };
@@ -614,10 +613,9 @@ __global__ __launch_bounds__(128 * NHG) void sfa_bf16_kernel(MlaDev a, int kps, 
             const uint32_t blk = tile_lds + (uint32_t)(buf * TB + (p * (RPP / 8) + wave) * GB);
             static_for<NJ>([&](auto jc) {
                 constexpr int j = decltype(jc)::value;
-                // the immediate offset moves both the global and the LDS address
-                const uint32_t dst = __builtin_amdgcn_readfirstlane(blk + (uint32_t)(j * (1024 - 128)));
-                __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(uintptr_t)dst, 16,
-                                                 j * 128, 0);
+                // the immediate offset moves both the global and the LDS address;
+                // block j lands at blk + j KB
+                lds_dma<16, j * 128>(g, blk + (uint32_t)(j * (1024 - 128)));
             });
         }
     };
@@ -991,10 +989,9 @@ __global__ __launch_bounds__(512) void sfa_w8_kernel(MlaDev a, int kps, int nspl
         const uint32_t blk = tile_lds + (uint32_t)(buf * TB + wave * GB);
         static_for<NJ>([&](auto jc) {
             constexpr int j = decltype(jc)::value;
-            // the immediate offset moves both the global and the LDS address
-            const uint32_t dst = __builtin_amdgcn_readfirstlane(blk + (uint32_t)(j * (1024 - 128)));
-            __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(uintptr_t)dst, 16,
-                                             j * 128, 0);
+            // the immediate offset moves both the global and the LDS address;
+            // block j lands at blk + j KB
+            lds_dma<16, j * 128>(g, blk + (uint32_t)(j * (1024 - 128)));
         });
     };
 
@@ -1185,11 +1182,9 @@ __global__ __launch_bounds__(512) void sfa_w8_kernel(MlaDev a, int kps, int nspl
             qk_groups(QB, 2 * NKS);
             __builtin_amdgcn_sched_barrier(0);
 
-            // Phase 2, PV(t), in two batches of MH M-tiles.  While direct-to-LDS
-            // loads are outstanding the compiler waits for every pending LDS
-            // read before an MFMA whose operands are pending, so the operands
-            // come in batches: the second batch's reads go out right after the
-            // first MFMA and fly under the rest of the first batch.
+            // Phase 2, PV(t), in two batches of MH M-tiles: the second batch's
+            // operand reads go out right after the first MFMA and fly under the
+            // rest of the first batch.
             constexpr int MH = MTV / 2;
             s16x4 ra[MH][2], rc[MH][2];
 #pragma unroll
@@ -1249,6 +1244,328 @@ __global__ __launch_bounds__(512) void sfa_w8_kernel(MlaDev a, int kps, int nspl
     };
     if (wave & 1) body(std::integral_constant<int, 1>{});
     else body(std::integral_constant<int, 0>{});
+}
+
+// Warp-specialised eight-wave kernel for 64 heads of 512 + 64 bf16 rows ---------
+//
+// Same tiles, layout, loads and lazy online softmax as sfa_w8_kernel, but the
+// waves split the work by kind instead of by columns:
+//  * q-waves 0..3: wave w owns heads 16 w .. 16 w + 15 of the block over all
+//    576 QK columns (query in 72 VGPRs): S^T of tile t+1 (36 MFMAs), masking,
+//    tile maximum, lazy reference raise and exponentials; it writes P^T to an
+//    LDS ring in the PV B-operand's lane layout (lane = head, K-slots 8 g ..
+//    8 g + 7 = keys 16 kb + 4 g + i), with a per-tile raise flag and factors.
+//  * p-waves 4..7: wave 4 + c owns value columns 128 c .. 128 c + 127 of all
+//    64 heads (O^T in 128 accumulator VGPRs): applies the raise factors of the
+//    flagged head tiles and runs PV of tile t (32 MFMAs), the value operand
+//    from transpose reads as in sfa_w8_kernel.  The p-waves also issue the
+//    direct-to-LDS tile loads, NBUF - 2 tiles ahead, from inline assembly
+//    (lds_dma): hidden from the compiler's wait-count model, they no longer
+//    turn every LDS operand wait of the issuing wave into a full drain; explicit
+//    vmcnt waits and the per-tile barrier order them instead.
+// Waves w and w + 4 share a SIMD, so QK^T + softmax of tile t+1 and PV of tile
+// t overlap; one barrier per tile hands P over.  The two roles run separate
+// loops with the same number of barriers, so their registers do not add up.
+template <int DLAT, int DROPE, int NBUF, int MAXK>
+__global__ __launch_bounds__(512) void sfa_ws_kernel(MlaDev a, int kps, int nsplit, int nhb,
+                                                      __bf16* __restrict__ out, float* __restrict__ lse,
+                                                      float* __restrict__ part_o, float* __restrict__ part_lse) {
+    constexpr int DQK = DLAT + DROPE;
+    constexpr int CPK = DQK * 2 / 16;       // 16-byte chunks per row
+    static_assert((DQK * 2) % 128 == 0 && CPK * 16 <= 2048, "rows must be whole 128-byte groups");
+    constexpr int NJ = CPK / 8;             // 1 KB blocks per 8-row group
+    constexpr int GB = NJ * 1024;           // bytes per 8-row group
+    constexpr int TROWS = 32;
+    constexpr int TB = (TROWS / 8) * GB;    // bytes per tile
+    static_assert(NBUF >= 3, "PV(t) | QK(t+1) | tiles t+2 .. in flight");
+    constexpr int NT = 512;
+    constexpr int KS = DQK / 32;            // 16x16x32 K-steps of a row
+    constexpr int DVP = DLAT / 4;           // value columns per p-wave
+    constexpr int MTP = DVP / 16;           // PV M-tiles per p-wave
+    static_assert(DVP % 64 == 0, "whole 1 KB blocks per p-wave");
+    typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+    __shared__ __attribute__((aligned(1024))) uint8_t tile[NBUF * TB];
+    __shared__ uint32_t rslot[MAXK];                   // cache slot of each selected row, ~0 = skip
+    __shared__ uint32_t vmask[MAXK / 32];              // valid-row bits of each 32-row tile
+    __shared__ __attribute__((aligned(16))) uint8_t pbuf[2][4][64 * 16];   // P^T operands [slot][head tile][lane]
+    __shared__ float alph[2][64];                      // raise factors [slot][head]
+    __shared__ int rflag[2][4];                        // raised head tiles [slot][head tile]
+    float* const fin_l = (float*)&pbuf[0][0][0];       // softmax totals after the last tile (the P ring is
+                                                       // free by then)
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int bid = blockIdx.x;
+    const int hb = (bid >> 3) % nhb;
+    const int u = ((bid >> 3) / nhb) * 8 + (bid & 7);
+    if (u >= a.R * nsplit) return;
+    const int r = u / nsplit, sp = u % nsplit;
+    const int k0 = sp * kps;
+    const int k1 = (k0 + kps < a.K) ? k0 + kps : a.K;
+    const int nk = k1 - k0;
+    const int seq = a.row_seq[r];
+    const int nt_fill = (nk + TROWS - 1) / TROWS;
+    __shared__ int s_ntiles;
+    if (tid == 0) s_ntiles = 1;
+
+    for (int i0 = 0; i0 < nt_fill * TROWS; i0 += NT) {
+        const int i = i0 + tid;
+        int64_t s = -1;
+        if (i < nk) {
+            const int p = a.idx[(int64_t)r * a.K + k0 + i];
+            s = p >= 0 ? slot_of(a.kv, seq, p) : -1;
+        }
+        if (i < nt_fill * TROWS) rslot[i] = s >= 0 ? (uint32_t)s : 0xFFFFFFFFu;
+        const uint64_t bal = __ballot(s >= 0);
+        if (lane == 0 && i < nt_fill * TROWS) {
+            vmask[i / 32] = (uint32_t)bal;
+            if (i + 32 < nt_fill * TROWS) vmask[i / 32 + 1] = (uint32_t)(bal >> 32);
+        }
+    }
+    __syncthreads();
+    // trailing tiles without a valid row are skipped; at least one tile is
+    // always processed (an empty tile contributes nothing)
+    for (int t = tid; t < nt_fill; t += NT)
+        if (vmask[t] != 0u) atomicMax(&s_ntiles, t + 1);
+    __syncthreads();
+    const int ntiles = s_ntiles;
+
+    const lds_u8* tile0 = (const lds_u8*)tile;
+    const int g = lane >> 4, l16 = lane & 15;
+    const float kLazy = 8.0f;
+
+    if (wave < 4) {
+        // ---------------------------------------------------------------- q-wave
+        const int hq = wave;
+        const int head = hb * 64 + hq * 16 + l16;
+        // the query in B-operand layout: lane = head, 8 consecutive d of K-step ks
+        bf16x8 qb[KS];
+#pragma unroll
+        for (int j = 0; j < KS; ++j) {
+            if (head < a.H)
+                qb[j] = *(const bf16x8*)(a.q + (((int64_t)r * a.H + head) * DQK + j * 32 + g * 8) * 2);
+            else
+                qb[j] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+        }
+        // QK operand of key block kb, K-step ks: row 16 kb + l16, chunk 4 ks + g
+        uint32_t qa[2];
+#pragma unroll
+        for (int par = 0; par < 2; ++par)
+            qa[par] = (uint32_t)((l16 >> 3) * GB + (l16 & 7) * 128 + (((4 * par + g) ^ sfa_swz8(l16)) << 4));
+        auto qk_op = [&](const lds_u8* T, int kb, int ks) -> bf16x8 {   // compile-time kb, ks
+            return *(const lds_bf16x8*)(T + qa[ks & 1] + kb * 2 * GB + (ks >> 1) * 1024);
+        };
+        float m2 = -__builtin_inff(), lsum = 0.f;
+        const float c = a.scale_log2;
+
+        // S^T of one tile, softmax statistics, P^T to LDS slot ps
+        auto q_tile = [&](const lds_u8* T, uint32_t vm, int ps) {
+            f32x4v s[2] = {f32x4v{0.f, 0.f, 0.f, 0.f}, f32x4v{0.f, 0.f, 0.f, 0.f}};
+            constexpr int PB = 6;   // operand reads per batch
+            static_for<(2 * KS) / PB>([&](auto bc) {
+                constexpr int b0 = decltype(bc)::value * PB;
+                bf16x8 av[PB];
+#pragma unroll
+                for (int j = 0; j < PB; ++j) av[j] = qk_op(T, (b0 + j) & 1, (b0 + j) >> 1);
+#pragma unroll
+                for (int j = 0; j < PB; ++j)
+                    s[(b0 + j) & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[j], qb[(b0 + j) >> 1],
+                                                                              s[(b0 + j) & 1], 0, 0, 0);
+            });
+            if (vm != 0xFFFFFFFFu) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (!((vm >> (16 * kb + 4 * g + i)) & 1u)) s[kb][i] = -__builtin_inff();
+            }
+            float tmax = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                               fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+            {
+                const auto w16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+                tmax = fmaxf(__uint_as_float(w16[0]), __uint_as_float(w16[1]));
+                const auto w32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+                tmax = fmaxf(__uint_as_float(w32[0]), __uint_as_float(w32[1]));
+            }
+            tmax *= c;   // c > 0
+            const bool raise = tmax > m2 + kLazy;   // also true on the first valid tile
+            const bool any = __ballot(raise) != 0ull;
+            if (any) {
+                const float mnew = raise ? tmax : m2;
+                const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);  // m2 = -inf -> 0
+                lsum *= alpha;
+                m2 = mnew;
+                if (g == 0) alph[ps][hq * 16 + l16] = alpha;
+            }
+            if (lane == 0) rflag[ps][hq] = any ? 1 : 0;
+            const float negm = m2 == -__builtin_inff() ? 0.f : -m2;
+            float pe[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e >> 2][e & 3], c, negm));
+            float rs = ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
+            {
+                const auto w16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(rs), __float_as_uint(rs), false, false);
+                rs = __uint_as_float(w16[0]) + __uint_as_float(w16[1]);
+                const auto w32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(rs), __float_as_uint(rs), false, false);
+                rs = __uint_as_float(w32[0]) + __uint_as_float(w32[1]);
+            }
+            lsum += rs;
+            bf16x8 pb;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pb[e] = (__bf16)pe[e];
+            *(__attribute__((address_space(3))) bf16x8*)((lds_u8*)pbuf[ps][hq] + lane * 16) = pb;
+        };
+
+        __syncthreads();                                   // barrier P: tile 0 landed
+        q_tile(tile0, vmask[0], 0);
+        int bq = 1;                                        // buffer of tile t+1
+        for (int t = 0; t < ntiles; ++t) {
+            __syncthreads();                               // barrier t: P(t) published, tile t+1 landed
+            if (t + 1 < ntiles) {
+                const uint32_t vmn = __builtin_amdgcn_readfirstlane(vmask[t + 1]);
+                q_tile(tile0 + bq * TB, vmn, (t + 1) & 1);
+            }
+            bq = bq == NBUF - 1 ? 0 : bq + 1;
+        }
+        // softmax totals for the p-waves, and the normaliser
+        __syncthreads();                                   // barrier F: the P ring is no longer read
+        if (g == 0) {
+            fin_l[hq * 16 + l16] = lsum;
+            if (head < a.H) {
+                const float l_nat = lsum > 0.f ? (m2 + log2f(lsum)) * kLn2 : -__builtin_inff();
+                if (nsplit == 1 && out != nullptr) {
+                    if (lse != nullptr) lse[(int64_t)r * a.H + head] = l_nat;
+                } else {
+                    part_lse[((int64_t)r * nsplit + sp) * a.H + head] = l_nat;
+                }
+            }
+        }
+        __syncthreads();                                   // barrier E
+    } else {
+        // ---------------------------------------------------------------- p-wave
+        // The p-waves also load the tiles (see the kernel comment).
+        const int pc = wave - 4;
+        const uint32_t tile_lds = (uint32_t)(uintptr_t)tile;
+        const int lrow = (tid >> 3) & 31;
+        const uint32_t goff = (uint32_t)(((tid & 7) ^ sfa_swz8(lrow)) << 4);
+        auto read_slot = [&](int t) -> uint32_t { return rslot[(t < ntiles ? t : 0) * TROWS + lrow]; };
+        auto issue_tile = [&](uint32_t s, int buf) {
+            const uint8_t* gp = (s != 0xFFFFFFFFu ? a.kv.data + (uint64_t)s * (uint32_t)a.kv.row_stride : g_zero_row) + goff;
+            const uint32_t blk = tile_lds + (uint32_t)(buf * TB + pc * GB);
+            static_for<NJ>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                // the immediate offset moves both the global and the LDS address;
+                // block j lands at blk + j KB
+                lds_dma<16, j * 128>(gp, blk + (uint32_t)(j * (1024 - 128)));
+            });
+        };
+        // tiles 0 .. LA up front; tile t + 1 + LA goes out in iteration t into the
+        // buffer PV(t-1) has released.  Each thread issues NJ loads per tile, so
+        // "tile j landed" = at most NJ * (tiles issued after j) loads pending.
+        constexpr int LA = NBUF - 2;
+        static_assert(LA <= 2, "wait counts cover two tiles in flight");
+        auto wait_tile = [&](int j, int last) {            // tile j landed; tiles up to `last` issued
+            const int after = (ntiles - 1 < last ? ntiles - 1 : last) - j;
+            if (after >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NJ) : "memory");
+            else if (after == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NJ) : "memory");
+            else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        };
+        for (int j = 0; j <= LA; ++j)
+            if (j < ntiles) issue_tile(read_slot(j), j);
+        uint32_t sl = read_slot(LA + 1);
+        // PV operand of M-tile mt: transpose reads of rows 4 g + l16 / 4 (keys of
+        // K-slots 0..3) and 16 + 4 g + l16 / 4 (K-slots 4..7), 4 value columns each
+        uint32_t pva[4];
+#pragma unroll
+        for (int m4 = 0; m4 < 4; ++m4) {
+            const int rr = 4 * g + (l16 >> 2);
+            const int cc = 2 * m4 + ((l16 & 3) >> 1);
+            pva[m4] = (uint32_t)((rr >> 3) * GB + (rr & 7) * 128 + ((cc ^ sfa_swz8(rr)) << 4) + 8 * (l16 & 1));
+        }
+        typedef short s16x4 __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+        auto trd = [&](const lds_u8* T, int mt, int half) -> s16x4 {   // compile-time mt, half
+            return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4*)(T + pva[mt & 3] + half * 2 * GB + (2 * pc + (mt >> 2)) * 1024));
+        };
+        f32x4v o[4][MTP];
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+            for (int mt = 0; mt < MTP; ++mt) o[ht][mt] = f32x4v{0.f, 0.f, 0.f, 0.f};
+
+        wait_tile(0, LA);
+        __syncthreads();                                   // barrier P: tile 0 landed
+        int bc = 0;                                        // buffer of tile t
+        for (int t = 0; t < ntiles; ++t) {
+            wait_tile(t + 1, t + LA);
+            __syncthreads();                               // barrier t: tile t+1 landed
+            {
+                const int bn = bc + LA + 1 >= NBUF ? bc + LA + 1 - NBUF : bc + LA + 1;   // = buffer of tile t-1
+                if (t + 1 + LA < ntiles) issue_tile(sl, bn);
+                sl = read_slot(t + 2 + LA);
+            }
+            const int ps = t & 1;
+            const lds_u8* T = tile0 + bc * TB;
+            s16x4 va[MTP][2];
+#pragma unroll
+            for (int mt = 0; mt < MTP; ++mt) {
+                va[mt][0] = trd(T, mt, 0);
+                va[mt][1] = trd(T, mt, 1);
+            }
+            bf16x8 pbt[4];
+#pragma unroll
+            for (int ht = 0; ht < 4; ++ht)
+                pbt[ht] = *(const __attribute__((address_space(3))) bf16x8*)((const lds_u8*)pbuf[ps][ht] + lane * 16);
+            const int fl = rflag[ps][0] | (rflag[ps][1] << 1) | (rflag[ps][2] << 2) | (rflag[ps][3] << 3);
+            if (fl != 0) {
+#pragma unroll
+                for (int ht = 0; ht < 4; ++ht) {
+                    if ((fl >> ht) & 1) {
+                        const float al = alph[ps][ht * 16 + l16];
+#pragma unroll
+                        for (int mt = 0; mt < MTP; ++mt) o[ht][mt] *= al;
+                    }
+                }
+            }
+#pragma unroll
+            for (int mt = 0; mt < MTP; ++mt) {
+                const u32x2 lo = __builtin_bit_cast(u32x2, va[mt][0]);
+                const u32x2 hi = __builtin_bit_cast(u32x2, va[mt][1]);
+                const bf16x8 v = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+#pragma unroll
+                for (int ht = 0; ht < 4; ++ht)
+                    o[ht][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pbt[ht], o[ht][mt], 0, 0, 0);
+            }
+            bc = bc == NBUF - 1 ? 0 : bc + 1;
+        }
+        __syncthreads();                                   // barrier F
+        __syncthreads();                                   // barrier E
+        // normalise and store.  O^T accumulator of head tile ht, M-tile mt: lane =
+        // head l16, register i = value column 128 pc + 16 mt + 4 g + i.
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht) {
+            const int head = hb * 64 + ht * 16 + l16;
+            if (head >= a.H) continue;
+            const float ls = fin_l[ht * 16 + l16];
+            const float inv = ls > 0.f ? 1.f / ls : 0.f;
+            if (nsplit == 1 && out != nullptr) {
+                __bf16* orow = out + ((int64_t)r * a.H + head) * DLAT + pc * DVP + 4 * g;
+#pragma unroll
+                for (int mt = 0; mt < MTP; ++mt) {
+                    bf16x4 v;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) v[i] = (__bf16)(o[ht][mt][i] * inv);
+                    *(bf16x4*)(orow + 16 * mt) = v;
+                }
+            } else {
+                float* prow = part_o + (((int64_t)r * nsplit + sp) * a.H + head) * DLAT + pc * DVP + 4 * g;
+#pragma unroll
+                for (int mt = 0; mt < MTP; ++mt) *(f32x4v*)(prow + 16 * mt) = o[ht][mt] * inv;
+            }
+        }
+    }
 }
 
 // Merge partial results: out = sum_i e^{lse_i - M} O_i / sum_i e^{lse_i - M},
@@ -1379,7 +1696,13 @@ static hipError_t launch_sfa_t(const MlaDev& a, const SfaPlan& p, __bf16* out, f
         part_o = out_f32;
         part_lse = lse;
     }
-    if constexpr (!FP8 && ((DLAT + DROPE) * 2) % 128 == 0 && NHG == 2)
+    if (!FP8 && DLAT == 512 && DROPE == 64 && NHG == 2 && kSfaWarpSpecialised && p.kps <= 1024)
+        hipLaunchKernelGGL((sfa_ws_kernel<512, 64, 4, 1024>), dim3((unsigned)nwg), dim3(512), 0, stream, a, p.kps,
+                           p.nsplit, p.nhb, out, lse, part_o, part_lse);
+    else if (!FP8 && DLAT == 512 && DROPE == 64 && NHG == 2 && kSfaWarpSpecialised)
+        hipLaunchKernelGGL((sfa_ws_kernel<512, 64, 3, kSfaMaxKeys>), dim3((unsigned)nwg), dim3(512), 0, stream, a,
+                           p.kps, p.nsplit, p.nhb, out, lse, part_o, part_lse);
+    else if constexpr (!FP8 && ((DLAT + DROPE) * 2) % 128 == 0 && NHG == 2)
         hipLaunchKernelGGL((sfa_w8_kernel<DLAT, DROPE>), dim3((unsigned)nwg), dim3(512), 0, stream, a, p.kps,
                            p.nsplit, p.nhb, out, lse, part_o, part_lse);
     else if constexpr (!FP8 && ((DLAT + DROPE) * 2) % 128 == 0)
