@@ -1362,16 +1362,29 @@ __global__ __launch_bounds__(512) void sfa_ws_kernel(MlaDev a, int kps, int nspl
         // S^T of one tile, softmax statistics, P^T to LDS slot ps
         auto q_tile = [&](const lds_u8* T, uint32_t vm, int ps) {
             f32x4v s[2] = {f32x4v{0.f, 0.f, 0.f, 0.f}, f32x4v{0.f, 0.f, 0.f, 0.f}};
-            constexpr int PB = 6;   // operand reads per batch
-            static_for<(2 * KS) / PB>([&](auto bc) {
-                constexpr int b0 = decltype(bc)::value * PB;
-                bf16x8 av[PB];
+            // operand reads in batches of PB, software-pipelined: the reads of
+            // batch b + 1 go out before the MFMAs of batch b, so 6 .. 12 reads
+            // are in flight while the MFMAs run (the scheduling barriers keep the
+            // compiler from pairing each read with its MFMA)
+            constexpr int PB = 6;
+            constexpr int NB = (2 * KS) / PB;
+            static_assert((2 * KS) % PB == 0, "whole batches");
+            bf16x8 av[2][PB];
 #pragma unroll
-                for (int j = 0; j < PB; ++j) av[j] = qk_op(T, (b0 + j) & 1, (b0 + j) >> 1);
+            for (int j = 0; j < PB; ++j) av[0][j] = qk_op(T, j & 1, j >> 1);
+            static_for<NB>([&](auto bc) {
+                constexpr int b = decltype(bc)::value;
+                if constexpr (b + 1 < NB) {
+#pragma unroll
+                    for (int j = 0; j < PB; ++j)
+                        av[(b + 1) & 1][j] = qk_op(T, ((b + 1) * PB + j) & 1, ((b + 1) * PB + j) >> 1);
+                }
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int j = 0; j < PB; ++j)
-                    s[(b0 + j) & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[j], qb[(b0 + j) >> 1],
-                                                                              s[(b0 + j) & 1], 0, 0, 0);
+                    s[(b * PB + j) & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        av[b & 1][j], qb[(b * PB + j) >> 1], s[(b * PB + j) & 1], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
             });
             if (vm != 0xFFFFFFFFu) {
 #pragma unroll
