@@ -1309,15 +1309,24 @@ __global__ __launch_bounds__(512) void sfa_ws_kernel(MlaDev a, int kps, int nspl
     __shared__ int s_ntiles;
     if (tid == 0) s_ntiles = 1;
 
-    for (int i0 = 0; i0 < nt_fill * TROWS; i0 += NT) {
-        const int i = i0 + tid;
-        int64_t s = -1;
-        if (i < nk) {
-            const int p = a.idx[(int64_t)r * a.K + k0 + i];
-            s = p >= 0 ? slot_of(a.kv, seq, p) : -1;
-        }
-        if (i < nt_fill * TROWS) rslot[i] = s >= 0 ? (uint32_t)s : 0xFFFFFFFFu;
-        const uint64_t bal = __ballot(s >= 0);
+    // every index load of the thread first, then every block-table lookup, so
+    // the slots cost two dependent global round trips in all
+    constexpr int EPT = MAXK / NT;          // index entries per thread
+    static_assert(MAXK % NT == 0, "whole rounds");
+    int pidx[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        const int i = j * NT + tid;
+        pidx[j] = i < nk ? a.idx[(int64_t)r * a.K + k0 + i] : -1;
+    }
+    int64_t sv[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) sv[j] = pidx[j] >= 0 ? slot_of(a.kv, seq, pidx[j]) : -1;
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        const int i = j * NT + tid;
+        if (i < nt_fill * TROWS) rslot[i] = sv[j] >= 0 ? (uint32_t)sv[j] : 0xFFFFFFFFu;
+        const uint64_t bal = __ballot(sv[j] >= 0);
         if (lane == 0 && i < nt_fill * TROWS) {
             vmask[i / 32] = (uint32_t)bal;
             if (i + 32 < nt_fill * TROWS) vmask[i / 32 + 1] = (uint32_t)(bal >> 32);
