@@ -102,7 +102,7 @@ def stored_traffic(stage: str, workload: str):
 STAGE_KERNELS = {
     "li_score": ["li_score"],
     "topk_select": ["topk"],
-    "sparse_mla_attn": ["sfa_w8_kernel", "sfa_bf16_kernel", "sfa_kernel<", "sfa_combine_kernel"],
+    "sparse_mla_attn": ["sfa_ws_kernel", "sfa_w8_kernel", "sfa_bf16_kernel", "sfa_kernel<", "sfa_combine_kernel"],
 }
 
 
