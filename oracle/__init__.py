@@ -6,6 +6,7 @@ by CPU tests against exact arithmetic, brute force, closed forms and library
 routines (see tests/test_oracle.py)."""
 from .lisfa_oracle import (  # noqa: F401
     decode_bf16, decode_e4m3, e4m3_table, decode_e8m0, decode_mx, encode_e4m3, mx_quantize, slots, indexer_keys, latent_rows,
+    decode_tile_scaled, KV_TILE,
     indexer_query, mla_query, indexer_scores, select_topk, sparse_mla,
     layer_row, attend_row, scores_row,
 )

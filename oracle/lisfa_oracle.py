@@ -33,6 +33,16 @@ format itself is the OCP 8-bit floating point definition: 1 sign bit, 4
 exponent bits with bias 7, 3 mantissa bits, no infinities, S.1111.111 = NaN).
 Scaled values are code_value * scale, evaluated in float64.
 
+FP8 latent cache with tile scales ("Day0 Inference Adaptation and
+Performance Optimization for Kimi K3.1 Pro", section 4; "Large Language Model
+Inference Acceleration in Practice", section 4 and its table of formats): e4m3
+codes quantised per token, per head and per tile of 128 elements.  The MLA
+latent row is one vector shared by all heads, so a row of width W carries
+ceil(W / 128) fp32 scales, scale j covering columns [128 j, 128 j + 128) (the
+last tile of a 576-wide row holds the 64 rope columns).  The pages fix the
+tile size only; one fp32 factor per tile is the reading taken here.  Values are
+code_value * scale[slot, column // 128].
+
 MXFP8 indexer ("Day0 Inference Adaptation and Performance Optimization for
 Kimi K3.1 Pro", section 4 and "... for a New Model", section 4: indexer
 queries and keys in MXFP8 with one shared scale per group of 32 elements):
@@ -97,9 +107,20 @@ def decode_mx(codes: np.ndarray, scales: np.ndarray, block: int = 32) -> np.ndar
 def _decode(arr: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         return decode_bf16(arr)
-    if dtype in ("fp8", "mxfp8"):
+    if dtype in ("fp8", "mxfp8", "fp8_tile128"):
         return decode_e4m3(arr)
     raise ValueError(dtype)
+
+
+KV_TILE = 128   # elements per scale tile of the tile-scaled fp8 latent cache
+
+
+def decode_tile_scaled(codes: np.ndarray, scales: np.ndarray, tile: int = KV_TILE) -> np.ndarray:
+    """Rows of e4m3 codes [n, W] with fp32 scales [n, ceil(W / tile)]: element
+    (i, c) = code_value * scales[i, c // tile], float64."""
+    codes = np.asarray(codes)
+    col_tile = np.arange(codes.shape[-1]) // tile
+    return decode_e4m3(codes) * np.asarray(scales, dtype=np.float64)[..., col_tile]
 
 
 def encode_e4m3(v: np.ndarray) -> np.ndarray:
@@ -166,6 +187,8 @@ def indexer_keys(inp: Dict, seq: int, n: int) -> np.ndarray:
 def latent_rows(inp: Dict, seq: int, positions: np.ndarray) -> np.ndarray:
     """Latent cache rows [latent | rope] of the given positions, float64."""
     sl = slots(inp, seq, positions)
+    if inp["kv_dtype"] == "fp8_tile128":
+        return decode_tile_scaled(inp["kv_data"][sl], inp["kv_scale"][sl])
     rows = _decode(inp["kv_data"][sl], inp["kv_dtype"])
     if inp["kv_dtype"] == "fp8":
         g = int(inp["kv_scale_group"])

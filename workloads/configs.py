@@ -40,7 +40,7 @@ class Workload:
     softmax_scale: float = 1.0 / math.sqrt(576.0)
     # storage
     indexer_dtype: str = "bf16"     # "bf16" | "fp8" | "mxfp8" (e4m3 + E8M0 scale per 32 elements)
-    kv_dtype: str = "bf16"          # "bf16" | "fp8"
+    kv_dtype: str = "bf16"          # "bf16" | "fp8" | "fp8_tile128"
     paged: bool = False
     block_size: int = 64
     kv_scale_group: int = 64        # tokens per fp32 latent-cache scale (fp8 only)

@@ -20,7 +20,9 @@ weight logits, MLA queries.
 fp8 storage (OCP e4m3, max 448) uses amax/448 scales (1 when amax is 0):
 indexer keys one scale per token, indexer queries one scale per query token
 (over all heads), latent rows one scale per group of kv_scale_group
-consecutive physical slots.  The quantisation is part of input preparation:
+consecutive physical slots, or (kv_dtype "fp8_tile128") one scale per tile of
+128 elements of each row (integer inputs: the power-of-two scales 1/2, 1, 2
+in turn over the tiles, so every value stays exact).  The quantisation is part of input preparation:
 both the kernels and the oracle consume the stored codes and scales.
 
 Paged layout: blocks of block_size tokens; the physical block ids are a
@@ -62,7 +64,8 @@ class Batch:
     k_data: torch.Tensor                # [num_slots, D_I] bf16 / uint8
     k_scale: Optional[torch.Tensor]     # [num_slots] fp32
     kv_data: torch.Tensor               # [num_slots, D_qk] bf16 / uint8
-    kv_scale: Optional[torch.Tensor]    # [num_slots // kv_scale_group] fp32
+    kv_scale: Optional[torch.Tensor]    # [num_slots // kv_scale_group] fp32, or [num_slots, ceil(D_qk / 128)]
+                                        # for fp8_tile128
     block_table: Optional[torch.Tensor]  # [num_seqs, bt_stride] int32 (paged)
     seq_base: Optional[torch.Tensor]    # [num_seqs] int64 (contiguous)
 
@@ -86,6 +89,31 @@ def quantize_e4m3(x: torch.Tensor, dim) -> (torch.Tensor, torch.Tensor):
     y = (x.to(torch.float32) / scale).clamp_(-E4M3_MAX, E4M3_MAX)
     codes = y.to(torch.float8_e4m3fn).view(torch.uint8)
     return codes, scale
+
+
+KV_TILE = 128   # elements per scale tile of the tile-scaled fp8 latent cache
+
+
+def quantize_tiles(x: torch.Tensor, tile: int, exact_pow2: bool = False) -> (torch.Tensor, torch.Tensor):
+    """Rows x [n, W] -> e4m3 codes [n, W] and fp32 scales [n, ceil(W / tile)],
+    one per tile of `tile` columns: amax/448 (1 for an all-zero tile), or with
+    exact_pow2 the scales 1/2, 1, 2 in turn over the tiles (for integer-valued
+    rows, whose quotients stay exact in e4m3)."""
+    n, W = x.shape
+    nt = (W + tile - 1) // tile
+    xf = x.to(torch.float32)
+    pad = nt * tile - W
+    xp = torch.cat([xf, torch.zeros(n, pad, device=x.device)], dim=1) if pad else xf
+    g = xp.view(n, nt, tile)
+    if exact_pow2:
+        sc = torch.tensor([0.5, 1.0, 2.0], device=x.device)[torch.arange(nt, device=x.device) % 3]
+        sc = sc.view(1, nt, 1).expand(n, nt, 1).contiguous()
+    else:
+        amax = g.abs().amax(dim=2, keepdim=True)
+        sc = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
+    y = (g / sc).clamp_(-E4M3_MAX, E4M3_MAX)
+    codes = y.to(torch.float8_e4m3fn).view(torch.uint8).view(n, nt * tile)[:, :W].contiguous()
+    return codes, sc.view(n, nt)
 
 
 def quantize_mx(x: torch.Tensor, block: int = 32) -> (torch.Tensor, torch.Tensor):
@@ -160,6 +188,7 @@ def make_batch(wl: Workload, device="cpu", chunk_tokens: int = 1 << 16) -> Batch
     fp8_idx = wl.indexer_dtype == "fp8"
     mx_idx = wl.indexer_dtype == "mxfp8"
     fp8_kv = wl.kv_dtype == "fp8"
+    tile_kv = wl.kv_dtype == "fp8_tile128"
 
     # 3. indexer keys
     if mx_idx:
@@ -201,6 +230,10 @@ def make_batch(wl: Workload, device="cpu", chunk_tokens: int = 1 << 16) -> Batch
             assert bs % g == 0
         kv_data = torch.full((num_slots, D_qk), E4M3_NAN_BITS, dtype=torch.uint8, device=device)
         kv_scale = torch.full((num_slots // g,), float("nan"), dtype=torch.float32, device=device)
+    elif tile_kv:
+        n_tiles = (D_qk + KV_TILE - 1) // KV_TILE
+        kv_data = torch.full((num_slots, D_qk), E4M3_NAN_BITS, dtype=torch.uint8, device=device)
+        kv_scale = torch.full((num_slots, n_tiles), float("nan"), dtype=torch.float32, device=device)
     else:
         kv_data = torch.full((num_slots, D_qk), BF16_NAN_BITS, dtype=torch.int16,
                              device=device).view(torch.bfloat16)
@@ -227,6 +260,10 @@ def make_batch(wl: Workload, device="cpu", chunk_tokens: int = 1 << 16) -> Batch
                     codes, sc = quantize_e4m3(xg, dim=(1, 2))
                 kv_data[sl] = codes.view(ng * g, D_qk)[:n]
                 kv_scale[(sl[::g] // g)] = sc.view(ng)
+            elif tile_kv:
+                codes, sc = quantize_tiles(x, KV_TILE, wl.dist == "int8range")
+                kv_data[sl] = codes
+                kv_scale[sl] = sc
             else:
                 kv_data[sl] = _store(x, "bf16")
 
