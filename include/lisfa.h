@@ -64,6 +64,10 @@ typedef struct ihipStream_t* lisfa_stream_t; /* a hipStream_t */
                                (2^(e-127)) per 32 consecutive elements of a row; indexer
                                queries and keys only ("Day0 Inference Adaptation and
                                Performance Optimization for Kimi K3.1 Pro", section 4) */
+#define LISFA_FP8_TILE128 3 /* e4m3 codes with one fp32 factor per tile of 128 elements of
+                               each row (per token and head, tile 128: the same page,
+                               section 4, and "Large Language Model Inference Acceleration
+                               in Practice", section 4); MLA latent cache only */
 
 /*
  * A cache of fixed-width rows, one per token slot ("Kimi New Model Open
@@ -81,10 +85,14 @@ typedef struct ihipStream_t* lisfa_stream_t; /* a hipStream_t */
 typedef struct {
     const void*    data;               /* [num_slots, row_stride_bytes] */
     int64_t        num_slots;          /* slots in the pool (bounds checks) */
-    int32_t        dtype;              /* LISFA_BF16, LISFA_FP8_E4M3 or LISFA_MXFP8 */
+    int32_t        dtype;              /* LISFA_BF16, LISFA_FP8_E4M3, LISFA_MXFP8 or
+                                          LISFA_FP8_TILE128 */
     int32_t        row_stride_bytes;   /* multiple of 16, >= row width in bytes */
     const void*    scale;              /* fp8: fp32 [num_slots / scale_group_tokens];
-                                          mxfp8: uint8 E8M0 [num_slots, width / 32]; bf16: NULL */
+                                          mxfp8: uint8 E8M0 [num_slots, width / 32];
+                                          fp8 tile 128: fp32 [num_slots, ceil(width / 128)],
+                                          entry j covering columns [128 j, 128 j + 128),
+                                          4-byte aligned; bf16: NULL */
     int32_t        scale_group_tokens; /* fp8: >= 1 */
     int32_t        block_size;         /* paged: tokens per block (> 0) */
     const int32_t* block_table;        /* paged: [num_seqs, bt_stride], else NULL */

@@ -70,8 +70,9 @@ class KVCache:
     """A cache of fixed-width rows (indexer keys or MLA latent rows).
 
     data:        [num_slots, width] bf16, or uint8 e4m3 codes
-    scale:       fp8: fp32 [num_slots // scale_group]; mxfp8 (uint8 scale):
-                 E8M0 bytes [num_slots, width // 32]
+    scale:       fp8: fp32 [num_slots // scale_group], or fp32 [num_slots,
+                 ceil(width / 128)] for one scale per 128-element tile (latent
+                 cache); mxfp8 (uint8 scale): E8M0 bytes [num_slots, width // 32]
     block_table: paged layout: int32 [num_seqs, blocks_per_seq]
     seq_base:    contiguous layout: int64 [num_seqs] first slot of each sequence
     """
@@ -91,9 +92,16 @@ class KVCache:
         return self.fp8 and self.scale is not None and self.scale.dtype == torch.uint8
 
     @property
+    def tile_scaled(self) -> bool:
+        """fp8 rows with one fp32 scale per 128-element tile: scale [num_slots, ceil(width / 128)]."""
+        return self.fp8 and self.scale is not None and self.scale.dtype == torch.float32 and self.scale.dim() == 2
+
+    @property
     def dtype_code(self) -> int:
         if self.mx:
             return _c.LISFA_MXFP8
+        if self.tile_scaled:
+            return _c.LISFA_FP8_TILE128
         return _c.LISFA_FP8_E4M3 if self.fp8 else _c.LISFA_BF16
 
     def c_struct(self) -> _c.Cache:
@@ -108,6 +116,9 @@ class KVCache:
             raise ValueError("seq_base must be int64")
         if self.fp8 and (self.scale is None or self.scale.dtype not in (torch.float32, torch.uint8)):
             raise ValueError("fp8 caches need fp32 scales (e4m3) or uint8 E8M0 scales (mxfp8)")
+        if self.tile_scaled and (tuple(self.scale.shape) != (d.shape[0], (d.shape[1] + 127) // 128)
+                                 or not self.scale.is_contiguous()):
+            raise ValueError("tile scales must be fp32 [num_slots, ceil(width / 128)], contiguous")
         return _c.Cache(
             data=_ptr(d), num_slots=d.shape[0],
             dtype=self.dtype_code,

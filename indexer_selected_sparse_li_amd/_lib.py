@@ -18,6 +18,7 @@ LISFA_ERR_UNSUPPORTED = -6
 LISFA_BF16 = 0
 LISFA_FP8_E4M3 = 1
 LISFA_MXFP8 = 2
+LISFA_FP8_TILE128 = 3
 
 LISFA_OP_TOPK = 0
 LISFA_OP_SPARSE_MLA = 1

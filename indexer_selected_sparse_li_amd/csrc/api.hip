@@ -17,10 +17,10 @@ hipError_t topk_merge_dispatch(const float* cand_score, const int32_t* cand_pos,
                                int ordered, int32_t* idx, float* idx_score, hipStream_t stream);
 int topk_slices(int64_t ld, int K);
 size_t topk_workspace_bytes(int R, int64_t ld, int K);
-hipError_t sfa_dispatch(const MlaDev& a, int D_latent, int fp8, __bf16* out, float* out_f32, float* lse, void* ws,
+hipError_t sfa_dispatch(const MlaDev& a, int D_latent, int kv_mode, __bf16* out, float* out_f32, float* lse, void* ws,
                         hipStream_t stream);
 size_t sfa_workspace_bytes(int R, int K, int H, int D_latent);
-hipError_t sfa_partial_dispatch(const MlaDev& a, const int32_t* range, int D_latent, int fp8, float* out_f32,
+hipError_t sfa_partial_dispatch(const MlaDev& a, const int32_t* range, int D_latent, int kv_mode, float* out_f32,
                                 float* lse, void* ws, hipStream_t stream);
 size_t sfa_partial_workspace_bytes(int R, int K, int H, int D_latent, int with_range);
 hipError_t lse_combine_dispatch(const float* part_o, const float* part_lse, int G, int R, int H, int D, __bf16* out,
@@ -41,7 +41,8 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 
 int check_cache(const lisfa_cache& c, int width) {
     if (!c.data) return LISFA_ERR_NULL_ARG;
-    if (c.dtype != LISFA_BF16 && c.dtype != LISFA_FP8_E4M3 && c.dtype != LISFA_MXFP8) return LISFA_ERR_BAD_DTYPE;
+    if (c.dtype != LISFA_BF16 && c.dtype != LISFA_FP8_E4M3 && c.dtype != LISFA_MXFP8 && c.dtype != LISFA_FP8_TILE128)
+        return LISFA_ERR_BAD_DTYPE;
     const int elt = c.dtype == LISFA_BF16 ? 2 : 1;
     if (c.row_stride_bytes < width * elt || c.row_stride_bytes % 16 != 0) return LISFA_ERR_BAD_SHAPE;
     if (!aligned(c.data, 16)) return LISFA_ERR_BAD_SHAPE;
@@ -55,6 +56,10 @@ int check_cache(const lisfa_cache& c, int width) {
         if (width % 32 != 0) return LISFA_ERR_BAD_SHAPE;
         if (!aligned(c.scale, 4)) return LISFA_ERR_BAD_SHAPE;
     }
+    if (c.dtype == LISFA_FP8_TILE128) {
+        if (!c.scale) return LISFA_ERR_NULL_ARG;
+        if (!aligned(c.scale, 4)) return LISFA_ERR_BAD_SHAPE;
+    }
     if (c.block_table) {
         if (c.block_size < 1 || c.block_size > (1 << 20) || (c.block_size & (c.block_size - 1)))
             return LISFA_ERR_BAD_SHAPE;
@@ -65,11 +70,16 @@ int check_cache(const lisfa_cache& c, int width) {
     return LISFA_OK;
 }
 
+// attention kernels' view of the latent cache format
+int kv_mode(const lisfa_cache& c) {
+    return c.dtype == LISFA_FP8_TILE128 ? 2 : c.dtype == LISFA_FP8_E4M3 ? 1 : 0;
+}
+
 CacheDev to_dev(const lisfa_cache& c) {
     CacheDev d;
     d.data = (const uint8_t*)c.data;
     d.num_slots = c.num_slots;
-    d.scale = c.dtype == LISFA_FP8_E4M3 ? (const float*)c.scale : nullptr;
+    d.scale = (c.dtype == LISFA_FP8_E4M3 || c.dtype == LISFA_FP8_TILE128) ? (const float*)c.scale : nullptr;
     d.mx_scale = c.dtype == LISFA_MXFP8 ? (const uint8_t*)c.scale : nullptr;
     d.block_table = c.block_table;
     d.seq_base = c.seq_base_slot;
@@ -94,6 +104,7 @@ int check_indexer(const lisfa_indexer_args* a) {
     if (!a->q || !a->w || !a->row_seq || !a->row_pos) return LISFA_ERR_NULL_ARG;
     int e = check_cache(a->k_cache, a->D_I);
     if (e) return e;
+    if (a->k_cache.dtype == LISFA_FP8_TILE128) return LISFA_ERR_BAD_DTYPE;   // a latent-cache format
     if (a->k_cache.dtype == LISFA_MXFP8) {
         if (a->D_I != 128) return LISFA_ERR_UNSUPPORTED;
         if (!a->q_scale) return LISFA_ERR_NULL_ARG;
@@ -286,7 +297,7 @@ int sparse_mla_attn(const lisfa_mla_args* args, const int32_t* idx, int32_t K, v
     if (need > 0 && (!ws || ws_bytes < need)) return LISFA_ERR_WORKSPACE;
     if (!aligned(out, 8)) return LISFA_ERR_BAD_SHAPE;
     const MlaDev d = to_dev(args, idx, K);
-    return hip_status(sfa_dispatch(d, args->D_latent, args->kv_cache.dtype == LISFA_FP8_E4M3, (__bf16*)out,
+    return hip_status(sfa_dispatch(d, args->D_latent, kv_mode(args->kv_cache), (__bf16*)out,
                                    nullptr, lse, ws, (hipStream_t)stream));
 }
 
@@ -302,7 +313,7 @@ int sparse_mla_attn_partial(const lisfa_mla_args* args, const int32_t* idx, int3
     if (need > 0 && !aligned(ws, 256)) return LISFA_ERR_BAD_SHAPE;
     if (!aligned(out, 16)) return LISFA_ERR_BAD_SHAPE;
     const MlaDev d = to_dev(args, idx, K);
-    return hip_status(sfa_partial_dispatch(d, range, args->D_latent, args->kv_cache.dtype == LISFA_FP8_E4M3, out,
+    return hip_status(sfa_partial_dispatch(d, range, args->D_latent, kv_mode(args->kv_cache), out,
                                            lse, ws, (hipStream_t)stream));
 }
 
@@ -381,7 +392,7 @@ int li_topk_sfa(const lisfa_indexer_args* iargs, const lisfa_mla_args* margs, in
         if (he != hipSuccess) return LISFA_ERR_HIP;
     }
     const MlaDev md = to_dev(margs, idx, K);
-    return hip_status(sfa_dispatch(md, margs->D_latent, margs->kv_cache.dtype == LISFA_FP8_E4M3, (__bf16*)out,
+    return hip_status(sfa_dispatch(md, margs->D_latent, kv_mode(margs->kv_cache), (__bf16*)out,
                                    nullptr, lse, sfa_ws, st));
 }
 
@@ -405,6 +416,7 @@ int indexer_k_store(const void* k, int32_t T, int32_t D_I, const float* gamma, c
     if (!k_cache) return LISFA_ERR_NULL_ARG;
     int e = check_cache(*k_cache, D_I);
     if (e) return e;
+    if (k_cache->dtype == LISFA_FP8_TILE128) return LISFA_ERR_BAD_DTYPE;   // a latent-cache format
     if (k_cache->dtype == LISFA_FP8_E4M3 && k_cache->scale_group_tokens != 1) return LISFA_ERR_BAD_SHAPE;
     if (!(eps >= 0.f)) return LISFA_ERR_BAD_SHAPE;
     if (T == 0) return LISFA_OK;

@@ -48,7 +48,7 @@ constexpr bool kSfaWarpSpecialised = true;   // 512 + 64 bf16 rows, 64-head bloc
 // the PV operand (8 consecutive rows x 4 chunks) are at the 2-way minimum.
 __device__ __forceinline__ int sfa_swz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
 
-template <int DLAT, int DROPE, bool FP8, int NHG>
+template <int DLAT, int DROPE, bool FP8, int NHG, bool TSC = false>
 __global__ __launch_bounds__(128 * NHG) void sfa_kernel(MlaDev a, int kps, int nsplit, int nhb,
                                                         __bf16* __restrict__ out, float* __restrict__ lse,
                                                         float* __restrict__ part_o,
@@ -74,10 +74,17 @@ __global__ __launch_bounds__(128 * NHG) void sfa_kernel(MlaDev a, int kps, int n
     constexpr int MTV = DVH / 32;           // PV M-tiles per wave
     constexpr bool ILV = !SWZ && (MTV % 4 == 0);  // interleaved value columns (gathered path)
     static_assert(DQK % 16 == 0 && DVH % 32 == 0, "shape");
+    // TSC: fp8 rows with one fp32 scale per 128-column tile.  QK^T sums each
+    // tile's K-steps apart and adds them with the key's tile scale; PV takes
+    // the probabilities times the key's scale of the value tile.
+    constexpr int NTL = TSC ? (DQK + 127) / 128 : 1;
+    static_assert(!TSC || FP8, "tile scales come with fp8 rows");
+    static_assert(!TSC || (ILV && DVH % 128 == 0) || NTL == 1, "value tiles: whole 128-column groups per wave");
 
     __shared__ __attribute__((aligned(16))) uint8_t tile[NBUF][TROWS * RBP];
     __shared__ int64_t roff[kSfaMaxKeys];              // byte offset of each selected row, -1 = skip
-    __shared__ float kvs[FP8 ? kSfaMaxKeys : 1];        // fp8 row factor (0 for skipped rows)
+    __shared__ __attribute__((aligned(16))) float kvs[FP8 ? NTL * kSfaMaxKeys : 1];   // fp8 factors [tile][row]
+                                                                                       // (0 for skipped rows)
     __shared__ uint32_t vmask[kSfaMaxKeys / 32];        // valid-row bits of each 32-row tile
     __shared__ __attribute__((aligned(16))) float xbuf[2][NHG * 2 * 4 * 64 * 4];
 
@@ -122,7 +129,12 @@ __global__ __launch_bounds__(128 * NHG) void sfa_kernel(MlaDev a, int kps, int n
         }
         if (i < nt_fill * TROWS) {
             roff[i] = s >= 0 ? s * a.kv.row_stride : -1;
-            if constexpr (FP8) kvs[i] = s >= 0 ? a.kv.scale[s / a.kv.scale_group] : 0.f;
+            if constexpr (TSC) {
+#pragma unroll
+                for (int j = 0; j < NTL; ++j) kvs[j * kSfaMaxKeys + i] = s >= 0 ? a.kv.scale[s * NTL + j] : 0.f;
+            } else if constexpr (FP8) {
+                kvs[i] = s >= 0 ? a.kv.scale[s / a.kv.scale_group] : 0.f;
+            }
         }
         const uint64_t bal = __ballot(s >= 0);
         if (lane == 0 && i < nt_fill * TROWS) {
@@ -183,7 +195,7 @@ __global__ __launch_bounds__(128 * NHG) void sfa_kernel(MlaDev a, int kps, int n
 #pragma unroll
     for (int m = 0; m < 4; ++m)
         qkb[m] = (uint32_t)(krow * RBP + ((((2 * m) + (lane >> 5)) ^ kswz) << 4));
-    auto qk_half = [&](const lds_u8* T, auto ksb_c) {
+    auto qk_half = [&](const lds_u8* T, int kbase, auto ksb_c) {
         constexpr int KSB = decltype(ksb_c)::value;
         constexpr int NKS = KSB == 0 ? KS0 : KS - KS0;
         auto operand = [&](int ks) -> bf16x8 {
@@ -197,9 +209,9 @@ __global__ __launch_bounds__(128 * NHG) void sfa_kernel(MlaDev a, int kps, int n
             }
         };
         constexpr int PF = 3;  // operands in flight ahead of the MFMA that uses them
-        f32x16 s;
+        f32x16 s, seg;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[i] = 0.f;
+        for (int i = 0; i < 16; ++i) s[i] = seg[i] = 0.f;
         bf16x8 buf[PF];
 #pragma unroll
         for (int j = 0; j < PF && j < NKS; ++j) buf[j] = operand(KSB + j);
@@ -207,13 +219,32 @@ __global__ __launch_bounds__(128 * NHG) void sfa_kernel(MlaDev a, int kps, int n
         for (int j = 0; j < NKS; ++j) {
             const bf16x8 av = buf[j % PF];
             if (j + PF < NKS) buf[j % PF] = operand(KSB + j + PF);
-            s = mfma32x32x16_bf16(av, qb[j], s);
+            if constexpr (TSC) {
+                seg = mfma32x32x16_bf16(av, qb[j], seg);
+                const int ks = KSB + j;
+                if ((ks + 1) % 8 == 0 || j + 1 == NKS) {   // last K-step of a 128-column tile
+                    // accumulator i holds key 8 (i / 4) + 4 (lane / 32) + i % 4
+                    const float* f0 = &kvs[(ks / 8) * kSfaMaxKeys + kbase + 4 * (lane >> 5)];
+#pragma unroll
+                    for (int j4 = 0; j4 < 4; ++j4) {
+                        const f32x4 f = *(const f32x4*)(f0 + 8 * j4);
+                        s[4 * j4] = fmaf(seg[4 * j4], f.x, s[4 * j4]);
+                        s[4 * j4 + 1] = fmaf(seg[4 * j4 + 1], f.y, s[4 * j4 + 1]);
+                        s[4 * j4 + 2] = fmaf(seg[4 * j4 + 2], f.z, s[4 * j4 + 2]);
+                        s[4 * j4 + 3] = fmaf(seg[4 * j4 + 3], f.w, s[4 * j4 + 3]);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) seg[i] = 0.f;
+                }
+            } else {
+                s = mfma32x32x16_bf16(av, qb[j], s);
+            }
         }
         return s;
     };
-    auto qk = [&](const lds_u8* T) {
-        if (dh == 0) return qk_half(T, std::integral_constant<int, 0>{});
-        return qk_half(T, std::integral_constant<int, KS0>{});
+    auto qk = [&](const lds_u8* T, int kbase) {
+        if (dh == 0) return qk_half(T, kbase, std::integral_constant<int, 0>{});
+        return qk_half(T, kbase, std::integral_constant<int, KS0>{});
     };
     // the two waves of a pair exchange partial logits through LDS;
     // layout [pair][i/4][lane][4]: consecutive lanes write consecutive 16 bytes
@@ -238,7 +269,7 @@ __global__ __launch_bounds__(128 * NHG) void sfa_kernel(MlaDev a, int kps, int n
     if (ntiles > 0) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        s_cur = qk((const lds_u8*)tile[0]);
+        s_cur = qk((const lds_u8*)tile[0], 0);
         put_partial(s_cur, 0);
     }
 
@@ -269,6 +300,7 @@ __global__ __launch_bounds__(128 * NHG) void sfa_kernel(MlaDev a, int kps, int n
             }
         }
         bf16x8 pb[2];
+        bf16x8 pbv[TSC && ILV ? MTV / 4 : 1][2];   // TSC: probabilities times each value tile's scale
         {
             // logits (base 2), masking, online softmax in place on s.  The
             // reference maximum m2 of a head is raised only when a tile's maximum
@@ -277,7 +309,7 @@ __global__ __launch_bounds__(128 * NHG) void sfa_kernel(MlaDev a, int kps, int n
             // accumulator is not rescaled.  Same softmax; only rounding differs.
             constexpr float kLazy = 8.0f;
             float tmax = -__builtin_inff();
-            if constexpr (FP8) {
+            if constexpr (FP8 && !TSC) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int key = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
@@ -327,13 +359,20 @@ __global__ __launch_bounds__(128 * NHG) void sfa_kernel(MlaDev a, int kps, int n
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     float p = s[8 * kk + e];
-                    if constexpr (FP8) p *= kvs[t * TROWS + 8 * (2 * kk + (e >> 2)) + 4 * (lane >> 5) + (e & 3)];
+                    const int key = t * TROWS + 8 * (2 * kk + (e >> 2)) + 4 * (lane >> 5) + (e & 3);
+                    if constexpr (TSC && ILV) {
+#pragma unroll
+                        for (int gv = 0; gv < MTV / 4; ++gv)
+                            pbv[gv][kk][e] = (__bf16)(p * kvs[((dh * DVH) / 128 + gv) * kSfaMaxKeys + key]);
+                    } else if constexpr (FP8) {
+                        p *= kvs[key];   // TSC with one tile: that tile's scale
+                    }
                     pb[kk][e] = (__bf16)p;
                 }
         }
         // QK^T of the next tile: independent of this tile's PV, so the two MFMA
         // streams interleave (same basic block, no branch in between)
-        if (t + 1 < ntiles) s_cur = qk(tile0 + bnext * (TROWS * RBP));
+        if (t + 1 < ntiles) s_cur = qk(tile0 + bnext * (TROWS * RBP), (t + 1) * TROWS);
         {
 
             // PV: O^T[32 value columns x 32 heads] += V^T[32 x 16 keys] * P^T.
@@ -403,7 +442,10 @@ __global__ __launch_bounds__(128 * NHG) void sfa_kernel(MlaDev a, int kps, int n
                                 const uint32_t a1 = (j < 2) ? x[2 * m + 1].x : x[2 * m + 1].y;
                                 w[m] = __builtin_amdgcn_perm(a1, a0, sel);
                             }
-                            o[4 * g + j] = mfma32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pb[kk], o[4 * g + j]);
+                            if constexpr (TSC)
+                                o[4 * g + j] = mfma32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pbv[g][kk], o[4 * g + j]);
+                            else
+                                o[4 * g + j] = mfma32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pb[kk], o[4 * g + j]);
                         }
                     }
                 }
@@ -1709,7 +1751,7 @@ SfaPlan sfa_plan(int R, int K, int H) {
 
 // out != nullptr: bf16 output; out == nullptr: fp32 normalised output in
 // out_f32 (partial results of one context shard) and lse required.
-template <int DLAT, int DROPE, bool FP8, int NHG>
+template <int DLAT, int DROPE, bool FP8, int NHG, bool TSC>
 static hipError_t launch_sfa_t(const MlaDev& a, const SfaPlan& p, __bf16* out, float* out_f32, float* lse,
                                float* part_o, float* part_lse, hipStream_t stream) {
     const int64_t units = (int64_t)a.R * p.nsplit;
@@ -1731,7 +1773,7 @@ static hipError_t launch_sfa_t(const MlaDev& a, const SfaPlan& p, __bf16* out, f
         hipLaunchKernelGGL((sfa_bf16_kernel<DLAT, DROPE, NHG>), dim3((unsigned)nwg), dim3(128 * NHG), 0, stream,
                            a, p.kps, p.nsplit, p.nhb, out, lse, part_o, part_lse);
     else
-        hipLaunchKernelGGL((sfa_kernel<DLAT, DROPE, FP8, NHG>), dim3((unsigned)nwg), dim3(128 * NHG), 0, stream, a,
+        hipLaunchKernelGGL((sfa_kernel<DLAT, DROPE, FP8, NHG, TSC>), dim3((unsigned)nwg), dim3(128 * NHG), 0, stream, a,
                            p.kps, p.nsplit, p.nhb, out, lse, part_o, part_lse);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.nsplit == 1) return e;
@@ -1748,22 +1790,28 @@ static hipError_t launch_sfa_t(const MlaDev& a, const SfaPlan& p, __bf16* out, f
     return hipGetLastError();
 }
 
-hipError_t sfa_dispatch(const MlaDev& a, int D_latent, int fp8, __bf16* out, float* out_f32, float* lse, void* ws,
+hipError_t sfa_dispatch(const MlaDev& a, int D_latent, int kv_mode, __bf16* out, float* out_f32, float* lse, void* ws,
                         hipStream_t stream) {
+    // kv_mode: 0 bf16 rows, 1 fp8 rows with per-group factors, 2 fp8 rows with
+    // one factor per 128-column tile
     const SfaPlan p = sfa_plan(a.R, a.K, a.H);
     float* part_o = (float*)ws;
     float* part_lse = part_o + (size_t)a.R * p.nsplit * a.H * D_latent;
-#define LISFA_SFA_CASE(DL_, DR_, F8_, G_)                                                     \
-    if (D_latent == DL_ && (fp8 != 0) == F8_ && p.nhg == G_)                                   \
-        return launch_sfa_t<DL_, DR_, F8_, G_>(a, p, out, out_f32, lse, part_o, part_lse, stream);
-    LISFA_SFA_CASE(512, 64, false, 2)
-    LISFA_SFA_CASE(512, 64, true, 2)
-    LISFA_SFA_CASE(512, 64, false, 1)
-    LISFA_SFA_CASE(512, 64, true, 1)
-    LISFA_SFA_CASE(64, 16, false, 1)
-    LISFA_SFA_CASE(64, 16, true, 1)
-    LISFA_SFA_CASE(64, 16, false, 2)
-    LISFA_SFA_CASE(64, 16, true, 2)
+#define LISFA_SFA_CASE(DL_, DR_, F8_, TS_, G_)                                                         \
+    if (D_latent == DL_ && kv_mode == (TS_ ? 2 : F8_ ? 1 : 0) && p.nhg == G_)                          \
+        return launch_sfa_t<DL_, DR_, F8_, G_, TS_>(a, p, out, out_f32, lse, part_o, part_lse, stream);
+    LISFA_SFA_CASE(512, 64, false, false, 2)
+    LISFA_SFA_CASE(512, 64, true, false, 2)
+    LISFA_SFA_CASE(512, 64, true, true, 2)
+    LISFA_SFA_CASE(512, 64, false, false, 1)
+    LISFA_SFA_CASE(512, 64, true, false, 1)
+    LISFA_SFA_CASE(512, 64, true, true, 1)
+    LISFA_SFA_CASE(64, 16, false, false, 1)
+    LISFA_SFA_CASE(64, 16, true, false, 1)
+    LISFA_SFA_CASE(64, 16, true, true, 1)
+    LISFA_SFA_CASE(64, 16, false, false, 2)
+    LISFA_SFA_CASE(64, 16, true, false, 2)
+    LISFA_SFA_CASE(64, 16, true, true, 2)
 #undef LISFA_SFA_CASE
     return hipErrorInvalidValue;
 }
@@ -1774,7 +1822,7 @@ static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 // it holds: range[r] = {lo, hi} are the logical positions of row r's
 // sequence in this shard (its cache addresses them as 0..hi-lo-1); NULL =
 // the list already holds local positions.  fp32 normalised output + lse.
-hipError_t sfa_partial_dispatch(const MlaDev& a, const int32_t* range, int D_latent, int fp8, float* out_f32,
+hipError_t sfa_partial_dispatch(const MlaDev& a, const int32_t* range, int D_latent, int kv_mode, float* out_f32,
                                 float* lse, void* ws, hipStream_t stream) {
     MlaDev d = a;
     uint8_t* w = (uint8_t*)ws;
@@ -1786,7 +1834,7 @@ hipError_t sfa_partial_dispatch(const MlaDev& a, const int32_t* range, int D_lat
         d.idx = li;
         w += align256((size_t)a.R * a.K * sizeof(int32_t));
     }
-    return sfa_dispatch(d, D_latent, fp8, nullptr, out_f32, lse, w, stream);
+    return sfa_dispatch(d, D_latent, kv_mode, nullptr, out_f32, lse, w, stream);
 }
 
 // LSE combine of G gathered partial results [G, R, H, D] -> [R, H, D] bf16.

@@ -114,6 +114,8 @@ def _mla_args(**kw):
     (dict(k_cache=_fake_cache(dtype=C.LISFA_MXFP8, row_stride_bytes=128, scale=16)), C.LISFA_ERR_NULL_ARG),
     (dict(k_cache=_fake_cache(dtype=C.LISFA_MXFP8, row_stride_bytes=32, scale=16), q_scale=16, D_I=32),
      C.LISFA_ERR_UNSUPPORTED),
+    (dict(k_cache=_fake_cache(dtype=C.LISFA_FP8_TILE128, row_stride_bytes=128, scale=16), q_scale=16),
+     C.LISFA_ERR_BAD_DTYPE),
 ])
 def test_li_score_validation(clib, kw, code):
     a = _idx_args(**kw)
@@ -149,6 +151,9 @@ def test_topk_validation(clib):
     (dict(kv_cache=_fake_cache(row_stride_bytes=1024)), C.LISFA_ERR_BAD_SHAPE),
     (dict(softmax_scale=float("nan")), C.LISFA_ERR_BAD_SHAPE),
     (dict(kv_cache=_fake_cache(dtype=C.LISFA_MXFP8, row_stride_bytes=1152, scale=16)), C.LISFA_ERR_BAD_DTYPE),
+    (dict(kv_cache=_fake_cache(dtype=C.LISFA_FP8_TILE128, row_stride_bytes=576)), C.LISFA_ERR_NULL_ARG),
+    (dict(kv_cache=_fake_cache(dtype=C.LISFA_FP8_TILE128, row_stride_bytes=576, scale=18)), C.LISFA_ERR_BAD_SHAPE),
+    (dict(kv_cache=_fake_cache(dtype=C.LISFA_FP8_TILE128, row_stride_bytes=560, scale=16)), C.LISFA_ERR_BAD_SHAPE),
 ])
 def test_sparse_mla_validation(clib, kw, code):
     m = _mla_args(**kw)

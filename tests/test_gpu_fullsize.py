@@ -28,7 +28,7 @@ def _run(wl, rows):
     idx, out, lse = _np(idx), _np(out), _np(lse)
     assert np.isfinite(out).all() and np.isfinite(lse).all()
     inp = W.to_numpy(b)
-    fp8 = wl.kv_dtype == "fp8"
+    fp8 = wl.kv_dtype in ("fp8", "fp8_tile128")
     for r in rows:
         r = r % b.R
         say(f"  oracle row {r} (position {int(inp['row_pos'][r])})")
@@ -64,3 +64,7 @@ def test_bench_workload_64x32768_full(lib):
 
 def test_bench_workload_mxfp8_full(lib):
     _run(W.BENCH["decode_paged_64x32768_mxfp8"], [0, 63])
+
+
+def test_bench_workload_fp8_tile_kv_full(lib):
+    _run(W.BENCH["decode_paged_64x32768_fp8tilekv"], [0, 33, 63])

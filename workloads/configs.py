@@ -101,7 +101,13 @@ M32K_B64_MX = Workload(
     paged=True, indexer_dtype="mxfp8")
 
 CONFIGS = [TINY, DECODE_8K, BATCHED_PAGED, PREFILL_64K, FP8_LONG]
-BENCH = {w.name: w for w in CONFIGS + [M32K_B64, M32K_B1, M32K_B64_MX]}
+# the same with the attention's latent cache in fp8 with one scale per
+# 128-element tile of each row
+M32K_B64_FP8KV = Workload(
+    name="decode_paged_64x32768_fp8tilekv", seed=8, mode="decode", num_seqs=64, seq_len=32768,
+    paged=True, kv_dtype="fp8_tile128")
+
+BENCH = {w.name: w for w in CONFIGS + [M32K_B64, M32K_B1, M32K_B64_MX, M32K_B64_FP8KV]}
 
 
 def get(name: str) -> Workload:
