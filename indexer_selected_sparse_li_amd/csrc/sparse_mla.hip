@@ -1308,7 +1308,7 @@ __global__ __launch_bounds__(512) void sfa_w8_kernel(MlaDev a, int kps, int nspl
 // Waves w and w + 4 share a SIMD, so QK^T + softmax of tile t+1 and PV of tile
 // t overlap; one barrier per tile hands P over.  The two roles run separate
 // loops with the same number of barriers, so their registers do not add up.
-template <int DLAT, int DROPE, int NBUF, int MAXK>
+template <int DLAT, int DROPE, int NBUF, int MAXK, int KVF = 0>
 __global__ __launch_bounds__(512) void sfa_ws_kernel(MlaDev a, int kps, int nsplit, int nhb,
                                                       __bf16* __restrict__ out, float* __restrict__ lse,
                                                       float* __restrict__ part_o, float* __restrict__ part_lse) {
@@ -1327,8 +1327,16 @@ __global__ __launch_bounds__(512) void sfa_ws_kernel(MlaDev a, int kps, int nspl
     static_assert(DVP % 64 == 0, "whole 1 KB blocks per p-wave");
     typedef float f32x4v __attribute__((ext_vector_type(4)));
 
+    // KVF (cached rows): 0 bf16; 1 e4m3 with one factor per row (group); 2 e4m3
+    // with one factor per 128-column tile.  fp8 rows are turned into bf16 rows
+    // of the same tile layout by the loading waves, so the QK and PV code is the
+    // same for every format.
+    constexpr int NTL = KVF == 2 ? (DQK + 127) / 128 : 1;     // factors per row
+    static_assert(KVF == 0 || (DQK % 128 == 0 || (DQK - DQK / 128 * 128) % 64 == 0),
+                  "fp8 rows: 1 KB blocks never straddle a factor tile");
     __shared__ __attribute__((aligned(1024))) uint8_t tile[NBUF * TB];
     __shared__ uint32_t rslot[MAXK];                   // cache slot of each selected row, ~0 = skip
+    __shared__ float kvf[KVF ? NTL * MAXK : 1];        // fp8 factors [tile][row] (0 for skipped rows)
     __shared__ uint32_t vmask[MAXK / 32];              // valid-row bits of each 32-row tile
     __shared__ __attribute__((aligned(16))) uint8_t pbuf[2][4][64 * 16];   // P^T operands [slot][head tile][lane]
     __shared__ float alph[2][64];                      // raise factors [slot][head]
@@ -1368,6 +1376,14 @@ __global__ __launch_bounds__(512) void sfa_ws_kernel(MlaDev a, int kps, int nspl
     for (int j = 0; j < EPT; ++j) {
         const int i = j * NT + tid;
         if (i < nt_fill * TROWS) rslot[i] = sv[j] >= 0 ? (uint32_t)sv[j] : 0xFFFFFFFFu;
+        if constexpr (KVF == 1) {
+            if (i < nt_fill * TROWS) kvf[i] = sv[j] >= 0 ? a.kv.scale[sv[j] / a.kv.scale_group] : 0.f;
+        } else if constexpr (KVF == 2) {
+            if (i < nt_fill * TROWS) {
+#pragma unroll
+                for (int q = 0; q < NTL; ++q) kvf[q * MAXK + i] = sv[j] >= 0 ? a.kv.scale[sv[j] * NTL + q] : 0.f;
+            }
+        }
         const uint64_t bal = __ballot(sv[j] >= 0);
         if (lane == 0 && i < nt_fill * TROWS) {
             vmask[i / 32] = (uint32_t)bal;
@@ -1535,9 +1551,54 @@ __global__ __launch_bounds__(512) void sfa_ws_kernel(MlaDev a, int kps, int nspl
             else if (after == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NJ) : "memory");
             else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         };
-        for (int j = 0; j <= LA; ++j)
-            if (j < ntiles) issue_tile(read_slot(j), j);
-        uint32_t sl = read_slot(LA + 1);
+        // fp8 rows: wave pc fills rows 8 pc .. 8 pc + 7 of each tile.  In 1 KB block
+        // j, lane l owns position l % 8 of row 8 pc + l / 8, i.e. bf16 chunk c = 8 j
+        // + ((l % 8) ^ swz8(row)) = columns 8 c .. 8 c + 7: it loads their 8 e4m3
+        // codes, multiplies by the row's factor of that column tile (block j lies in
+        // tile j / 2) and writes the 16 bytes, one contiguous 1 KB per instruction.
+        // Codes are fetched two tiles ahead into registers.
+        const int frow = 8 * pc + (lane >> 3);
+        const int fsw = (lane & 7) ^ sfa_swz8(frow);
+        auto fetch = [&](int t, u32x2 (&v)[NJ]) {
+            const uint32_t s = t < ntiles ? rslot[t * TROWS + frow] : 0xFFFFFFFFu;
+            const uint8_t* gp = s != 0xFFFFFFFFu ? a.kv.data + (uint64_t)s * (uint32_t)a.kv.row_stride : g_zero_row;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) v[j] = __builtin_nontemporal_load((const u32x2*)(gp + (8 * j + fsw) * 8));
+        };
+        auto put = [&](int t, const u32x2 (&v)[NJ], int buf) {
+            lds_u8* dst = (lds_u8*)tile + buf * TB + pc * GB + lane * 16;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const float f = KVF == 1 ? kvf[t * TROWS + frow] : kvf[(j / 2) * MAXK + t * TROWS + frow];
+                const f32x2 x0 = fp8x2_to_f32<false>(v[j].x), x1 = fp8x2_to_f32<true>(v[j].x);
+                const f32x2 x2 = fp8x2_to_f32<false>(v[j].y), x3 = fp8x2_to_f32<true>(v[j].y);
+                bf16x8 b;
+                b[0] = (__bf16)(x0.x * f);
+                b[1] = (__bf16)(x0.y * f);
+                b[2] = (__bf16)(x1.x * f);
+                b[3] = (__bf16)(x1.y * f);
+                b[4] = (__bf16)(x2.x * f);
+                b[5] = (__bf16)(x2.y * f);
+                b[6] = (__bf16)(x3.x * f);
+                b[7] = (__bf16)(x3.y * f);
+                *(__attribute__((address_space(3))) bf16x8*)(dst + j * 1024) = b;
+            }
+        };
+        static_assert(KVF == 0 || NBUF == 3, "fp8 rows: PV(t) | QK(t+1) | tile t+2 being written");
+        u32x2 fv[KVF ? 2 : 1][NJ];
+        uint32_t sl = 0;
+        if constexpr (KVF == 0) {
+            for (int j = 0; j <= LA; ++j)
+                if (j < ntiles) issue_tile(read_slot(j), j);
+            sl = read_slot(LA + 1);
+        } else {
+            fetch(0, fv[0]);
+            fetch(1, fv[1]);
+            put(0, fv[0], 0);
+            put(1, fv[1], 1);
+            fetch(2, fv[0]);
+            fetch(3, fv[1]);
+        }
         // PV operand of M-tile mt: transpose reads of rows 4 g + l16 / 4 (keys of
         // K-slots 0..3) and 16 + 4 g + l16 / 4 (K-slots 4..7), 4 value columns each
         uint32_t pva[4];
@@ -1559,16 +1620,20 @@ __global__ __launch_bounds__(512) void sfa_ws_kernel(MlaDev a, int kps, int nspl
 #pragma unroll
             for (int mt = 0; mt < MTP; ++mt) o[ht][mt] = f32x4v{0.f, 0.f, 0.f, 0.f};
 
-        wait_tile(0, LA);
+        if constexpr (KVF == 0) wait_tile(0, LA);
         __syncthreads();                                   // barrier P: tile 0 landed
         int bc = 0;                                        // buffer of tile t
         for (int t = 0; t < ntiles; ++t) {
-            wait_tile(t + 1, t + LA);
+            if constexpr (KVF == 0) wait_tile(t + 1, t + LA);
             __syncthreads();                               // barrier t: tile t+1 landed
-            {
+            if constexpr (KVF == 0) {
                 const int bn = bc + LA + 1 >= NBUF ? bc + LA + 1 - NBUF : bc + LA + 1;   // = buffer of tile t-1
                 if (t + 1 + LA < ntiles) issue_tile(sl, bn);
                 sl = read_slot(t + 2 + LA);
+            } else {
+                // tile t+2 into the buffer tile t-1 has released; codes of tile t+4 out
+                if (t + 2 < ntiles) put(t + 2, fv[t & 1], bc == 0 ? 2 : bc - 1);
+                if (t + 4 < ntiles) fetch(t + 4, fv[t & 1]);
             }
             const int ps = t & 1;
             const lds_u8* T = tile0 + bc * TB;
@@ -1766,6 +1831,10 @@ static hipError_t launch_sfa_t(const MlaDev& a, const SfaPlan& p, __bf16* out, f
     else if (!FP8 && DLAT == 512 && DROPE == 64 && NHG == 2 && kSfaWarpSpecialised)
         hipLaunchKernelGGL((sfa_ws_kernel<512, 64, 3, kSfaMaxKeys>), dim3((unsigned)nwg), dim3(512), 0, stream, a,
                            p.kps, p.nsplit, p.nhb, out, lse, part_o, part_lse);
+    else if (FP8 && DLAT == 512 && DROPE == 64 && NHG == 2 && kSfaWarpSpecialised && p.kps <= 1024)
+        // fp8 rows turned into bf16 tiles by the loading waves (factor per row or per 128-column tile)
+        hipLaunchKernelGGL((sfa_ws_kernel<512, 64, 3, 1024, TSC ? 2 : 1>), dim3((unsigned)nwg), dim3(512), 0, stream,
+                           a, p.kps, p.nsplit, p.nhb, out, lse, part_o, part_lse);
     else if constexpr (!FP8 && ((DLAT + DROPE) * 2) % 128 == 0 && NHG == 2)
         hipLaunchKernelGGL((sfa_w8_kernel<DLAT, DROPE>), dim3((unsigned)nwg), dim3(512), 0, stream, a, p.kps,
                            p.nsplit, p.nhb, out, lse, part_o, part_lse);
