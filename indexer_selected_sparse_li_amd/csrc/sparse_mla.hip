@@ -1567,9 +1567,12 @@ __global__ __launch_bounds__(512) void sfa_ws_kernel(MlaDev a, int kps, int nspl
         };
         auto put = [&](int t, const u32x2 (&v)[NJ], int buf) {
             lds_u8* dst = (lds_u8*)tile + buf * TB + pc * GB + lane * 16;
+            float fr[NTL];                                 // the row's factors, read once
+#pragma unroll
+            for (int q = 0; q < NTL; ++q) fr[q] = kvf[q * MAXK + t * TROWS + frow];
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-                const float f = KVF == 1 ? kvf[t * TROWS + frow] : kvf[(j / 2) * MAXK + t * TROWS + frow];
+                const float f = fr[KVF == 1 ? 0 : j / 2];
                 const f32x2 x0 = fp8x2_to_f32<false>(v[j].x), x1 = fp8x2_to_f32<true>(v[j].x);
                 const f32x2 x2 = fp8x2_to_f32<false>(v[j].y), x3 = fp8x2_to_f32<true>(v[j].y);
                 bf16x8 b;
