@@ -42,8 +42,8 @@ def algorithmic(wl, b):
     seq = [int(s) for s in b.row_seq.tolist()]
     ke = 1 if wl.indexer_dtype in ("fp8", "mxfp8") else 2
     ks = {"fp8": 4, "mxfp8": wl.D_I // 32}.get(wl.indexer_dtype, 0)   # scale bytes per key (or query head)
-    ve = 1 if wl.kv_dtype == "fp8" else 2
-    vs = 4 if wl.kv_dtype == "fp8" else 0
+    ve = 1 if wl.kv_dtype in ("fp8", "fp8_tile128") else 2
+    vs = {"fp8": 4, "fp8_tile128": 4 * ((wl.D_qk + 127) // 128)}.get(wl.kv_dtype, 0)   # scale bytes per row
     vis = sum(p + 1 for p in pos)
     sel = sum(min(wl.K, p + 1) for p in pos)
     seq_vis, seq_sel = {}, {}
@@ -792,7 +792,7 @@ def report_prolog(args):
 
 REPORT_ORDER = ["tiny_l256", "decode_l8192", "batched_paged_64x4k_32k", "prefill_4096q_l65536",
                 "fp8_decode_16x131072", "decode_paged_1x32768", "decode_paged_64x32768",
-                "decode_paged_64x32768_mxfp8"]
+                "decode_paged_64x32768_mxfp8", "decode_paged_64x32768_fp8tilekv"]
 
 
 def write_report_md(path, lines, args):
