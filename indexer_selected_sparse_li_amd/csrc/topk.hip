@@ -391,6 +391,36 @@ __device__ __forceinline__ void tk_threshold(TkShared& sh, const uint32_t (&kr)[
                 ncand = inbin;
             }
             __syncthreads();
+            if (compact && ncand <= 64u) {
+                // at most 64 candidates left: one wavefront sorts them (bitonic,
+                // descending, in registers) instead of further block-wide levels.
+                // The need-th largest d is the threshold; the candidates strictly
+                // above it are taken whole.
+                if (wave == 0) {
+                    const uint32_t d = (uint32_t)lane < ncand ? sh.cand[lane] : 0u;
+                    const bool ok = (uint32_t)lane < ncand && ((d ^ prefix) >> lo) == 0u;
+                    uint64_t x = ok ? ((1ull << 32) | d) : 0ull;
+#pragma unroll
+                    for (int k = 2; k <= 64; k <<= 1)
+#pragma unroll
+                        for (int j = k >> 1; j > 0; j >>= 1) {
+                            const uint64_t y = ((uint64_t)(uint32_t)__shfl_xor((int)(x >> 32), j) << 32) |
+                                               (uint32_t)__shfl_xor((int)(uint32_t)x, j);
+                            const bool keep_max = ((lane & j) == 0) == ((lane & k) == 0);
+                            x = keep_max ? (x > y ? x : y) : (x < y ? x : y);
+                        }
+                    const uint32_t v = (uint32_t)__shfl((int)(uint32_t)x, (int)need - 1);
+                    const uint64_t gt = __ballot(ok && d > v);
+                    if (lane == 0) {
+                        sh.digit = v;
+                        sh.above = (uint32_t)__popcll(gt);
+                    }
+                }
+                __syncthreads();
+                prefix = sh.digit;   // the full d of the threshold
+                need -= sh.above;
+                break;
+            }
             hi = lo - 1;
         }
         T = kmin + prefix;
