@@ -1634,9 +1634,17 @@ __global__ __launch_bounds__(512) void sfa_ws_kernel(MlaDev a, int kps, int nspl
                 if (t + 1 + LA < ntiles) issue_tile(sl, bn);
                 sl = read_slot(t + 2 + LA);
             } else {
-                // tile t+2 into the buffer tile t-1 has released; codes of tile t+4 out
-                if (t + 2 < ntiles) put(t + 2, fv[t & 1], bc == 0 ? 2 : bc - 1);
-                if (t + 4 < ntiles) fetch(t + 4, fv[t & 1]);
+                // tile t+2 into the buffer tile t-1 has released; codes of tile t+4 out.
+                // Constant register-set indices in each branch keep fv in registers (an
+                // index of t & 1 would put the array in scratch memory).
+                const int bw = bc == 0 ? 2 : bc - 1;
+                if (t & 1) {
+                    if (t + 2 < ntiles) put(t + 2, fv[1], bw);
+                    if (t + 4 < ntiles) fetch(t + 4, fv[1]);
+                } else {
+                    if (t + 2 < ntiles) put(t + 2, fv[0], bw);
+                    if (t + 4 < ntiles) fetch(t + 4, fv[0]);
+                }
             }
             const int ps = t & 1;
             const lds_u8* T = tile0 + bc * TB;
@@ -1720,12 +1728,31 @@ __global__ __launch_bounds__(256) void sfa_combine_kernel(const float* __restric
     const int r = rh / H, h = rh % H;
     const int c = (threadIdx.x % TPH) * 8;
     float M = -__builtin_inff();
-    for (int i = 0; i < nsplit; ++i) M = fmaxf(M, part_lse[((int64_t)r * row_str + i * split_str) * H + h]);
     float acc[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] = 0.f;
     float W = 0.f;
-    if (M != -__builtin_inff()) {
+    if (nsplit == 2) {
+        // both parts' loads in one round trip; the same arithmetic in the same order
+        // as the general loop below
+        const int64_t e0 = (int64_t)r * row_str * H + h, e1 = ((int64_t)r * row_str + split_str) * H + h;
+        const float l0 = part_lse[e0], l1 = part_lse[e1];
+        const f32x4* p0 = (const f32x4*)(part_o + e0 * DLAT + c);
+        const f32x4* p1 = (const f32x4*)(part_o + e1 * DLAT + c);
+        const f32x4 a0 = p0[0], a1 = p0[1], b0 = p1[0], b1 = p1[1];
+        M = fmaxf(fmaxf(M, l0), l1);
+        if (M != -__builtin_inff()) {
+            const float w0 = __expf(l0 - M), w1 = __expf(l1 - M);
+            W = w0 + w1;
+            const float x0[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+            const float x1[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[j] = fmaf(w1, x1[j], fmaf(w0, x0[j], 0.f));
+        }
+    } else {
+        for (int i = 0; i < nsplit; ++i) M = fmaxf(M, part_lse[((int64_t)r * row_str + i * split_str) * H + h]);
+    }
+    if (nsplit != 2 && M != -__builtin_inff()) {
         for (int i = 0; i < nsplit; ++i) {
             const int64_t e = ((int64_t)r * row_str + i * split_str) * H + h;
             const float wi = __expf(part_lse[e] - M);
