@@ -280,6 +280,8 @@ def main():
     ap.add_argument("--workload", default="decode_paged_64x32768")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-each", type=float, default=4.0,
+                    help="with --report-all: seconds of oracle time per workload")
     ap.add_argument("--stage-steps", type=int, default=None)
     ap.add_argument("--only", choices=["li_score", "topk_select", "sparse_mla_attn", "layer"],
                     help="profiling mode: run just this stage (no JSON line)")
@@ -559,6 +561,11 @@ def report_all(args):
     for name in REPORT_ORDER:
         wl = W.get(name)
         res, b = run_workload(args, wl, cold=True, graph=True)
+        if not args.no_cpu_baseline:
+            # the oracle on the same batch, in the same run (bounded sample)
+            log(f"[bench] cpu oracle baseline for {wl.name}")
+            res["cpu_baseline"] = cpu_baseline(b, args.cpu_budget_each)
+            res["vs_cpu_oracle"] = res["value"] / res["cpu_baseline"]["value"]
         del b
         torch.cuda.empty_cache()
         lines.append(res)
@@ -812,14 +819,22 @@ def write_report_md(path, lines, args):
         fh.write(f"    python3 bench.py --report-all --steps {args.steps} --warmup {args.warmup} "
                  f"--report-md {os.path.relpath(path, ROOT)}\n\n")
         fh.write("| workload | rows | layer cold us | tokens/s cold | layer hot us | tokens/s hot | "
-                 "graph replay us | tokens/s graph | li_score us | topk_select us | sparse_mla_attn us |\n")
-        fh.write("|---|---|---|---|---|---|---|---|---|---|---|\n")
+                 "graph replay us | tokens/s graph | li_score us | topk_select us | sparse_mla_attn us | "
+                 "oracle tokens/s (threads) |\n")
+        fh.write("|---|---|---|---|---|---|---|---|---|---|---|---|\n")
         for r in lines:
+            cb = r.get("cpu_baseline")
+            orc = f'{cb["value"]:.3g} ({cb["cores"]})' if cb else "not run"
             fh.write(f'| {r["config"]["workload"]} | {r["config"]["rows"]} | '
                      f'{r["ms_per_step_cold"] * 1e3:.1f} | {r["value_cold"]:.0f} | '
                      f'{r["ms_per_step"] * 1e3:.1f} | {r["value"]:.0f} | '
                      f'{r["ms_per_step_graph"] * 1e3:.1f} | {r["value_graph"]:.0f} | '
-                     f'{st(r, "li_score")} | {st(r, "topk_select")} | {st(r, "sparse_mla_attn")} |\n')
+                     f'{st(r, "li_score")} | {st(r, "topk_select")} | {st(r, "sparse_mla_attn")} | {orc} |\n')
+        if any(r.get("cpu_baseline") for r in lines):
+            fh.write("\nOracle: the CPU oracle (float64 NumPy, scores over the full visible context, selection, "
+                     "attention) on the first rows of the same batch in the same run, about "
+                     f"{args.cpu_budget_each:g} s per workload (at least one row); threads = the BLAS pool's size. "
+                     "A baseline, not the target.\n")
     log(f"[bench] wrote {path}")
 
 
