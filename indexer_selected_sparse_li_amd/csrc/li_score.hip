@@ -461,7 +461,12 @@ __device__ __forceinline__ i32x8 mx_operand(const uint8_t* row, int g) {
     return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
-template <int MT>
+// TOK: e4m3 queries and keys with per-token fp32 scales instead (config-4
+// style): the same instruction with unit E8M0 scales (127 = 2^0) gives the
+// exact e4m3 dot products, the query scale is folded into the head weights
+// and the key's scale is the score factor, in the order of the LDS-ring fp8
+// kernel (w * s_q, then the weighted ReLU sum, then * s_k).
+template <int MT, bool TOK = false>
 __global__ __launch_bounds__(64 * kLiDecWaves) void li_score_mx_kernel(IndexerDev a, float* __restrict__ scores,
                                                                     int64_t ld, int keys_per_wg) {
     constexpr int DI = 128;
@@ -524,7 +529,7 @@ __global__ __launch_bounds__(64 * kLiDecWaves) void li_score_mx_kernel(IndexerDe
         if (head < a.H_I) {
             const int64_t hr = (int64_t)r * a.H_I + head;
             qa[mt] = mx_operand(a.q + hr * DI, g);
-            qs[mt] = a.q_mx_scale[hr * NB + g];
+            qs[mt] = TOK ? 127 : a.q_mx_scale[hr * NB + g];
         } else {
             qa[mt] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
             qs[mt] = 127;
@@ -532,7 +537,12 @@ __global__ __launch_bounds__(64 * kLiDecWaves) void li_score_mx_kernel(IndexerDe
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int h = mt * 16 + 4 * g + i;
-            wv[mt][i] = h < a.H_I ? a.w[(int64_t)r * a.H_I + h] : 0.f;
+            float wvv = 0.f;
+            if (h < a.H_I) {
+                wvv = a.w[(int64_t)r * a.H_I + h];
+                if constexpr (TOK) wvv *= a.q_scale_per_head ? a.q_scale[(int64_t)r * a.H_I + h] : a.q_scale[r];
+            }
+            wv[mt][i] = wvv;
         }
     }
     __syncthreads();  // block map ready
@@ -553,9 +563,11 @@ __global__ __launch_bounds__(64 * kLiDecWaves) void li_score_mx_kernel(IndexerDe
         const int64_t base = c0 + (int64_t)(wave + i * kLiDecWaves) * 64;
         const int64_t slot = i < mine ? slot_of_key(base + 16 * s4 + (lane & 15)) : -1;
         kb = mx_operand(slot >= 0 ? a.k.data + slot * a.k.row_stride : g_li_zero_row, g);
-        fac = slot >= 0 ? 1.f : __builtin_nanf("");
+        if constexpr (TOK) fac = slot >= 0 ? a.k.scale[slot / a.k.scale_group] : __builtin_nanf("");
+        else fac = slot >= 0 ? 1.f : __builtin_nanf("");
     };
     auto fetch_scales = [&](int i) -> uint32_t {
+        if constexpr (TOK) return 0x7F7F7F7Fu;
         const int64_t base = c0 + (int64_t)(wave + i * kLiDecWaves) * 64;
         const int64_t ks = i < mine ? slot_of_key(base + lane) : -1;
         return ks >= 0 ? __builtin_nontemporal_load((const uint32_t*)(a.k.mx_scale + ks * NB)) : 0x7F7F7F7Fu;
@@ -660,7 +672,7 @@ static hipError_t launch_li_dec(const IndexerDev& a, float* scores, int64_t ld, 
     return hipGetLastError();
 }
 
-template <int MT>
+template <int MT, bool TOK>
 static hipError_t launch_li_mx(const IndexerDev& a, float* scores, int64_t ld, int64_t max_visible,
                                hipStream_t stream) {
     const int sh = a.k.paged ? a.k.bs_shift : 6;
@@ -677,7 +689,8 @@ static hipError_t launch_li_mx(const IndexerDev& a, float* scores, int64_t ld, i
     nchunk = (max_visible + kpw - 1) / kpw;
     if (nchunk < 1) nchunk = 1;
     dim3 grid((unsigned)nchunk, (unsigned)a.R);
-    hipLaunchKernelGGL((li_score_mx_kernel<MT>), grid, dim3(64 * kLiDecWaves), 0, stream, a, scores, ld, (int)kpw);
+    hipLaunchKernelGGL((li_score_mx_kernel<MT, TOK>), grid, dim3(64 * kLiDecWaves), 0, stream, a, scores, ld,
+                       (int)kpw);
     return hipGetLastError();
 }
 
@@ -686,11 +699,16 @@ hipError_t li_score_dispatch(const IndexerDev& a, int D_I, int dtype, int qg, fl
     const int mt = a.H_I <= 16 ? 1 : (a.H_I <= 32 ? 2 : 4);
     if (dtype == LISFA_MXFP8) {   // one row at a time whatever the grouping
         if (D_I != 128) return hipErrorInvalidValue;
-        if (mt == 4) return launch_li_mx<4>(a, scores, ld, max_visible, stream);
-        if (mt == 2) return launch_li_mx<2>(a, scores, ld, max_visible, stream);
-        return launch_li_mx<1>(a, scores, ld, max_visible, stream);
+        if (mt == 4) return launch_li_mx<4, false>(a, scores, ld, max_visible, stream);
+        if (mt == 2) return launch_li_mx<2, false>(a, scores, ld, max_visible, stream);
+        return launch_li_mx<1, false>(a, scores, ld, max_visible, stream);
     }
     const int fp8 = dtype == LISFA_FP8_E4M3;
+    if (qg == 1 && fp8 != 0 && D_I == 128) {   // one row at a time: stream the keys
+        if (mt == 4) return launch_li_mx<4, true>(a, scores, ld, max_visible, stream);
+        if (mt == 2) return launch_li_mx<2, true>(a, scores, ld, max_visible, stream);
+        return launch_li_mx<1, true>(a, scores, ld, max_visible, stream);
+    }
     if (qg == 1 && fp8 == 0) {
         if (D_I == 128 && mt == 4) return launch_li_dec<128, 4>(a, scores, ld, max_visible, stream);
         if (D_I == 128 && mt == 2) return launch_li_dec<128, 2>(a, scores, ld, max_visible, stream);

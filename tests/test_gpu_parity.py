@@ -8,9 +8,10 @@ import numpy as np
 import pytest
 import torch
 
+import indexer_selected_sparse_li_amd as lisfa
 import oracle as O
 import workloads as W
-from gpu_util import (batch_on_gpu, check_index_set, check_lse, check_out, gpu_fused, gpu_scores,
+from gpu_util import (batch_on_gpu, caches, check_index_set, check_lse, check_out, gpu_fused, gpu_scores,
                       gpu_sfa, gpu_topk, say, score_bound)
 
 pytestmark = pytest.mark.gpu
@@ -157,6 +158,30 @@ def test_fp8_integer_bit_exact(lib):
         assert np.array_equal(sc[r, :n].astype(np.float64), o["scores"])
         assert np.array_equal(idx[r], o["idx"])
         check_out(out[r], o["out"], True, "fp8 int")
+
+
+def test_fp8_per_head_query_scales(lib):
+    """Per-(row, head) query scales: multiplying head h's scale by 2^e_h must give
+    the same fp32 scores, bit for bit, as multiplying its weight by 2^e_h instead
+    (both are exact power-of-two rescalings of the same products)."""
+    wl = W.CONFIGS[4].with_(num_seqs=2, seq_len=3000, name="fp8_head_scales")
+    say(f"[case] fp8 per-head query scales {wl.name}")
+    b = batch_on_gpu(wl)
+    assert b.q_scale is not None and b.q_scale.dim() == 1
+    kc, _ = caches(b)
+    e = torch.tensor([2.0 ** ((h % 3) - 1) for h in range(wl.H_I)], dtype=torch.float32, device="cuda")
+    ld = (b.max_visible + 63) // 64 * 64
+    by_w = torch.full((b.R, ld), float("nan"), dtype=torch.float32, device="cuda")
+    by_s = torch.full((b.R, ld), float("nan"), dtype=torch.float32, device="cuda")
+    lisfa.li_score(b.q_idx, (b.w * e[None, :]).contiguous(), kc, b.row_seq, b.row_pos, by_w, b.max_visible,
+                   q_scale=b.q_scale)
+    lisfa.li_score(b.q_idx, b.w, kc, b.row_seq, b.row_pos, by_s, b.max_visible,
+                   q_scale=(b.q_scale[:, None] * e[None, :]).contiguous())
+    torch.cuda.synchronize()
+    for r in range(b.R):
+        n = int(b.row_pos[r]) + 1
+        assert torch.equal(by_w[r, :n], by_s[r, :n]), f"row {r}"
+        assert torch.isfinite(by_s[r, :n]).all()
 
 
 # ----------------------------------------------------------------- edges ---
