@@ -26,6 +26,8 @@
 
 namespace lisfa {
 
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kTkThreads = 1024;
 constexpr int kTkWaves = kTkThreads / kWave;
 constexpr int kTkSegChunks = kTkThreads / kTkWaves;  // chunks per emission segment (64)
@@ -646,13 +648,30 @@ __global__ __launch_bounds__(kTkThreads) void topk_merge_kernel(const float* __r
     uint32_t kr[EPT];
     int32_t pr[EPT];
     uint64_t vm = 0ull;
+    // 16-byte loads when this thread's candidates are whole and aligned
+    const bool vec = EPT % 4 == 0 && (ldc & 3) == 0 && base + EPT <= n &&
+                     ((((uintptr_t)cand_score) | ((uintptr_t)cand_pos)) & 15) == 0;
+    if (vec) {
 #pragma unroll
-    for (int c = 0; c < EPT; ++c) {
-        const int i = base + c;
-        const int32_t p = i < n ? cp[i] : -1;
-        pr[c] = p;
-        kr[c] = float_key(p >= 0 ? cs[i] : 0.0f);
-        vm |= (uint64_t)(p >= 0) << c;
+        for (int c = 0; c < EPT; c += 4) {
+            const i32x4 p4 = *(const i32x4*)(cp + base + c);
+            const f32x4 s4 = *(const f32x4*)(cs + base + c);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                pr[c + e] = p4[e];
+                kr[c + e] = float_key(p4[e] >= 0 ? s4[e] : 0.0f);
+                vm |= (uint64_t)(p4[e] >= 0) << (c + e);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < EPT; ++c) {
+            const int i = base + c;
+            const int32_t p = i < n ? cp[i] : -1;
+            pr[c] = p;
+            kr[c] = float_key(p >= 0 ? cs[i] : 0.0f);
+            vm |= (uint64_t)(p >= 0) << c;
+        }
     }
     uint32_t nvalid;
     uint32_t first = block_excl_scan((uint32_t)__popcll(vm), sh.tk.wsum, nvalid);
