@@ -47,7 +47,7 @@ struct LiCfg {
     static constexpr int ELT = FP8 ? 1 : 2;
     static constexpr int RB = DI * ELT;                    // bytes of one key row
     static constexpr int CPK = RB / 16;                    // 16-byte chunks per row
-    static constexpr int TK0 = QG == 1 ? 128 : 64;
+    static constexpr int TK0 = 128;
     static constexpr int TK = (TK0 * CPK >= 512) ? TK0 : 512 / CPK;  // >= one chunk per thread
     static constexpr int LPT = TK * CPK / 512;             // chunk loads per thread per tile
     static constexpr int TILE = TK * RB;                   // bytes per tile
@@ -169,7 +169,11 @@ __global__ __launch_bounds__(512) void li_score_kernel(IndexerDev a, float* __re
     // tile (the extra one: 64 key factors), so vmcnt counts are uniform.
     const uint32_t ring0 = (uint32_t)(uintptr_t)(&ring[0][0]);
     const uint32_t kmul0 = (uint32_t)(uintptr_t)(&kmul[0][0]);
+    // Every source address of a tile is computed (block-map reads from LDS)
+    // before the first load goes out: the loads are opaque to the compiler,
+    // which would otherwise wait for each lookup separately.
     auto issue_tile = [&](int64_t t0, int buf) {
+        const uint8_t* src[LPT];
 #pragma unroll
         for (int j = 0; j < LPT; ++j) {
             const int P = j * 512 + tid;
@@ -179,26 +183,30 @@ __global__ __launch_bounds__(512) void li_score_kernel(IndexerDev a, float* __re
             const bool inr = kp < kend;
             const int bi = inr ? (int)((kp >> sh) - b0) : 0;   // tiles may run past kend
             const int off = (int)(kp & (bsz - 1));
-            const uint8_t* g = g_li_zero16;
-            if (inr && off < blk_lim[bi])
-                g = a.k.data + (blk_slot0[bi] + off) * a.k.row_stride + part * 16;
-            lds_dma<16, 0>(g, ring0 + (uint32_t)(buf * TILE + (j * 512 + (tid & ~63)) * 16));
+            const int lim = blk_lim[bi];                       // entry 0 always exists: read unconditionally
+            const int64_t s0 = blk_slot0[bi];
+            src[j] = (inr && off < lim) ? a.k.data + (s0 + off) * a.k.row_stride + part * 16 : g_li_zero16;
         }
+        const float* fsrc = &g_li_nan;   // waves whose keys lie past the tile load a dummy
         {
-            const int key = tid;  // waves whose keys lie past the tile load a dummy
-            const float* g = &g_li_nan;
+            const int key = tid;
             if (key < TK) {
                 const int64_t kp = t0 + key;
                 const bool inr = kp < kend;
                 const int bi = inr ? (int)((kp >> sh) - b0) : 0;
                 const int off = (int)(kp & (bsz - 1));
-                if (inr && off < blk_lim[bi]) {
-                    if constexpr (FP8) g = a.k.scale + (blk_slot0[bi] + off) / a.k.scale_group;
-                    else g = &g_li_one;
+                const int lim = blk_lim[bi];
+                const int64_t s0 = blk_slot0[bi];
+                if (inr && off < lim) {
+                    if constexpr (FP8) fsrc = a.k.scale + (s0 + off) / a.k.scale_group;
+                    else fsrc = &g_li_one;
                 }
             }
-            lds_dma<4, 0>(g, kmul0 + (uint32_t)((buf * 512 + (tid & ~63)) * 4));
         }
+#pragma unroll
+        for (int j = 0; j < LPT; ++j)
+            lds_dma<16, 0>(src[j], ring0 + (uint32_t)(buf * TILE + (j * 512 + (tid & ~63)) * 16));
+        lds_dma<4, 0>(fsrc, kmul0 + (uint32_t)((buf * 512 + (tid & ~63)) * 4));
     };
 
     // per-lane LDS byte offset of the B operand of subtile sub, K-step ks
@@ -229,13 +237,17 @@ __global__ __launch_bounds__(512) void li_score_kernel(IndexerDev a, float* __re
 
         const int64_t t0 = c0 + (int64_t)t * TK;
         const lds_u8* T = (const lds_u8*)&ring[buf][0];
-        // subtiles of this wave: decode splits the tile over the 8 waves
+        // subtiles of this wave: decode splits the tile over the 8 waves.  The
+        // products and head sums of all of them come first, in one branch-free
+        // block the compiler can software-pipeline (operand reads of subtile
+        // u + 1 under the products of u); the stores follow.
         constexpr int SUBW = QG == 1 ? NSUB / 8 : NSUB;
+        const int64_t tfirst = t0 + (QG == 1 ? wave * 16 : 0);
+        if ((row_ok || row_bad) && tfirst < vis) {       // wave-uniform
+            float sc[SUBW];
 #pragma unroll
-        for (int u = 0; u < SUBW; ++u) {
-            const int sub = QG == 1 ? (u * 8 + wave) : u;
-            const int64_t kb = t0 + sub * 16;
-            if (row_ok && kb < vis) {
+            for (int u = 0; u < SUBW; ++u) {
+                const int sub = QG == 1 ? (u * 8 + wave) : u;
                 f32x4 acc[MT];
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -256,14 +268,26 @@ __global__ __launch_bounds__(512) void li_score_kernel(IndexerDev a, float* __re
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) part = fmaf(wv[mt][i], fmaxf(acc[mt][i], 0.f), part);
-                part += __shfl_xor(part, 16);
-                part += __shfl_xor(part, 32);
-                const int64_t key = kb + (lane & 15);
-                if (lane < 16 && key < vis) scores[(int64_t)r * ld + key] = part * kmul[buf][sub * 16 + lane];
-            } else if (row_bad && kb < vis) {
-                const int64_t key = kb + (lane & 15);
-                if (lane < 16 && key < vis) scores[(int64_t)r * ld + key] = __builtin_nanf("");
+                    for (int i = 0; i < 4; ++i) {
+                        // ReLU as an integer max on the bit pattern (negative
+                        // floats, -0.0 included, are negative integers)
+                        const int bits = __float_as_int(acc[mt][i]);
+                        part = fmaf(wv[mt][i], __int_as_float(bits > 0 ? bits : 0), part);
+                    }
+                {   // sum over the four 16-lane groups (lanes l ^ 16, l ^ 32) without LDS
+                    const auto w16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+                    part = __uint_as_float(w16[0]) + __uint_as_float(w16[1]);
+                    const auto w32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+                    part = __uint_as_float(w32[0]) + __uint_as_float(w32[1]);
+                }
+                sc[u] = part;
+            }
+#pragma unroll
+            for (int u = 0; u < SUBW; ++u) {
+                const int sub = QG == 1 ? (u * 8 + wave) : u;
+                const int64_t key = t0 + sub * 16 + (lane & 15);
+                if (lane < 16 && key < vis)
+                    scores[(int64_t)r * ld + key] = row_ok ? sc[u] * kmul[buf][sub * 16 + lane] : __builtin_nanf("");
             }
         }
     }
