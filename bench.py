@@ -363,7 +363,7 @@ def run_workload(args, wl, cold=False, graph=False):
                        block_size=wl.block_size, seq_base=b.seq_base)
     vc = lisfa.KVCache(data=b.kv_data, scale=b.kv_scale, scale_group=wl.kv_scale_group,
                        block_table=b.block_table, block_size=wl.block_size, seq_base=b.seq_base)
-    rpg = 8 if (wl.mode == "prefill" and R % 8 == 0) else 1
+    rpg = (16 if R % 16 == 0 else 8 if R % 8 == 0 else 1) if wl.mode == "prefill" else 1
     out = torch.empty(R, wl.H, wl.D_v, dtype=torch.bfloat16, device="cuda")
     lse = torch.empty(R, wl.H, dtype=torch.float32, device="cuda")
     idx = torch.empty(R, wl.K, dtype=torch.int32, device="cuda")

@@ -241,7 +241,7 @@ int li_score(const lisfa_indexer_args* args, float* scores, int64_t ld_scores, l
     if (!scores) return LISFA_ERR_NULL_ARG;
     if (ld_scores < args->max_visible) return LISFA_ERR_BAD_SHAPE;
     const IndexerDev d = to_dev(args);
-    const int qg = (args->rows_per_group % 8 == 0) ? 8 : 1;
+    const int qg = (args->rows_per_group % 16 == 0) ? 16 : (args->rows_per_group % 8 == 0) ? 8 : 1;
     return hip_status(li_score_dispatch(d, args->D_I, args->k_cache.dtype, qg, scores, ld_scores,
                                         args->max_visible, (hipStream_t)stream));
 }
@@ -369,7 +369,7 @@ int li_topk_sfa(const lisfa_indexer_args* iargs, const lisfa_mla_args* margs, in
 
     const int64_t ld = scores_ld(iargs->max_visible) > 0 ? scores_ld(iargs->max_visible) : 64;
     const int64_t rc = fused_chunk_rows(R, iargs->max_visible);
-    const int qg = (iargs->rows_per_group % 8 == 0) ? 8 : 1;
+    const int qg = (iargs->rows_per_group % 16 == 0) ? 16 : (iargs->rows_per_group % 8 == 0) ? 8 : 1;
     const int elt = iargs->k_cache.dtype == LISFA_BF16 ? 2 : 1;
     const bool mx = iargs->k_cache.dtype == LISFA_MXFP8;
     IndexerDev d = to_dev(iargs);

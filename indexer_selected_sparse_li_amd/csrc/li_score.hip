@@ -29,6 +29,7 @@ namespace lisfa {
 
 constexpr int kLiMaxBlocks = 512;  // block-table entries one workgroup may touch
 constexpr int kLiNbuf = 4;         // tiles in the LDS ring
+constexpr int64_t kLiL2Bytes = 4 << 20;   // L2 of one XCD
 
 __device__ __attribute__((aligned(16))) uint8_t g_li_zero16[16];
 __device__ __attribute__((aligned(16))) uint8_t g_li_zero_row[256];   // stands in for unaddressable key rows
@@ -71,9 +72,12 @@ __global__ __launch_bounds__(512) void li_score_kernel(IndexerDev a, float* __re
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int qi = wave % QG;
+    // rows of this wave: QG <= 8: row wave % QG of the group; QG = 16: rows
+    // wave and wave + 8 (each operand read then feeds both rows' products)
+    constexpr int RPW = QG > 8 ? QG / 8 : 1;
+    static_assert(QG <= 8 || QG % 8 == 0, "groups of up to 8 rows, or whole multiples of 8");
     const int r0 = blockIdx.y * QG;
-    const int r = r0 + qi;
+    const int rw0 = r0 + wave % (QG < 8 ? QG : 8);
     const int64_t c0 = (int64_t)blockIdx.x * keys_per_wg;
 
     const int seq0 = a.row_seq[r0];
@@ -89,14 +93,24 @@ __global__ __launch_bounds__(512) void li_score_kernel(IndexerDev a, float* __re
     const int64_t kend = (c0 + keys_per_wg < gvis) ? c0 + keys_per_wg : gvis;
     if (c0 >= kend) return;  // uniform across the workgroup
 
-    int64_t vis = 0;
-    bool row_ok = false, row_bad = false;
-    if (r < a.R) {
-        vis = (int64_t)a.row_pos[r] + 1;
-        if (vis < 0) vis = 0;
-        if (vis > ld) vis = ld;
-        row_ok = a.row_seq[r] == seq0;
-        row_bad = !row_ok;
+    int64_t vis[RPW];
+    bool row_ok[RPW], row_bad[RPW];
+    int64_t vis_any = 0;
+    bool live = false;
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+        const int r = rw0 + 8 * i;
+        vis[i] = 0;
+        row_ok[i] = row_bad[i] = false;
+        if (r < a.R) {
+            vis[i] = (int64_t)a.row_pos[r] + 1;
+            if (vis[i] < 0) vis[i] = 0;
+            if (vis[i] > ld) vis[i] = ld;
+            row_ok[i] = a.row_seq[r] == seq0;
+            row_bad[i] = !row_ok[i];
+            live = true;
+            vis_any = vis[i] > vis_any ? vis[i] : vis_any;
+        }
     }
 
     // Block map of [c0, kend): first slot and addressable length of each block.
@@ -133,32 +147,36 @@ __global__ __launch_bounds__(512) void li_score_kernel(IndexerDev a, float* __re
     // query heads of this wave's row in A-operand layout (row = head l%16, 8 d)
     // and weights in the accumulator's head layout (4 heads per M-tile)
     typedef typename std::conditional<FP8, int64_t, bf16x8>::type OpT;
-    OpT qa[MT][KS];
-    float wv[MT][4];
+    OpT qa[RPW][MT][KS];
+    float wv[RPW][MT][4];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        const int head = mt * 16 + (lane & 15);
+    for (int q = 0; q < RPW; ++q) {
+        const int r = rw0 + 8 * q;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            if (row_ok && head < a.H_I) {
-                const uint8_t* p = a.q + (((int64_t)r * a.H_I + head) * DI + ks * 32 + (lane >> 4) * 8) * ELT;
-                if constexpr (FP8) qa[mt][ks] = *(const int64_t*)p;
-                else qa[mt][ks] = *(const bf16x8*)p;
-            } else {
-                if constexpr (FP8) qa[mt][ks] = 0;
-                else qa[mt][ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+        for (int mt = 0; mt < MT; ++mt) {
+            const int head = mt * 16 + (lane & 15);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                if (row_ok[q] && head < a.H_I) {
+                    const uint8_t* p = a.q + (((int64_t)r * a.H_I + head) * DI + ks * 32 + (lane >> 4) * 8) * ELT;
+                    if constexpr (FP8) qa[q][mt][ks] = *(const int64_t*)p;
+                    else qa[q][mt][ks] = *(const bf16x8*)p;
+                } else {
+                    if constexpr (FP8) qa[q][mt][ks] = 0;
+                    else qa[q][mt][ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+                }
             }
-        }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int h = mt * 16 + 4 * (lane >> 4) + i;
-            float wvv = 0.f;
-            if (row_ok && h < a.H_I) {
-                wvv = a.w[(int64_t)r * a.H_I + h];
-                if constexpr (FP8)
-                    wvv *= a.q_scale_per_head ? a.q_scale[(int64_t)r * a.H_I + h] : a.q_scale[r];
+            for (int i = 0; i < 4; ++i) {
+                const int h = mt * 16 + 4 * (lane >> 4) + i;
+                float wvv = 0.f;
+                if (row_ok[q] && h < a.H_I) {
+                    wvv = a.w[(int64_t)r * a.H_I + h];
+                    if constexpr (FP8)
+                        wvv *= a.q_scale_per_head ? a.q_scale[(int64_t)r * a.H_I + h] : a.q_scale[r];
+                }
+                wv[q][mt][i] = wvv;
             }
-            wv[mt][i] = wvv;
         }
     }
     __syncthreads();  // block map ready
@@ -243,51 +261,74 @@ __global__ __launch_bounds__(512) void li_score_kernel(IndexerDev a, float* __re
         // u + 1 under the products of u); the stores follow.
         constexpr int SUBW = QG == 1 ? NSUB / 8 : NSUB;
         const int64_t tfirst = t0 + (QG == 1 ? wave * 16 : 0);
-        if ((row_ok || row_bad) && tfirst < vis) {       // wave-uniform
-            float sc[SUBW];
+        if (live && tfirst < vis_any) {                  // wave-uniform
+            // in batches of SB subtiles (fewer scores held at once with two rows)
+            constexpr int SB = (RPW > 1 && SUBW > 4) ? 4 : SUBW;
+            static_assert(SUBW % SB == 0, "whole batches");
 #pragma unroll
-            for (int u = 0; u < SUBW; ++u) {
-                const int sub = QG == 1 ? (u * 8 + wave) : u;
-                f32x4 acc[MT];
+            for (int u0 = 0; u0 < SUBW; u0 += SB) {
+                float sc[RPW][SB];
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int uu = 0; uu < SB; ++uu) {
+                    const int u = u0 + uu;
+                    const int sub = QG == 1 ? (u * 8 + wave) : u;
+                    f32x4 acc[RPW][MT];
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const uint32_t bo = b_off(sub, ks);
-                    if constexpr (FP8) {
-                        const int64_t b = *(const __attribute__((address_space(3))) int64_t*)(T + bo);
+                    for (int q = 0; q < RPW; ++q)
 #pragma unroll
-                        for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma16x16x32_fp8(qa[mt][ks], b, acc[mt]);
-                    } else {
-                        const bf16x8 b = *(const lds_bf16x8*)(T + bo);
+                        for (int mt = 0; mt < MT; ++mt) acc[q][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                        for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma16x16x32_bf16(qa[mt][ks], b, acc[mt]);
+                    for (int ks = 0; ks < KS; ++ks) {
+                        const uint32_t bo = b_off(sub, ks);
+                        if constexpr (FP8) {
+                            const int64_t b = *(const __attribute__((address_space(3))) int64_t*)(T + bo);
+#pragma unroll
+                            for (int q = 0; q < RPW; ++q)
+#pragma unroll
+                                for (int mt = 0; mt < MT; ++mt)
+                                    acc[q][mt] = mfma16x16x32_fp8(qa[q][mt][ks], b, acc[q][mt]);
+                        } else {
+                            const bf16x8 b = *(const lds_bf16x8*)(T + bo);
+#pragma unroll
+                            for (int q = 0; q < RPW; ++q)
+#pragma unroll
+                                for (int mt = 0; mt < MT; ++mt)
+                                    acc[q][mt] = mfma16x16x32_bf16(qa[q][mt][ks], b, acc[q][mt]);
+                        }
+                    }
+#pragma unroll
+                    for (int q = 0; q < RPW; ++q) {
+                        float part = 0.f;
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                // ReLU as an integer max on the bit pattern (negative
+                                // floats, -0.0 included, are negative integers)
+                                const int bits = __float_as_int(acc[q][mt][i]);
+                                part = fmaf(wv[q][mt][i], __int_as_float(bits > 0 ? bits : 0), part);
+                            }
+                        {   // sum over the four 16-lane groups (lanes l ^ 16, l ^ 32) without LDS
+                            const auto w16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+                            part = __uint_as_float(w16[0]) + __uint_as_float(w16[1]);
+                            const auto w32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+                            part = __uint_as_float(w32[0]) + __uint_as_float(w32[1]);
+                        }
+                        sc[q][uu] = part;
                     }
                 }
-                float part = 0.f;
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
+                for (int q = 0; q < RPW; ++q) {
+                    const int r = rw0 + 8 * q;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        // ReLU as an integer max on the bit pattern (negative
-                        // floats, -0.0 included, are negative integers)
-                        const int bits = __float_as_int(acc[mt][i]);
-                        part = fmaf(wv[mt][i], __int_as_float(bits > 0 ? bits : 0), part);
+                    for (int uu = 0; uu < SB; ++uu) {
+                        const int sub = QG == 1 ? ((u0 + uu) * 8 + wave) : u0 + uu;
+                        const int64_t key = t0 + sub * 16 + (lane & 15);
+                        if (lane < 16 && key < vis[q] && (row_ok[q] || row_bad[q]))
+                            scores[(int64_t)r * ld + key] =
+                                row_ok[q] ? sc[q][uu] * kmul[buf][sub * 16 + lane] : __builtin_nanf("");
                     }
-                {   // sum over the four 16-lane groups (lanes l ^ 16, l ^ 32) without LDS
-                    const auto w16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(part), __float_as_uint(part), false, false);
-                    part = __uint_as_float(w16[0]) + __uint_as_float(w16[1]);
-                    const auto w32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
-                    part = __uint_as_float(w32[0]) + __uint_as_float(w32[1]);
                 }
-                sc[u] = part;
-            }
-#pragma unroll
-            for (int u = 0; u < SUBW; ++u) {
-                const int sub = QG == 1 ? (u * 8 + wave) : u;
-                const int64_t key = t0 + sub * 16 + (lane & 15);
-                if (lane < 16 && key < vis)
-                    scores[(int64_t)r * ld + key] = row_ok ? sc[u] * kmul[buf][sub * 16 + lane] : __builtin_nanf("");
             }
         }
     }
@@ -668,6 +709,25 @@ static hipError_t launch_li(const IndexerDev& a, float* scores, int64_t ld, int6
     if (kpw > (1 << 30)) kpw = (int64_t)(1 << 30) / align * align;
     nchunk = (max_visible + kpw - 1) / kpw;
     if (nchunk < 1) nchunk = 1;
+    if (QG > 1) {
+        // Grouped rows of one sequence all stream the same keys.  Workgroup
+        // ids go round-robin over the 8 XCDs, so with a power-of-two number
+        // of key chunks (<= 8) every XCD streams one fixed chunk; keeping a
+        // chunk's keys within the XCD's L2 lets all groups on it share them
+        // (a 1024-row prefill chunk at 65536 keys: 2000 -> 1100 us per call
+        // with 8 MB -> 4 MB chunks).
+        const int64_t l2_keys = kLiL2Bytes / LiCfg<DI, MT, QG, FP8>::RB;
+        int64_t nc = 1;
+        while (nc < 8 && (max_visible + nc - 1) / nc > l2_keys) nc *= 2;
+        if (nc > nchunk) {
+            int64_t k2 = (max_visible + nc - 1) / nc;
+            k2 = (k2 + align - 1) / align * align;
+            if (k2 < kpw) {
+                kpw = k2;
+                nchunk = (max_visible + kpw - 1) / kpw;
+            }
+        }
+    }
     dim3 grid((unsigned)nchunk, (unsigned)groups);
     hipLaunchKernelGGL((li_score_kernel<DI, MT, QG, FP8>), grid, dim3(512), 0, stream, a, scores, ld, (int)kpw);
     return hipGetLastError();
@@ -741,9 +801,14 @@ hipError_t li_score_dispatch(const IndexerDev& a, int D_I, int dtype, int qg, fl
         if (D_I == 32 && mt == 2) return launch_li_dec<32, 2>(a, scores, ld, max_visible, stream);
         if (D_I == 32 && mt == 1) return launch_li_dec<32, 1>(a, scores, ld, max_visible, stream);
     }
+    // 16-row groups are built for the 64 x 128 indexer; other shapes take the
+    // 16-aligned group as two 8-row groups
+    if (qg == 16 && !(D_I == 128 && mt == 4)) qg = 8;
 #define LISFA_LI_CASE(DI_, MT_, QG_, F8_)                                                    \
     if (D_I == DI_ && mt == MT_ && qg == QG_ && (fp8 != 0) == F8_)                            \
         return launch_li<DI_, MT_, QG_, F8_>(a, scores, ld, max_visible, stream);
+    LISFA_LI_CASE(128, 4, 16, false)
+    LISFA_LI_CASE(128, 4, 16, true)
     LISFA_LI_CASE(128, 4, 1, false)
     LISFA_LI_CASE(128, 4, 8, false)
     LISFA_LI_CASE(128, 4, 1, true)

@@ -44,7 +44,9 @@ def caches(b: W.Batch):
 
 
 def rows_per_group(b: W.Batch) -> int:
-    return 8 if (b.wl.mode == "prefill" and b.R % 8 == 0) else 1
+    if b.wl.mode != "prefill":
+        return 1
+    return 16 if b.R % 16 == 0 else 8 if b.R % 8 == 0 else 1
 
 
 def gpu_scores(b: W.Batch, ld: int = None) -> torch.Tensor:

@@ -236,6 +236,34 @@ def test_determinism(lib):
             assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
 
 
+def test_rows_per_group_16_matches_8(lib):
+    """Groups of 16 rows (two rows per wave, each key operand read feeding
+    both) give the same fp32 scores, bit for bit, as groups of 8 and as one row
+    at a time would for the same rows: every row's products and sums are
+    evaluated in the same order."""
+    wl = W.CONFIGS[3].with_(seq_len=3000, q_rows=48, name="prefill_groups")
+    say(f"[case] 16- vs 8-row groups {wl.name}")
+    b = batch_on_gpu(wl)
+    kc, _ = caches(b)
+    ld = (b.max_visible + 63) // 64 * 64
+    out = {}
+    for g in (16, 8):
+        sc = torch.full((b.R, ld), float("nan"), dtype=torch.float32, device="cuda")
+        lisfa.li_score(b.q_idx, b.w, kc, b.row_seq, b.row_pos, sc, b.max_visible, q_scale=b.q_scale,
+                       rows_per_group=g)
+        out[g] = sc
+    torch.cuda.synchronize()
+    inp = W.to_numpy(b)
+    for r in range(b.R):
+        n = int(b.row_pos[r]) + 1
+        assert torch.equal(out[16][r, :n], out[8][r, :n]), f"row {r}"
+    for r in (0, 17, 47):
+        n = int(b.row_pos[r]) + 1
+        ref = O.scores_row(inp, r)
+        got = out[16][r, :n].cpu().numpy().astype(np.float64)
+        assert np.all(np.abs(got - ref) <= score_bound(inp, r) + 0.0), f"row {r}"
+
+
 def test_rows_per_group_mismatch_poisons_scores(lib):
     """A row whose sequence differs from its group's first row gets NaN
     scores instead of silently reading another sequence's keys."""
