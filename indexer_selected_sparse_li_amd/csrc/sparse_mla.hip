@@ -40,7 +40,6 @@ namespace lisfa {
 __device__ __attribute__((aligned(16))) uint8_t g_zero16[64];
 
 constexpr int kSfaMaxKeys = 2048;  // index entries one workgroup handles
-constexpr bool kSfaWarpSpecialised = true;   // 512 + 64 bf16 rows, 64-head blocks: sfa_ws_kernel
 
 // XOR swizzle of the 16-byte chunks of LDS row r (values < 8, so a chunk stays
 // inside its aligned group of 8).  With it, 16 consecutive rows read at one
@@ -931,367 +930,18 @@ __global__ __launch_bounds__(128 * NHG) void sfa_bf16_kernel(MlaDev a, int kps, 
     else body(std::integral_constant<int, 0>{});
 }
 
-// Chunk permutation of the eight-wave kernel: for rows of one parity,
+// Chunk permutation of the warp-specialised kernel: for rows of one parity,
 // swz8 maps (r / 2) % 8 = m to 2 (m % 4) + m / 4, a bijection (16 consecutive
 // rows read at one chunk hit 16 distinct 16-byte bank groups) whose halves
 // m < 4 and m >= 4 give distinct chunk pairs (8 consecutive rows read at two
 // adjacent chunks by a transpose read hit 16 distinct bank groups).
 __device__ __forceinline__ int sfa_swz8(int r) { return (((r >> 1) & 3) << 1) | ((r >> 3) & 1); }
 
-// Eight waves per workgroup (two per SIMD) for 64 heads of wide bf16 rows ---
-//
-// Wave w owns 16 heads (quarter hq = w / 2) and one half dh = w % 2 of the
-// QK^T reduction and of the value columns, on 16x16x32 MFMAs:
-//   QK:  S^T[16 keys x 16 heads] += K[16 keys x 32 d] * Q^T[32 d x 16 heads],
-//        two key blocks per 32-row tile, the query half in VGPRs (36 regs);
-//        the two halves' partial logits are summed through LDS.
-//   PV:  O^T[16 value columns x 16 heads] += V^T[16 x 32 keys] * P^T, 16 M-tiles
-//        per wave (64 accumulator regs).
-// In the S^T accumulator lane l holds head l % 16 and keys 16 kb + 4 (l / 16)
-// + i of key block kb; the P^T operand takes them as K-slots 8 (l / 16) + 4 kb
-// + i, and the value operand is read for the same key order (two transpose
-// reads of 4 consecutive rows each), so probabilities feed the PV product
-// straight from the accumulators.  At under 256 registers per wave two waves
-// share each SIMD and cover each other's waits.  Tile layout and loads are
-// those of sfa_bf16_kernel (the first four waves load) with the chunk
-// permutation sfa_swz8.
-template <int DLAT, int DROPE>
-__global__ __launch_bounds__(512) void sfa_w8_kernel(MlaDev a, int kps, int nsplit, int nhb,
-                                                      __bf16* __restrict__ out, float* __restrict__ lse,
-                                                      float* __restrict__ part_o, float* __restrict__ part_lse) {
-    constexpr int DQK = DLAT + DROPE;
-    constexpr int CPK = DQK * 2 / 16;       // 16-byte chunks per row
-    static_assert((DQK * 2) % 128 == 0 && CPK * 16 <= 2048, "rows must be whole 128-byte groups");
-    constexpr int NJ = CPK / 8;             // 1 KB blocks per 8-row group
-    constexpr int GB = NJ * 1024;           // bytes per 8-row group
-    constexpr int TROWS = 32;
-    constexpr int TB = (TROWS / 8) * GB;    // bytes per tile
-    constexpr int NBUF = 3;                 // tile ring: PV(t) | QK(t+1) | loading t+2
-    constexpr int NT = 512;
-    constexpr int KS = DQK / 32;            // 16x16x32 K-steps
-    static_assert(DQK % 64 == 0, "even K-step count");
-    constexpr int NKS = KS / 2;             // K-steps per wave
-    constexpr int DVH = DLAT / 2;           // value columns per wave
-    constexpr int MTV = DVH / 16;           // PV M-tiles per wave
-    static_assert(DVH % 64 == 0, "shape");
-    typedef float f32x4v __attribute__((ext_vector_type(4)));
-
-    __shared__ __attribute__((aligned(1024))) uint8_t tile[NBUF * TB];
-    __shared__ uint32_t rslot[kSfaMaxKeys];            // cache slot of each selected row, ~0 = skip
-    __shared__ uint32_t vmask[kSfaMaxKeys / 32];       // valid-row bits of each 32-row tile
-    __shared__ __attribute__((aligned(16))) float xbuf[2][8 * 2 * 64 * 4];   // [buf][wave][2][lane][4]
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int hq = wave >> 1;
-    const int bid = blockIdx.x;
-    const int hb = (bid >> 3) % nhb;
-    const int u = ((bid >> 3) / nhb) * 8 + (bid & 7);
-    if (u >= a.R * nsplit) return;
-    const int r = u / nsplit, sp = u % nsplit;
-    const int k0 = sp * kps;
-    const int k1 = (k0 + kps < a.K) ? k0 + kps : a.K;
-    const int nk = k1 - k0;
-    const int seq = a.row_seq[r];
-    const int nt_fill = (nk + TROWS - 1) / TROWS;
-    __shared__ int s_ntiles;
-    if (tid == 0) s_ntiles = 1;
-
-    for (int i0 = 0; i0 < nt_fill * TROWS; i0 += NT) {
-        const int i = i0 + tid;
-        int64_t s = -1;
-        if (i < nk) {
-            const int p = a.idx[(int64_t)r * a.K + k0 + i];
-            s = p >= 0 ? slot_of(a.kv, seq, p) : -1;
-        }
-        if (i < nt_fill * TROWS) rslot[i] = s >= 0 ? (uint32_t)s : 0xFFFFFFFFu;
-        const uint64_t bal = __ballot(s >= 0);
-        if (lane == 0 && i < nt_fill * TROWS) {
-            vmask[i / 32] = (uint32_t)bal;
-            if (i + 32 < nt_fill * TROWS) vmask[i / 32 + 1] = (uint32_t)(bal >> 32);
-        }
-    }
-    __syncthreads();
-    // trailing tiles without a valid row are skipped; at least one tile is
-    // always processed (an empty tile contributes nothing)
-    for (int t = tid; t < nt_fill; t += NT)
-        if (vmask[t] != 0u) atomicMax(&s_ntiles, t + 1);
-    __syncthreads();
-    const int ntiles = s_ntiles;
-
-    const lds_u8* tile0 = (const lds_u8*)tile;
-    const uint32_t tile_lds = (uint32_t)(uintptr_t)tile;
-    // loads (waves 0..3): thread tid brings chunks of tile row tid / 8
-    const bool loader = wave < 4;
-    const int lrow = (tid >> 3) & 31;
-    const uint32_t goff = (uint32_t)(((tid & 7) ^ sfa_swz8(lrow)) << 4);
-    auto read_slot = [&](int t) -> uint32_t { return rslot[(t < ntiles ? t : 0) * TROWS + lrow]; };
-    auto issue_tile = [&](uint32_t s, int buf) {
-        const uint8_t* g = (s != 0xFFFFFFFFu ? a.kv.data + (uint64_t)s * (uint32_t)a.kv.row_stride : g_zero_row) + goff;
-        const uint32_t blk = tile_lds + (uint32_t)(buf * TB + wave * GB);
-        static_for<NJ>([&](auto jc) {
-            constexpr int j = decltype(jc)::value;
-            // the immediate offset moves both the global and the LDS address;
-            // block j lands at blk + j KB
-            lds_dma<16, j * 128>(g, blk + (uint32_t)(j * (1024 - 128)));
-        });
-    };
-
-    auto body = [&](auto dh_c) {
-        constexpr int DH = decltype(dh_c)::value;
-        constexpr int KSB = DH * NKS;
-        const int g = lane >> 4, l16 = lane & 15;
-        const int head = hb * 64 + hq * 16 + l16;
-        // query half in B-operand layout: lane = head, 8 consecutive d of K-step ks
-        bf16x8 qb[NKS];
-#pragma unroll
-        for (int j = 0; j < NKS; ++j) {
-            if (head < a.H)
-                qb[j] = *(const bf16x8*)(a.q + (((int64_t)r * a.H + head) * DQK + (KSB + j) * 32 + g * 8) * 2);
-            else
-                qb[j] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-        }
-        // QK operand of key block kb, K-step ks: row 16 kb + l16, chunk 4 ks + g
-        uint32_t qa[2];
-#pragma unroll
-        for (int par = 0; par < 2; ++par)
-            qa[par] = (uint32_t)((l16 >> 3) * GB + (l16 & 7) * 128 + (((4 * par + g) ^ sfa_swz8(l16)) << 4));
-        auto qk_op = [&](const lds_u8* T, int kb, int ks) -> bf16x8 {   // compile-time kb, ks
-            return *(const lds_bf16x8*)(T + qa[ks & 1] + kb * 2 * GB + (ks >> 1) * 1024);
-        };
-        // PV operand of M-tile mt: transpose reads of rows 4 g + l16 / 4 (keys of
-        // K-slots 0..3) and 16 + 4 g + l16 / 4 (K-slots 4..7), 4 value columns
-        // each; lane then holds column 16 mt + l16 of those 8 keys
-        uint32_t pva[4];
-#pragma unroll
-        for (int m4 = 0; m4 < 4; ++m4) {
-            const int rr = 4 * g + (l16 >> 2);
-            const int cc = 2 * m4 + ((l16 & 3) >> 1);
-            pva[m4] = (uint32_t)((rr >> 3) * GB + (rr & 7) * 128 + ((cc ^ sfa_swz8(rr)) << 4) + 8 * (l16 & 1));
-        }
-        typedef short s16x4 __attribute__((ext_vector_type(4)));
-        typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-        auto trd = [&](const lds_u8* T, int mt, int half) -> s16x4 {   // compile-time mt, half
-            return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4*)(T + pva[mt & 3] + half * 2 * GB + (4 * DH + (mt >> 2)) * 1024));
-        };
-        auto put_partial = [&](const f32x4v (&s)[2], int xb) {
-            float* xs = xbuf[xb] + wave * 512 + lane * 4;
-            *(f32x4v*)(xs) = s[0];
-            *(f32x4v*)(xs + 256) = s[1];
-        };
-
-        f32x4v o[MTV];
-#pragma unroll
-        for (int mt = 0; mt < MTV; ++mt) o[mt] = f32x4v{0.f, 0.f, 0.f, 0.f};
-        float m2 = -__builtin_inff(), lsum = 0.f;
-        const float c = a.scale_log2;
-        f32x4v s_cur[2] = {f32x4v{0.f, 0.f, 0.f, 0.f}, f32x4v{0.f, 0.f, 0.f, 0.f}};
-        constexpr int PF = 4;   // QK^T operand reads in flight
-
-        auto qk = [&](const lds_u8* T, f32x4v (&s)[2]) {
-            s[0] = f32x4v{0.f, 0.f, 0.f, 0.f};
-            s[1] = s[0];
-            bf16x8 buf[PF];
-#pragma unroll
-            for (int j = 0; j < PF; ++j) buf[j] = qk_op(T, j & 1, KSB + (j >> 1));
-#pragma unroll
-            for (int j = 0; j < 2 * NKS; ++j) {
-                const bf16x8 av = buf[j % PF];
-                if (j + PF < 2 * NKS) buf[j % PF] = qk_op(T, (j + PF) & 1, KSB + ((j + PF) >> 1));
-                s[j & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qb[j >> 1], s[j & 1], 0, 0, 0);
-            }
-        };
-
-        uint32_t sl = 0xFFFFFFFFu;
-        if (loader) {
-            if (ntiles > 0) issue_tile(read_slot(0), 0);
-            if (ntiles > 1) issue_tile(read_slot(1), 1);
-            sl = read_slot(2);
-        }
-        if (ntiles > 0) {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __syncthreads();
-            qk(tile0, s_cur);
-            put_partial(s_cur, 0);
-        }
-
-        uint32_t vm = __builtin_amdgcn_readfirstlane(vmask[0]);   // valid rows of tile t
-        int bcur = 0;
-        for (int t = 0; t < ntiles; ++t) {
-            const int bnext = bcur == NBUF - 1 ? 0 : bcur + 1;
-            const int bnext2 = bnext == NBUF - 1 ? 0 : bnext + 1;
-            // tile t+1 landed; tile t-1's buffer is free; partials of tile t published
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __syncthreads();
-            const lds_u8* T = tile0 + bcur * TB;
-            const lds_u8* Tn = tile0 + bnext * TB;
-
-            // LDS reads needed first, then the loads of tile t+2
-            f32x4v xr[2];
-            {
-                const float* xp = xbuf[t & 1] + (wave ^ 1) * 512 + lane * 4;
-                xr[0] = *(const f32x4v*)(xp);
-                xr[1] = *(const f32x4v*)(xp + 256);
-            }
-            const uint32_t vmr_next = vmask[t + 1 < ntiles ? t + 1 : 0];
-            bf16x8 buf[PF];
-#pragma unroll
-            for (int j = 0; j < PF; ++j) buf[j] = qk_op(Tn, j & 1, KSB + (j >> 1));
-            if (loader) {
-                if (t + 2 < ntiles) issue_tile(sl, bnext2);
-                sl = read_slot(t + 3);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-
-            // QK^T of tile t+1 (independent of this tile's softmax) in three
-            // stretches, with the softmax of tile t in between: the matrix pipe
-            // stays busy while the statistics are formed.
-            f32x4v s_next[2] = {f32x4v{0.f, 0.f, 0.f, 0.f}, f32x4v{0.f, 0.f, 0.f, 0.f}};
-            auto qk_step = [&](int j) {   // compile-time j after unrolling
-                const bf16x8 av = buf[j % PF];
-                if (j + PF < 2 * NKS) buf[j % PF] = qk_op(Tn, (j + PF) & 1, KSB + ((j + PF) >> 1));
-                s_next[j & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qb[j >> 1], s_next[j & 1], 0, 0, 0);
-            };
-            auto qk_groups = [&](int j0, int j1) {
-                for (int j = j0; j < j1; ++j) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    if (j + PF < 2 * NKS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                }
-            };
-            constexpr int QA = 4, QB = 8;
-
-            // stretch A: raw logits of tile t (keys 16 kb + 4 g + i)
-#pragma unroll
-            for (int j = 0; j < QA; ++j) qk_step(j);
-            f32x4v s[2] = {s_cur[0] + xr[0], s_cur[1] + xr[1]};
-            qk_groups(0, QA);
-            __builtin_amdgcn_sched_barrier(0);
-            if (vm != 0xFFFFFFFFu) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (!((vm >> (16 * kb + 4 * g + i)) & 1u)) s[kb][i] = -__builtin_inff();
-            }
-            // stretch B: tile maximum of each head over its 4 lane groups (log2 units)
-#pragma unroll
-            for (int j = QA; j < QB; ++j) qk_step(j);
-            float tmax = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                               fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-            {
-                const auto w16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
-                tmax = fmaxf(__uint_as_float(w16[0]), __uint_as_float(w16[1]));
-                const auto w32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
-                tmax = fmaxf(__uint_as_float(w32[0]), __uint_as_float(w32[1]));
-            }
-            tmax *= c;   // c > 0
-            // lazy reference maximum (raised only past kLazy log2 units)
-            constexpr float kLazy = 8.0f;
-            const bool raise = tmax > m2 + kLazy;   // also true on the first valid tile
-            qk_groups(QA, QB);
-            __builtin_amdgcn_sched_barrier(0);
-            if (__ballot(raise) != 0ull) {
-                const float mnew = raise ? tmax : m2;
-                const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);  // m2 = -inf -> 0
-                lsum *= alpha;
-#pragma unroll
-                for (int mt = 0; mt < MTV; ++mt) o[mt] *= alpha;
-                m2 = mnew;
-            }
-            // a head with no valid row so far keeps m2 = -inf: its (masked)
-            // probabilities must come out 0, not NaN
-            const float negm = m2 == -__builtin_inff() ? 0.f : -m2;
-
-            // stretch C: the rest of QK^T(t+1) with the exponentials of tile t
-            float pe[8];
-#pragma unroll
-            for (int j = QB; j < 2 * NKS; ++j) {
-                qk_step(j);
-                if (j - QB < 8) pe[j - QB] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[(j - QB) >> 2][(j - QB) & 3], c, negm));
-            }
-            float rs = ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
-            {
-                const auto w16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(rs), __float_as_uint(rs), false, false);
-                rs = __uint_as_float(w16[0]) + __uint_as_float(w16[1]);
-                const auto w32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(rs), __float_as_uint(rs), false, false);
-                rs = __uint_as_float(w32[0]) + __uint_as_float(w32[1]);
-            }
-            lsum += rs;
-            bf16x8 pb;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) pb[e] = (__bf16)pe[e];
-            qk_groups(QB, 2 * NKS);
-            __builtin_amdgcn_sched_barrier(0);
-
-            // Phase 2, PV(t), in two batches of MH M-tiles: the second batch's
-            // operand reads go out right after the first MFMA and fly under the
-            // rest of the first batch.
-            constexpr int MH = MTV / 2;
-            s16x4 ra[MH][2], rc[MH][2];
-#pragma unroll
-            for (int m = 0; m < MH; ++m)
-#pragma unroll
-                for (int h = 0; h < 2; ++h) ra[m][h] = trd(T, m, h);
-            auto pv_step = [&](int mt, const s16x4 (&v)[2]) {
-                const u32x2 lo = __builtin_bit_cast(u32x2, v[0]);
-                const u32x2 hi = __builtin_bit_cast(u32x2, v[1]);
-                const u32x4 w = {lo.x, lo.y, hi.x, hi.y};
-                o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w), pb, o[mt], 0, 0, 0);
-            };
-            pv_step(0, ra[0]);
-#pragma unroll
-            for (int m = 0; m < MH; ++m)
-#pragma unroll
-                for (int h = 0; h < 2; ++h) rc[m][h] = trd(T, MH + m, h);
-#pragma unroll
-            for (int m = 1; m < MH; ++m) pv_step(m, ra[m]);
-#pragma unroll
-            for (int m = 0; m < MH; ++m) pv_step(MH + m, rc[m]);
-            put_partial(s_next, (t + 1) & 1);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2 * MH, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2 * MH, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, MTV - 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
-            __builtin_amdgcn_sched_barrier(0);
-            s_cur[0] = s_next[0];
-            s_cur[1] = s_next[1];
-            vm = __builtin_amdgcn_readfirstlane(vmr_next);
-            bcur = bnext;
-        }
-
-        // epilogue: normalise and store.  O^T accumulator of M-tile mt: lane =
-        // head l16, register i = value column 16 mt + 4 g + i of this half.
-        if (head < a.H) {
-            const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-            const float l_nat = lsum > 0.f ? (m2 + log2f(lsum)) * kLn2 : -__builtin_inff();
-            if (nsplit == 1 && out != nullptr) {
-                __bf16* orow = out + ((int64_t)r * a.H + head) * DLAT + DH * DVH + 4 * g;
-#pragma unroll
-                for (int mt = 0; mt < MTV; ++mt) {
-                    bf16x4 v;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) v[i] = (__bf16)(o[mt][i] * inv);
-                    *(bf16x4*)(orow + 16 * mt) = v;
-                }
-                if (lse != nullptr && DH == 0 && g == 0) lse[(int64_t)r * a.H + head] = l_nat;
-            } else {
-                float* prow = part_o + (((int64_t)r * nsplit + sp) * a.H + head) * DLAT + DH * DVH + 4 * g;
-#pragma unroll
-                for (int mt = 0; mt < MTV; ++mt) *(f32x4v*)(prow + 16 * mt) = o[mt] * inv;
-                if (DH == 0 && g == 0) part_lse[((int64_t)r * nsplit + sp) * a.H + head] = l_nat;
-            }
-        }
-    };
-    if (wave & 1) body(std::integral_constant<int, 1>{});
-    else body(std::integral_constant<int, 0>{});
-}
-
 // Warp-specialised eight-wave kernel for 64 heads of 512 + 64 bf16 rows ---------
 //
-// Same tiles, layout, loads and lazy online softmax as sfa_w8_kernel, but the
-// waves split the work by kind instead of by columns:
+// Tiles of 32 gathered rows in 8-row groups of 1 KB blocks (chunk permutation
+// sfa_swz8), a lazy online softmax (the reference maximum is raised only when a
+// tile exceeds it by 2^8), and the waves split the work by kind:
 //  * q-waves 0..3: wave w owns heads 16 w .. 16 w + 15 of the block over all
 //    576 QK columns (query in 72 VGPRs): S^T of tile t+1 (36 MFMAs), masking,
 //    tile maximum, lazy reference raise and exponentials; it writes P^T to an
@@ -1300,7 +950,8 @@ __global__ __launch_bounds__(512) void sfa_w8_kernel(MlaDev a, int kps, int nspl
 //  * p-waves 4..7: wave 4 + c owns value columns 128 c .. 128 c + 127 of all
 //    64 heads (O^T in 128 accumulator VGPRs): applies the raise factors of the
 //    flagged head tiles and runs PV of tile t (32 MFMAs), the value operand
-//    from transpose reads as in sfa_w8_kernel.  The p-waves also issue the
+//    from transpose reads of 4 consecutive rows at 4 value columns per lane
+//    (the P^T operand's key order).  The p-waves also issue the
 //    direct-to-LDS tile loads, NBUF - 2 tiles ahead, from inline assembly
 //    (lds_dma): hidden from the compiler's wait-count model, they no longer
 //    turn every LDS operand wait of the issuing wave into a full drain; explicit
@@ -1855,19 +1506,16 @@ static hipError_t launch_sfa_t(const MlaDev& a, const SfaPlan& p, __bf16* out, f
         part_o = out_f32;
         part_lse = lse;
     }
-    if (!FP8 && DLAT == 512 && DROPE == 64 && NHG == 2 && kSfaWarpSpecialised && p.kps <= 1024)
+    if (!FP8 && DLAT == 512 && DROPE == 64 && NHG == 2 && p.kps <= 1024)
         hipLaunchKernelGGL((sfa_ws_kernel<512, 64, 4, 1024>), dim3((unsigned)nwg), dim3(512), 0, stream, a, p.kps,
                            p.nsplit, p.nhb, out, lse, part_o, part_lse);
-    else if (!FP8 && DLAT == 512 && DROPE == 64 && NHG == 2 && kSfaWarpSpecialised)
+    else if (!FP8 && DLAT == 512 && DROPE == 64 && NHG == 2)
         hipLaunchKernelGGL((sfa_ws_kernel<512, 64, 3, kSfaMaxKeys>), dim3((unsigned)nwg), dim3(512), 0, stream, a,
                            p.kps, p.nsplit, p.nhb, out, lse, part_o, part_lse);
-    else if (FP8 && DLAT == 512 && DROPE == 64 && NHG == 2 && kSfaWarpSpecialised && p.kps <= 1024)
+    else if (FP8 && DLAT == 512 && DROPE == 64 && NHG == 2 && p.kps <= 1024)
         // fp8 rows turned into bf16 tiles by the loading waves (factor per row or per 128-column tile)
         hipLaunchKernelGGL((sfa_ws_kernel<512, 64, 3, 1024, TSC ? 2 : 1>), dim3((unsigned)nwg), dim3(512), 0, stream,
                            a, p.kps, p.nsplit, p.nhb, out, lse, part_o, part_lse);
-    else if constexpr (!FP8 && ((DLAT + DROPE) * 2) % 128 == 0 && NHG == 2)
-        hipLaunchKernelGGL((sfa_w8_kernel<DLAT, DROPE>), dim3((unsigned)nwg), dim3(512), 0, stream, a, p.kps,
-                           p.nsplit, p.nhb, out, lse, part_o, part_lse);
     else if constexpr (!FP8 && ((DLAT + DROPE) * 2) % 128 == 0)
         hipLaunchKernelGGL((sfa_bf16_kernel<DLAT, DROPE, NHG>), dim3((unsigned)nwg), dim3(128 * NHG), 0, stream,
                            a, p.kps, p.nsplit, p.nhb, out, lse, part_o, part_lse);
