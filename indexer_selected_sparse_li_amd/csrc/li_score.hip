@@ -738,8 +738,9 @@ static hipError_t launch_li_dec(const IndexerDev& a, float* scores, int64_t ld, 
                                 hipStream_t stream) {
     const int sh = a.k.paged ? a.k.bs_shift : 6;
     const int64_t bsz = (int64_t)1 << sh;
-    // about two four-wave workgroups per CU in total
-    const int64_t want_wg = 512;
+    // one four-wave workgroup per CU (measured against two per CU: 2 % faster
+    // on uniform and on mixed-length batches; finer chunks are slower)
+    const int64_t want_wg = 256;
     int64_t nchunk = (want_wg + a.R - 1) / a.R;
     int64_t kpw = (max_visible + nchunk - 1) / nchunk;
     if (kpw < 1024) kpw = 1024;
