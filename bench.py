@@ -339,7 +339,7 @@ def main():
         report_prolog(args)
         return
     wl = W.get(args.workload)
-    res, b = run_workload(args, wl)
+    res, b = run_workload(args, wl, cold=not args.only)
     if res is None:
         return
     if not args.no_cpu_baseline:
@@ -488,9 +488,14 @@ def run_workload(args, wl, cold=False, graph=False):
     roofline["kernel"] = dominant
     roofline["traffic"] = stored_traffic(dominant, wl.name)
 
+    # headline: cold steps (every step after a flush of the L2s and the MALL)
+    # when measured, else back-to-back ("hot") steps
+    ms_head = ms_cold if ms_cold is not None else ms_step
     res = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "metric": METRIC, "value": round(R / (ms_head * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_head, 4),
+        "timing": "cold: each timed step follows a 512 MiB write that evicts the L2s and the MALL"
+                  if ms_cold is not None else "hot: back-to-back steps",
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.kv_dtype,
         "data": "synthetic (seeded; inputs resident in HBM)",
         "config": {"workload": wl.name, "rows": R, "context": b.max_visible, "K": wl.K,
@@ -501,6 +506,8 @@ def run_workload(args, wl, cold=False, graph=False):
         "roofline": roofline,
         "stages": stages,
     }
+    res["ms_per_step_hot"] = round(ms_step, 4)
+    res["value_hot"] = round(value, 1)
     if ms_cold is not None:
         res["ms_per_step_cold"] = round(ms_cold, 4)
         res["value_cold"] = round(R / (ms_cold * 1e-3), 1)
@@ -827,7 +834,7 @@ def write_report_md(path, lines, args):
             orc = f'{cb["value"]:.3g} ({cb["cores"]})' if cb else "not run"
             fh.write(f'| {r["config"]["workload"]} | {r["config"]["rows"]} | '
                      f'{r["ms_per_step_cold"] * 1e3:.1f} | {r["value_cold"]:.0f} | '
-                     f'{r["ms_per_step"] * 1e3:.1f} | {r["value"]:.0f} | '
+                     f'{r["ms_per_step_hot"] * 1e3:.1f} | {r["value_hot"]:.0f} | '
                      f'{r["ms_per_step_graph"] * 1e3:.1f} | {r["value_graph"]:.0f} | '
                      f'{st(r, "li_score")} | {st(r, "topk_select")} | {st(r, "sparse_mla_attn")} | {orc} |\n')
         if any(r.get("cpu_baseline") for r in lines):

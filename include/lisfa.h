@@ -131,7 +131,7 @@ typedef struct {
     int32_t        H;            /* heads: 1..128 */
     int32_t        D_latent;     /* 512 (with D_rope 64) or 64 (with D_rope 16) */
     int32_t        D_rope;
-    float          softmax_scale;
+    float          softmax_scale; /* > 0 and finite (else LISFA_ERR_BAD_SHAPE) */
 } lisfa_mla_args;
 
 /*

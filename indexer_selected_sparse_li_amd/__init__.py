@@ -24,6 +24,7 @@ from __future__ import annotations
 
 import ctypes
 import dataclasses
+import math
 from typing import Optional
 
 import torch
@@ -152,6 +153,8 @@ def _mla_args(q, kv_cache, row_seq, D_latent, softmax_scale):
     R, H, D_qk = q.shape
     if q.dtype != torch.bfloat16:
         raise ValueError("MLA queries must be bf16")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D_qk)   # the usual 1/sqrt(latent + rope)
     return _c.MlaArgs(q=_ptr(q), kv_cache=kv_cache.c_struct(), row_seq=_ptr(row_seq), R=R, H=H,
                       D_latent=D_latent, D_rope=D_qk - D_latent, softmax_scale=float(softmax_scale))
 
@@ -160,14 +163,34 @@ def workspace_size(op: int, R: int, max_visible: int, K: int, H: int, D_latent: 
     return int(_c.load().lisfa_workspace_size(op, R, max_visible, K, H, D_latent))
 
 
-def _workspace(ws: Optional[torch.Tensor], need: int, device) -> Optional[torch.Tensor]:
+# Workspaces the binding owns, one per (device, stream), grown on demand and
+# reused: calls on one stream run in order, so they never overlap in it.
+_WS_CACHE = {}
+
+
+def _workspace(ws: Optional[torch.Tensor], need: int, device, stream=None) -> Optional[torch.Tensor]:
+    """The caller's workspace (checked against `need`), or the binding's cached
+    one for this device and stream.  A caller that passes no workspace gets a
+    buffer that stays allocated for later calls on the same stream; pass one
+    explicitly to control its lifetime."""
     if need == 0:
         return ws
-    if ws is None:
-        return torch.empty(need, dtype=torch.uint8, device=device)
-    if ws.numel() * ws.element_size() < need:
-        raise ValueError(f"workspace of {ws.numel() * ws.element_size()} bytes < {need}")
-    return ws
+    if ws is not None:
+        if ws.numel() * ws.element_size() < need:
+            raise ValueError(f"workspace of {ws.numel() * ws.element_size()} bytes < {need}")
+        return ws
+    dev = torch.device(device)
+    st = _stream(stream)
+    key = (dev.index if dev.index is not None else torch.cuda.current_device(), st)
+    cur = _WS_CACHE.get(key)
+    if cur is None or cur.numel() < need:
+        # the caching allocator may hand a freed block to other work on its own
+        # stream; record the stream that uses this one so that cannot happen early
+        cur = torch.empty(need, dtype=torch.uint8, device=dev)
+        if st != torch.cuda.current_stream(dev).cuda_stream:
+            cur.record_stream(torch.cuda.ExternalStream(st, device=dev))
+        _WS_CACHE[key] = cur
+    return cur
 
 
 def li_score(q_idx, w, k_cache: KVCache, row_seq, row_pos, scores, max_visible: int,
@@ -188,7 +211,7 @@ def topk_select(scores, row_pos, K: int, idx, workspace=None, stream=None):
         raise ValueError("idx must be [R, K] int32")
     R, ld = scores.shape
     need = lib.lisfa_workspace_size(_c.LISFA_OP_TOPK, R, ld, K, 0, 0)
-    ws = _workspace(workspace, need, scores.device)
+    ws = _workspace(workspace, need, scores.device, stream)
     _check(lib.topk_select(_ptr(scores), ld, _ptr(row_pos), R, K, _ptr(idx),
                            _ptr(ws) if (ws is not None and need) else None, need, _stream(stream)),
            "topk_select")
@@ -206,7 +229,7 @@ def topk_candidates(scores, row_pos, K: int, cand_pos, cand_score, pos_offset=No
         if t.dtype != dt or tuple(t.shape) != (R, K):
             raise ValueError(f"candidate outputs must be [R, K] {dt}")
     need = lib.lisfa_workspace_size(_c.LISFA_OP_TOPK_CANDIDATES, R, ld, K, 0, 0)
-    ws = _workspace(workspace, need, scores.device)
+    ws = _workspace(workspace, need, scores.device, stream)
     _check(lib.topk_candidates(_ptr(scores), ld, _ptr(row_pos), R, K, _ptr(pos_offset), _ptr(cand_pos),
                                _ptr(cand_score), _ptr(ws) if (ws is not None and need) else None, need,
                                _stream(stream)), "topk_candidates")
@@ -226,7 +249,7 @@ def topk_merge(cand_score, cand_pos, K: int, idx, idx_score=None, ordered: bool 
     return idx
 
 
-def sparse_mla_attn(q, kv_cache: KVCache, row_seq, idx, out, lse=None, softmax_scale: float = None,
+def sparse_mla_attn(q, kv_cache: KVCache, row_seq, idx, out, lse=None, softmax_scale: Optional[float] = None,
                     workspace=None, stream=None):
     """out[r, h] = softmax attention of q[r, h] over the latent rows named by idx[r]."""
     lib = _c.load()
@@ -235,7 +258,7 @@ def sparse_mla_attn(q, kv_cache: KVCache, row_seq, idx, out, lse=None, softmax_s
     K = idx.shape[1]
     a = _mla_args(q, kv_cache, row_seq, D_latent, softmax_scale)
     need = lib.lisfa_workspace_size(_c.LISFA_OP_SPARSE_MLA, R, 0, K, H, D_latent)
-    ws = _workspace(workspace, need, q.device)
+    ws = _workspace(workspace, need, q.device, stream)
     _check(lib.sparse_mla_attn(ctypes.byref(a), _ptr(idx), K, _ptr(out), _ptr(lse),
                                _ptr(ws) if ws is not None else None, need, _stream(stream)),
            "sparse_mla_attn")
@@ -243,7 +266,7 @@ def sparse_mla_attn(q, kv_cache: KVCache, row_seq, idx, out, lse=None, softmax_s
 
 
 def sparse_mla_attn_partial(q, kv_cache: KVCache, row_seq, idx, out, lse, shard_range=None,
-                            softmax_scale: float = None, workspace=None, stream=None):
+                            softmax_scale: Optional[float] = None, workspace=None, stream=None):
     """fp32 partial attention of one context shard over the rows of idx
     (logical positions) inside shard_range[r] = (lo, hi); kv_cache addresses
     the shard's rows by local position (logical - lo)."""
@@ -255,7 +278,7 @@ def sparse_mla_attn_partial(q, kv_cache: KVCache, row_seq, idx, out, lse, shard_
         raise ValueError("partial outputs are fp32 out [R, H, D_latent] and lse [R, H]")
     a = _mla_args(q, kv_cache, row_seq, D_latent, softmax_scale)
     need = lib.lisfa_workspace_size(_c.LISFA_OP_SPARSE_MLA_PARTIAL, R, 0, K, H, D_latent)
-    ws = _workspace(workspace, need, q.device)
+    ws = _workspace(workspace, need, q.device, stream)
     _check(lib.sparse_mla_attn_partial(ctypes.byref(a), _ptr(idx), K, _ptr(shard_range), _ptr(out), _ptr(lse),
                                        _ptr(ws) if ws is not None else None, need, _stream(stream)),
            "sparse_mla_attn_partial")
@@ -327,7 +350,7 @@ def indexer_k_store(k, tok_seq, tok_pos, k_cache: KVCache, gamma=None, beta=None
 
 def li_topk_sfa(q_idx, w, k_cache: KVCache, q, kv_cache: KVCache, row_seq, row_pos, K: int,
                 max_visible: int, out, lse=None, idx_out=None, q_scale=None, rows_per_group: int = 1,
-                softmax_scale: float = None, workspace=None, stream=None):
+                softmax_scale: Optional[float] = None, workspace=None, stream=None):
     """The whole layer on one stream: scores -> Top-K -> sparse attention."""
     lib = _c.load()
     R, H, D_qk = q.shape
@@ -335,7 +358,7 @@ def li_topk_sfa(q_idx, w, k_cache: KVCache, q, kv_cache: KVCache, row_seq, row_p
     ia = _indexer_args(q_idx, w, k_cache, row_seq, row_pos, max_visible, q_scale, rows_per_group)
     ma = _mla_args(q, kv_cache, row_seq, D_latent, softmax_scale)
     need = lib.lisfa_workspace_size(_c.LISFA_OP_FUSED, R, max_visible, K, H, D_latent)
-    ws = _workspace(workspace, need, q.device)
+    ws = _workspace(workspace, need, q.device, stream)
     _check(lib.li_topk_sfa(ctypes.byref(ia), ctypes.byref(ma), K, _ptr(idx_out), _ptr(out), _ptr(lse),
                            _ptr(ws), need, _stream(stream)), "li_topk_sfa")
     return out, lse

@@ -140,7 +140,9 @@ int check_mla(const lisfa_mla_args* a) {
     if (a->H < 1 || a->H > 128) return LISFA_ERR_UNSUPPORTED;
     if (!((a->D_latent == 512 && a->D_rope == 64) || (a->D_latent == 64 && a->D_rope == 16)))
         return LISFA_ERR_UNSUPPORTED;
-    if (!(a->softmax_scale == a->softmax_scale)) return LISFA_ERR_BAD_SHAPE;
+    // the online softmax raises its running maximum with scale * max(q.k), which
+    // needs a positive, finite scale
+    if (!(a->softmax_scale > 0.f) || !(a->softmax_scale < __builtin_inff())) return LISFA_ERR_BAD_SHAPE;
     if (a->R == 0) return LISFA_OK;
     if (!a->q || !a->row_seq) return LISFA_ERR_NULL_ARG;
     if (!aligned(a->q, 16)) return LISFA_ERR_BAD_SHAPE;
@@ -169,8 +171,12 @@ int64_t fused_chunk_rows(int32_t R, int64_t max_visible) {
     const int64_t ld = scores_ld(max_visible) > 0 ? scores_ld(max_visible) : 64;
     int64_t rc = kScoreScratchCap / (ld * 4);
     if (rc >= R) return R;
-    rc = rc / 8 * 8;
-    return rc < 8 ? 8 : rc;
+    // chunks start on multiples of 16 rows: the indexer forms its row groups
+    // (1, 8 or 16 rows, each dividing the caller's rows_per_group) from the
+    // chunk start, so every group it forms stays inside one of the caller's
+    // aligned groups
+    rc = rc / 16 * 16;
+    return rc < 16 ? 16 : rc;
 }
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }

@@ -803,34 +803,27 @@ hipError_t li_score_dispatch(const IndexerDev& a, int D_I, int dtype, int qg, fl
         if (D_I == 32 && mt == 1) return launch_li_dec<32, 1>(a, scores, ld, max_visible, stream);
     }
     // 16-row groups are built for the 64 x 128 indexer; other shapes take the
-    // 16-aligned group as two 8-row groups
+    // 16-aligned group as two 8-row groups.  What reaches the grouped kernel:
+    // bf16 keys with 8- or 16-row groups, per-token fp8 keys with 8- or 16-row
+    // groups, and per-token fp8 keys with D_I = 32 one row at a time.
     if (qg == 16 && !(D_I == 128 && mt == 4)) qg = 8;
 #define LISFA_LI_CASE(DI_, MT_, QG_, F8_)                                                    \
     if (D_I == DI_ && mt == MT_ && qg == QG_ && (fp8 != 0) == F8_)                            \
         return launch_li<DI_, MT_, QG_, F8_>(a, scores, ld, max_visible, stream);
     LISFA_LI_CASE(128, 4, 16, false)
     LISFA_LI_CASE(128, 4, 16, true)
-    LISFA_LI_CASE(128, 4, 1, false)
     LISFA_LI_CASE(128, 4, 8, false)
-    LISFA_LI_CASE(128, 4, 1, true)
     LISFA_LI_CASE(128, 4, 8, true)
-    LISFA_LI_CASE(128, 2, 1, false)
     LISFA_LI_CASE(128, 2, 8, false)
-    LISFA_LI_CASE(128, 2, 1, true)
     LISFA_LI_CASE(128, 2, 8, true)
-    LISFA_LI_CASE(128, 1, 1, false)
     LISFA_LI_CASE(128, 1, 8, false)
-    LISFA_LI_CASE(128, 1, 1, true)
     LISFA_LI_CASE(128, 1, 8, true)
-    LISFA_LI_CASE(32, 4, 1, false)
     LISFA_LI_CASE(32, 4, 8, false)
     LISFA_LI_CASE(32, 4, 1, true)
     LISFA_LI_CASE(32, 4, 8, true)
-    LISFA_LI_CASE(32, 2, 1, false)
     LISFA_LI_CASE(32, 2, 8, false)
     LISFA_LI_CASE(32, 2, 1, true)
     LISFA_LI_CASE(32, 2, 8, true)
-    LISFA_LI_CASE(32, 1, 1, false)
     LISFA_LI_CASE(32, 1, 8, false)
     LISFA_LI_CASE(32, 1, 1, true)
     LISFA_LI_CASE(32, 1, 8, true)

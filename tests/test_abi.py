@@ -150,6 +150,9 @@ def test_topk_validation(clib):
     (dict(q=None), C.LISFA_ERR_NULL_ARG),
     (dict(kv_cache=_fake_cache(row_stride_bytes=1024)), C.LISFA_ERR_BAD_SHAPE),
     (dict(softmax_scale=float("nan")), C.LISFA_ERR_BAD_SHAPE),
+    (dict(softmax_scale=0.0), C.LISFA_ERR_BAD_SHAPE),
+    (dict(softmax_scale=-0.04), C.LISFA_ERR_BAD_SHAPE),
+    (dict(softmax_scale=float("inf")), C.LISFA_ERR_BAD_SHAPE),
     (dict(kv_cache=_fake_cache(dtype=C.LISFA_MXFP8, row_stride_bytes=1152, scale=16)), C.LISFA_ERR_BAD_DTYPE),
     (dict(kv_cache=_fake_cache(dtype=C.LISFA_FP8_TILE128, row_stride_bytes=576)), C.LISFA_ERR_NULL_ARG),
     (dict(kv_cache=_fake_cache(dtype=C.LISFA_FP8_TILE128, row_stride_bytes=576, scale=18)), C.LISFA_ERR_BAD_SHAPE),

@@ -1,6 +1,7 @@
 """Parity at the workloads' full sizes, in the launch configuration the
 benchmark times (one li_topk_sfa call over the whole batch): the oracle
-recomputes sampled query rows one by one.  Inputs are generated on the GPU
+recomputes query rows one by one, every row of the decode batches and
+spread rows of the 4096-row prefill chunk.  Inputs are generated on the GPU
 (seeded) and copied to the host for the oracle."""
 import numpy as np
 import pytest
@@ -29,9 +30,10 @@ def _run(wl, rows):
     assert np.isfinite(out).all() and np.isfinite(lse).all()
     inp = W.to_numpy(b)
     fp8 = wl.kv_dtype in ("fp8", "fp8_tile128")
+    rows = list(rows)
+    say(f"  oracle over {len(rows)} rows")
     for r in rows:
         r = r % b.R
-        say(f"  oracle row {r} (position {int(inp['row_pos'][r])})")
         o = O.layer_row(inp, r)
         nd = check_index_set(idx[r], o["scores"], o["idx"], wl.K)
         g_out, g_lse = O.attend_row(inp, r, idx[r])
@@ -47,24 +49,28 @@ def test_decode_l8192_full(lib):
 
 
 def test_batched_paged_full(lib):
-    _run(W.CONFIGS[2], [0, 17, 40, 63])
+    _run(W.CONFIGS[2], range(64))
 
 
 def test_prefill_4096q_l65536_full(lib):
-    _run(W.CONFIGS[3], [0, 1, 2047, 4095])
+    _run(W.CONFIGS[3], [0, 1, 15, 16, 1023, 1024, 2047, 2048, 3071, 3072, 4094, 4095])
 
 
 def test_fp8_decode_16x131072_full(lib):
-    _run(W.CONFIGS[4], [0, 15])
+    _run(W.CONFIGS[4], range(16))
 
 
 def test_bench_workload_64x32768_full(lib):
-    _run(W.BENCH["decode_paged_64x32768"], [0, 31, 63])
+    _run(W.BENCH["decode_paged_64x32768"], range(64))
+
+
+def test_bench_workload_1x32768_full(lib):
+    _run(W.BENCH["decode_paged_1x32768"], [0])
 
 
 def test_bench_workload_mxfp8_full(lib):
-    _run(W.BENCH["decode_paged_64x32768_mxfp8"], [0, 63])
+    _run(W.BENCH["decode_paged_64x32768_mxfp8"], range(64))
 
 
 def test_bench_workload_fp8_tile_kv_full(lib):
-    _run(W.BENCH["decode_paged_64x32768_fp8tilekv"], [0, 33, 63])
+    _run(W.BENCH["decode_paged_64x32768_fp8tilekv"], range(64))

@@ -289,6 +289,31 @@ def test_paged_slots_are_a_bijection_onto_non_poisoned_slots():
     assert np.isnan(O.decode_bf16(inp["k_data"][unused])).all()
 
 
+def test_paged_slots_read_back_the_positions_of_a_contiguous_layout():
+    """Position-tagged read-back of the paged slot map.  The generator draws a
+    sequence's values in position order whatever the layout, so the same
+    workload laid out contiguously (slot = base + position, no table) holds the
+    same value at every (sequence, position).  Reading every position back
+    through the paged map must give those values, row for row, for the key
+    cache and the latent cache (a wrong block index, offset or block size
+    would read another position's row)."""
+    base = W.CONFIGS[2].with_(num_seqs=6, len_range=(1, 400), H_I=4, D_I=32, H=8, D_latent=64, D_rope=16,
+                              dist="int8range", block_size=16)
+    paged = W.to_numpy(W.make_batch(base))
+    contig = W.to_numpy(W.make_batch(base.with_(paged=False)))
+    assert paged["seq_lens"] == contig["seq_lens"]
+    assert paged["block_table"] is not None and contig["block_table"] is None
+    for s, L in enumerate(paged["seq_lens"]):
+        pos = np.arange(L)
+        # integer tags: position p of sequence s must hold the row the contiguous
+        # layout keeps at base[s] + p (values are integers, so equality is exact)
+        np.testing.assert_array_equal(O.indexer_keys(paged, s, L), O.indexer_keys(contig, s, L))
+        np.testing.assert_array_equal(O.latent_rows(paged, s, pos), O.latent_rows(contig, s, pos))
+        # and the rows of distinct positions are not all the same (the check has teeth)
+        if L > 1:
+            assert not np.array_equal(O.latent_rows(paged, s, pos[:1]), O.latent_rows(paged, s, pos[1:2]))
+
+
 def test_contiguous_fp8_scale_groups_follow_slots():
     wl = W.CONFIGS[4].with_(num_seqs=2, seq_len=150, H_I=4, D_I=32, H=8,
                             D_latent=64, D_rope=16)
