@@ -9,9 +9,19 @@
 //   z_k = scale * q[r,h,:] . row_k      (row = [latent | rope], D_qk wide)
 //   out[r,h,:] = sum_k softmax(z)_k * row_k[:D_latent],  lse = log sum_k e^{z_k}
 //
-// Work decomposition.  A workgroup owns one query row, 32*NHG heads and a
-// contiguous range of the row's index list (split-K over the list when one
-// row alone cannot fill the chip).  Every gathered latent row is therefore
+// Two kernels compute it:
+//  * sfa_mla_kernel, for 512 + 64 rows (the MLA shape of the layer): 64 heads
+//    per workgroup, eight waves split by role (scores, value products), bf16
+//    MFMA on tiles of 32 gathered rows staged in LDS; fp8 rows are converted
+//    to bf16 exactly and their fp32 factors applied to the logits and
+//    probabilities (see the kernel's comment);
+//  * sfa_kernel, for 64 + 16 rows (the small shape): the four-wave design
+//    below.
+// Split-K over the index list when rows alone cannot fill the chip, with an
+// LSE merge of the parts (sfa_combine_kernel).
+//
+// sfa_kernel.  A workgroup owns one query row, 32*NHG heads and a
+// contiguous range of the row's index list.  Every gathered latent row is
 // read from HBM once per (row, split) and shared by all heads of the
 // workgroup through LDS.  Rows are gathered 32 at a time with direct
 // global->LDS 16-byte loads (no VGPR staging) into a double-buffered, padded
@@ -539,24 +549,8 @@ __global__ __launch_bounds__(128 * NHG) void sfa_kernel(MlaDev a, int kps, int n
     }
 }
 
-// Wide bf16 rows (a whole number of 128-byte groups, e.g. 512 + 64) -----------
-//
-// Same decomposition, softmax and MFMA layouts as sfa_kernel; what differs is
-// how the tile is brought in and how each wave's stream is laid out.
-//
-// Blocked tile layout: the 32 rows of a tile form 4 groups of 8 rows; group g
-// holds NJ = CPK / 8 blocks of 1 KB, block j = chunks [8j, 8j + 8) of the
-// group's rows (128 B per row), chunk slots of row r permuted by XOR
-// sfa_swz(r).  Chunk c of tile row r sits at
-//   (r / 8) * NJ KB + (c / 8) KB + (r % 8) * 128 + ((c % 8) ^ swz(r)) * 16.
-// A wave's load instruction j fills exactly one block: lane l brings chunk
-// 8j + ((l % 8) ^ swz(row)) of row 8 w + l / 8 to block + 16 l.  A thread
-// therefore looks up one cache slot per tile and issues NJ loads that differ
-// only in their immediate offsets.
-//
-// Each wave runs a loop specialised for its half of the QK^T reduction (no
-// divergent branch inside), and the exponentials of tile t are computed
-// between the QK^T MFMAs of tile t + 1, which do not depend on them.
+// Rows that a tile leaves empty (an index of -1, or a position the cache cannot
+// address) are loaded from here.
 __device__ __attribute__((aligned(16))) uint8_t g_zero_row[2048];
 
 // fn(std::integral_constant<int, i>) for i = 0 .. N-1 (immediate operands)
@@ -569,39 +563,103 @@ __device__ __forceinline__ void static_for_impl(F&& fn) {
 }
 template <int N, typename F>
 __device__ __forceinline__ void static_for(F&& fn) { static_for_impl<0, N>(fn); }
+// Chunk permutation of the 512 + 64 tiles: for rows of one parity, swz8 maps
+// (r / 2) % 8 = m to 2 (m % 4) + m / 4, a bijection (16 consecutive rows read
+// at one chunk hit 16 distinct 16-byte bank groups) whose halves m < 4 and
+// m >= 4 give distinct chunk pairs (8 consecutive rows read at two adjacent
+// chunks by a transpose read hit 16 distinct bank groups).
+__device__ __forceinline__ int sfa_swz8(int r) { return (((r >> 1) & 3) << 1) | ((r >> 3) & 1); }
 
-template <int DLAT, int DROPE, int NHG>
-__global__ __launch_bounds__(128 * NHG) void sfa_bf16_kernel(MlaDev a, int kps, int nsplit, int nhb,
-                                                             __bf16* __restrict__ out, float* __restrict__ lse,
-                                                             float* __restrict__ part_o,
-                                                             float* __restrict__ part_lse) {
-    constexpr int DQK = DLAT + DROPE;
-    constexpr int CPK = DQK * 2 / 16;       // 16-byte chunks per row
-    static_assert((DQK * 2) % 128 == 0 && CPK * 16 <= 2048, "rows must be whole 128-byte groups");
-    constexpr int NJ = CPK / 8;             // 1 KB blocks per 8-row group
+// Sparse MLA attention over 512 + 64 latent rows ---------------------------------
+//
+// A workgroup owns one query row, a block of 64 heads and a range of the row's
+// index list.  Tiles of 32 gathered rows sit in LDS as 8-row groups of 1 KB
+// blocks (chunk c of tile row r at (r / 8) * 9 KB + (c / 8) KB + (r % 8) * 128
+// + ((c % 8) ^ swz8(r)) * 16), and the eight waves split the work by role; wave
+// w runs on SIMD w % 4, so every SIMD holds one q-wave and one p-wave, and the
+// PV products of the p-wave keep the matrix core busy while its q-wave runs
+// the softmax:
+//  * q-waves 0..3: q-wave (h, kb) = (w / 2, w % 2) owns heads 32 h .. 32 h + 31
+//    of the block (the query as two 16-head B operands, 144 VGPRs) and keys
+//    16 kb .. 16 kb + 15 of every tile.  For tile t + 1 it computes its
+//    S^T[16 keys, 32 heads] (36 MFMAs of 16x16x32; every key operand read from
+//    LDS feeds both head tiles, so the tile is read once per 32 heads), masks,
+//    takes its per-head maxima and trades them with its partner (the other key
+//    block, on the neighbouring SIMD) through LDS with a flag handshake inside
+//    the period; both then raise the base-2 reference lazily
+//    in the same way (only when the tile's maximum exceeds it by 2^8), and each
+//    writes its half of P^T into a two-slot LDS ring in the PV B-operand layout
+//    (lane = head, K-slots 8 g .. 8 g + 7 = keys 4 g + i and 16 + 4 g + i), the
+//    key block 0 wave with a raise flag and factors per head tile.  Each keeps
+//    the partial row sums of its keys.
+//  * p-waves 4..7: p-wave c = w - 4 owns value columns
+//    128 c .. 128 c + 127 of the 64 heads (O^T in 128 VGPRs): it applies the
+//    raise factors of flagged head tiles and runs PV of tile t (32 MFMAs), the
+//    value operand from transposed LDS reads in the P^T operand's key order.
+//    The p-waves also bring the tiles, p-wave c rows 8 c .. 8 c + 7.  bf16
+//    rows: direct global->LDS loads NBUF - 2 tiles ahead, issued from inline
+//    assembly (lds_dma) and ordered by explicit vmcnt waits and the tile
+//    barrier; the first tiles go out before the slot table is complete.  fp8
+//    rows: e4m3 codes two tiles ahead into registers, converted exactly to
+//    bf16 (v_cvt_scalef32_pk_bf16_fp8 with scale 1) into the tile, the rows'
+//    fp32 factors beside it (NBUF = 3).
+// MFMA cycles per tile on every SIMD: 576 (QK^T) + 512 (PV).  One barrier per
+// tile hands P over; the roles run separate loops with the same number of
+// barriers.
+//
+// fp8 factors are applied exactly, never folded into the bf16 rows:
+//  KVF 1 (one factor f per row):  z = scale * f * (q . code), and the P^T
+//        operand is p * f (the normaliser sums p);
+//  KVF 2 (one factor per 128-column tile j of the row): the QK^T K-steps of
+//        each column tile accumulate apart and are added with the row's f_j;
+//        p-wave c, whose value columns are column tile c, multiplies its P^T
+//        operand by f_c.
+//
+// Outputs: nsplit == 1: bf16 out (+ lse) or, with out == nullptr, normalised
+// fp32 out_f32 + lse; nsplit > 1: normalised bf16 partials part_o [R, nsplit,
+// H, 512] + part_lse [R, nsplit, H] for the combine kernel.
+template <int NBUF, int MAXK, int KVF>
+__global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsplit, int nhb,
+                                                       __bf16* __restrict__ out, float* __restrict__ lse,
+                                                       float* __restrict__ out_f32, __bf16* __restrict__ part_o,
+                                                       float* __restrict__ part_lse) {
+    constexpr int DLAT = 512, DQK = 576;
+    constexpr int CPK = DQK * 2 / 16;       // 16-byte chunks per row (72)
+    constexpr int NJ = CPK / 8;             // 1 KB blocks per 8-row group (9)
     constexpr int GB = NJ * 1024;           // bytes per 8-row group
     constexpr int TROWS = 32;
     constexpr int TB = (TROWS / 8) * GB;    // bytes per tile
-    constexpr int NBUF = 3;                 // tile ring: PV(t) | QK(t+1) | loading t+2
-    constexpr int NT = 128 * NHG;
-    constexpr int RPP = NT / 8;             // tile rows loaded per pass
-    constexpr int NPASS = TROWS / RPP;
-    constexpr int KS = DQK / 16;            // QK K-steps
-    static_assert(KS % 2 == 0, "even K-step count");
-    constexpr int NKS = KS / 2;             // K-steps per wave
-    constexpr int DVH = DLAT / 2;           // value columns per wave
-    constexpr int MTV = DVH / 32;           // PV M-tiles per wave
-    static_assert(DVH % 64 == 0, "shape");
+    constexpr int NQT = 256;                // threads of the q-waves 0..3 (they build the slot table)
+    constexpr int KS = DQK / 32;            // 16x16x32 K-steps of a row (18)
+    constexpr int DVP = DLAT / 4;           // value columns per p-wave
+    constexpr int MTP = DVP / 16;           // PV M-tiles per p-wave
+    constexpr int NTL = KVF == 2 ? (DQK + 127) / 128 : 1;   // fp8 factors per row
+    constexpr int LA = NBUF - 2;            // tiles in flight ahead of QK^T
+    static_assert(NBUF >= 3 && (KVF == 0 || NBUF == 3), "PV(t) | QK(t+1) | tiles t+2 ..");
+    static_assert(MAXK % NQT == 0, "whole rounds of index entries");
+    typedef float f32x4v __attribute__((ext_vector_type(4)));
+    typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
 
     __shared__ __attribute__((aligned(1024))) uint8_t tile[NBUF * TB];
-    __shared__ uint32_t rslot[kSfaMaxKeys];            // cache slot of each selected row, ~0 = skip
-    __shared__ uint32_t vmask[kSfaMaxKeys / 32];       // valid-row bits of each 32-row tile
-    __shared__ __attribute__((aligned(16))) float xbuf[2][NHG * 2 * 1024];
+    __shared__ uint32_t rslot[MAXK];                    // cache slot of each selected row, ~0 = skip
+    __shared__ uint32_t vmask[MAXK / 32];               // valid-row bits of each 32-row tile
+    __shared__ __attribute__((aligned(16))) float kvf[KVF ? NBUF * NTL * TROWS : 4];   // [buf][tile j][row]
+    __shared__ __attribute__((aligned(16))) uint8_t pbuf[2][4][64 * 16];   // P^T [slot][head tile][lane]
+    __shared__ float alph[2][64];                       // raise factors [slot][head]
+    __shared__ int rflag[2][4];                         // raised head tiles [slot][head tile]
+    __shared__ float xmax[2][2][32];                    // per-head tile maxima [head half][key block][head]
+    __shared__ int xflag[2][2];                         // tiles whose maxima are in xmax
+    __shared__ int s_ntiles;
+    // after the last tile the P ring is free: partial row sums [head half][key
+    // block][head] and the references [head half][head]
+    float* const fin_l = (float*)&pbuf[0][0][0];
+    float* const fin_m = fin_l + 128;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int hg = wave >> 1;
     const int bid = blockIdx.x;
+    // the head blocks of one (row, split) get workgroup ids 8 apart: they run on
+    // one XCD and share its L2 for the rows they both gather
     const int hb = (bid >> 3) % nhb;
     const int u = ((bid >> 3) / nhb) * 8 + (bid & 7);
     if (u >= a.R * nsplit) return;
@@ -611,647 +669,336 @@ __global__ __launch_bounds__(128 * NHG) void sfa_bf16_kernel(MlaDev a, int kps, 
     const int nk = k1 - k0;
     const int seq = a.row_seq[r];
     const int nt_fill = (nk + TROWS - 1) / TROWS;
-    __shared__ int s_ntiles;
+    const bool is_q = wave < 4;
     if (tid == 0) s_ntiles = 1;
-
-    for (int i0 = 0; i0 < nt_fill * TROWS; i0 += NT) {
-        const int i = i0 + tid;
-        int64_t s = -1;
-        if (i < nk) {
-            const int p = a.idx[(int64_t)r * a.K + k0 + i];
-            s = p >= 0 ? slot_of(a.kv, seq, p) : -1;
-        }
-        if (i < nt_fill * TROWS) rslot[i] = s >= 0 ? (uint32_t)s : 0xFFFFFFFFu;
-        const uint64_t bal = __ballot(s >= 0);
-        if (lane == 0 && i < nt_fill * TROWS) {
-            vmask[i / 32] = (uint32_t)bal;
-            if (i + 32 < nt_fill * TROWS) vmask[i / 32 + 1] = (uint32_t)(bal >> 32);
-        }
-    }
-    __syncthreads();
-    // trailing tiles without a valid row are skipped; at least one tile is
-    // always processed (an empty tile contributes nothing)
-    for (int t = tid; t < nt_fill; t += NT)
-        if (vmask[t] != 0u) atomicMax(&s_ntiles, t + 1);
-    __syncthreads();
-    const int ntiles = s_ntiles;
+    if (tid < 4) xflag[tid >> 1][tid & 1] = 0;
 
     const lds_u8* tile0 = (const lds_u8*)tile;
     const uint32_t tile_lds = (uint32_t)(uintptr_t)tile;
-    // loads: this thread's row within a pass and its chunk permutation
-    const int lrow = tid >> 3;
-    const uint32_t goff = (uint32_t)(((tid & 7) ^ sfa_swz(lrow)) << 4);  // swz(lrow) == swz(lrow + 16)
-    // slots of this thread's rows of tile t (read one iteration ahead of use)
-    auto read_slots = [&](int t, uint32_t (&sl)[NPASS]) {
-#pragma unroll
-        for (int p = 0; p < NPASS; ++p) sl[p] = rslot[(t < ntiles ? t : 0) * TROWS + p * RPP + lrow];
+    const int g = lane >> 4, l16 = lane & 15;
+    const int pc = wave - 4;                            // p-waves 4..7 -> value column block
+    // bf16 tile loads of a p-wave: lane l brings chunk 8 j + ((l % 8) ^ swz8(row))
+    // of row 8 pc + l / 8 into block j of the row group, at block + 16 l
+    const uint32_t goff = (uint32_t)(((lane & 7) ^ sfa_swz8(8 * pc + (lane >> 3))) << 4);
+    auto issue_rows = [&](uint32_t s, int buf) {        // one tile's row of this lane
+        const uint8_t* gp = (s != 0xFFFFFFFFu ? a.kv.data + (uint64_t)s * (uint32_t)a.kv.row_stride : g_zero_row) + goff;
+        const uint32_t blk = tile_lds + (uint32_t)(buf * TB + pc * GB);
+        static_for<NJ>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            // the immediate offset moves both the global and the LDS address;
+            // block j lands at blk + j KB
+            lds_dma<16, j * 128>(gp, blk + (uint32_t)(j * (1024 - 128)));
+        });
     };
-    auto issue_tile = [&](const uint32_t (&sl)[NPASS], int buf) {
+
+    if (is_q) {
+        // the q-waves build the slot table: every index load of the thread first,
+        // then every block-table lookup (two dependent global round trips)
+        constexpr int EPT = MAXK / NQT;
+        const int qt = tid;                             // 0 .. 255
+        int pidx[EPT];
 #pragma unroll
-        for (int p = 0; p < NPASS; ++p) {
-            const uint32_t s = sl[p];
-            const uint8_t* g = (s != 0xFFFFFFFFu ? a.kv.data + (uint64_t)s * (uint32_t)a.kv.row_stride : g_zero_row) + goff;
-            const uint32_t blk = tile_lds + (uint32_t)(buf * TB + (p * (RPP / 8) + wave) * GB);
-            static_for<NJ>([&](auto jc) {
-                constexpr int j = decltype(jc)::value;
-                // the immediate offset moves both the global and the LDS address;
-                // block j lands at blk + j KB
-                lds_dma<16, j * 128>(g, blk + (uint32_t)(j * (1024 - 128)));
-            });
+        for (int j = 0; j < EPT; ++j) {
+            const int i = j * NQT + qt;
+            pidx[j] = i < nk ? a.idx[(int64_t)r * a.K + k0 + i] : -1;
         }
-    };
-    auto body = [&](auto dh_c) {
-        constexpr int DH = decltype(dh_c)::value;
-        constexpr int KSB = DH * NKS;
-        const int head = hb * 32 * NHG + hg * 32 + (lane & 31);
-        bf16x8 qb[NKS];
+        int64_t sv[EPT];
 #pragma unroll
-        for (int j = 0; j < NKS; ++j) {
-            if (head < a.H)
-                qb[j] = *(const bf16x8*)(a.q + (((int64_t)r * a.H + head) * DQK + (KSB + j) * 16 + (lane >> 5) * 8) * 2);
-            else
-                qb[j] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-        }
-        // QK operand: lane = key row krow, 8 values of chunk 2 ks + lane / 32
-        const int krow = lane & 31;
-        uint32_t qkb[4];
+        for (int j = 0; j < EPT; ++j) sv[j] = pidx[j] >= 0 ? slot_of(a.kv, seq, pidx[j]) : -1;
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
-            qkb[m] = (uint32_t)((krow >> 3) * GB + (krow & 7) * 128 + ((((2 * m) + (lane >> 5)) ^ sfa_swz(krow)) << 4));
-        auto qk_op = [&](const lds_u8* T, int ks) -> bf16x8 {   // ks: compile-time after unrolling
-            return *(const lds_bf16x8*)(T + qkb[ks & 3] + (ks >> 2) * 1024);
-        };
-        // PV operand (transpose reads): 16-lane group g16 reads rows 8 j + trow
-        // of each 16-key half, at 4 consecutive value columns per lane
-        const int g16 = lane >> 4, i16 = lane & 15;
-        const int trow = 4 * (g16 >> 1) + (i16 >> 2);
-        uint32_t pvb[2][2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int par = 0; par < 2; ++par) {
-                const int cc = 4 * par + 2 * (g16 & 1) + ((i16 & 3) >> 1);
-                pvb[j][par] = (uint32_t)(j * GB + trow * 128 + ((cc ^ sfa_swz(8 * j + trow)) << 4) + 8 * (i16 & 1));
-            }
-        typedef short s16x4 __attribute__((ext_vector_type(4)));
-        typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-        auto trd = [&](const lds_u8* T, int mt, int kk, int j) -> s16x4 {
-            return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4*)(T + pvb[j][mt & 1] + kk * 2 * GB + (4 * DH + (mt >> 1)) * 1024));
-        };
-        auto qk = [&](const lds_u8* T) {
-            f32x16 s;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) s[i] = 0.f;
-            constexpr int PF = 4;
-            bf16x8 buf[PF];
-#pragma unroll
-            for (int j = 0; j < PF; ++j) buf[j] = qk_op(T, KSB + j);
-#pragma unroll
-            for (int j = 0; j < NKS; ++j) {
-                const bf16x8 av = buf[j % PF];
-                if (j + PF < NKS) buf[j % PF] = qk_op(T, KSB + j + PF);
-                s = mfma32x32x16_bf16(av, qb[j], s);
-            }
-            return s;
-        };
-        auto put_partial = [&](const f32x16& s, int xb) {
-            float* xs = xbuf[xb] + (hg * 2 + DH) * 1024 + lane * 4;
-#pragma unroll
-            for (int i = 0; i < 16; i += 4) *(f32x4*)(xs + i * 64) = f32x4{s[i], s[i + 1], s[i + 2], s[i + 3]};
-        };
-
-        f32x16 o[MTV];
-#pragma unroll
-        for (int mt = 0; mt < MTV; ++mt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) o[mt][i] = 0.f;
-        float m2 = -__builtin_inff(), lsum = 0.f;
-        const float c = a.scale_log2;
-        f32x16 s_cur;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s_cur[i] = 0.f;
-
-        uint32_t sl[NPASS];
-        if (ntiles > 0) {
-            read_slots(0, sl);
-            issue_tile(sl, 0);
-        }
-        if (ntiles > 1) {
-            read_slots(1, sl);
-            issue_tile(sl, 1);
-        }
-        read_slots(2, sl);
-        if (ntiles > 0) {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __syncthreads();
-            s_cur = qk(tile0);
-            put_partial(s_cur, 0);
-        }
-
-        int bcur = 0;
-        for (int t = 0; t < ntiles; ++t) {
-            const int bnext = bcur == NBUF - 1 ? 0 : bcur + 1;
-            const int bnext2 = bnext == NBUF - 1 ? 0 : bnext + 1;
-            // tile t+1 landed; tile t-1's buffer is free; partials of tile t published
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __syncthreads();
-            const lds_u8* T = tile0 + bcur * TB;
-            const lds_u8* Tn = tile0 + bnext * TB;
-            constexpr int PF = 4;   // QK^T operand reads in flight
-            constexpr int PD = 2;   // PV: M-tiles of operands in flight
-
-            // every LDS read this step needs first is issued here, ahead of
-            // the loads of tile t+2, so a single wait covers them
-            f32x4 xr[4];
-            {
-                const float* xp = xbuf[t & 1] + (hg * 2 + (DH ^ 1)) * 1024 + lane * 4;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) xr[i] = *(const f32x4*)(xp + i * 256);
-            }
-            const uint32_t vmr = vmask[t];
-            bf16x8 buf[PF];
-#pragma unroll
-            for (int j = 0; j < PF; ++j) buf[j] = qk_op(Tn, KSB + j);
-            if (t + 2 < ntiles) issue_tile(sl, bnext2);
-            read_slots(t + 3, sl);
-            __builtin_amdgcn_sched_barrier(0);
-
-            // raw logits of tile t = own partial + partner's partial
-            f32x16 s = s_cur;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                s[4 * i] += xr[i].x;
-                s[4 * i + 1] += xr[i].y;
-                s[4 * i + 2] += xr[i].z;
-                s[4 * i + 3] += xr[i].w;
-            }
-            const uint32_t vm = __builtin_amdgcn_readfirstlane(vmr);
-            if (vm != 0xFFFFFFFFu) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-                    if (!((vm >> key) & 1u)) s[i] = -__builtin_inff();
-                }
-            }
-            // tile maximum of each head (both lane halves), in log2 units
-            float tmax = fmaxf(fmaxf(s[0], s[1]), s[2]);
-#pragma unroll
-            for (int i = 3; i < 15; i += 2) tmax = fmaxf(fmaxf(tmax, s[i]), s[i + 1]);
-            tmax = fmaxf(tmax, s[15]);
-            {
-                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
-                tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-            }
-            tmax *= c;   // c > 0
-            // lazy reference maximum (raised only past kLazy log2 units)
-            constexpr float kLazy = 8.0f;
-            const bool raise = tmax > m2 + kLazy;   // also true on the first valid tile
-            if (__ballot(raise) != 0ull) {
-                const float mnew = raise ? tmax : m2;
-                const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);  // m2 = -inf -> 0
-                lsum *= alpha;
-#pragma unroll
-                for (int mt = 0; mt < MTV; ++mt)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) o[mt][i] *= alpha;
-                m2 = mnew;
-            }
-            // a head with no valid row so far keeps m2 = -inf: its (masked)
-            // probabilities must come out 0, not NaN
-            const float negm = m2 == -__builtin_inff() ? 0.f : -m2;
-
-            // Phase 1: QK^T of tile t+1 (independent of this tile's softmax)
-            // with the exponentials of tile t between its MFMAs; operand reads
-            // run PF K-steps ahead.
-            s16x4 rb[PD + 1][4];
-            f32x16 s_next;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) s_next[i] = 0.f;
-            float pe[16];
-            {
-#pragma unroll
-                for (int j = 0; j < NKS; ++j) {
-                    const bf16x8 av = buf[j % PF];
-                    if (j + PF < NKS) buf[j % PF] = qk_op(Tn, KSB + j + PF);
-                    s_next = mfma32x32x16_bf16(av, qb[j], s_next);
-                    if (j < 16) pe[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], c, negm));
-                }
-            }
-            float rs = 0.f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) rs += pe[i];
-            {
-                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(rs), __float_as_uint(rs), false, false);
-                rs = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-            }
-            lsum += rs;
-            bf16x8 pb[2];
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) pb[kk][e] = (__bf16)pe[8 * kk + e];
-#pragma unroll
-            for (int j = 0; j < NKS; ++j) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (j + PF < NKS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int m = 0; m < PD; ++m)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) rb[m][q] = trd(T, m, q >> 1, q & 1);
-
-            // Phase 2, PV(t): O^T[32 value columns x 32 heads] += V^T[32 x 16
-            // keys] * P^T.  Keys of K-step kk for lane half h: 16 kk + 4 h +
-            // {0..3} (operand elements 0..3) and 16 kk + 8 + 4 h + {0..3}
-            // (elements 4..7): the keys of S^T accumulator registers 8 kk ..
-            // 8 kk + 7.  Transpose reads run PD M-tiles ahead.
-#pragma unroll
-            for (int mt = 0; mt < MTV; ++mt) {
-                if (mt + PD < MTV) {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) rb[(mt + PD) % (PD + 1)][q] = trd(T, mt + PD, q >> 1, q & 1);
-                }
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    const u32x2 lo = __builtin_bit_cast(u32x2, rb[mt % (PD + 1)][2 * kk]);
-                    const u32x2 hi = __builtin_bit_cast(u32x2, rb[mt % (PD + 1)][2 * kk + 1]);
-                    const u32x4 w = {lo.x, lo.y, hi.x, hi.y};
-                    o[mt] = mfma32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pb[kk], o[mt]);
-                }
-            }
-            put_partial(s_next, (t + 1) & 1);
-            __builtin_amdgcn_sched_group_barrier(0x100, 4 * PD, 0);
-#pragma unroll
-            for (int mt = 0; mt < MTV; ++mt) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-                if (mt + PD < MTV) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x200, 4, 0);
-            __builtin_amdgcn_sched_barrier(0);
-            s_cur = s_next;
-            bcur = bnext;
-        }
-
-        // epilogue: normalise and store.  O^T layout: lane = head; accumulator
-        // register i of M-tile m is value column 32 m + 8 (i / 4) + 4 h + i % 4.
-        if (head < a.H) {
-            const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-            const float l_nat = lsum > 0.f ? (m2 + log2f(lsum)) * kLn2 : -__builtin_inff();
-            if (nsplit == 1 && out != nullptr) {
-                __bf16* orow = out + ((int64_t)r * a.H + head) * DLAT;
-#pragma unroll
-                for (int mt = 0; mt < MTV; ++mt)
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        const int col = DH * DVH + mt * 32 + 8 * q4 + 4 * (lane >> 5);
-                        bf16x4 v;
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) v[j] = (__bf16)(o[mt][4 * q4 + j] * inv);
-                        *(bf16x4*)(orow + col) = v;
-                    }
-                if (lse != nullptr && DH == 0 && lane < 32) lse[(int64_t)r * a.H + head] = l_nat;
-            } else {
-                float* prow = part_o + (((int64_t)r * nsplit + sp) * a.H + head) * DLAT;
-#pragma unroll
-                for (int mt = 0; mt < MTV; ++mt)
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        const int col = DH * DVH + mt * 32 + 8 * q4 + 4 * (lane >> 5);
-                        *(f32x4*)(prow + col) = f32x4{o[mt][4 * q4] * inv, o[mt][4 * q4 + 1] * inv,
-                                                      o[mt][4 * q4 + 2] * inv, o[mt][4 * q4 + 3] * inv};
-                    }
-                if (DH == 0 && lane < 32) part_lse[((int64_t)r * nsplit + sp) * a.H + head] = l_nat;
+        for (int j = 0; j < EPT; ++j) {
+            const int i = j * NQT + qt;
+            if (i < nt_fill * TROWS) rslot[i] = sv[j] >= 0 ? (uint32_t)sv[j] : 0xFFFFFFFFu;
+            const uint64_t bal = __ballot(sv[j] >= 0);
+            if (lane == 0 && i < nt_fill * TROWS) {
+                vmask[i / 32] = (uint32_t)bal;
+                if (i + 32 < nt_fill * TROWS) vmask[i / 32 + 1] = (uint32_t)(bal >> 32);
             }
         }
-    };
-    if (wave & 1) body(std::integral_constant<int, 1>{});
-    else body(std::integral_constant<int, 0>{});
-}
-
-// Chunk permutation of the warp-specialised kernel: for rows of one parity,
-// swz8 maps (r / 2) % 8 = m to 2 (m % 4) + m / 4, a bijection (16 consecutive
-// rows read at one chunk hit 16 distinct 16-byte bank groups) whose halves
-// m < 4 and m >= 4 give distinct chunk pairs (8 consecutive rows read at two
-// adjacent chunks by a transpose read hit 16 distinct bank groups).
-__device__ __forceinline__ int sfa_swz8(int r) { return (((r >> 1) & 3) << 1) | ((r >> 3) & 1); }
-
-// Warp-specialised eight-wave kernel for 64 heads of 512 + 64 bf16 rows ---------
-//
-// Tiles of 32 gathered rows in 8-row groups of 1 KB blocks (chunk permutation
-// sfa_swz8), a lazy online softmax (the reference maximum is raised only when a
-// tile exceeds it by 2^8), and the waves split the work by kind:
-//  * q-waves 0..3: wave w owns heads 16 w .. 16 w + 15 of the block over all
-//    576 QK columns (query in 72 VGPRs): S^T of tile t+1 (36 MFMAs), masking,
-//    tile maximum, lazy reference raise and exponentials; it writes P^T to an
-//    LDS ring in the PV B-operand's lane layout (lane = head, K-slots 8 g ..
-//    8 g + 7 = keys 16 kb + 4 g + i), with a per-tile raise flag and factors.
-//  * p-waves 4..7: wave 4 + c owns value columns 128 c .. 128 c + 127 of all
-//    64 heads (O^T in 128 accumulator VGPRs): applies the raise factors of the
-//    flagged head tiles and runs PV of tile t (32 MFMAs), the value operand
-//    from transpose reads of 4 consecutive rows at 4 value columns per lane
-//    (the P^T operand's key order).  The p-waves also issue the
-//    direct-to-LDS tile loads, NBUF - 2 tiles ahead, from inline assembly
-//    (lds_dma): hidden from the compiler's wait-count model, they no longer
-//    turn every LDS operand wait of the issuing wave into a full drain; explicit
-//    vmcnt waits and the per-tile barrier order them instead.
-// Waves w and w + 4 share a SIMD, so QK^T + softmax of tile t+1 and PV of tile
-// t overlap; one barrier per tile hands P over.  The two roles run separate
-// loops with the same number of barriers, so their registers do not add up.
-template <int DLAT, int DROPE, int NBUF, int MAXK, int KVF = 0>
-__global__ __launch_bounds__(512) void sfa_ws_kernel(MlaDev a, int kps, int nsplit, int nhb,
-                                                      __bf16* __restrict__ out, float* __restrict__ lse,
-                                                      float* __restrict__ part_o, float* __restrict__ part_lse) {
-    constexpr int DQK = DLAT + DROPE;
-    constexpr int CPK = DQK * 2 / 16;       // 16-byte chunks per row
-    static_assert((DQK * 2) % 128 == 0 && CPK * 16 <= 2048, "rows must be whole 128-byte groups");
-    constexpr int NJ = CPK / 8;             // 1 KB blocks per 8-row group
-    constexpr int GB = NJ * 1024;           // bytes per 8-row group
-    constexpr int TROWS = 32;
-    constexpr int TB = (TROWS / 8) * GB;    // bytes per tile
-    static_assert(NBUF >= 3, "PV(t) | QK(t+1) | tiles t+2 .. in flight");
-    constexpr int NT = 512;
-    constexpr int KS = DQK / 32;            // 16x16x32 K-steps of a row
-    constexpr int DVP = DLAT / 4;           // value columns per p-wave
-    constexpr int MTP = DVP / 16;           // PV M-tiles per p-wave
-    static_assert(DVP % 64 == 0, "whole 1 KB blocks per p-wave");
-    typedef float f32x4v __attribute__((ext_vector_type(4)));
-
-    // KVF (cached rows): 0 bf16; 1 e4m3 with one factor per row (group); 2 e4m3
-    // with one factor per 128-column tile.  fp8 rows are turned into bf16 rows
-    // of the same tile layout by the loading waves, so the QK and PV code is the
-    // same for every format.
-    constexpr int NTL = KVF == 2 ? (DQK + 127) / 128 : 1;     // factors per row
-    static_assert(KVF == 0 || (DQK % 128 == 0 || (DQK - DQK / 128 * 128) % 64 == 0),
-                  "fp8 rows: 1 KB blocks never straddle a factor tile");
-    __shared__ __attribute__((aligned(1024))) uint8_t tile[NBUF * TB];
-    __shared__ uint32_t rslot[MAXK];                   // cache slot of each selected row, ~0 = skip
-    __shared__ float kvf[KVF ? NTL * MAXK : 1];        // fp8 factors [tile][row] (0 for skipped rows)
-    __shared__ uint32_t vmask[MAXK / 32];              // valid-row bits of each 32-row tile
-    __shared__ __attribute__((aligned(16))) uint8_t pbuf[2][4][64 * 16];   // P^T operands [slot][head tile][lane]
-    __shared__ float alph[2][64];                      // raise factors [slot][head]
-    __shared__ int rflag[2][4];                        // raised head tiles [slot][head tile]
-    float* const fin_l = (float*)&pbuf[0][0][0];       // softmax totals after the last tile (the P ring is
-                                                       // free by then)
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int bid = blockIdx.x;
-    const int hb = (bid >> 3) % nhb;
-    const int u = ((bid >> 3) / nhb) * 8 + (bid & 7);
-    if (u >= a.R * nsplit) return;
-    const int r = u / nsplit, sp = u % nsplit;
-    const int k0 = sp * kps;
-    const int k1 = (k0 + kps < a.K) ? k0 + kps : a.K;
-    const int nk = k1 - k0;
-    const int seq = a.row_seq[r];
-    const int nt_fill = (nk + TROWS - 1) / TROWS;
-    __shared__ int s_ntiles;
-    if (tid == 0) s_ntiles = 1;
-
-    // every index load of the thread first, then every block-table lookup, so
-    // the slots cost two dependent global round trips in all
-    constexpr int EPT = MAXK / NT;          // index entries per thread
-    static_assert(MAXK % NT == 0, "whole rounds");
-    int pidx[EPT];
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) {
-        const int i = j * NT + tid;
-        pidx[j] = i < nk ? a.idx[(int64_t)r * a.K + k0 + i] : -1;
-    }
-    int64_t sv[EPT];
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) sv[j] = pidx[j] >= 0 ? slot_of(a.kv, seq, pidx[j]) : -1;
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) {
-        const int i = j * NT + tid;
-        if (i < nt_fill * TROWS) rslot[i] = sv[j] >= 0 ? (uint32_t)sv[j] : 0xFFFFFFFFu;
-        if constexpr (KVF == 1) {
-            if (i < nt_fill * TROWS) kvf[i] = sv[j] >= 0 ? a.kv.scale[sv[j] / a.kv.scale_group] : 0.f;
-        } else if constexpr (KVF == 2) {
-            if (i < nt_fill * TROWS) {
-#pragma unroll
-                for (int q = 0; q < NTL; ++q) kvf[q * MAXK + i] = sv[j] >= 0 ? a.kv.scale[sv[j] * NTL + q] : 0.f;
-            }
+    } else if constexpr (KVF == 0) {
+        // p-waves: the slots of their rows of tiles 0 .. LA, looked up directly, so
+        // the first tile loads go out while the table is still being built
+        int32_t es = -1;                                // lane 8 t + k: row 8 pc + k of tile t
+        {
+            const int t = lane >> 3, i = t * TROWS + 8 * pc + (lane & 7);
+            const int p = (t <= LA && i < nk) ? a.idx[(int64_t)r * a.K + k0 + i] : -1;
+            const int64_t sl = p >= 0 ? slot_of(a.kv, seq, p) : -1;
+            es = sl >= 0 ? (int32_t)(uint32_t)sl : -1;
         }
-        const uint64_t bal = __ballot(sv[j] >= 0);
-        if (lane == 0 && i < nt_fill * TROWS) {
-            vmask[i / 32] = (uint32_t)bal;
-            if (i + 32 < nt_fill * TROWS) vmask[i / 32 + 1] = (uint32_t)(bal >> 32);
+#pragma unroll
+        for (int t = 0; t <= LA; ++t) {
+            const uint32_t s = (uint32_t)__shfl(es, 8 * t + (lane >> 3));
+            if (t < nt_fill) issue_rows(s, t);
         }
     }
     __syncthreads();
     // trailing tiles without a valid row are skipped; at least one tile is
     // always processed (an empty tile contributes nothing)
-    for (int t = tid; t < nt_fill; t += NT)
+    for (int t = tid; t < nt_fill; t += 512)
         if (vmask[t] != 0u) atomicMax(&s_ntiles, t + 1);
     __syncthreads();
     const int ntiles = s_ntiles;
-
-    const lds_u8* tile0 = (const lds_u8*)tile;
-    const int g = lane >> 4, l16 = lane & 15;
     const float kLazy = 8.0f;
 
-    if (wave < 4) {
+    if (is_q) {
         // ---------------------------------------------------------------- q-wave
-        const int hq = wave;
-        const int head = hb * 64 + hq * 16 + l16;
-        // the query in B-operand layout: lane = head, 8 consecutive d of K-step ks
-        bf16x8 qb[KS];
+        const int qh = wave >> 1, kb = wave & 1;
+        // the query in B-operand layout: lane = head, 8 consecutive columns of K-step ks
+        bf16x8 qb[2][KS];
 #pragma unroll
-        for (int j = 0; j < KS; ++j) {
-            if (head < a.H)
-                qb[j] = *(const bf16x8*)(a.q + (((int64_t)r * a.H + head) * DQK + j * 32 + g * 8) * 2);
-            else
-                qb[j] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+        for (int ht = 0; ht < 2; ++ht) {
+            const int head = hb * 64 + qh * 32 + ht * 16 + l16;
+#pragma unroll
+            for (int j = 0; j < KS; ++j) {
+                if (head < a.H)
+                    qb[ht][j] = *(const bf16x8*)(a.q + (((int64_t)r * a.H + head) * DQK + j * 32 + g * 8) * 2);
+                else
+                    qb[ht][j] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+            }
         }
-        // QK operand of key block kb, K-step ks: row 16 kb + l16, chunk 4 ks + g
+        // key operand of K-step ks: row 16 kb + l16, chunk 4 ks + g (swz8 of the
+        // row does not depend on kb)
         uint32_t qa[2];
 #pragma unroll
         for (int par = 0; par < 2; ++par)
-            qa[par] = (uint32_t)((l16 >> 3) * GB + (l16 & 7) * 128 + (((4 * par + g) ^ sfa_swz8(l16)) << 4));
-        auto qk_op = [&](const lds_u8* T, int kb, int ks) -> bf16x8 {   // compile-time kb, ks
-            return *(const lds_bf16x8*)(T + qa[ks & 1] + kb * 2 * GB + (ks >> 1) * 1024);
+            qa[par] = (uint32_t)(kb * 2 * GB + (l16 >> 3) * GB + (l16 & 7) * 128 +
+                                 (((4 * par + g) ^ sfa_swz8(l16)) << 4));
+        auto qk_op = [&](const lds_u8* T, int ks) -> bf16x8 {   // compile-time ks
+            return *(const lds_bf16x8*)(T + qa[ks & 1] + (ks >> 1) * 1024);
         };
-        float m2 = -__builtin_inff(), lsum = 0.f;
+        float m2[2] = {-__builtin_inff(), -__builtin_inff()}, lsum[2] = {0.f, 0.f};
         const float c = a.scale_log2;
 
-        // S^T of one tile, softmax statistics, P^T to LDS slot ps
-        auto q_tile = [&](const lds_u8* T, uint32_t vm, int ps) {
-            f32x4v s[2] = {f32x4v{0.f, 0.f, 0.f, 0.f}, f32x4v{0.f, 0.f, 0.f, 0.f}};
-            // operand reads in batches of PB, software-pipelined: the reads of
-            // batch b + 1 go out before the MFMAs of batch b, so 6 .. 12 reads
-            // are in flight while the MFMAs run (the scheduling barriers keep the
-            // compiler from pairing each read with its MFMA)
-            constexpr int PB = 6;
-            constexpr int NB = (2 * KS) / PB;
-            static_assert((2 * KS) % PB == 0, "whole batches");
-            bf16x8 av[2][PB];
+        // S^T of this wave's keys of one tile for both head tiles, the maxima
+        // trade, softmax statistics, this key block's half of P^T to LDS slot ps
+        auto q_tile = [&](const lds_u8* T, int buf, uint32_t vm, int ps, int seqno) {
+            f32x4v s[2] = {f32x4v{0.f, 0.f, 0.f, 0.f}, f32x4v{0.f, 0.f, 0.f, 0.f}};   // [head tile]
+            // operand reads in batches of KPB K-steps, software-pipelined: the
+            // reads of batch b + 1 go out before the MFMAs of batch b (the
+            // scheduling barriers keep the compiler from pairing each read with
+            // its MFMAs)
+            constexpr int KPB = KVF == 2 ? 2 : 6;
+            constexpr int NB = KS / KPB;
+            static_assert(KS % KPB == 0, "whole batches");
+            bf16x8 av[2][KPB];
 #pragma unroll
-            for (int j = 0; j < PB; ++j) av[0][j] = qk_op(T, j & 1, j >> 1);
-            static_for<NB>([&](auto bc) {
-                constexpr int b = decltype(bc)::value;
-                if constexpr (b + 1 < NB) {
+            for (int j = 0; j < KPB; ++j) av[0][j] = qk_op(T, j);
+            if constexpr (KVF != 2) {
+                static_for<NB>([&](auto bc) {
+                    constexpr int b = decltype(bc)::value;
+                    if constexpr (b + 1 < NB) {
 #pragma unroll
-                    for (int j = 0; j < PB; ++j)
-                        av[(b + 1) & 1][j] = qk_op(T, ((b + 1) * PB + j) & 1, ((b + 1) * PB + j) >> 1);
-                }
-                __builtin_amdgcn_sched_barrier(0);
+                        for (int j = 0; j < KPB; ++j) av[(b + 1) & 1][j] = qk_op(T, (b + 1) * KPB + j);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int j = 0; j < PB; ++j)
-                    s[(b * PB + j) & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        av[b & 1][j], qb[(b * PB + j) >> 1], s[(b * PB + j) & 1], 0, 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
-            });
+                    for (int j = 0; j < KPB; ++j) {
+                        const int ks = b * KPB + j;
+                        s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[b & 1][j], qb[0][ks], s[0], 0, 0, 0);
+                        s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[b & 1][j], qb[1][ks], s[1], 0, 0, 0);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+            } else {
+                // column tile j = K-steps 4 j .. 4 j + 3 (the rope tile: 16, 17)
+                // accumulates into sc[j & 1]; it is added, times the keys' factor
+                // f_j, after the first batch of the next column tile went out
+                f32x4v sc[2][2];
+#pragma unroll
+                for (int p = 0; p < 2; ++p)
+#pragma unroll
+                    for (int ht = 0; ht < 2; ++ht) sc[p][ht] = f32x4v{0.f, 0.f, 0.f, 0.f};
+                const float* kf = kvf + buf * NTL * TROWS + 16 * kb + 4 * g;
+                auto fold = [&](int j, int p) {   // s += f_j(key) * sc[p]; sc[p] = 0
+                    const f32x4v f = *(const f32x4v*)(kf + j * TROWS);
+#pragma unroll
+                    for (int ht = 0; ht < 2; ++ht) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) s[ht][i] = __builtin_fmaf(f[i], sc[p][ht][i], s[ht][i]);
+                        sc[p][ht] = f32x4v{0.f, 0.f, 0.f, 0.f};
+                    }
+                };
+                static_for<NB>([&](auto bc) {
+                    constexpr int b = decltype(bc)::value;
+                    constexpr int jt = (b * KPB) / 4;          // column tile of this batch
+                    if constexpr (b + 1 < NB) {
+#pragma unroll
+                        for (int j = 0; j < KPB; ++j) av[(b + 1) & 1][j] = qk_op(T, (b + 1) * KPB + j);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int j = 0; j < KPB; ++j) {
+                        const int ks = b * KPB + j;
+                        sc[jt & 1][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[b & 1][j], qb[0][ks], sc[jt & 1][0],
+                                                                                 0, 0, 0);
+                        sc[jt & 1][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[b & 1][j], qb[1][ks], sc[jt & 1][1],
+                                                                                 0, 0, 0);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    // first batch of column tile jt >= 1: the previous tile is complete
+                    if constexpr (jt >= 1 && (b * KPB) % 4 == 0) fold(jt - 1, (jt - 1) & 1);
+                });
+                fold(NTL - 1, (NTL - 1) & 1);
+            }
+            float fk[4];   // KVF 1: the factor of each of this lane's keys
+            if constexpr (KVF == 1) {
+                const f32x4v f = *(const f32x4v*)(kvf + buf * TROWS + 16 * kb + 4 * g);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) fk[i] = f[i];
+                // one factor per row: the logit is scale * f * (q . code)
+                s[0] *= f;
+                s[1] *= f;
+            }
             if (vm != 0xFFFFFFFFu) {
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
+                for (int i = 0; i < 4; ++i)
+                    if (!((vm >> (16 * kb + 4 * g + i)) & 1u)) {
+                        s[0][i] = -__builtin_inff();
+                        s[1][i] = -__builtin_inff();
+                    }
+            }
+            // per-head maxima over this wave's 16 keys, traded with the partner
+            float tm[2];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (!((vm >> (16 * kb + 4 * g + i)) & 1u)) s[kb][i] = -__builtin_inff();
+            for (int ht = 0; ht < 2; ++ht) {
+                float m = fmaxf(fmaxf(s[ht][0], s[ht][1]), fmaxf(s[ht][2], s[ht][3]));
+                const auto w16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+                m = fmaxf(__uint_as_float(w16[0]), __uint_as_float(w16[1]));
+                const auto w32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+                tm[ht] = fmaxf(__uint_as_float(w32[0]), __uint_as_float(w32[1]));
+                if (g == 0) xmax[qh][kb][ht * 16 + l16] = tm[ht];
             }
-            float tmax = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                               fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-            {
-                const auto w16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
-                tmax = fmaxf(__uint_as_float(w16[0]), __uint_as_float(w16[1]));
-                const auto w32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
-                tmax = fmaxf(__uint_as_float(w32[0]), __uint_as_float(w32[1]));
-            }
-            tmax *= c;   // c > 0
-            const bool raise = tmax > m2 + kLazy;   // also true on the first valid tile
-            const bool any = __ballot(raise) != 0ull;
-            if (any) {
-                const float mnew = raise ? tmax : m2;
-                const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);  // m2 = -inf -> 0
-                lsum *= alpha;
-                m2 = mnew;
-                if (g == 0) alph[ps][hq * 16 + l16] = alpha;
-            }
-            if (lane == 0) rflag[ps][hq] = any ? 1 : 0;
-            const float negm = m2 == -__builtin_inff() ? 0.f : -m2;
-            float pe[8];
+            if (lane == 0) __hip_atomic_store(&xflag[qh][kb], seqno, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+            while (__hip_atomic_load(&xflag[qh][kb ^ 1], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != seqno)
+                __builtin_amdgcn_s_sleep(1);
+            // both head tiles side by side (independent chains), without branches
+            float tmax[2], alpha[2], pe[2][4], rs[2];
+            bool any[2];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e >> 2][e & 3], c, negm));
-            float rs = ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
-            {
-                const auto w16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(rs), __float_as_uint(rs), false, false);
-                rs = __uint_as_float(w16[0]) + __uint_as_float(w16[1]);
-                const auto w32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(rs), __float_as_uint(rs), false, false);
-                rs = __uint_as_float(w32[0]) + __uint_as_float(w32[1]);
-            }
-            lsum += rs;
-            bf16x8 pb;
+            for (int ht = 0; ht < 2; ++ht) tmax[ht] = fmaxf(tm[ht], xmax[qh][kb ^ 1][ht * 16 + l16]) * c;   // c > 0
 #pragma unroll
-            for (int e = 0; e < 8; ++e) pb[e] = (__bf16)pe[e];
-            *(__attribute__((address_space(3))) bf16x8*)((lds_u8*)pbuf[ps][hq] + lane * 16) = pb;
+            for (int ht = 0; ht < 2; ++ht) {
+                const bool raise = tmax[ht] > m2[ht] + kLazy;   // also true on the first valid tile
+                any[ht] = __ballot(raise) != 0ull;
+                const float mnew = raise ? tmax[ht] : m2[ht];
+                alpha[ht] = raise ? __builtin_amdgcn_exp2f(m2[ht] - mnew) : 1.f;   // m2 = -inf -> 0
+                lsum[ht] *= alpha[ht];
+                m2[ht] = mnew;
+                const float negm = mnew == -__builtin_inff() ? 0.f : -mnew;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pe[ht][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[ht][i], c, negm));
+                rs[ht] = (pe[ht][0] + pe[ht][1]) + (pe[ht][2] + pe[ht][3]);
+            }
+#pragma unroll
+            for (int ht = 0; ht < 2; ++ht) {
+                const auto w16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(rs[ht]), __float_as_uint(rs[ht]),
+                                                                  false, false);
+                rs[ht] = __uint_as_float(w16[0]) + __uint_as_float(w16[1]);
+            }
+#pragma unroll
+            for (int ht = 0; ht < 2; ++ht) {
+                const auto w32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(rs[ht]), __float_as_uint(rs[ht]),
+                                                                  false, false);
+                lsum[ht] += __uint_as_float(w32[0]) + __uint_as_float(w32[1]);
+            }
+#pragma unroll
+            for (int ht = 0; ht < 2; ++ht) {
+                const int htg = qh * 2 + ht;   // head tile within the block
+                if (kb == 0) {
+                    if (g == 0) alph[ps][htg * 16 + l16] = alpha[ht];
+                    if (lane == 0) rflag[ps][htg] = any[ht] ? 1 : 0;
+                }
+                bf16x4v pb;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pb[i] = (__bf16)(KVF == 1 ? pe[ht][i] * fk[i] : pe[ht][i]);
+                *(__attribute__((address_space(3))) bf16x4v*)((lds_u8*)pbuf[ps][htg] + lane * 16 + kb * 8) = pb;
+            }
         };
 
         __syncthreads();                                   // barrier P: tile 0 landed
-        q_tile(tile0, vmask[0], 0);
+        q_tile(tile0, 0, vmask[0], 0, 1);
         int bq = 1;                                        // buffer of tile t+1
         for (int t = 0; t < ntiles; ++t) {
             __syncthreads();                               // barrier t: P(t) published, tile t+1 landed
             if (t + 1 < ntiles) {
                 const uint32_t vmn = __builtin_amdgcn_readfirstlane(vmask[t + 1]);
-                q_tile(tile0 + bq * TB, vmn, (t + 1) & 1);
+                q_tile(tile0 + bq * TB, bq, vmn, (t + 1) & 1, t + 2);
             }
             bq = bq == NBUF - 1 ? 0 : bq + 1;
         }
-        // softmax totals for the p-waves, and the normaliser
         __syncthreads();                                   // barrier F: the P ring is no longer read
         if (g == 0) {
-            fin_l[hq * 16 + l16] = lsum;
-            if (head < a.H) {
-                const float l_nat = lsum > 0.f ? (m2 + log2f(lsum)) * kLn2 : -__builtin_inff();
-                if (nsplit == 1 && out != nullptr) {
-                    if (lse != nullptr) lse[(int64_t)r * a.H + head] = l_nat;
-                } else {
-                    part_lse[((int64_t)r * nsplit + sp) * a.H + head] = l_nat;
-                }
+#pragma unroll
+            for (int ht = 0; ht < 2; ++ht) {
+                fin_l[(qh * 2 + kb) * 32 + ht * 16 + l16] = lsum[ht];
+                if (kb == 0) fin_m[qh * 32 + ht * 16 + l16] = m2[ht];
             }
         }
         __syncthreads();                                   // barrier E
     } else {
         // ---------------------------------------------------------------- p-wave
-        // The p-waves also load the tiles (see the kernel comment).
-        const int pc = wave - 4;
-        const uint32_t tile_lds = (uint32_t)(uintptr_t)tile;
-        const int lrow = (tid >> 3) & 31;
-        const uint32_t goff = (uint32_t)(((tid & 7) ^ sfa_swz8(lrow)) << 4);
-        auto read_slot = [&](int t) -> uint32_t { return rslot[(t < ntiles ? t : 0) * TROWS + lrow]; };
-        auto issue_tile = [&](uint32_t s, int buf) {
-            const uint8_t* gp = (s != 0xFFFFFFFFu ? a.kv.data + (uint64_t)s * (uint32_t)a.kv.row_stride : g_zero_row) + goff;
-            const uint32_t blk = tile_lds + (uint32_t)(buf * TB + pc * GB);
-            static_for<NJ>([&](auto jc) {
-                constexpr int j = decltype(jc)::value;
-                // the immediate offset moves both the global and the LDS address;
-                // block j lands at blk + j KB
-                lds_dma<16, j * 128>(gp, blk + (uint32_t)(j * (1024 - 128)));
-            });
-        };
-        // tiles 0 .. LA up front; tile t + 1 + LA goes out in iteration t into the
-        // buffer PV(t-1) has released.  Each thread issues NJ loads per tile, so
-        // "tile j landed" = at most NJ * (tiles issued after j) loads pending.
-        constexpr int LA = NBUF - 2;
-        static_assert(LA <= 2, "wait counts cover two tiles in flight");
+        // bf16 rows: tile t + 1 + LA goes out in iteration t into the buffer
+        // tile t - 1 has released.  Every tile is NJ loads per thread: "tile j
+        // landed" = at most NJ * (tiles issued after j) loads still pending.
+        static_assert(LA <= 2 && NJ * LA < 64, "vmcnt covers the tiles in flight");
+        auto issued = [&](int i) { return i <= LA ? i < nt_fill : i < ntiles; };
         auto wait_tile = [&](int j, int last) {            // tile j landed; tiles up to `last` issued
-            const int after = (ntiles - 1 < last ? ntiles - 1 : last) - j;
+            int after = 0;
+#pragma unroll
+            for (int d = 1; d <= LA; ++d) after += (j + d <= last && issued(j + d)) ? 1 : 0;
             if (after >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NJ) : "memory");
             else if (after == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NJ) : "memory");
             else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         };
-        // fp8 rows: wave pc fills rows 8 pc .. 8 pc + 7 of each tile.  In 1 KB block
-        // j, lane l owns position l % 8 of row 8 pc + l / 8, i.e. bf16 chunk c = 8 j
-        // + ((l % 8) ^ swz8(row)) = columns 8 c .. 8 c + 7: it loads their 8 e4m3
-        // codes, multiplies by the row's factor of that column tile (block j lies in
-        // tile j / 2) and writes the 16 bytes, one contiguous 1 KB per instruction.
-        // Codes are fetched two tiles ahead into registers.
+        // fp8 rows: in 1 KB block j, lane l owns position l % 8 of row 8 pc + l / 8,
+        // i.e. bf16 chunk 8 j + ((l % 8) ^ swz8(row)) = 8 columns: it loads their 8
+        // e4m3 codes, converts them exactly and writes the 16 bytes (one
+        // contiguous 1 KB per instruction).  Codes go out two tiles ahead.
         const int frow = 8 * pc + (lane >> 3);
         const int fsw = (lane & 7) ^ sfa_swz8(frow);
-        auto fetch = [&](int t, u32x2 (&v)[NJ]) {
-            const uint32_t s = t < ntiles ? rslot[t * TROWS + frow] : 0xFFFFFFFFu;
-            const uint8_t* gp = s != 0xFFFFFFFFu ? a.kv.data + (uint64_t)s * (uint32_t)a.kv.row_stride : g_zero_row;
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) v[j] = __builtin_nontemporal_load((const u32x2*)(gp + (8 * j + fsw) * 8));
+        struct Codes {
+            u32x2 v[NJ];
+            float f[NTL];
         };
-        auto put = [&](int t, const u32x2 (&v)[NJ], int buf) {
-            lds_u8* dst = (lds_u8*)tile + buf * TB + pc * GB + lane * 16;
-            float fr[NTL];                                 // the row's factors, read once
+        auto fetch = [&](int t, Codes& cd) {
+            const uint32_t s = t < ntiles ? rslot[t * TROWS + frow] : 0xFFFFFFFFu;
+            const bool ok = s != 0xFFFFFFFFu;
+            const uint8_t* gp = ok ? a.kv.data + (uint64_t)s * (uint32_t)a.kv.row_stride : g_zero_row;
 #pragma unroll
-            for (int q = 0; q < NTL; ++q) fr[q] = kvf[q * MAXK + t * TROWS + frow];
+            for (int j = 0; j < NJ; ++j) cd.v[j] = __builtin_nontemporal_load((const u32x2*)(gp + (8 * j + fsw) * 8));
+            if constexpr (KVF == 1) {
+                cd.f[0] = ok ? a.kv.scale[(int64_t)s / a.kv.scale_group] : 0.f;
+            } else if constexpr (KVF == 2) {
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                const float f = fr[KVF == 1 ? 0 : j / 2];
-                const f32x2 x0 = fp8x2_to_f32<false>(v[j].x), x1 = fp8x2_to_f32<true>(v[j].x);
-                const f32x2 x2 = fp8x2_to_f32<false>(v[j].y), x3 = fp8x2_to_f32<true>(v[j].y);
-                bf16x8 b;
-                b[0] = (__bf16)(x0.x * f);
-                b[1] = (__bf16)(x0.y * f);
-                b[2] = (__bf16)(x1.x * f);
-                b[3] = (__bf16)(x1.y * f);
-                b[4] = (__bf16)(x2.x * f);
-                b[5] = (__bf16)(x2.y * f);
-                b[6] = (__bf16)(x3.x * f);
-                b[7] = (__bf16)(x3.y * f);
-                *(__attribute__((address_space(3))) bf16x8*)(dst + j * 1024) = b;
+                for (int q = 0; q < NTL; ++q) cd.f[q] = ok ? a.kv.scale[(int64_t)s * NTL + q] : 0.f;
             }
         };
-        static_assert(KVF == 0 || NBUF == 3, "fp8 rows: PV(t) | QK(t+1) | tile t+2 being written");
-        u32x2 fv[KVF ? 2 : 1][NJ];
-        uint32_t sl = 0;
+        auto put = [&](const Codes& cd, int buf) {
+            lds_u8* dst = (lds_u8*)tile + buf * TB + pc * GB + lane * 16;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                u32x4 b;
+                b.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cd.v[j].x, 1.0f, false));
+                b.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cd.v[j].x, 1.0f, true));
+                b.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cd.v[j].y, 1.0f, false));
+                b.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cd.v[j].y, 1.0f, true));
+                *(__attribute__((address_space(3))) u32x4*)(dst + j * 1024) = b;
+            }
+            if ((lane & 7) == 0) {
+#pragma unroll
+                for (int q = 0; q < NTL; ++q) kvf[(buf * NTL + q) * TROWS + frow] = cd.f[q];
+            }
+        };
+        Codes c0, c1;
         if constexpr (KVF == 0) {
-            for (int j = 0; j <= LA; ++j)
-                if (j < ntiles) issue_tile(read_slot(j), j);
-            sl = read_slot(LA + 1);
+            wait_tile(0, LA);
         } else {
-            fetch(0, fv[0]);
-            fetch(1, fv[1]);
-            put(0, fv[0], 0);
-            put(1, fv[1], 1);
-            fetch(2, fv[0]);
-            fetch(3, fv[1]);
+            fetch(0, c0);
+            fetch(1, c1);
+            put(c0, 0);
+            put(c1, 1);
+            fetch(2, c0);
+            fetch(3, c1);
         }
         // PV operand of M-tile mt: transpose reads of rows 4 g + l16 / 4 (keys of
         // K-slots 0..3) and 16 + 4 g + l16 / 4 (K-slots 4..7), 4 value columns each
@@ -1274,27 +1021,24 @@ __global__ __launch_bounds__(512) void sfa_ws_kernel(MlaDev a, int kps, int nspl
 #pragma unroll
             for (int mt = 0; mt < MTP; ++mt) o[ht][mt] = f32x4v{0.f, 0.f, 0.f, 0.f};
 
-        if constexpr (KVF == 0) wait_tile(0, LA);
         __syncthreads();                                   // barrier P: tile 0 landed
         int bc = 0;                                        // buffer of tile t
         for (int t = 0; t < ntiles; ++t) {
             if constexpr (KVF == 0) wait_tile(t + 1, t + LA);
-            __syncthreads();                               // barrier t: tile t+1 landed
+            __syncthreads();                               // barrier t: P(t) published, tile t+1 landed
             if constexpr (KVF == 0) {
                 const int bn = bc + LA + 1 >= NBUF ? bc + LA + 1 - NBUF : bc + LA + 1;   // = buffer of tile t-1
-                if (t + 1 + LA < ntiles) issue_tile(sl, bn);
-                sl = read_slot(t + 2 + LA);
+                if (t + 1 + LA < ntiles) issue_rows(rslot[(t + 1 + LA) * TROWS + frow], bn);
             } else {
                 // tile t+2 into the buffer tile t-1 has released; codes of tile t+4 out.
-                // Constant register-set indices in each branch keep fv in registers (an
-                // index of t & 1 would put the array in scratch memory).
+                // Constant register-set names in each branch keep the codes in registers.
                 const int bw = bc == 0 ? 2 : bc - 1;
                 if (t & 1) {
-                    if (t + 2 < ntiles) put(t + 2, fv[1], bw);
-                    if (t + 4 < ntiles) fetch(t + 4, fv[1]);
+                    if (t + 2 < ntiles) put(c1, bw);
+                    if (t + 4 < ntiles) fetch(t + 4, c1);
                 } else {
-                    if (t + 2 < ntiles) put(t + 2, fv[0], bw);
-                    if (t + 4 < ntiles) fetch(t + 4, fv[0]);
+                    if (t + 2 < ntiles) put(c0, bw);
+                    if (t + 4 < ntiles) fetch(t + 4, c0);
                 }
             }
             const int ps = t & 1;
@@ -1309,6 +1053,17 @@ __global__ __launch_bounds__(512) void sfa_ws_kernel(MlaDev a, int kps, int nspl
 #pragma unroll
             for (int ht = 0; ht < 4; ++ht)
                 pbt[ht] = *(const __attribute__((address_space(3))) bf16x8*)((const lds_u8*)pbuf[ps][ht] + lane * 16);
+            if constexpr (KVF == 2) {
+                // value columns of column tile pc: the P^T operand times the keys' f_pc
+                const float* kf = kvf + (bc * NTL + pc) * TROWS;
+                const f32x4v f0 = *(const f32x4v*)(kf + 4 * g);
+                const f32x4v f1 = *(const f32x4v*)(kf + 16 + 4 * g);
+#pragma unroll
+                for (int ht = 0; ht < 4; ++ht) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) pbt[ht][e] = (__bf16)((float)pbt[ht][e] * (e < 4 ? f0[e] : f1[e - 4]));
+                }
+            }
             const int fl = rflag[ps][0] | (rflag[ps][1] << 1) | (rflag[ps][2] << 2) | (rflag[ps][3] << 3);
             if (fl != 0) {
 #pragma unroll
@@ -1338,11 +1093,26 @@ __global__ __launch_bounds__(512) void sfa_ws_kernel(MlaDev a, int kps, int nspl
 #pragma unroll
         for (int ht = 0; ht < 4; ++ht) {
             const int head = hb * 64 + ht * 16 + l16;
+            const int hh = ht >> 1, hl = (ht & 1) * 16 + l16;
+            const float ls = fin_l[(hh * 2) * 32 + hl] + fin_l[(hh * 2 + 1) * 32 + hl];
             if (head >= a.H) continue;
-            const float ls = fin_l[ht * 16 + l16];
             const float inv = ls > 0.f ? 1.f / ls : 0.f;
-            if (nsplit == 1 && out != nullptr) {
-                __bf16* orow = out + ((int64_t)r * a.H + head) * DLAT + pc * DVP + 4 * g;
+            if (pc == 0 && g == 0) {
+                const float l_nat = ls > 0.f ? (fin_m[hh * 32 + hl] + log2f(ls)) * kLn2 : -__builtin_inff();
+                if (nsplit == 1) {
+                    if (lse != nullptr) lse[(int64_t)r * a.H + head] = l_nat;
+                } else {
+                    part_lse[((int64_t)r * nsplit + sp) * a.H + head] = l_nat;
+                }
+            }
+            const int64_t col0 = pc * DVP + 4 * g;
+            if (nsplit == 1 && out_f32 != nullptr) {
+                float* orow = out_f32 + ((int64_t)r * a.H + head) * DLAT + col0;
+#pragma unroll
+                for (int mt = 0; mt < MTP; ++mt) *(f32x4v*)(orow + 16 * mt) = o[ht][mt] * inv;
+            } else {
+                __bf16* orow = nsplit == 1 ? out + ((int64_t)r * a.H + head) * DLAT + col0
+                                           : part_o + (((int64_t)r * nsplit + sp) * a.H + head) * DLAT + col0;
 #pragma unroll
                 for (int mt = 0; mt < MTP; ++mt) {
                     bf16x4 v;
@@ -1350,10 +1120,6 @@ __global__ __launch_bounds__(512) void sfa_ws_kernel(MlaDev a, int kps, int nspl
                     for (int i = 0; i < 4; ++i) v[i] = (__bf16)(o[ht][mt][i] * inv);
                     *(bf16x4*)(orow + 16 * mt) = v;
                 }
-            } else {
-                float* prow = part_o + (((int64_t)r * nsplit + sp) * a.H + head) * DLAT + pc * DVP + 4 * g;
-#pragma unroll
-                for (int mt = 0; mt < MTP; ++mt) *(f32x4v*)(prow + 16 * mt) = o[ht][mt] * inv;
             }
         }
     }
@@ -1363,11 +1129,12 @@ __global__ __launch_bounds__(512) void sfa_ws_kernel(MlaDev a, int kps, int nspl
 // lse = M + log sum_i e^{lse_i - M} (M = max_i lse_i; a part with lse = -inf
 // holds no row).  Partial i of row r lives at entry (r * row_str + i *
 // split_str) * H + h: split-K partials [R, nsplit, H] use (nsplit, 1), the
-// gathered shards of a context split [G, R, H] use (1, R).  8 consecutive
-// value columns per thread (two 16-byte loads per part), DLAT / 8 threads per
-// (row, head), 256 threads per block; bf16 or fp32 output.
-template <int DLAT, bool F32OUT>
-__global__ __launch_bounds__(256) void sfa_combine_kernel(const float* __restrict__ part_o,
+// gathered shards of a context split [G, R, H] use (1, R).  Partials are bf16
+// (the 512 + 64 attention's split-K parts) or fp32; 8 consecutive value
+// columns per thread, DLAT / 8 threads per (row, head), 256 threads per
+// block; bf16 or fp32 output.
+template <int DLAT, typename PT, bool F32OUT>
+__global__ __launch_bounds__(256) void sfa_combine_kernel(const PT* __restrict__ part_o,
                                                           const float* __restrict__ part_lse, int nsplit,
                                                           int64_t row_str, int64_t split_str, int H, int RH,
                                                           void* __restrict__ out, float* __restrict__ lse) {
@@ -1378,6 +1145,18 @@ __global__ __launch_bounds__(256) void sfa_combine_kernel(const float* __restric
     if (rh >= RH) return;
     const int r = rh / H, h = rh % H;
     const int c = (threadIdx.x % TPH) * 8;
+    auto load8 = [&](int64_t e, float (&x)[8]) {   // 8 values of part entry e from column c
+        if constexpr (std::is_same<PT, float>::value) {
+            const f32x4* po = (const f32x4*)(part_o + e * DLAT + c);
+            const f32x4 v0 = po[0], v1 = po[1];
+            x[0] = v0.x; x[1] = v0.y; x[2] = v0.z; x[3] = v0.w;
+            x[4] = v1.x; x[5] = v1.y; x[6] = v1.z; x[7] = v1.w;
+        } else {
+            const bf16x8 v = *(const bf16x8*)(part_o + e * DLAT + c);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) x[j] = (float)v[j];
+        }
+    };
     float M = -__builtin_inff();
     float acc[8];
 #pragma unroll
@@ -1388,15 +1167,13 @@ __global__ __launch_bounds__(256) void sfa_combine_kernel(const float* __restric
         // as the general loop below
         const int64_t e0 = (int64_t)r * row_str * H + h, e1 = ((int64_t)r * row_str + split_str) * H + h;
         const float l0 = part_lse[e0], l1 = part_lse[e1];
-        const f32x4* p0 = (const f32x4*)(part_o + e0 * DLAT + c);
-        const f32x4* p1 = (const f32x4*)(part_o + e1 * DLAT + c);
-        const f32x4 a0 = p0[0], a1 = p0[1], b0 = p1[0], b1 = p1[1];
+        float x0[8], x1[8];
+        load8(e0, x0);
+        load8(e1, x1);
         M = fmaxf(fmaxf(M, l0), l1);
         if (M != -__builtin_inff()) {
             const float w0 = __expf(l0 - M), w1 = __expf(l1 - M);
             W = w0 + w1;
-            const float x0[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-            const float x1[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
 #pragma unroll
             for (int j = 0; j < 8; ++j) acc[j] = fmaf(w1, x1[j], fmaf(w0, x0[j], 0.f));
         }
@@ -1408,16 +1185,10 @@ __global__ __launch_bounds__(256) void sfa_combine_kernel(const float* __restric
             const int64_t e = ((int64_t)r * row_str + i * split_str) * H + h;
             const float wi = __expf(part_lse[e] - M);
             W += wi;
-            const f32x4* po = (const f32x4*)(part_o + e * DLAT + c);
-            const f32x4 v0 = po[0], v1 = po[1];
-            acc[0] = fmaf(wi, v0.x, acc[0]);
-            acc[1] = fmaf(wi, v0.y, acc[1]);
-            acc[2] = fmaf(wi, v0.z, acc[2]);
-            acc[3] = fmaf(wi, v0.w, acc[3]);
-            acc[4] = fmaf(wi, v1.x, acc[4]);
-            acc[5] = fmaf(wi, v1.y, acc[5]);
-            acc[6] = fmaf(wi, v1.z, acc[6]);
-            acc[7] = fmaf(wi, v1.w, acc[7]);
+            float x[8];
+            load8(e, x);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[j] = fmaf(wi, x[j], acc[j]);
         }
     }
     const float inv = W > 0.f ? 1.f / W : 0.f;
@@ -1470,16 +1241,19 @@ __global__ __launch_bounds__(256) void sfa_localize_kernel(const int32_t* __rest
 // split heuristic shared with the workspace query ------------------------------
 
 struct SfaPlan {
-    int nhg;      // 32-head groups per workgroup
+    int hpb;      // heads per workgroup
     int nhb;      // head blocks
     int nsplit;   // splits of the index list
     int kps;      // index entries per split
 };
 
-SfaPlan sfa_plan(int R, int K, int H) {
+// 512 + 64 rows: 64-head workgroups (sfa_mla_kernel); 64 + 16 rows: 32 or 64
+// heads (sfa_kernel).  The index list of a row is split only as far as needed
+// to give the chip about 256 workgroups, keeping >= 4 tiles per split.
+SfaPlan sfa_plan(int R, int K, int H, int D_latent) {
     SfaPlan p;
-    p.nhg = H <= 32 ? 1 : 2;  // 4 waves (64 heads) per workgroup, 1 per SIMD
-    p.nhb = (H + 32 * p.nhg - 1) / (32 * p.nhg);
+    p.hpb = D_latent == 512 ? 64 : (H <= 32 ? 32 : 64);
+    p.nhb = (H + p.hpb - 1) / p.hpb;
     const int64_t wgs = (int64_t)(R > 0 ? R : 1) * p.nhb;
     int64_t ns = (256 + wgs - 1) / wgs;
     const int64_t max_by_len = (K + 127) / 128;  // keep >= 4 tiles per split
@@ -1495,10 +1269,34 @@ SfaPlan sfa_plan(int R, int K, int H) {
     return p;
 }
 
-// out != nullptr: bf16 output; out == nullptr: fp32 normalised output in
-// out_f32 (partial results of one context shard) and lse required.
-template <int DLAT, int DROPE, bool FP8, int NHG, bool TSC>
-static hipError_t launch_sfa_t(const MlaDev& a, const SfaPlan& p, __bf16* out, float* out_f32, float* lse,
+// bytes of split-K partials: bf16 outputs for 512 + 64 rows, fp32 otherwise,
+// then the fp32 lse of every part
+static size_t sfa_part_elt(int D_latent) { return D_latent == 512 ? 2 : 4; }
+
+// kv_mode: 0 bf16 rows, 1 fp8 rows with per-group factors, 2 fp8 rows with one
+// factor per 128-column tile.  out != nullptr: bf16 output; out == nullptr:
+// fp32 normalised output in out_f32 (partial results of one context shard),
+// lse required.
+static hipError_t launch_sfa512(const MlaDev& a, const SfaPlan& p, int kv_mode, __bf16* out, float* out_f32,
+                                float* lse, __bf16* part_o, float* part_lse, hipStream_t stream) {
+    const int64_t units = (int64_t)a.R * p.nsplit;
+    const dim3 grid((unsigned)((units + 7) / 8 * 8 * p.nhb)), block(512);
+#define LISFA_MLA(NB_, MK_, KVF_)                                                                        \
+    hipLaunchKernelGGL((sfa_mla_kernel<NB_, MK_, KVF_>), grid, block, 0, stream, a, p.kps, p.nsplit, p.nhb, \
+                       out, lse, out_f32, part_o, part_lse)
+    const bool short_list = p.kps <= 1024;
+    if (kv_mode == 0 && short_list) LISFA_MLA(4, 1024, 0);
+    else if (kv_mode == 0) LISFA_MLA(3, kSfaMaxKeys, 0);
+    else if (kv_mode == 1 && short_list) LISFA_MLA(3, 1024, 1);
+    else if (kv_mode == 1) LISFA_MLA(3, kSfaMaxKeys, 1);
+    else if (short_list) LISFA_MLA(3, 1024, 2);
+    else LISFA_MLA(3, kSfaMaxKeys, 2);
+#undef LISFA_MLA
+    return hipGetLastError();
+}
+
+template <bool FP8, int NHG, bool TSC>
+static hipError_t launch_sfa64(const MlaDev& a, const SfaPlan& p, __bf16* out, float* out_f32, float* lse,
                                float* part_o, float* part_lse, hipStream_t stream) {
     const int64_t units = (int64_t)a.R * p.nsplit;
     const int64_t nwg = (units + 7) / 8 * 8 * p.nhb;
@@ -1506,61 +1304,49 @@ static hipError_t launch_sfa_t(const MlaDev& a, const SfaPlan& p, __bf16* out, f
         part_o = out_f32;
         part_lse = lse;
     }
-    if (!FP8 && DLAT == 512 && DROPE == 64 && NHG == 2 && p.kps <= 1024)
-        hipLaunchKernelGGL((sfa_ws_kernel<512, 64, 4, 1024>), dim3((unsigned)nwg), dim3(512), 0, stream, a, p.kps,
-                           p.nsplit, p.nhb, out, lse, part_o, part_lse);
-    else if (!FP8 && DLAT == 512 && DROPE == 64 && NHG == 2)
-        hipLaunchKernelGGL((sfa_ws_kernel<512, 64, 3, kSfaMaxKeys>), dim3((unsigned)nwg), dim3(512), 0, stream, a,
-                           p.kps, p.nsplit, p.nhb, out, lse, part_o, part_lse);
-    else if (FP8 && DLAT == 512 && DROPE == 64 && NHG == 2 && p.kps <= 1024)
-        // fp8 rows turned into bf16 tiles by the loading waves (factor per row or per 128-column tile)
-        hipLaunchKernelGGL((sfa_ws_kernel<512, 64, 3, 1024, TSC ? 2 : 1>), dim3((unsigned)nwg), dim3(512), 0, stream,
-                           a, p.kps, p.nsplit, p.nhb, out, lse, part_o, part_lse);
-    else if constexpr (!FP8 && ((DLAT + DROPE) * 2) % 128 == 0)
-        hipLaunchKernelGGL((sfa_bf16_kernel<DLAT, DROPE, NHG>), dim3((unsigned)nwg), dim3(128 * NHG), 0, stream,
-                           a, p.kps, p.nsplit, p.nhb, out, lse, part_o, part_lse);
-    else
-        hipLaunchKernelGGL((sfa_kernel<DLAT, DROPE, FP8, NHG, TSC>), dim3((unsigned)nwg), dim3(128 * NHG), 0, stream, a,
-                           p.kps, p.nsplit, p.nhb, out, lse, part_o, part_lse);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || p.nsplit == 1) return e;
+    hipLaunchKernelGGL((sfa_kernel<64, 16, FP8, NHG, TSC>), dim3((unsigned)nwg), dim3(128 * NHG), 0, stream, a,
+                       p.kps, p.nsplit, p.nhb, out, lse, part_o, part_lse);
+    return hipGetLastError();
+}
+
+template <int DLAT, typename PT>
+static hipError_t launch_combine(const MlaDev& a, const SfaPlan& p, const PT* part_o, const float* part_lse,
+                                 __bf16* out, float* out_f32, float* lse, hipStream_t stream) {
     constexpr int HPB = 256 / (DLAT / 8);
     const int RH = a.R * a.H;
+    const dim3 grid((unsigned)((RH + HPB - 1) / HPB));
     if (out != nullptr)
-        hipLaunchKernelGGL((sfa_combine_kernel<DLAT, false>), dim3((unsigned)((RH + HPB - 1) / HPB)), dim3(256), 0,
-                           stream, part_o, part_lse, p.nsplit, (int64_t)p.nsplit, (int64_t)1, a.H, RH, (void*)out,
-                           lse);
+        hipLaunchKernelGGL((sfa_combine_kernel<DLAT, PT, false>), grid, dim3(256), 0, stream, part_o, part_lse,
+                           p.nsplit, (int64_t)p.nsplit, (int64_t)1, a.H, RH, (void*)out, lse);
     else
-        hipLaunchKernelGGL((sfa_combine_kernel<DLAT, true>), dim3((unsigned)((RH + HPB - 1) / HPB)), dim3(256), 0,
-                           stream, part_o, part_lse, p.nsplit, (int64_t)p.nsplit, (int64_t)1, a.H, RH,
-                           (void*)out_f32, lse);
+        hipLaunchKernelGGL((sfa_combine_kernel<DLAT, PT, true>), grid, dim3(256), 0, stream, part_o, part_lse,
+                           p.nsplit, (int64_t)p.nsplit, (int64_t)1, a.H, RH, (void*)out_f32, lse);
     return hipGetLastError();
 }
 
 hipError_t sfa_dispatch(const MlaDev& a, int D_latent, int kv_mode, __bf16* out, float* out_f32, float* lse, void* ws,
                         hipStream_t stream) {
-    // kv_mode: 0 bf16 rows, 1 fp8 rows with per-group factors, 2 fp8 rows with
-    // one factor per 128-column tile
-    const SfaPlan p = sfa_plan(a.R, a.K, a.H);
+    const SfaPlan p = sfa_plan(a.R, a.K, a.H, D_latent);
+    const size_t npart = (size_t)a.R * p.nsplit * a.H;
+    float* part_lse = (float*)((uint8_t*)ws + npart * D_latent * sfa_part_elt(D_latent));
+    hipError_t e;
+    if (D_latent == 512) {
+        __bf16* part_o = (__bf16*)ws;
+        e = launch_sfa512(a, p, kv_mode, out, out_f32, lse, part_o, part_lse, stream);
+        if (e != hipSuccess || p.nsplit == 1) return e;
+        return launch_combine<512, __bf16>(a, p, part_o, part_lse, out, out_f32, lse, stream);
+    }
+    if (D_latent != 64) return hipErrorInvalidValue;
     float* part_o = (float*)ws;
-    float* part_lse = part_o + (size_t)a.R * p.nsplit * a.H * D_latent;
-#define LISFA_SFA_CASE(DL_, DR_, F8_, TS_, G_)                                                         \
-    if (D_latent == DL_ && kv_mode == (TS_ ? 2 : F8_ ? 1 : 0) && p.nhg == G_)                          \
-        return launch_sfa_t<DL_, DR_, F8_, G_, TS_>(a, p, out, out_f32, lse, part_o, part_lse, stream);
-    LISFA_SFA_CASE(512, 64, false, false, 2)
-    LISFA_SFA_CASE(512, 64, true, false, 2)
-    LISFA_SFA_CASE(512, 64, true, true, 2)
-    LISFA_SFA_CASE(512, 64, false, false, 1)
-    LISFA_SFA_CASE(512, 64, true, false, 1)
-    LISFA_SFA_CASE(512, 64, true, true, 1)
-    LISFA_SFA_CASE(64, 16, false, false, 1)
-    LISFA_SFA_CASE(64, 16, true, false, 1)
-    LISFA_SFA_CASE(64, 16, true, true, 1)
-    LISFA_SFA_CASE(64, 16, false, false, 2)
-    LISFA_SFA_CASE(64, 16, true, false, 2)
-    LISFA_SFA_CASE(64, 16, true, true, 2)
-#undef LISFA_SFA_CASE
-    return hipErrorInvalidValue;
+    const bool g2 = p.hpb == 64;
+    if (kv_mode == 0) e = g2 ? launch_sfa64<false, 2, false>(a, p, out, out_f32, lse, part_o, part_lse, stream)
+                             : launch_sfa64<false, 1, false>(a, p, out, out_f32, lse, part_o, part_lse, stream);
+    else if (kv_mode == 1) e = g2 ? launch_sfa64<true, 2, false>(a, p, out, out_f32, lse, part_o, part_lse, stream)
+                                  : launch_sfa64<true, 1, false>(a, p, out, out_f32, lse, part_o, part_lse, stream);
+    else e = g2 ? launch_sfa64<true, 2, true>(a, p, out, out_f32, lse, part_o, part_lse, stream)
+                : launch_sfa64<true, 1, true>(a, p, out, out_f32, lse, part_o, part_lse, stream);
+    if (e != hipSuccess || p.nsplit == 1) return e;
+    return launch_combine<64, float>(a, p, part_o, part_lse, out, out_f32, lse, stream);
 }
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -1592,7 +1378,7 @@ hipError_t lse_combine_dispatch(const float* part_o, const float* part_lse, int 
 #define LISFA_COMB(D_)                                                                                   \
     if (D == D_) {                                                                                       \
         constexpr int HPB = 256 / (D_ / 8);                                                              \
-        hipLaunchKernelGGL((sfa_combine_kernel<D_, false>), dim3((unsigned)((RH + HPB - 1) / HPB)), dim3(256), 0, \
+        hipLaunchKernelGGL((sfa_combine_kernel<D_, float, false>), dim3((unsigned)((RH + HPB - 1) / HPB)), dim3(256), 0, \
                            stream, part_o, part_lse, G, (int64_t)1, (int64_t)R, H, RH, (void*)out, lse);  \
         return hipGetLastError();                                                                        \
     }
@@ -1603,9 +1389,10 @@ hipError_t lse_combine_dispatch(const float* part_o, const float* part_lse, int 
 }
 
 size_t sfa_workspace_bytes(int R, int K, int H, int D_latent) {
-    const SfaPlan p = sfa_plan(R, K, H);
+    const SfaPlan p = sfa_plan(R, K, H, D_latent);
     if (p.nsplit <= 1) return 0;
-    return (size_t)R * p.nsplit * H * ((size_t)D_latent + 1) * sizeof(float);
+    const size_t npart = (size_t)R * p.nsplit * H;
+    return npart * D_latent * sfa_part_elt(D_latent) + npart * sizeof(float);
 }
 
 size_t sfa_partial_workspace_bytes(int R, int K, int H, int D_latent, int with_range) {
