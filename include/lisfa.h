@@ -26,7 +26,8 @@
  *     structs themselves live in host memory and are read during the call only.
  *   - The caller owns every buffer, including the workspace (size it with
  *     lisfa_workspace_size).  The library never allocates or frees device
- *     memory, keeps no global state and is safe to call from several threads.
+ *     memory and is safe to call from several threads; its only global state
+ *     is the scratch array of li_topk_sfa_noalloc (one per GPU).
  *   - All work is enqueued on `stream` (0 = the default stream) and is
  *     asynchronous; the call returns as soon as the kernels are queued.
  *     Device faults surface at the caller's next synchronisation.
@@ -343,6 +344,25 @@ int indexer_k_store(const void* k, int32_t T, int32_t D_I, const float* gamma,
 int li_topk_sfa(const lisfa_indexer_args* iargs, const lisfa_mla_args* margs,
                 int32_t K, int32_t* idx_out, void* out, float* lse,
                 void* ws, size_t ws_bytes, lisfa_stream_t stream);
+
+/*
+ * li_topk_sfa_noalloc - li_topk_sfa without a workspace argument, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  The call allocates nothing:
+ * the scores, index lists and partial results live in a static device array of
+ * LISFA_NOALLOC_SCRATCH_BYTES bytes that the library holds on every GPU it runs
+ * on until the process ends.  Rows are scored in chunks small enough for the
+ * array; a call whose smallest layout still does not fit returns
+ * LISFA_ERR_WORKSPACE (use li_topk_sfa with a caller workspace then).  The first
+ * call on a GPU looks up the array's address on that GPU (the stream's device).
+ * All calls on one GPU share its array: calls that overlap in time on one GPU
+ * (different streams, or threads) race and must be serialised by the caller.
+ * Arguments and results otherwise as li_topk_sfa.
+ */
+#define LISFA_NOALLOC_SCRATCH_BYTES (64ull << 20)
+int li_topk_sfa_noalloc(const lisfa_indexer_args* iargs, const lisfa_mla_args* margs,
+                        int32_t K, int32_t* idx_out, void* out, float* lse,
+                        lisfa_stream_t stream);
 
 #define LISFA_OP_TOPK               0   /* max_visible argument = ld_scores */
 #define LISFA_OP_SPARSE_MLA         1

@@ -10,6 +10,8 @@ Entry points (same names as the C ABI):
   topk_select(...)     per-row Top-K index lists [R, K] int32
   sparse_mla_attn(...) sparse MLA attention      [R, H, D_latent] bf16 (+ lse)
   li_topk_sfa(...)     all three in one call on one stream
+  li_topk_sfa_noalloc(...)  the same with no workspace: the library's static
+                       per-GPU scratch array (for callers that cannot allocate)
 One GPU's share of a context-parallel split:
   topk_candidates(...)         local Top-K of a shard as (position, score) pairs
   topk_merge(...)              the K best of the gathered candidates
@@ -31,7 +33,7 @@ import torch
 
 from . import _lib as _c
 
-__all__ = ["KVCache", "LisfaError", "li_score", "topk_select", "sparse_mla_attn", "li_topk_sfa",
+__all__ = ["KVCache", "LisfaError", "li_score", "topk_select", "sparse_mla_attn", "li_topk_sfa", "li_topk_sfa_noalloc",
            "topk_candidates", "topk_merge", "sparse_mla_attn_partial", "lse_combine", "zigzag_share",
            "zigzag_restore", "indexer_q_quant", "indexer_k_store", "workspace_size", "load", "status_string"]
 
@@ -361,4 +363,19 @@ def li_topk_sfa(q_idx, w, k_cache: KVCache, q, kv_cache: KVCache, row_seq, row_p
     ws = _workspace(workspace, need, q.device, stream)
     _check(lib.li_topk_sfa(ctypes.byref(ia), ctypes.byref(ma), K, _ptr(idx_out), _ptr(out), _ptr(lse),
                            _ptr(ws), need, _stream(stream)), "li_topk_sfa")
+    return out, lse
+
+
+def li_topk_sfa_noalloc(q_idx, w, k_cache: KVCache, q, kv_cache: KVCache, row_seq, row_pos, K: int,
+                        max_visible: int, out, lse=None, idx_out=None, q_scale=None, rows_per_group: int = 1,
+                        softmax_scale: Optional[float] = None, stream=None):
+    """li_topk_sfa without a workspace: the library's static scratch array of
+    the GPU serves as one (nothing is allocated, so the call can be captured in
+    a HIP graph or run where allocation is not allowed).  Calls that overlap in
+    time on one GPU share that array and must be serialised by the caller."""
+    lib = _c.load()
+    ia = _indexer_args(q_idx, w, k_cache, row_seq, row_pos, max_visible, q_scale, rows_per_group)
+    ma = _mla_args(q, kv_cache, row_seq, out.shape[2], softmax_scale)
+    _check(lib.li_topk_sfa_noalloc(ctypes.byref(ia), ctypes.byref(ma), K, _ptr(idx_out), _ptr(out), _ptr(lse),
+                                   _stream(stream)), "li_topk_sfa_noalloc")
     return out, lse

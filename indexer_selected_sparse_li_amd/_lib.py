@@ -26,8 +26,10 @@ LISFA_OP_FUSED = 2
 LISFA_OP_TOPK_CANDIDATES = 3
 LISFA_OP_SPARSE_MLA_PARTIAL = 4
 
+LISFA_NOALLOC_SCRATCH_BYTES = 64 << 20
+
 EXPORTS = (
-    "li_score", "topk_select", "sparse_mla_attn", "li_topk_sfa",
+    "li_score", "topk_select", "sparse_mla_attn", "li_topk_sfa", "li_topk_sfa_noalloc",
     "topk_candidates", "topk_merge", "sparse_mla_attn_partial", "lse_combine",
     "lisfa_zigzag_share", "zigzag_restore", "indexer_q_quant", "indexer_k_store",
     "lisfa_workspace_size", "lisfa_status_string", "lisfa_struct_size", "lisfa_abi_version",
@@ -103,6 +105,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.li_topk_sfa.argtypes = [ctypes.POINTER(IndexerArgs), ctypes.POINTER(MlaArgs), i32, vp, vp, vp,
                                 vp, sz, vp]
     lib.li_topk_sfa.restype = ctypes.c_int
+    lib.li_topk_sfa_noalloc.argtypes = [ctypes.POINTER(IndexerArgs), ctypes.POINTER(MlaArgs), i32, vp, vp, vp, vp]
+    lib.li_topk_sfa_noalloc.restype = ctypes.c_int
     lib.topk_candidates.argtypes = [vp, i64, vp, i32, i32, vp, vp, vp, vp, sz, vp]
     lib.topk_candidates.restype = ctypes.c_int
     lib.topk_merge.argtypes = [vp, vp, i64, i32, i32, i32, i32, vp, vp, vp]

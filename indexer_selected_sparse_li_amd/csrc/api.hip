@@ -1,6 +1,9 @@
 // C ABI entry points: argument validation, workspace layout and kernel
-// sequencing on the caller's stream.  No allocation, no global state.
+// sequencing on the caller's stream.  No allocation; the only global state is
+// the per-GPU scratch array of li_topk_sfa_noalloc and its device addresses.
 #include <string.h>
+
+#include <mutex>
 
 #include "common.hpp"
 
@@ -167,9 +170,11 @@ int hip_status(hipError_t e) { return e == hipSuccess ? LISFA_OK : LISFA_ERR_HIP
 
 int64_t scores_ld(int64_t max_visible) { return (max_visible + 63) / 64 * 64; }
 
-int64_t fused_chunk_rows(int32_t R, int64_t max_visible) {
+// rows per chunk of the fused call: as many as keep the scores of a chunk
+// within score_cap bytes
+int64_t fused_chunk_rows(int32_t R, int64_t max_visible, int64_t score_cap) {
     const int64_t ld = scores_ld(max_visible) > 0 ? scores_ld(max_visible) : 64;
-    int64_t rc = kScoreScratchCap / (ld * 4);
+    int64_t rc = score_cap / (ld * 4);
     if (rc >= R) return R;
     // chunks start on multiples of 16 rows: the indexer forms its row groups
     // (1, 8 or 16 rows, each dividing the caller's rows_per_group) from the
@@ -185,15 +190,100 @@ struct FusedLayout {
     size_t scores, idx, cand, sfa, total;
 };
 
-FusedLayout fused_layout(int32_t R, int64_t max_visible, int32_t K, int32_t H, int32_t D_latent) {
+FusedLayout fused_layout(int32_t R, int64_t max_visible, int32_t K, int32_t H, int32_t D_latent,
+                         int64_t score_cap = kScoreScratchCap) {
     FusedLayout L;
-    const int64_t rc = fused_chunk_rows(R, max_visible);
+    const int64_t rc = fused_chunk_rows(R, max_visible, score_cap);
     L.scores = 0;
     L.idx = align256((size_t)rc * scores_ld(max_visible) * sizeof(float));
     L.cand = L.idx + align256((size_t)R * K * sizeof(int32_t));
     L.sfa = L.cand + align256(topk_workspace_bytes((int)rc, scores_ld(max_visible), K));
     L.total = L.sfa + align256(sfa_workspace_bytes(R, K, H, D_latent));
     return L;
+}
+
+int check_fused(const lisfa_indexer_args* iargs, const lisfa_mla_args* margs, int32_t K, const void* out) {
+    int e = check_indexer(iargs);
+    if (e) return e;
+    e = check_mla(margs);
+    if (e) return e;
+    if (K < 1) return LISFA_ERR_BAD_SHAPE;
+    if (iargs->R != margs->R) return LISFA_ERR_BAD_SHAPE;
+    if (iargs->R == 0) return LISFA_OK;
+    if (!out) return LISFA_ERR_NULL_ARG;
+    if (!aligned(out, 8)) return LISFA_ERR_BAD_SHAPE;
+    return LISFA_OK;
+}
+
+// The layer on validated arguments, scores in row chunks of at most score_cap
+// bytes, with the workspace at w (laid out by fused_layout with the same cap).
+int fused_run(const lisfa_indexer_args* iargs, const lisfa_mla_args* margs, int32_t K, int32_t* idx_out, void* out,
+              float* lse, uint8_t* w, int64_t score_cap, hipStream_t st) {
+    const int32_t R = iargs->R;
+    const FusedLayout L = fused_layout(R, iargs->max_visible, K, margs->H, margs->D_latent, score_cap);
+    float* scores = (float*)(w + L.scores);
+    int32_t* idx = idx_out ? idx_out : (int32_t*)(w + L.idx);
+    void* sfa_ws = w + L.sfa;
+
+    const int64_t ld = scores_ld(iargs->max_visible) > 0 ? scores_ld(iargs->max_visible) : 64;
+    const int64_t rc = fused_chunk_rows(R, iargs->max_visible, score_cap);
+    const int qg = (iargs->rows_per_group % 16 == 0) ? 16 : (iargs->rows_per_group % 8 == 0) ? 8 : 1;
+    const int elt = iargs->k_cache.dtype == LISFA_BF16 ? 2 : 1;
+    const bool mx = iargs->k_cache.dtype == LISFA_MXFP8;
+    IndexerDev d = to_dev(iargs);
+    for (int64_t c0 = 0; c0 < R; c0 += rc) {
+        const int64_t c1 = c0 + rc < R ? c0 + rc : R;
+        IndexerDev dc = d;
+        dc.R = (int32_t)(c1 - c0);
+        dc.q = d.q + c0 * (int64_t)iargs->H_I * iargs->D_I * elt;
+        dc.w = d.w + c0 * iargs->H_I;
+        if (d.q_scale) dc.q_scale = d.q_scale + c0 * (iargs->q_scale_per_head ? iargs->H_I : 1);
+        if (mx) dc.q_mx_scale = d.q_mx_scale + c0 * (int64_t)iargs->H_I * (iargs->D_I / 32);
+        dc.row_seq = d.row_seq + c0;
+        dc.row_pos = d.row_pos + c0;
+        if (iargs->max_visible > 0) {
+            hipError_t he = li_score_dispatch(dc, iargs->D_I, iargs->k_cache.dtype, qg, scores, ld,
+                                              iargs->max_visible, st);
+            if (he != hipSuccess) return LISFA_ERR_HIP;
+        }
+        hipError_t he = topk_dispatch(scores, ld, dc.row_pos, dc.R, K, idx + c0 * K, w + L.cand, st);
+        if (he != hipSuccess) return LISFA_ERR_HIP;
+    }
+    const MlaDev md = to_dev(margs, idx, K);
+    return hip_status(sfa_dispatch(md, margs->D_latent, kv_mode(margs->kv_cache), (__bf16*)out,
+                                   nullptr, lse, sfa_ws, st));
+}
+
+// Scratch of the allocation-free fused entry point: one array per GPU, held
+// until the process ends.  In host code `scratch` only names the array; its
+// device address (one per GPU) comes from hipGetSymbolAddress, taken once per
+// device with that device current.
+constexpr size_t kNoAllocScratchBytes = LISFA_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+uint8_t* noalloc_scratch(hipStream_t stream) {
+    int dev = -1;
+    if (stream != nullptr) {
+        if (hipStreamGetDevice(stream, &dev) != hipSuccess) return nullptr;
+    } else if (hipGetDevice(&dev) != hipSuccess) {
+        return nullptr;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    static std::mutex mu;
+    static uint8_t* ptr[kMaxDevices] = {};
+    std::lock_guard<std::mutex> lock(mu);
+    if (ptr[dev] == nullptr) {
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) (void)hipSetDevice(cur);
+        if (e != hipSuccess || p == nullptr) return nullptr;
+        ptr[dev] = (uint8_t*)p;
+    }
+    return ptr[dev];
 }
 
 }  // namespace
@@ -354,52 +444,30 @@ int zigzag_restore(const void* src, void* dst, int64_t n, int32_t G, int64_t row
 
 int li_topk_sfa(const lisfa_indexer_args* iargs, const lisfa_mla_args* margs, int32_t K, int32_t* idx_out,
                 void* out, float* lse, void* ws, size_t ws_bytes, lisfa_stream_t stream) {
-    int e = check_indexer(iargs);
-    if (e) return e;
-    e = check_mla(margs);
-    if (e) return e;
-    if (K < 1) return LISFA_ERR_BAD_SHAPE;
-    if (iargs->R != margs->R) return LISFA_ERR_BAD_SHAPE;
-    const int32_t R = iargs->R;
-    if (R == 0) return LISFA_OK;
-    if (!out) return LISFA_ERR_NULL_ARG;
-    if (!aligned(out, 8)) return LISFA_ERR_BAD_SHAPE;
-    const FusedLayout L = fused_layout(R, iargs->max_visible, K, margs->H, margs->D_latent);
+    int e = check_fused(iargs, margs, K, out);
+    if (e || iargs->R == 0) return e;
+    const FusedLayout L = fused_layout(iargs->R, iargs->max_visible, K, margs->H, margs->D_latent);
     if (!ws || ws_bytes < L.total) return LISFA_ERR_WORKSPACE;
     if (!aligned(ws, 256)) return LISFA_ERR_BAD_SHAPE;
-    hipStream_t st = (hipStream_t)stream;
-    uint8_t* w = (uint8_t*)ws;
-    float* scores = (float*)(w + L.scores);
-    int32_t* idx = idx_out ? idx_out : (int32_t*)(w + L.idx);
-    void* sfa_ws = w + L.sfa;
+    return fused_run(iargs, margs, K, idx_out, out, lse, (uint8_t*)ws, kScoreScratchCap, (hipStream_t)stream);
+}
 
-    const int64_t ld = scores_ld(iargs->max_visible) > 0 ? scores_ld(iargs->max_visible) : 64;
-    const int64_t rc = fused_chunk_rows(R, iargs->max_visible);
-    const int qg = (iargs->rows_per_group % 16 == 0) ? 16 : (iargs->rows_per_group % 8 == 0) ? 8 : 1;
-    const int elt = iargs->k_cache.dtype == LISFA_BF16 ? 2 : 1;
-    const bool mx = iargs->k_cache.dtype == LISFA_MXFP8;
-    IndexerDev d = to_dev(iargs);
-    for (int64_t c0 = 0; c0 < R; c0 += rc) {
-        const int64_t c1 = c0 + rc < R ? c0 + rc : R;
-        IndexerDev dc = d;
-        dc.R = (int32_t)(c1 - c0);
-        dc.q = d.q + c0 * (int64_t)iargs->H_I * iargs->D_I * elt;
-        dc.w = d.w + c0 * iargs->H_I;
-        if (d.q_scale) dc.q_scale = d.q_scale + c0 * (iargs->q_scale_per_head ? iargs->H_I : 1);
-        if (mx) dc.q_mx_scale = d.q_mx_scale + c0 * (int64_t)iargs->H_I * (iargs->D_I / 32);
-        dc.row_seq = d.row_seq + c0;
-        dc.row_pos = d.row_pos + c0;
-        if (iargs->max_visible > 0) {
-            hipError_t he = li_score_dispatch(dc, iargs->D_I, iargs->k_cache.dtype, qg, scores, ld,
-                                              iargs->max_visible, st);
-            if (he != hipSuccess) return LISFA_ERR_HIP;
-        }
-        hipError_t he = topk_dispatch(scores, ld, dc.row_pos, dc.R, K, idx + c0 * K, w + L.cand, st);
-        if (he != hipSuccess) return LISFA_ERR_HIP;
+int li_topk_sfa_noalloc(const lisfa_indexer_args* iargs, const lisfa_mla_args* margs, int32_t K,
+                        int32_t* idx_out, void* out, float* lse, lisfa_stream_t stream) {
+    int e = check_fused(iargs, margs, K, out);
+    if (e || iargs->R == 0) return e;
+    // the largest score chunk whose layout fits the scratch array (more, smaller
+    // chunks when it must); sizes whose smallest layout does not fit are refused
+    int64_t cap = kScoreScratchCap;
+    FusedLayout L = fused_layout(iargs->R, iargs->max_visible, K, margs->H, margs->D_latent, cap);
+    while (L.total > kNoAllocScratchBytes && fused_chunk_rows(iargs->R, iargs->max_visible, cap) > 16) {
+        cap /= 2;
+        L = fused_layout(iargs->R, iargs->max_visible, K, margs->H, margs->D_latent, cap);
     }
-    const MlaDev md = to_dev(margs, idx, K);
-    return hip_status(sfa_dispatch(md, margs->D_latent, kv_mode(margs->kv_cache), (__bf16*)out,
-                                   nullptr, lse, sfa_ws, st));
+    if (L.total > kNoAllocScratchBytes) return LISFA_ERR_WORKSPACE;
+    uint8_t* w = noalloc_scratch((hipStream_t)stream);
+    if (!w) return LISFA_ERR_HIP;
+    return fused_run(iargs, margs, K, idx_out, out, lse, w, cap, (hipStream_t)stream);
 }
 
 int indexer_q_quant(const void* q, int32_t R, int32_t H_I, int32_t D_I, int32_t dtype, void* q_out,

@@ -183,6 +183,26 @@ def test_fused_validation(clib):
                             None) == C.LISFA_ERR_BAD_SHAPE
 
 
+def test_noalloc_validation(clib):
+    """The allocation-free entry validates like li_topk_sfa and refuses, before
+    touching the GPU, sizes whose smallest layout does not fit its scratch."""
+    a, m = _idx_args(R=2), _mla_args(R=3)
+    assert clib.li_topk_sfa_noalloc(ctypes.byref(a), ctypes.byref(m), 2048, None, 16, None,
+                                    None) == C.LISFA_ERR_BAD_SHAPE
+    m = _mla_args(R=2)
+    assert clib.li_topk_sfa_noalloc(ctypes.byref(a), ctypes.byref(m), 0, None, 16, None,
+                                    None) == C.LISFA_ERR_BAD_SHAPE
+    assert clib.li_topk_sfa_noalloc(ctypes.byref(a), ctypes.byref(m), 2048, None, None, None,
+                                    None) == C.LISFA_ERR_NULL_ARG
+    # 32768 rows x 2048 indices alone take 256 MB of the 64 MB array
+    a, m = _idx_args(R=32768), _mla_args(R=32768)
+    assert clib.li_topk_sfa_noalloc(ctypes.byref(a), ctypes.byref(m), 2048, None, 16, None,
+                                    None) == C.LISFA_ERR_WORKSPACE
+    a, m = _idx_args(R=0), _mla_args(R=0)
+    assert clib.li_topk_sfa_noalloc(ctypes.byref(a), ctypes.byref(m), 2048, None, None, None,
+                                    None) == C.LISFA_OK
+
+
 def test_python_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(ValueError):
