@@ -3,25 +3,25 @@
 // selected indices; "Large Language Model Inference Acceleration in
 // Practice", section 3.1: Top-K on chip generating index pointers).
 //
-// One workgroup of 1024 threads (16 wavefronts) per query row.  Scores map to
-// order-preserving uint32 keys (-0.0 folded onto +0.0); selection is a radix
-// select on d = key - kmin (so the first digit starts at the top bit of the
-// row's range) followed by an ordered emission that writes the selected
-// positions in ascending order, ties at the K-th value going to the lowest
-// positions.  Every step is integer counting, so the result is deterministic.
-//  * topk_reg_kernel (rows up to 64K positions): thread t keeps the keys of
-//    positions [t * EPT, t * EPT + EPT) in registers; one histogram level
-//    runs over all keys, later levels only over the threshold bin's keys once
-//    they fit in LDS; the emission is a single block scan of per-thread
-//    (greater, equal) counts.
-//  * topk_cand_kernel + topk_merge_kernel (rows longer than 64K positions,
-//    and the local / merged selection of a context-parallel split): slices of
+// Scores map to order-preserving uint32 keys (-0.0 folded onto +0.0; NaN
+// above +inf).  The K largest keys of a row are selected; equal keys at the
+// K-th place go to the lowest positions; the positions are written in
+// ascending order.  Every step is integer counting, so the result is
+// deterministic and the same on every path.
+//  * topk_row_kernel (topk_select): one 1024-thread workgroup per row.  The
+//    keys stay in registers (rows up to 64K positions; longer rows re-read
+//    them from global memory).  One histogram of the first 12 bits of the
+//    keys finds the bin holding the K-th largest key; only the keys in that
+//    bin or above (a few thousand for K = 2048) move on, to LDS in position
+//    order, where two 10-bit levels over that bin's keys fix the threshold
+//    and one block scan orders the output.  A row with more candidates than
+//    LDS holds (few distinct first digits near the K-th value) takes the
+//    general selection: radix select from the top bit of the row's key range
+//    (tk_select on registers, tk_row_global on global memory).
+//  * topk_cand_kernel + topk_merge_kernel (context-parallel shards): slices of
 //    a row keep their own Top-K as (position, score) pairs, a merge selects
 //    the K best of the gathered pairs.  Every globally selected position is
 //    among its own slice's Top-K, so the result is the same.
-//  * topk_kernel<0> (long rows without workspace): keys are re-read from
-//    global memory on every pass; emission per 1024-position chunk from
-//    wavefront ballots.
 #include "common.hpp"
 
 namespace lisfa {
@@ -59,191 +59,6 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, 
     total = wsum[kTkWaves - 1];
     __syncthreads();
     return before + x - v;
-}
-
-// Keys come from registers (EPT > 0: element i = c * 1024 + tid lives in
-// register c of thread tid, all loads issued up front) or are re-read from
-// global memory on every pass (EPT == 0, rows longer than 64K positions).
-template <int EPT>
-__global__ __launch_bounds__(kTkThreads) void topk_kernel(const float* __restrict__ scores, int64_t ld,
-                                                          const int32_t* __restrict__ row_pos, int K,
-                                                          int32_t* __restrict__ idx) {
-    __shared__ uint32_t hist[kTkBins];
-    __shared__ uint32_t cnt_gt[kTkSegChunks * kTkWaves];
-    __shared__ uint32_t cnt_eq[kTkSegChunks * kTkWaves];
-    __shared__ uint32_t wsum[kTkWaves];
-    __shared__ uint32_t red[2 * kTkWaves];
-    __shared__ uint32_t sh_digit, sh_above;
-
-    const int r = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    int32_t* out = idx + (int64_t)r * K;
-    int64_t n = (int64_t)row_pos[r] + 1;
-    if (n < 0) n = 0;
-    if (n > ld) n = ld;
-    if (n <= K) {
-        for (int64_t i = tid; i < K; i += kTkThreads) out[i] = i < n ? (int32_t)i : -1;
-        return;
-    }
-    const float* s = scores + (int64_t)r * ld;
-    const int64_t nch = (n + kTkThreads - 1) / kTkThreads;
-
-    // 1. keys (registers when they fit)
-    constexpr int NR = EPT > 0 ? EPT : 1;
-    uint32_t kr[NR];
-    if constexpr (EPT > 0) {
-#pragma unroll
-        for (int c = 0; c < EPT; ++c) {
-            const int64_t i = (int64_t)c * kTkThreads + tid;
-            kr[c] = (c < nch && i < n) ? float_key(s[i]) : 0u;
-        }
-    }
-    static_assert(EPT <= kTkSegChunks, "register rows must fit one emission segment");
-    auto key_at = [&](int c, int64_t i) -> uint32_t {
-        if constexpr (EPT > 0) return kr[c];
-        else return float_key(s[i]);
-    };
-    auto for_each = [&](auto&& fn) {   // fn(c, i, key) over this thread's valid positions
-        if constexpr (EPT > 0) {
-#pragma unroll
-            for (int c = 0; c < EPT; ++c) {
-                const int64_t i = (int64_t)c * kTkThreads + tid;
-                if (c < nch && i < n) fn(c, i, kr[c]);
-            }
-        } else {
-            for (int64_t c = 0; c < nch; ++c) {
-                const int64_t i = c * kTkThreads + tid;
-                if (i < n) fn((int)c, i, float_key(s[i]));
-            }
-        }
-    };
-
-    // 2. min / max key
-    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-    for_each([&](int, int64_t, uint32_t k) {
-        kmin = k < kmin ? k : kmin;
-        kmax = k > kmax ? k : kmax;
-    });
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        uint32_t a = __shfl_xor(kmin, o), b = __shfl_xor(kmax, o);
-        kmin = a < kmin ? a : kmin;
-        kmax = b > kmax ? b : kmax;
-    }
-    if (lane == 0) {
-        red[wave] = kmin;
-        red[kTkWaves + wave] = kmax;
-    }
-    __syncthreads();
-    kmin = red[0];
-    kmax = red[kTkWaves];
-#pragma unroll
-    for (int w = 1; w < kTkWaves; ++w) {
-        kmin = red[w] < kmin ? red[w] : kmin;
-        kmax = red[kTkWaves + w] > kmax ? red[kTkWaves + w] : kmax;
-    }
-
-    // 3. radix select on d = key - kmin (a monotone map onto [0, kmax - kmin]):
-    // starting the digits at the top bit of the range spreads the bulk of the
-    // row over many bins (the top bits of the keys themselves may only split
-    // the range into a handful of exponent bins).
-    uint32_t need = (uint32_t)K;
-    uint32_t T;
-    const uint32_t range = kmax - kmin;
-    if (range == 0u) {
-        T = kmin;
-    } else {
-        int hi = 31 - __clz(range);
-        uint32_t prefix = 0u;   // chosen high digits of d
-        while (true) {
-            const int lo = hi - (kTkDigitBits - 1) > 0 ? hi - (kTkDigitBits - 1) : 0;
-            const uint32_t mask = (1u << (hi - lo + 1)) - 1u;
-#pragma unroll
-            for (int j = 0; j < kTkBins / kTkThreads; ++j) hist[tid + j * kTkThreads] = 0u;
-            __syncthreads();
-            for_each([&](int, int64_t, uint32_t k) {
-                const uint32_t d = k - kmin;
-                const bool match = hi == 31 ? true : ((d ^ prefix) >> (hi + 1)) == 0u;
-                if (match) atomicAdd(&hist[(d >> lo) & mask], 1u);
-            });
-            __syncthreads();
-            // thread t owns the kTkBins / 1024 consecutive bins counted from the top
-            constexpr int PB = kTkBins / kTkThreads;
-            uint32_t c[PB], loc = 0u;
-#pragma unroll
-            for (int j = 0; j < PB; ++j) {
-                c[j] = hist[kTkBins - 1 - (tid * PB + j)];
-                loc += c[j];
-            }
-            uint32_t tot;
-            uint32_t E = block_excl_scan(loc, wsum, tot);
-            if (E < need && need <= E + loc) {
-#pragma unroll
-                for (int j = 0; j < PB; ++j) {
-                    if (E < need && need <= E + c[j]) {
-                        sh_digit = (uint32_t)(kTkBins - 1 - (tid * PB + j));
-                        sh_above = E;
-                    }
-                    E += c[j];
-                }
-            }
-            __syncthreads();
-            const uint32_t dg = sh_digit;
-            need -= sh_above;
-            prefix |= dg << lo;
-            __syncthreads();
-            if (lo == 0) break;
-            hi = lo - 1;
-        }
-        T = kmin + prefix;
-    }
-    const uint32_t need_eq = need;
-
-    // 4. ordered emission
-    uint32_t base_gt = 0u, base_eq = 0u;
-    for (int64_t seg0 = 0; seg0 < nch; seg0 += kTkSegChunks) {
-        const int segn = (int)((nch - seg0) < kTkSegChunks ? (nch - seg0) : kTkSegChunks);
-#pragma unroll
-        for (int c = 0; c < (EPT > 0 ? (EPT < kTkSegChunks ? EPT : kTkSegChunks) : kTkSegChunks); ++c) {
-            if (c >= segn) break;
-            const int64_t i = (seg0 + c) * kTkThreads + tid;
-            const bool v = i < n;
-            const uint32_t k = v ? key_at(c, i) : 0u;  // EPT > 0: seg0 == 0 (one segment)
-            const uint64_t bg = __ballot(v && k > T);
-            const uint64_t be = __ballot(v && k == T);
-            if (lane == 0) {
-                cnt_gt[c * kTkWaves + wave] = (uint32_t)__popcll(bg);
-                cnt_eq[c * kTkWaves + wave] = (uint32_t)__popcll(be);
-            }
-        }
-        __syncthreads();
-        const bool own = tid < segn * kTkWaves;
-        const uint32_t g = own ? cnt_gt[tid] : 0u, e = own ? cnt_eq[tid] : 0u;
-        uint32_t tg, te;
-        const uint32_t eg = block_excl_scan(g, wsum, tg);
-        const uint32_t ee = block_excl_scan(e, wsum, te);
-        if (own) {
-            cnt_gt[tid] = eg + base_gt;
-            cnt_eq[tid] = ee + base_eq;
-        }
-        base_gt += tg;
-        base_eq += te;
-        __syncthreads();
-#pragma unroll
-        for (int c = 0; c < (EPT > 0 ? (EPT < kTkSegChunks ? EPT : kTkSegChunks) : kTkSegChunks); ++c) {
-            if (c >= segn) break;
-            const int64_t i = (seg0 + c) * kTkThreads + tid;
-            const bool v = i < n;
-            const uint32_t k = v ? key_at(c, i) : 0u;  // EPT > 0: seg0 == 0 (one segment)
-            const bool gt = v && k > T, eq = v && k == T;
-            const uint64_t bg = __ballot(gt), be = __ballot(eq);
-            const uint32_t rg = cnt_gt[c * kTkWaves + wave] + lanemask_count(bg);
-            const uint32_t re = cnt_eq[c * kTkWaves + wave] + lanemask_count(be);
-            if (gt) out[rg + (re < need_eq ? re : need_eq)] = (int32_t)i;
-            else if (eq && re < need_eq) out[rg + re] = (int32_t)i;
-        }
-        __syncthreads();
-    }
 }
 
 // Exclusive block-wide scan of one 64-bit value per thread; also returns the total.
@@ -480,9 +295,9 @@ __device__ __forceinline__ void tk_select(TkShared& sh, const uint32_t (&kr)[EPT
 template <int EPT>
 __device__ __forceinline__ int tk_load(const float* s, bool vec, int64_t base, int64_t n, uint32_t (&kr)[EPT]) {
     const int nv = n - base >= EPT ? EPT : (n > base ? (int)(n - base) : 0);
-    if (vec && nv == EPT) {
+    if (EPT % 4 == 0 && vec && nv == EPT) {
 #pragma unroll
-        for (int c = 0; c < EPT; c += 4) {
+        for (int c = 0; c + 3 < EPT; c += 4) {
             const f32x4 v = *(const f32x4*)(s + base + c);
             kr[c] = float_key(v.x);
             kr[c + 1] = float_key(v.y);
@@ -496,27 +311,368 @@ __device__ __forceinline__ int tk_load(const float* s, bool vec, int64_t base, i
     return nv;
 }
 
-// One workgroup per row; thread t owns positions [t * EPT, t * EPT + EPT).
-template <int EPT>
-__global__ __launch_bounds__(kTkThreads) void topk_reg_kernel(const float* __restrict__ scores, int64_t ld,
-                                                              const int32_t* __restrict__ row_pos, int K,
-                                                              int32_t* __restrict__ idx) {
-    __shared__ TkShared sh;
-    const int r = blockIdx.x, tid = threadIdx.x;
-    int32_t* out = idx + (int64_t)r * K;
-    int64_t n = (int64_t)row_pos[r] + 1;
+// visible positions of a row: row_pos + 1, clamped to [0, ld]
+__device__ __forceinline__ int64_t tk_row_len(int32_t row_pos, int64_t ld) {
+    int64_t n = (int64_t)row_pos + 1;
     if (n < 0) n = 0;
     if (n > ld) n = ld;
+    return n;
+}
+
+__device__ __forceinline__ void tk_write_all(int32_t* out, int64_t n, int K) {
+    for (int64_t i = threadIdx.x; i < K; i += kTkThreads) out[i] = i < n ? (int32_t)i : -1;
+}
+
+// The K largest of the n > K keys of one row by one workgroup, with the keys
+// re-read from global memory on every pass (no workspace): min / max key, a
+// radix select on d = key - kmin from the top bit of the range (digits of at
+// most 13 bits; starting at the range's top bit spreads the row over many
+// bins even when the keys share their exponent), then the ordered emission:
+// per 1024-position chunk, wavefront ballots count the keys above and equal
+// to the threshold, a block scan turns the counts into output slots.
+__device__ void tk_row_global(TkShared& sh, const float* __restrict__ s, int64_t n, int K,
+                              int32_t* __restrict__ out) {
+    static_assert(2 * kTkSegChunks * kTkWaves <= kTkCandMax, "emission counts fit the candidate buffer");
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint32_t* cnt_gt = sh.cand;
+    uint32_t* cnt_eq = sh.cand + kTkSegChunks * kTkWaves;
+    const int64_t nch = (n + kTkThreads - 1) / kTkThreads;
+
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+    for (int64_t i = tid; i < n; i += kTkThreads) {
+        const uint32_t k = float_key(s[i]);
+        kmin = k < kmin ? k : kmin;
+        kmax = k > kmax ? k : kmax;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const uint32_t a = __shfl_xor(kmin, o), b = __shfl_xor(kmax, o);
+        kmin = a < kmin ? a : kmin;
+        kmax = b > kmax ? b : kmax;
+    }
+    if (lane == 0) {
+        sh.red[wave] = kmin;
+        sh.red[kTkWaves + wave] = kmax;
+    }
+    __syncthreads();
+    kmin = sh.red[0];
+    kmax = sh.red[kTkWaves];
+#pragma unroll
+    for (int w = 1; w < kTkWaves; ++w) {
+        kmin = sh.red[w] < kmin ? sh.red[w] : kmin;
+        kmax = sh.red[kTkWaves + w] > kmax ? sh.red[kTkWaves + w] : kmax;
+    }
+
+    uint32_t need = (uint32_t)K;
+    uint32_t T;
+    const uint32_t range = kmax - kmin;
+    if (range == 0u) {
+        T = kmin;
+    } else {
+        int hi = 31 - __clz(range);
+        uint32_t prefix = 0u;   // chosen high digits of d
+        while (true) {
+            const int lo = hi - (kTkDigitBits - 1) > 0 ? hi - (kTkDigitBits - 1) : 0;
+            const uint32_t mask = (1u << (hi - lo + 1)) - 1u;
+#pragma unroll
+            for (int j = 0; j < kTkBins / kTkThreads; ++j) sh.hist[tid + j * kTkThreads] = 0u;
+            __syncthreads();
+            for (int64_t i = tid; i < n; i += kTkThreads) {
+                const uint32_t d = float_key(s[i]) - kmin;
+                const bool match = hi == 31 ? true : ((d ^ prefix) >> (hi + 1)) == 0u;
+                if (match) atomicAdd(&sh.hist[(d >> lo) & mask], 1u);
+            }
+            __syncthreads();
+            // thread t owns the kTkBins / 1024 consecutive bins counted from the top
+            constexpr int PB = kTkBins / kTkThreads;
+            uint32_t c[PB], loc = 0u;
+#pragma unroll
+            for (int j = 0; j < PB; ++j) {
+                c[j] = sh.hist[kTkBins - 1 - (tid * PB + j)];
+                loc += c[j];
+            }
+            uint32_t tot;
+            uint32_t E = block_excl_scan(loc, sh.wsum, tot);
+            if (E < need && need <= E + loc) {
+#pragma unroll
+                for (int j = 0; j < PB; ++j) {
+                    if (E < need && need <= E + c[j]) {
+                        sh.digit = (uint32_t)(kTkBins - 1 - (tid * PB + j));
+                        sh.above = E;
+                    }
+                    E += c[j];
+                }
+            }
+            __syncthreads();
+            const uint32_t dg = sh.digit;
+            need -= sh.above;
+            prefix |= dg << lo;
+            __syncthreads();
+            if (lo == 0) break;
+            hi = lo - 1;
+        }
+        T = kmin + prefix;
+    }
+    const uint32_t need_eq = need;
+
+    uint32_t base_gt = 0u, base_eq = 0u;
+    for (int64_t seg0 = 0; seg0 < nch; seg0 += kTkSegChunks) {
+        const int segn = (int)((nch - seg0) < kTkSegChunks ? (nch - seg0) : kTkSegChunks);
+        for (int c = 0; c < segn; ++c) {
+            const int64_t i = (seg0 + c) * kTkThreads + tid;
+            const bool v = i < n;
+            const uint32_t k = v ? float_key(s[i]) : 0u;
+            const uint64_t bg = __ballot(v && k > T);
+            const uint64_t be = __ballot(v && k == T);
+            if (lane == 0) {
+                cnt_gt[c * kTkWaves + wave] = (uint32_t)__popcll(bg);
+                cnt_eq[c * kTkWaves + wave] = (uint32_t)__popcll(be);
+            }
+        }
+        __syncthreads();
+        const bool own = tid < segn * kTkWaves;
+        const uint32_t g = own ? cnt_gt[tid] : 0u, e = own ? cnt_eq[tid] : 0u;
+        uint32_t tg, te;
+        const uint32_t eg = block_excl_scan(g, sh.wsum, tg);
+        const uint32_t ee = block_excl_scan(e, sh.wsum, te);
+        if (own) {
+            cnt_gt[tid] = eg + base_gt;
+            cnt_eq[tid] = ee + base_eq;
+        }
+        base_gt += tg;
+        base_eq += te;
+        __syncthreads();
+        for (int c = 0; c < segn; ++c) {
+            const int64_t i = (seg0 + c) * kTkThreads + tid;
+            const bool v = i < n;
+            const uint32_t k = v ? float_key(s[i]) : 0u;
+            const bool gt = v && k > T, eq = v && k == T;
+            const uint64_t bg = __ballot(gt), be = __ballot(eq);
+            const uint32_t rg = cnt_gt[c * kTkWaves + wave] + lanemask_count(bg);
+            const uint32_t re = cnt_eq[c * kTkWaves + wave] + lanemask_count(be);
+            if (gt) out[rg + (re < need_eq ? re : need_eq)] = (int32_t)i;
+            else if (eq && re < need_eq) out[rg + re] = (int32_t)i;
+        }
+        __syncthreads();
+    }
+}
+
+// ------------------------------------------------- one workgroup per row ---
+
+constexpr int kTkD1Bins = 4096;                         // first-digit bins
+constexpr int kTkCandCap = 8192;                        // candidates kept in LDS
+static_assert(kTkD1Bins == 4 * kTkThreads, "four first-digit bins per thread");
+
+struct TkRowShared {
+    uint32_t hist[kTkD1Bins];
+    union {
+        struct {
+            int32_t pos[kTkCandCap];
+            uint32_t key[kTkCandCap];
+        } c;
+        TkShared tk;   // the general selection, for rows with too many candidates
+    } u;
+    uint64_t wsum64[kTkWaves];
+    uint32_t wsum[kTkWaves];
+    uint32_t red[2 * kTkWaves];
+    uint32_t bin, above;
+};
+
+// Top-K of one row per workgroup, the row's keys in registers (n > K
+// visible positions):
+//  1. min and max key; d = key - kmin maps the row onto [0, range] in order;
+//  2. a histogram of the first digit of d (its top 12 bits below the range's
+//     top bit, so the row spreads over up to 4096 bins) and the bin B holding
+//     the K-th largest key: every key with digit > B is selected, the C keys
+//     with digit >= B are the candidates;
+//  3. the candidates' (position, d) move to LDS in position order;
+//  4. 10-bit digits of the remaining bits of d, over the candidates in bin B
+//     only, fix the threshold and how many keys equal to it are taken;
+//  5. the ordered emission over the candidate list.
+// A row with more than kTkCandCap candidates (few distinct digits near the
+// K-th value) takes the general selection on global memory instead.
+template <int EPT>
+__global__ __launch_bounds__(kTkThreads) void topk_row_kernel(const float* __restrict__ scores, int64_t ld,
+                                                              const int32_t* __restrict__ row_pos, int K,
+                                                              int32_t* __restrict__ idx) {
+    __shared__ TkRowShared sh;
+    const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t n = tk_row_len(row_pos[r], ld);
+    int32_t* out = idx + (int64_t)r * K;
     if (n <= K) {
-        for (int64_t i = tid; i < K; i += kTkThreads) out[i] = i < n ? (int32_t)i : -1;
+        tk_write_all(out, n, K);
         return;
     }
-    const bool vec = ((ld & 3) == 0) && ((((uintptr_t)scores) & 15) == 0);
-    const int64_t base = (int64_t)tid * EPT;
+    const float* s = scores + (int64_t)r * ld;
+
+    // 1. keys, min and max
     uint32_t kr[EPT];
-    const int nv = tk_load<EPT>(scores + (int64_t)r * ld, vec, base, n, kr);
-    tk_select<EPT>(sh, kr, TkPrefix{nv}, (uint32_t)K,
-                   [&](int c, uint32_t slot) { out[slot] = (int32_t)(base + c); });
+    const int64_t base = (int64_t)tid * EPT;
+    const bool vec = ((ld & 3) == 0) && ((((uintptr_t)scores) & 15) == 0);
+    const int nv = tk_load<EPT>(s, vec, base, n, kr);
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+    for (int c = 0; c < EPT; ++c) {
+        if (c < nv) {
+            kmin = kr[c] < kmin ? kr[c] : kmin;
+            kmax = kr[c] > kmax ? kr[c] : kmax;
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const uint32_t a = __shfl_xor(kmin, o), b = __shfl_xor(kmax, o);
+        kmin = a < kmin ? a : kmin;
+        kmax = b > kmax ? b : kmax;
+    }
+    if (lane == 0) {
+        sh.red[wave] = kmin;
+        sh.red[kTkWaves + wave] = kmax;
+    }
+    *(u32x4*)&sh.hist[4 * tid] = u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();
+    {
+        const u32x4* rm = (const u32x4*)sh.red;
+#pragma unroll
+        for (int q = 0; q < kTkWaves / 4; ++q) {
+            const u32x4 a = rm[q], b = rm[kTkWaves / 4 + q];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                kmin = a[e] < kmin ? a[e] : kmin;
+                kmax = b[e] > kmax ? b[e] : kmax;
+            }
+        }
+    }
+    const uint32_t range = kmax - kmin;
+    if (range == 0u) {   // all keys equal: the first K positions
+        for (int i = tid; i < K; i += kTkThreads) out[i] = i;
+        return;
+    }
+    const int top = 31 - __clz(range);
+    const int sh1 = top >= 11 ? top - 11 : 0;   // first digit: d >> sh1, below 4096
+
+    // 2. first-digit histogram; thread t owns bins 4095 - 4t - j (j < 4), top first
+#pragma unroll
+    for (int c = 0; c < EPT; ++c)
+        if (c < nv) atomicAdd(&sh.hist[(kr[c] - kmin) >> sh1], 1u);
+    __syncthreads();
+    {
+        uint32_t cb[4], loc = 0u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            cb[j] = sh.hist[kTkD1Bins - 1 - (4 * tid + j)];
+            loc += cb[j];
+        }
+        uint32_t tot;
+        uint32_t E = block_excl_scan(loc, sh.wsum, tot);
+        if (E < (uint32_t)K && (uint32_t)K <= E + loc) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (E < (uint32_t)K && (uint32_t)K <= E + cb[j]) {
+                    sh.bin = (uint32_t)(kTkD1Bins - 1 - (4 * tid + j));
+                    sh.above = E;
+                }
+                E += cb[j];
+            }
+        }
+        __syncthreads();
+    }
+    const uint32_t bin = sh.bin, above = sh.above;
+    const uint32_t C = above + sh.hist[bin];
+    if (C > (uint32_t)kTkCandCap) {
+        tk_row_global(sh.u.tk, s, n, K, out);
+        return;
+    }
+
+    // 3. candidates (position, d) to LDS in position order
+    {
+        uint64_t fm = 0ull;
+#pragma unroll
+        for (int c = 0; c < EPT; ++c) fm |= (uint64_t)(c < nv && ((kr[c] - kmin) >> sh1) >= bin) << c;
+        uint32_t tot;
+        uint32_t at = block_excl_scan((uint32_t)__popcll(fm), sh.wsum, tot);
+#pragma unroll
+        for (int c = 0; c < EPT; ++c) {
+            if ((fm >> c) & 1ull) {
+                sh.u.c.pos[at] = (int32_t)(base + c);
+                sh.u.c.key[at] = kr[c] - kmin;
+                ++at;
+            }
+        }
+    }
+    __syncthreads();
+
+    // 4. the remaining sh1 bits of d, 10 at a time, over bin B's candidates
+    uint32_t need = (uint32_t)K - above;   // taken from bin B, >= 1
+    uint32_t prefix = bin;
+    for (int hi = sh1; hi > 0;) {
+        const int w = hi < 10 ? hi : 10, lo = hi - w;
+        const uint32_t nb = 1u << w;
+        sh.hist[tid] = 0u;
+        __syncthreads();
+        for (uint32_t i = tid; i < C; i += kTkThreads) {
+            const uint32_t d = sh.u.c.key[i];
+            if ((d >> hi) == prefix) atomicAdd(&sh.hist[(d >> lo) & (nb - 1u)], 1u);
+        }
+        __syncthreads();
+        const uint32_t cb = (uint32_t)tid < nb ? sh.hist[nb - 1u - tid] : 0u;
+        uint32_t tot;
+        const uint32_t E = block_excl_scan(cb, sh.wsum, tot);
+        if (E < need && need <= E + cb) {
+            sh.bin = nb - 1u - (uint32_t)tid;
+            sh.above = E;
+        }
+        __syncthreads();
+        prefix = (prefix << w) | sh.bin;
+        need -= sh.above;
+        __syncthreads();
+        hi = lo;
+    }
+    const uint32_t T = prefix, need_eq = need;   // threshold d
+
+    // 5. ordered emission: thread t takes list entries [t * E2, t * E2 + E2)
+    const uint32_t E2 = (C + kTkThreads - 1) / kTkThreads;   // <= 8
+    const uint32_t b0 = (uint32_t)tid * E2;
+    uint32_t g = 0u, e = 0u;
+    for (uint32_t j = 0; j < E2; ++j) {
+        const uint32_t i = b0 + j;
+        if (i < C) {
+            const uint32_t d = sh.u.c.key[i];
+            g += d > T;
+            e += d == T;
+        }
+    }
+    uint64_t total;
+    const uint64_t ex = block_excl_scan64(((uint64_t)e << 32) | g, sh.wsum64, total);
+    uint32_t rg = (uint32_t)ex, re = (uint32_t)(ex >> 32);
+    for (uint32_t j = 0; j < E2; ++j) {
+        const uint32_t i = b0 + j;
+        if (i < C) {
+            const uint32_t d = sh.u.c.key[i];
+            if (d > T) {
+                out[rg + (re < need_eq ? re : need_eq)] = sh.u.c.pos[i];
+                ++rg;
+            } else if (d == T) {
+                if (re < need_eq) out[rg + re] = sh.u.c.pos[i];
+                ++re;
+            }
+        }
+    }
+}
+
+// One workgroup per row with the keys re-read from global memory: rows
+// longer than 64K positions when no workspace is given.
+__global__ __launch_bounds__(kTkThreads) void topk_stream_kernel(const float* __restrict__ scores, int64_t ld,
+                                                                 const int32_t* __restrict__ row_pos, int K,
+                                                                 int32_t* __restrict__ idx) {
+    __shared__ TkShared sh;
+    const int r = blockIdx.x;
+    const int64_t n = tk_row_len(row_pos[r], ld);
+    int32_t* out = idx + (int64_t)r * K;
+    if (n <= K) {
+        tk_write_all(out, n, K);
+        return;
+    }
+    tk_row_global(sh, scores + (int64_t)r * ld, n, K, out);
 }
 
 // Local Top-K of slices: workgroup (s, r) selects among positions
@@ -728,11 +884,14 @@ __global__ __launch_bounds__(kTkThreads) void topk_merge_kernel(const float* __r
     tk_emit_sorted<EPT>(sh, pr, cs, base, selm, K, out, outs);
 }
 
-constexpr int kTkSliceEPT = 16;                            // long rows: slices of 16384 positions
+// ------------------------------------------------------------------ host ---
+
+constexpr int kTkSliceEPT = 16;                            // shard candidates: slices of 16384 positions
 constexpr int64_t kTkSliceLen = (int64_t)kTkThreads * kTkSliceEPT;
 constexpr int kTkMergeMaxN = kTkThreads * 16;            // candidates one merge workgroup holds
 
-// Slices a long row is cut into, or 0 when the two-pass selection does not apply.
+// Slices a long shard row is cut into for topk_candidates, or 0 when its
+// two-pass selection does not apply.
 int topk_slices(int64_t ld, int K) {
     if (ld <= (int64_t)kTkThreads * 64) return 0;
     const int64_t S = (ld + kTkSliceLen - 1) / kTkSliceLen;
@@ -796,33 +955,35 @@ hipError_t topk_candidates_dispatch(const float* scores, int64_t ld, const int32
     return launch_merge(cs, cp, (int64_t)S * K, S * K, R, K, 1, cand_pos, cand_score, stream);
 }
 
+// Rows up to 64K positions: one workgroup per row, keys in registers.
+// Longer rows: with ws, slices of 16384 positions keep their own Top-K and
+// an ordered merge selects (topk_workspace_bytes); without, one
+// workgroup per row re-reads the keys from global memory.
 hipError_t topk_dispatch(const float* scores, int64_t ld, const int32_t* row_pos, int R, int K,
                          int32_t* idx, void* ws, hipStream_t stream) {
     if (R <= 0) return hipSuccess;
-    // registers per thread needed for the longest possible row (ld)
     const int64_t ept = (ld + kTkThreads - 1) / kTkThreads;
-    const int S = topk_slices(ld, K);
-    if (ept > 64 && S > 0 && ws) {
-        // rows longer than one workgroup's registers: slice candidates, then an ordered merge
-        int32_t* cp = (int32_t*)ws;
-        float* cs = (float*)((uint8_t*)ws + (size_t)R * S * K * sizeof(int32_t));
-        hipError_t e = launch_cand(scores, ld, row_pos, R, K, S, kTkSliceEPT, nullptr, cp, cs, stream);
-        if (e != hipSuccess) return e;
-        return launch_merge(cs, cp, (int64_t)S * K, S * K, R, K, 1, idx, nullptr, stream);
+    if (ept > 64) {
+        const int S = topk_slices(ld, K);
+        if (S > 0 && ws) {
+            int32_t* cp = (int32_t*)ws;
+            float* cs = (float*)((uint8_t*)ws + (size_t)R * S * K * sizeof(int32_t));
+            hipError_t e = launch_cand(scores, ld, row_pos, R, K, S, kTkSliceEPT, nullptr, cp, cs, stream);
+            if (e != hipSuccess) return e;
+            return launch_merge(cs, cp, (int64_t)S * K, S * K, R, K, 1, idx, nullptr, stream);
+        }
+        hipLaunchKernelGGL(topk_stream_kernel, dim3((unsigned)R), dim3(kTkThreads), 0, stream, scores, ld, row_pos,
+                           K, idx);
+        return hipGetLastError();
     }
-#define LISFA_TK(E_)                                                                               \
-    hipLaunchKernelGGL((topk_kernel<E_>), dim3((unsigned)R), dim3(kTkThreads), 0, stream, scores, ld, \
+#define LISFA_TK(E_)                                                                                       \
+    hipLaunchKernelGGL((topk_row_kernel<E_>), dim3((unsigned)R), dim3(kTkThreads), 0, stream, scores, ld, \
                        row_pos, K, idx)
-#define LISFA_TKR(E_)                                                                              \
-    hipLaunchKernelGGL((topk_reg_kernel<E_>), dim3((unsigned)R), dim3(kTkThreads), 0, stream, scores, ld,  \
-                       row_pos, K, idx)
-    if (ept <= 8) LISFA_TKR(8);
-    else if (ept <= 16) LISFA_TKR(16);
-    else if (ept <= 32) LISFA_TKR(32);
-    else if (ept <= 64) LISFA_TKR(64);
-    else LISFA_TK(0);
+    if (ept <= 8) LISFA_TK(8);
+    else if (ept <= 16) LISFA_TK(16);
+    else if (ept <= 32) LISFA_TK(32);
+    else LISFA_TK(64);
 #undef LISFA_TK
-#undef LISFA_TKR
     return hipGetLastError();
 }
 

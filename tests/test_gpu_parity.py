@@ -98,6 +98,23 @@ def test_topk_isolated_bit_exact(lib, kind):
             assert np.array_equal(idx[r], ref), (kind, K, r)
 
 
+def test_topk_many_candidates_general_path(lib):
+    """Rows whose first-digit bin at the K-th value holds more candidates than
+    the LDS list keeps (three distinct values over 30000 positions): the
+    general selection takes over; still bit-exact."""
+    say("[case] topk many candidates")
+    g = torch.Generator().manual_seed(7)
+    for ld in (20000, 40000):
+        s = torch.randint(0, 3, (4, ld), generator=g).to(torch.float32) * 0.5
+        pos = torch.tensor([ld - 1, ld // 2, 9000, 12345], dtype=torch.int32)
+        for K in (2048, 9000):
+            idx = _np(gpu_topk(s.cuda(), pos.cuda(), K))
+            for r in range(4):
+                n = int(pos[r]) + 1
+                ref = O.select_topk(s[r, :n].numpy().astype(np.float64), K)
+                assert np.array_equal(idx[r], ref), (ld, K, r)
+
+
 def test_topk_long_rows(lib):
     say("[case] topk long rows")
     for kind in ("gauss", "ties"):
