@@ -784,8 +784,39 @@ def report_prolog(args):
             sc = {"bf16": 0, "fp8": 4, "mxfp8": 4}[fmt]
             by = k.numel() * 2 + n * (128 * elt + sc) + 2 * 128 * 4 + n * 8
             rows.append(("indexer_k_store (LayerNorm)", fmt, n, t * 1e6, by))
+    # the whole prolog: key store and query quantisation in turn on one
+    # stream, or on two side streams side by side (graph-captured, so the
+    # replay runs the two branches concurrently)
+    both = []
+    for n in (64, 4096):
+        g = torch.Generator(device="cuda").manual_seed(n + 1)
+        q = torch.randn(n, 64, 128, device="cuda", generator=g).to(torch.bfloat16)
+        k = torch.randn(n, 128, device="cuda", generator=g).to(torch.bfloat16)
+        gamma = torch.rand(128, device="cuda", generator=g) + 0.5
+        beta = torch.randn(128, device="cuda", generator=g) * 0.1
+        nblk = 2 * (n // 64 + 1)
+        bt = torch.randperm(nblk, device="cuda", generator=g).to(torch.int32).view(1, nblk)
+        seq = torch.zeros(n, dtype=torch.int32, device="cuda")
+        pos = torch.arange(n, dtype=torch.int32, device="cuda")
+        for fmt in ("fp8", "mxfp8"):
+            qo = torch.empty(n, 64, 128, dtype=torch.uint8, device="cuda")
+            qs = (torch.empty(n, dtype=torch.float32, device="cuda") if fmt == "fp8"
+                  else torch.empty(n, 64, 4, dtype=torch.uint8, device="cuda"))
+            data = torch.empty(nblk * 64, 128, dtype=torch.uint8, device="cuda")
+            scale = (torch.empty(nblk * 64, dtype=torch.float32, device="cuda") if fmt == "fp8"
+                     else torch.empty(nblk * 64, 4, dtype=torch.uint8, device="cuda"))
+            kc = lisfa.KVCache(data=data, scale=scale, block_table=bt, block_size=64)
+            t = {}
+            for mode in ("serial", "streams", "fused"):
+                t[mode] = time_on_stream(lambda st: lisfa.indexer_prolog(q, fmt, qo, qs, k, seq, pos, kc, gamma=gamma,
+                                                                         beta=beta, mode=mode, stream=st),
+                                         stream, 2, args.steps, graph=True)
+            both.append((fmt, n, t["serial"] * 1e6, t["streams"] * 1e6, t["fused"] * 1e6))
     for r in rows:
         log(f"[bench] {r[0]} {r[1]} n={r[2]}: {r[3]:.2f} us, {r[4] / r[3] / 1e3:.2f} GB/s")
+    for b_ in both:
+        log(f"[bench] prolog {b_[0]} n={b_[1]}: serial {b_[2]:.2f} us, two streams {b_[3]:.2f} us, "
+            f"one launch {b_[4]:.2f} us")
     print(json.dumps([dict(kernel=r[0], format=r[1], rows=r[2], us=round(r[3], 2), bytes=r[4]) for r in rows]),
           flush=True)
     if args.report_md:
@@ -801,6 +832,15 @@ def report_prolog(args):
             for r in rows:
                 gbs = r[4] / r[3] / 1e3
                 fh.write(f"| {r[0]} | {r[1]} | {r[2]} | {r[3]:.2f} | {gbs:.1f} | {gbs / HBM_PEAK_GBS * 100:.1f} |\n")
+            fh.write("\nThe whole prolog of a step (key LayerNorm + store and query quantisation) with n new keys\n"
+                     "and n query rows, graph-captured: the two calls in turn on one stream (serial); the two on\n"
+                     "side streams that fork from and join back into the launch stream (two streams); the C ABI's\n"
+                     "`indexer_prolog`, one launch whose workgroups split between query rows and keys (one\n"
+                     "launch).  All three write the same bytes\n"
+                     "(`tests/test_gpu_prolog.py::test_prolog_overlap_bit_identical`).\n\n")
+            fh.write("| format | n | serial us | two streams us | one launch us |\n|---|---|---|---|---|\n")
+            for b_ in both:
+                fh.write(f"| {b_[0]} | {b_[1]} | {b_[2]:.2f} | {b_[3]:.2f} | {b_[4]:.2f} |\n")
         log(f"[bench] wrote {args.report_md}")
 
 

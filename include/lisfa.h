@@ -330,6 +330,22 @@ int indexer_k_store(const void* k, int32_t T, int32_t D_I, const float* gamma,
                     const lisfa_cache* k_cache, lisfa_stream_t stream);
 
 /*
+ * indexer_prolog - indexer_k_store and indexer_q_quant in one launch, with the
+ * arguments and results of the two (q_dtype as indexer_q_quant's dtype; the
+ * keys and the queries share D_I).  The pages run these two independent parts
+ * of the prolog side by side on separate streams ("Day0 Inference Adaptation
+ * and Performance Optimization for a New Model", section 3.2); here one
+ * launch splits its workgroups between the query rows and the keys, which
+ * overlaps them without a dependency between streams.  R or T may be 0.
+ * Results are bit-identical to the two calls made one after the other.
+ */
+int indexer_prolog(const void* q, int32_t R, int32_t H_I, int32_t D_I, int32_t q_dtype,
+                   void* q_out, void* q_scale_out, const void* k, int32_t T,
+                   const float* gamma, const float* beta, float eps, int32_t normalize,
+                   const int32_t* tok_seq, const int32_t* tok_pos,
+                   const lisfa_cache* k_cache, lisfa_stream_t stream);
+
+/*
  * li_topk_sfa - the whole layer in one call on one stream: scores, Top-K and
  * sparse attention ("Day0 Inference Adaptation and Performance Optimization
  * for Kimi K3.1 Pro", section 3, and "Large Language Model Inference

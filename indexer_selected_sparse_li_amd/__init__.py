@@ -35,7 +35,8 @@ from . import _lib as _c
 
 __all__ = ["KVCache", "LisfaError", "li_score", "topk_select", "sparse_mla_attn", "li_topk_sfa", "li_topk_sfa_noalloc",
            "topk_candidates", "topk_merge", "sparse_mla_attn_partial", "lse_combine", "zigzag_share",
-           "zigzag_restore", "indexer_q_quant", "indexer_k_store", "workspace_size", "load", "status_string"]
+           "zigzag_restore", "indexer_q_quant", "indexer_k_store", "indexer_prolog", "workspace_size", "load",
+           "status_string"]
 
 
 class LisfaError(RuntimeError):
@@ -348,6 +349,85 @@ def indexer_k_store(k, tok_seq, tok_pos, k_cache: KVCache, gamma=None, beta=None
     c = k_cache.c_struct()
     _check(lib.indexer_k_store(_ptr(k), T, D_I, _ptr(gamma), _ptr(beta), float(eps), int(normalize), _ptr(tok_seq),
                                _ptr(tok_pos), ctypes.byref(c), _stream(stream)), "indexer_k_store")
+
+
+_SIDE_STREAMS = {}
+
+
+def _side_streams(device):
+    """Two streams per device for the prolog, created once (default priority)."""
+    dev = torch.device(device)
+    key = dev.index if dev.index is not None else torch.cuda.current_device()
+    if key not in _SIDE_STREAMS:
+        _SIDE_STREAMS[key] = (torch.cuda.Stream(device=key), torch.cuda.Stream(device=key))
+    return _SIDE_STREAMS[key]
+
+
+def indexer_prolog(q, fmt: Optional[str], q_out, q_scale_out, k, tok_seq, tok_pos, k_cache: KVCache, gamma=None,
+                   beta=None, eps: float = 1e-6, normalize: bool = True, mode: str = "fused", stream=None):
+    """The indexer prolog of one step ahead of li_score: LayerNorm and store
+    of the new keys into k_cache, and the dynamic quantisation of the queries
+    (fmt "fp8" / "mxfp8"; None for bf16 queries, which need none).  The two
+    parts are independent ("Day0 Inference Adaptation ... for a New Model",
+    section 3.2, overlaps them on separate streams).  mode:
+      "fused"   - one launch whose workgroups split between the two (default);
+      "streams" - the two calls on two side streams that fork from `stream`
+                  and that `stream` then waits for;
+      "serial"  - the two calls in turn on `stream`.
+    Every mode writes the same bytes, and everything launched next on
+    `stream` sees them."""
+    main = stream if stream is not None else torch.cuda.current_stream(q.device)
+    if mode == "fused" and fmt is not None:
+        lib = _c.load()
+        R, H_I, D_I = q.shape
+        T = k.shape[0]
+        if q.dtype != torch.bfloat16 or q_out.dtype != torch.uint8 or tuple(q_out.shape) != (R, H_I, D_I):
+            raise ValueError("q must be bf16 and q_out uint8 of the same shape")
+        if k.dtype != torch.bfloat16 or tuple(k.shape) != (T, D_I):
+            raise ValueError("k must be bf16 [T, D_I] with the queries' D_I")
+        want = (torch.float32, (R,)) if fmt == "fp8" else (torch.uint8, (R, H_I, D_I // 32))
+        if q_scale_out.dtype != want[0] or tuple(q_scale_out.shape) != want[1]:
+            raise ValueError(f"q_scale_out must be {want[0]} {want[1]}")
+        for t in (gamma, beta):
+            if t is not None and (t.dtype != torch.float32 or t.numel() != D_I):
+                raise ValueError("gamma / beta must be fp32 [D_I]")
+        dt = {"fp8": _c.LISFA_FP8_E4M3, "mxfp8": _c.LISFA_MXFP8}[fmt]
+        c = k_cache.c_struct()
+        _check(lib.indexer_prolog(_ptr(q), R, H_I, D_I, dt, _ptr(q_out), _ptr(q_scale_out), _ptr(k), T, _ptr(gamma),
+                                  _ptr(beta), float(eps), int(normalize), _ptr(tok_seq), _ptr(tok_pos),
+                                  ctypes.byref(c), _stream(main)), "indexer_prolog")
+        return
+    if mode in ("serial", "fused"):
+        indexer_k_store(k, tok_seq, tok_pos, k_cache, gamma=gamma, beta=beta, eps=eps, normalize=normalize,
+                        stream=main)
+        if fmt is not None:
+            indexer_q_quant(q, fmt, q_out, q_scale_out, stream=main)
+        return
+    if mode != "streams":
+        raise ValueError(f"unknown prolog mode {mode!r}")
+    s_k, s_q = _side_streams(q.device)
+    ready = torch.cuda.Event()
+    ready.record(main)
+    s_k.wait_event(ready)
+    indexer_k_store(k, tok_seq, tok_pos, k_cache, gamma=gamma, beta=beta, eps=eps, normalize=normalize, stream=s_k)
+    done_k = torch.cuda.Event()
+    done_k.record(s_k)
+    used = {s_k: [k, tok_seq, tok_pos, gamma, beta, k_cache.data, k_cache.scale, k_cache.block_table,
+                  k_cache.seq_base]}
+    if fmt is not None:
+        s_q.wait_event(ready)
+        indexer_q_quant(q, fmt, q_out, q_scale_out, stream=s_q)
+        done_q = torch.cuda.Event()
+        done_q.record(s_q)
+        main.wait_event(done_q)
+        used[s_q] = [q, q_out, q_scale_out]
+    main.wait_event(done_k)
+    if not torch.cuda.is_current_stream_capturing():
+        # the caching allocator must not hand these blocks to other work before the side streams finish
+        for st, ts in used.items():
+            for t in ts:
+                if t is not None:
+                    t.record_stream(st)
 
 
 def li_topk_sfa(q_idx, w, k_cache: KVCache, q, kv_cache: KVCache, row_seq, row_pos, K: int,

@@ -31,7 +31,7 @@ LISFA_NOALLOC_SCRATCH_BYTES = 64 << 20
 EXPORTS = (
     "li_score", "topk_select", "sparse_mla_attn", "li_topk_sfa", "li_topk_sfa_noalloc",
     "topk_candidates", "topk_merge", "sparse_mla_attn_partial", "lse_combine",
-    "lisfa_zigzag_share", "zigzag_restore", "indexer_q_quant", "indexer_k_store",
+    "lisfa_zigzag_share", "zigzag_restore", "indexer_q_quant", "indexer_k_store", "indexer_prolog",
     "lisfa_workspace_size", "lisfa_status_string", "lisfa_struct_size", "lisfa_abi_version",
 )
 
@@ -123,6 +123,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.indexer_q_quant.restype = ctypes.c_int
     lib.indexer_k_store.argtypes = [vp, i32, i32, vp, vp, ctypes.c_float, i32, vp, vp, ctypes.POINTER(Cache), vp]
     lib.indexer_k_store.restype = ctypes.c_int
+    lib.indexer_prolog.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, i32, vp, vp, ctypes.c_float, i32, vp, vp,
+                                   ctypes.POINTER(Cache), vp]
+    lib.indexer_prolog.restype = ctypes.c_int
     lib.lisfa_workspace_size.argtypes = [i32, i32, i64, i32, i32, i32]
     lib.lisfa_workspace_size.restype = sz
     lib.lisfa_status_string.argtypes = [i32]

@@ -32,6 +32,10 @@ hipError_t zigzag_restore_dispatch(const void* src, void* dst, int64_t n, int G,
                                    hipStream_t stream);
 void zigzag_share_ranges(int64_t n, int G, int g, int64_t* r4);
 hipError_t q_quant_dispatch(const void* q, int R, int n, int mx, void* out, void* scale_out, hipStream_t stream);
+hipError_t prolog_dispatch(const void* q, int R, int n, int mx, void* q_out, void* q_scale_out, const void* k, int T,
+                           int D_I, const float* gamma, const float* beta, float eps, int normalize,
+                           const int32_t* tok_seq, const int32_t* tok_pos, const CacheDev& c, int dtype,
+                           hipStream_t stream);
 hipError_t k_store_dispatch(const void* k, int T, int D_I, const float* gamma, const float* beta, float eps,
                             int normalize, const int32_t* tok_seq, const int32_t* tok_pos, const CacheDev& c,
                             int dtype, hipStream_t stream);
@@ -286,6 +290,34 @@ uint8_t* noalloc_scratch(hipStream_t stream) {
     return ptr[dev];
 }
 
+int check_q_quant(const void* q, int32_t R, int32_t H_I, int32_t D_I, int32_t dtype, const void* q_out,
+                  const void* q_scale_out) {
+    if (R < 0 || H_I < 1 || H_I > 64) return LISFA_ERR_BAD_SHAPE;
+    if (D_I != 32 && D_I != 128) return LISFA_ERR_UNSUPPORTED;
+    if (dtype != LISFA_FP8_E4M3 && dtype != LISFA_MXFP8) return LISFA_ERR_BAD_DTYPE;
+    if (R == 0) return LISFA_OK;
+    if (!q || !q_out || !q_scale_out) return LISFA_ERR_NULL_ARG;
+    if (!aligned(q, 16) || !aligned(q_out, 16) || !aligned(q_scale_out, 4)) return LISFA_ERR_BAD_SHAPE;
+    return LISFA_OK;
+}
+
+int check_k_store(const void* k, int32_t T, int32_t D_I, float eps, const int32_t* tok_seq, const int32_t* tok_pos,
+                  const lisfa_cache* k_cache) {
+    if (T < 0) return LISFA_ERR_BAD_SHAPE;
+    if (D_I != 32 && D_I != 128) return LISFA_ERR_UNSUPPORTED;
+    if (!k_cache) return LISFA_ERR_NULL_ARG;
+    int e = check_cache(*k_cache, D_I);
+    if (e) return e;
+    if (k_cache->dtype == LISFA_FP8_TILE128) return LISFA_ERR_BAD_DTYPE;   // a latent-cache format
+    if (k_cache->dtype == LISFA_FP8_E4M3 && k_cache->scale_group_tokens != 1) return LISFA_ERR_BAD_SHAPE;
+    if (!(eps >= 0.f)) return LISFA_ERR_BAD_SHAPE;
+    if (T == 0) return LISFA_OK;
+    if (!k || !tok_seq || !tok_pos) return LISFA_ERR_NULL_ARG;
+    if (!aligned(k, 4) || (k_cache->dtype == LISFA_FP8_E4M3 && !aligned(k_cache->scale, 4))) return LISFA_ERR_BAD_SHAPE;
+    return LISFA_OK;
+}
+
+
 }  // namespace
 }  // namespace lisfa
 
@@ -472,30 +504,33 @@ int li_topk_sfa_noalloc(const lisfa_indexer_args* iargs, const lisfa_mla_args* m
 
 int indexer_q_quant(const void* q, int32_t R, int32_t H_I, int32_t D_I, int32_t dtype, void* q_out,
                     void* q_scale_out, lisfa_stream_t stream) {
-    if (R < 0 || H_I < 1 || H_I > 64) return LISFA_ERR_BAD_SHAPE;
-    if (D_I != 32 && D_I != 128) return LISFA_ERR_UNSUPPORTED;
-    if (dtype != LISFA_FP8_E4M3 && dtype != LISFA_MXFP8) return LISFA_ERR_BAD_DTYPE;
-    if (R == 0) return LISFA_OK;
-    if (!q || !q_out || !q_scale_out) return LISFA_ERR_NULL_ARG;
-    if (!aligned(q, 16) || !aligned(q_out, 16) || !aligned(q_scale_out, 4)) return LISFA_ERR_BAD_SHAPE;
+    const int e = check_q_quant(q, R, H_I, D_I, dtype, q_out, q_scale_out);
+    if (e || R == 0) return e;
     return hip_status(q_quant_dispatch(q, R, H_I * D_I, dtype == LISFA_MXFP8, q_out, q_scale_out,
                                        (hipStream_t)stream));
+}
+
+
+int indexer_prolog(const void* q, int32_t R, int32_t H_I, int32_t D_I, int32_t q_dtype, void* q_out,
+                   void* q_scale_out, const void* k, int32_t T, const float* gamma, const float* beta, float eps,
+                   int32_t normalize, const int32_t* tok_seq, const int32_t* tok_pos, const lisfa_cache* k_cache,
+                   lisfa_stream_t stream) {
+    int e = check_q_quant(q, R, H_I, D_I, q_dtype, q_out, q_scale_out);
+    if (e) return e;
+    e = check_k_store(k, T, D_I, eps, tok_seq, tok_pos, k_cache);
+    if (e) return e;
+    if (R == 0 && T == 0) return LISFA_OK;
+    return hip_status(prolog_dispatch(q, R, H_I * D_I, q_dtype == LISFA_MXFP8, q_out, q_scale_out, k, T, D_I, gamma,
+                                      beta, eps, normalize != 0, tok_seq, tok_pos, to_dev(*k_cache), k_cache->dtype,
+                                      (hipStream_t)stream));
 }
 
 int indexer_k_store(const void* k, int32_t T, int32_t D_I, const float* gamma, const float* beta, float eps,
                     int32_t normalize, const int32_t* tok_seq, const int32_t* tok_pos, const lisfa_cache* k_cache,
                     lisfa_stream_t stream) {
-    if (T < 0) return LISFA_ERR_BAD_SHAPE;
-    if (D_I != 32 && D_I != 128) return LISFA_ERR_UNSUPPORTED;
-    if (!k_cache) return LISFA_ERR_NULL_ARG;
-    int e = check_cache(*k_cache, D_I);
+    int e = check_k_store(k, T, D_I, eps, tok_seq, tok_pos, k_cache);
     if (e) return e;
-    if (k_cache->dtype == LISFA_FP8_TILE128) return LISFA_ERR_BAD_DTYPE;   // a latent-cache format
-    if (k_cache->dtype == LISFA_FP8_E4M3 && k_cache->scale_group_tokens != 1) return LISFA_ERR_BAD_SHAPE;
-    if (!(eps >= 0.f)) return LISFA_ERR_BAD_SHAPE;
     if (T == 0) return LISFA_OK;
-    if (!k || !tok_seq || !tok_pos) return LISFA_ERR_NULL_ARG;
-    if (!aligned(k, 4) || (k_cache->dtype == LISFA_FP8_E4M3 && !aligned(k_cache->scale, 4))) return LISFA_ERR_BAD_SHAPE;
     return hip_status(k_store_dispatch(k, T, D_I, gamma, beta, eps, normalize != 0, tok_seq, tok_pos,
                                        to_dev(*k_cache), k_cache->dtype, (hipStream_t)stream));
 }

@@ -14,6 +14,9 @@
 //    (IEEE division) rounded to e4m3; MXFP8: per 32-element block the shared
 //    exponent floor(log2 amax) - 8 (clamped to [-127, 127], 0 for a zero
 //    block), element = x * 2^-shared rounded to e4m3 (exact scaling).
+//  * indexer_prolog: both in one launch, the workgroups split between the
+//    query rows and the keys (the overlap of the two parts without a second
+//    stream).
 //  * indexer_k_store: one wavefront per new key.  Optional LayerNorm in fp32
 //    (y = (x - mean) / sqrt(var + eps) * gamma + beta, biased variance), then
 //    the cache's format: bf16, fp8 with a per-token scale, or MXFP8, written
@@ -60,10 +63,9 @@ __device__ __forceinline__ int mx_shared_exp(float amax) {
 // holds the 32-element block t (four 16-byte loads) in registers, so the row
 // is read once whichever the format.
 template <bool MX>
-__global__ __launch_bounds__(256) void q_quant_kernel(const uint16_t* __restrict__ q, int n, uint8_t* __restrict__ out,
-                                                      void* __restrict__ scale_out) {
-    __shared__ float red[4];
-    const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__device__ __forceinline__ void q_quant_row(const uint16_t* __restrict__ q, int n, uint8_t* __restrict__ out,
+                                            void* __restrict__ scale_out, int r, float* red) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const bool on = tid < n / 32;
     float v[32];
     float amax = 0.f;
@@ -114,6 +116,13 @@ __global__ __launch_bounds__(256) void q_quant_kernel(const uint16_t* __restrict
     }
 }
 
+template <bool MX>
+__global__ __launch_bounds__(256) void q_quant_kernel(const uint16_t* __restrict__ q, int n, uint8_t* __restrict__ out,
+                                                      void* __restrict__ scale_out) {
+    __shared__ float red[4];
+    q_quant_row<MX>(q, n, out, scale_out, blockIdx.x, red);
+}
+
 hipError_t q_quant_dispatch(const void* q, int R, int n, int mx, void* out, void* scale_out, hipStream_t stream) {
     if (R <= 0) return hipSuccess;
     if (n > 256 * 32 || n % 32 != 0) return hipErrorInvalidValue;
@@ -131,13 +140,13 @@ hipError_t q_quant_dispatch(const void* q, int R, int n, int mx, void* out, void
 // One wavefront per key: lane l holds elements 2l, 2l + 1 (D_I = 128) or,
 // for D_I = 32, lanes 0..15 hold them.  FMT: 0 bf16, 1 fp8 per token, 2 MXFP8.
 template <int DI, int FMT>
-__global__ __launch_bounds__(64) void k_store_kernel(const uint32_t* __restrict__ k, int T, const float* __restrict__ gamma,
-                                                     const float* __restrict__ beta, float eps, int normalize,
-                                                     const int32_t* __restrict__ tok_seq,
-                                                     const int32_t* __restrict__ tok_pos, CacheDev c) {
+__device__ __forceinline__ void k_store_key(const uint32_t* __restrict__ k, const float* __restrict__ gamma,
+                                            const float* __restrict__ beta, float eps, int normalize,
+                                            const int32_t* __restrict__ tok_seq, const int32_t* __restrict__ tok_pos,
+                                            const CacheDev& c, int t) {
     static_assert(DI == 32 || DI == 128, "indexer key width");
     constexpr int ACT = DI / 2;          // active lanes
-    const int t = blockIdx.x, lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
     // destination slot; keys the cache cannot address are skipped
     const int seq = tok_seq[t], pos = tok_pos[t];
     int64_t slot = -1;
@@ -203,13 +212,77 @@ __global__ __launch_bounds__(64) void k_store_kernel(const uint32_t* __restrict_
     }
 }
 
+template <int DI, int FMT>
+__global__ __launch_bounds__(64) void k_store_kernel(const uint32_t* __restrict__ k, const float* __restrict__ gamma,
+                                                     const float* __restrict__ beta, float eps, int normalize,
+                                                     const int32_t* __restrict__ tok_seq,
+                                                     const int32_t* __restrict__ tok_pos, CacheDev c) {
+    k_store_key<DI, FMT>(k, gamma, beta, eps, normalize, tok_seq, tok_pos, c, blockIdx.x);
+}
+
+// both ----------------------------------------------------------------------
+
+// The two parts of the prolog in one launch: workgroups 0..R-1 quantise a
+// query row each, the others store four keys each (one per wavefront), so
+// the two independent parts run side by side without a second launch or a
+// dependency between streams.
+constexpr int kKeysPerGroup = 4;
+
+template <bool MX, int DI, int FMT>
+__global__ __launch_bounds__(256) void prolog_kernel(const uint16_t* __restrict__ q, int R, int n,
+                                                     uint8_t* __restrict__ q_out, void* __restrict__ q_scale_out,
+                                                     const uint32_t* __restrict__ k, int T,
+                                                     const float* __restrict__ gamma, const float* __restrict__ beta,
+                                                     float eps, int normalize, const int32_t* __restrict__ tok_seq,
+                                                     const int32_t* __restrict__ tok_pos, CacheDev c) {
+    __shared__ float red[4];
+    const int b = blockIdx.x;
+    if (b < R) {
+        q_quant_row<MX>(q, n, q_out, q_scale_out, b, red);
+        return;
+    }
+    const int t = (b - R) * kKeysPerGroup + (threadIdx.x >> 6);
+    if (t < T) k_store_key<DI, FMT>(k, gamma, beta, eps, normalize, tok_seq, tok_pos, c, t);
+}
+
+hipError_t prolog_dispatch(const void* q, int R, int n, int mx, void* q_out, void* q_scale_out, const void* k, int T,
+                           int D_I, const float* gamma, const float* beta, float eps, int normalize,
+                           const int32_t* tok_seq, const int32_t* tok_pos, const CacheDev& c, int dtype,
+                           hipStream_t stream) {
+    if (n > 256 * 32 || n % 32 != 0) return hipErrorInvalidValue;
+    const int groups = R + (T + kKeysPerGroup - 1) / kKeysPerGroup;
+    if (groups <= 0) return hipSuccess;
+    const int fmt = dtype == LISFA_MXFP8 ? 2 : (dtype == LISFA_FP8_E4M3 ? 1 : 0);
+#define LISFA_PL(MX_, DI_, F_)                                                                                  \
+    if ((mx != 0) == MX_ && D_I == DI_ && fmt == F_) {                                                          \
+        hipLaunchKernelGGL((prolog_kernel<MX_, DI_, F_>), dim3((unsigned)groups), dim3(256), 0, stream,        \
+                           (const uint16_t*)q, R, n, (uint8_t*)q_out, q_scale_out, (const uint32_t*)k, T, gamma, \
+                           beta, eps, normalize, tok_seq, tok_pos, c);                                          \
+        return hipGetLastError();                                                                               \
+    }
+    LISFA_PL(false, 128, 0)
+    LISFA_PL(false, 128, 1)
+    LISFA_PL(false, 128, 2)
+    LISFA_PL(false, 32, 0)
+    LISFA_PL(false, 32, 1)
+    LISFA_PL(false, 32, 2)
+    LISFA_PL(true, 128, 0)
+    LISFA_PL(true, 128, 1)
+    LISFA_PL(true, 128, 2)
+    LISFA_PL(true, 32, 0)
+    LISFA_PL(true, 32, 1)
+    LISFA_PL(true, 32, 2)
+#undef LISFA_PL
+    return hipErrorInvalidValue;
+}
+
 hipError_t k_store_dispatch(const void* k, int T, int D_I, const float* gamma, const float* beta, float eps,
                             int normalize, const int32_t* tok_seq, const int32_t* tok_pos, const CacheDev& c,
                             int dtype, hipStream_t stream) {
     if (T <= 0) return hipSuccess;
 #define LISFA_KS(DI_, F_)                                                                                    \
     if (D_I == DI_ && fmt == F_) {                                                                           \
-        hipLaunchKernelGGL((k_store_kernel<DI_, F_>), dim3((unsigned)T), dim3(64), 0, stream, (const uint32_t*)k, T, \
+        hipLaunchKernelGGL((k_store_kernel<DI_, F_>), dim3((unsigned)T), dim3(64), 0, stream, (const uint32_t*)k,    \
                            gamma, beta, eps, normalize, tok_seq, tok_pos, c);                              \
         return hipGetLastError();                                                                            \
     }

@@ -288,3 +288,23 @@ def test_prolog_validation(clib):
     assert clib.indexer_k_store(16, 4, 128, None, None, 1e-6, 1, None, 16, ctypes.byref(kc), None) == \
         C.LISFA_ERR_NULL_ARG
     assert clib.indexer_k_store(None, 0, 128, None, None, 1e-6, 1, None, None, ctypes.byref(kc), None) == C.LISFA_OK
+
+
+def test_prolog_one_launch_validation(clib):
+    """indexer_prolog applies both calls' checks; nothing to do is OK."""
+    kc = _fake_cache()
+    args = dict(gamma=None, beta=None, eps=1e-6, normalize=1)
+
+    def call(q=16, R=2, H_I=64, D_I=128, dt=C.LISFA_MXFP8, qo=16, qs=16, k=16, T=4, eps=1e-6, seq=16, pos=16,
+             cache=ctypes.byref(kc)):
+        return clib.indexer_prolog(q, R, H_I, D_I, dt, qo, qs, k, T, args["gamma"], args["beta"], eps,
+                                   args["normalize"], seq, pos, cache, None)
+
+    assert call(D_I=64) == C.LISFA_ERR_UNSUPPORTED
+    assert call(dt=C.LISFA_BF16) == C.LISFA_ERR_BAD_DTYPE
+    assert call(qs=None) == C.LISFA_ERR_NULL_ARG
+    assert call(qo=24) == C.LISFA_ERR_BAD_SHAPE
+    assert call(eps=-1.0) == C.LISFA_ERR_BAD_SHAPE
+    assert call(seq=None) == C.LISFA_ERR_NULL_ARG
+    assert call(cache=None) == C.LISFA_ERR_NULL_ARG
+    assert call(q=None, R=0, qo=None, qs=None, k=None, T=0, seq=None, pos=None) == C.LISFA_OK

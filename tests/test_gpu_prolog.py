@@ -4,7 +4,10 @@ sides), key store without normalisation (bit-exact in every cache format and
 layout, other slots untouched), with LayerNorm on exactly representable rows
 (bit-exact), and with LayerNorm on Gaussian rows (every stored value a
 correct rounding of a value within 1e-5 relative of the float64 oracle: the
-fp32 LayerNorm may land on the other side of a rounding boundary)."""
+fp32 LayerNorm may land on the other side of a rounding boundary).  The
+prolog with its two parts in one launch, or overlapped on side streams,
+writes the same bytes as the two calls in turn, also when captured in a
+graph and replayed."""
 import numpy as np
 import pytest
 import torch
@@ -174,3 +177,65 @@ def test_k_store_layer_norm_gaussian(lib, fmt):
         sat = np.abs(y / X) > 448
         assert np.all((np.abs(v - y) <= _e4m3_half_step(y / X) * X + tol)[~sat])
         assert np.all(np.abs(O.decode_e4m3(d.numpy())[sat]) == 448)
+
+
+def _prolog_inputs(fmt, n, seed):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(n, 64, 128, generator=g).to(torch.bfloat16).cuda()
+    k = (torch.randn(n, 128, generator=g) * 2).to(torch.bfloat16).cuda()
+    gamma = (torch.rand(128, generator=g) + 0.5).cuda()
+    beta = (torch.randn(128, generator=g) * 0.1).cuda()
+    kc = _cache(fmt, True, 8 * 64 * ((n + 63) // 64 + 1), 128, 4, 2 * ((n + 63) // 64 + 1), seed)
+    flat = np.random.default_rng(seed).choice(4 * 64 * 2 * ((n + 63) // 64 + 1), size=n, replace=False)
+    bps = 2 * ((n + 63) // 64 + 1)
+    seq = torch.tensor(flat // (bps * 64), dtype=torch.int32, device="cuda")
+    pos = torch.tensor(flat % (bps * 64), dtype=torch.int32, device="cuda")
+    qo = torch.full((n, 64, 128), 0xEE, dtype=torch.uint8, device="cuda")
+    qs = (torch.zeros(n, dtype=torch.float32, device="cuda") if fmt == "fp8"
+          else torch.zeros(n, 64, 4, dtype=torch.uint8, device="cuda"))
+    return q, k, gamma, beta, kc, seq, pos, qo, qs
+
+
+def _clone_cache(kc):
+    return lisfa.KVCache(data=kc.data.clone(), scale=None if kc.scale is None else kc.scale.clone(),
+                         block_table=kc.block_table, block_size=kc.block_size)
+
+
+def _bytes(t):
+    return t.view(torch.uint8).cpu()
+
+
+@pytest.mark.parametrize("mode", ["fused", "streams"])
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp8"])
+@pytest.mark.parametrize("n", [64, 4096])
+def test_prolog_overlap_bit_identical(lib, mode, fmt, n):
+    say(f"[case] prolog {mode} {fmt} n={n}")
+    q, k, gamma, beta, kc, seq, pos, qo, qs = _prolog_inputs(fmt, n, 90 + n)
+    kc2, qo2, qs2 = _clone_cache(kc), qo.clone(), qs.clone()
+    lisfa.indexer_prolog(q, fmt, qo, qs, k, seq, pos, kc, gamma=gamma, beta=beta, mode="serial")
+    lisfa.indexer_prolog(q, fmt, qo2, qs2, k, seq, pos, kc2, gamma=gamma, beta=beta, mode=mode)
+    torch.cuda.synchronize()
+    assert torch.equal(_bytes(kc.data), _bytes(kc2.data))
+    assert torch.equal(_bytes(kc.scale), _bytes(kc2.scale))
+    assert torch.equal(qo.cpu(), qo2.cpu()) and torch.equal(_bytes(qs), _bytes(qs2))
+    # captured in a graph: every replay writes the same bytes again
+    kc3, qo3, qs3 = _clone_cache(kc2), torch.zeros_like(qo2), torch.zeros_like(qs2)
+    kc3.data.view(torch.uint8).fill_(0x33)
+    if kc3.scale is not None:
+        kc3.scale.view(torch.uint8).fill_(0x33)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph):
+            lisfa.indexer_prolog(q, fmt, qo3, qs3, k, seq, pos, kc3, gamma=gamma, beta=beta, mode=mode)
+    torch.cuda.current_stream().wait_stream(side)
+    for rep in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(qo3.cpu(), qo.cpu()) and torch.equal(_bytes(qs3), _bytes(qs)), rep
+        written = torch.zeros(kc.data.shape[0], dtype=torch.bool)
+        written[[_slot(kc, int(a), int(b)) for a, b in zip(seq.tolist(), pos.tolist())]] = True
+        assert torch.equal(_bytes(kc3.data)[written], _bytes(kc.data)[written]), rep
+        qo3.zero_()
+        torch.cuda.synchronize()
