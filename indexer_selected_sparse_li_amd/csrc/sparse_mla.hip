@@ -647,11 +647,11 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
     __shared__ __attribute__((aligned(16))) uint8_t pbuf[2][4][64 * 16];   // P^T [slot][head tile][lane]
     __shared__ float alph[2][64];                       // raise factors [slot][head]
     __shared__ int rflag[2][4];                         // raised head tiles [slot][head tile]
-    __shared__ float xmax[2][2][32];                    // per-head tile maxima [head half][key block][head]
-    __shared__ int xflag[2][2];                         // tiles whose maxima are in xmax
+    __shared__ float xmax[2][2][32];                    // fp8 rows: per-head tile maxima [head half][key block][head]
+    __shared__ int xflag[2][2];                         // fp8 rows: tiles whose maxima are in xmax
     __shared__ int s_ntiles;
-    // after the last tile the P ring is free: partial row sums [head half][key
-    // block][head] and the references [head half][head]
+    // after the last tile the P ring is free: partial row sums [key block][head]
+    // (one block for bf16 rows) and the references [head]
     float* const fin_l = (float*)&pbuf[0][0][0];
     float* const fin_m = fin_l + 128;
 
@@ -659,7 +659,8 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int bid = blockIdx.x;
     // the head blocks of one (row, split) get workgroup ids 8 apart: they run on
-    // one XCD and share its L2 for the rows they both gather
+    // one XCD and share its L2 for the rows they both gather (grouping the splits
+    // of a row on one XCD as well measured slower)
     const int hb = (bid >> 3) % nhb;
     const int u = ((bid >> 3) / nhb) * 8 + (bid & 7);
     if (u >= a.R * nsplit) return;
@@ -691,252 +692,468 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
         });
     };
 
-    if (is_q) {
-        // the q-waves build the slot table: every index load of the thread first,
-        // then every block-table lookup (two dependent global round trips)
-        constexpr int EPT = MAXK / NQT;
-        const int qt = tid;                             // 0 .. 255
-        int pidx[EPT];
-#pragma unroll
-        for (int j = 0; j < EPT; ++j) {
-            const int i = j * NQT + qt;
-            pidx[j] = i < nk ? a.idx[(int64_t)r * a.K + k0 + i] : -1;
-        }
-        int64_t sv[EPT];
-#pragma unroll
-        for (int j = 0; j < EPT; ++j) sv[j] = pidx[j] >= 0 ? slot_of(a.kv, seq, pidx[j]) : -1;
-#pragma unroll
-        for (int j = 0; j < EPT; ++j) {
-            const int i = j * NQT + qt;
-            if (i < nt_fill * TROWS) rslot[i] = sv[j] >= 0 ? (uint32_t)sv[j] : 0xFFFFFFFFu;
-            const uint64_t bal = __ballot(sv[j] >= 0);
-            if (lane == 0 && i < nt_fill * TROWS) {
-                vmask[i / 32] = (uint32_t)bal;
-                if (i + 32 < nt_fill * TROWS) vmask[i / 32 + 1] = (uint32_t)(bal >> 32);
-            }
-        }
-    } else if constexpr (KVF == 0) {
-        // p-waves: the slots of their rows of tiles 0 .. LA, looked up directly, so
-        // the first tile loads go out while the table is still being built
-        int32_t es = -1;                                // lane 8 t + k: row 8 pc + k of tile t
-        {
-            const int t = lane >> 3, i = t * TROWS + 8 * pc + (lane & 7);
-            const int p = (t <= LA && i < nk) ? a.idx[(int64_t)r * a.K + k0 + i] : -1;
-            const int64_t sl = p >= 0 ? slot_of(a.kv, seq, p) : -1;
-            es = sl >= 0 ? (int32_t)(uint32_t)sl : -1;
-        }
-#pragma unroll
-        for (int t = 0; t <= LA; ++t) {
-            const uint32_t s = (uint32_t)__shfl(es, 8 * t + (lane >> 3));
-            if (t < nt_fill) issue_rows(s, t);
-        }
-    }
-    __syncthreads();
-    // trailing tiles without a valid row are skipped; at least one tile is
-    // always processed (an empty tile contributes nothing)
-    for (int t = tid; t < nt_fill; t += 512)
-        if (vmask[t] != 0u) atomicMax(&s_ntiles, t + 1);
-    __syncthreads();
-    const int ntiles = s_ntiles;
     const float kLazy = 8.0f;
+    // the last tile with a valid row (trailing tiles without one are skipped; at
+    // least one tile is always processed): the q-waves, which build the slot
+    // table, count between the two prologue barriers
+    auto count_tiles = [&]() {
+        for (int t = tid; t < nt_fill; t += NQT)
+            if (vmask[t] != 0u) atomicMax(&s_ntiles, t + 1);
+    };
 
     if (is_q) {
         // ---------------------------------------------------------------- q-wave
-        const int qh = wave >> 1, kb = wave & 1;
-        // the query in B-operand layout: lane = head, 8 consecutive columns of K-step ks
-        bf16x8 qb[2][KS];
+        if constexpr (KVF == 0) {
+            // q-wave w owns head tile w (16 heads) and all 32 keys of every tile.  The
+            // query in B-operand layout: lane = head, 8 consecutive columns of K-step ks
+            bf16x8 qb[KS];
+            {
+                const int head = hb * 64 + wave * 16 + l16;
 #pragma unroll
-        for (int ht = 0; ht < 2; ++ht) {
-            const int head = hb * 64 + qh * 32 + ht * 16 + l16;
-#pragma unroll
-            for (int j = 0; j < KS; ++j) {
-                if (head < a.H)
-                    qb[ht][j] = *(const bf16x8*)(a.q + (((int64_t)r * a.H + head) * DQK + j * 32 + g * 8) * 2);
-                else
-                    qb[ht][j] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-            }
-        }
-        // key operand of K-step ks: row 16 kb + l16, chunk 4 ks + g (swz8 of the
-        // row does not depend on kb)
-        uint32_t qa[2];
-#pragma unroll
-        for (int par = 0; par < 2; ++par)
-            qa[par] = (uint32_t)(kb * 2 * GB + (l16 >> 3) * GB + (l16 & 7) * 128 +
-                                 (((4 * par + g) ^ sfa_swz8(l16)) << 4));
-        auto qk_op = [&](const lds_u8* T, int ks) -> bf16x8 {   // compile-time ks
-            return *(const lds_bf16x8*)(T + qa[ks & 1] + (ks >> 1) * 1024);
-        };
-        float m2[2] = {-__builtin_inff(), -__builtin_inff()}, lsum[2] = {0.f, 0.f};
-        const float c = a.scale_log2;
-
-        // S^T of this wave's keys of one tile for both head tiles, the maxima
-        // trade, softmax statistics, this key block's half of P^T to LDS slot ps
-        auto q_tile = [&](const lds_u8* T, int buf, uint32_t vm, int ps, int seqno) {
-            f32x4v s[2] = {f32x4v{0.f, 0.f, 0.f, 0.f}, f32x4v{0.f, 0.f, 0.f, 0.f}};   // [head tile]
-            // operand reads in batches of KPB K-steps, software-pipelined: the
-            // reads of batch b + 1 go out before the MFMAs of batch b (the
-            // scheduling barriers keep the compiler from pairing each read with
-            // its MFMAs)
-            constexpr int KPB = KVF == 2 ? 2 : 6;
-            constexpr int NB = KS / KPB;
-            static_assert(KS % KPB == 0, "whole batches");
-            bf16x8 av[2][KPB];
-#pragma unroll
-            for (int j = 0; j < KPB; ++j) av[0][j] = qk_op(T, j);
-            if constexpr (KVF != 2) {
-                static_for<NB>([&](auto bc) {
-                    constexpr int b = decltype(bc)::value;
-                    if constexpr (b + 1 < NB) {
-#pragma unroll
-                        for (int j = 0; j < KPB; ++j) av[(b + 1) & 1][j] = qk_op(T, (b + 1) * KPB + j);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                    for (int j = 0; j < KPB; ++j) {
-                        const int ks = b * KPB + j;
-                        s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[b & 1][j], qb[0][ks], s[0], 0, 0, 0);
-                        s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[b & 1][j], qb[1][ks], s[1], 0, 0, 0);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                });
-            } else {
-                // column tile j = K-steps 4 j .. 4 j + 3 (the rope tile: 16, 17)
-                // accumulates into sc[j & 1]; it is added, times the keys' factor
-                // f_j, after the first batch of the next column tile went out
-                f32x4v sc[2][2];
-#pragma unroll
-                for (int p = 0; p < 2; ++p)
-#pragma unroll
-                    for (int ht = 0; ht < 2; ++ht) sc[p][ht] = f32x4v{0.f, 0.f, 0.f, 0.f};
-                const float* kf = kvf + buf * NTL * TROWS + 16 * kb + 4 * g;
-                auto fold = [&](int j, int p) {   // s += f_j(key) * sc[p]; sc[p] = 0
-                    const f32x4v f = *(const f32x4v*)(kf + j * TROWS);
-#pragma unroll
-                    for (int ht = 0; ht < 2; ++ht) {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) s[ht][i] = __builtin_fmaf(f[i], sc[p][ht][i], s[ht][i]);
-                        sc[p][ht] = f32x4v{0.f, 0.f, 0.f, 0.f};
-                    }
-                };
-                static_for<NB>([&](auto bc) {
-                    constexpr int b = decltype(bc)::value;
-                    constexpr int jt = (b * KPB) / 4;          // column tile of this batch
-                    if constexpr (b + 1 < NB) {
-#pragma unroll
-                        for (int j = 0; j < KPB; ++j) av[(b + 1) & 1][j] = qk_op(T, (b + 1) * KPB + j);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                    for (int j = 0; j < KPB; ++j) {
-                        const int ks = b * KPB + j;
-                        sc[jt & 1][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[b & 1][j], qb[0][ks], sc[jt & 1][0],
-                                                                                 0, 0, 0);
-                        sc[jt & 1][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[b & 1][j], qb[1][ks], sc[jt & 1][1],
-                                                                                 0, 0, 0);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                    // first batch of column tile jt >= 1: the previous tile is complete
-                    if constexpr (jt >= 1 && (b * KPB) % 4 == 0) fold(jt - 1, (jt - 1) & 1);
-                });
-                fold(NTL - 1, (NTL - 1) & 1);
-            }
-            float fk[4];   // KVF 1: the factor of each of this lane's keys
-            if constexpr (KVF == 1) {
-                const f32x4v f = *(const f32x4v*)(kvf + buf * TROWS + 16 * kb + 4 * g);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) fk[i] = f[i];
-                // one factor per row: the logit is scale * f * (q . code)
-                s[0] *= f;
-                s[1] *= f;
-            }
-            if (vm != 0xFFFFFFFFu) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (!((vm >> (16 * kb + 4 * g + i)) & 1u)) {
-                        s[0][i] = -__builtin_inff();
-                        s[1][i] = -__builtin_inff();
-                    }
-            }
-            // per-head maxima over this wave's 16 keys, traded with the partner
-            float tm[2];
-#pragma unroll
-            for (int ht = 0; ht < 2; ++ht) {
-                float m = fmaxf(fmaxf(s[ht][0], s[ht][1]), fmaxf(s[ht][2], s[ht][3]));
-                const auto w16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-                m = fmaxf(__uint_as_float(w16[0]), __uint_as_float(w16[1]));
-                const auto w32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-                tm[ht] = fmaxf(__uint_as_float(w32[0]), __uint_as_float(w32[1]));
-                if (g == 0) xmax[qh][kb][ht * 16 + l16] = tm[ht];
-            }
-            if (lane == 0) __hip_atomic_store(&xflag[qh][kb], seqno, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-            while (__hip_atomic_load(&xflag[qh][kb ^ 1], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != seqno)
-                __builtin_amdgcn_s_sleep(1);
-            // both head tiles side by side (independent chains), without branches
-            float tmax[2], alpha[2], pe[2][4], rs[2];
-            bool any[2];
-#pragma unroll
-            for (int ht = 0; ht < 2; ++ht) tmax[ht] = fmaxf(tm[ht], xmax[qh][kb ^ 1][ht * 16 + l16]) * c;   // c > 0
-#pragma unroll
-            for (int ht = 0; ht < 2; ++ht) {
-                const bool raise = tmax[ht] > m2[ht] + kLazy;   // also true on the first valid tile
-                any[ht] = __ballot(raise) != 0ull;
-                const float mnew = raise ? tmax[ht] : m2[ht];
-                alpha[ht] = raise ? __builtin_amdgcn_exp2f(m2[ht] - mnew) : 1.f;   // m2 = -inf -> 0
-                lsum[ht] *= alpha[ht];
-                m2[ht] = mnew;
-                const float negm = mnew == -__builtin_inff() ? 0.f : -mnew;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) pe[ht][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[ht][i], c, negm));
-                rs[ht] = (pe[ht][0] + pe[ht][1]) + (pe[ht][2] + pe[ht][3]);
-            }
-#pragma unroll
-            for (int ht = 0; ht < 2; ++ht) {
-                const auto w16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(rs[ht]), __float_as_uint(rs[ht]),
-                                                                  false, false);
-                rs[ht] = __uint_as_float(w16[0]) + __uint_as_float(w16[1]);
-            }
-#pragma unroll
-            for (int ht = 0; ht < 2; ++ht) {
-                const auto w32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(rs[ht]), __float_as_uint(rs[ht]),
-                                                                  false, false);
-                lsum[ht] += __uint_as_float(w32[0]) + __uint_as_float(w32[1]);
-            }
-#pragma unroll
-            for (int ht = 0; ht < 2; ++ht) {
-                const int htg = qh * 2 + ht;   // head tile within the block
-                if (kb == 0) {
-                    if (g == 0) alph[ps][htg * 16 + l16] = alpha[ht];
-                    if (lane == 0) rflag[ps][htg] = any[ht] ? 1 : 0;
+                for (int j = 0; j < KS; ++j) {
+                    if (head < a.H)
+                        qb[j] = *(const bf16x8*)(a.q + (((int64_t)r * a.H + head) * DQK + j * 32 + g * 8) * 2);
+                    else
+                        qb[j] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
                 }
-                bf16x4v pb;
+            }
+            // then the slot table: every index load of the thread first,
+            // then every block-table lookup (two dependent global round trips)
+            constexpr int EPT = MAXK / NQT;
+            const int qt = tid;                             // 0 .. 255
+            int pidx[EPT];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) pb[i] = (__bf16)(KVF == 1 ? pe[ht][i] * fk[i] : pe[ht][i]);
-                *(__attribute__((address_space(3))) bf16x4v*)((lds_u8*)pbuf[ps][htg] + lane * 16 + kb * 8) = pb;
+            for (int j = 0; j < EPT; ++j) {
+                const int i = j * NQT + qt;
+                pidx[j] = i < nk ? a.idx[(int64_t)r * a.K + k0 + i] : -1;
             }
-        };
+            int64_t sv[EPT];
+#pragma unroll
+            for (int j = 0; j < EPT; ++j) sv[j] = pidx[j] >= 0 ? slot_of(a.kv, seq, pidx[j]) : -1;
+#pragma unroll
+            for (int j = 0; j < EPT; ++j) {
+                const int i = j * NQT + qt;
+                if (i < nt_fill * TROWS) rslot[i] = sv[j] >= 0 ? (uint32_t)sv[j] : 0xFFFFFFFFu;
+                const uint64_t bal = __ballot(sv[j] >= 0);
+                if (lane == 0 && i < nt_fill * TROWS) {
+                    vmask[i / 32] = (uint32_t)bal;
+                    if (i + 32 < nt_fill * TROWS) vmask[i / 32 + 1] = (uint32_t)(bal >> 32);
+                }
+            }
+            __syncthreads();                                   // the slot table is complete
+            count_tiles();
+            __syncthreads();
+            const int ntiles = s_ntiles;
+            // key operand of K-step ks for key block kb: row 16 kb + l16, chunk 4 ks + g
+            // (swz8 of the row does not depend on kb)
+            uint32_t qa[2];
+#pragma unroll
+            for (int par = 0; par < 2; ++par)
+                qa[par] = (uint32_t)((l16 >> 3) * GB + (l16 & 7) * 128 + (((4 * par + g) ^ sfa_swz8(l16)) << 4));
+            auto qk_op = [&](const lds_u8* T, int kb, int ks) -> bf16x8 {   // compile-time kb, ks
+                return *(const lds_bf16x8*)(T + kb * 2 * GB + qa[ks & 1] + (ks >> 1) * 1024);
+            };
+            float m2 = -__builtin_inff(), lsum = 0.f;
+            const float c = a.scale_log2;
 
-        __syncthreads();                                   // barrier P: tile 0 landed
-        q_tile(tile0, 0, vmask[0], 0, 1);
-        int bq = 1;                                        // buffer of tile t+1
-        for (int t = 0; t < ntiles; ++t) {
-            __syncthreads();                               // barrier t: P(t) published, tile t+1 landed
-            if (t + 1 < ntiles) {
-                const uint32_t vmn = __builtin_amdgcn_readfirstlane(vmask[t + 1]);
-                q_tile(tile0 + bq * TB, bq, vmn, (t + 1) & 1, t + 2);
+            // S^T of the tile's 32 keys (two 16-key blocks) for this wave's 16 heads,
+            // the per-head maxima over all 32 keys inside the wave, softmax statistics,
+            // P^T to LDS slot ps
+            auto q_tile = [&](const lds_u8* T, int buf, uint32_t vm, int ps) {
+                f32x4v s[2] = {f32x4v{0.f, 0.f, 0.f, 0.f}, f32x4v{0.f, 0.f, 0.f, 0.f}};   // [key block]
+                // operand reads in batches of KPB K-steps (both key blocks), software-
+                // pipelined: the reads of batch b + 1 go out before the MFMAs of batch b
+                constexpr int KPB = KVF == 2 ? 2 : 3;
+                constexpr int NB = KS / KPB;
+                static_assert(KS % KPB == 0, "whole batches");
+                bf16x8 av[2][2][KPB];   // [batch parity][key block][K-step]
+#pragma unroll
+                for (int j = 0; j < KPB; ++j) {
+                    av[0][0][j] = qk_op(T, 0, j);
+                    av[0][1][j] = qk_op(T, 1, j);
+                }
+                if constexpr (KVF != 2) {
+                    static_for<NB>([&](auto bc) {
+                        constexpr int b = decltype(bc)::value;
+                        if constexpr (b + 1 < NB) {
+#pragma unroll
+                            for (int j = 0; j < KPB; ++j) {
+                                av[(b + 1) & 1][0][j] = qk_op(T, 0, (b + 1) * KPB + j);
+                                av[(b + 1) & 1][1][j] = qk_op(T, 1, (b + 1) * KPB + j);
+                            }
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                        for (int j = 0; j < KPB; ++j) {
+                            const int ks = b * KPB + j;
+                            s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[b & 1][0][j], qb[ks], s[0], 0, 0, 0);
+                            s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[b & 1][1][j], qb[ks], s[1], 0, 0, 0);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                    });
+                } else {
+                    // column tile j = K-steps 4 j .. 4 j + 3 (the rope tile: 16, 17)
+                    // accumulates into sc[j & 1]; it is added, times the keys' factor
+                    // f_j, after the first batch of the next column tile went out
+                    f32x4v sc[2][2];
+#pragma unroll
+                    for (int p = 0; p < 2; ++p)
+#pragma unroll
+                        for (int kb = 0; kb < 2; ++kb) sc[p][kb] = f32x4v{0.f, 0.f, 0.f, 0.f};
+                    const float* kf = kvf + buf * NTL * TROWS + 4 * g;
+                    auto fold = [&](int j, int p) {   // s += f_j(key) * sc[p]; sc[p] = 0
+#pragma unroll
+                        for (int kb = 0; kb < 2; ++kb) {
+                            const f32x4v f = *(const f32x4v*)(kf + j * TROWS + 16 * kb);
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) s[kb][i] = __builtin_fmaf(f[i], sc[p][kb][i], s[kb][i]);
+                            sc[p][kb] = f32x4v{0.f, 0.f, 0.f, 0.f};
+                        }
+                    };
+                    static_for<NB>([&](auto bc) {
+                        constexpr int b = decltype(bc)::value;
+                        constexpr int jt = (b * KPB) / 4;          // column tile of this batch
+                        if constexpr (b + 1 < NB) {
+#pragma unroll
+                            for (int j = 0; j < KPB; ++j) {
+                                av[(b + 1) & 1][0][j] = qk_op(T, 0, (b + 1) * KPB + j);
+                                av[(b + 1) & 1][1][j] = qk_op(T, 1, (b + 1) * KPB + j);
+                            }
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                        for (int j = 0; j < KPB; ++j) {
+                            const int ks = b * KPB + j;
+                            sc[jt & 1][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[b & 1][0][j], qb[ks], sc[jt & 1][0],
+                                                                                     0, 0, 0);
+                            sc[jt & 1][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[b & 1][1][j], qb[ks], sc[jt & 1][1],
+                                                                                     0, 0, 0);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                        // first batch of column tile jt >= 1: the previous tile is complete
+                        if constexpr (jt >= 1 && (b * KPB) % 4 == 0) fold(jt - 1, (jt - 1) & 1);
+                    });
+                    fold(NTL - 1, (NTL - 1) & 1);
+                }
+                float fk[2][4];   // KVF 1: the factor of each of this lane's keys
+                if constexpr (KVF == 1) {
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb) {
+                        const f32x4v f = *(const f32x4v*)(kvf + buf * TROWS + 16 * kb + 4 * g);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) fk[kb][i] = f[i];
+                        // one factor per row: the logit is scale * f * (q . code)
+                        s[kb] *= f;
+                    }
+                }
+                if (vm != 0xFFFFFFFFu) {
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (!((vm >> (16 * kb + 4 * g + i)) & 1u)) s[kb][i] = -__builtin_inff();
+                }
+                // per-head maximum over the 32 keys: this lane's 8, then across the 4 key groups
+                float tm = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                                 fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+                {
+                    const auto w16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(tm), __float_as_uint(tm), false, false);
+                    tm = fmaxf(__uint_as_float(w16[0]), __uint_as_float(w16[1]));
+                    const auto w32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(tm), __float_as_uint(tm), false, false);
+                    tm = fmaxf(__uint_as_float(w32[0]), __uint_as_float(w32[1]));
+                }
+                const float tmax = tm * c;   // c > 0
+                const bool raise = tmax > m2 + kLazy;   // also true on the first valid tile
+                const bool any = __ballot(raise) != 0ull;
+                const float mnew = raise ? tmax : m2;
+                const float alpha = raise ? __builtin_amdgcn_exp2f(m2 - mnew) : 1.f;   // m2 = -inf -> 0
+                lsum *= alpha;
+                m2 = mnew;
+                const float negm = mnew == -__builtin_inff() ? 0.f : -mnew;
+                float pe[2][4];
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) pe[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], c, negm));
+                float rs = ((pe[0][0] + pe[0][1]) + (pe[0][2] + pe[0][3])) + ((pe[1][0] + pe[1][1]) + (pe[1][2] + pe[1][3]));
+                {
+                    const auto w16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(rs), __float_as_uint(rs), false, false);
+                    rs = __uint_as_float(w16[0]) + __uint_as_float(w16[1]);
+                    const auto w32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(rs), __float_as_uint(rs), false, false);
+                    lsum += __uint_as_float(w32[0]) + __uint_as_float(w32[1]);
+                }
+                if (g == 0) alph[ps][wave * 16 + l16] = alpha;
+                if (lane == 0) rflag[ps][wave] = any ? 1 : 0;
+                // P^T operand: lane (g, head), K-slots 0..3 = keys 4 g + i, 4..7 = keys 16 + 4 g + i
+                bf16x8 pb;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    pb[i] = (__bf16)(KVF == 1 ? pe[0][i] * fk[0][i] : pe[0][i]);
+                    pb[4 + i] = (__bf16)(KVF == 1 ? pe[1][i] * fk[1][i] : pe[1][i]);
+                }
+                *(__attribute__((address_space(3))) bf16x8*)((lds_u8*)pbuf[ps][wave] + lane * 16) = pb;
+            };
+
+            __syncthreads();                                   // barrier P: tile 0 landed
+            q_tile(tile0, 0, vmask[0], 0);
+            int bq = 1;                                        // buffer of tile t+1
+            for (int t = 0; t < ntiles; ++t) {
+                __syncthreads();                               // barrier t: P(t) published, tile t+1 landed
+                if (t + 1 < ntiles) {
+                    const uint32_t vmn = __builtin_amdgcn_readfirstlane(vmask[t + 1]);
+                    q_tile(tile0 + bq * TB, bq, vmn, (t + 1) & 1);
+                }
+                bq = bq == NBUF - 1 ? 0 : bq + 1;
             }
-            bq = bq == NBUF - 1 ? 0 : bq + 1;
-        }
-        __syncthreads();                                   // barrier F: the P ring is no longer read
-        if (g == 0) {
+            __syncthreads();                                   // barrier F: the P ring is no longer read
+            if (g == 0) {
+                fin_l[wave * 16 + l16] = lsum;
+                fin_m[wave * 16 + l16] = m2;
+            }
+            __syncthreads();                                   // barrier E
+        } else {
+            const int qh = wave >> 1, kb = wave & 1;
+            // the query in B-operand layout: lane = head, 8 consecutive columns of K-step ks
+            bf16x8 qb[2][KS];
 #pragma unroll
             for (int ht = 0; ht < 2; ++ht) {
-                fin_l[(qh * 2 + kb) * 32 + ht * 16 + l16] = lsum[ht];
-                if (kb == 0) fin_m[qh * 32 + ht * 16 + l16] = m2[ht];
+                const int head = hb * 64 + qh * 32 + ht * 16 + l16;
+#pragma unroll
+                for (int j = 0; j < KS; ++j) {
+                    if (head < a.H)
+                        qb[ht][j] = *(const bf16x8*)(a.q + (((int64_t)r * a.H + head) * DQK + j * 32 + g * 8) * 2);
+                    else
+                        qb[ht][j] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+                }
             }
+            // then the slot table: every index load of the thread first,
+            // then every block-table lookup (two dependent global round trips)
+            constexpr int EPT = MAXK / NQT;
+            const int qt = tid;                             // 0 .. 255
+            int pidx[EPT];
+#pragma unroll
+            for (int j = 0; j < EPT; ++j) {
+                const int i = j * NQT + qt;
+                pidx[j] = i < nk ? a.idx[(int64_t)r * a.K + k0 + i] : -1;
+            }
+            int64_t sv[EPT];
+#pragma unroll
+            for (int j = 0; j < EPT; ++j) sv[j] = pidx[j] >= 0 ? slot_of(a.kv, seq, pidx[j]) : -1;
+#pragma unroll
+            for (int j = 0; j < EPT; ++j) {
+                const int i = j * NQT + qt;
+                if (i < nt_fill * TROWS) rslot[i] = sv[j] >= 0 ? (uint32_t)sv[j] : 0xFFFFFFFFu;
+                const uint64_t bal = __ballot(sv[j] >= 0);
+                if (lane == 0 && i < nt_fill * TROWS) {
+                    vmask[i / 32] = (uint32_t)bal;
+                    if (i + 32 < nt_fill * TROWS) vmask[i / 32 + 1] = (uint32_t)(bal >> 32);
+                }
+            }
+            __syncthreads();                                   // the slot table is complete
+            count_tiles();
+            __syncthreads();
+            const int ntiles = s_ntiles;
+            // key operand of K-step ks: row 16 kb + l16, chunk 4 ks + g (swz8 of the
+            // row does not depend on kb)
+            uint32_t qa[2];
+#pragma unroll
+            for (int par = 0; par < 2; ++par)
+                qa[par] = (uint32_t)(kb * 2 * GB + (l16 >> 3) * GB + (l16 & 7) * 128 +
+                                     (((4 * par + g) ^ sfa_swz8(l16)) << 4));
+            auto qk_op = [&](const lds_u8* T, int ks) -> bf16x8 {   // compile-time ks
+                return *(const lds_bf16x8*)(T + qa[ks & 1] + (ks >> 1) * 1024);
+            };
+            float m2[2] = {-__builtin_inff(), -__builtin_inff()}, lsum[2] = {0.f, 0.f};
+            const float c = a.scale_log2;
+
+            // S^T of this wave's keys of one tile for both head tiles, the maxima
+            // trade, softmax statistics, this key block's half of P^T to LDS slot ps
+            auto q_tile = [&](const lds_u8* T, int buf, uint32_t vm, int ps, int seqno) {
+                f32x4v s[2] = {f32x4v{0.f, 0.f, 0.f, 0.f}, f32x4v{0.f, 0.f, 0.f, 0.f}};   // [head tile]
+                // operand reads in batches of KPB K-steps, software-pipelined: the
+                // reads of batch b + 1 go out before the MFMAs of batch b (the
+                // scheduling barriers keep the compiler from pairing each read with
+                // its MFMAs)
+                constexpr int KPB = KVF == 2 ? 2 : 6;
+                constexpr int NB = KS / KPB;
+                static_assert(KS % KPB == 0, "whole batches");
+                bf16x8 av[2][KPB];
+#pragma unroll
+                for (int j = 0; j < KPB; ++j) av[0][j] = qk_op(T, j);
+                if constexpr (KVF != 2) {
+                    static_for<NB>([&](auto bc) {
+                        constexpr int b = decltype(bc)::value;
+                        if constexpr (b + 1 < NB) {
+#pragma unroll
+                            for (int j = 0; j < KPB; ++j) av[(b + 1) & 1][j] = qk_op(T, (b + 1) * KPB + j);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                        for (int j = 0; j < KPB; ++j) {
+                            const int ks = b * KPB + j;
+                            s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[b & 1][j], qb[0][ks], s[0], 0, 0, 0);
+                            s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[b & 1][j], qb[1][ks], s[1], 0, 0, 0);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                    });
+                } else {
+                    // column tile j = K-steps 4 j .. 4 j + 3 (the rope tile: 16, 17)
+                    // accumulates into sc[j & 1]; it is added, times the keys' factor
+                    // f_j, after the first batch of the next column tile went out
+                    f32x4v sc[2][2];
+#pragma unroll
+                    for (int p = 0; p < 2; ++p)
+#pragma unroll
+                        for (int ht = 0; ht < 2; ++ht) sc[p][ht] = f32x4v{0.f, 0.f, 0.f, 0.f};
+                    const float* kf = kvf + buf * NTL * TROWS + 16 * kb + 4 * g;
+                    auto fold = [&](int j, int p) {   // s += f_j(key) * sc[p]; sc[p] = 0
+                        const f32x4v f = *(const f32x4v*)(kf + j * TROWS);
+#pragma unroll
+                        for (int ht = 0; ht < 2; ++ht) {
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) s[ht][i] = __builtin_fmaf(f[i], sc[p][ht][i], s[ht][i]);
+                            sc[p][ht] = f32x4v{0.f, 0.f, 0.f, 0.f};
+                        }
+                    };
+                    static_for<NB>([&](auto bc) {
+                        constexpr int b = decltype(bc)::value;
+                        constexpr int jt = (b * KPB) / 4;          // column tile of this batch
+                        if constexpr (b + 1 < NB) {
+#pragma unroll
+                            for (int j = 0; j < KPB; ++j) av[(b + 1) & 1][j] = qk_op(T, (b + 1) * KPB + j);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                        for (int j = 0; j < KPB; ++j) {
+                            const int ks = b * KPB + j;
+                            sc[jt & 1][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[b & 1][j], qb[0][ks], sc[jt & 1][0],
+                                                                                     0, 0, 0);
+                            sc[jt & 1][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[b & 1][j], qb[1][ks], sc[jt & 1][1],
+                                                                                     0, 0, 0);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                        // first batch of column tile jt >= 1: the previous tile is complete
+                        if constexpr (jt >= 1 && (b * KPB) % 4 == 0) fold(jt - 1, (jt - 1) & 1);
+                    });
+                    fold(NTL - 1, (NTL - 1) & 1);
+                }
+                float fk[4];   // KVF 1: the factor of each of this lane's keys
+                if constexpr (KVF == 1) {
+                    const f32x4v f = *(const f32x4v*)(kvf + buf * TROWS + 16 * kb + 4 * g);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) fk[i] = f[i];
+                    // one factor per row: the logit is scale * f * (q . code)
+                    s[0] *= f;
+                    s[1] *= f;
+                }
+                if (vm != 0xFFFFFFFFu) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (!((vm >> (16 * kb + 4 * g + i)) & 1u)) {
+                            s[0][i] = -__builtin_inff();
+                            s[1][i] = -__builtin_inff();
+                        }
+                }
+                // per-head maxima over this wave's 16 keys, traded with the partner
+                float tm[2];
+#pragma unroll
+                for (int ht = 0; ht < 2; ++ht) {
+                    float m = fmaxf(fmaxf(s[ht][0], s[ht][1]), fmaxf(s[ht][2], s[ht][3]));
+                    const auto w16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+                    m = fmaxf(__uint_as_float(w16[0]), __uint_as_float(w16[1]));
+                    const auto w32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+                    tm[ht] = fmaxf(__uint_as_float(w32[0]), __uint_as_float(w32[1]));
+                    if (g == 0) xmax[qh][kb][ht * 16 + l16] = tm[ht];
+                }
+                if (lane == 0) __hip_atomic_store(&xflag[qh][kb], seqno, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+                while (__hip_atomic_load(&xflag[qh][kb ^ 1], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != seqno)
+                    __builtin_amdgcn_s_sleep(1);
+                // both head tiles side by side (independent chains), without branches
+                float tmax[2], alpha[2], pe[2][4], rs[2];
+                bool any[2];
+#pragma unroll
+                for (int ht = 0; ht < 2; ++ht) tmax[ht] = fmaxf(tm[ht], xmax[qh][kb ^ 1][ht * 16 + l16]) * c;   // c > 0
+#pragma unroll
+                for (int ht = 0; ht < 2; ++ht) {
+                    const bool raise = tmax[ht] > m2[ht] + kLazy;   // also true on the first valid tile
+                    any[ht] = __ballot(raise) != 0ull;
+                    const float mnew = raise ? tmax[ht] : m2[ht];
+                    alpha[ht] = raise ? __builtin_amdgcn_exp2f(m2[ht] - mnew) : 1.f;   // m2 = -inf -> 0
+                    lsum[ht] *= alpha[ht];
+                    m2[ht] = mnew;
+                    const float negm = mnew == -__builtin_inff() ? 0.f : -mnew;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) pe[ht][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[ht][i], c, negm));
+                    rs[ht] = (pe[ht][0] + pe[ht][1]) + (pe[ht][2] + pe[ht][3]);
+                }
+#pragma unroll
+                for (int ht = 0; ht < 2; ++ht) {
+                    const auto w16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(rs[ht]), __float_as_uint(rs[ht]),
+                                                                      false, false);
+                    rs[ht] = __uint_as_float(w16[0]) + __uint_as_float(w16[1]);
+                }
+#pragma unroll
+                for (int ht = 0; ht < 2; ++ht) {
+                    const auto w32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(rs[ht]), __float_as_uint(rs[ht]),
+                                                                      false, false);
+                    lsum[ht] += __uint_as_float(w32[0]) + __uint_as_float(w32[1]);
+                }
+#pragma unroll
+                for (int ht = 0; ht < 2; ++ht) {
+                    const int htg = qh * 2 + ht;   // head tile within the block
+                    if (kb == 0) {
+                        if (g == 0) alph[ps][htg * 16 + l16] = alpha[ht];
+                        if (lane == 0) rflag[ps][htg] = any[ht] ? 1 : 0;
+                    }
+                    bf16x4v pb;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) pb[i] = (__bf16)(KVF == 1 ? pe[ht][i] * fk[i] : pe[ht][i]);
+                    *(__attribute__((address_space(3))) bf16x4v*)((lds_u8*)pbuf[ps][htg] + lane * 16 + kb * 8) = pb;
+                }
+            };
+
+            __syncthreads();                                   // barrier P: tile 0 landed
+            q_tile(tile0, 0, vmask[0], 0, 1);
+            int bq = 1;                                        // buffer of tile t+1
+            for (int t = 0; t < ntiles; ++t) {
+                __syncthreads();                               // barrier t: P(t) published, tile t+1 landed
+                if (t + 1 < ntiles) {
+                    const uint32_t vmn = __builtin_amdgcn_readfirstlane(vmask[t + 1]);
+                    q_tile(tile0 + bq * TB, bq, vmn, (t + 1) & 1, t + 2);
+                }
+                bq = bq == NBUF - 1 ? 0 : bq + 1;
+            }
+            __syncthreads();                                   // barrier F: the P ring is no longer read
+            if (g == 0) {
+#pragma unroll
+                for (int ht = 0; ht < 2; ++ht) {
+                    fin_l[(qh * 2 + kb) * 32 + ht * 16 + l16] = lsum[ht];
+                    if (kb == 0) fin_m[qh * 32 + ht * 16 + l16] = m2[ht];
+                }
+            }
+            __syncthreads();                                   // barrier E
         }
-        __syncthreads();                                   // barrier E
     } else {
         // ---------------------------------------------------------------- p-wave
+        if constexpr (KVF == 0) {
+            // p-waves: the slots of their rows of tiles 0 .. LA, looked up directly, so
+            // the first tile loads go out while the table is still being built
+            int32_t es = -1;                                // lane 8 t + k: row 8 pc + k of tile t
+            {
+                const int t = lane >> 3, i = t * TROWS + 8 * pc + (lane & 7);
+                const int p = (t <= LA && i < nk) ? a.idx[(int64_t)r * a.K + k0 + i] : -1;
+                const int64_t sl = p >= 0 ? slot_of(a.kv, seq, p) : -1;
+                es = sl >= 0 ? (int32_t)(uint32_t)sl : -1;
+            }
+#pragma unroll
+            for (int t = 0; t <= LA; ++t) {
+                const uint32_t s = (uint32_t)__shfl(es, 8 * t + (lane >> 3));
+                if (t < nt_fill) issue_rows(s, t);
+            }
+        }
+        __syncthreads();                                   // the slot table is complete
+        __syncthreads();
+        const int ntiles = s_ntiles;
         // bf16 rows: tile t + 1 + LA goes out in iteration t into the buffer
         // tile t - 1 has released.  Every tile is NJ loads per thread: "tile j
         // landed" = at most NJ * (tiles issued after j) loads still pending.
@@ -1021,7 +1238,21 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
 #pragma unroll
             for (int mt = 0; mt < MTP; ++mt) o[ht][mt] = f32x4v{0.f, 0.f, 0.f, 0.f};
 
+        // bf16 rows: the V operands of tile t + 1 are read in period t, into the
+        // registers the PV products of tile t have just taken theirs from, so after
+        // barrier t + 1 only the P^T operand stands between the p-wave and its
+        // MFMAs.  fp8 rows (whose codes in flight hold registers of their own):
+        // read after the barrier.
+        auto read_v = [&](const lds_u8* T, s16x4 (&va)[MTP][2]) {
+#pragma unroll
+            for (int mt = 0; mt < MTP; ++mt) {
+                va[mt][0] = trd(T, mt, 0);
+                va[mt][1] = trd(T, mt, 1);
+            }
+        };
+        s16x4 va[MTP][2];
         __syncthreads();                                   // barrier P: tile 0 landed
+        if constexpr (KVF == 0) read_v(tile0, va);
         int bc = 0;                                        // buffer of tile t
         for (int t = 0; t < ntiles; ++t) {
             if constexpr (KVF == 0) wait_tile(t + 1, t + LA);
@@ -1041,14 +1272,8 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
                     if (t + 4 < ntiles) fetch(t + 4, c0);
                 }
             }
+            if constexpr (KVF != 0) read_v(tile0 + bc * TB, va);
             const int ps = t & 1;
-            const lds_u8* T = tile0 + bc * TB;
-            s16x4 va[MTP][2];
-#pragma unroll
-            for (int mt = 0; mt < MTP; ++mt) {
-                va[mt][0] = trd(T, mt, 0);
-                va[mt][1] = trd(T, mt, 1);
-            }
             bf16x8 pbt[4];
 #pragma unroll
             for (int ht = 0; ht < 4; ++ht)
@@ -1084,6 +1309,8 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
                 for (int ht = 0; ht < 4; ++ht)
                     o[ht][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pbt[ht], o[ht][mt], 0, 0, 0);
             }
+            if constexpr (KVF == 0)
+                if (t + 1 < ntiles) read_v(tile0 + (bc == NBUF - 1 ? 0 : bc + 1) * TB, va);
             bc = bc == NBUF - 1 ? 0 : bc + 1;
         }
         __syncthreads();                                   // barrier F
@@ -1094,11 +1321,12 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
         for (int ht = 0; ht < 4; ++ht) {
             const int head = hb * 64 + ht * 16 + l16;
             const int hh = ht >> 1, hl = (ht & 1) * 16 + l16;
-            const float ls = fin_l[(hh * 2) * 32 + hl] + fin_l[(hh * 2 + 1) * 32 + hl];
+            const float ls = KVF == 0 ? fin_l[ht * 16 + l16] : fin_l[(hh * 2) * 32 + hl] + fin_l[(hh * 2 + 1) * 32 + hl];
+            const float mref = KVF == 0 ? fin_m[ht * 16 + l16] : fin_m[hh * 32 + hl];
             if (head >= a.H) continue;
             const float inv = ls > 0.f ? 1.f / ls : 0.f;
             if (pc == 0 && g == 0) {
-                const float l_nat = ls > 0.f ? (fin_m[hh * 32 + hl] + log2f(ls)) * kLn2 : -__builtin_inff();
+                const float l_nat = ls > 0.f ? (mref + log2f(ls)) * kLn2 : -__builtin_inff();
                 if (nsplit == 1) {
                     if (lse != nullptr) lse[(int64_t)r * a.H + head] = l_nat;
                 } else {
