@@ -579,23 +579,29 @@ __device__ __forceinline__ int sfa_swz8(int r) { return (((r >> 1) & 3) << 1) | 
 // w runs on SIMD w % 4, so every SIMD holds one q-wave and one p-wave, and the
 // PV products of the p-wave keep the matrix core busy while its q-wave runs
 // the softmax:
-//  * q-waves 0..3: q-wave (h, kb) = (w / 2, w % 2) owns heads 32 h .. 32 h + 31
-//    of the block (the query as two 16-head B operands, 144 VGPRs) and keys
-//    16 kb .. 16 kb + 15 of every tile.  For tile t + 1 it computes its
-//    S^T[16 keys, 32 heads] (36 MFMAs of 16x16x32; every key operand read from
-//    LDS feeds both head tiles, so the tile is read once per 32 heads), masks,
-//    takes its per-head maxima and trades them with its partner (the other key
-//    block, on the neighbouring SIMD) through LDS with a flag handshake inside
-//    the period; both then raise the base-2 reference lazily
-//    in the same way (only when the tile's maximum exceeds it by 2^8), and each
-//    writes its half of P^T into a two-slot LDS ring in the PV B-operand layout
-//    (lane = head, K-slots 8 g .. 8 g + 7 = keys 4 g + i and 16 + 4 g + i), the
-//    key block 0 wave with a raise flag and factors per head tile.  Each keeps
-//    the partial row sums of its keys.
+//  * q-waves 0..3, bf16 rows: q-wave w owns head tile w (16 heads of the block,
+//    the query as one B operand, 72 VGPRs) and all 32 keys of every tile.  For
+//    tile t + 1 it computes S^T[32 keys, 16 heads] (36 MFMAs of 16x16x32),
+//    masks, takes the per-head maxima inside the wave, raises the base-2
+//    reference lazily (only when the tile's maximum exceeds it by 2^8), and
+//    writes P^T into a two-slot LDS ring in the PV B-operand layout (lane =
+//    head, K-slots 8 g .. 8 g + 7 = keys 4 g + i and 16 + 4 g + i) with a raise
+//    flag and factors per head tile.
+//  * q-waves 0..3, fp8 rows: q-wave (h, kb) = (w / 2, w % 2) owns heads
+//    32 h .. 32 h + 31 (two 16-head B operands, 144 VGPRs) and keys
+//    16 kb .. 16 kb + 15, so every key operand read from LDS feeds both head
+//    tiles (half the LDS reads of the bf16 split, which matters here because
+//    the p-waves also write the converted tiles through LDS); the two key
+//    blocks trade their per-head maxima through LDS with a flag handshake
+//    inside the period, raise in the same way, and each writes its half of P^T;
+//    each keeps the partial row sums of its keys.
 //  * p-waves 4..7: p-wave c = w - 4 owns value columns
 //    128 c .. 128 c + 127 of the 64 heads (O^T in 128 VGPRs): it applies the
 //    raise factors of flagged head tiles and runs PV of tile t (32 MFMAs), the
 //    value operand from transposed LDS reads in the P^T operand's key order.
+//    bf16 rows: it reads the V operands of tile t + 1 in period t, into the
+//    registers PV(t) has just taken its operands from, so after the barrier
+//    only the P^T operand stands between it and its MFMAs.
 //    The p-waves also bring the tiles, p-wave c rows 8 c .. 8 c + 7.  bf16
 //    rows: direct global->LDS loads NBUF - 2 tiles ahead, issued from inline
 //    assembly (lds_dma) and ordered by explicit vmcnt waits and the tile
@@ -704,7 +710,8 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
     if (is_q) {
         // ---------------------------------------------------------------- q-wave
         if constexpr (KVF == 0) {
-            // q-wave w owns head tile w (16 heads) and all 32 keys of every tile.  The
+            // bf16 rows: q-wave w owns head tile w (16 heads) and all 32 keys of every
+            // tile, so the per-head maxima need no exchange between waves.  The
             // query in B-operand layout: lane = head, 8 consecutive columns of K-step ks
             bf16x8 qb[KS];
             {
@@ -759,11 +766,11 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
             // S^T of the tile's 32 keys (two 16-key blocks) for this wave's 16 heads,
             // the per-head maxima over all 32 keys inside the wave, softmax statistics,
             // P^T to LDS slot ps
-            auto q_tile = [&](const lds_u8* T, int buf, uint32_t vm, int ps) {
+            auto q_tile = [&](const lds_u8* T, uint32_t vm, int ps) {
                 f32x4v s[2] = {f32x4v{0.f, 0.f, 0.f, 0.f}, f32x4v{0.f, 0.f, 0.f, 0.f}};   // [key block]
                 // operand reads in batches of KPB K-steps (both key blocks), software-
                 // pipelined: the reads of batch b + 1 go out before the MFMAs of batch b
-                constexpr int KPB = KVF == 2 ? 2 : 3;
+                constexpr int KPB = 3;
                 constexpr int NB = KS / KPB;
                 static_assert(KS % KPB == 0, "whole batches");
                 bf16x8 av[2][2][KPB];   // [batch parity][key block][K-step]
@@ -772,80 +779,24 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
                     av[0][0][j] = qk_op(T, 0, j);
                     av[0][1][j] = qk_op(T, 1, j);
                 }
-                if constexpr (KVF != 2) {
-                    static_for<NB>([&](auto bc) {
-                        constexpr int b = decltype(bc)::value;
-                        if constexpr (b + 1 < NB) {
-#pragma unroll
-                            for (int j = 0; j < KPB; ++j) {
-                                av[(b + 1) & 1][0][j] = qk_op(T, 0, (b + 1) * KPB + j);
-                                av[(b + 1) & 1][1][j] = qk_op(T, 1, (b + 1) * KPB + j);
-                            }
-                        }
-                        __builtin_amdgcn_sched_barrier(0);
+                static_for<NB>([&](auto bc) {
+                    constexpr int b = decltype(bc)::value;
+                    if constexpr (b + 1 < NB) {
 #pragma unroll
                         for (int j = 0; j < KPB; ++j) {
-                            const int ks = b * KPB + j;
-                            s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[b & 1][0][j], qb[ks], s[0], 0, 0, 0);
-                            s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[b & 1][1][j], qb[ks], s[1], 0, 0, 0);
+                            av[(b + 1) & 1][0][j] = qk_op(T, 0, (b + 1) * KPB + j);
+                            av[(b + 1) & 1][1][j] = qk_op(T, 1, (b + 1) * KPB + j);
                         }
-                        __builtin_amdgcn_sched_barrier(0);
-                    });
-                } else {
-                    // column tile j = K-steps 4 j .. 4 j + 3 (the rope tile: 16, 17)
-                    // accumulates into sc[j & 1]; it is added, times the keys' factor
-                    // f_j, after the first batch of the next column tile went out
-                    f32x4v sc[2][2];
-#pragma unroll
-                    for (int p = 0; p < 2; ++p)
-#pragma unroll
-                        for (int kb = 0; kb < 2; ++kb) sc[p][kb] = f32x4v{0.f, 0.f, 0.f, 0.f};
-                    const float* kf = kvf + buf * NTL * TROWS + 4 * g;
-                    auto fold = [&](int j, int p) {   // s += f_j(key) * sc[p]; sc[p] = 0
-#pragma unroll
-                        for (int kb = 0; kb < 2; ++kb) {
-                            const f32x4v f = *(const f32x4v*)(kf + j * TROWS + 16 * kb);
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) s[kb][i] = __builtin_fmaf(f[i], sc[p][kb][i], s[kb][i]);
-                            sc[p][kb] = f32x4v{0.f, 0.f, 0.f, 0.f};
-                        }
-                    };
-                    static_for<NB>([&](auto bc) {
-                        constexpr int b = decltype(bc)::value;
-                        constexpr int jt = (b * KPB) / 4;          // column tile of this batch
-                        if constexpr (b + 1 < NB) {
-#pragma unroll
-                            for (int j = 0; j < KPB; ++j) {
-                                av[(b + 1) & 1][0][j] = qk_op(T, 0, (b + 1) * KPB + j);
-                                av[(b + 1) & 1][1][j] = qk_op(T, 1, (b + 1) * KPB + j);
-                            }
-                        }
-                        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                        for (int j = 0; j < KPB; ++j) {
-                            const int ks = b * KPB + j;
-                            sc[jt & 1][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[b & 1][0][j], qb[ks], sc[jt & 1][0],
-                                                                                     0, 0, 0);
-                            sc[jt & 1][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[b & 1][1][j], qb[ks], sc[jt & 1][1],
-                                                                                     0, 0, 0);
-                        }
-                        __builtin_amdgcn_sched_barrier(0);
-                        // first batch of column tile jt >= 1: the previous tile is complete
-                        if constexpr (jt >= 1 && (b * KPB) % 4 == 0) fold(jt - 1, (jt - 1) & 1);
-                    });
-                    fold(NTL - 1, (NTL - 1) & 1);
-                }
-                float fk[2][4];   // KVF 1: the factor of each of this lane's keys
-                if constexpr (KVF == 1) {
-#pragma unroll
-                    for (int kb = 0; kb < 2; ++kb) {
-                        const f32x4v f = *(const f32x4v*)(kvf + buf * TROWS + 16 * kb + 4 * g);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) fk[kb][i] = f[i];
-                        // one factor per row: the logit is scale * f * (q . code)
-                        s[kb] *= f;
                     }
-                }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int j = 0; j < KPB; ++j) {
+                        const int ks = b * KPB + j;
+                        s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[b & 1][0][j], qb[ks], s[0], 0, 0, 0);
+                        s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[b & 1][1][j], qb[ks], s[1], 0, 0, 0);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                });
                 if (vm != 0xFFFFFFFFu) {
 #pragma unroll
                     for (int kb = 0; kb < 2; ++kb)
@@ -888,20 +839,20 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
                 bf16x8 pb;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    pb[i] = (__bf16)(KVF == 1 ? pe[0][i] * fk[0][i] : pe[0][i]);
-                    pb[4 + i] = (__bf16)(KVF == 1 ? pe[1][i] * fk[1][i] : pe[1][i]);
+                    pb[i] = (__bf16)pe[0][i];
+                    pb[4 + i] = (__bf16)pe[1][i];
                 }
                 *(__attribute__((address_space(3))) bf16x8*)((lds_u8*)pbuf[ps][wave] + lane * 16) = pb;
             };
 
             __syncthreads();                                   // barrier P: tile 0 landed
-            q_tile(tile0, 0, vmask[0], 0);
+            q_tile(tile0, vmask[0], 0);
             int bq = 1;                                        // buffer of tile t+1
             for (int t = 0; t < ntiles; ++t) {
                 __syncthreads();                               // barrier t: P(t) published, tile t+1 landed
                 if (t + 1 < ntiles) {
                     const uint32_t vmn = __builtin_amdgcn_readfirstlane(vmask[t + 1]);
-                    q_tile(tile0 + bq * TB, bq, vmn, (t + 1) & 1);
+                    q_tile(tile0 + bq * TB, vmn, (t + 1) & 1);
                 }
                 bq = bq == NBUF - 1 ? 0 : bq + 1;
             }
