@@ -102,7 +102,7 @@ def stored_traffic(stage: str, workload: str):
 STAGE_KERNELS = {
     "li_score": ["li_score"],
     "topk_select": ["topk"],
-    "sparse_mla_attn": ["sfa_ws_kernel", "sfa_w8_kernel", "sfa_bf16_kernel", "sfa_kernel<", "sfa_combine_kernel"],
+    "sparse_mla_attn": ["sfa_mla_kernel", "sfa_kernel<", "sfa_combine_kernel"],
 }
 
 
@@ -216,6 +216,68 @@ def write_mfma_summary(args):
     print(f"wrote {path}")
 
 
+def kernel_short_name(n: str) -> str:
+    """lisfa::kernel<args> from a demangled name, or from a mangled one that the
+    profiler left as is (template arguments: integer, bool, float, __bf16)."""
+    if not n.startswith("_ZN5lisfa"):
+        return n.split("(")[0].replace("void ", "")
+    import re
+    m = re.match(r"_ZN5lisfa(\d+)", n)
+    k = m.end() + int(m.group(1))
+    base, rest, args = n[m.end():k], n[k:], []
+    if rest.startswith("I"):
+        i = 1
+        while i < len(rest) and rest[i] != "E":
+            t = re.match(r"L[ib](-?\d+)E|DF16b|f|i", rest[i:])
+            if t is None:
+                break
+            tok = t.group(0)
+            args.append(t.group(1) if t.group(1) is not None else {"DF16b": "__bf16", "f": "float", "i": "int"}[tok])
+            i += len(tok)
+    return f"lisfa::{base}<{', '.join(args)}>" if args else f"lisfa::{base}"
+
+
+def write_kernel_stats(args):
+    """Turn a rocprofv3 --kernel-trace --stats kernel_stats.csv (and, with
+    --bench-json, the line of a plain bench.py run in the same GPU session)
+    into profiles/layer_<workload>_kernel_stats.md."""
+    import csv
+    rows = []
+    with open(args.stats_csv) as fh:
+        for r in csv.DictReader(fh):
+            if "lisfa" not in r["Name"]:
+                continue
+            name = kernel_short_name(r["Name"])
+            rows.append((name, int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                         float(r["MaxNs"]) / 1e3))
+    rows.sort(key=lambda x: -x[2] * x[1])
+    path = os.path.join(ROOT, "profiles", f"layer_{args.workload}_kernel_stats.md")
+    with open(path, "w") as fh:
+        fh.write(f"# Kernel trace: the layer on {args.workload}\n\n")
+        fh.write("Commands (repository root, GPU box):\n\n")
+        for c in args.commands or []:
+            fh.write(f"    {c}\n")
+        fh.write("\nThe profiled bench.py run makes warmup + steps fused layer calls, then steps cold layer "
+                 "calls (each after an\nL2 / MALL flush), then warmup + steps calls of each stage alone (the "
+                 "stage timing): 2 + 10 + 10 + 2 + 10 = 34\ncalls of every kernel.\n\n")
+        fh.write("| kernel | calls | average us | min us | max us |\n|---|---|---|---|---|\n")
+        for r in rows:
+            fh.write(f"| `{r[0]}` | {r[1]} | {r[2]:.1f} | {r[3]:.1f} | {r[4]:.1f} |\n")
+        if args.bench_json:
+            d = json.loads(open(args.bench_json).read().strip().splitlines()[-1])
+            fh.write("\nThe plain bench.py run of the same GPU session (no profiler attached), its own HIP-event "
+                     "timing of each stage:\n\n")
+            fh.write("| stage | us | algorithmic bytes | roofline fraction |\n|---|---|---|---|\n")
+            for k, v in d["stages"].items():
+                rf = v["roofline"]
+                fh.write(f"| {k} | {v['us']} | {v['algorithmic_bytes']} | {rf['frac']} ({rf['bound']}) |\n")
+            fh.write(f"\nLayer: {d['ms_per_step'] * 1e3:.1f} us per step cold ({d['value']:.0f} query rows/s), "
+                     f"{d['ms_per_step_hot'] * 1e3:.1f} us hot.  Line roofline: {d['roofline']['kernel']} "
+                     f"{d['roofline']['achieved']} GB/s = {d['roofline']['frac']} of peak, traffic "
+                     f"{d['roofline']['traffic']} B per launch.\n")
+    print(f"wrote {path}")
+
+
 def time_on_stream(fn, stream, warmup, steps, graph=False):
     """Seconds per call of fn(stream).  With graph=True the calls are captured
     into one HIP graph first, so the time excludes the host's per-call cost."""
@@ -298,6 +360,9 @@ def main():
     ap.add_argument("--report-all", action="store_true",
                     help="time every workload (hot and cold), one JSON line each")
     ap.add_argument("--write-mfma-summary", action="store_true")
+    ap.add_argument("--write-kernel-stats", action="store_true")
+    ap.add_argument("--stats-csv")
+    ap.add_argument("--bench-json")
     ap.add_argument("--mfma-csv")
     ap.add_argument("--report-cp", action="store_true",
                     help="time one GPU's context-parallel share and the Zigzag prefill balance")
@@ -309,6 +374,9 @@ def main():
         return
     if args.write_mfma_summary:
         write_mfma_summary(args)
+        return
+    if args.write_kernel_stats:
+        write_kernel_stats(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
