@@ -22,6 +22,8 @@
 //    a row keep their own Top-K as (position, score) pairs, a merge selects
 //    the K best of the gathered pairs.  Every globally selected position is
 //    among its own slice's Top-K, so the result is the same.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace lisfa {
@@ -463,9 +465,12 @@ constexpr int kTkD1Bins = 4096;                         // first-digit bins
 constexpr int kTkCandCap = 8192;                        // candidates kept in LDS
 static_assert(kTkD1Bins == 4 * kTkThreads, "four first-digit bins per thread");
 
+constexpr int kTkStageChunks = 8192;   // 16-byte chunks of a row staged in LDS at once (128 KB)
+
 struct TkRowShared {
     uint32_t hist[kTkD1Bins];
     union {
+        f32x4 stage[kTkStageChunks];   // the row on its way to the registers (kept until the bin keys are read)
         struct {
             int32_t pos[kTkCandCap];
             uint32_t key[kTkCandCap];
@@ -475,8 +480,96 @@ struct TkRowShared {
     uint64_t wsum64[kTkWaves];
     uint32_t wsum[kTkWaves];
     uint32_t red[2 * kTkWaves];
-    uint32_t bin, above;
+    alignas(16) uint32_t binkey[kWave];   // d of the threshold bin's keys, when it holds at most 64
+    uint32_t binown[kWave];               // their owners: thread * 32 + key index
+    uint32_t own_gt[kTkThreads], own_eq[kTkThreads];   // per thread: its bin keys above / at the threshold
+    uint32_t bin, above, nbin;
 };
+
+// m * 2 + (key > thr): the compare's lane mask is the add's carry-in, so a
+// per-thread bit mask grows by one bit in two instructions (keys taken from the
+// last to the first leave key c's bit at position c)
+__device__ __forceinline__ uint32_t tk_push_gt(uint32_t m, uint32_t key, uint32_t thr) {
+    asm volatile("v_cmp_gt_u32 vcc, %1, %2\n\tv_addc_co_u32 %0, vcc, %0, %0, vcc" : "+v"(m) : "v"(key), "v"(thr)
+                 : "vcc");
+    return m;
+}
+
+// LDS slot of staged chunk k, for runs of S = 2^L chunks a thread: the low 4
+// bits of k are XORed with the 4 bits above the run index (bits L .. L+3), a
+// GF(2)-linear bijection that keeps each group of 16 chunks in place.  The 16
+// threads t0 .. t0+15 that read chunk t * S + j (fixed j) then hit 16 distinct
+// 16-byte bank groups, and any 8 aligned ones of them 8 distinct 32-byte
+// halves, where plain runs would be S-strided.
+template <int S>
+__device__ __forceinline__ int tk_slot(int k) {
+    constexpr int L = S == 2 ? 1 : S == 4 ? 2 : S == 8 ? 3 : 4;
+    return k ^ ((k >> L) & 15);
+}
+// inverse of tk_slot: y ^ N(y) ^ N(N(y)) ^ ... with N(y) = (y >> L) & 15,
+// which vanishes after at most 4 steps
+template <int S>
+__device__ __forceinline__ int tk_chunk(int y) {
+    constexpr int L = S == 2 ? 1 : S == 4 ? 2 : S == 8 ? 3 : 4;
+    int k = y, x = y;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x = (x >> L) & 15;
+        k ^= x;
+    }
+    return k;
+}
+
+// Keys of positions base .. base + EPT - 1 (base = tid * EPT) of a row whose
+// floats are 16-byte aligned: the row's 16-byte chunks come in whole cache lines
+// per wave instruction (direct-to-LDS loads; a thread-contiguous load from
+// global memory touches 64 lines per instruction), up to 8192 chunks at a time,
+// and each thread then reads its own run from LDS.  Chunks past the last valid
+// position are not read from global memory (their lanes fetch chunk 0); keys
+// past n are zero.  The caller's next barrier precedes any reuse of the stage.
+template <int EPT>
+__device__ __forceinline__ int tk_load_staged(const float* s, int64_t n, f32x4* stage, uint32_t (&kr)[EPT]) {
+    constexpr int S = EPT / 4;
+    constexpr int ROWCH = kTkThreads * S;
+    constexpr int CH = ROWCH < kTkStageChunks ? ROWCH : kTkStageChunks;
+    constexpr int NPH = ROWCH / CH;   // 1, or 2 for 64 keys a thread
+    constexpr int TPP = CH / S;       // threads whose runs one phase holds
+    static_assert(EPT % 4 == 0 && S <= 16 && ROWCH % CH == 0, "runs of 2..16 chunks");
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t base = (int64_t)tid * EPT;
+    const int nv = n - base >= EPT ? EPT : (n > base ? (int)(n - base) : 0);
+    const int nch = (int)((n + 3) >> 2), nch16 = (nch + 15) & ~15;
+    const uint32_t lds_w = (uint32_t)(uintptr_t)stage + (uint32_t)(wave * kWave * 16);
+#pragma unroll
+    for (int ph = 0; ph < NPH; ++ph) {
+        if (ph > 0) __syncthreads();   // the previous phase's runs are read
+        const int c0 = ph * CH;
+#pragma unroll
+        for (int i = 0; i < CH / kTkThreads; ++i) {
+            const int p0 = i * kTkThreads + wave * kWave;
+            if (c0 + p0 < nch16) {   // wave-uniform: a group of 16 chunks maps onto itself
+                const int k = c0 + tk_chunk<S>(p0 + lane);
+                lds_dma<16, 0>(s + 4 * (int64_t)(k < nch ? k : 0), lds_w + (uint32_t)(i * kTkThreads * 16));
+            }
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (NPH == 1 || tid / TPP == ph) {
+            const int tl = tid - ph * TPP;
+#pragma unroll
+            for (int j = 0; j < S; ++j) {
+                const f32x4 v = stage[tk_slot<S>(tl * S + j)];
+                kr[4 * j] = float_key(v.x);
+                kr[4 * j + 1] = float_key(v.y);
+                kr[4 * j + 2] = float_key(v.z);
+                kr[4 * j + 3] = float_key(v.w);
+            }
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < EPT; ++c) kr[c] = c < nv ? kr[c] : 0u;
+    return nv;
+}
 
 // Top-K of one row per workgroup, the row's keys in registers (n > K
 // visible positions):
@@ -505,17 +598,28 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(const float* __res
     }
     const float* s = scores + (int64_t)r * ld;
 
-    // 1. keys, min and max
+    // 1. keys, min and max.  Every pass over the keys has a copy without the
+    // per-key validity test for the threads whose keys are all valid; only the
+    // thread holding the row's end runs the tested one.
     uint32_t kr[EPT];
     const int64_t base = (int64_t)tid * EPT;
     const bool vec = ((ld & 3) == 0) && ((((uintptr_t)scores) & 15) == 0);
-    const int nv = tk_load<EPT>(s, vec, base, n, kr);
+    const int nv = vec ? tk_load_staged<EPT>(s, n, sh.u.stage, kr) : tk_load<EPT>(s, false, base, n, kr);
+    const bool full = nv == EPT;
     uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+    if (full) {
 #pragma unroll
-    for (int c = 0; c < EPT; ++c) {
-        if (c < nv) {
+        for (int c = 0; c < EPT; ++c) {
             kmin = kr[c] < kmin ? kr[c] : kmin;
             kmax = kr[c] > kmax ? kr[c] : kmax;
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < EPT; ++c) {
+            if (c < nv) {
+                kmin = kr[c] < kmin ? kr[c] : kmin;
+                kmax = kr[c] > kmax ? kr[c] : kmax;
+            }
         }
     }
 #pragma unroll
@@ -529,6 +633,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(const float* __res
         sh.red[kTkWaves + wave] = kmax;
     }
     *(u32x4*)&sh.hist[4 * tid] = u32x4{0u, 0u, 0u, 0u};
+    if (tid == 0) sh.nbin = 0u;
     __syncthreads();
     {
         const u32x4* rm = (const u32x4*)sh.red;
@@ -551,9 +656,14 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(const float* __res
     const int sh1 = top >= 11 ? top - 11 : 0;   // first digit: d >> sh1, below 4096
 
     // 2. first-digit histogram; thread t owns bins 4095 - 4t - j (j < 4), top first
+    if (full) {
 #pragma unroll
-    for (int c = 0; c < EPT; ++c)
-        if (c < nv) atomicAdd(&sh.hist[(kr[c] - kmin) >> sh1], 1u);
+        for (int c = 0; c < EPT; ++c) atomicAdd(&sh.hist[(kr[c] - kmin) >> sh1], 1u);
+    } else {
+#pragma unroll
+        for (int c = 0; c < EPT; ++c)
+            if (c < nv) atomicAdd(&sh.hist[(kr[c] - kmin) >> sh1], 1u);
+    }
     __syncthreads();
     {
         uint32_t cb[4], loc = 0u;
@@ -577,7 +687,167 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(const float* __res
         __syncthreads();
     }
     const uint32_t bin = sh.bin, above = sh.above;
-    const uint32_t C = above + sh.hist[bin];
+    const uint32_t inbin = sh.hist[bin];
+    const uint32_t C = above + inbin;
+    uint32_t need = (uint32_t)K - above;   // taken from bin B, >= 1
+
+    if (sh1 == 0 || inbin <= (uint32_t)kWave) {
+        // 3'. small threshold bin (at most 64 keys, or one value when sh1 = 0)
+        uint32_t rg, re, need_eq;
+        if constexpr (EPT <= 32) {
+            // one pass marks the keys above bin B (above_m) and in it (bin_m) and
+            // puts bin B's keys with their owners in LDS; one wavefront ranks them,
+            // finds the threshold and sets the owners' bits (own.gt / own.eq)
+            // bin B's keys lie in [Klo, Khi]; the invalid keys (0) lie below kmin
+            const uint32_t Klo = kmin + (bin << sh1);
+            const uint64_t hi = (uint64_t)Klo + ((uint64_t)1 << sh1) - 1u;
+            const uint32_t Khi = hi > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)hi;
+            uint32_t above_m = 0u, bin_m = 0u;
+#pragma unroll
+            for (int c = EPT - 1; c >= 0; --c) {
+                above_m = tk_push_gt(above_m, kr[c], Khi);
+                bin_m = tk_push_gt(bin_m, kr[c], Klo - 1u);
+            }
+            bin_m &= ~above_m;
+            if (sh1 > 0) {
+                if (bin_m != 0u) {
+                    sh.own_gt[tid] = 0u;
+                    sh.own_eq[tid] = 0u;
+                    // the few bin keys: from the row's LDS copy when there is one
+                    // (registers cannot be indexed at run time)
+                    const float* stf = (const float*)sh.u.stage;
+                    for (uint32_t m = bin_m; m != 0u; m &= m - 1u) {
+                        const int c = __builtin_ctz(m);
+                        uint32_t key = 0u;
+                        if (vec) {
+                            key = float_key(stf[tk_slot<EPT / 4>(tid * (EPT / 4) + (c >> 2)) * 4 + (c & 3)]);
+                        } else {
+#pragma unroll
+                            for (int cc = 0; cc < EPT; ++cc) key = cc == c ? kr[cc] : key;
+                        }
+                        const uint32_t slot = atomicAdd(&sh.nbin, 1u);
+                        sh.binkey[slot] = key - kmin;
+                        sh.binown[slot] = ((uint32_t)tid << 5) | (uint32_t)c;
+                    }
+                }
+                __syncthreads();
+                if (wave == 0) {
+                    // the need-th largest d of the bin is the d of every key with
+                    // #greater < need <= #greater-or-equal
+                    const bool ok = (uint32_t)lane < inbin;
+                    const uint32_t d = ok ? sh.binkey[lane] : 0u;
+                    uint32_t gt = 0u, ge = 0u;
+#pragma unroll 1
+                    for (uint32_t j = 0; j < inbin; j += 4) {
+                        const uint4 o = *reinterpret_cast<const uint4*>(&sh.binkey[j]);
+                        gt += (o.x > d) + (j + 1 < inbin && o.y > d) + (j + 2 < inbin && o.z > d) +
+                              (j + 3 < inbin && o.w > d);
+                        ge += (o.x >= d) + (j + 1 < inbin && o.y >= d) + (j + 2 < inbin && o.z >= d) +
+                              (j + 3 < inbin && o.w >= d);
+                    }
+                    const uint64_t hit = __ballot(ok && gt < need && need <= ge);
+                    const uint32_t dT = (uint32_t)__shfl((int)d, (int)__builtin_ctzll(hit));
+                    const uint64_t gtb = __ballot(ok && d > dT);
+                    if (ok && d >= dT) {
+                        const uint32_t ow = sh.binown[lane];
+                        atomicOr(d > dT ? &sh.own_gt[ow >> 5] : &sh.own_eq[ow >> 5], 1u << (ow & 31u));
+                    }
+                    if (lane == 0) sh.above = (uint32_t)__popcll(gtb);
+                }
+                __syncthreads();
+                need -= sh.above;
+                above_m |= sh.own_gt[tid] & bin_m;
+                bin_m &= sh.own_eq[tid];
+            }
+            need_eq = need;
+            // counts of rows up to 32768 positions fit 16 bits each
+            uint32_t total;
+            const uint32_t ex = block_excl_scan(((uint32_t)__popc(bin_m) << 16) | (uint32_t)__popc(above_m), sh.wsum,
+                                                total);
+            rg = ex & 0xFFFFu;
+            re = ex >> 16;
+            // this thread's selected keys in position order (a loop over set bits:
+            // only the position is needed)
+            uint32_t m = above_m | bin_m;
+            while (m != 0u) {
+                const int c = __builtin_ctz(m);
+                m &= m - 1u;
+                if ((above_m >> c) & 1u) {
+                    out[rg + (re < need_eq ? re : need_eq)] = (int32_t)(base + c);
+                    ++rg;
+                } else {
+                    if (re < need_eq) out[rg + re] = (int32_t)(base + c);
+                    ++re;
+                }
+            }
+        } else {
+            // 64 keys a thread: bin B's keys go to LDS, one wavefront sorts them,
+            // a second pass takes the masks (fewer live registers)
+            uint32_t dT = bin;   // sh1 = 0: every key of bin B has d = B
+            if (sh1 > 0) {
+#pragma unroll
+                for (int c = 0; c < EPT; ++c) {
+                    const uint32_t d = kr[c] - kmin;
+                    if (c < nv && (d >> sh1) == bin) sh.binkey[atomicAdd(&sh.nbin, 1u)] = d;
+                }
+                __syncthreads();
+                if (wave == 0) {
+                    const bool ok = (uint32_t)lane < inbin;
+                    const uint32_t d = ok ? sh.binkey[lane] : 0u;
+                    uint32_t gt = 0u, ge = 0u;
+#pragma unroll 1
+                    for (uint32_t j = 0; j < inbin; j += 4) {
+                        const uint4 o = *reinterpret_cast<const uint4*>(&sh.binkey[j]);
+                        gt += (o.x > d) + (j + 1 < inbin && o.y > d) + (j + 2 < inbin && o.z > d) +
+                              (j + 3 < inbin && o.w > d);
+                        ge += (o.x >= d) + (j + 1 < inbin && o.y >= d) + (j + 2 < inbin && o.z >= d) +
+                              (j + 3 < inbin && o.w >= d);
+                    }
+                    const uint64_t hit = __ballot(ok && gt < need && need <= ge);
+                    const uint32_t v = (uint32_t)__shfl((int)d, (int)__builtin_ctzll(hit));
+                    const uint64_t gtb = __ballot(ok && d > v);
+                    if (lane == 0) {
+                        sh.bin = v;
+                        sh.above = (uint32_t)__popcll(gtb);
+                    }
+                }
+                __syncthreads();
+                dT = sh.bin;
+                need -= sh.above;
+            }
+            need_eq = need;
+            // invalid keys (0) lie below kmin <= T
+            const uint32_t T = kmin + dT;
+            uint32_t g0 = 0u, g1 = 0u, e0 = 0u, e1 = 0u;
+#pragma unroll
+            for (int c = EPT / 2 - 1; c >= 0; --c) {
+                g0 = tk_push_gt(g0, kr[c], T);
+                e0 = tk_push_gt(e0, kr[c], T - 1u);
+                g1 = tk_push_gt(g1, kr[c + EPT / 2], T);
+                e1 = tk_push_gt(e1, kr[c + EPT / 2], T - 1u);
+            }
+            const uint64_t gtm = ((uint64_t)g1 << 32) | g0;
+            const uint64_t eqm = (((uint64_t)e1 << 32) | e0) & ~gtm;
+            uint64_t total;
+            const uint64_t ex = block_excl_scan64(((uint64_t)__popcll(eqm) << 32) | (uint64_t)__popcll(gtm),
+                                                  sh.wsum64, total);
+            rg = (uint32_t)ex;
+            re = (uint32_t)(ex >> 32);
+            uint64_t m = gtm | eqm;
+            while (m != 0ull) {
+                const int c = __builtin_ctzll(m);
+                m &= m - 1ull;
+                if ((gtm >> c) & 1ull) {
+                    out[rg + (re < need_eq ? re : need_eq)] = (int32_t)(base + c);
+                    ++rg;
+                } else {
+                    if (re < need_eq) out[rg + re] = (int32_t)(base + c);
+                    ++re;
+                }
+            }
+        }
+        return;
+    }
     if (C > (uint32_t)kTkCandCap) {
         tk_row_global(sh.u.tk, s, n, K, out);
         return;
@@ -602,7 +872,6 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(const float* __res
     __syncthreads();
 
     // 4. the remaining sh1 bits of d, 10 at a time, over bin B's candidates
-    uint32_t need = (uint32_t)K - above;   // taken from bin B, >= 1
     uint32_t prefix = bin;
     for (int hi = sh1; hi > 0;) {
         const int w = hi < 10 ? hi : 10, lo = hi - w;
