@@ -63,6 +63,73 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, 
     return before + x - v;
 }
 
+// Wave-wide inclusive scans through DPP (row shifts by 1, 2, 4, 8 within
+// each row of 16 lanes, then row 0/2's last lane to rows 1/3 and lane 31 to
+// rows 2 and 3); lanes without a source keep the identity.  Lane 63 ends
+// with the wave's total.
+template <int CTRL, int ROWM>
+__device__ __forceinline__ uint32_t tk_dpp(uint32_t old, uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)x, CTRL, ROWM, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t x) {
+    x += tk_dpp<0x111, 0xF>(0u, x);
+    x += tk_dpp<0x112, 0xF>(0u, x);
+    x += tk_dpp<0x114, 0xF>(0u, x);
+    x += tk_dpp<0x118, 0xF>(0u, x);
+    x += tk_dpp<0x142, 0xA>(0u, x);
+    x += tk_dpp<0x143, 0xC>(0u, x);
+    return x;
+}
+__device__ __forceinline__ uint32_t wave_incl_min(uint32_t x) {
+    x = min(x, tk_dpp<0x111, 0xF>(~0u, x));
+    x = min(x, tk_dpp<0x112, 0xF>(~0u, x));
+    x = min(x, tk_dpp<0x114, 0xF>(~0u, x));
+    x = min(x, tk_dpp<0x118, 0xF>(~0u, x));
+    x = min(x, tk_dpp<0x142, 0xA>(~0u, x));
+    x = min(x, tk_dpp<0x143, 0xC>(~0u, x));
+    return x;
+}
+__device__ __forceinline__ uint32_t wave_incl_max(uint32_t x) {
+    x = max(x, tk_dpp<0x111, 0xF>(0u, x));
+    x = max(x, tk_dpp<0x112, 0xF>(0u, x));
+    x = max(x, tk_dpp<0x114, 0xF>(0u, x));
+    x = max(x, tk_dpp<0x118, 0xF>(0u, x));
+    x = max(x, tk_dpp<0x142, 0xA>(0u, x));
+    x = max(x, tk_dpp<0x143, 0xC>(0u, x));
+    return x;
+}
+
+// Inclusive scan / minimum / maximum within each row of 16 lanes (DPP row shifts).
+__device__ __forceinline__ uint32_t row16_incl_sum(uint32_t x) {
+    x += tk_dpp<0x111, 0xF>(0u, x);
+    x += tk_dpp<0x112, 0xF>(0u, x);
+    x += tk_dpp<0x114, 0xF>(0u, x);
+    x += tk_dpp<0x118, 0xF>(0u, x);
+    return x;
+}
+
+// Exclusive block-wide scans of two values per thread with one barrier: wave
+// totals go to wsum[0 .. 15] and wsum[16 .. 31]; each wave then scans the 16
+// totals across a row of its lanes and reads its own prefix from lane
+// wave - 1.  The caller keeps wsum unwritten until a later barrier.
+__device__ __forceinline__ void block_excl_scan2(uint32_t& a, uint32_t& b, uint32_t* wsum, uint32_t& ta, uint32_t& tb) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t xa = wave_incl_sum(a), xb = wave_incl_sum(b);
+    if (lane == 63) {
+        wsum[wave] = xa;
+        wsum[kTkWaves + wave] = xb;
+    }
+    __syncthreads();
+    const uint32_t sa = row16_incl_sum(wsum[lane & 15]), sb = row16_incl_sum(wsum[kTkWaves + (lane & 15)]);
+    ta = (uint32_t)__builtin_amdgcn_readlane((int)sa, 15);
+    tb = (uint32_t)__builtin_amdgcn_readlane((int)sb, 15);
+    const uint32_t ba = wave > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)sa, wave - 1) : 0u;
+    const uint32_t bb = wave > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)sb, wave - 1) : 0u;
+    a = ba + xa - a;
+    b = bb + xb - b;
+}
+
 // Exclusive block-wide scan of one 64-bit value per thread; also returns the total.
 __device__ __forceinline__ uint64_t block_excl_scan64(uint64_t v, uint64_t* wsum, uint64_t& total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -479,6 +546,7 @@ struct TkRowShared {
     } u;
     uint64_t wsum64[kTkWaves];
     uint32_t wsum[kTkWaves];
+    alignas(16) uint32_t wsum2[2 * kTkWaves];
     uint32_t red[2 * kTkWaves];
     alignas(16) uint32_t binkey[kWave];   // d of the threshold bin's keys, when it holds at most 64
     uint32_t binown[kWave];               // their owners: thread * 32 + key index
@@ -493,6 +561,13 @@ __device__ __forceinline__ uint32_t tk_push_gt(uint32_t m, uint32_t key, uint32_
     asm volatile("v_cmp_gt_u32 vcc, %1, %2\n\tv_addc_co_u32 %0, vcc, %0, %0, vcc" : "+v"(m) : "v"(key), "v"(thr)
                  : "vcc");
     return m;
+}
+
+// x * 4 + c in one instruction (an LDS word address from an index)
+__device__ __forceinline__ uint32_t tk_lshl2_add(uint32_t x, uint32_t c) {
+    uint32_t r;
+    asm("v_lshl_add_u32 %0, %1, 2, %2" : "=v"(r) : "v"(x), "v"(c));
+    return r;
 }
 
 // LDS slot of staged chunk k, for runs of S = 2^L chunks a thread: the low 4
@@ -622,20 +697,16 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(const float* __res
             }
         }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const uint32_t a = __shfl_xor(kmin, o), b = __shfl_xor(kmax, o);
-        kmin = a < kmin ? a : kmin;
-        kmax = b > kmax ? b : kmax;
-    }
-    if (lane == 0) {
+    kmin = wave_incl_min(kmin);
+    kmax = wave_incl_max(kmax);
+    if (lane == 63) {
         sh.red[wave] = kmin;
         sh.red[kTkWaves + wave] = kmax;
     }
     *(u32x4*)&sh.hist[4 * tid] = u32x4{0u, 0u, 0u, 0u};
     if (tid == 0) sh.nbin = 0u;
     __syncthreads();
-    {
+    if constexpr (EPT == 64) {   // (fewer live registers)
         const u32x4* rm = (const u32x4*)sh.red;
 #pragma unroll
         for (int q = 0; q < kTkWaves / 4; ++q) {
@@ -646,23 +717,44 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(const float* __res
                 kmax = b[e] > kmax ? b[e] : kmax;
             }
         }
+    } else {
+        // the 16 wave results across a row of lanes, reduced by DPP; lane 15 has the block's
+        uint32_t vmin = sh.red[lane & 15], vmax = sh.red[kTkWaves + (lane & 15)];
+        vmin = min(vmin, tk_dpp<0x111, 0xF>(~0u, vmin));
+        vmax = max(vmax, tk_dpp<0x111, 0xF>(0u, vmax));
+        vmin = min(vmin, tk_dpp<0x112, 0xF>(~0u, vmin));
+        vmax = max(vmax, tk_dpp<0x112, 0xF>(0u, vmax));
+        vmin = min(vmin, tk_dpp<0x114, 0xF>(~0u, vmin));
+        vmax = max(vmax, tk_dpp<0x114, 0xF>(0u, vmax));
+        vmin = min(vmin, tk_dpp<0x118, 0xF>(~0u, vmin));
+        vmax = max(vmax, tk_dpp<0x118, 0xF>(0u, vmax));
+        kmin = (uint32_t)__builtin_amdgcn_readlane((int)vmin, 15);
+        kmax = (uint32_t)__builtin_amdgcn_readlane((int)vmax, 15);
     }
     const uint32_t range = kmax - kmin;
     if (range == 0u) {   // all keys equal: the first K positions
         for (int i = tid; i < K; i += kTkThreads) out[i] = i;
         return;
     }
+    // first digit of a key: (key >> sh1) - (kmin >> sh1) = d >> sh1 with
+    // d = key - kb, kb = kmin with its low sh1 bits cleared; sh1 is the
+    // smallest shift that keeps the digit below 4096
     const int top = 31 - __clz(range);
-    const int sh1 = top >= 11 ? top - 11 : 0;   // first digit: d >> sh1, below 4096
+    int sh1 = top >= 11 ? top - 11 : 0;
+    if ((kmax >> sh1) - (kmin >> sh1) >= (uint32_t)kTkD1Bins) ++sh1;
+    const uint32_t kb = (kmin >> sh1) << sh1;
 
     // 2. first-digit histogram; thread t owns bins 4095 - 4t - j (j < 4), top first
     if (full) {
+        const uint32_t hb = (uint32_t)(uintptr_t)sh.hist - ((kb >> sh1) << 2);
 #pragma unroll
-        for (int c = 0; c < EPT; ++c) atomicAdd(&sh.hist[(kr[c] - kmin) >> sh1], 1u);
+        for (int c = 0; c < EPT; ++c)
+            __hip_atomic_fetch_add((lds_u32*)(uintptr_t)tk_lshl2_add(kr[c] >> sh1, hb), 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
     } else {
 #pragma unroll
         for (int c = 0; c < EPT; ++c)
-            if (c < nv) atomicAdd(&sh.hist[(kr[c] - kmin) >> sh1], 1u);
+            if (c < nv) atomicAdd(&sh.hist[(kr[c] - kb) >> sh1], 1u);
     }
     __syncthreads();
     {
@@ -672,8 +764,8 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(const float* __res
             cb[j] = sh.hist[kTkD1Bins - 1 - (4 * tid + j)];
             loc += cb[j];
         }
-        uint32_t tot;
-        uint32_t E = block_excl_scan(loc, sh.wsum, tot);
+        uint32_t E = loc, dummy = 0u, tot, tot2;
+        block_excl_scan2(E, dummy, sh.wsum2, tot, tot2);
         if (E < (uint32_t)K && (uint32_t)K <= E + loc) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -698,9 +790,10 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(const float* __res
             // one pass marks the keys above bin B (above_m) and in it (bin_m) and
             // puts bin B's keys with their owners in LDS; one wavefront ranks them,
             // finds the threshold and sets the owners' bits (own.gt / own.eq)
-            // bin B's keys lie in [Klo, Khi]; the invalid keys (0) lie below kmin
-            const uint32_t Klo = kmin + (bin << sh1);
-            const uint64_t hi = (uint64_t)Klo + ((uint64_t)1 << sh1) - 1u;
+            // bin B's valid keys lie in [max(Klo, kmin), Khi]; the invalid keys (0) below kmin
+            const uint32_t Kb = kb + (bin << sh1);
+            const uint32_t Klo = Kb > kmin ? Kb : kmin;
+            const uint64_t hi = (uint64_t)Kb + ((uint64_t)1 << sh1) - 1u;
             const uint32_t Khi = hi > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)hi;
             uint32_t above_m = 0u, bin_m = 0u;
 #pragma unroll
@@ -726,13 +819,13 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(const float* __res
                             for (int cc = 0; cc < EPT; ++cc) key = cc == c ? kr[cc] : key;
                         }
                         const uint32_t slot = atomicAdd(&sh.nbin, 1u);
-                        sh.binkey[slot] = key - kmin;
+                        sh.binkey[slot] = key;
                         sh.binown[slot] = ((uint32_t)tid << 5) | (uint32_t)c;
                     }
                 }
                 __syncthreads();
                 if (wave == 0) {
-                    // the need-th largest d of the bin is the d of every key with
+                    // the need-th largest key of the bin is every key with
                     // #greater < need <= #greater-or-equal
                     const bool ok = (uint32_t)lane < inbin;
                     const uint32_t d = ok ? sh.binkey[lane] : 0u;
@@ -760,12 +853,10 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(const float* __res
                 bin_m &= sh.own_eq[tid];
             }
             need_eq = need;
-            // counts of rows up to 32768 positions fit 16 bits each
-            uint32_t total;
-            const uint32_t ex = block_excl_scan(((uint32_t)__popc(bin_m) << 16) | (uint32_t)__popc(above_m), sh.wsum,
-                                                total);
-            rg = ex & 0xFFFFu;
-            re = ex >> 16;
+            rg = (uint32_t)__popc(above_m);
+            re = (uint32_t)__popc(bin_m);
+            uint32_t tg, te;
+            block_excl_scan2(rg, re, sh.wsum2, tg, te);
             // this thread's selected keys in position order (a loop over set bits:
             // only the position is needed)
             uint32_t m = above_m | bin_m;
@@ -773,23 +864,22 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(const float* __res
                 const int c = __builtin_ctz(m);
                 m &= m - 1u;
                 if ((above_m >> c) & 1u) {
-                    out[rg + (re < need_eq ? re : need_eq)] = (int32_t)(base + c);
+                    const uint32_t o = rg + (re < need_eq ? re : need_eq);
+                    if (o < (uint32_t)K) out[o] = (int32_t)(base + c);   // always true; bounds the store
                     ++rg;
                 } else {
-                    if (re < need_eq) out[rg + re] = (int32_t)(base + c);
+                    if (re < need_eq && rg + re < (uint32_t)K) out[rg + re] = (int32_t)(base + c);
                     ++re;
                 }
             }
         } else {
             // 64 keys a thread: bin B's keys go to LDS, one wavefront sorts them,
             // a second pass takes the masks (fewer live registers)
-            uint32_t dT = bin;   // sh1 = 0: every key of bin B has d = B
+            uint32_t T = kb + bin;   // sh1 = 0: every key of bin B is kb + B
             if (sh1 > 0) {
 #pragma unroll
-                for (int c = 0; c < EPT; ++c) {
-                    const uint32_t d = kr[c] - kmin;
-                    if (c < nv && (d >> sh1) == bin) sh.binkey[atomicAdd(&sh.nbin, 1u)] = d;
-                }
+                for (int c = 0; c < EPT; ++c)
+                    if (c < nv && ((kr[c] - kb) >> sh1) == bin) sh.binkey[atomicAdd(&sh.nbin, 1u)] = kr[c];
                 __syncthreads();
                 if (wave == 0) {
                     const bool ok = (uint32_t)lane < inbin;
@@ -812,12 +902,11 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(const float* __res
                     }
                 }
                 __syncthreads();
-                dT = sh.bin;
+                T = sh.bin;
                 need -= sh.above;
             }
             need_eq = need;
             // invalid keys (0) lie below kmin <= T
-            const uint32_t T = kmin + dT;
             uint32_t g0 = 0u, g1 = 0u, e0 = 0u, e1 = 0u;
 #pragma unroll
             for (int c = EPT / 2 - 1; c >= 0; --c) {
@@ -828,20 +917,20 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(const float* __res
             }
             const uint64_t gtm = ((uint64_t)g1 << 32) | g0;
             const uint64_t eqm = (((uint64_t)e1 << 32) | e0) & ~gtm;
-            uint64_t total;
-            const uint64_t ex = block_excl_scan64(((uint64_t)__popcll(eqm) << 32) | (uint64_t)__popcll(gtm),
-                                                  sh.wsum64, total);
-            rg = (uint32_t)ex;
-            re = (uint32_t)(ex >> 32);
+            rg = (uint32_t)__popcll(gtm);
+            re = (uint32_t)__popcll(eqm);
+            uint32_t tg, te;
+            block_excl_scan2(rg, re, sh.wsum2, tg, te);
             uint64_t m = gtm | eqm;
             while (m != 0ull) {
                 const int c = __builtin_ctzll(m);
                 m &= m - 1ull;
                 if ((gtm >> c) & 1ull) {
-                    out[rg + (re < need_eq ? re : need_eq)] = (int32_t)(base + c);
+                    const uint32_t o = rg + (re < need_eq ? re : need_eq);
+                    if (o < (uint32_t)K) out[o] = (int32_t)(base + c);   // always true; bounds the store
                     ++rg;
                 } else {
-                    if (re < need_eq) out[rg + re] = (int32_t)(base + c);
+                    if (re < need_eq && rg + re < (uint32_t)K) out[rg + re] = (int32_t)(base + c);
                     ++re;
                 }
             }
@@ -857,14 +946,14 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(const float* __res
     {
         uint64_t fm = 0ull;
 #pragma unroll
-        for (int c = 0; c < EPT; ++c) fm |= (uint64_t)(c < nv && ((kr[c] - kmin) >> sh1) >= bin) << c;
+        for (int c = 0; c < EPT; ++c) fm |= (uint64_t)(c < nv && ((kr[c] - kb) >> sh1) >= bin) << c;
         uint32_t tot;
         uint32_t at = block_excl_scan((uint32_t)__popcll(fm), sh.wsum, tot);
 #pragma unroll
         for (int c = 0; c < EPT; ++c) {
             if ((fm >> c) & 1ull) {
                 sh.u.c.pos[at] = (int32_t)(base + c);
-                sh.u.c.key[at] = kr[c] - kmin;
+                sh.u.c.key[at] = kr[c] - kb;
                 ++at;
             }
         }
