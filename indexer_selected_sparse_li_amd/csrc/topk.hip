@@ -646,41 +646,63 @@ __device__ __forceinline__ int tk_load_staged(const float* s, int64_t n, f32x4* 
     return nv;
 }
 
-// Top-K of one row per workgroup, the row's keys in registers (n > K
-// visible positions):
-//  1. min and max key; d = key - kmin maps the row onto [0, range] in order;
-//  2. a histogram of the first digit of d (its top 12 bits below the range's
-//     top bit, so the row spreads over up to 4096 bins) and the bin B holding
-//     the K-th largest key: every key with digit > B is selected, the C keys
-//     with digit >= B are the candidates;
-//  3. the candidates' (position, d) move to LDS in position order;
-//  4. 10-bit digits of the remaining bits of d, over the candidates in bin B
-//     only, fix the threshold and how many keys equal to it are taken;
-//  5. the ordered emission over the candidate list.
-// A row with more than kTkCandCap candidates (few distinct digits near the
-// K-th value) takes the general selection on global memory instead.
 template <int EPT>
-__global__ __launch_bounds__(kTkThreads) void topk_row_kernel(const float* __restrict__ scores, int64_t ld,
-                                                              const int32_t* __restrict__ row_pos, int K,
-                                                              int32_t* __restrict__ idx) {
-    __shared__ TkRowShared sh;
-    const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t n = tk_row_len(row_pos[r], ld);
-    int32_t* out = idx + (int64_t)r * K;
-    if (n <= K) {
-        tk_write_all(out, n, K);
-        return;
-    }
-    const float* s = scores + (int64_t)r * ld;
+using TkBits = typename std::conditional<(EPT <= 32), uint32_t, uint64_t>::type;
 
-    // 1. keys, min and max.  Every pass over the keys has a copy without the
-    // per-key validity test for the threads whose keys are all valid; only the
-    // thread holding the row's end runs the tested one.
-    uint32_t kr[EPT];
-    const int64_t base = (int64_t)tid * EPT;
-    const bool vec = ((ld & 3) == 0) && ((((uintptr_t)scores) & 15) == 0);
-    const int nv = vec ? tk_load_staged<EPT>(s, n, sh.u.stage, kr) : tk_load<EPT>(s, false, base, n, kr);
-    const bool full = nv == EPT;
+// Ordered emission from per-thread masks: every key in gtm, and of the keys in
+// eqm the first need_eq in list order (thread t's keys c are list entries
+// t * EPT + c).  One block scan of the per-thread counts; the stores are
+// bounded by K.
+template <int EPT, class Emit>
+__device__ __forceinline__ void tk_emit_masks(TkRowShared& sh, TkBits<EPT> gtm, TkBits<EPT> eqm, uint32_t need_eq,
+                                              uint32_t K, Emit& emit) {
+    using M = TkBits<EPT>;
+    uint32_t rg = (uint32_t)__builtin_popcountll(gtm), re = (uint32_t)__builtin_popcountll(eqm), tg, te;
+    block_excl_scan2(rg, re, sh.wsum2, tg, te);
+    // a loop over set bits: only the list index is needed
+    M m = gtm | eqm;
+    while (m != (M)0) {
+        const int c = (int)__builtin_ctzll((uint64_t)m);
+        m &= m - (M)1;
+        if ((gtm >> c) & (M)1) {
+            const uint32_t o = rg + (re < need_eq ? re : need_eq);
+            if (o < K) emit(c, o);   // always true; bounds the store
+            ++rg;
+        } else {
+            if (re < need_eq && rg + re < K) emit(c, rg + re);
+            ++re;
+        }
+    }
+}
+
+// The K largest of the valid keys held by a workgroup, in registers: thread t
+// holds list entries t * EPT + c as keys kr[c] (float_key order; invalid
+// entries are 0, below every key of a float), valid(c) tells them apart and
+// `full` says that all EPT are valid (the passes then skip the test).  More
+// than K entries are valid.  Larger keys win, equal keys go to the lower list
+// index; the selected entries come out in list order through
+// emit(c, slot) (by the owning thread) or emit_list(slot, list index) (any
+// thread), and `fallback` takes over when bin B holds too many candidates.
+// stf: the workgroup's floats staged in LDS (tk_load_staged layout), or null.
+//  1. min and max key;
+//  2. a histogram of the first digit (key >> s) - (kmin >> s), with s the
+//     smallest shift that keeps the row below 4096 bins, and the bin B
+//     holding the K-th largest key: the keys with a larger digit are selected;
+//  3'. bin B with at most 64 keys (or one value): its keys go to LDS with
+//     their owners, one wavefront ranks them, finds the threshold and sets
+//     the owners' bits; then the emission straight from the registers;
+//  3. otherwise the C keys with digit >= B move to LDS in list order, 10-bit
+//     digits of their remaining bits fix the threshold, and the emission
+//     walks the list.
+template <int EPT, class Valid, class Emit, class EmitList, class Fallback>
+__device__ __forceinline__ void tk_block_topk(TkRowShared& sh, const uint32_t (&kr)[EPT], Valid valid, bool full,
+                                              const float* stf, uint32_t K, Emit emit, EmitList emit_list,
+                                              Fallback fallback) {
+    using M = TkBits<EPT>;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    // 1. min and max.  Every pass over the keys has a copy without the per-key
+    // validity test for the threads whose keys are all valid.
     uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
     if (full) {
 #pragma unroll
@@ -691,7 +713,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(const float* __res
     } else {
 #pragma unroll
         for (int c = 0; c < EPT; ++c) {
-            if (c < nv) {
+            if (valid(c)) {
                 kmin = kr[c] < kmin ? kr[c] : kmin;
                 kmax = kr[c] > kmax ? kr[c] : kmax;
             }
@@ -732,8 +754,11 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(const float* __res
         kmax = (uint32_t)__builtin_amdgcn_readlane((int)vmax, 15);
     }
     const uint32_t range = kmax - kmin;
-    if (range == 0u) {   // all keys equal: the first K positions
-        for (int i = tid; i < K; i += kTkThreads) out[i] = i;
+    if (range == 0u) {   // every valid key equal: the first K valid entries
+        M vm = (M)0;
+#pragma unroll
+        for (int c = 0; c < EPT; ++c) vm |= (M)valid(c) << c;
+        tk_emit_masks<EPT>(sh, (M)0, vm, K, K, emit);
         return;
     }
     // first digit of a key: (key >> sh1) - (kmin >> sh1) = d >> sh1 with
@@ -754,7 +779,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(const float* __res
     } else {
 #pragma unroll
         for (int c = 0; c < EPT; ++c)
-            if (c < nv) atomicAdd(&sh.hist[(kr[c] - kb) >> sh1], 1u);
+            if (valid(c)) atomicAdd(&sh.hist[(kr[c] - kb) >> sh1], 1u);
     }
     __syncthreads();
     {
@@ -766,10 +791,10 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(const float* __res
         }
         uint32_t E = loc, dummy = 0u, tot, tot2;
         block_excl_scan2(E, dummy, sh.wsum2, tot, tot2);
-        if (E < (uint32_t)K && (uint32_t)K <= E + loc) {
+        if (E < K && K <= E + loc) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                if (E < (uint32_t)K && (uint32_t)K <= E + cb[j]) {
+                if (E < K && K <= E + cb[j]) {
                     sh.bin = (uint32_t)(kTkD1Bins - 1 - (4 * tid + j));
                     sh.above = E;
                 }
@@ -781,16 +806,13 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(const float* __res
     const uint32_t bin = sh.bin, above = sh.above;
     const uint32_t inbin = sh.hist[bin];
     const uint32_t C = above + inbin;
-    uint32_t need = (uint32_t)K - above;   // taken from bin B, >= 1
+    uint32_t need = K - above;   // taken from bin B, >= 1
 
     if (sh1 == 0 || inbin <= (uint32_t)kWave) {
         // 3'. small threshold bin (at most 64 keys, or one value when sh1 = 0)
-        uint32_t rg, re, need_eq;
         if constexpr (EPT <= 32) {
-            // one pass marks the keys above bin B (above_m) and in it (bin_m) and
-            // puts bin B's keys with their owners in LDS; one wavefront ranks them,
-            // finds the threshold and sets the owners' bits (own.gt / own.eq)
-            // bin B's valid keys lie in [max(Klo, kmin), Khi]; the invalid keys (0) below kmin
+            // one pass marks the keys above bin B (above_m) and in it (bin_m)
+            // bin B's valid keys lie in [max(Kb, kmin), Khi]; the invalid keys (0) below kmin
             const uint32_t Kb = kb + (bin << sh1);
             const uint32_t Klo = Kb > kmin ? Kb : kmin;
             const uint64_t hi = (uint64_t)Kb + ((uint64_t)1 << sh1) - 1u;
@@ -806,13 +828,12 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(const float* __res
                 if (bin_m != 0u) {
                     sh.own_gt[tid] = 0u;
                     sh.own_eq[tid] = 0u;
-                    // the few bin keys: from the row's LDS copy when there is one
-                    // (registers cannot be indexed at run time)
-                    const float* stf = (const float*)sh.u.stage;
+                    // the few bin keys with their owners to LDS: from the staged
+                    // floats when there are some (registers cannot be indexed at run time)
                     for (uint32_t m = bin_m; m != 0u; m &= m - 1u) {
                         const int c = __builtin_ctz(m);
                         uint32_t key = 0u;
-                        if (vec) {
+                        if (stf) {
                             key = float_key(stf[tk_slot<EPT / 4>(tid * (EPT / 4) + (c >> 2)) * 4 + (c & 3)]);
                         } else {
 #pragma unroll
@@ -852,34 +873,15 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(const float* __res
                 above_m |= sh.own_gt[tid] & bin_m;
                 bin_m &= sh.own_eq[tid];
             }
-            need_eq = need;
-            rg = (uint32_t)__popc(above_m);
-            re = (uint32_t)__popc(bin_m);
-            uint32_t tg, te;
-            block_excl_scan2(rg, re, sh.wsum2, tg, te);
-            // this thread's selected keys in position order (a loop over set bits:
-            // only the position is needed)
-            uint32_t m = above_m | bin_m;
-            while (m != 0u) {
-                const int c = __builtin_ctz(m);
-                m &= m - 1u;
-                if ((above_m >> c) & 1u) {
-                    const uint32_t o = rg + (re < need_eq ? re : need_eq);
-                    if (o < (uint32_t)K) out[o] = (int32_t)(base + c);   // always true; bounds the store
-                    ++rg;
-                } else {
-                    if (re < need_eq && rg + re < (uint32_t)K) out[rg + re] = (int32_t)(base + c);
-                    ++re;
-                }
-            }
+            tk_emit_masks<EPT>(sh, above_m, bin_m, need, K, emit);
         } else {
-            // 64 keys a thread: bin B's keys go to LDS, one wavefront sorts them,
+            // 64 keys a thread: bin B's keys go to LDS, one wavefront ranks them,
             // a second pass takes the masks (fewer live registers)
             uint32_t T = kb + bin;   // sh1 = 0: every key of bin B is kb + B
             if (sh1 > 0) {
 #pragma unroll
                 for (int c = 0; c < EPT; ++c)
-                    if (c < nv && ((kr[c] - kb) >> sh1) == bin) sh.binkey[atomicAdd(&sh.nbin, 1u)] = kr[c];
+                    if (valid(c) && ((kr[c] - kb) >> sh1) == bin) sh.binkey[atomicAdd(&sh.nbin, 1u)] = kr[c];
                 __syncthreads();
                 if (wave == 0) {
                     const bool ok = (uint32_t)lane < inbin;
@@ -905,7 +907,6 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(const float* __res
                 T = sh.bin;
                 need -= sh.above;
             }
-            need_eq = need;
             // invalid keys (0) lie below kmin <= T
             uint32_t g0 = 0u, g1 = 0u, e0 = 0u, e1 = 0u;
 #pragma unroll
@@ -917,42 +918,26 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(const float* __res
             }
             const uint64_t gtm = ((uint64_t)g1 << 32) | g0;
             const uint64_t eqm = (((uint64_t)e1 << 32) | e0) & ~gtm;
-            rg = (uint32_t)__popcll(gtm);
-            re = (uint32_t)__popcll(eqm);
-            uint32_t tg, te;
-            block_excl_scan2(rg, re, sh.wsum2, tg, te);
-            uint64_t m = gtm | eqm;
-            while (m != 0ull) {
-                const int c = __builtin_ctzll(m);
-                m &= m - 1ull;
-                if ((gtm >> c) & 1ull) {
-                    const uint32_t o = rg + (re < need_eq ? re : need_eq);
-                    if (o < (uint32_t)K) out[o] = (int32_t)(base + c);   // always true; bounds the store
-                    ++rg;
-                } else {
-                    if (re < need_eq && rg + re < (uint32_t)K) out[rg + re] = (int32_t)(base + c);
-                    ++re;
-                }
-            }
+            tk_emit_masks<EPT>(sh, gtm, eqm, need, K, emit);
         }
         return;
     }
     if (C > (uint32_t)kTkCandCap) {
-        tk_row_global(sh.u.tk, s, n, K, out);
+        fallback();
         return;
     }
 
-    // 3. candidates (position, d) to LDS in position order
+    // 3. candidates (list index, d) to LDS in list order
     {
         uint64_t fm = 0ull;
 #pragma unroll
-        for (int c = 0; c < EPT; ++c) fm |= (uint64_t)(c < nv && ((kr[c] - kb) >> sh1) >= bin) << c;
-        uint32_t tot;
-        uint32_t at = block_excl_scan((uint32_t)__popcll(fm), sh.wsum, tot);
+        for (int c = 0; c < EPT; ++c) fm |= (uint64_t)(valid(c) && ((kr[c] - kb) >> sh1) >= bin) << c;
+        uint32_t at = (uint32_t)__popcll(fm), dummy = 0u, tot, tot2;
+        block_excl_scan2(at, dummy, sh.wsum2, tot, tot2);
 #pragma unroll
         for (int c = 0; c < EPT; ++c) {
             if ((fm >> c) & 1ull) {
-                sh.u.c.pos[at] = (int32_t)(base + c);
+                sh.u.c.pos[at] = (int32_t)(tid * EPT + c);
                 sh.u.c.key[at] = kr[c] - kb;
                 ++at;
             }
@@ -973,8 +958,8 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(const float* __res
         }
         __syncthreads();
         const uint32_t cb = (uint32_t)tid < nb ? sh.hist[nb - 1u - tid] : 0u;
-        uint32_t tot;
-        const uint32_t E = block_excl_scan(cb, sh.wsum, tot);
+        uint32_t E = cb, dummy = 0u, tot, tot2;
+        block_excl_scan2(E, dummy, sh.wsum2, tot, tot2);
         if (E < need && need <= E + cb) {
             sh.bin = nb - 1u - (uint32_t)tid;
             sh.above = E;
@@ -990,31 +975,59 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(const float* __res
     // 5. ordered emission: thread t takes list entries [t * E2, t * E2 + E2)
     const uint32_t E2 = (C + kTkThreads - 1) / kTkThreads;   // <= 8
     const uint32_t b0 = (uint32_t)tid * E2;
-    uint32_t g = 0u, e = 0u;
+    uint32_t rg = 0u, re = 0u;
     for (uint32_t j = 0; j < E2; ++j) {
         const uint32_t i = b0 + j;
         if (i < C) {
             const uint32_t d = sh.u.c.key[i];
-            g += d > T;
-            e += d == T;
+            rg += d > T;
+            re += d == T;
         }
     }
-    uint64_t total;
-    const uint64_t ex = block_excl_scan64(((uint64_t)e << 32) | g, sh.wsum64, total);
-    uint32_t rg = (uint32_t)ex, re = (uint32_t)(ex >> 32);
+    uint32_t tg, te;
+    block_excl_scan2(rg, re, sh.wsum2, tg, te);
     for (uint32_t j = 0; j < E2; ++j) {
         const uint32_t i = b0 + j;
         if (i < C) {
             const uint32_t d = sh.u.c.key[i];
             if (d > T) {
-                out[rg + (re < need_eq ? re : need_eq)] = sh.u.c.pos[i];
+                const uint32_t o = rg + (re < need_eq ? re : need_eq);
+                if (o < K) emit_list(o, (uint32_t)sh.u.c.pos[i]);
                 ++rg;
             } else if (d == T) {
-                if (re < need_eq) out[rg + re] = sh.u.c.pos[i];
+                if (re < need_eq && rg + re < K) emit_list(rg + re, (uint32_t)sh.u.c.pos[i]);
                 ++re;
             }
         }
     }
+}
+
+// Top-K of one row per workgroup (n > K visible positions), the row's keys in
+// registers (16-byte aligned rows come through the LDS stage); rows whose
+// threshold bin holds more than kTkCandCap candidates take the general
+// selection on global memory.
+template <int EPT>
+__global__ __launch_bounds__(kTkThreads) void topk_row_kernel(const float* __restrict__ scores, int64_t ld,
+                                                              const int32_t* __restrict__ row_pos, int K,
+                                                              int32_t* __restrict__ idx) {
+    __shared__ TkRowShared sh;
+    const int r = blockIdx.x, tid = threadIdx.x;
+    const int64_t n = tk_row_len(row_pos[r], ld);
+    int32_t* out = idx + (int64_t)r * K;
+    if (n <= K) {
+        tk_write_all(out, n, K);
+        return;
+    }
+    const float* s = scores + (int64_t)r * ld;
+    uint32_t kr[EPT];
+    const int64_t base = (int64_t)tid * EPT;
+    const bool vec = ((ld & 3) == 0) && ((((uintptr_t)scores) & 15) == 0);
+    const int nv = vec ? tk_load_staged<EPT>(s, n, sh.u.stage, kr) : tk_load<EPT>(s, false, base, n, kr);
+    tk_block_topk<EPT>(
+        sh, kr, TkPrefix{nv}, nv == EPT, (vec && EPT <= 32) ? (const float*)sh.u.stage : nullptr, (uint32_t)K,
+        [&](int c, uint32_t o) { out[o] = (int32_t)(base + c); },
+        [&](uint32_t o, uint32_t li) { out[o] = (int32_t)li; },
+        [&]() { tk_row_global(sh.u.tk, s, n, K, out); });
 }
 
 // One workgroup per row with the keys re-read from global memory: rows
@@ -1045,7 +1058,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_cand_kernel(const float* __re
                                                                const int32_t* __restrict__ pos_offset,
                                                                int32_t* __restrict__ cand_pos,
                                                                float* __restrict__ cand_score) {
-    __shared__ TkShared sh;
+    __shared__ TkRowShared sh;
     const int sl = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
     int64_t n = (int64_t)row_pos[r] + 1;
     if (n < 0) n = 0;
@@ -1057,23 +1070,108 @@ __global__ __launch_bounds__(kTkThreads) void topk_cand_kernel(const float* __re
     const int32_t off = pos_offset ? pos_offset[r] : 0;
     int32_t* op = cand_pos + ((int64_t)r * S + sl) * K;
     float* os = cand_score + ((int64_t)r * S + sl) * K;
-    const float* s = scores + (int64_t)r * ld;
+    const float* s = scores + (int64_t)r * ld + lo;   // the slice
     if (cnt <= K) {
         for (int64_t i = tid; i < K; i += kTkThreads) {
             const bool v = i < cnt;
             op[i] = v ? (int32_t)(lo + i + off) : -1;
-            os[i] = v ? s[lo + i] : -__builtin_inff();
+            os[i] = v ? s[i] : -__builtin_inff();
         }
         return;
     }
-    const bool vec = ((ld & 3) == 0) && ((((uintptr_t)scores) & 15) == 0);
-    const int64_t base = lo + (int64_t)tid * EPT;
+    const bool vec = ((ld & 3) == 0) && ((((uintptr_t)scores) & 15) == 0);   // lo is a multiple of 4
+    const int64_t base = (int64_t)tid * EPT;
     uint32_t kr[EPT];
-    const int nv = tk_load<EPT>(s, vec, base, lo + cnt, kr);
-    tk_select<EPT>(sh, kr, TkPrefix{nv}, (uint32_t)K, [&](int c, uint32_t slot) {
-        op[slot] = (int32_t)(base + c + off);
-        os[slot] = s[base + c];
-    });
+    const int nv = vec ? tk_load_staged<EPT>(s, cnt, sh.u.stage, kr) : tk_load<EPT>(s, false, base, cnt, kr);
+    auto put = [&](int64_t li, uint32_t o) {
+        op[o] = (int32_t)(lo + li + off);
+        os[o] = s[li];
+    };
+    tk_block_topk<EPT>(
+        sh, kr, TkPrefix{nv}, nv == EPT, (vec && EPT <= 32) ? (const float*)sh.u.stage : nullptr, (uint32_t)K,
+        [&](int c, uint32_t o) { put(base + c, o); }, [&](uint32_t o, uint32_t li) { put(li, o); },
+        [&]() { tk_select<EPT>(sh.u.tk, kr, TkPrefix{nv}, (uint32_t)K, [&](int c, uint32_t o) { put(base + c, o); }); });
+}
+
+// Ordered merge (the valid candidates of a row in ascending position order,
+// so list order settles ties): the K best of n (position, score) pairs,
+// position < 0 = none, out in list order, -1 padded.
+template <int EPT>
+__global__ __launch_bounds__(kTkThreads) void topk_merge_ordered_kernel(const float* __restrict__ cand_score,
+                                                                        const int32_t* __restrict__ cand_pos,
+                                                                        int64_t ldc, int n, int K,
+                                                                        int32_t* __restrict__ idx,
+                                                                        float* __restrict__ idx_score) {
+    __shared__ TkRowShared sh;
+    const int r = blockIdx.x, tid = threadIdx.x;
+    const float* cs = cand_score + (int64_t)r * ldc;
+    const int32_t* cp = cand_pos + (int64_t)r * ldc;
+    int32_t* out = idx + (int64_t)r * K;
+    float* outs = idx_score ? idx_score + (int64_t)r * K : nullptr;
+    const int base = tid * EPT;
+    uint32_t kr[EPT];
+    int32_t pr[EPT];
+    uint64_t vm = 0ull;
+    // 16-byte loads when this thread's candidates are whole and aligned
+    const bool vec = EPT % 4 == 0 && (ldc & 3) == 0 && base + EPT <= n &&
+                     ((((uintptr_t)cand_score) | ((uintptr_t)cand_pos)) & 15) == 0;
+    if (vec) {
+#pragma unroll
+        for (int c = 0; c < EPT; c += 4) {
+            const i32x4 p4 = *(const i32x4*)(cp + base + c);
+            const f32x4 s4 = *(const f32x4*)(cs + base + c);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                pr[c + e] = p4[e];
+                kr[c + e] = p4[e] >= 0 ? float_key(s4[e]) : 0u;
+                vm |= (uint64_t)(p4[e] >= 0) << (c + e);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < EPT; ++c) {
+            const int i = base + c;
+            const int32_t p = i < n ? cp[i] : -1;
+            pr[c] = p;
+            kr[c] = p >= 0 ? float_key(cs[i]) : 0u;
+            vm |= (uint64_t)(p >= 0) << c;
+        }
+    }
+    uint32_t first = (uint32_t)__popcll(vm), dummy = 0u, nvalid, tot2;
+    block_excl_scan2(first, dummy, sh.wsum2, nvalid, tot2);
+    if (nvalid <= (uint32_t)K) {
+#pragma unroll
+        for (int c = 0; c < EPT; ++c) {
+            if ((vm >> c) & 1ull) {
+                out[first] = pr[c];
+                if (outs) outs[first] = cs[base + c];
+                ++first;
+            }
+        }
+        for (int i = (int)nvalid + tid; i < K; i += kTkThreads) {
+            out[i] = -1;
+            if (outs) outs[i] = -__builtin_inff();
+        }
+        return;
+    }
+    __syncthreads();   // wsum2 is read above and written again below
+    constexpr uint64_t all = EPT == 64 ? ~0ull : ((1ull << EPT) - 1ull);
+    tk_block_topk<EPT>(
+        sh, kr, TkMask{vm}, vm == all, nullptr, (uint32_t)K,
+        [&](int c, uint32_t o) {
+            out[o] = pr[c];
+            if (outs) outs[o] = cs[base + c];
+        },
+        [&](uint32_t o, uint32_t li) {
+            out[o] = cp[li];
+            if (outs) outs[o] = cs[li];
+        },
+        [&]() {
+            tk_select<EPT>(sh.u.tk, kr, TkMask{vm}, (uint32_t)K, [&](int c, uint32_t o) {
+                out[o] = pr[c];
+                if (outs) outs[o] = cs[base + c];
+            });
+        });
 }
 
 constexpr int kTkMergeMaxK = 4096;   // unordered merge: selected pairs sorted in LDS
@@ -1269,8 +1367,17 @@ static hipError_t launch_merge(const float* cs, const int32_t* cp, int64_t ldc, 
 #define LISFA_TKM(E_)                                                                                    \
     hipLaunchKernelGGL((topk_merge_kernel<E_>), dim3((unsigned)R), dim3(kTkThreads), 0, stream, cs, cp, ldc, n, \
                        K, ordered, idx, idx_score)
-    if (ept <= 8) LISFA_TKM(8);
-    else LISFA_TKM(16);
+#define LISFA_TKMO(E_)                                                                                       \
+    hipLaunchKernelGGL((topk_merge_ordered_kernel<E_>), dim3((unsigned)R), dim3(kTkThreads), 0, stream, cs, cp, \
+                       ldc, n, K, idx, idx_score)
+    if (ordered) {
+        if (ept <= 8) LISFA_TKMO(8);
+        else LISFA_TKMO(16);
+    } else {
+        if (ept <= 8) LISFA_TKM(8);
+        else LISFA_TKM(16);
+    }
+#undef LISFA_TKMO
 #undef LISFA_TKM
     return hipGetLastError();
 }
