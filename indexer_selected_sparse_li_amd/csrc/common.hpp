@@ -85,15 +85,6 @@ __device__ __forceinline__ int64_t slot_of(const CacheDev& c, int seq, int64_t p
     return (s >= 0 && s < c.num_slots) ? s : -1;
 }
 
-// Order-preserving map fp32 -> uint32 (-0.0 is folded onto +0.0).
-__device__ __forceinline__ uint32_t float_key(float f) {
-    // sign clear: b + 2^31; sign set: 2^31 - |b| (b's two's complement), so
-    // -0 and +0 share a key and no float maps to 0
-    const uint32_t b = __float_as_uint(f);
-    const uint32_t s = (uint32_t)((int32_t)b >> 31);
-    return (b ^ (s | 0x80000000u)) - s;
-}
-
 // Exact e4m3 (OCP) pair -> fp32 pair via the hardware converter.
 template <bool HI>
 __device__ __forceinline__ f32x2 fp8x2_to_f32(uint32_t word) {
