@@ -367,6 +367,8 @@ def main():
     ap.add_argument("--report-cp", action="store_true",
                     help="time one GPU's context-parallel share and the Zigzag prefill balance")
     ap.add_argument("--report-prolog", action="store_true", help="time the indexer prolog kernels")
+    ap.add_argument("--report-cold", action="store_true",
+                    help="time the layer's stages hot and cold (after an L2 / MALL eviction)")
     ap.add_argument("--report-md", help="with --report-all / --report-cp: write a markdown table here")
     args = ap.parse_args()
     if args.write_traffic_summary:
@@ -405,6 +407,9 @@ def main():
         return
     if args.report_prolog:
         report_prolog(args)
+        return
+    if args.report_cold:
+        report_cold(args)
         return
     wl = W.get(args.workload)
     res, b = run_workload(args, wl, cold=not args.only)
@@ -808,6 +813,113 @@ def report_cp(args):
                 fh.write(f"| {part} | " + " | ".join(str(x) for x in zz[part]["ms"]) +
                          f' | {zz[part]["max_over_min"]} |\n')
         log(f"[bench] wrote {args.report_md}")
+
+
+def report_cold(args):
+    """The layer's stages hot and cold on a few workloads: each stage on its
+    own, back-to-back (hot) and after a 512 MiB write that evicts the L2s and
+    the MALL (cold), then the layer's three stages in turn with HIP events at
+    the stage boundaries, cold and hot.  Eager launches on one stream."""
+    import torch
+    import indexer_selected_sparse_li_amd as lisfa
+    import workloads as W
+    names = [args.workload] if args.workload != "decode_paged_64x32768" else [
+        "decode_paged_64x32768", "decode_paged_64x32768_mxfp8", "batched_paged_64x4k_32k", "fp8_decode_16x131072"]
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    n = args.steps
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    rows = []
+    for name in names:
+        wl = W.get(name)
+        log(f"[bench] cold/hot stages of {name}")
+        b = W.make_batch(wl, device="cuda")
+        R = b.R
+        kc = lisfa.KVCache(data=b.k_data, scale=b.k_scale, scale_group=1, block_table=b.block_table,
+                           block_size=wl.block_size, seq_base=b.seq_base)
+        vc = lisfa.KVCache(data=b.kv_data, scale=b.kv_scale, scale_group=wl.kv_scale_group,
+                           block_table=b.block_table, block_size=wl.block_size, seq_base=b.seq_base)
+        out = torch.empty(R, wl.H, wl.D_v, dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty(R, wl.H, dtype=torch.float32, device="cuda")
+        idx = torch.empty(R, wl.K, dtype=torch.int32, device="cuda")
+        ld = (b.max_visible + 63) // 64 * 64
+        scores = torch.empty(R, ld, dtype=torch.float32, device="cuda")
+        sws = torch.empty(max(1, lisfa.workspace_size(1, R, 0, wl.K, wl.H, wl.D_v)), dtype=torch.uint8,
+                          device="cuda")
+        stages = [
+            ("li_score", lambda: lisfa.li_score(b.q_idx, b.w, kc, b.row_seq, b.row_pos, scores, b.max_visible,
+                                                q_scale=b.q_scale, stream=stream)),
+            ("topk_select", lambda: lisfa.topk_select(scores, b.row_pos, wl.K, idx, stream=stream)),
+            ("sparse_mla_attn", lambda: lisfa.sparse_mla_attn(b.q, vc, b.row_seq, idx, out, lse,
+                                                              softmax_scale=wl.softmax_scale, workspace=sws,
+                                                              stream=stream)),
+        ]
+        for _, f in stages:
+            f()
+        torch.cuda.synchronize()
+        alone = {}
+        for sname, f in stages:
+            for _ in range(args.warmup):
+                f()
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            for _ in range(n):
+                f()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            hot = e0.elapsed_time(e1) / n * 1e3
+            es = []
+            for i in range(n):
+                flush.fill_(i & 255)
+                a, c = ev(), ev()
+                a.record(stream)
+                f()
+                c.record(stream)
+                es.append((a, c))
+            torch.cuda.synchronize()
+            alone[sname] = (hot, sum(a.elapsed_time(c) for a, c in es) / n * 1e3)
+        split = {}
+        for mode in ("cold", "hot"):
+            es = []
+            for i in range(n):
+                if mode == "cold":
+                    flush.fill_(i & 255)
+                e = [ev() for _ in range(len(stages) + 1)]
+                e[0].record(stream)
+                for j, (_, f) in enumerate(stages):
+                    f()
+                    e[j + 1].record(stream)
+                es.append(e)
+            torch.cuda.synchronize()
+            split[mode] = [sum(e[j].elapsed_time(e[j + 1]) for e in es) / n * 1e3 for j in range(len(stages))]
+        for j, (sname, _) in enumerate(stages):
+            rows.append((name, sname, alone[sname][0], alone[sname][1], split["hot"][j], split["cold"][j]))
+        rows.append((name, "layer", sum(v[0] for v in alone.values()), sum(v[1] for v in alone.values()),
+                     sum(split["hot"]), sum(split["cold"])))
+        for r in rows[-4:]:
+            log(f"[bench] {r[0]} {r[1]}: alone hot {r[2]:.1f} cold {r[3]:.1f} us; in the layer hot {r[4]:.1f} "
+                f"cold {r[5]:.1f} us")
+        del b, kc, vc, scores
+        torch.cuda.empty_cache()
+    print(json.dumps([dict(workload=r[0], stage=r[1], alone_hot_us=round(r[2], 1), alone_cold_us=round(r[3], 1),
+                           layer_hot_us=round(r[4], 1), layer_cold_us=round(r[5], 1)) for r in rows]), flush=True)
+    if args.report_md:
+        with open(args.report_md, "w") as fh:
+            fh.write("# The layer's stages hot and cold (one MI355X)\n\n")
+            fh.write("Each stage alone: back-to-back calls (hot), and calls that each follow a 512 MiB write that\n"
+                     "evicts the L2s and the MALL (cold). In the layer: the three stages in turn with HIP events at\n"
+                     "the stage boundaries, hot and cold (the flush before each layer step). Eager launches on one\n"
+                     f"stream, {n} timed calls each.\n\n")
+            fh.write("Command (from the repository root):\n\n")
+            fh.write(f"    python3 bench.py --report-cold --steps {n} --report-md "
+                     f"{os.path.relpath(args.report_md, ROOT)}\n\n")
+            fh.write("| workload | stage | alone hot us | alone cold us | in the layer hot us | in the layer cold us |\n"
+                     "|---|---|---|---|---|---|\n")
+            for r in rows:
+                fh.write(f"| {r[0]} | {r[1]} | {r[2]:.1f} | {r[3]:.1f} | {r[4]:.1f} | {r[5]:.1f} |\n")
 
 
 def report_prolog(args):

@@ -191,7 +191,7 @@ __global__ __launch_bounds__(128 * NHG) void sfa_kernel(MlaDev a, int kps, int n
                 const int part = SWZ ? (pos ^ sfa_swz(row)) : pos;
                 const int64_t off = roff[t * TROWS + row];
                 const uint8_t* g = (off >= 0 && part < CPK) ? a.kv.data + off + part * 16 : g_zero16;
-                lds_dma<16, 0>(g, lds0 + (uint32_t)(j * NT * 16));
+                lds_dma<16, 0, true>(g, lds0 + (uint32_t)(j * NT * 16));
             }
         }
     };
@@ -694,7 +694,7 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
             constexpr int j = decltype(jc)::value;
             // the immediate offset moves both the global and the LDS address;
             // block j lands at blk + j KB
-            lds_dma<16, j * 128>(gp, blk + (uint32_t)(j * (1024 - 128)));
+            lds_dma<16, j * 128, true>(gp, blk + (uint32_t)(j * (1024 - 128)));
         });
     };
 
