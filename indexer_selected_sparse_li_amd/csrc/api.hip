@@ -167,6 +167,11 @@ MlaDev to_dev(const lisfa_mla_args* a, const int32_t* idx, int K) {
     d.H = a->H;
     d.K = K;
     d.scale_log2 = a->softmax_scale * kLog2e;
+    // at most one query row per sequence: no cached row is gathered twice by
+    // different query rows, so the gathers go non-temporal (2.8 -> 5.3 TB/s for
+    // scattered rows from HBM); rows that share sequences (prefill) keep the
+    // ordinary loads, whose cached lines the other rows reuse
+    d.gather_nt = a->R <= a->kv_cache.num_seqs ? 1 : 0;
     return d;
 }
 

@@ -66,6 +66,7 @@ struct MlaDev {
     CacheDev kv;
     int32_t R, H, K;
     float scale_log2;        // softmax_scale * log2(e)
+    int32_t gather_nt;       // latent rows gathered with non-temporal loads (no row shared by two query rows)
 };
 
 // Physical slot of (sequence, logical position), or -1 when the position is

@@ -191,7 +191,8 @@ __global__ __launch_bounds__(128 * NHG) void sfa_kernel(MlaDev a, int kps, int n
                 const int part = SWZ ? (pos ^ sfa_swz(row)) : pos;
                 const int64_t off = roff[t * TROWS + row];
                 const uint8_t* g = (off >= 0 && part < CPK) ? a.kv.data + off + part * 16 : g_zero16;
-                lds_dma<16, 0, true>(g, lds0 + (uint32_t)(j * NT * 16));
+                if (a.gather_nt) lds_dma<16, 0, true>(g, lds0 + (uint32_t)(j * NT * 16));
+                else lds_dma<16, 0>(g, lds0 + (uint32_t)(j * NT * 16));
             }
         }
     };
@@ -624,7 +625,7 @@ __device__ __forceinline__ int sfa_swz8(int r) { return (((r >> 1) & 3) << 1) | 
 // Outputs: nsplit == 1: bf16 out (+ lse) or, with out == nullptr, normalised
 // fp32 out_f32 + lse; nsplit > 1: normalised bf16 partials part_o [R, nsplit,
 // H, 512] + part_lse [R, nsplit, H] for the combine kernel.
-template <int NBUF, int MAXK, int KVF>
+template <int NBUF, int MAXK, int KVF, bool GNT = false>
 __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsplit, int nhb,
                                                        __bf16* __restrict__ out, float* __restrict__ lse,
                                                        float* __restrict__ out_f32, __bf16* __restrict__ part_o,
@@ -690,11 +691,11 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
     auto issue_rows = [&](uint32_t s, int buf) {        // one tile's row of this lane
         const uint8_t* gp = (s != 0xFFFFFFFFu ? a.kv.data + (uint64_t)s * (uint32_t)a.kv.row_stride : g_zero_row) + goff;
         const uint32_t blk = tile_lds + (uint32_t)(buf * TB + pc * GB);
+        // the immediate offset moves both the global and the LDS address; block j
+        // lands at blk + j KB.  GNT: non-temporal gathers (the launch's gather_nt)
         static_for<NJ>([&](auto jc) {
             constexpr int j = decltype(jc)::value;
-            // the immediate offset moves both the global and the LDS address;
-            // block j lands at blk + j KB
-            lds_dma<16, j * 128, true>(gp, blk + (uint32_t)(j * (1024 - 128)));
+            lds_dma<16, j * 128, GNT>(gp, blk + (uint32_t)(j * (1024 - 128)));
         });
     };
 
@@ -1133,7 +1134,10 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
             const bool ok = s != 0xFFFFFFFFu;
             const uint8_t* gp = ok ? a.kv.data + (uint64_t)s * (uint32_t)a.kv.row_stride : g_zero_row;
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) cd.v[j] = __builtin_nontemporal_load((const u32x2*)(gp + (8 * j + fsw) * 8));
+            for (int j = 0; j < NJ; ++j) {
+                const u32x2* src = (const u32x2*)(gp + (8 * j + fsw) * 8);
+                cd.v[j] = a.gather_nt ? __builtin_nontemporal_load(src) : *src;
+            }
             if constexpr (KVF == 1) {
                 cd.f[0] = ok ? a.kv.scale[(int64_t)s / a.kv.scale_group] : 0.f;
             } else if constexpr (KVF == 2) {
@@ -1460,17 +1464,29 @@ static hipError_t launch_sfa512(const MlaDev& a, const SfaPlan& p, int kv_mode, 
                                 float* lse, __bf16* part_o, float* part_lse, hipStream_t stream) {
     const int64_t units = (int64_t)a.R * p.nsplit;
     const dim3 grid((unsigned)((units + 7) / 8 * 8 * p.nhb)), block(512);
-#define LISFA_MLA(NB_, MK_, KVF_)                                                                        \
-    hipLaunchKernelGGL((sfa_mla_kernel<NB_, MK_, KVF_>), grid, block, 0, stream, a, p.kps, p.nsplit, p.nhb, \
+#define LISFA_MLA4(NB_, MK_, KVF_, GNT_)                                                                     \
+    hipLaunchKernelGGL((sfa_mla_kernel<NB_, MK_, KVF_, GNT_>), grid, block, 0, stream, a, p.kps, p.nsplit, p.nhb, \
                        out, lse, out_f32, part_o, part_lse)
+#define LISFA_MLA(NB_, MK_, KVF_) LISFA_MLA4(NB_, MK_, KVF_, false)
     const bool short_list = p.kps <= 1024;
-    if (kv_mode == 0 && short_list) LISFA_MLA(4, 1024, 0);
-    else if (kv_mode == 0) LISFA_MLA(3, kSfaMaxKeys, 0);
-    else if (kv_mode == 1 && short_list) LISFA_MLA(3, 1024, 1);
-    else if (kv_mode == 1) LISFA_MLA(3, kSfaMaxKeys, 1);
-    else if (short_list) LISFA_MLA(3, 1024, 2);
-    else LISFA_MLA(3, kSfaMaxKeys, 2);
+    // bf16 rows: the gather policy is a template argument (fp8 rows read a.gather_nt)
+    if (kv_mode == 0 && short_list) {
+        if (a.gather_nt) LISFA_MLA4(4, 1024, 0, true);
+        else LISFA_MLA4(4, 1024, 0, false);
+    } else if (kv_mode == 0) {
+        if (a.gather_nt) LISFA_MLA4(3, kSfaMaxKeys, 0, true);
+        else LISFA_MLA4(3, kSfaMaxKeys, 0, false);
+    } else if (kv_mode == 1 && short_list) {
+        LISFA_MLA(3, 1024, 1);
+    } else if (kv_mode == 1) {
+        LISFA_MLA(3, kSfaMaxKeys, 1);
+    } else if (short_list) {
+        LISFA_MLA(3, 1024, 2);
+    } else {
+        LISFA_MLA(3, kSfaMaxKeys, 2);
+    }
 #undef LISFA_MLA
+#undef LISFA_MLA4
     return hipGetLastError();
 }
 
