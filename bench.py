@@ -62,7 +62,8 @@ def algorithmic(wl, b):
 
 
 KERNEL_SOURCES = {
-    "li_score": ["li_score.hip", "common.hpp"],
+    "li_score": ["li_score.hip", "li_dec.hpp", "common.hpp"],
+    "li_topk": ["li_topk.hip", "li_dec.hpp", "common.hpp"],
     "topk_select": ["topk.hip", "common.hpp"],
     "sparse_mla_attn": ["sparse_mla.hip", "common.hpp"],
 }

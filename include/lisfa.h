@@ -174,6 +174,28 @@ int topk_select(const float* scores, int64_t ld_scores, const int32_t* row_pos,
                 lisfa_stream_t stream);
 
 /*
+ * li_topk - indexer scores and Top-K in one step: the per-row list of selected
+ * positions without the scores ("Kimi New Model Open Source ...", section 3:
+ * one operator reads the paged key cache and outputs only the index list;
+ * "Large Language Model Inference Acceleration in Practice", section 3.1:
+ * weighting and Top-K on chip, the pointers handed to the sparse attention).
+ *   args: as li_score (row r sees positions 0..row_pos[r], clamped to
+ *         max_visible rounded up to a multiple of 64).
+ *   idx:  [R, K] int32 out, ascending positions, -1 padded.
+ *   ws:   lisfa_workspace_size(LISFA_OP_LI_TOPK, R, max_visible, K, 0, 0) bytes,
+ *         256-byte aligned (NULL when that size is 0).
+ * The result equals li_score followed by topk_select on the same inputs, bit for
+ * bit.  Decode rows (rows_per_group 1) with bf16 or per-token fp8 keys
+ * (D_I = 128 for fp8) and MXFP8 keys are scored and selected in one launch
+ * whose scores stay on chip when a row spans at most 64 workgroups of at most
+ * 16384 positions and the launch has at most 256 workgroups (or one workgroup
+ * per row); other shapes score into the workspace in row chunks and select
+ * from there.
+ */
+int li_topk(const lisfa_indexer_args* args, int32_t K, int32_t* idx, void* ws,
+            size_t ws_bytes, lisfa_stream_t stream);
+
+/*
  * Context parallelism: the cached positions of a sequence are split over G
  * GPUs; each GPU scores its own positions, keeps its local Top-K with the
  * scores, the candidates of all GPUs are gathered and merged into the
@@ -385,6 +407,7 @@ int li_topk_sfa_noalloc(const lisfa_indexer_args* iargs, const lisfa_mla_args* m
 #define LISFA_OP_FUSED              2
 #define LISFA_OP_TOPK_CANDIDATES    3   /* max_visible argument = ld_scores */
 #define LISFA_OP_SPARSE_MLA_PARTIAL 4
+#define LISFA_OP_LI_TOPK            5
 
 /* Workspace bytes an entry point needs for the given sizes (host function). */
 size_t lisfa_workspace_size(int32_t op, int32_t R, int64_t max_visible, int32_t K,

@@ -8,6 +8,8 @@ streams.  If the library has not been built, every call raises.
 Entry points (same names as the C ABI):
   li_score(...)        lightning-indexer scores  [R, ld] fp32
   topk_select(...)     per-row Top-K index lists [R, K] int32
+  li_topk(...)         scores and Top-K in one step (decode rows: one launch,
+                       the scores stay on chip) -> index lists [R, K] int32
   sparse_mla_attn(...) sparse MLA attention      [R, H, D_latent] bf16 (+ lse)
   li_topk_sfa(...)     all three in one call on one stream
   li_topk_sfa_noalloc(...)  the same with no workspace: the library's static
@@ -33,7 +35,7 @@ import torch
 
 from . import _lib as _c
 
-__all__ = ["KVCache", "LisfaError", "li_score", "topk_select", "sparse_mla_attn", "li_topk_sfa", "li_topk_sfa_noalloc",
+__all__ = ["KVCache", "LisfaError", "li_score", "li_topk", "topk_select", "sparse_mla_attn", "li_topk_sfa", "li_topk_sfa_noalloc",
            "topk_candidates", "topk_merge", "sparse_mla_attn_partial", "lse_combine", "zigzag_share",
            "zigzag_restore", "indexer_q_quant", "indexer_k_store", "indexer_prolog", "workspace_size", "load",
            "status_string"]
@@ -205,6 +207,22 @@ def li_score(q_idx, w, k_cache: KVCache, row_seq, row_pos, scores, max_visible: 
         raise ValueError("scores must be [R, ld] fp32")
     _check(lib.li_score(ctypes.byref(a), _ptr(scores), scores.shape[1], _stream(stream)), "li_score")
     return scores
+
+
+def li_topk(q_idx, w, k_cache: KVCache, row_seq, row_pos, K: int, idx, max_visible: int, q_scale=None,
+            rows_per_group: int = 1, workspace=None, stream=None):
+    """idx[r] = ascending positions of the K largest indexer scores of row r
+    (those li_score would write), -1 padded; the scores are not returned."""
+    lib = _c.load()
+    a = _indexer_args(q_idx, w, k_cache, row_seq, row_pos, max_visible, q_scale, rows_per_group)
+    R = a.R
+    if idx.dtype != torch.int32 or tuple(idx.shape) != (R, K):
+        raise ValueError("idx must be [R, K] int32")
+    need = lib.lisfa_workspace_size(_c.LISFA_OP_LI_TOPK, R, max_visible, K, 0, 0)
+    ws = _workspace(workspace, need, q_idx.device, stream)
+    _check(lib.li_topk(ctypes.byref(a), K, _ptr(idx), _ptr(ws) if (ws is not None and need) else None, need,
+                       _stream(stream)), "li_topk")
+    return idx
 
 
 def topk_select(scores, row_pos, K: int, idx, workspace=None, stream=None):

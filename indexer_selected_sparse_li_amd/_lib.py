@@ -25,11 +25,12 @@ LISFA_OP_SPARSE_MLA = 1
 LISFA_OP_FUSED = 2
 LISFA_OP_TOPK_CANDIDATES = 3
 LISFA_OP_SPARSE_MLA_PARTIAL = 4
+LISFA_OP_LI_TOPK = 5
 
 LISFA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 EXPORTS = (
-    "li_score", "topk_select", "sparse_mla_attn", "li_topk_sfa", "li_topk_sfa_noalloc",
+    "li_score", "li_topk", "topk_select", "sparse_mla_attn", "li_topk_sfa", "li_topk_sfa_noalloc",
     "topk_candidates", "topk_merge", "sparse_mla_attn_partial", "lse_combine",
     "lisfa_zigzag_share", "zigzag_restore", "indexer_q_quant", "indexer_k_store", "indexer_prolog",
     "lisfa_workspace_size", "lisfa_status_string", "lisfa_struct_size", "lisfa_abi_version",
@@ -98,6 +99,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     lib.li_score.argtypes = [ctypes.POINTER(IndexerArgs), vp, i64, vp]
     lib.li_score.restype = ctypes.c_int
+    lib.li_topk.argtypes = [ctypes.POINTER(IndexerArgs), i32, vp, vp, sz, vp]
+    lib.li_topk.restype = ctypes.c_int
     lib.topk_select.argtypes = [vp, i64, vp, i32, i32, vp, vp, sz, vp]
     lib.topk_select.restype = ctypes.c_int
     lib.sparse_mla_attn.argtypes = [ctypes.POINTER(MlaArgs), vp, i32, vp, vp, vp, sz, vp]

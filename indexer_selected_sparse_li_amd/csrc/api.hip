@@ -23,6 +23,9 @@ size_t topk_workspace_bytes(int R, int64_t ld, int K);
 hipError_t sfa_dispatch(const MlaDev& a, int D_latent, int kv_mode, __bf16* out, float* out_f32, float* lse, void* ws,
                         hipStream_t stream);
 size_t sfa_workspace_bytes(int R, int K, int H, int D_latent);
+size_t li_topk_workspace_bytes(int R);
+hipError_t li_topk_dispatch(const IndexerDev& a, int D_I, int dtype, int qg, int64_t ld, int K, int32_t* idx,
+                            void* ws, size_t ws_bytes, hipStream_t st);
 hipError_t sfa_partial_dispatch(const MlaDev& a, const int32_t* range, int D_latent, int kv_mode, float* out_f32,
                                 float* lse, void* ws, hipStream_t stream);
 size_t sfa_partial_workspace_bytes(int R, int K, int H, int D_latent, int with_range);
@@ -195,51 +198,55 @@ int64_t fused_chunk_rows(int32_t R, int64_t max_visible, int64_t score_cap) {
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
+// Workspace of the index step (scores + Top-K): the score chunk, or the
+// exchange area of the fused kernel, at offset 0, then Top-K scratch.
+struct IndexLayout {
+    size_t cand, total;
+};
+
+IndexLayout index_layout(int32_t R, int64_t max_visible, int32_t K, int64_t score_cap = kScoreScratchCap) {
+    IndexLayout L;
+    const int64_t rc = fused_chunk_rows(R, max_visible, score_cap);
+    const size_t sc = align256((size_t)rc * scores_ld(max_visible) * sizeof(float));
+    const size_t lt = align256(li_topk_workspace_bytes(R));
+    L.cand = sc > lt ? sc : lt;
+    L.total = L.cand + align256(topk_workspace_bytes((int)rc, scores_ld(max_visible), K));
+    return L;
+}
+
 struct FusedLayout {
-    size_t scores, idx, cand, sfa, total;
+    size_t idx, sfa, total;
 };
 
 FusedLayout fused_layout(int32_t R, int64_t max_visible, int32_t K, int32_t H, int32_t D_latent,
                          int64_t score_cap = kScoreScratchCap) {
     FusedLayout L;
-    const int64_t rc = fused_chunk_rows(R, max_visible, score_cap);
-    L.scores = 0;
-    L.idx = align256((size_t)rc * scores_ld(max_visible) * sizeof(float));
-    L.cand = L.idx + align256((size_t)R * K * sizeof(int32_t));
-    L.sfa = L.cand + align256(topk_workspace_bytes((int)rc, scores_ld(max_visible), K));
+    L.idx = index_layout(R, max_visible, K, score_cap).total;
+    L.sfa = L.idx + align256((size_t)R * K * sizeof(int32_t));
     L.total = L.sfa + align256(sfa_workspace_bytes(R, K, H, D_latent));
     return L;
 }
 
-int check_fused(const lisfa_indexer_args* iargs, const lisfa_mla_args* margs, int32_t K, const void* out) {
-    int e = check_indexer(iargs);
-    if (e) return e;
-    e = check_mla(margs);
-    if (e) return e;
-    if (K < 1) return LISFA_ERR_BAD_SHAPE;
-    if (iargs->R != margs->R) return LISFA_ERR_BAD_SHAPE;
-    if (iargs->R == 0) return LISFA_OK;
-    if (!out) return LISFA_ERR_NULL_ARG;
-    if (!aligned(out, 8)) return LISFA_ERR_BAD_SHAPE;
-    return LISFA_OK;
-}
-
-// The layer on validated arguments, scores in row chunks of at most score_cap
-// bytes, with the workspace at w (laid out by fused_layout with the same cap).
-int fused_run(const lisfa_indexer_args* iargs, const lisfa_mla_args* margs, int32_t K, int32_t* idx_out, void* out,
-              float* lse, uint8_t* w, int64_t score_cap, hipStream_t st) {
+// Indices of validated indexer rows: one fused score + Top-K launch where the
+// shape and format allow it (scores stay on chip), else scores in row chunks
+// of at most score_cap bytes followed by topk_select.  The workspace at w is
+// laid out by index_layout with the same cap.
+int index_rows(const lisfa_indexer_args* iargs, int32_t K, int32_t* idx, uint8_t* w, int64_t score_cap,
+               hipStream_t st) {
     const int32_t R = iargs->R;
-    const FusedLayout L = fused_layout(R, iargs->max_visible, K, margs->H, margs->D_latent, score_cap);
-    float* scores = (float*)(w + L.scores);
-    int32_t* idx = idx_out ? idx_out : (int32_t*)(w + L.idx);
-    void* sfa_ws = w + L.sfa;
-
+    const IndexLayout L = index_layout(R, iargs->max_visible, K, score_cap);
+    float* scores = (float*)w;
     const int64_t ld = scores_ld(iargs->max_visible) > 0 ? scores_ld(iargs->max_visible) : 64;
-    const int64_t rc = fused_chunk_rows(R, iargs->max_visible, score_cap);
     const int qg = (iargs->rows_per_group % 16 == 0) ? 16 : (iargs->rows_per_group % 8 == 0) ? 8 : 1;
+    IndexerDev d = to_dev(iargs);
+    if (iargs->max_visible > 0) {
+        const hipError_t he = li_topk_dispatch(d, iargs->D_I, iargs->k_cache.dtype, qg, ld, K, idx, w, L.cand, st);
+        if (he == hipSuccess) return LISFA_OK;
+        if (he != hipErrorNotSupported) return LISFA_ERR_HIP;
+    }
+    const int64_t rc = fused_chunk_rows(R, iargs->max_visible, score_cap);
     const int elt = iargs->k_cache.dtype == LISFA_BF16 ? 2 : 1;
     const bool mx = iargs->k_cache.dtype == LISFA_MXFP8;
-    IndexerDev d = to_dev(iargs);
     for (int64_t c0 = 0; c0 < R; c0 += rc) {
         const int64_t c1 = c0 + rc < R ? c0 + rc : R;
         IndexerDev dc = d;
@@ -258,9 +265,34 @@ int fused_run(const lisfa_indexer_args* iargs, const lisfa_mla_args* margs, int3
         hipError_t he = topk_dispatch(scores, ld, dc.row_pos, dc.R, K, idx + c0 * K, w + L.cand, st);
         if (he != hipSuccess) return LISFA_ERR_HIP;
     }
+    return LISFA_OK;
+}
+
+int check_fused(const lisfa_indexer_args* iargs, const lisfa_mla_args* margs, int32_t K, const void* out) {
+    int e = check_indexer(iargs);
+    if (e) return e;
+    e = check_mla(margs);
+    if (e) return e;
+    if (K < 1) return LISFA_ERR_BAD_SHAPE;
+    if (iargs->R != margs->R) return LISFA_ERR_BAD_SHAPE;
+    if (iargs->R == 0) return LISFA_OK;
+    if (!out) return LISFA_ERR_NULL_ARG;
+    if (!aligned(out, 8)) return LISFA_ERR_BAD_SHAPE;
+    return LISFA_OK;
+}
+
+// The layer on validated arguments, the index step as index_rows with the
+// given score cap, with the workspace at w (laid out by fused_layout with the
+// same cap).
+int fused_run(const lisfa_indexer_args* iargs, const lisfa_mla_args* margs, int32_t K, int32_t* idx_out, void* out,
+              float* lse, uint8_t* w, int64_t score_cap, hipStream_t st) {
+    const FusedLayout L = fused_layout(iargs->R, iargs->max_visible, K, margs->H, margs->D_latent, score_cap);
+    int32_t* idx = idx_out ? idx_out : (int32_t*)(w + L.idx);
+    const int e = index_rows(iargs, K, idx, w, score_cap, st);
+    if (e) return e;
     const MlaDev md = to_dev(margs, idx, K);
     return hip_status(sfa_dispatch(md, margs->D_latent, kv_mode(margs->kv_cache), (__bf16*)out,
-                                   nullptr, lse, sfa_ws, st));
+                                   nullptr, lse, w + L.sfa, st));
 }
 
 // Scratch of the allocation-free fused entry point: one array per GPU, held
@@ -363,6 +395,7 @@ size_t lisfa_workspace_size(int32_t op, int32_t R, int64_t max_visible, int32_t 
         case LISFA_OP_SPARSE_MLA: return sfa_workspace_bytes(R, K, H, D_latent);
         case LISFA_OP_FUSED: return fused_layout(R, max_visible, K, H, D_latent).total;
         case LISFA_OP_SPARSE_MLA_PARTIAL: return sfa_partial_workspace_bytes(R, K, H, D_latent, 1);
+        case LISFA_OP_LI_TOPK: return index_layout(R, max_visible, K).total;
         default: return 0;
     }
 }
@@ -377,6 +410,19 @@ int li_score(const lisfa_indexer_args* args, float* scores, int64_t ld_scores, l
     const int qg = (args->rows_per_group % 16 == 0) ? 16 : (args->rows_per_group % 8 == 0) ? 8 : 1;
     return hip_status(li_score_dispatch(d, args->D_I, args->k_cache.dtype, qg, scores, ld_scores,
                                         args->max_visible, (hipStream_t)stream));
+}
+
+int li_topk(const lisfa_indexer_args* args, int32_t K, int32_t* idx, void* ws, size_t ws_bytes,
+            lisfa_stream_t stream) {
+    int e = check_indexer(args);
+    if (e) return e;
+    if (K < 1) return LISFA_ERR_BAD_SHAPE;
+    if (args->R == 0) return LISFA_OK;
+    if (!idx) return LISFA_ERR_NULL_ARG;
+    const IndexLayout L = index_layout(args->R, args->max_visible, K);
+    if (L.total > 0 && (!ws || ws_bytes < L.total)) return LISFA_ERR_WORKSPACE;
+    if (L.total > 0 && !aligned(ws, 256)) return LISFA_ERR_BAD_SHAPE;
+    return index_rows(args, K, idx, (uint8_t*)ws, kScoreScratchCap, (hipStream_t)stream);
 }
 
 int topk_select(const float* scores, int64_t ld_scores, const int32_t* row_pos, int32_t R, int32_t K,

@@ -117,6 +117,16 @@ __device__ __forceinline__ f32x16 mfma32x32x16_fp8(int64_t a, int64_t b, f32x16 
     return __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a, b, c, 0, 0, 0);
 }
 
+// Order-preserving map fp32 -> uint32 with -0.0 and +0.0 on one key: sign
+// clear: b + 2^31; sign set: 2^31 - |b| (b's two's complement), so no float
+// maps to 0, which marks an invalid entry below every key.  NaN (sign clear)
+// orders above +inf.  Both Top-K paths select on these keys.
+__device__ __forceinline__ uint32_t float_key(float f) {
+    const uint32_t b = __float_as_uint(f);
+    const uint32_t s = (uint32_t)((int32_t)b >> 31);
+    return (b ^ (s | 0x80000000u)) - s;
+}
+
 __device__ __forceinline__ uint32_t lanemask_count(uint64_t mask) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
                                      __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));

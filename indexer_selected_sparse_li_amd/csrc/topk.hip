@@ -30,15 +30,6 @@ namespace lisfa {
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
-// Order-preserving map fp32 -> uint32 with -0.0 and +0.0 on one key: sign
-// clear: b + 2^31; sign set: 2^31 - |b| (b's two's complement), so no float
-// maps to 0, which marks an invalid entry below every key.
-__device__ __forceinline__ uint32_t float_key(float f) {
-    const uint32_t b = __float_as_uint(f);
-    const uint32_t s = (uint32_t)((int32_t)b >> 31);
-    return (b ^ (s | 0x80000000u)) - s;
-}
-
 constexpr int kTkThreads = 1024;
 constexpr int kTkWaves = kTkThreads / kWave;
 constexpr int kTkSegChunks = kTkThreads / kTkWaves;  // chunks per emission segment (64)

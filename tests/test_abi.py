@@ -183,6 +183,34 @@ def test_fused_validation(clib):
                             None) == C.LISFA_ERR_BAD_SHAPE
 
 
+def test_li_topk_validation(clib):
+    """li_topk validates like li_score, then K, the output and the workspace,
+    all before any launch."""
+    a = _idx_args(R=2)
+    need = clib.lisfa_workspace_size(C.LISFA_OP_LI_TOPK, 2, 100, 2048, 0, 0)
+    assert need > 0   # rows that span several workgroups exchange through the workspace
+    assert clib.li_topk(ctypes.byref(a), 0, 16, 256, need, None) == C.LISFA_ERR_BAD_SHAPE
+    assert clib.li_topk(ctypes.byref(a), 2048, None, 256, need, None) == C.LISFA_ERR_NULL_ARG
+    assert clib.li_topk(ctypes.byref(a), 2048, 16, 256, need - 1, None) == C.LISFA_ERR_WORKSPACE
+    assert clib.li_topk(ctypes.byref(a), 2048, 16, None, need, None) == C.LISFA_ERR_WORKSPACE
+    assert clib.li_topk(ctypes.byref(a), 2048, 16, 16, need, None) == C.LISFA_ERR_BAD_SHAPE
+    assert clib.li_topk(None, 2048, 16, 256, need, None) == C.LISFA_ERR_NULL_ARG
+    assert clib.li_topk(ctypes.byref(_idx_args(H_I=65)), 2048, 16, 256, need, None) == C.LISFA_ERR_UNSUPPORTED
+    assert clib.li_topk(ctypes.byref(_idx_args(R=0, q=None, w=None)), 4, None, None, 0, None) == C.LISFA_OK
+
+
+def test_li_topk_workspace_covers_both_paths(clib):
+    # few rows: the fused exchange area (up to 256 workgroups of 3 x 16 KB)
+    few = clib.lisfa_workspace_size(C.LISFA_OP_LI_TOPK, 64, 32768, 2048, 0, 0)
+    assert few >= 3 * 256 * 16384
+    assert few >= 64 * 32768 * 4          # the score scratch of the separate kernels
+    # many rows: one workgroup per row, no exchange; bounded score chunks
+    many = clib.lisfa_workspace_size(C.LISFA_OP_LI_TOPK, 4096, 65536, 2048, 0, 0)
+    assert (256 << 20) <= many < (300 << 20)
+    fused = clib.lisfa_workspace_size(C.LISFA_OP_FUSED, 64, 32768, 2048, 128, 512)
+    assert fused >= few + 64 * 2048 * 4
+
+
 def test_noalloc_validation(clib):
     """The allocation-free entry validates like li_topk_sfa and refuses, before
     touching the GPU, sizes whose smallest layout does not fit its scratch."""
