@@ -58,7 +58,9 @@ def algorithmic(wl, b):
     sfa_bytes = rows * (wl.D_qk * ve + vs) + R * wl.H * (wl.D_qk * 2 + wl.D_v * 2 + 4) + sel * 4
     sfa_flops = 2.0 * wl.H * sel * (wl.D_qk + wl.D_v)
     topk_bytes = vis * 4 + R * wl.K * 4
-    return dict(li=(li_bytes, li_flops), topk=(topk_bytes, 0.0), sfa=(sfa_bytes, sfa_flops))
+    lt_bytes = li_bytes + R * wl.K * 4    # fused: keys and queries in, index lists out, no scores
+    return dict(li=(li_bytes, li_flops), topk=(topk_bytes, 0.0), sfa=(sfa_bytes, sfa_flops),
+                lt=(lt_bytes, li_flops))
 
 
 KERNEL_SOURCES = {
@@ -346,7 +348,7 @@ def main():
     ap.add_argument("--cpu-budget-each", type=float, default=4.0,
                     help="with --report-all: seconds of oracle time per workload")
     ap.add_argument("--stage-steps", type=int, default=None)
-    ap.add_argument("--only", choices=["li_score", "topk_select", "sparse_mla_attn", "layer"],
+    ap.add_argument("--only", choices=["li_score", "topk_select", "li_topk", "sparse_mla_attn", "layer"],
                     help="profiling mode: run just this stage (no JSON line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="profiling mode: run a plain device copy of --copy-bytes bytes")
@@ -463,6 +465,8 @@ def run_workload(args, wl, cold=False, graph=False):
             "li_score": lambda: lisfa.li_score(b.q_idx, b.w, kc, b.row_seq, b.row_pos, scores_o, b.max_visible,
                                                q_scale=b.q_scale, rows_per_group=rpg, stream=stream),
             "topk_select": lambda: lisfa.topk_select(scores_o, b.row_pos, wl.K, idx, stream=stream),
+            "li_topk": lambda: lisfa.li_topk(b.q_idx, b.w, kc, b.row_seq, b.row_pos, wl.K, idx, b.max_visible,
+                                             q_scale=b.q_scale, rows_per_group=rpg, workspace=ws, stream=stream),
             "sparse_mla_attn": lambda: lisfa.sparse_mla_attn(b.q, vc, b.row_seq, idx, out, lse,
                                                              softmax_scale=wl.softmax_scale, workspace=sfa_ws_o,
                                                              stream=stream),
@@ -526,6 +530,12 @@ def run_workload(args, wl, cold=False, graph=False):
                                                     stream=st), stream, 2, ss, graph)
     t_tk = time_on_stream(lambda st: lisfa.topk_select(scores, b.row_pos, wl.K, idx, stream=st),
                           stream, 2, ss, graph)
+    # the index step as the layer runs it: one fused launch when li_topk_plan says so
+    lt_wg = lisfa.li_topk_plan(b.q_idx, b.w, kc, b.row_seq, b.row_pos, wl.K, b.max_visible, q_scale=b.q_scale,
+                               rows_per_group=rpg, layer=True)
+    t_lt = time_on_stream(lambda st: lisfa.li_topk(b.q_idx, b.w, kc, b.row_seq, b.row_pos, wl.K, idx,
+                                                   b.max_visible, q_scale=b.q_scale, rows_per_group=rpg,
+                                                   workspace=ws, stream=st), stream, 2, ss, graph)
     t_sfa = time_on_stream(lambda st: lisfa.sparse_mla_attn(b.q, vc, b.row_seq, idx, out, lse,
                                                             softmax_scale=wl.softmax_scale, workspace=sfa_ws,
                                                             stream=st), stream, 2, ss, graph)
@@ -533,7 +543,8 @@ def run_workload(args, wl, cold=False, graph=False):
 
     def peak_tflops(name):
         # the indexer's contraction runs on fp8 MFMA for fp8 keys; sparse MLA always on bf16 MFMA
-        return FP8_PEAK_TFLOPS if (name == "li" and wl.indexer_dtype in ("fp8", "mxfp8")) else BF16_PEAK_TFLOPS
+        fp8 = name in ("li", "lt") and wl.indexer_dtype in ("fp8", "mxfp8")
+        return FP8_PEAK_TFLOPS if fp8 else BF16_PEAK_TFLOPS
 
     def roof(name, t, bound):
         by, fl = alg[name]
@@ -551,13 +562,15 @@ def run_workload(args, wl, cold=False, graph=False):
             return "hbm"
         return "mfma" if fl / max(by, 1) > peak_tflops(name) * 1e12 / (HBM_PEAK_GBS * 1e9) else "hbm"
 
+    fused = lt_wg > 0
+    in_layer = {"li_score": not fused, "topk_select": not fused, "li_topk": fused, "sparse_mla_attn": True}
     stages = {}
-    for name, t in (("li_score", t_li), ("topk_select", t_tk), ("sparse_mla_attn", t_sfa)):
-        key = {"li_score": "li", "topk_select": "topk", "sparse_mla_attn": "sfa"}[name]
+    for name, t in (("li_score", t_li), ("topk_select", t_tk), ("li_topk", t_lt), ("sparse_mla_attn", t_sfa)):
+        key = {"li_score": "li", "topk_select": "topk", "li_topk": "lt", "sparse_mla_attn": "sfa"}[name]
         r = roof(key, t, bound_of(key))
         stages[name] = dict(us=round(t * 1e6, 2), algorithmic_bytes=int(alg[key][0]),
-                            algorithmic_flops=int(alg[key][1]), roofline=r)
-    dominant = max(stages, key=lambda k: stages[k]["us"])
+                            algorithmic_flops=int(alg[key][1]), roofline=r, in_layer=in_layer[name])
+    dominant = max((k for k in stages if stages[k]["in_layer"]), key=lambda k: stages[k]["us"])
     roofline = dict(stages[dominant]["roofline"])
     roofline["kernel"] = dominant
     roofline["traffic"] = stored_traffic(dominant, wl.name)
@@ -576,6 +589,8 @@ def run_workload(args, wl, cold=False, graph=False):
                    "indexer": f"{wl.H_I}x{wl.D_I} {wl.indexer_dtype}",
                    "mla": f"{wl.H} heads {wl.D_latent}+{wl.D_rope} {wl.kv_dtype}",
                    "cache": f"paged {wl.block_size}" if wl.paged else "contiguous",
+                   "index_step": (f"li_topk fused, {lt_wg} workgroups per row, scores on chip" if fused
+                                  else "li_score + topk_select, scores through the workspace"),
                    "parallelism": "single GPU"},
         "roofline": roofline,
         "stages": stages,
@@ -850,19 +865,28 @@ def report_cold(args):
         scores = torch.empty(R, ld, dtype=torch.float32, device="cuda")
         sws = torch.empty(max(1, lisfa.workspace_size(1, R, 0, wl.K, wl.H, wl.D_v)), dtype=torch.uint8,
                           device="cuda")
-        stages = [
-            ("li_score", lambda: lisfa.li_score(b.q_idx, b.w, kc, b.row_seq, b.row_pos, scores, b.max_visible,
-                                                q_scale=b.q_scale, stream=stream)),
-            ("topk_select", lambda: lisfa.topk_select(scores, b.row_pos, wl.K, idx, stream=stream)),
-            ("sparse_mla_attn", lambda: lisfa.sparse_mla_attn(b.q, vc, b.row_seq, idx, out, lse,
-                                                              softmax_scale=wl.softmax_scale, workspace=sws,
-                                                              stream=stream)),
-        ]
-        for _, f in stages:
+        lws = torch.empty(max(1, lisfa.workspace_size(5, R, b.max_visible, wl.K, 0, 0)), dtype=torch.uint8,
+                          device="cuda")
+        fns = {
+            "li_score": lambda: lisfa.li_score(b.q_idx, b.w, kc, b.row_seq, b.row_pos, scores, b.max_visible,
+                                               q_scale=b.q_scale, stream=stream),
+            "topk_select": lambda: lisfa.topk_select(scores, b.row_pos, wl.K, idx, stream=stream),
+            "li_topk": lambda: lisfa.li_topk(b.q_idx, b.w, kc, b.row_seq, b.row_pos, wl.K, idx, b.max_visible,
+                                             q_scale=b.q_scale, workspace=lws, stream=stream),
+            "sparse_mla_attn": lambda: lisfa.sparse_mla_attn(b.q, vc, b.row_seq, idx, out, lse,
+                                                             softmax_scale=wl.softmax_scale, workspace=sws,
+                                                             stream=stream),
+        }
+        fused = lisfa.li_topk_plan(b.q_idx, b.w, kc, b.row_seq, b.row_pos, wl.K, b.max_visible,
+                                   q_scale=b.q_scale, layer=True) > 0
+        # the layer's own sequence of stages
+        stages = [(k, fns[k]) for k in (("li_topk", "sparse_mla_attn") if fused
+                                        else ("li_score", "topk_select", "sparse_mla_attn"))]
+        for f in fns.values():
             f()
         torch.cuda.synchronize()
         alone = {}
-        for sname, f in stages:
+        for sname, f in fns.items():
             for _ in range(args.warmup):
                 f()
             e0, e1 = ev(), ev()
@@ -896,11 +920,16 @@ def report_cold(args):
                 es.append(e)
             torch.cuda.synchronize()
             split[mode] = [sum(e[j].elapsed_time(e[j + 1]) for e in es) / n * 1e3 for j in range(len(stages))]
+        nrow0 = len(rows)
         for j, (sname, _) in enumerate(stages):
             rows.append((name, sname, alone[sname][0], alone[sname][1], split["hot"][j], split["cold"][j]))
-        rows.append((name, "layer", sum(v[0] for v in alone.values()), sum(v[1] for v in alone.values()),
+        for sname in fns:   # stages the layer does not run here, alone only
+            if sname not in dict(stages):
+                rows.append((name, sname + " (not in the layer)", alone[sname][0], alone[sname][1],
+                             float("nan"), float("nan")))
+        rows.append((name, "layer", sum(alone[k][0] for k, _ in stages), sum(alone[k][1] for k, _ in stages),
                      sum(split["hot"]), sum(split["cold"])))
-        for r in rows[-4:]:
+        for r in rows[nrow0:]:
             log(f"[bench] {r[0]} {r[1]}: alone hot {r[2]:.1f} cold {r[3]:.1f} us; in the layer hot {r[4]:.1f} "
                 f"cold {r[5]:.1f} us")
         del b, kc, vc, scores
@@ -911,9 +940,10 @@ def report_cold(args):
         with open(args.report_md, "w") as fh:
             fh.write("# The layer's stages hot and cold (one MI355X)\n\n")
             fh.write("Each stage alone: back-to-back calls (hot), and calls that each follow a 512 MiB write that\n"
-                     "evicts the L2s and the MALL (cold). In the layer: the three stages in turn with HIP events at\n"
-                     "the stage boundaries, hot and cold (the flush before each layer step). Eager launches on one\n"
-                     f"stream, {n} timed calls each.\n\n")
+                     "evicts the L2s and the MALL (cold). In the layer: the layer's stages in turn (li_topk +\n"
+                     "sparse_mla_attn where the fused index step takes the shape, else li_score + topk_select +\n"
+                     "sparse_mla_attn) with HIP events at the stage boundaries, hot and cold (the flush before each\n"
+                     f"layer step). Eager launches on one stream, {n} timed calls each.\n\n")
             fh.write("Command (from the repository root):\n\n")
             fh.write(f"    python3 bench.py --report-cold --steps {n} --report-md "
                      f"{os.path.relpath(args.report_md, ROOT)}\n\n")
@@ -1042,14 +1072,16 @@ def write_report_md(path, lines, args):
                  "calls from Python; graph = the same call captured once in a HIP graph and replayed (no\n"
                  "host overhead per call; every replay checked against the eager result first).\n"
                  "Stage times are hot, each stage launched on its own (graph-captured); the fraction is of the stage's binding\n"
-                 "roofline (HBM 8 TB/s; MFMA bf16 2.5 PFLOP/s, fp8 5.0) on algorithmic bytes or flops.\n\n")
+                 "roofline (HBM 8 TB/s; MFMA bf16 2.5 PFLOP/s, fp8 5.0) on algorithmic bytes or flops.\n"
+                 "The layer's index step is li_topk (scores and Top-K in one launch, the scores on chip) where\n"
+                 "li_topk_plan takes the shape, else li_score + topk_select; both are timed on every workload.\n\n")
         fh.write("Command (from the repository root):\n\n")
         fh.write(f"    python3 bench.py --report-all --steps {args.steps} --warmup {args.warmup} "
                  f"--report-md {os.path.relpath(path, ROOT)}\n\n")
         fh.write("| workload | rows | layer cold us | tokens/s cold | layer hot us | tokens/s hot | "
-                 "graph replay us | tokens/s graph | li_score us | topk_select us | sparse_mla_attn us | "
-                 "oracle tokens/s (threads) |\n")
-        fh.write("|---|---|---|---|---|---|---|---|---|---|---|---|\n")
+                 "graph replay us | tokens/s graph | li_topk us | li_score us | topk_select us | "
+                 "sparse_mla_attn us | oracle tokens/s (threads) |\n")
+        fh.write("|---|---|---|---|---|---|---|---|---|---|---|---|---|\n")
         for r in lines:
             cb = r.get("cpu_baseline")
             orc = f'{cb["value"]:.3g} ({cb["cores"]})' if cb else "not run"
@@ -1057,6 +1089,7 @@ def write_report_md(path, lines, args):
                      f'{r["ms_per_step_cold"] * 1e3:.1f} | {r["value_cold"]:.0f} | '
                      f'{r["ms_per_step_hot"] * 1e3:.1f} | {r["value_hot"]:.0f} | '
                      f'{r["ms_per_step_graph"] * 1e3:.1f} | {r["value_graph"]:.0f} | '
+                     f'{st(r, "li_topk")}{"" if r["stages"]["li_topk"]["in_layer"] else " (separate kernels)"} | '
                      f'{st(r, "li_score")} | {st(r, "topk_select")} | {st(r, "sparse_mla_attn")} | {orc} |\n')
         if any(r.get("cpu_baseline") for r in lines):
             fh.write("\nOracle: the CPU oracle (float64 NumPy, scores over the full visible context, selection, "

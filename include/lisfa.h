@@ -196,6 +196,18 @@ int li_topk(const lisfa_indexer_args* args, int32_t K, int32_t* idx, void* ws,
             size_t ws_bytes, lisfa_stream_t stream);
 
 /*
+ * li_topk_plan - how these arguments are scored and selected (host function,
+ * no GPU work): the number of workgroups that score and select each row in
+ * the single fused launch (>= 1; the scores never reach device memory), 0 when
+ * the separate score and Top-K kernels run instead, or a negative status for
+ * arguments li_topk would refuse.
+ *   layer = 0: li_topk, which takes the fused launch wherever the shape allows;
+ *   layer = 1: the index step of li_topk_sfa, which takes it only where it is
+ *              the faster path (bf16 keys, at most 4 workgroups per row).
+ */
+int32_t li_topk_plan(const lisfa_indexer_args* args, int32_t K, int32_t layer);
+
+/*
  * Context parallelism: the cached positions of a sequence are split over G
  * GPUs; each GPU scores its own positions, keeps its local Top-K with the
  * scores, the candidates of all GPUs are gathered and merged into the

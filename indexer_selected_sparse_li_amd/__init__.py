@@ -35,7 +35,7 @@ import torch
 
 from . import _lib as _c
 
-__all__ = ["KVCache", "LisfaError", "li_score", "li_topk", "topk_select", "sparse_mla_attn", "li_topk_sfa", "li_topk_sfa_noalloc",
+__all__ = ["KVCache", "LisfaError", "li_score", "li_topk", "li_topk_plan", "topk_select", "sparse_mla_attn", "li_topk_sfa", "li_topk_sfa_noalloc",
            "topk_candidates", "topk_merge", "sparse_mla_attn_partial", "lse_combine", "zigzag_share",
            "zigzag_restore", "indexer_q_quant", "indexer_k_store", "indexer_prolog", "workspace_size", "load",
            "status_string"]
@@ -223,6 +223,18 @@ def li_topk(q_idx, w, k_cache: KVCache, row_seq, row_pos, K: int, idx, max_visib
     _check(lib.li_topk(ctypes.byref(a), K, _ptr(idx), _ptr(ws) if (ws is not None and need) else None, need,
                        _stream(stream)), "li_topk")
     return idx
+
+
+def li_topk_plan(q_idx, w, k_cache: KVCache, row_seq, row_pos, K: int, max_visible: int, q_scale=None,
+                 rows_per_group: int = 1, layer: bool = False) -> int:
+    """Workgroups per row of the fused score + Top-K launch for these
+    arguments, or 0 when the separate score and Top-K kernels run (host query,
+    no GPU work); layer=True answers for the index step of li_topk_sfa."""
+    a = _indexer_args(q_idx, w, k_cache, row_seq, row_pos, max_visible, q_scale, rows_per_group)
+    n = int(_c.load().li_topk_plan(ctypes.byref(a), K, int(bool(layer))))
+    if n < 0:
+        raise LisfaError(n, "li_topk_plan")
+    return n
 
 
 def topk_select(scores, row_pos, K: int, idx, workspace=None, stream=None):

@@ -30,7 +30,7 @@ LISFA_OP_LI_TOPK = 5
 LISFA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 EXPORTS = (
-    "li_score", "li_topk", "topk_select", "sparse_mla_attn", "li_topk_sfa", "li_topk_sfa_noalloc",
+    "li_score", "li_topk", "li_topk_plan", "topk_select", "sparse_mla_attn", "li_topk_sfa", "li_topk_sfa_noalloc",
     "topk_candidates", "topk_merge", "sparse_mla_attn_partial", "lse_combine",
     "lisfa_zigzag_share", "zigzag_restore", "indexer_q_quant", "indexer_k_store", "indexer_prolog",
     "lisfa_workspace_size", "lisfa_status_string", "lisfa_struct_size", "lisfa_abi_version",
@@ -101,6 +101,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.li_score.restype = ctypes.c_int
     lib.li_topk.argtypes = [ctypes.POINTER(IndexerArgs), i32, vp, vp, sz, vp]
     lib.li_topk.restype = ctypes.c_int
+    lib.li_topk_plan.argtypes = [ctypes.POINTER(IndexerArgs), i32, i32]
+    lib.li_topk_plan.restype = i32
     lib.topk_select.argtypes = [vp, i64, vp, i32, i32, vp, vp, sz, vp]
     lib.topk_select.restype = ctypes.c_int
     lib.sparse_mla_attn.argtypes = [ctypes.POINTER(MlaArgs), vp, i32, vp, vp, vp, sz, vp]

@@ -24,8 +24,9 @@ hipError_t sfa_dispatch(const MlaDev& a, int D_latent, int kv_mode, __bf16* out,
                         hipStream_t stream);
 size_t sfa_workspace_bytes(int R, int K, int H, int D_latent);
 size_t li_topk_workspace_bytes(int R);
+int li_topk_fused_chunks(const IndexerDev& a, int D_I, int dtype, int qg, int64_t ld, int K, int layer);
 hipError_t li_topk_dispatch(const IndexerDev& a, int D_I, int dtype, int qg, int64_t ld, int K, int32_t* idx,
-                            void* ws, size_t ws_bytes, hipStream_t st);
+                            void* ws, size_t ws_bytes, int layer, hipStream_t st);
 hipError_t sfa_partial_dispatch(const MlaDev& a, const int32_t* range, int D_latent, int kv_mode, float* out_f32,
                                 float* lse, void* ws, hipStream_t stream);
 size_t sfa_partial_workspace_bytes(int R, int K, int H, int D_latent, int with_range);
@@ -228,10 +229,11 @@ FusedLayout fused_layout(int32_t R, int64_t max_visible, int32_t K, int32_t H, i
 }
 
 // Indices of validated indexer rows: one fused score + Top-K launch where the
-// shape and format allow it (scores stay on chip), else scores in row chunks
-// of at most score_cap bytes followed by topk_select.  The workspace at w is
-// laid out by index_layout with the same cap.
-int index_rows(const lisfa_indexer_args* iargs, int32_t K, int32_t* idx, uint8_t* w, int64_t score_cap,
+// shape and format allow it (scores stay on chip; layer != 0: only where that
+// is the faster path), else scores in row chunks of at most score_cap bytes
+// followed by topk_select.  The workspace at w is laid out by index_layout
+// with the same cap.
+int index_rows(const lisfa_indexer_args* iargs, int32_t K, int32_t* idx, uint8_t* w, int64_t score_cap, int layer,
                hipStream_t st) {
     const int32_t R = iargs->R;
     const IndexLayout L = index_layout(R, iargs->max_visible, K, score_cap);
@@ -240,7 +242,8 @@ int index_rows(const lisfa_indexer_args* iargs, int32_t K, int32_t* idx, uint8_t
     const int qg = (iargs->rows_per_group % 16 == 0) ? 16 : (iargs->rows_per_group % 8 == 0) ? 8 : 1;
     IndexerDev d = to_dev(iargs);
     if (iargs->max_visible > 0) {
-        const hipError_t he = li_topk_dispatch(d, iargs->D_I, iargs->k_cache.dtype, qg, ld, K, idx, w, L.cand, st);
+        const hipError_t he =
+            li_topk_dispatch(d, iargs->D_I, iargs->k_cache.dtype, qg, ld, K, idx, w, L.cand, layer, st);
         if (he == hipSuccess) return LISFA_OK;
         if (he != hipErrorNotSupported) return LISFA_ERR_HIP;
     }
@@ -288,7 +291,7 @@ int fused_run(const lisfa_indexer_args* iargs, const lisfa_mla_args* margs, int3
               float* lse, uint8_t* w, int64_t score_cap, hipStream_t st) {
     const FusedLayout L = fused_layout(iargs->R, iargs->max_visible, K, margs->H, margs->D_latent, score_cap);
     int32_t* idx = idx_out ? idx_out : (int32_t*)(w + L.idx);
-    const int e = index_rows(iargs, K, idx, w, score_cap, st);
+    const int e = index_rows(iargs, K, idx, w, score_cap, 1, st);
     if (e) return e;
     const MlaDev md = to_dev(margs, idx, K);
     return hip_status(sfa_dispatch(md, margs->D_latent, kv_mode(margs->kv_cache), (__bf16*)out,
@@ -422,7 +425,17 @@ int li_topk(const lisfa_indexer_args* args, int32_t K, int32_t* idx, void* ws, s
     const IndexLayout L = index_layout(args->R, args->max_visible, K);
     if (L.total > 0 && (!ws || ws_bytes < L.total)) return LISFA_ERR_WORKSPACE;
     if (L.total > 0 && !aligned(ws, 256)) return LISFA_ERR_BAD_SHAPE;
-    return index_rows(args, K, idx, (uint8_t*)ws, kScoreScratchCap, (hipStream_t)stream);
+    return index_rows(args, K, idx, (uint8_t*)ws, kScoreScratchCap, 0, (hipStream_t)stream);
+}
+
+int32_t li_topk_plan(const lisfa_indexer_args* args, int32_t K, int32_t layer) {
+    const int e = check_indexer(args);
+    if (e) return e;
+    if (K < 1) return LISFA_ERR_BAD_SHAPE;
+    if (args->R == 0 || args->max_visible == 0) return 0;
+    const int qg = (args->rows_per_group % 16 == 0) ? 16 : (args->rows_per_group % 8 == 0) ? 8 : 1;
+    return li_topk_fused_chunks(to_dev(args), args->D_I, args->k_cache.dtype, qg, scores_ld(args->max_visible), K,
+                                layer != 0);
 }
 
 int topk_select(const float* scores, int64_t ld_scores, const int32_t* row_pos, int32_t R, int32_t K,

@@ -127,6 +127,42 @@ __device__ __forceinline__ uint32_t float_key(float f) {
     return (b ^ (s | 0x80000000u)) - s;
 }
 
+// Wave-wide inclusive scans through DPP (row shifts by 1, 2, 4, 8 within
+// each row of 16 lanes, then row 0/2's last lane to rows 1/3 and lane 31 to
+// rows 2 and 3); lanes without a source keep the identity.  Lane 63 ends
+// with the wave's total.
+template <int CTRL, int ROWM>
+__device__ __forceinline__ uint32_t dpp(uint32_t old, uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)x, CTRL, ROWM, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t x) {
+    x += dpp<0x111, 0xF>(0u, x);
+    x += dpp<0x112, 0xF>(0u, x);
+    x += dpp<0x114, 0xF>(0u, x);
+    x += dpp<0x118, 0xF>(0u, x);
+    x += dpp<0x142, 0xA>(0u, x);
+    x += dpp<0x143, 0xC>(0u, x);
+    return x;
+}
+__device__ __forceinline__ uint32_t wave_incl_min(uint32_t x) {
+    x = min(x, dpp<0x111, 0xF>(~0u, x));
+    x = min(x, dpp<0x112, 0xF>(~0u, x));
+    x = min(x, dpp<0x114, 0xF>(~0u, x));
+    x = min(x, dpp<0x118, 0xF>(~0u, x));
+    x = min(x, dpp<0x142, 0xA>(~0u, x));
+    x = min(x, dpp<0x143, 0xC>(~0u, x));
+    return x;
+}
+__device__ __forceinline__ uint32_t wave_incl_max(uint32_t x) {
+    x = max(x, dpp<0x111, 0xF>(0u, x));
+    x = max(x, dpp<0x112, 0xF>(0u, x));
+    x = max(x, dpp<0x114, 0xF>(0u, x));
+    x = max(x, dpp<0x118, 0xF>(0u, x));
+    x = max(x, dpp<0x142, 0xA>(0u, x));
+    x = max(x, dpp<0x143, 0xC>(0u, x));
+    return x;
+}
+
 __device__ __forceinline__ uint32_t lanemask_count(uint64_t mask) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
                                      __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));

@@ -63,48 +63,12 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, 
     return before + x - v;
 }
 
-// Wave-wide inclusive scans through DPP (row shifts by 1, 2, 4, 8 within
-// each row of 16 lanes, then row 0/2's last lane to rows 1/3 and lane 31 to
-// rows 2 and 3); lanes without a source keep the identity.  Lane 63 ends
-// with the wave's total.
-template <int CTRL, int ROWM>
-__device__ __forceinline__ uint32_t tk_dpp(uint32_t old, uint32_t x) {
-    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)x, CTRL, ROWM, 0xF, false);
-}
-__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t x) {
-    x += tk_dpp<0x111, 0xF>(0u, x);
-    x += tk_dpp<0x112, 0xF>(0u, x);
-    x += tk_dpp<0x114, 0xF>(0u, x);
-    x += tk_dpp<0x118, 0xF>(0u, x);
-    x += tk_dpp<0x142, 0xA>(0u, x);
-    x += tk_dpp<0x143, 0xC>(0u, x);
-    return x;
-}
-__device__ __forceinline__ uint32_t wave_incl_min(uint32_t x) {
-    x = min(x, tk_dpp<0x111, 0xF>(~0u, x));
-    x = min(x, tk_dpp<0x112, 0xF>(~0u, x));
-    x = min(x, tk_dpp<0x114, 0xF>(~0u, x));
-    x = min(x, tk_dpp<0x118, 0xF>(~0u, x));
-    x = min(x, tk_dpp<0x142, 0xA>(~0u, x));
-    x = min(x, tk_dpp<0x143, 0xC>(~0u, x));
-    return x;
-}
-__device__ __forceinline__ uint32_t wave_incl_max(uint32_t x) {
-    x = max(x, tk_dpp<0x111, 0xF>(0u, x));
-    x = max(x, tk_dpp<0x112, 0xF>(0u, x));
-    x = max(x, tk_dpp<0x114, 0xF>(0u, x));
-    x = max(x, tk_dpp<0x118, 0xF>(0u, x));
-    x = max(x, tk_dpp<0x142, 0xA>(0u, x));
-    x = max(x, tk_dpp<0x143, 0xC>(0u, x));
-    return x;
-}
-
 // Inclusive scan / minimum / maximum within each row of 16 lanes (DPP row shifts).
 __device__ __forceinline__ uint32_t row16_incl_sum(uint32_t x) {
-    x += tk_dpp<0x111, 0xF>(0u, x);
-    x += tk_dpp<0x112, 0xF>(0u, x);
-    x += tk_dpp<0x114, 0xF>(0u, x);
-    x += tk_dpp<0x118, 0xF>(0u, x);
+    x += dpp<0x111, 0xF>(0u, x);
+    x += dpp<0x112, 0xF>(0u, x);
+    x += dpp<0x114, 0xF>(0u, x);
+    x += dpp<0x118, 0xF>(0u, x);
     return x;
 }
 
@@ -742,14 +706,14 @@ __device__ __forceinline__ void tk_block_topk(TkRowShared& sh, const uint32_t (&
     } else {
         // the 16 wave results across a row of lanes, reduced by DPP; lane 15 has the block's
         uint32_t vmin = sh.red[lane & 15], vmax = sh.red[kTkWaves + (lane & 15)];
-        vmin = min(vmin, tk_dpp<0x111, 0xF>(~0u, vmin));
-        vmax = max(vmax, tk_dpp<0x111, 0xF>(0u, vmax));
-        vmin = min(vmin, tk_dpp<0x112, 0xF>(~0u, vmin));
-        vmax = max(vmax, tk_dpp<0x112, 0xF>(0u, vmax));
-        vmin = min(vmin, tk_dpp<0x114, 0xF>(~0u, vmin));
-        vmax = max(vmax, tk_dpp<0x114, 0xF>(0u, vmax));
-        vmin = min(vmin, tk_dpp<0x118, 0xF>(~0u, vmin));
-        vmax = max(vmax, tk_dpp<0x118, 0xF>(0u, vmax));
+        vmin = min(vmin, dpp<0x111, 0xF>(~0u, vmin));
+        vmax = max(vmax, dpp<0x111, 0xF>(0u, vmax));
+        vmin = min(vmin, dpp<0x112, 0xF>(~0u, vmin));
+        vmax = max(vmax, dpp<0x112, 0xF>(0u, vmax));
+        vmin = min(vmin, dpp<0x114, 0xF>(~0u, vmin));
+        vmax = max(vmax, dpp<0x114, 0xF>(0u, vmax));
+        vmin = min(vmin, dpp<0x118, 0xF>(~0u, vmin));
+        vmax = max(vmax, dpp<0x118, 0xF>(0u, vmax));
         kmin = (uint32_t)__builtin_amdgcn_readlane((int)vmin, 15);
         kmax = (uint32_t)__builtin_amdgcn_readlane((int)vmax, 15);
     }

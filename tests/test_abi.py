@@ -200,15 +200,40 @@ def test_li_topk_validation(clib):
 
 
 def test_li_topk_workspace_covers_both_paths(clib):
-    # few rows: the fused exchange area (up to 256 workgroups of 3 x 16 KB)
+    # few rows: the fused exchange area (up to 256 workgroups, 3 levels of
+    # 16-bit suffix sums: 64 coarse + 4096 fine each)
     few = clib.lisfa_workspace_size(C.LISFA_OP_LI_TOPK, 64, 32768, 2048, 0, 0)
-    assert few >= 3 * 256 * 16384
+    assert few >= 3 * 256 * (64 + 4096) * 2
     assert few >= 64 * 32768 * 4          # the score scratch of the separate kernels
     # many rows: one workgroup per row, no exchange; bounded score chunks
     many = clib.lisfa_workspace_size(C.LISFA_OP_LI_TOPK, 4096, 65536, 2048, 0, 0)
     assert (256 << 20) <= many < (300 << 20)
     fused = clib.lisfa_workspace_size(C.LISFA_OP_FUSED, 64, 32768, 2048, 128, 512)
     assert fused >= few + 64 * 2048 * 4
+
+
+def test_li_topk_plan(clib):
+    """Which index step runs (host rule, no GPU): li_topk fuses wherever the
+    shape allows; the layer only where fusing measured faster (bf16 keys, at
+    most 4 workgroups per row)."""
+    def plan(layer, **kw):
+        a = _idx_args(**kw)
+        return clib.li_topk_plan(ctypes.byref(a), 2048, layer)
+    paged = dict(k_cache=_fake_cache(block_table=16, block_size=64, bt_stride=512))
+    assert plan(0, R=64, max_visible=32768, **paged) == 4      # 4 x 8192 positions
+    assert plan(1, R=64, max_visible=32768, **paged) == 4
+    assert plan(0, R=1, max_visible=32768, **paged) == 32      # 32 x 1024
+    assert plan(1, R=1, max_visible=32768, **paged) == 0
+    assert plan(0, R=2, max_visible=131072, **paged) == 64     # 64 x 2048
+    assert plan(0, R=300, max_visible=3000, **paged) == 1      # one workgroup per row
+    assert plan(0, R=200, max_visible=4000, **paged) == 0      # 2 x 200 > 256 workgroups
+    assert plan(0, R=64, max_visible=32768, rows_per_group=16, **paged) == 0   # grouped prefill rows
+    mx = dict(k_cache=_fake_cache(dtype=C.LISFA_MXFP8, row_stride_bytes=128, scale=16), q_scale=16)
+    assert plan(0, R=64, max_visible=32768, **mx) == 4
+    assert plan(1, R=64, max_visible=32768, **mx) == 0
+    assert plan(0, R=64, max_visible=0) == 0
+    assert clib.li_topk_plan(ctypes.byref(_idx_args(H_I=65)), 2048, 0) == C.LISFA_ERR_UNSUPPORTED
+    assert clib.li_topk_plan(ctypes.byref(_idx_args()), 0, 0) == C.LISFA_ERR_BAD_SHAPE
 
 
 def test_noalloc_validation(clib):

@@ -159,3 +159,31 @@ def test_li_topk_crafted_scores(lib, kind, B, L, K):
             check_index_set(got[r], sc, want, K)
         else:                  # exact in fp32: the same set, ties included
             assert np.array_equal(got[r], want), f"row {r}"
+
+
+@pytest.mark.parametrize("K", [1, 7, 300, 32000, 32767])
+def test_li_topk_boundary_outside_the_first_range(lib, K):
+    """The first histogram of a row split over workgroups bins a sample of the
+    scores; with K this small or this large the K-th place lies above or below
+    the sample's range, in a clamped edge bin, and the levels that follow
+    refine it from there."""
+    say(f"[case] li_topk 2 x 32768, K={K}")
+    b = batch_on_gpu(decode_wl(2, 32768, K, 64, 128, seed=5))
+    got, ref = both(b, K)
+    assert np.array_equal(got, ref)
+    inp = W.to_numpy(b)
+    sc = O.scores_row(inp, 1)
+    check_index_set(got[1], sc, O.select_topk(sc, K), K)
+
+
+@pytest.mark.parametrize("K", [8, 130, 2048])
+def test_li_topk_outliers_outside_the_sample(lib, K):
+    """Huge and tiny outlier scores that a sample of each workgroup's first
+    keys may miss (the first level's edge bins then hold them)."""
+    say(f"[case] li_topk crafted wide, 2 x 32768, K={K}")
+    b = crafted(2, 32768, K, "wide", seed=3)
+    got, ref = both(b, K)
+    assert np.array_equal(got, ref)
+    inp = W.to_numpy(b)
+    for r in range(2):
+        assert np.array_equal(got[r], O.select_topk(O.scores_row(inp, r), K)), f"row {r}"
