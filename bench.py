@@ -105,6 +105,7 @@ def stored_traffic(stage: str, workload: str):
 STAGE_KERNELS = {
     "li_score": ["li_score"],
     "topk_select": ["topk"],
+    "li_topk": ["li_topk_kernel", "lt_clear_kernel"],
     "sparse_mla_attn": ["sfa_mla_kernel", "sfa_kernel<", "sfa_combine_kernel"],
 }
 
