@@ -62,3 +62,16 @@ def test_noalloc_cuts_rows_to_fit_the_scratch(lib):
     ld = (b.max_visible + 63) // 64 * 64
     assert b.R * ld * 4 > lisfa._c.LISFA_NOALLOC_SCRATCH_BYTES, "the scores alone must exceed the scratch"
     _same(b, [0, 1023, 2047], "prefill 2048 rows")
+
+
+def test_noalloc_fused_index_step(lib):
+    """Rows whose index step is the fused scoring + Top-K launch: its exchange
+    area and control words live in the static scratch too, and are cleared
+    anew on every call (two calls in a row, the second smaller)."""
+    say("[case] no-alloc: 64 rows x 8192 (fused index step), then 64 rows x 4096")
+    b1 = batch_on_gpu(W.BENCH["decode_paged_64x32768"].with_(seq_len=8192, name="noalloc_fused", seed=71))
+    kc, _ = caches(b1)
+    assert lisfa.li_topk_plan(b1.q_idx, b1.w, kc, b1.row_seq, b1.row_pos, b1.wl.K, b1.max_visible, layer=True) == 4
+    _same(b1, [0, 63], "fused 64 x 8192")
+    b2 = batch_on_gpu(W.BENCH["decode_paged_64x32768"].with_(seq_len=4096, name="noalloc_fused2", seed=72))
+    _same(b2, [5], "fused 64 x 4096")
