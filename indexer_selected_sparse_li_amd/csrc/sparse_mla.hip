@@ -624,7 +624,9 @@ __device__ __forceinline__ int sfa_swz8(int r) { return (((r >> 1) & 3) << 1) | 
 //
 // Outputs: nsplit == 1: bf16 out (+ lse) or, with out == nullptr, normalised
 // fp32 out_f32 + lse; nsplit > 1: normalised bf16 partials part_o [R, nsplit,
-// H, 512] + part_lse [R, nsplit, H] for the combine kernel.
+// H, 512] + part_lse [R, nsplit, H] for the combine kernel, the 512 columns of
+// a part in the store order of the p-waves (value column 32 b + 16 h + 4 g + i
+// at 32 b + 8 g + 4 h + i: each lane stores 16 contiguous bytes).
 template <int NBUF, int MAXK, int KVF, bool GNT = false>
 __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsplit, int nhb,
                                                        __bf16* __restrict__ out, float* __restrict__ lse,
@@ -1289,13 +1291,28 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
                 }
             }
             const int64_t col0 = pc * DVP + 4 * g;
-            if (nsplit == 1 && out_f32 != nullptr) {
+            if (nsplit > 1) {
+                // split-K part in store order: of the head's 128 columns of this
+                // p-wave, M-tiles 2s and 2s + 1 of lane group g go to the 16 bytes
+                // at 32 s + 8 g (each store writes 64 contiguous bytes per head);
+                // the combine kernel reads this order back
+                __bf16* prow = part_o + (((int64_t)r * nsplit + sp) * a.H + head) * DLAT + pc * DVP + 8 * g;
+#pragma unroll
+                for (int s2 = 0; s2 < MTP / 2; ++s2) {
+                    bf16x8 v;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        v[i] = (__bf16)(o[ht][2 * s2][i] * inv);
+                        v[4 + i] = (__bf16)(o[ht][2 * s2 + 1][i] * inv);
+                    }
+                    *(bf16x8*)(prow + 32 * s2) = v;
+                }
+            } else if (out_f32 != nullptr) {
                 float* orow = out_f32 + ((int64_t)r * a.H + head) * DLAT + col0;
 #pragma unroll
                 for (int mt = 0; mt < MTP; ++mt) *(f32x4v*)(orow + 16 * mt) = o[ht][mt] * inv;
             } else {
-                __bf16* orow = nsplit == 1 ? out + ((int64_t)r * a.H + head) * DLAT + col0
-                                           : part_o + (((int64_t)r * nsplit + sp) * a.H + head) * DLAT + col0;
+                __bf16* orow = out + ((int64_t)r * a.H + head) * DLAT + col0;
 #pragma unroll
                 for (int mt = 0; mt < MTP; ++mt) {
                     bf16x4 v;
@@ -1315,8 +1332,10 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
 // gathered shards of a context split [G, R, H] use (1, R).  Partials are bf16
 // (the 512 + 64 attention's split-K parts) or fp32; 8 consecutive value
 // columns per thread, DLAT / 8 threads per (row, head), 256 threads per
-// block; bf16 or fp32 output.
-template <int DLAT, typename PT, bool F32OUT>
+// block; bf16 or fp32 output.  SORD: the parts hold their columns in the
+// 512 + 64 kernel's store order (of each 32 columns, 4-column groups 0 and 4,
+// 1 and 5, 2 and 6, 3 and 7 side by side); the output is in value order.
+template <int DLAT, typename PT, bool F32OUT, bool SORD = false>
 __global__ __launch_bounds__(256) void sfa_combine_kernel(const PT* __restrict__ part_o,
                                                           const float* __restrict__ part_lse, int nsplit,
                                                           int64_t row_str, int64_t split_str, int H, int RH,
@@ -1361,21 +1380,62 @@ __global__ __launch_bounds__(256) void sfa_combine_kernel(const PT* __restrict__
             for (int j = 0; j < 8; ++j) acc[j] = fmaf(w1, x1[j], fmaf(w0, x0[j], 0.f));
         }
     } else {
-        for (int i = 0; i < nsplit; ++i) M = fmaxf(M, part_lse[((int64_t)r * row_str + i * split_str) * H + h]);
+        // the parts' lse values 16 at a time, all in flight together (a loop of
+        // single loads waits one round trip per part)
+        for (int i0 = 0; i0 < nsplit; i0 += 16) {
+            float l[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int i = i0 + j < nsplit ? i0 + j : nsplit - 1;
+                l[j] = part_lse[((int64_t)r * row_str + i * split_str) * H + h];
+            }
+#pragma unroll
+            for (int j = 0; j < 16; ++j) M = fmaxf(M, l[j]);
+        }
     }
     if (nsplit != 2 && M != -__builtin_inff()) {
-        for (int i = 0; i < nsplit; ++i) {
-            const int64_t e = ((int64_t)r * row_str + i * split_str) * H + h;
-            const float wi = __expf(part_lse[e] - M);
-            W += wi;
-            float x[8];
-            load8(e, x);
+        // CH parts' loads issued together, then their terms added in part order
+        constexpr int CH = std::is_same<PT, float>::value ? 8 : 16;
+        for (int i0 = 0; i0 < nsplit; i0 += CH) {
+            float l[CH], x[CH][8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) acc[j] = fmaf(wi, x[j], acc[j]);
+            for (int j = 0; j < CH; ++j) {
+                const int i = i0 + j < nsplit ? i0 + j : nsplit - 1;
+                const int64_t e = ((int64_t)r * row_str + i * split_str) * H + h;
+                l[j] = part_lse[e];
+                load8(e, x[j]);
+            }
+#pragma unroll
+            for (int j = 0; j < CH; ++j) {
+                if (i0 + j < nsplit) {
+                    const float wi = __expf(l[j] - M);
+                    W += wi;
+#pragma unroll
+                    for (int c8 = 0; c8 < 8; ++c8) acc[c8] = fmaf(wi, x[j][c8], acc[c8]);
+                }
+            }
         }
     }
     const float inv = W > 0.f ? 1.f / W : 0.f;
-    if constexpr (F32OUT) {
+    if constexpr (SORD) {
+        // part column c + j holds value column c0 + j (j < 4) and c0 + 12 + j (j >= 4)
+        const int c0 = (c & ~31) + ((c >> 1) & 12);
+        if constexpr (F32OUT) {
+            float* o = (float*)out + (int64_t)rh * DLAT + c0;
+            *(f32x4*)o = f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+            *(f32x4*)(o + 16) = f32x4{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
+        } else {
+            bf16x4 v0, v1;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v0[j] = (__bf16)(acc[j] * inv);
+                v1[j] = (__bf16)(acc[4 + j] * inv);
+            }
+            __bf16* o = (__bf16*)out + (int64_t)rh * DLAT + c0;
+            *(bf16x4*)o = v0;
+            *(bf16x4*)(o + 16) = v1;
+        }
+    } else if constexpr (F32OUT) {
         f32x4* o = (f32x4*)((float*)out + (int64_t)rh * DLAT + c);
         o[0] = f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
         o[1] = f32x4{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
@@ -1504,17 +1564,18 @@ static hipError_t launch_sfa64(const MlaDev& a, const SfaPlan& p, __bf16* out, f
     return hipGetLastError();
 }
 
-template <int DLAT, typename PT>
+// SORD: the parts are in the 512 + 64 kernel's store order
+template <int DLAT, typename PT, bool SORD>
 static hipError_t launch_combine(const MlaDev& a, const SfaPlan& p, const PT* part_o, const float* part_lse,
                                  __bf16* out, float* out_f32, float* lse, hipStream_t stream) {
     constexpr int HPB = 256 / (DLAT / 8);
     const int RH = a.R * a.H;
     const dim3 grid((unsigned)((RH + HPB - 1) / HPB));
     if (out != nullptr)
-        hipLaunchKernelGGL((sfa_combine_kernel<DLAT, PT, false>), grid, dim3(256), 0, stream, part_o, part_lse,
+        hipLaunchKernelGGL((sfa_combine_kernel<DLAT, PT, false, SORD>), grid, dim3(256), 0, stream, part_o, part_lse,
                            p.nsplit, (int64_t)p.nsplit, (int64_t)1, a.H, RH, (void*)out, lse);
     else
-        hipLaunchKernelGGL((sfa_combine_kernel<DLAT, PT, true>), grid, dim3(256), 0, stream, part_o, part_lse,
+        hipLaunchKernelGGL((sfa_combine_kernel<DLAT, PT, true, SORD>), grid, dim3(256), 0, stream, part_o, part_lse,
                            p.nsplit, (int64_t)p.nsplit, (int64_t)1, a.H, RH, (void*)out_f32, lse);
     return hipGetLastError();
 }
@@ -1529,7 +1590,7 @@ hipError_t sfa_dispatch(const MlaDev& a, int D_latent, int kv_mode, __bf16* out,
         __bf16* part_o = (__bf16*)ws;
         e = launch_sfa512(a, p, kv_mode, out, out_f32, lse, part_o, part_lse, stream);
         if (e != hipSuccess || p.nsplit == 1) return e;
-        return launch_combine<512, __bf16>(a, p, part_o, part_lse, out, out_f32, lse, stream);
+        return launch_combine<512, __bf16, true>(a, p, part_o, part_lse, out, out_f32, lse, stream);
     }
     if (D_latent != 64) return hipErrorInvalidValue;
     float* part_o = (float*)ws;
@@ -1541,7 +1602,7 @@ hipError_t sfa_dispatch(const MlaDev& a, int D_latent, int kv_mode, __bf16* out,
     else e = g2 ? launch_sfa64<true, 2, true>(a, p, out, out_f32, lse, part_o, part_lse, stream)
                 : launch_sfa64<true, 1, true>(a, p, out, out_f32, lse, part_o, part_lse, stream);
     if (e != hipSuccess || p.nsplit == 1) return e;
-    return launch_combine<64, float>(a, p, part_o, part_lse, out, out_f32, lse, stream);
+    return launch_combine<64, float, false>(a, p, part_o, part_lse, out, out_f32, lse, stream);
 }
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
