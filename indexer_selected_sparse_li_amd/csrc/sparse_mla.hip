@@ -1418,24 +1418,23 @@ __global__ __launch_bounds__(256) void sfa_combine_kernel(const PT* __restrict__
     }
     const float inv = W > 0.f ? 1.f / W : 0.f;
     if constexpr (SORD) {
-        // part column c + j holds value column c0 + j (j < 4) and c0 + 12 + j (j >= 4)
-        const int c0 = (c & ~31) + ((c >> 1) & 12);
-        if constexpr (F32OUT) {
-            float* o = (float*)out + (int64_t)rh * DLAT + c0;
-            *(f32x4*)o = f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
-            *(f32x4*)(o + 16) = f32x4{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
-        } else {
-            bf16x4 v0, v1;
+        // lane q of each quad holds 4-column groups q and q + 4 of a 32-column
+        // block; two quad permutations give it groups 2 q and 2 q + 1, the 8
+        // value columns from c (every lane of a quad works on the same head)
+        const bool lowq = (threadIdx.x & 2) == 0;
+        float y[8];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                v0[j] = (__bf16)(acc[j] * inv);
-                v1[j] = (__bf16)(acc[4 + j] * inv);
-            }
-            __bf16* o = (__bf16*)out + (int64_t)rh * DLAT + c0;
-            *(bf16x4*)o = v0;
-            *(bf16x4*)(o + 16) = v1;
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t a = __float_as_uint(acc[j]), b = __float_as_uint(acc[4 + j]);
+            const uint32_t a0 = dpp<0x88, 0xF>(0u, a), b0 = dpp<0x88, 0xF>(0u, b);   // from quad lanes 0 2 0 2
+            const uint32_t a1 = dpp<0xDD, 0xF>(0u, a), b1 = dpp<0xDD, 0xF>(0u, b);   // from quad lanes 1 3 1 3
+            y[j] = __uint_as_float(lowq ? a0 : b0);
+            y[4 + j] = __uint_as_float(lowq ? a1 : b1);
         }
-    } else if constexpr (F32OUT) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = y[j];
+    }
+    if constexpr (F32OUT) {
         f32x4* o = (f32x4*)((float*)out + (int64_t)rh * DLAT + c);
         o[0] = f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
         o[1] = f32x4{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
