@@ -577,48 +577,42 @@ __device__ __forceinline__ int sfa_swz8(int r) { return (((r >> 1) & 3) << 1) | 
 // index list.  Tiles of 32 gathered rows sit in LDS as 8-row groups of 1 KB
 // blocks (chunk c of tile row r at (r / 8) * 9 KB + (c / 8) KB + (r % 8) * 128
 // + ((c % 8) ^ swz8(r)) * 16), and the eight waves split the work by role; wave
-// w runs on SIMD w % 4, so every SIMD holds one q-wave and one p-wave, and the
-// PV products of the p-wave keep the matrix core busy while its q-wave runs
-// the softmax:
-//  * q-waves 0..3, bf16 rows: q-wave w owns head tile w (16 heads of the block,
-//    the query as one B operand, 72 VGPRs) and all 32 keys of every tile.  For
-//    tile t + 1 it computes S^T[32 keys, 16 heads] (36 MFMAs of 16x16x32),
-//    masks, takes the per-head maxima inside the wave, raises the base-2
-//    reference lazily (only when the tile's maximum exceeds it by 2^8), and
-//    writes P^T into a two-slot LDS ring in the PV B-operand layout (lane =
-//    head, K-slots 8 g .. 8 g + 7 = keys 4 g + i and 16 + 4 g + i) with a raise
-//    flag and factors per head tile.
-//  * q-waves 0..3, fp8 rows: q-wave (h, kb) = (w / 2, w % 2) owns heads
-//    32 h .. 32 h + 31 (two 16-head B operands, 144 VGPRs) and keys
-//    16 kb .. 16 kb + 15, so every key operand read from LDS feeds both head
-//    tiles (half the LDS reads of the bf16 split, which matters here because
-//    the p-waves also write the converted tiles through LDS); the two key
-//    blocks trade their per-head maxima through LDS with a flag handshake
-//    inside the period, raise in the same way, and each writes its half of P^T;
-//    each keeps the partial row sums of its keys.
-//  * p-waves 4..7: p-wave c = w - 4 owns value columns
-//    128 c .. 128 c + 127 of the 64 heads (O^T in 128 VGPRs): it applies the
-//    raise factors of flagged head tiles and runs PV of tile t (32 MFMAs), the
-//    value operand from transposed LDS reads in the P^T operand's key order.
-//    bf16 rows: it reads the V operands of tile t + 1 in period t, into the
-//    registers PV(t) has just taken its operands from, so after the barrier
-//    only the P^T operand stands between it and its MFMAs.
-//    The p-waves also bring the tiles, p-wave c rows 8 c .. 8 c + 7.  bf16
-//    rows: direct global->LDS loads NBUF - 2 tiles ahead, issued from inline
-//    assembly (lds_dma) and ordered by explicit vmcnt waits and the tile
-//    barrier; the first tiles go out before the slot table is complete.  fp8
-//    rows: e4m3 codes two tiles ahead into registers, converted exactly to
-//    bf16 (v_cvt_scalef32_pk_bf16_fp8 with scale 1) into the tile, the rows'
-//    fp32 factors beside it (NBUF = 3).
-// MFMA cycles per tile on every SIMD: 576 (QK^T) + 512 (PV).  One barrier per
-// tile hands P over; the roles run separate loops with the same number of
-// barriers.
+// w runs on SIMD w % 4, so the score work sits on SIMDs 0 and 1 and the value
+// products on SIMDs 2 and 3:
+//  * q-waves 0, 1 (SIMDs 0, 1): q-wave h owns heads 32 h .. 32 h + 31 of the
+//    block (the query as 36 B operands of v_mfma_f32_32x32x16_bf16, 144 VGPRs)
+//    and all 32 keys of every tile.  For tile t + 1 it computes
+//    S^T[32 keys, 32 heads] (36 MFMAs; every 1 KB key operand read from LDS
+//    feeds 32 heads), masks, takes the per-head maxima inside the wave (one
+//    permlane swap), raises the base-2 reference lazily (only when the tile's
+//    maximum exceeds it by 2^8), and writes P^T into a two-slot LDS ring in the
+//    16-head PV B-operand layout (lane = head, K-slots 8 g .. 8 g + 7 = keys
+//    4 g + i and 16 + 4 g + i) with a raise flag and factors per head tile.
+//  * p-waves 2, 3, 6, 7 (two on each of SIMDs 2, 3): p-wave c (0..3) owns value
+//    columns 128 c .. 128 c + 127 of the 64 heads (O^T in 128 VGPRs): it applies
+//    the raise factors of flagged head tiles and runs PV of tile t (32 MFMAs of
+//    16x16x32), the value operand from transposed LDS reads in the P^T
+//    operand's key order, read for tile t + 1 in period t into the registers
+//    PV(t) has just taken its operands from, so after the barrier only the P^T
+//    operand stands between it and its MFMAs.  bf16 rows: the p-waves also bring
+//    the tiles (p-wave c rows 8 c .. 8 c + 7) by direct global->LDS loads
+//    NBUF - 2 tiles ahead, issued from inline assembly (lds_dma) and ordered by
+//    explicit vmcnt waits and the tile barrier; the first tiles go out before
+//    the slot table is complete.
+//  * helper waves 4, 5 (SIMDs 0, 1, beside the q-waves' matrix work): the slot
+//    table; fp8 rows: the tiles, e4m3 codes two tiles ahead into registers,
+//    converted exactly to bf16 (v_cvt_scalef32_pk_bf16_fp8 with scale 1) into
+//    the tile one tile ahead, the rows' fp32 factors beside it (NBUF = 3).
+// MFMA cycles per tile: 1152 on SIMDs 0 and 1 (QK^T), 1024 on SIMDs 2 and 3
+// (PV).  One barrier per tile hands P over; the roles run separate loops with
+// the same number of barriers.
 //
 // fp8 factors are applied exactly, never folded into the bf16 rows:
 //  KVF 1 (one factor f per row):  z = scale * f * (q . code), and the P^T
 //        operand is p * f (the normaliser sums p);
 //  KVF 2 (one factor per 128-column tile j of the row): the QK^T K-steps of
-//        each column tile accumulate apart and are added with the row's f_j;
+//        each column tile accumulate apart (two alternating accumulators) and
+//        are added with the row's f_j two K-steps into the next column tile;
 //        p-wave c, whose value columns are column tile c, multiplies its P^T
 //        operand by f_c.
 //
@@ -638,14 +632,13 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
     constexpr int GB = NJ * 1024;           // bytes per 8-row group
     constexpr int TROWS = 32;
     constexpr int TB = (TROWS / 8) * GB;    // bytes per tile
-    constexpr int NQT = 256;                // threads of the q-waves 0..3 (they build the slot table)
+    constexpr int NQT = 128;                // threads that build the slot table (waves 4, 5)
     constexpr int KS = DQK / 32;            // 16x16x32 K-steps of a row (18)
     constexpr int DVP = DLAT / 4;           // value columns per p-wave
     constexpr int MTP = DVP / 16;           // PV M-tiles per p-wave
     constexpr int NTL = KVF == 2 ? (DQK + 127) / 128 : 1;   // fp8 factors per row
     constexpr int LA = NBUF - 2;            // tiles in flight ahead of QK^T
     static_assert(NBUF >= 3 && (KVF == 0 || NBUF == 3), "PV(t) | QK(t+1) | tiles t+2 ..");
-    static_assert(MAXK % NQT == 0, "whole rounds of index entries");
     typedef float f32x4v __attribute__((ext_vector_type(4)));
     typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
 
@@ -656,9 +649,7 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
     __shared__ __attribute__((aligned(16))) uint8_t pbuf[2][4][64 * 16];   // P^T [slot][head tile][lane]
     __shared__ float alph[2][64];                       // raise factors [slot][head]
     __shared__ int rflag[2][4];                         // raised head tiles [slot][head tile]
-    __shared__ float xmax[2][2][32];                    // fp8 rows: per-head tile maxima [head half][key block][head]
-    __shared__ int xflag[2][2];                         // fp8 rows: tiles whose maxima are in xmax
-    __shared__ int s_ntiles;
+    __shared__ int s_ntw[2];                            // tiles up to the last valid row, per table-building wave
     // after the last tile the P ring is free: partial row sums [key block][head]
     // (one block for bf16 rows) and the references [head]
     float* const fin_l = (float*)&pbuf[0][0][0];
@@ -679,14 +670,17 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
     const int nk = k1 - k0;
     const int seq = a.row_seq[r];
     const int nt_fill = (nk + TROWS - 1) / TROWS;
-    const bool is_q = wave < 4;
-    if (tid == 0) s_ntiles = 1;
-    if (tid < 4) xflag[tid >> 1][tid & 1] = 0;
+    // roles.  bf16 rows: q-waves 0, 1 (32 heads each, SIMDs 0 and 1), p-waves
+    // 2, 3, 6, 7 (SIMDs 2 and 3), waves 4 and 5 help with the slot table only.
+    // fp8 rows: q-waves 0..3, p-waves 4..7.
+    const bool is_q = wave < 2;
+    const bool is_p = (wave & 3) >= 2;
 
     const lds_u8* tile0 = (const lds_u8*)tile;
     const uint32_t tile_lds = (uint32_t)(uintptr_t)tile;
     const int g = lane >> 4, l16 = lane & 15;
-    const int pc = wave - 4;                            // p-waves 4..7 -> value column block
+    // value column block of a p-wave
+    const int pc = (wave & 3) - 2 + 2 * (wave >> 2);
     // bf16 tile loads of a p-wave: lane l brings chunk 8 j + ((l % 8) ^ swz8(row))
     // of row 8 pc + l / 8 into block j of the row group, at block + 16 l
     const uint32_t goff = (uint32_t)(((lane & 7) ^ sfa_swz8(8 * pc + (lane >> 3))) << 4);
@@ -705,388 +699,316 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
     // the last tile with a valid row (trailing tiles without one are skipped; at
     // least one tile is always processed): the q-waves, which build the slot
     // table, count between the two prologue barriers
-    auto count_tiles = [&]() {
-        for (int t = tid; t < nt_fill; t += NQT)
-            if (vmask[t] != 0u) atomicMax(&s_ntiles, t + 1);
+    // The slot table: every index load of the thread first, then every
+    // block-table lookup (two dependent global round trips).  NT threads
+    // qt = 0 .. NT - 1 in whole waves; builder wave bw also publishes the number
+    // of tiles up to its last valid row in s_ntw[bw] (trailing tiles without a
+    // valid row are skipped; at least one tile is always processed).
+    auto build_slots = [&](auto nt_c, int qt, int bw) {
+        constexpr int NT = decltype(nt_c)::value;
+        constexpr int EPT = MAXK / NT;
+        static_assert(MAXK % NT == 0, "whole rounds of index entries");
+        int pidx[EPT];
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) {
+            const int i = j * NT + qt;
+            pidx[j] = i < nk ? a.idx[(int64_t)r * a.K + k0 + i] : -1;
+        }
+        int64_t sv[EPT];
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) sv[j] = pidx[j] >= 0 ? slot_of(a.kv, seq, pidx[j]) : -1;
+        int nt_mine = 0;
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) {
+            const int i = j * NT + qt;
+            if (i < nt_fill * TROWS) rslot[i] = sv[j] >= 0 ? (uint32_t)sv[j] : 0xFFFFFFFFu;
+            if (sv[j] >= 0) nt_mine = i / TROWS + 1;
+            const uint64_t bal = __ballot(sv[j] >= 0);
+            if ((qt & 63) == 0 && i < nt_fill * TROWS) {
+                vmask[i / 32] = (uint32_t)bal;
+                if (i + 32 < nt_fill * TROWS) vmask[i / 32 + 1] = (uint32_t)(bal >> 32);
+            }
+        }
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) nt_mine = max(nt_mine, __shfl_xor(nt_mine, d));
+        if ((qt & 63) == 0) s_ntw[bw] = nt_mine;
     };
+    // after the slot-table barrier
+    auto read_ntiles = [&]() { return max(1, max(s_ntw[0], s_ntw[1])); };
 
     if (is_q) {
         // ---------------------------------------------------------------- q-wave
-        if constexpr (KVF == 0) {
-            // bf16 rows: q-wave w owns head tile w (16 heads) and all 32 keys of every
-            // tile, so the per-head maxima need no exchange between waves.  The
-            // query in B-operand layout: lane = head, 8 consecutive columns of K-step ks
-            bf16x8 qb[KS];
+        {
+            // q-wave qh owns heads 32 qh .. 32 qh + 31 of the block and all
+            // 32 keys of every tile: S^T[32 keys, 32 heads] from 36 K-steps of
+            // v_mfma_f32_32x32x16_bf16, every key operand read from LDS feeding 32
+            // heads; the per-head maxima need no exchange between waves.  The query
+            // as B operand: lane = head l % 32, columns 16 ks + 8 (l / 32) .. + 8.
+            constexpr int KS2 = DQK / 16;                  // 36
+            const int qh = wave, hq = lane & 31, kh = lane >> 5;
+            bf16x8 qb[KS2];
             {
-                const int head = hb * 64 + wave * 16 + l16;
+                const int head = hb * 64 + qh * 32 + hq;
 #pragma unroll
-                for (int j = 0; j < KS; ++j) {
+                for (int j = 0; j < KS2; ++j) {
                     if (head < a.H)
-                        qb[j] = *(const bf16x8*)(a.q + (((int64_t)r * a.H + head) * DQK + j * 32 + g * 8) * 2);
+                        qb[j] = *(const bf16x8*)(a.q + (((int64_t)r * a.H + head) * DQK + j * 16 + kh * 8) * 2);
                     else
                         qb[j] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
                 }
             }
-            // then the slot table: every index load of the thread first,
-            // then every block-table lookup (two dependent global round trips)
-            constexpr int EPT = MAXK / NQT;
-            const int qt = tid;                             // 0 .. 255
-            int pidx[EPT];
-#pragma unroll
-            for (int j = 0; j < EPT; ++j) {
-                const int i = j * NQT + qt;
-                pidx[j] = i < nk ? a.idx[(int64_t)r * a.K + k0 + i] : -1;
-            }
-            int64_t sv[EPT];
-#pragma unroll
-            for (int j = 0; j < EPT; ++j) sv[j] = pidx[j] >= 0 ? slot_of(a.kv, seq, pidx[j]) : -1;
-#pragma unroll
-            for (int j = 0; j < EPT; ++j) {
-                const int i = j * NQT + qt;
-                if (i < nt_fill * TROWS) rslot[i] = sv[j] >= 0 ? (uint32_t)sv[j] : 0xFFFFFFFFu;
-                const uint64_t bal = __ballot(sv[j] >= 0);
-                if (lane == 0 && i < nt_fill * TROWS) {
-                    vmask[i / 32] = (uint32_t)bal;
-                    if (i + 32 < nt_fill * TROWS) vmask[i / 32 + 1] = (uint32_t)(bal >> 32);
-                }
-            }
             __syncthreads();                                   // the slot table is complete
-            count_tiles();
-            __syncthreads();
-            const int ntiles = s_ntiles;
-            // key operand of K-step ks for key block kb: row 16 kb + l16, chunk 4 ks + g
-            // (swz8 of the row does not depend on kb)
-            uint32_t qa[2];
+            const int ntiles = read_ntiles();
+            // key operand of K-step ks: row hq, chunk 2 ks + kh = block ks / 4,
+            // chunk 2 (ks % 4) + kh inside it
+            uint32_t qa[4];
 #pragma unroll
-            for (int par = 0; par < 2; ++par)
-                qa[par] = (uint32_t)((l16 >> 3) * GB + (l16 & 7) * 128 + (((4 * par + g) ^ sfa_swz8(l16)) << 4));
-            auto qk_op = [&](const lds_u8* T, int kb, int ks) -> bf16x8 {   // compile-time kb, ks
-                return *(const lds_bf16x8*)(T + kb * 2 * GB + qa[ks & 1] + (ks >> 1) * 1024);
+            for (int m = 0; m < 4; ++m)
+                qa[m] = (uint32_t)((hq >> 3) * GB + (hq & 7) * 128 + (((2 * m + kh) ^ sfa_swz8(hq)) << 4));
+            auto qk_op = [&](const lds_u8* T, int ks) -> bf16x8 {   // compile-time ks
+                return *(const lds_bf16x8*)(T + qa[ks & 3] + (ks >> 2) * 1024);
             };
             float m2 = -__builtin_inff(), lsum = 0.f;
             const float c = a.scale_log2;
-
-            // S^T of the tile's 32 keys (two 16-key blocks) for this wave's 16 heads,
-            // the per-head maxima over all 32 keys inside the wave, softmax statistics,
-            // P^T to LDS slot ps
-            auto q_tile = [&](const lds_u8* T, uint32_t vm, int ps) {
-                f32x4v s[2] = {f32x4v{0.f, 0.f, 0.f, 0.f}, f32x4v{0.f, 0.f, 0.f, 0.f}};   // [key block]
-                // operand reads in batches of KPB K-steps (both key blocks), software-
-                // pipelined: the reads of batch b + 1 go out before the MFMAs of batch b
-                constexpr int KPB = 3;
-                constexpr int NB = KS / KPB;
-                static_assert(KS % KPB == 0, "whole batches");
-                bf16x8 av[2][2][KPB];   // [batch parity][key block][K-step]
+            // accumulator register i of lane l: key 8 (i / 4) + 4 (l / 32) + i % 4
+            // of head l % 32.  The P^T ring keeps the 16-head operand layout of the
+            // p-waves (lane (g, head), K-slots 0..3 = keys 4 g + i, 4..7 = keys
+            // 16 + 4 g + i): registers 0..3 and 8..11 of this lane are K-slots of
+            // group g = kh, registers 4..7 and 12..15 of group g = 2 + kh.
+            const int pt = 2 * qh + (hq >> 4), phl = hq & 15;
+            // the fp32 factors of this lane's 16 keys from row table tb of buffer buf
+            // (keys 8 k + 4 kh .. + 3 are contiguous)
+            auto key_factors = [&](int buf, int tb, float (&f)[16]) {
+                const float* kf = kvf + (buf * NTL + tb) * TROWS + 4 * kh;
 #pragma unroll
-                for (int j = 0; j < KPB; ++j) {
-                    av[0][0][j] = qk_op(T, 0, j);
-                    av[0][1][j] = qk_op(T, 1, j);
+                for (int k = 0; k < 4; ++k) {
+                    const f32x4v v = *(const f32x4v*)(kf + 8 * k);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) f[4 * k + i] = v[i];
                 }
+            };
+            auto q_tile = [&](const lds_u8* T, int buf, uint32_t vm, int ps) {
+                // operand reads in batches of KPB K-steps, software-pipelined: the reads
+                // of batch b + 1 go out before the MFMAs of batch b (the scheduling
+                // barriers keep the compiler from pairing each read with its MFMA)
+                constexpr int KPB = KVF == 2 ? 2 : 6;
+                constexpr int NB = KS2 / KPB;
+                static_assert(KS2 % KPB == 0, "whole batches");
+                f32x16 s;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) s[i] = 0.f;
+                // KVF 2: column tile j (K-steps 8 j .. 8 j + 7; the rope tile 4: 32 .. 35)
+                // accumulates into sc[j & 1] and is added, times the keys' f_j, two
+                // K-steps into the next column tile
+                f32x16 sc[KVF == 2 ? 2 : 1];
+                if constexpr (KVF == 2) {
+#pragma unroll
+                    for (int u = 0; u < 2; ++u)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) sc[u][i] = 0.f;
+                }
+                auto fold = [&](int j) {   // compile-time j: s += f_j(key) * sc[j & 1]
+                    const float* kf = kvf + (buf * NTL + j) * TROWS + 4 * kh;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const f32x4v f = *(const f32x4v*)(kf + 8 * k);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            s[4 * k + i] = __builtin_fmaf(f[i], sc[j & 1][4 * k + i], s[4 * k + i]);
+                            sc[j & 1][4 * k + i] = 0.f;
+                        }
+                    }
+                };
+                bf16x8 av[2][KPB];
+#pragma unroll
+                for (int j = 0; j < KPB; ++j) av[0][j] = qk_op(T, j);
                 static_for<NB>([&](auto bc) {
                     constexpr int b = decltype(bc)::value;
                     if constexpr (b + 1 < NB) {
 #pragma unroll
-                        for (int j = 0; j < KPB; ++j) {
-                            av[(b + 1) & 1][0][j] = qk_op(T, 0, (b + 1) * KPB + j);
-                            av[(b + 1) & 1][1][j] = qk_op(T, 1, (b + 1) * KPB + j);
-                        }
+                        for (int j = 0; j < KPB; ++j) av[(b + 1) & 1][j] = qk_op(T, (b + 1) * KPB + j);
                     }
                     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                    for (int j = 0; j < KPB; ++j) {
-                        const int ks = b * KPB + j;
-                        s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[b & 1][0][j], qb[ks], s[0], 0, 0, 0);
-                        s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[b & 1][1][j], qb[ks], s[1], 0, 0, 0);
-                    }
+                    static_for<KPB>([&](auto jc) {
+                        constexpr int j = decltype(jc)::value;
+                        constexpr int ks = b * KPB + j;
+                        if constexpr (KVF == 2) {
+                            sc[(ks / 8) & 1] = mfma32x32x16_bf16(av[b & 1][j], qb[ks], sc[(ks / 8) & 1]);
+                            if constexpr (ks >= 9 && ks % 8 == 1) fold(ks / 8 - 1);
+                        } else {
+                            s = mfma32x32x16_bf16(av[b & 1][j], qb[ks], s);
+                        }
+                    });
                     __builtin_amdgcn_sched_barrier(0);
                 });
+                if constexpr (KVF == 2) fold(NTL - 1);
+                float fk[16];   // KVF 1: the factor of each of this lane's keys
+                if constexpr (KVF == 1) {
+                    key_factors(buf, 0, fk);
+                    // one factor per row: the logit is scale * f * (q . code)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) s[i] *= fk[i];
+                }
                 if (vm != 0xFFFFFFFFu) {
 #pragma unroll
-                    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            if (!((vm >> (16 * kb + 4 * g + i)) & 1u)) s[kb][i] = -__builtin_inff();
+                    for (int i = 0; i < 16; ++i)
+                        if (!((vm >> (8 * (i >> 2) + 4 * kh + (i & 3))) & 1u)) s[i] = -__builtin_inff();
                 }
-                // per-head maximum over the 32 keys: this lane's 8, then across the 4 key groups
-                float tm = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                                 fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+                // per-head maximum over the 32 keys: this lane's 16, then the other half
+                float tm = s[0];
+#pragma unroll
+                for (int i = 1; i < 16; ++i) tm = fmaxf(tm, s[i]);
                 {
-                    const auto w16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(tm), __float_as_uint(tm), false, false);
-                    tm = fmaxf(__uint_as_float(w16[0]), __uint_as_float(w16[1]));
                     const auto w32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(tm), __float_as_uint(tm), false, false);
                     tm = fmaxf(__uint_as_float(w32[0]), __uint_as_float(w32[1]));
                 }
                 const float tmax = tm * c;   // c > 0
                 const bool raise = tmax > m2 + kLazy;   // also true on the first valid tile
-                const bool any = __ballot(raise) != 0ull;
+                const uint64_t rb = __ballot(raise);
                 const float mnew = raise ? tmax : m2;
                 const float alpha = raise ? __builtin_amdgcn_exp2f(m2 - mnew) : 1.f;   // m2 = -inf -> 0
                 lsum *= alpha;
                 m2 = mnew;
                 const float negm = mnew == -__builtin_inff() ? 0.f : -mnew;
-                float pe[2][4];
+                float pe[16];
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) pe[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], c, negm));
-                float rs = ((pe[0][0] + pe[0][1]) + (pe[0][2] + pe[0][3])) + ((pe[1][0] + pe[1][1]) + (pe[1][2] + pe[1][3]));
+                for (int i = 0; i < 16; ++i) pe[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, negm));
+                float rs = (((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]))) +
+                           (((pe[8] + pe[9]) + (pe[10] + pe[11])) + ((pe[12] + pe[13]) + (pe[14] + pe[15])));
                 {
-                    const auto w16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(rs), __float_as_uint(rs), false, false);
-                    rs = __uint_as_float(w16[0]) + __uint_as_float(w16[1]);
                     const auto w32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(rs), __float_as_uint(rs), false, false);
                     lsum += __uint_as_float(w32[0]) + __uint_as_float(w32[1]);
                 }
-                if (g == 0) alph[ps][wave * 16 + l16] = alpha;
-                if (lane == 0) rflag[ps][wave] = any ? 1 : 0;
-                // P^T operand: lane (g, head), K-slots 0..3 = keys 4 g + i, 4..7 = keys 16 + 4 g + i
-                bf16x8 pb;
+                if (kh == 0) alph[ps][qh * 32 + hq] = alpha;
+                if (lane == 0) {
+                    rflag[ps][2 * qh] = (rb & 0x0000FFFF0000FFFFull) != 0ull ? 1 : 0;
+                    rflag[ps][2 * qh + 1] = (rb & 0xFFFF0000FFFF0000ull) != 0ull ? 1 : 0;
+                }
+                // KVF 1: the P^T operand is p * f (the normaliser sums p)
+                float pf[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) pf[i] = KVF == 1 ? pe[i] * fk[i] : pe[i];
+                bf16x8 p0, p1;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    pb[i] = (__bf16)pe[0][i];
-                    pb[4 + i] = (__bf16)pe[1][i];
+                    p0[i] = (__bf16)pf[i];
+                    p0[4 + i] = (__bf16)pf[8 + i];
+                    p1[i] = (__bf16)pf[4 + i];
+                    p1[4 + i] = (__bf16)pf[12 + i];
                 }
-                *(__attribute__((address_space(3))) bf16x8*)((lds_u8*)pbuf[ps][wave] + lane * 16) = pb;
+                lds_u8* pp = (lds_u8*)pbuf[ps][pt];
+                *(__attribute__((address_space(3))) bf16x8*)(pp + (kh * 16 + phl) * 16) = p0;
+                *(__attribute__((address_space(3))) bf16x8*)(pp + ((2 + kh) * 16 + phl) * 16) = p1;
             };
 
             __syncthreads();                                   // barrier P: tile 0 landed
-            q_tile(tile0, vmask[0], 0);
+            q_tile(tile0, 0, vmask[0], 0);
             int bq = 1;                                        // buffer of tile t+1
             for (int t = 0; t < ntiles; ++t) {
                 __syncthreads();                               // barrier t: P(t) published, tile t+1 landed
                 if (t + 1 < ntiles) {
                     const uint32_t vmn = __builtin_amdgcn_readfirstlane(vmask[t + 1]);
-                    q_tile(tile0 + bq * TB, vmn, (t + 1) & 1);
+                    q_tile(tile0 + bq * TB, bq, vmn, (t + 1) & 1);
                 }
                 bq = bq == NBUF - 1 ? 0 : bq + 1;
             }
             __syncthreads();                                   // barrier F: the P ring is no longer read
-            if (g == 0) {
-                fin_l[wave * 16 + l16] = lsum;
-                fin_m[wave * 16 + l16] = m2;
-            }
-            __syncthreads();                                   // barrier E
-        } else {
-            const int qh = wave >> 1, kb = wave & 1;
-            // the query in B-operand layout: lane = head, 8 consecutive columns of K-step ks
-            bf16x8 qb[2][KS];
-#pragma unroll
-            for (int ht = 0; ht < 2; ++ht) {
-                const int head = hb * 64 + qh * 32 + ht * 16 + l16;
-#pragma unroll
-                for (int j = 0; j < KS; ++j) {
-                    if (head < a.H)
-                        qb[ht][j] = *(const bf16x8*)(a.q + (((int64_t)r * a.H + head) * DQK + j * 32 + g * 8) * 2);
-                    else
-                        qb[ht][j] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-                }
-            }
-            // then the slot table: every index load of the thread first,
-            // then every block-table lookup (two dependent global round trips)
-            constexpr int EPT = MAXK / NQT;
-            const int qt = tid;                             // 0 .. 255
-            int pidx[EPT];
-#pragma unroll
-            for (int j = 0; j < EPT; ++j) {
-                const int i = j * NQT + qt;
-                pidx[j] = i < nk ? a.idx[(int64_t)r * a.K + k0 + i] : -1;
-            }
-            int64_t sv[EPT];
-#pragma unroll
-            for (int j = 0; j < EPT; ++j) sv[j] = pidx[j] >= 0 ? slot_of(a.kv, seq, pidx[j]) : -1;
-#pragma unroll
-            for (int j = 0; j < EPT; ++j) {
-                const int i = j * NQT + qt;
-                if (i < nt_fill * TROWS) rslot[i] = sv[j] >= 0 ? (uint32_t)sv[j] : 0xFFFFFFFFu;
-                const uint64_t bal = __ballot(sv[j] >= 0);
-                if (lane == 0 && i < nt_fill * TROWS) {
-                    vmask[i / 32] = (uint32_t)bal;
-                    if (i + 32 < nt_fill * TROWS) vmask[i / 32 + 1] = (uint32_t)(bal >> 32);
-                }
-            }
-            __syncthreads();                                   // the slot table is complete
-            count_tiles();
-            __syncthreads();
-            const int ntiles = s_ntiles;
-            // key operand of K-step ks: row 16 kb + l16, chunk 4 ks + g (swz8 of the
-            // row does not depend on kb)
-            uint32_t qa[2];
-#pragma unroll
-            for (int par = 0; par < 2; ++par)
-                qa[par] = (uint32_t)(kb * 2 * GB + (l16 >> 3) * GB + (l16 & 7) * 128 +
-                                     (((4 * par + g) ^ sfa_swz8(l16)) << 4));
-            auto qk_op = [&](const lds_u8* T, int ks) -> bf16x8 {   // compile-time ks
-                return *(const lds_bf16x8*)(T + qa[ks & 1] + (ks >> 1) * 1024);
-            };
-            float m2[2] = {-__builtin_inff(), -__builtin_inff()}, lsum[2] = {0.f, 0.f};
-            const float c = a.scale_log2;
-
-            // S^T of this wave's keys of one tile for both head tiles, the maxima
-            // trade, softmax statistics, this key block's half of P^T to LDS slot ps
-            auto q_tile = [&](const lds_u8* T, int buf, uint32_t vm, int ps, int seqno) {
-                f32x4v s[2] = {f32x4v{0.f, 0.f, 0.f, 0.f}, f32x4v{0.f, 0.f, 0.f, 0.f}};   // [head tile]
-                // operand reads in batches of KPB K-steps, software-pipelined: the
-                // reads of batch b + 1 go out before the MFMAs of batch b (the
-                // scheduling barriers keep the compiler from pairing each read with
-                // its MFMAs)
-                constexpr int KPB = KVF == 2 ? 2 : 6;
-                constexpr int NB = KS / KPB;
-                static_assert(KS % KPB == 0, "whole batches");
-                bf16x8 av[2][KPB];
-#pragma unroll
-                for (int j = 0; j < KPB; ++j) av[0][j] = qk_op(T, j);
-                if constexpr (KVF != 2) {
-                    static_for<NB>([&](auto bc) {
-                        constexpr int b = decltype(bc)::value;
-                        if constexpr (b + 1 < NB) {
-#pragma unroll
-                            for (int j = 0; j < KPB; ++j) av[(b + 1) & 1][j] = qk_op(T, (b + 1) * KPB + j);
-                        }
-                        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                        for (int j = 0; j < KPB; ++j) {
-                            const int ks = b * KPB + j;
-                            s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[b & 1][j], qb[0][ks], s[0], 0, 0, 0);
-                            s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[b & 1][j], qb[1][ks], s[1], 0, 0, 0);
-                        }
-                        __builtin_amdgcn_sched_barrier(0);
-                    });
-                } else {
-                    // column tile j = K-steps 4 j .. 4 j + 3 (the rope tile: 16, 17)
-                    // accumulates into sc[j & 1]; it is added, times the keys' factor
-                    // f_j, after the first batch of the next column tile went out
-                    f32x4v sc[2][2];
-#pragma unroll
-                    for (int p = 0; p < 2; ++p)
-#pragma unroll
-                        for (int ht = 0; ht < 2; ++ht) sc[p][ht] = f32x4v{0.f, 0.f, 0.f, 0.f};
-                    const float* kf = kvf + buf * NTL * TROWS + 16 * kb + 4 * g;
-                    auto fold = [&](int j, int p) {   // s += f_j(key) * sc[p]; sc[p] = 0
-                        const f32x4v f = *(const f32x4v*)(kf + j * TROWS);
-#pragma unroll
-                        for (int ht = 0; ht < 2; ++ht) {
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) s[ht][i] = __builtin_fmaf(f[i], sc[p][ht][i], s[ht][i]);
-                            sc[p][ht] = f32x4v{0.f, 0.f, 0.f, 0.f};
-                        }
-                    };
-                    static_for<NB>([&](auto bc) {
-                        constexpr int b = decltype(bc)::value;
-                        constexpr int jt = (b * KPB) / 4;          // column tile of this batch
-                        if constexpr (b + 1 < NB) {
-#pragma unroll
-                            for (int j = 0; j < KPB; ++j) av[(b + 1) & 1][j] = qk_op(T, (b + 1) * KPB + j);
-                        }
-                        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                        for (int j = 0; j < KPB; ++j) {
-                            const int ks = b * KPB + j;
-                            sc[jt & 1][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[b & 1][j], qb[0][ks], sc[jt & 1][0],
-                                                                                     0, 0, 0);
-                            sc[jt & 1][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[b & 1][j], qb[1][ks], sc[jt & 1][1],
-                                                                                     0, 0, 0);
-                        }
-                        __builtin_amdgcn_sched_barrier(0);
-                        // first batch of column tile jt >= 1: the previous tile is complete
-                        if constexpr (jt >= 1 && (b * KPB) % 4 == 0) fold(jt - 1, (jt - 1) & 1);
-                    });
-                    fold(NTL - 1, (NTL - 1) & 1);
-                }
-                float fk[4];   // KVF 1: the factor of each of this lane's keys
-                if constexpr (KVF == 1) {
-                    const f32x4v f = *(const f32x4v*)(kvf + buf * TROWS + 16 * kb + 4 * g);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) fk[i] = f[i];
-                    // one factor per row: the logit is scale * f * (q . code)
-                    s[0] *= f;
-                    s[1] *= f;
-                }
-                if (vm != 0xFFFFFFFFu) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (!((vm >> (16 * kb + 4 * g + i)) & 1u)) {
-                            s[0][i] = -__builtin_inff();
-                            s[1][i] = -__builtin_inff();
-                        }
-                }
-                // per-head maxima over this wave's 16 keys, traded with the partner
-                float tm[2];
-#pragma unroll
-                for (int ht = 0; ht < 2; ++ht) {
-                    float m = fmaxf(fmaxf(s[ht][0], s[ht][1]), fmaxf(s[ht][2], s[ht][3]));
-                    const auto w16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-                    m = fmaxf(__uint_as_float(w16[0]), __uint_as_float(w16[1]));
-                    const auto w32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-                    tm[ht] = fmaxf(__uint_as_float(w32[0]), __uint_as_float(w32[1]));
-                    if (g == 0) xmax[qh][kb][ht * 16 + l16] = tm[ht];
-                }
-                if (lane == 0) __hip_atomic_store(&xflag[qh][kb], seqno, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-                while (__hip_atomic_load(&xflag[qh][kb ^ 1], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != seqno)
-                    __builtin_amdgcn_s_sleep(1);
-                // both head tiles side by side (independent chains), without branches
-                float tmax[2], alpha[2], pe[2][4], rs[2];
-                bool any[2];
-#pragma unroll
-                for (int ht = 0; ht < 2; ++ht) tmax[ht] = fmaxf(tm[ht], xmax[qh][kb ^ 1][ht * 16 + l16]) * c;   // c > 0
-#pragma unroll
-                for (int ht = 0; ht < 2; ++ht) {
-                    const bool raise = tmax[ht] > m2[ht] + kLazy;   // also true on the first valid tile
-                    any[ht] = __ballot(raise) != 0ull;
-                    const float mnew = raise ? tmax[ht] : m2[ht];
-                    alpha[ht] = raise ? __builtin_amdgcn_exp2f(m2[ht] - mnew) : 1.f;   // m2 = -inf -> 0
-                    lsum[ht] *= alpha[ht];
-                    m2[ht] = mnew;
-                    const float negm = mnew == -__builtin_inff() ? 0.f : -mnew;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) pe[ht][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[ht][i], c, negm));
-                    rs[ht] = (pe[ht][0] + pe[ht][1]) + (pe[ht][2] + pe[ht][3]);
-                }
-#pragma unroll
-                for (int ht = 0; ht < 2; ++ht) {
-                    const auto w16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(rs[ht]), __float_as_uint(rs[ht]),
-                                                                      false, false);
-                    rs[ht] = __uint_as_float(w16[0]) + __uint_as_float(w16[1]);
-                }
-#pragma unroll
-                for (int ht = 0; ht < 2; ++ht) {
-                    const auto w32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(rs[ht]), __float_as_uint(rs[ht]),
-                                                                      false, false);
-                    lsum[ht] += __uint_as_float(w32[0]) + __uint_as_float(w32[1]);
-                }
-#pragma unroll
-                for (int ht = 0; ht < 2; ++ht) {
-                    const int htg = qh * 2 + ht;   // head tile within the block
-                    if (kb == 0) {
-                        if (g == 0) alph[ps][htg * 16 + l16] = alpha[ht];
-                        if (lane == 0) rflag[ps][htg] = any[ht] ? 1 : 0;
-                    }
-                    bf16x4v pb;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) pb[i] = (__bf16)(KVF == 1 ? pe[ht][i] * fk[i] : pe[ht][i]);
-                    *(__attribute__((address_space(3))) bf16x4v*)((lds_u8*)pbuf[ps][htg] + lane * 16 + kb * 8) = pb;
-                }
-            };
-
-            __syncthreads();                                   // barrier P: tile 0 landed
-            q_tile(tile0, 0, vmask[0], 0, 1);
-            int bq = 1;                                        // buffer of tile t+1
-            for (int t = 0; t < ntiles; ++t) {
-                __syncthreads();                               // barrier t: P(t) published, tile t+1 landed
-                if (t + 1 < ntiles) {
-                    const uint32_t vmn = __builtin_amdgcn_readfirstlane(vmask[t + 1]);
-                    q_tile(tile0 + bq * TB, bq, vmn, (t + 1) & 1, t + 2);
-                }
-                bq = bq == NBUF - 1 ? 0 : bq + 1;
-            }
-            __syncthreads();                                   // barrier F: the P ring is no longer read
-            if (g == 0) {
-#pragma unroll
-                for (int ht = 0; ht < 2; ++ht) {
-                    fin_l[(qh * 2 + kb) * 32 + ht * 16 + l16] = lsum[ht];
-                    if (kb == 0) fin_m[qh * 32 + ht * 16 + l16] = m2[ht];
-                }
+            if (kh == 0) {
+                fin_l[qh * 32 + hq] = lsum;
+                fin_m[qh * 32 + hq] = m2;
             }
             __syncthreads();                                   // barrier E
         }
+    } else if (!is_p) {
+        // ------------------------------------------------------ helper waves 4, 5
+        // the slot table; fp8 rows: the tiles (helper hw brings rows 16 hw .. 16 hw + 15
+        // of every tile): in 1 KB block j, lane l owns position l % 8 of row
+        // 16 hw + 8 rr + l / 8, i.e. bf16 chunk 8 j + ((l % 8) ^ swz8(row)) = 8
+        // columns: it loads their 8 e4m3 codes, converts them exactly and writes
+        // the 16 bytes (one contiguous 1 KB per instruction).  Codes go out two
+        // tiles ahead, converted tiles one tile ahead (tile t + 2 into the buffer
+        // tile t - 1 has released, in period t).
+        const int hw = wave - 4;
+        build_slots(std::integral_constant<int, NQT>{}, lane + 64 * hw, hw);
+        __syncthreads();                                   // the slot table is complete
+        const int ntiles = read_ntiles();
+        struct Codes {
+            u32x2 v[2][NJ];
+            float f[2][NTL];
+        };
+        int frow[2], fsw[2];
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+            frow[rr] = 16 * hw + 8 * rr + (lane >> 3);
+            fsw[rr] = (lane & 7) ^ sfa_swz8(frow[rr]);
+        }
+        auto fetch = [&](int t, Codes& cd) {
+#pragma unroll
+            for (int rr = 0; rr < 2; ++rr) {
+                const uint32_t sl = t < ntiles ? rslot[t * TROWS + frow[rr]] : 0xFFFFFFFFu;
+                const bool ok = sl != 0xFFFFFFFFu;
+                const uint8_t* gp = ok ? a.kv.data + (uint64_t)sl * (uint32_t)a.kv.row_stride : g_zero_row;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    const u32x2* src = (const u32x2*)(gp + (8 * j + fsw[rr]) * 8);
+                    cd.v[rr][j] = a.gather_nt ? __builtin_nontemporal_load(src) : *src;
+                }
+                if constexpr (KVF == 1) {
+                    cd.f[rr][0] = ok ? a.kv.scale[(int64_t)sl / a.kv.scale_group] : 0.f;
+                } else if constexpr (KVF == 2) {
+#pragma unroll
+                    for (int q = 0; q < NTL; ++q) cd.f[rr][q] = ok ? a.kv.scale[(int64_t)sl * NTL + q] : 0.f;
+                }
+            }
+        };
+        auto put = [&](const Codes& cd, int buf) {
+#pragma unroll
+            for (int rr = 0; rr < 2; ++rr) {
+                lds_u8* dst = (lds_u8*)tile + buf * TB + (2 * hw + rr) * GB + lane * 16;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    u32x4 b;
+                    b.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cd.v[rr][j].x, 1.0f, false));
+                    b.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cd.v[rr][j].x, 1.0f, true));
+                    b.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cd.v[rr][j].y, 1.0f, false));
+                    b.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cd.v[rr][j].y, 1.0f, true));
+                    *(__attribute__((address_space(3))) u32x4*)(dst + j * 1024) = b;
+                }
+                if ((lane & 7) == 0) {
+#pragma unroll
+                    for (int q = 0; q < NTL; ++q) kvf[(buf * NTL + q) * TROWS + frow[rr]] = cd.f[rr][q];
+                }
+            }
+        };
+        Codes c0, c1;
+        if constexpr (KVF != 0) {
+            fetch(0, c0);
+            fetch(1, c1);
+            put(c0, 0);
+            put(c1, 1);
+            fetch(2, c0);
+            fetch(3, c1);
+        }
+        __syncthreads();                                   // barrier P
+        int bc = 0;                                        // buffer of tile t
+        for (int t = 0; t < ntiles; ++t) {
+            __syncthreads();                               // barrier t
+            if constexpr (KVF != 0) {
+                // tile t+2 into the buffer tile t-1 has released; codes of tile t+4 out.
+                // Constant register-set names in each branch keep the codes in registers.
+                const int bw = bc == 0 ? 2 : bc - 1;
+                if (t & 1) {
+                    if (t + 2 < ntiles) put(c1, bw);
+                    if (t + 4 < ntiles) fetch(t + 4, c1);
+                } else {
+                    if (t + 2 < ntiles) put(c0, bw);
+                    if (t + 4 < ntiles) fetch(t + 4, c0);
+                }
+            }
+            bc = bc == NBUF - 1 ? 0 : bc + 1;
+        }
+        __syncthreads();                                   // barrier F
+        __syncthreads();                                   // barrier E
     } else {
         // ---------------------------------------------------------------- p-wave
         if constexpr (KVF == 0) {
@@ -1106,8 +1028,7 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
             }
         }
         __syncthreads();                                   // the slot table is complete
-        __syncthreads();
-        const int ntiles = s_ntiles;
+        const int ntiles = read_ntiles();
         // bf16 rows: tile t + 1 + LA goes out in iteration t into the buffer
         // tile t - 1 has released.  Every tile is NJ loads per thread: "tile j
         // landed" = at most NJ * (tiles issued after j) loads still pending.
@@ -1121,59 +1042,8 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
             else if (after == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NJ) : "memory");
             else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         };
-        // fp8 rows: in 1 KB block j, lane l owns position l % 8 of row 8 pc + l / 8,
-        // i.e. bf16 chunk 8 j + ((l % 8) ^ swz8(row)) = 8 columns: it loads their 8
-        // e4m3 codes, converts them exactly and writes the 16 bytes (one
-        // contiguous 1 KB per instruction).  Codes go out two tiles ahead.
-        const int frow = 8 * pc + (lane >> 3);
-        const int fsw = (lane & 7) ^ sfa_swz8(frow);
-        struct Codes {
-            u32x2 v[NJ];
-            float f[NTL];
-        };
-        auto fetch = [&](int t, Codes& cd) {
-            const uint32_t s = t < ntiles ? rslot[t * TROWS + frow] : 0xFFFFFFFFu;
-            const bool ok = s != 0xFFFFFFFFu;
-            const uint8_t* gp = ok ? a.kv.data + (uint64_t)s * (uint32_t)a.kv.row_stride : g_zero_row;
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                const u32x2* src = (const u32x2*)(gp + (8 * j + fsw) * 8);
-                cd.v[j] = a.gather_nt ? __builtin_nontemporal_load(src) : *src;
-            }
-            if constexpr (KVF == 1) {
-                cd.f[0] = ok ? a.kv.scale[(int64_t)s / a.kv.scale_group] : 0.f;
-            } else if constexpr (KVF == 2) {
-#pragma unroll
-                for (int q = 0; q < NTL; ++q) cd.f[q] = ok ? a.kv.scale[(int64_t)s * NTL + q] : 0.f;
-            }
-        };
-        auto put = [&](const Codes& cd, int buf) {
-            lds_u8* dst = (lds_u8*)tile + buf * TB + pc * GB + lane * 16;
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                u32x4 b;
-                b.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cd.v[j].x, 1.0f, false));
-                b.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cd.v[j].x, 1.0f, true));
-                b.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cd.v[j].y, 1.0f, false));
-                b.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cd.v[j].y, 1.0f, true));
-                *(__attribute__((address_space(3))) u32x4*)(dst + j * 1024) = b;
-            }
-            if ((lane & 7) == 0) {
-#pragma unroll
-                for (int q = 0; q < NTL; ++q) kvf[(buf * NTL + q) * TROWS + frow] = cd.f[q];
-            }
-        };
-        Codes c0, c1;
-        if constexpr (KVF == 0) {
-            wait_tile(0, LA);
-        } else {
-            fetch(0, c0);
-            fetch(1, c1);
-            put(c0, 0);
-            put(c1, 1);
-            fetch(2, c0);
-            fetch(3, c1);
-        }
+        const int prow = 8 * pc + (lane >> 3);            // bf16 rows: this lane's row of every tile
+        if constexpr (KVF == 0) wait_tile(0, LA);
         // PV operand of M-tile mt: transpose reads of rows 4 g + l16 / 4 (keys of
         // K-slots 0..3) and 16 + 4 g + l16 / 4 (K-slots 4..7), 4 value columns each
         uint32_t pva[4];
@@ -1195,11 +1065,9 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
 #pragma unroll
             for (int mt = 0; mt < MTP; ++mt) o[ht][mt] = f32x4v{0.f, 0.f, 0.f, 0.f};
 
-        // bf16 rows: the V operands of tile t + 1 are read in period t, into the
-        // registers the PV products of tile t have just taken theirs from, so after
-        // barrier t + 1 only the P^T operand stands between the p-wave and its
-        // MFMAs.  fp8 rows (whose codes in flight hold registers of their own):
-        // read after the barrier.
+        // the V operands of tile t + 1 are read in period t, into the registers the
+        // PV products of tile t have just taken theirs from, so after barrier t + 1
+        // only the P^T operand stands between the p-wave and its MFMAs
         auto read_v = [&](const lds_u8* T, s16x4 (&va)[MTP][2]) {
 #pragma unroll
             for (int mt = 0; mt < MTP; ++mt) {
@@ -1209,27 +1077,15 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
         };
         s16x4 va[MTP][2];
         __syncthreads();                                   // barrier P: tile 0 landed
-        if constexpr (KVF == 0) read_v(tile0, va);
+        read_v(tile0, va);
         int bc = 0;                                        // buffer of tile t
         for (int t = 0; t < ntiles; ++t) {
             if constexpr (KVF == 0) wait_tile(t + 1, t + LA);
             __syncthreads();                               // barrier t: P(t) published, tile t+1 landed
             if constexpr (KVF == 0) {
                 const int bn = bc + LA + 1 >= NBUF ? bc + LA + 1 - NBUF : bc + LA + 1;   // = buffer of tile t-1
-                if (t + 1 + LA < ntiles) issue_rows(rslot[(t + 1 + LA) * TROWS + frow], bn);
-            } else {
-                // tile t+2 into the buffer tile t-1 has released; codes of tile t+4 out.
-                // Constant register-set names in each branch keep the codes in registers.
-                const int bw = bc == 0 ? 2 : bc - 1;
-                if (t & 1) {
-                    if (t + 2 < ntiles) put(c1, bw);
-                    if (t + 4 < ntiles) fetch(t + 4, c1);
-                } else {
-                    if (t + 2 < ntiles) put(c0, bw);
-                    if (t + 4 < ntiles) fetch(t + 4, c0);
-                }
+                if (t + 1 + LA < ntiles) issue_rows(rslot[(t + 1 + LA) * TROWS + prow], bn);
             }
-            if constexpr (KVF != 0) read_v(tile0 + bc * TB, va);
             const int ps = t & 1;
             bf16x8 pbt[4];
 #pragma unroll
@@ -1266,8 +1122,7 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
                 for (int ht = 0; ht < 4; ++ht)
                     o[ht][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pbt[ht], o[ht][mt], 0, 0, 0);
             }
-            if constexpr (KVF == 0)
-                if (t + 1 < ntiles) read_v(tile0 + (bc == NBUF - 1 ? 0 : bc + 1) * TB, va);
+            if (t + 1 < ntiles) read_v(tile0 + (bc == NBUF - 1 ? 0 : bc + 1) * TB, va);
             bc = bc == NBUF - 1 ? 0 : bc + 1;
         }
         __syncthreads();                                   // barrier F
@@ -1277,9 +1132,8 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
 #pragma unroll
         for (int ht = 0; ht < 4; ++ht) {
             const int head = hb * 64 + ht * 16 + l16;
-            const int hh = ht >> 1, hl = (ht & 1) * 16 + l16;
-            const float ls = KVF == 0 ? fin_l[ht * 16 + l16] : fin_l[(hh * 2) * 32 + hl] + fin_l[(hh * 2 + 1) * 32 + hl];
-            const float mref = KVF == 0 ? fin_m[ht * 16 + l16] : fin_m[hh * 32 + hl];
+            const float ls = fin_l[ht * 16 + l16];
+            const float mref = fin_m[ht * 16 + l16];
             if (head >= a.H) continue;
             const float inv = ls > 0.f ? 1.f / ls : 0.f;
             if (pc == 0 && g == 0) {
