@@ -632,7 +632,6 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
     constexpr int GB = NJ * 1024;           // bytes per 8-row group
     constexpr int TROWS = 32;
     constexpr int TB = (TROWS / 8) * GB;    // bytes per tile
-    constexpr int NQT = 128;                // threads that build the slot table (waves 4, 5)
     constexpr int KS = DQK / 32;            // 16x16x32 K-steps of a row (18)
     constexpr int DVP = DLAT / 4;           // value columns per p-wave
     constexpr int MTP = DVP / 16;           // PV M-tiles per p-wave
@@ -681,12 +680,14 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
     const int g = lane >> 4, l16 = lane & 15;
     // value column block of a p-wave
     const int pc = (wave & 3) - 2 + 2 * (wave >> 2);
-    // bf16 tile loads of a p-wave: lane l brings chunk 8 j + ((l % 8) ^ swz8(row))
-    // of row 8 pc + l / 8 into block j of the row group, at block + 16 l
-    const uint32_t goff = (uint32_t)(((lane & 7) ^ sfa_swz8(8 * pc + (lane >> 3))) << 4);
-    auto issue_rows = [&](uint32_t s, int buf) {        // one tile's row of this lane
-        const uint8_t* gp = (s != 0xFFFFFFFFu ? a.kv.data + (uint64_t)s * (uint32_t)a.kv.row_stride : g_zero_row) + goff;
-        const uint32_t blk = tile_lds + (uint32_t)(buf * TB + pc * GB);
+    // bf16 tile loads: lane l brings chunk 8 j + ((l % 8) ^ swz8(row)) of row
+    // 8 grp + l / 8 into block j of row group grp, at block + 16 l
+    auto row_goff = [&](int grp) { return (uint32_t)(((lane & 7) ^ sfa_swz8(8 * grp + (lane >> 3))) << 4); };
+    // one tile's row of this lane in 8-row group grp (row 8 grp + lane / 8);
+    // go = the lane's chunk offset for that row
+    auto issue_rows = [&](uint32_t s, int buf, int grp, uint32_t go) {
+        const uint8_t* gp = (s != 0xFFFFFFFFu ? a.kv.data + (uint64_t)s * (uint32_t)a.kv.row_stride : g_zero_row) + go;
+        const uint32_t blk = tile_lds + (uint32_t)(buf * TB + grp * GB);
         // the immediate offset moves both the global and the LDS address; block j
         // lands at blk + j KB.  GNT: non-temporal gathers (the launch's gather_nt)
         static_for<NJ>([&](auto jc) {
@@ -699,41 +700,77 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
     // the last tile with a valid row (trailing tiles without one are skipped; at
     // least one tile is always processed): the q-waves, which build the slot
     // table, count between the two prologue barriers
-    // The slot table: every index load of the thread first, then every
-    // block-table lookup (two dependent global round trips).  NT threads
-    // qt = 0 .. NT - 1 in whole waves; builder wave bw also publishes the number
-    // of tiles up to its last valid row in s_ntw[bw] (trailing tiles without a
-    // valid row are skipped; at least one tile is always processed).
-    auto build_slots = [&](auto nt_c, int qt, int bw) {
-        constexpr int NT = decltype(nt_c)::value;
-        constexpr int EPT = MAXK / NT;
-        static_assert(MAXK % NT == 0, "whole rounds of index entries");
+    // The slot table, built by the helper waves: helper hw owns rows
+    // 16 hw .. 16 hw + 15 of every tile (the rows it also brings), lane l entry
+    // j = row 16 hw + l % 16 of tile 4 j + l / 16.  Paged caches: the sequence's
+    // block-table row is staged in the tile buffer the prologue leaves free (one
+    // copy per helper wave) while the index loads are in flight, so a slot costs
+    // one LDS read instead of a second dependent global round trip.  Returns the
+    // slots in sv; publishes rslot, this helper's 16-bit halves of vmask and, in
+    // s_ntw[hw], the number of tiles up to its last valid row.
+    constexpr int EPT = MAXK / 128;
+    constexpr int kBtStage = (TB / 2) / 4;              // block-table entries one staged copy holds
+    auto build_slots = [&](int hw, int64_t (&sv)[EPT]) {
         int pidx[EPT];
 #pragma unroll
         for (int j = 0; j < EPT; ++j) {
-            const int i = j * NT + qt;
+            const int i = (4 * j + (lane >> 4)) * TROWS + 16 * hw + (lane & 15);
             pidx[j] = i < nk ? a.idx[(int64_t)r * a.K + k0 + i] : -1;
         }
-        int64_t sv[EPT];
+        const int nbt = a.kv.bt_stride;
+        const bool staged = a.kv.paged && seq >= 0 && seq < a.kv.num_seqs && (nbt & 3) == 0 && nbt <= kBtStage &&
+                            ((uintptr_t)a.kv.block_table & 15) == 0;
+        if (staged) {
+            const u32x4* src = (const u32x4*)(a.kv.block_table + (int64_t)seq * nbt);
+            uint32_t* bt = (uint32_t*)(tile + (NBUF - 1) * TB) + hw * kBtStage;
+            const int n4 = nbt >> 2;
+            for (int c0 = 0; c0 < n4; c0 += 8 * 64) {
+                u32x4 v[8];
 #pragma unroll
-        for (int j = 0; j < EPT; ++j) sv[j] = pidx[j] >= 0 ? slot_of(a.kv, seq, pidx[j]) : -1;
+                for (int m = 0; m < 8; ++m) {
+                    const int c = c0 + m * 64 + lane;
+                    if (c < n4) v[m] = src[c];
+                }
+#pragma unroll
+                for (int m = 0; m < 8; ++m) {
+                    const int c = c0 + m * 64 + lane;
+                    if (c < n4) *(__attribute__((address_space(3))) u32x4*)(bt + 4 * c) = v[m];
+                }
+            }
+            const int sh = a.kv.bs_shift;
+#pragma unroll
+            for (int j = 0; j < EPT; ++j) {
+                const int p = pidx[j];
+                int64_t sl = -1;
+                if (p >= 0 && (p >> sh) < nbt) {
+                    const int32_t blk = (int32_t)bt[p >> sh];
+                    if (blk >= 0) {
+                        sl = ((int64_t)blk << sh) + (p & ((1 << sh) - 1));
+                        if (sl >= a.kv.num_slots) sl = -1;
+                    }
+                }
+                sv[j] = sl;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < EPT; ++j) sv[j] = pidx[j] >= 0 ? slot_of(a.kv, seq, pidx[j]) : -1;
+        }
         int nt_mine = 0;
+        uint16_t* vm16 = (uint16_t*)vmask;
 #pragma unroll
         for (int j = 0; j < EPT; ++j) {
-            const int i = j * NT + qt;
-            if (i < nt_fill * TROWS) rslot[i] = sv[j] >= 0 ? (uint32_t)sv[j] : 0xFFFFFFFFu;
-            if (sv[j] >= 0) nt_mine = i / TROWS + 1;
+            const int t = 4 * j + (lane >> 4);
+            const int i = t * TROWS + 16 * hw + (lane & 15);
+            if (t < nt_fill) rslot[i] = sv[j] >= 0 ? (uint32_t)sv[j] : 0xFFFFFFFFu;
+            if (sv[j] >= 0) nt_mine = t + 1;
             const uint64_t bal = __ballot(sv[j] >= 0);
-            if ((qt & 63) == 0 && i < nt_fill * TROWS) {
-                vmask[i / 32] = (uint32_t)bal;
-                if (i + 32 < nt_fill * TROWS) vmask[i / 32 + 1] = (uint32_t)(bal >> 32);
-            }
+            if (lane < 4 && 4 * j + lane < nt_fill) vm16[(4 * j + lane) * 2 + hw] = (uint16_t)(bal >> (16 * lane));
         }
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) nt_mine = max(nt_mine, __shfl_xor(nt_mine, d));
-        if ((qt & 63) == 0) s_ntw[bw] = nt_mine;
+        if (lane == 0) s_ntw[hw] = nt_mine;
     };
-    // after the slot-table barrier
+    // after barrier P
     auto read_ntiles = [&]() { return max(1, max(s_ntw[0], s_ntw[1])); };
 
     if (is_q) {
@@ -757,8 +794,6 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
                         qb[j] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
                 }
             }
-            __syncthreads();                                   // the slot table is complete
-            const int ntiles = read_ntiles();
             // key operand of K-step ks: row hq, chunk 2 ks + kh = block ks / 4,
             // chunk 2 (ks % 4) + kh inside it
             uint32_t qa[4];
@@ -901,7 +936,8 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
                 *(__attribute__((address_space(3))) bf16x8*)(pp + ((2 + kh) * 16 + phl) * 16) = p1;
             };
 
-            __syncthreads();                                   // barrier P: tile 0 landed
+            __syncthreads();                                   // barrier P: the slot table is complete, tile 0 landed
+            const int ntiles = read_ntiles();
             q_tile(tile0, 0, vmask[0], 0);
             int bq = 1;                                        // buffer of tile t+1
             for (int t = 0; t < ntiles; ++t) {
@@ -921,17 +957,40 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
         }
     } else if (!is_p) {
         // ------------------------------------------------------ helper waves 4, 5
-        // the slot table; fp8 rows: the tiles (helper hw brings rows 16 hw .. 16 hw + 15
-        // of every tile): in 1 KB block j, lane l owns position l % 8 of row
-        // 16 hw + 8 rr + l / 8, i.e. bf16 chunk 8 j + ((l % 8) ^ swz8(row)) = 8
-        // columns: it loads their 8 e4m3 codes, converts them exactly and writes
-        // the 16 bytes (one contiguous 1 KB per instruction).  Codes go out two
-        // tiles ahead, converted tiles one tile ahead (tile t + 2 into the buffer
-        // tile t - 1 has released, in period t).
+        // The slot table, then the first tiles, helper hw rows 16 hw .. 16 hw + 15
+        // of each.  bf16 rows: tiles 0 .. LA by direct global->LDS loads from the
+        // slots still in registers (the p-waves bring the later tiles); the helper
+        // waits for tile t + 1 (t < LA) before barrier t.  fp8 rows: every tile: in
+        // 1 KB block j, lane l owns position l % 8 of row 16 hw + 8 rr + l / 8,
+        // i.e. bf16 chunk 8 j + ((l % 8) ^ swz8(row)) = 8 columns: it loads their 8
+        // e4m3 codes, converts them exactly and writes the 16 bytes (one
+        // contiguous 1 KB per instruction).  Codes go out two tiles ahead,
+        // converted tiles one tile ahead (tile t + 2 into the buffer tile t - 1 has
+        // released, in period t).
         const int hw = wave - 4;
-        build_slots(std::integral_constant<int, NQT>{}, lane + 64 * hw, hw);
-        __syncthreads();                                   // the slot table is complete
-        const int ntiles = read_ntiles();
+        int64_t sv[EPT];
+        build_slots(hw, sv);
+        // helper tile j landed (j <= LA); later helper tiles may still be in flight
+        auto hwait = [&](int j) {
+            int after = 0;
+#pragma unroll
+            for (int i = 1; i <= LA; ++i) after += (i > j && i < nt_fill) ? 1 : 0;
+            if (after >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * NJ) : "memory");
+            else if (after == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NJ) : "memory");
+            else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        };
+        if constexpr (KVF == 0) {
+            static_assert(LA <= 2 && 4 * NJ < 64, "vmcnt covers the helper tiles in flight");
+            // tile t row 16 hw + 8 rr + l / 8 = entry 0 of lane 16 t + 8 rr + l / 8
+#pragma unroll
+            for (int t = 0; t <= LA; ++t) {
+#pragma unroll
+                for (int rr = 0; rr < 2; ++rr) {
+                    const int64_t sl = __shfl(sv[0], 16 * t + 8 * rr + (lane >> 3));
+                    if (t < nt_fill) issue_rows(sl >= 0 ? (uint32_t)sl : 0xFFFFFFFFu, t, 2 * hw + rr, row_goff(2 * hw + rr));
+                }
+            }
+        }
         struct Codes {
             u32x2 v[2][NJ];
             float f[2][NTL];
@@ -945,7 +1004,7 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
         auto fetch = [&](int t, Codes& cd) {
 #pragma unroll
             for (int rr = 0; rr < 2; ++rr) {
-                const uint32_t sl = t < ntiles ? rslot[t * TROWS + frow[rr]] : 0xFFFFFFFFu;
+                const uint32_t sl = t < nt_fill ? rslot[t * TROWS + frow[rr]] : 0xFFFFFFFFu;
                 const bool ok = sl != 0xFFFFFFFFu;
                 const uint8_t* gp = ok ? a.kv.data + (uint64_t)sl * (uint32_t)a.kv.row_stride : g_zero_row;
 #pragma unroll
@@ -988,10 +1047,15 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
             put(c1, 1);
             fetch(2, c0);
             fetch(3, c1);
+        } else {
+            hwait(0);
         }
-        __syncthreads();                                   // barrier P
+        __syncthreads();                                   // barrier P: the slot table is complete, tile 0 landed
+        const int ntiles = read_ntiles();
         int bc = 0;                                        // buffer of tile t
         for (int t = 0; t < ntiles; ++t) {
+            if constexpr (KVF == 0)
+                if (t < LA) hwait(t + 1);
             __syncthreads();                               // barrier t
             if constexpr (KVF != 0) {
                 // tile t+2 into the buffer tile t-1 has released; codes of tile t+4 out.
@@ -1011,30 +1075,15 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
         __syncthreads();                                   // barrier E
     } else {
         // ---------------------------------------------------------------- p-wave
-        if constexpr (KVF == 0) {
-            // p-waves: the slots of their rows of tiles 0 .. LA, looked up directly, so
-            // the first tile loads go out while the table is still being built
-            int32_t es = -1;                                // lane 8 t + k: row 8 pc + k of tile t
-            {
-                const int t = lane >> 3, i = t * TROWS + 8 * pc + (lane & 7);
-                const int p = (t <= LA && i < nk) ? a.idx[(int64_t)r * a.K + k0 + i] : -1;
-                const int64_t sl = p >= 0 ? slot_of(a.kv, seq, p) : -1;
-                es = sl >= 0 ? (int32_t)(uint32_t)sl : -1;
-            }
-#pragma unroll
-            for (int t = 0; t <= LA; ++t) {
-                const uint32_t s = (uint32_t)__shfl(es, 8 * t + (lane >> 3));
-                if (t < nt_fill) issue_rows(s, t);
-            }
-        }
-        __syncthreads();                                   // the slot table is complete
-        const int ntiles = read_ntiles();
-        // bf16 rows: tile t + 1 + LA goes out in iteration t into the buffer
-        // tile t - 1 has released.  Every tile is NJ loads per thread: "tile j
-        // landed" = at most NJ * (tiles issued after j) loads still pending.
+        // bf16 rows: tile t + 1 + LA (> LA: the helpers bring tiles 0 .. LA) goes
+        // out in iteration t into the buffer tile t - 1 has released.  Every tile
+        // is NJ loads per thread: "tile j landed" = at most NJ * (tiles issued
+        // after j) loads still pending.
         static_assert(LA <= 2 && NJ * LA < 64, "vmcnt covers the tiles in flight");
-        auto issued = [&](int i) { return i <= LA ? i < nt_fill : i < ntiles; };
+        int ntiles = 1;
+        auto issued = [&](int i) { return i > LA && i < ntiles; };
         auto wait_tile = [&](int j, int last) {            // tile j landed; tiles up to `last` issued
+            if (j <= LA) return;                           // a helper tile: waited for by the helpers
             int after = 0;
 #pragma unroll
             for (int d = 1; d <= LA; ++d) after += (j + d <= last && issued(j + d)) ? 1 : 0;
@@ -1043,7 +1092,7 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
             else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         };
         const int prow = 8 * pc + (lane >> 3);            // bf16 rows: this lane's row of every tile
-        if constexpr (KVF == 0) wait_tile(0, LA);
+        const uint32_t pgo = row_goff(pc);
         // PV operand of M-tile mt: transpose reads of rows 4 g + l16 / 4 (keys of
         // K-slots 0..3) and 16 + 4 g + l16 / 4 (K-slots 4..7), 4 value columns each
         uint32_t pva[4];
@@ -1076,7 +1125,8 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
             }
         };
         s16x4 va[MTP][2];
-        __syncthreads();                                   // barrier P: tile 0 landed
+        __syncthreads();                                   // barrier P: the slot table is complete, tile 0 landed
+        ntiles = read_ntiles();
         read_v(tile0, va);
         int bc = 0;                                        // buffer of tile t
         for (int t = 0; t < ntiles; ++t) {
@@ -1084,7 +1134,7 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
             __syncthreads();                               // barrier t: P(t) published, tile t+1 landed
             if constexpr (KVF == 0) {
                 const int bn = bc + LA + 1 >= NBUF ? bc + LA + 1 - NBUF : bc + LA + 1;   // = buffer of tile t-1
-                if (t + 1 + LA < ntiles) issue_rows(rslot[(t + 1 + LA) * TROWS + prow], bn);
+                if (t + 1 + LA < ntiles) issue_rows(rslot[(t + 1 + LA) * TROWS + prow], bn, pc, pgo);
             }
             const int ps = t & 1;
             bf16x8 pbt[4];
