@@ -637,6 +637,7 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
     constexpr int MTP = DVP / 16;           // PV M-tiles per p-wave
     constexpr int NTL = KVF == 2 ? (DQK + 127) / 128 : 1;   // fp8 factors per row
     constexpr int LA = NBUF - 2;            // tiles in flight ahead of QK^T
+    constexpr int HT = 2;                   // bf16 rows: tiles the helper waves bring (the p-waves the rest)
     static_assert(NBUF >= 3 && (KVF == 0 || NBUF == 3), "PV(t) | QK(t+1) | tiles t+2 ..");
     typedef float f32x4v __attribute__((ext_vector_type(4)));
     typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
@@ -958,9 +959,9 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
     } else if (!is_p) {
         // ------------------------------------------------------ helper waves 4, 5
         // The slot table, then the first tiles, helper hw rows 16 hw .. 16 hw + 15
-        // of each.  bf16 rows: tiles 0 .. LA by direct global->LDS loads from the
-        // slots still in registers (the p-waves bring the later tiles); the helper
-        // waits for tile t + 1 (t < LA) before barrier t.  fp8 rows: every tile: in
+        // of each.  bf16 rows: tiles 0 .. HT - 1 by direct global->LDS loads from
+        // the slots still in registers (the p-waves bring the later tiles); the
+        // helper waits for tile t + 1 (< HT) before barrier t.  fp8 rows: every tile: in
         // 1 KB block j, lane l owns position l % 8 of row 16 hw + 8 rr + l / 8,
         // i.e. bf16 chunk 8 j + ((l % 8) ^ swz8(row)) = 8 columns: it loads their 8
         // e4m3 codes, converts them exactly and writes the 16 bytes (one
@@ -970,20 +971,16 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
         const int hw = wave - 4;
         int64_t sv[EPT];
         build_slots(hw, sv);
-        // helper tile j landed (j <= LA); later helper tiles may still be in flight
+        // helper tile j landed (j < HT); later helper tiles may still be in flight
+        static_assert(HT == 2 && HT <= LA + 1 && 2 * NJ < 64, "vmcnt covers the helper tiles in flight");
         auto hwait = [&](int j) {
-            int after = 0;
-#pragma unroll
-            for (int i = 1; i <= LA; ++i) after += (i > j && i < nt_fill) ? 1 : 0;
-            if (after >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * NJ) : "memory");
-            else if (after == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NJ) : "memory");
+            if (j == 0 && 1 < nt_fill) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NJ) : "memory");
             else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         };
         if constexpr (KVF == 0) {
-            static_assert(LA <= 2 && 4 * NJ < 64, "vmcnt covers the helper tiles in flight");
             // tile t row 16 hw + 8 rr + l / 8 = entry 0 of lane 16 t + 8 rr + l / 8
 #pragma unroll
-            for (int t = 0; t <= LA; ++t) {
+            for (int t = 0; t < HT; ++t) {
 #pragma unroll
                 for (int rr = 0; rr < 2; ++rr) {
                     const int64_t sl = __shfl(sv[0], 16 * t + 8 * rr + (lane >> 3));
@@ -1055,7 +1052,7 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
         int bc = 0;                                        // buffer of tile t
         for (int t = 0; t < ntiles; ++t) {
             if constexpr (KVF == 0)
-                if (t < LA) hwait(t + 1);
+                if (t + 1 < HT) hwait(t + 1);
             __syncthreads();                               // barrier t
             if constexpr (KVF != 0) {
                 // tile t+2 into the buffer tile t-1 has released; codes of tile t+4 out.
@@ -1075,15 +1072,15 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
         __syncthreads();                                   // barrier E
     } else {
         // ---------------------------------------------------------------- p-wave
-        // bf16 rows: tile t + 1 + LA (> LA: the helpers bring tiles 0 .. LA) goes
-        // out in iteration t into the buffer tile t - 1 has released.  Every tile
-        // is NJ loads per thread: "tile j landed" = at most NJ * (tiles issued
-        // after j) loads still pending.
+        // bf16 rows: the helpers bring tiles 0 .. HT - 1; tiles HT .. LA go out
+        // after barrier P, tile t + 1 + LA in iteration t, each into the buffer
+        // tile t - 1 has released.  Every tile is NJ loads per thread: "tile j
+        // landed" = at most NJ * (tiles issued after j) loads still pending.
         static_assert(LA <= 2 && NJ * LA < 64, "vmcnt covers the tiles in flight");
         int ntiles = 1;
-        auto issued = [&](int i) { return i > LA && i < ntiles; };
+        auto issued = [&](int i) { return i >= HT && i < ntiles; };
         auto wait_tile = [&](int j, int last) {            // tile j landed; tiles up to `last` issued
-            if (j <= LA) return;                           // a helper tile: waited for by the helpers
+            if (j < HT) return;                            // a helper tile: waited for by the helpers
             int after = 0;
 #pragma unroll
             for (int d = 1; d <= LA; ++d) after += (j + d <= last && issued(j + d)) ? 1 : 0;
@@ -1127,6 +1124,11 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
         s16x4 va[MTP][2];
         __syncthreads();                                   // barrier P: the slot table is complete, tile 0 landed
         ntiles = read_ntiles();
+        if constexpr (KVF == 0) {
+#pragma unroll
+            for (int t = HT; t <= LA; ++t)
+                if (t < ntiles) issue_rows(rslot[t * TROWS + prow], t, pc, pgo);
+        }
         read_v(tile0, va);
         int bc = 0;                                        // buffer of tile t
         for (int t = 0; t < ntiles; ++t) {
