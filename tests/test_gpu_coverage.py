@@ -156,6 +156,44 @@ def test_sparse_mla_single_split_rows(lib):
         _check_mla(b, idx, range(5), False, f"K={K}")
 
 
+@pytest.mark.parametrize("L", [2300, 2600], ids=["table-row-staged", "direct-lookups"])
+def test_sparse_mla_unaddressable_positions_skipped(lib, L):
+    """Index entries the paged cache cannot address (a position past the
+    sequence's block-table row, any negative value) are skipped, i.e. the
+    result is the attention over the addressable entries.  L = 2300 gives a
+    36-entry table row (staged in LDS by the kernel), L = 2600 a 41-entry row
+    (looked up entry by entry)."""
+    R, K = 4, 2048
+    b = _mla_batch(512, 64, "bf16", 128, R=R, L=L, nseq=2, seed=L)
+    bt_stride = int(b.block_table.shape[1])
+    far = bt_stride * b.wl.block_size
+    idx = _index_lists(R, K, L, seed=L + 1)
+    g = np.random.default_rng(L + 2)
+    valid = idx.copy()
+    for r in range(R):
+        n = int((idx[r] >= 0).sum())
+        if n < 8:
+            continue
+        pick = g.choice(n, size=n // 4, replace=False)
+        bad = np.where(g.random(pick.size) < 0.5, far + g.integers(0, 1 << 20, pick.size),
+                       -g.integers(2, 1 << 30, pick.size))
+        idx[r, pick] = bad.astype(np.int32)
+        valid[r, pick] = -1
+    say(f"[case] sparse MLA unaddressable entries, L={L}, table row {bt_stride}")
+    idx_t = torch.from_numpy(idx).cuda()
+    _, vc = caches(b)
+    out = torch.full((R, 128, 512), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((R, 128), float("nan"), dtype=torch.float32, device="cuda")
+    lisfa.sparse_mla_attn(b.q, vc, b.row_seq, idx_t, out, lse, softmax_scale=b.wl.softmax_scale)
+    torch.cuda.synchronize()
+    out, lse = _np(out), _np(lse)
+    inp = W.to_numpy(b)
+    for r in range(R):
+        ref_out, ref_lse = O.attend_row(inp, r, valid[r])
+        check_out(out[r], ref_out, False, f"L={L} row {r}")
+        check_lse(lse[r], ref_lse, f"L={L} row {r}")
+
+
 # ------------------------------------------------------------ fused call ---
 
 def test_fused_prefill_two_sequences_row_chunks(lib):
