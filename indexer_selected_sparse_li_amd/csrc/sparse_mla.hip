@@ -670,9 +670,9 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
     const int nk = k1 - k0;
     const int seq = a.row_seq[r];
     const int nt_fill = (nk + TROWS - 1) / TROWS;
-    // roles.  bf16 rows: q-waves 0, 1 (32 heads each, SIMDs 0 and 1), p-waves
-    // 2, 3, 6, 7 (SIMDs 2 and 3), waves 4 and 5 help with the slot table only.
-    // fp8 rows: q-waves 0..3, p-waves 4..7.
+    // roles: q-waves 0, 1 (32 heads each, SIMDs 0 and 1), p-waves 2, 3, 6, 7
+    // (SIMDs 2 and 3), helper waves 4 and 5 (the slot table, the first tiles;
+    // fp8 rows: every tile)
     const bool is_q = wave < 2;
     const bool is_p = (wave & 3) >= 2;
 
