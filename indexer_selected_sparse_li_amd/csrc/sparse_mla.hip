@@ -988,9 +988,12 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
                 }
             }
         }
+        // KVF 2: lane q (q < NTL) of a row's 8 lanes holds the row's factor of
+        // column tile q (one load per row group instead of NTL); KVF 1: every lane
+        // holds the row's factor
         struct Codes {
             u32x2 v[2][NJ];
-            float f[2][NTL];
+            float f[2];
         };
         int frow[2], fsw[2];
 #pragma unroll
@@ -1010,10 +1013,10 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
                     cd.v[rr][j] = a.gather_nt ? __builtin_nontemporal_load(src) : *src;
                 }
                 if constexpr (KVF == 1) {
-                    cd.f[rr][0] = ok ? a.kv.scale[(int64_t)sl / a.kv.scale_group] : 0.f;
+                    cd.f[rr] = ok ? a.kv.scale[(int64_t)sl / a.kv.scale_group] : 0.f;
                 } else if constexpr (KVF == 2) {
-#pragma unroll
-                    for (int q = 0; q < NTL; ++q) cd.f[rr][q] = ok ? a.kv.scale[(int64_t)sl * NTL + q] : 0.f;
+                    const int q = lane & 7;
+                    cd.f[rr] = ok && q < NTL ? a.kv.scale[(int64_t)sl * NTL + q] : 0.f;
                 }
             }
         };
@@ -1030,9 +1033,11 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
                     b.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cd.v[rr][j].y, 1.0f, true));
                     *(__attribute__((address_space(3))) u32x4*)(dst + j * 1024) = b;
                 }
-                if ((lane & 7) == 0) {
-#pragma unroll
-                    for (int q = 0; q < NTL; ++q) kvf[(buf * NTL + q) * TROWS + frow[rr]] = cd.f[rr][q];
+                if constexpr (KVF == 1) {
+                    if ((lane & 7) == 0) kvf[buf * TROWS + frow[rr]] = cd.f[rr];
+                } else if constexpr (KVF == 2) {
+                    const int q = lane & 7;
+                    if (q < NTL) kvf[(buf * NTL + q) * TROWS + frow[rr]] = cd.f[rr];
                 }
             }
         };
