@@ -991,8 +991,12 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
         // KVF 2: lane q (q < NTL) of a row's 8 lanes holds the row's factor of
         // column tile q (one load per row group instead of NTL); KVF 1: every lane
         // holds the row's factor
+        // codes of the 512 latent columns as 16-byte loads (lane: pair
+        // p = 8 k + l % 8 of 16 columns, bf16 chunks 2 p and 2 p + 1), the 64 rope
+        // columns as one 8-byte load (chunk 64 + ((l % 8) ^ swz8(row)))
         struct Codes {
-            u32x2 v[2][NJ];
+            u32x4 v[2][4];
+            u32x2 rope[2];
             float f[2];
         };
         int frow[2], fsw[2];
@@ -1008,9 +1012,13 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
                 const bool ok = sl != 0xFFFFFFFFu;
                 const uint8_t* gp = ok ? a.kv.data + (uint64_t)sl * (uint32_t)a.kv.row_stride : g_zero_row;
 #pragma unroll
-                for (int j = 0; j < NJ; ++j) {
-                    const u32x2* src = (const u32x2*)(gp + (8 * j + fsw[rr]) * 8);
-                    cd.v[rr][j] = a.gather_nt ? __builtin_nontemporal_load(src) : *src;
+                for (int k = 0; k < 4; ++k) {
+                    const u32x4* src = (const u32x4*)(gp + (8 * k + (lane & 7)) * 16);
+                    cd.v[rr][k] = a.gather_nt ? __builtin_nontemporal_load(src) : *src;
+                }
+                {
+                    const u32x2* src = (const u32x2*)(gp + (64 + fsw[rr]) * 8);
+                    cd.rope[rr] = a.gather_nt ? __builtin_nontemporal_load(src) : *src;
                 }
                 if constexpr (KVF == 1) {
                     cd.f[rr] = ok ? a.kv.scale[(int64_t)sl / a.kv.scale_group] : 0.f;
@@ -1021,18 +1029,29 @@ __global__ __launch_bounds__(512) void sfa_mla_kernel(MlaDev a, int kps, int nsp
             }
         };
         auto put = [&](const Codes& cd, int buf) {
+            auto cvt8 = [](u32x2 c) {   // 8 e4m3 codes -> 8 bf16, exact
+                u32x4 b;
+                b.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.0f, false));
+                b.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.0f, true));
+                b.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.0f, false));
+                b.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.0f, true));
+                return b;
+            };
 #pragma unroll
             for (int rr = 0; rr < 2; ++rr) {
-                lds_u8* dst = (lds_u8*)tile + buf * TB + (2 * hw + rr) * GB + lane * 16;
+                lds_u8* grp = (lds_u8*)tile + buf * TB + (2 * hw + rr) * GB;
+                lds_u8* rowp = grp + (lane >> 3) * 128;
+                const int sw = sfa_swz8(frow[rr]);
 #pragma unroll
-                for (int j = 0; j < NJ; ++j) {
-                    u32x4 b;
-                    b.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cd.v[rr][j].x, 1.0f, false));
-                    b.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cd.v[rr][j].x, 1.0f, true));
-                    b.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cd.v[rr][j].y, 1.0f, false));
-                    b.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cd.v[rr][j].y, 1.0f, true));
-                    *(__attribute__((address_space(3))) u32x4*)(dst + j * 1024) = b;
+                for (int k = 0; k < 4; ++k) {
+                    const int pp = 8 * k + (lane & 7);            // chunks 2 pp, 2 pp + 1 of block pp / 4
+                    lds_u8* blk = rowp + (pp >> 2) * 1024;
+                    const int c0 = (2 * pp) & 7;
+                    *(__attribute__((address_space(3))) u32x4*)(blk + ((c0 ^ sw) << 4)) = cvt8(u32x2{cd.v[rr][k].x, cd.v[rr][k].y});
+                    *(__attribute__((address_space(3))) u32x4*)(blk + (((c0 + 1) ^ sw) << 4)) =
+                        cvt8(u32x2{cd.v[rr][k].z, cd.v[rr][k].w});
                 }
+                *(__attribute__((address_space(3))) u32x4*)(grp + lane * 16 + 8 * 1024) = cvt8(cd.rope[rr]);
                 if constexpr (KVF == 1) {
                     if ((lane & 7) == 0) kvf[buf * TROWS + frow[rr]] = cd.f[rr];
                 } else if constexpr (KVF == 2) {
